@@ -1,0 +1,184 @@
+/*
+ * w8mp.h -- C ABI of the MI355X (gfx950) quantized-linear library libw8mp.so.
+ *
+ * Two weight-8-bit / activation-8-bit linear layers, Y = X W^T:
+ *
+ *  1. LLM.int8 mixed-precision decomposition ("Image21-INT8" model card,
+ *     section "Quantization": bitsandbytes LLM.int8 with outlier threshold
+ *     6.0, outliers handled in floating point, no calibration). Every input
+ *     column that holds some |x| > threshold is taken out to a 16-bit floating
+ *     side path; each token row of the rest gets a symmetric absmax int8 code;
+ *     the int8 x int8 contraction against rowwise int8 weights accumulates in
+ *     int32 and is dequantised by sx[m] * sw[n] / 127^2 (the vector-wise
+ *     scheme of LLM.int8(), Dettmers et al. 2022).
+ *
+ *  2. FP8-E4M3 W8A8 ("Qwen-Image-2.1 Text Encoder: FP8" card, section
+ *     "Format": E4M3 weights with one scale per output channel, activations
+ *     quantised per token at run time; "Darkstar-Qwen-Image-2.1-Base-ModelOpt-
+ *     FP8" card, section "Precision map": static per-tensor input scale).
+ *
+ * Conventions for every entry point
+ *  - Layouts are row-major and dense: X [M,K], W and Wq [N,K] (the [out,in]
+ *    order of a linear layer), Y [M,N]. Base pointers must be 16-byte aligned.
+ *  - Every array argument is DEVICE memory owned by the caller. The library
+ *    keeps no pointer after a call returns and allocates no device memory.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream of
+ *    the current device) and is asynchronous: the call returns before the GPU
+ *    has finished. Nothing in a call synchronises the host.
+ *  - Arguments are validated on the host before any HIP call; a rejected call
+ *    touches no memory and enqueues nothing. The status says why, and
+ *    w8_last_error() gives a readable detail (thread-local).
+ *  - Input values are not inspected: finite inputs are a precondition.
+ *  - Results are deterministic: the same inputs give the same bits.
+ *  - Concurrent calls on different streams need distinct workspaces.
+ */
+#ifndef W8MP_H
+#define W8MP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  W8_OK = 0,
+  W8_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, bad alignment, bad threshold */
+  W8_ERR_UNSUPPORTED = 2,      /* valid request this library does not implement      */
+  W8_ERR_WORKSPACE = 3,        /* workspace missing or smaller than the size query   */
+  W8_ERR_HIP = 4               /* a HIP launch failed (see w8_last_error)            */
+} w8_status;
+
+typedef enum { W8_DT_F16 = 0, W8_DT_BF16 = 1, W8_DT_F32 = 2 } w8_dtype;
+
+typedef enum { W8_Q_INT8 = 0, W8_Q_FP8_E4M3 = 1 } w8_qformat;
+
+/* Largest K the int8 contraction accepts: K * 127^2 < 2^31, so the int32
+ * accumulator cannot overflow. */
+#define W8_INT8_MAX_K 133144
+
+/*
+ * quantize_weight_rowwise -- one-off weight quantisation, per output row.
+ *
+ * The model cards store the quantized weights once and never re-quantise
+ * them at load ("Image21-INT8", "Installation and loading"); this call makes
+ * that stored form.
+ *
+ *   W    [N,K] f16 or bf16 (w_dt), device.
+ *   fmt  W8_Q_INT8:     sw[n] = max_k |W[n,k]| (fp32),
+ *                       Wq[n,k] = clamp(rne(fl32(W[n,k] * fl32(127/sw[n]))), +-127)
+ *                       as int8; rows with sw = 0 are all zero.
+ *        W8_Q_FP8_E4M3: sw[n] = bf16(fl32(max_k |W[n,k]| / 448)) held in fp32
+ *                       (the FP8 card stores one bf16 scale per output channel),
+ *                       Wq[n,k] = E4M3FN(fl32(W[n,k] / sw[n])), round to nearest
+ *                       even, saturating at +-448, sign of zero kept; rows with
+ *                       sw = 0 are all zero.
+ *   Wq   [N,K] int8 / uint8 E4M3 codes (output, device).
+ *   sw   [N] fp32 (output, device).
+ * Requires N >= 1, 16 <= K, K % 16 == 0.
+ */
+w8_status quantize_weight_rowwise(const void* W, int w_dt, int64_t N, int64_t K, int fmt,
+                                  void* Wq, float* sw, void* stream);
+
+/*
+ * int8_mixed_linear -- Y = X W^T with the LLM.int8 decomposition.
+ *
+ *   X          [M,K] f16 or bf16 (x_dt), device.
+ *   Wq, sw     the W8_Q_INT8 output of quantize_weight_rowwise ([N,K], [N]).
+ *   threshold  outlier threshold t (the model card uses 6.0). A column k is an
+ *              outlier column when |X[m,k]| > t for some row m of THIS call.
+ *              +inf gives plain vector-wise int8; t < 0 or NaN is rejected.
+ *   Y          [M,N] f16 or f32 (y_dt), device, written in full.
+ *   workspace  device scratch of at least int8_mixed_linear_workspace_size()
+ *              bytes, 256-byte aligned; contents undefined after the call.
+ *
+ * What is computed (O = outlier columns, ascending):
+ *   sx[m]   = max_{k not in O} |X[m,k]|                     (fp32, exact)
+ *   q[m,k]  = 0 for k in O, else clamp(rne(fl32(X * fl32(127/sx[m]))), +-127)
+ *   acc     = q Wq^T in int32 (exact)
+ *   Y[m,n]  = (sw[n]/127) * ((sx[m]/127) * acc[m,n] + sum_{k in O} X[m,k] Wq[n,k])
+ * where the outlier sum runs on 16-bit MFMA in X's own type with fp32
+ * accumulation (Wq's integers are exact in both 16-bit types) and the
+ * epilogue is fp32, rounded to nearest even into Y.
+ * Requires M, N >= 1, 16 <= K <= W8_INT8_MAX_K, K % 16 == 0.
+ */
+size_t int8_mixed_linear_workspace_size(int64_t M, int64_t N, int64_t K);
+w8_status int8_mixed_linear(const void* X, int x_dt, int64_t M, int64_t K,
+                            const int8_t* Wq, const float* sw, int64_t N, float threshold,
+                            void* Y, int y_dt, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
+ * fp8_w8a8_linear -- Y = X W^T with E4M3 weights and activations.
+ *
+ *   X          [M,K] f16 or bf16, device.
+ *   Wq8, sw    the W8_Q_FP8_E4M3 output of quantize_weight_rowwise. A
+ *              per-tensor weight scale is passed as a constant vector.
+ *   act_scale  NULL: dynamic per-token scale sx[m] = fl32(max_k |X[m,k]| / 448).
+ *              Otherwise a DEVICE pointer to one fp32 static per-tensor input
+ *              scale (must be finite and >= 0; 0 gives zero codes).
+ *   Y          [M,N] bf16, f16 or f32, device.
+ *   workspace  at least fp8_w8a8_linear_workspace_size() bytes.
+ * Codes: xq[m,k] = E4M3FN(fl32(X[m,k] / sx[m])) (saturating), all zero when
+ * sx[m] = 0. Y[m,n] = sx[m] * sw[n] * sum_k xq*wq, fp32 accumulation on FP8
+ * MFMA, rounded to nearest even into Y.
+ * Requires M, N >= 1, 16 <= K <= 65536, K % 16 == 0.
+ */
+size_t fp8_w8a8_linear_workspace_size(int64_t M, int64_t N, int64_t K);
+w8_status fp8_w8a8_linear(const void* X, int x_dt, int64_t M, int64_t K,
+                          const uint8_t* Wq8, const float* sw, int64_t N,
+                          const float* act_scale, void* Y, int y_dt,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Readable name of a status; never NULL. */
+const char* w8_status_string(int status);
+/* Detail of the last failed call on this host thread ("" if none). */
+const char* w8_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Parity exports: the same kernels as above, with their intermediate results
+ * written to caller buffers. Used by the test suite.
+ * ------------------------------------------------------------------------ */
+
+/* The activation half of int8_mixed_linear (outlier detection, row scales,
+ * int8 codes, outlier fix-up). Outputs (device): q [M,K] int8, sx [M] fp32,
+ * outlier_idx [K] int32 (first *n_outliers entries valid, ascending),
+ * n_outliers [1] int32. Workspace: w8dbg_int8_quantize_activations_workspace_size(M, K). */
+size_t w8dbg_int8_quantize_activations_workspace_size(int64_t M, int64_t K);
+w8_status w8dbg_int8_quantize_activations(const void* X, int x_dt, int64_t M, int64_t K,
+                                          float threshold, int8_t* q, float* sx,
+                                          int32_t* outlier_idx, int32_t* n_outliers,
+                                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* The int8 MFMA contraction alone: acc [M,N] int32 = q [M,K] . Wq [N,K]^T. */
+w8_status w8dbg_int8_gemm_i32(const int8_t* q, const int8_t* Wq, int64_t M, int64_t N, int64_t K,
+                              int32_t* acc, void* stream);
+
+/* The activation half of fp8_w8a8_linear: xq [M,K] E4M3 codes, sx [M] fp32. */
+w8_status w8dbg_fp8_quantize_activations(const void* X, int x_dt, int64_t M, int64_t K,
+                                         const float* act_scale, uint8_t* xq, float* sx,
+                                         void* stream);
+
+/* ------------------------------------------------------------------------
+ * Measurement hook (process-wide, for benchmarks; not for concurrent use).
+ *
+ * w8_profile_start(max_calls): from now on, each int8_mixed_linear and
+ * fp8_w8a8_linear call (up to max_calls of them) records HIP events on its own
+ * stream at its kernel boundaries. Creates the events (host-side HIP objects,
+ * no device memory). Returns W8_ERR_INVALID_ARGUMENT if max_calls < 1.
+ *
+ * w8_profile_stop(stage_ms, n_calls): waits for the recorded events, writes
+ * the summed GPU time of each stage in milliseconds -- stage_ms[0]: outlier
+ * mask clear + row quantisation pass, stage_ms[1]: outlier fix-up and gather
+ * (0 for FP8), stage_ms[2]: the GEMM -- and the number of calls recorded,
+ * then destroys the events and turns the hook off.
+ * ------------------------------------------------------------------------ */
+w8_status w8_profile_start(int max_calls);
+w8_status w8_profile_stop(double* stage_ms /*[3]*/, int* n_calls);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W8MP_H */

@@ -1,0 +1,134 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol,
+and rejects bad arguments on the host before any HIP call (no GPU needed:
+none of these calls reaches a kernel launch)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from w8a8_mixed_precision_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w8mp.h")
+
+# Fake, 256-byte aligned addresses: validation must reject the call before
+# anything dereferences them.
+A = 0x10000
+WS_BIG = 1 << 40
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"if", "sizeof"})
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _abi.lib()
+    names = declared_functions()
+    assert "int8_mixed_linear" in names and "fp8_w8a8_linear" in names and "quantize_weight_rowwise" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_abi.SIGNATURES), "binding and header disagree"
+
+
+def test_status_strings():
+    assert _abi.status_string(0) == "W8_OK"
+    assert _abi.status_string(3) == "W8_ERR_WORKSPACE"
+    assert _abi.status_string(99) == "W8_UNKNOWN_STATUS"
+
+
+def _int8(**kw):
+    a = dict(X=A, x_dt=_abi.W8_DT_BF16, M=64, K=256, Wq=A, sw=A, N=32, t=6.0, Y=A, y_dt=_abi.W8_DT_F16,
+             ws=A, ws_bytes=WS_BIG, stream=None)
+    a.update(kw)
+    return _abi.lib().int8_mixed_linear(a["X"], a["x_dt"], a["M"], a["K"], a["Wq"], a["sw"], a["N"], a["t"], a["Y"],
+                                        a["y_dt"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), _abi.W8_ERR_INVALID_ARGUMENT),
+    (dict(Wq=None), _abi.W8_ERR_INVALID_ARGUMENT),
+    (dict(Y=None), _abi.W8_ERR_INVALID_ARGUMENT),
+    (dict(M=0), _abi.W8_ERR_INVALID_ARGUMENT),
+    (dict(N=0), _abi.W8_ERR_INVALID_ARGUMENT),
+    (dict(K=0), _abi.W8_ERR_INVALID_ARGUMENT),
+    (dict(K=24), _abi.W8_ERR_INVALID_ARGUMENT),
+    (dict(K=8), _abi.W8_ERR_INVALID_ARGUMENT),
+    (dict(K=133152), _abi.W8_ERR_UNSUPPORTED),
+    (dict(t=-1.0), _abi.W8_ERR_INVALID_ARGUMENT),
+    (dict(t=math.nan), _abi.W8_ERR_INVALID_ARGUMENT),
+    (dict(x_dt=_abi.W8_DT_F32), _abi.W8_ERR_UNSUPPORTED),
+    (dict(y_dt=_abi.W8_DT_BF16), _abi.W8_ERR_UNSUPPORTED),
+    (dict(X=A + 8), _abi.W8_ERR_INVALID_ARGUMENT),
+    (dict(ws=None), _abi.W8_ERR_WORKSPACE),
+    (dict(ws=A + 16), _abi.W8_ERR_WORKSPACE),
+    (dict(ws_bytes=1024), _abi.W8_ERR_WORKSPACE),
+])
+def test_int8_mixed_linear_rejects(kw, status):
+    assert _int8(**kw) == status
+    assert _abi.lib().w8_last_error().decode() != ""
+
+
+def test_workspace_size_is_exact_boundary():
+    lib = _abi.lib()
+    need = lib.int8_mixed_linear_workspace_size(64, 32, 256)
+    assert need >= 64 * 256 + 2 * (64 + 32) * 256
+    assert _int8(ws_bytes=need - 1) == _abi.W8_ERR_WORKSPACE
+    assert lib.int8_mixed_linear_workspace_size(0, 32, 256) == 0
+    # grows with every dimension
+    assert lib.int8_mixed_linear_workspace_size(65, 32, 256) > need
+    assert lib.int8_mixed_linear_workspace_size(64, 33, 256) > need
+    assert lib.int8_mixed_linear_workspace_size(64, 32, 272) > need
+    assert lib.fp8_w8a8_linear_workspace_size(512, 4096, 4096) >= 512 * 4096 + 4 * 512
+
+
+def _fp8(**kw):
+    a = dict(X=A, x_dt=_abi.W8_DT_BF16, M=512, K=4096, Wq=A, sw=A, N=1024, s=None, Y=A, y_dt=_abi.W8_DT_BF16,
+             ws=A, ws_bytes=WS_BIG, stream=None)
+    a.update(kw)
+    return _abi.lib().fp8_w8a8_linear(a["X"], a["x_dt"], a["M"], a["K"], a["Wq"], a["sw"], a["N"], a["s"], a["Y"],
+                                      a["y_dt"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), _abi.W8_ERR_INVALID_ARGUMENT),
+    (dict(K=100), _abi.W8_ERR_INVALID_ARGUMENT),
+    (dict(K=65552), _abi.W8_ERR_UNSUPPORTED),
+    (dict(y_dt=7), _abi.W8_ERR_UNSUPPORTED),
+    (dict(x_dt=_abi.W8_DT_F32), _abi.W8_ERR_UNSUPPORTED),
+    (dict(ws_bytes=16), _abi.W8_ERR_WORKSPACE),
+    (dict(Y=A + 2), _abi.W8_ERR_INVALID_ARGUMENT),
+])
+def test_fp8_linear_rejects(kw, status):
+    assert _fp8(**kw) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, _abi.W8_DT_BF16, 16, 64, _abi.W8_Q_INT8, A, A, None), _abi.W8_ERR_INVALID_ARGUMENT),
+    ((A, _abi.W8_DT_F32, 16, 64, _abi.W8_Q_INT8, A, A, None), _abi.W8_ERR_UNSUPPORTED),
+    ((A, _abi.W8_DT_BF16, 16, 64, 5, A, A, None), _abi.W8_ERR_UNSUPPORTED),
+    ((A, _abi.W8_DT_BF16, 16, 60, _abi.W8_Q_INT8, A, A, None), _abi.W8_ERR_INVALID_ARGUMENT),
+    ((A, _abi.W8_DT_BF16, 0, 64, _abi.W8_Q_FP8_E4M3, A, A, None), _abi.W8_ERR_INVALID_ARGUMENT),
+])
+def test_weight_quantisation_rejects(args, status):
+    assert _abi.lib().quantize_weight_rowwise(*args) == status
+
+
+def test_debug_exports_reject():
+    lib = _abi.lib()
+    assert lib.w8dbg_int8_gemm_i32(A, A, 4, 4, 20, A, None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert lib.w8dbg_int8_gemm_i32(None, A, 4, 4, 32, A, None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert lib.w8dbg_fp8_quantize_activations(A, _abi.W8_DT_BF16, 4, 20, None, A, A, None) == \
+        _abi.W8_ERR_INVALID_ARGUMENT
+    assert lib.w8dbg_int8_quantize_activations(A, _abi.W8_DT_BF16, 4, 32, 6.0, A, A, A, A, A, 1,
+                                               None) == _abi.W8_ERR_WORKSPACE
+
+
+def test_binding_refuses_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_abi, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_abi, "_lib", None)
+    with pytest.raises(ImportError):
+        _abi.lib()

@@ -1,0 +1,118 @@
+"""GPU parity of the FP8-E4M3 W8A8 path against the CPU oracle.
+
+Bit-exact: E4M3 weight codes, bf16-valued weight scales, activation codes and
+scales (dynamic and static). Outputs: relative Frobenius error <= 1e-2 for
+16-bit outputs, <= 2e-3 for fp32 (the int8 path's bounds; FP8 accumulation is
+fp32 on both sides of the comparison's error budget), globally and per row.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import w8a8_mixed_precision_amd as w8
+from oracle import w8ref as o
+from tests.gpu_util import OUT, announce, dev16, host_stored, rel_fro, row_rel_fro
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f16": 1e-2, "bf16": 1e-2, "f32": 2e-3}
+
+
+def _weights(case):
+    wf = o.decode16(case.w_bits, case.w_dtype)
+    wq_ref, sw_ref = o.quantize_weight_fp8(wf)
+    wq, sw = w8.quantize_weight_rowwise(dev16(case.w_bits, case.w_dtype), "fp8")
+    torch.cuda.synchronize()
+    return wq, sw, wq_ref, sw_ref
+
+
+def _static_scale(case):
+    cal = o.decode16(case.extra["x_cal_bits"], case.x_dtype) if "x_cal_bits" in case.extra else \
+        o.decode16(case.x_bits, case.x_dtype)
+    return np.float32(np.abs(cal).max() / np.float32(448.0))
+
+
+SMALL = [
+    synth.random_linear(300, 272, 520, seed=51, x_dtype="bf16", name="ragged_bf16"),
+    synth.random_linear(129, 48, 77, seed=52, x_dtype="f16", name="ragged_f16"),
+    synth.random_linear(64, 1040, 256, seed=53, x_dtype="bf16", outlier_cols=3, outlier_lo=100, outlier_hi=2000,
+                        name="wide_range"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: c.name)
+def test_fp8_weight_quantisation_bit_exact(case):
+    announce("fp8 weight quant", case.name)
+    wq, sw, wq_ref, sw_ref = _weights(case)
+    assert np.array_equal(sw.cpu().numpy(), sw_ref)
+    assert np.array_equal(wq.cpu().numpy(), wq_ref)
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: c.name)
+@pytest.mark.parametrize("static", [False, True])
+def test_fp8_activation_quantisation_bit_exact(case, static):
+    xf = o.decode16(case.x_bits, case.x_dtype)
+    s = _static_scale(case) if static else None
+    xq_ref, sx_ref = o.quantize_activations_fp8(xf, s)
+    announce("fp8 act quant", case.name, static)
+    sp = torch.tensor([s], dtype=torch.float32, device="cuda") if static else None
+    xq, sx = w8.debug_fp8_quantize_activations(dev16(case.x_bits, case.x_dtype), sp)
+    assert np.array_equal(sx.cpu().numpy(), sx_ref)
+    assert np.array_equal(xq.cpu().numpy(), xq_ref)
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.125, 3.0, 2.0 ** -20])
+def test_every_bf16_value_encodes_like_the_oracle(scale):
+    """All finite bf16 patterns through the static-scale E4M3 encoder
+    (covers saturation, subnormals, ties and the sign of zero)."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    keep = np.isfinite(o.decode16(bits, "bf16"))
+    rows = bits[keep][: (keep.sum() // 256) * 256].reshape(-1, 256)
+    xf = o.decode16(rows, "bf16")
+    xq_ref, sx_ref = o.quantize_activations_fp8(xf, np.float32(scale))
+    announce("fp8 exhaustive bf16 encode", scale)
+    xq, sx = w8.debug_fp8_quantize_activations(dev16(rows, "bf16"),
+                                               torch.tensor([scale], dtype=torch.float32, device="cuda"))
+    assert np.array_equal(xq.cpu().numpy(), xq_ref)
+
+
+def _check(y, ref_stored, out_dtype, label):
+    got = o.stored_to_f64(host_stored(y, out_dtype), out_dtype)
+    want = o.stored_to_f64(ref_stored, out_dtype)
+    assert np.all(np.isfinite(got)) and np.std(got) > 0, label
+    e, er = rel_fro(got, want), row_rel_fro(got, want).max()
+    assert e <= TOL[out_dtype] and er <= TOL[out_dtype], (label, e, er)
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: c.name)
+@pytest.mark.parametrize("out_dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("static", [False, True])
+def test_fp8_linear_matches_oracle(case, out_dtype, static):
+    wq, sw, wq_ref, sw_ref = _weights(case)
+    s = _static_scale(case) if static else None
+    ref = o.fp8_w8a8_linear(case.x_bits, case.x_dtype, wq_ref, sw_ref, s, out_dtype)
+    announce("fp8_w8a8_linear", case.name, out_dtype, static)
+    sp = torch.tensor([s], dtype=torch.float32, device="cuda") if static else None
+    y = w8.fp8_w8a8_linear(dev16(case.x_bits, case.x_dtype), wq, sw, sp, OUT[out_dtype])
+    torch.cuda.synchronize()
+    _check(y, ref["Y"], out_dtype, (case.name, static))
+
+
+@pytest.mark.parametrize("layer", list(synth.FP8_TEXT_LAYERS))
+@pytest.mark.parametrize("static", [False, True])
+def test_fp8_text_encoder_full_size(layer, static):
+    c = synth.fp8_text_encoder(layer, massive=(layer == "q"))
+    wq, sw, wq_ref, sw_ref = _weights(c)
+    assert np.array_equal(sw.cpu().numpy(), sw_ref) and np.array_equal(wq.cpu().numpy(), wq_ref)
+    s = _static_scale(c) if static else None
+    xf = o.decode16(c.x_bits, "bf16")
+    xq_ref, sx_ref = o.quantize_activations_fp8(xf, s)
+    announce("fp8 text encoder", c.name, static)
+    sp = torch.tensor([s], dtype=torch.float32, device="cuda") if static else None
+    x = dev16(c.x_bits, "bf16")
+    xq, sx = w8.debug_fp8_quantize_activations(x, sp)
+    assert np.array_equal(xq.cpu().numpy(), xq_ref) and np.array_equal(sx.cpu().numpy(), sx_ref)
+    ref = o.fp8_w8a8_linear(c.x_bits, "bf16", wq_ref, sw_ref, s, "bf16")
+    y = w8.fp8_w8a8_linear(x, wq, sw, sp, torch.bfloat16)
+    _check(y, ref["Y"], "bf16", c.name)

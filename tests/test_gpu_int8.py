@@ -1,0 +1,225 @@
+"""GPU parity of the LLM.int8 path against the CPU oracle (through the C ABI).
+
+Bit-exact: int8 weight codes and scales, activation codes, row scales, the
+outlier-column set, int32 accumulators. Outputs: relative Frobenius error
+<= 1e-2 for fp16 output and <= 2e-3 for fp32 output, globally and per row.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import w8a8_mixed_precision_amd as w8
+from oracle import w8ref as o
+from tests.gpu_util import announce, dev16, host_stored, rel_fro, row_rel_fro
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f16": 1e-2, "f32": 2e-3}
+
+
+def _quant_weights_both(case):
+    wf = o.decode16(case.w_bits, case.w_dtype)
+    wq_ref, sw_ref = o.quantize_weight_int8(wf)
+    wq, sw = w8.quantize_weight_rowwise(dev16(case.w_bits, case.w_dtype), "int8")
+    torch.cuda.synchronize()
+    return wq, sw, wq_ref, sw_ref
+
+
+def _check_outputs(y_gpu, ref, out_dtype, label):
+    got = o.stored_to_f64(host_stored(y_gpu, out_dtype), out_dtype)
+    want = o.stored_to_f64(ref, out_dtype)
+    assert np.all(np.isfinite(got)), label
+    assert np.std(got) > 0, label          # finite and non-constant
+    e = rel_fro(got, want)
+    er = row_rel_fro(got, want).max()
+    assert e <= TOL[out_dtype] and er <= TOL[out_dtype], (label, e, er)
+    return e, er
+
+
+# ----------------------------------------------------------------------------
+# small and ragged cases (oracle runs on all of them in full)
+# ----------------------------------------------------------------------------
+
+def _cases():
+    yield synth.tiny_int8()
+    yield synth.random_linear(300, 272, 520, seed=31, x_dtype="bf16", outlier_cols=5, name="ragged_bf16")
+    yield synth.random_linear(257, 48, 130, seed=32, x_dtype="f16", outlier_cols=2, outlier_rows=[0, 100, 256],
+                              name="ragged_f16_rows")
+    yield synth.random_linear(513, 1040, 777, seed=33, x_dtype="bf16", outlier_cols=40, name="many_outliers")
+    yield synth.random_linear(70, 16, 33, seed=34, x_dtype="bf16", outlier_cols=0, name="k16_no_outliers")
+
+
+CASES = list(_cases())
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: c.name)
+def test_weight_quantisation_bit_exact(case):
+    announce("int8 weight quant", case.name)
+    wq, sw, wq_ref, sw_ref = _quant_weights_both(case)
+    assert np.array_equal(wq.cpu().numpy(), wq_ref)
+    assert np.array_equal(sw.cpu().numpy(), sw_ref)
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: c.name)
+@pytest.mark.parametrize("t", [6.0, math.inf, 0.0, 2.0])
+def test_activation_quantisation_bit_exact(case, t):
+    announce("int8 act quant", case.name, t)
+    xf = o.decode16(case.x_bits, case.x_dtype)
+    O_ref, sx_ref, q_ref = o.quantize_activations_int8(xf, t)
+    q, sx, O = w8.debug_int8_quantize_activations(dev16(case.x_bits, case.x_dtype), t)
+    assert np.array_equal(O.cpu().numpy(), O_ref)
+    assert np.array_equal(sx.cpu().numpy(), sx_ref)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+
+
+def test_activation_quantisation_fixup_rows():
+    """Rows whose largest |x| <= t sits in a column that another row makes
+    an outlier column must be re-scaled without that column."""
+    rng = np.random.default_rng(40)
+    x = rng.standard_normal((96, 512)).astype(np.float32)
+    x[5, 100] = 7.5                   # column 100 becomes an outlier column
+    x[6, 100] = 5.5                   # ...and is row 6's provisional absmax
+    x[7, 100] = -6.0                  # exactly t: not an outlier, but its column is
+    x[8, 300] = 9.0
+    x[8, 301] = 5.9                   # row 8: max in a clean column
+    x[9, :] = 0.0
+    x[9, 100] = 3.0                   # row 9: all clean columns zero -> sx = 0
+    bits = synth.encode16(x, "bf16")
+    xf = o.decode16(bits, "bf16")
+    O_ref, sx_ref, q_ref = o.quantize_activations_int8(xf, 6.0)
+    assert 100 in O_ref and sx_ref[9] == 0
+    announce("int8 fixup rows")
+    q, sx, O = w8.debug_int8_quantize_activations(dev16(bits, "bf16"), 6.0)
+    assert np.array_equal(O.cpu().numpy(), O_ref)
+    assert np.array_equal(sx.cpu().numpy(), sx_ref)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+
+
+@pytest.mark.parametrize("K", [16400, 20480])
+def test_activation_quantisation_long_rows(K):
+    """K above 16384 takes the two-pass (streaming) row kernel."""
+    c = synth.random_linear(40, K, 16, seed=41, x_dtype="bf16", outlier_cols=3)
+    xf = o.decode16(c.x_bits, "bf16")
+    O_ref, sx_ref, q_ref = o.quantize_activations_int8(xf, 6.0)
+    announce("int8 act quant long rows", K)
+    q, sx, O = w8.debug_int8_quantize_activations(dev16(c.x_bits, "bf16"), 6.0)
+    assert np.array_equal(O.cpu().numpy(), O_ref)
+    assert np.array_equal(sx.cpu().numpy(), sx_ref)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+
+
+def test_every_bf16_value_encodes_like_the_oracle():
+    """All finite bf16 patterns, 256 per row, each row with its own scale."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = o.decode16(bits, "bf16")
+    keep = np.isfinite(vals)
+    rows = bits[keep][: (keep.sum() // 256) * 256].reshape(-1, 256)
+    xf = o.decode16(rows, "bf16")
+    O_ref, sx_ref, q_ref = o.quantize_activations_int8(xf, math.inf)
+    announce("int8 exhaustive bf16 encode")
+    q, sx, O = w8.debug_int8_quantize_activations(dev16(rows, "bf16"), math.inf)
+    assert O.numel() == 0
+    assert np.array_equal(sx.cpu().numpy(), sx_ref)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 520, 272), (257, 130, 48), (600, 700, 320), (64, 512, 256), (1, 1, 16),
+                                   (256, 256, 16384)])
+def test_int8_gemm_accumulators_bit_exact(M, N, K):
+    rng = np.random.default_rng(M * 7 + N * 3 + K)
+    q = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    w = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    if M > 2 and N > 2:
+        q[0, :] = 127
+        w[0, :] = 127      # largest positive sum: 127^2 K
+        w[1, :] = -127     # largest negative sum
+    ref = o.int8_contract(q, w)
+    announce("int8 gemm i32", M, N, K)
+    acc = w8.debug_int8_gemm_i32(torch.from_numpy(q).cuda(), torch.from_numpy(w).cuda())
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), ref)
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: c.name)
+@pytest.mark.parametrize("out_dtype", ["f16", "f32"])
+@pytest.mark.parametrize("t", [6.0, math.inf, 0.0])
+def test_int8_mixed_linear_matches_oracle(case, out_dtype, t):
+    wq, sw, wq_ref, sw_ref = _quant_weights_both(case)
+    ref = o.int8_mixed_linear(case.x_bits, case.x_dtype, wq_ref, sw_ref, t, out_dtype)
+    announce("int8_mixed_linear", case.name, out_dtype, t)
+    y = w8.int8_mixed_linear(dev16(case.x_bits, case.x_dtype), wq, sw, t, {"f16": torch.float16,
+                                                                          "f32": torch.float32}[out_dtype])
+    torch.cuda.synchronize()
+    _check_outputs(y, ref["Y"], out_dtype, (case.name, t))
+
+
+def test_zero_row_gives_zero_output_row():
+    c = synth.random_linear(40, 128, 64, seed=42, x_dtype="bf16", outlier_cols=2)
+    x = c.x_bits.copy()
+    x[17] = 0
+    wq, sw, _, _ = _quant_weights_both(c)
+    announce("int8 zero row")
+    y = w8.int8_mixed_linear(dev16(x, "bf16"), wq, sw, 6.0, torch.float32).cpu().numpy()
+    assert not y[17].any() and y[16].any()
+
+
+def test_deterministic_non_default_stream_and_no_out_of_bounds_writes():
+    c = synth.random_linear(333, 528, 270, seed=43, x_dtype="bf16", outlier_cols=3)
+    wq, sw, wq_ref, sw_ref = _quant_weights_both(c)
+    x = dev16(c.x_bits, "bf16")
+    M, N = c.M, c.N
+    guard = 4096
+    buf = torch.full((M * N + 2 * guard,), 12345.0, dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    announce("int8 determinism/stream/guard")
+    with torch.cuda.stream(s):
+        y1 = w8.int8_mixed_linear(x, wq, sw, 6.0, torch.float32, out=buf[guard:guard + M * N].view(M, N))
+        y1c = y1.clone()
+        y2 = w8.int8_mixed_linear(x, wq, sw, 6.0, torch.float32)
+    s.synchronize()
+    assert torch.equal(y1c, y2)
+    b = buf.cpu().numpy()
+    assert np.all(b[:guard] == 12345.0) and np.all(b[guard + M * N:] == 12345.0)
+    ref = o.int8_mixed_linear(c.x_bits, "bf16", wq_ref, sw_ref, 6.0, "f32")
+    _check_outputs(y2, ref["Y"], "f32", "stream")
+
+
+# ----------------------------------------------------------------------------
+# the DiT workloads at full size, in the configuration bench.py times
+# ----------------------------------------------------------------------------
+
+FULL = {
+    "dit1024_qkv": synth.dit_qkv_1024,
+    "dit1024_mlp_up": lambda: synth.dit_mlp_1024("up"),
+    "dit1024_mlp_down": lambda: synth.dit_mlp_1024("down"),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_dit_1024_full_size(name):
+    c = FULL[name]()
+    announce("full-size", c.name)
+    xf = o.decode16(c.x_bits, "bf16")
+    wq, sw, wq_ref, sw_ref = _quant_weights_both(c)
+    assert np.array_equal(wq.cpu().numpy(), wq_ref) and np.array_equal(sw.cpu().numpy(), sw_ref)
+    x = dev16(c.x_bits, "bf16")
+    # codes, scales and outlier set on every row
+    O_ref, sx_ref, q_ref = o.quantize_activations_int8(xf, 6.0)
+    q, sx, O = w8.debug_int8_quantize_activations(x, 6.0)
+    assert np.array_equal(O.cpu().numpy(), O_ref)
+    assert set(c.injected_cols) <= set(O_ref.tolist())
+    assert np.array_equal(sx.cpu().numpy(), sx_ref)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    # accumulators and outputs on sampled rows (every injected row included)
+    rng = np.random.default_rng(44)
+    rows = np.unique(np.concatenate([rng.choice(c.M, 96, replace=False), np.array(c.injected_rows, int),
+                                     [0, c.M - 1]])).astype(int)
+    acc = w8.debug_int8_gemm_i32(q, wq)
+    acc_rows = acc[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.int64)
+    assert np.array_equal(acc_rows, o.int8_contract(q_ref[rows], wq_ref))
+    del acc
+    y = w8.int8_mixed_linear(x, wq, sw, 6.0, torch.float16)
+    ref = o.int8_mixed_linear(c.x_bits, "bf16", wq_ref, sw_ref, 6.0, "f16", rows=rows)
+    _check_outputs(y[torch.from_numpy(rows).cuda()], ref["Y"], "f16", c.name)

@@ -50,10 +50,10 @@ def test_encode_matches_torch_below_saturation():
 
 
 def test_encode_saturates_and_keeps_sign_of_zero():
-    v = np.array([448, 449, 463.9, 464, 500, 1e30, -448, -1e9, 0.0, -0.0, -2.0 ** -11, -2.0 ** -12, 2.0 ** -11],
-                 np.float32)
+    v = np.array([448, 449, 463.9, 464, 500, 1e30, -448, -1e9, 0.0, -0.0, -2.0 ** -11, -2.0 ** -12, 2.0 ** -11,
+                  np.inf, -np.inf], np.float32)
     got = o.e4m3_encode(v).tolist()
-    assert got == [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE, 0x00, 0x80, 0x80, 0x80, 0x00]
+    assert got == [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE, 0x00, 0x80, 0x80, 0x80, 0x00, 0x7E, 0xFE]
     # torch agrees once the input is clamped to the finite range
     assert np.array_equal(o.e4m3_encode(v), torch_e4m3(np.clip(v, -448, 448)))
 

@@ -1,0 +1,158 @@
+"""MI355X (gfx950) quantized linear layers: LLM.int8 mixed precision and FP8-E4M3 W8A8.
+
+Thin binding over libw8mp.so. Every step of the computation runs in the
+library's HIP kernels; this module only allocates outputs and workspaces with
+torch and passes device pointers and the current HIP stream.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _abi
+from ._abi import W8Error, lib  # noqa: F401
+
+_DT = {torch.float16: _abi.W8_DT_F16, torch.bfloat16: _abi.W8_DT_BF16, torch.float32: _abi.W8_DT_F32}
+
+__all__ = [
+    "quantize_weight_rowwise", "int8_mixed_linear", "fp8_w8a8_linear",
+    "debug_int8_quantize_activations", "debug_int8_gemm_i32", "debug_fp8_quantize_activations",
+    "int8_mixed_linear_workspace_size", "fp8_w8a8_linear_workspace_size", "W8Error",
+]
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _dt(t: torch.Tensor) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise ValueError(f"unsupported dtype {t.dtype}") from None
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's allocator returns 256-byte aligned blocks
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def int8_mixed_linear_workspace_size(M: int, N: int, K: int) -> int:
+    return int(lib().int8_mixed_linear_workspace_size(M, N, K))
+
+
+def fp8_w8a8_linear_workspace_size(M: int, N: int, K: int) -> int:
+    return int(lib().fp8_w8a8_linear_workspace_size(M, N, K))
+
+
+def quantize_weight_rowwise(w: torch.Tensor, fmt: str = "int8"):
+    """W [N,K] f16/bf16 -> (Wq [N,K] int8 or uint8 E4M3 codes, sw [N] fp32)."""
+    _dev(w, "w")
+    N, K = w.shape
+    if fmt == "int8":
+        wq = torch.empty((N, K), dtype=torch.int8, device=w.device)
+        f = _abi.W8_Q_INT8
+    elif fmt == "fp8":
+        wq = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+        f = _abi.W8_Q_FP8_E4M3
+    else:
+        raise ValueError(fmt)
+    sw = torch.empty((N,), dtype=torch.float32, device=w.device)
+    _abi.check(lib().quantize_weight_rowwise(w.data_ptr(), _dt(w), N, K, f, wq.data_ptr(), sw.data_ptr(),
+                                             _stream(w)))
+    return wq, sw
+
+
+def int8_mixed_linear(x: torch.Tensor, wq: torch.Tensor, sw: torch.Tensor, threshold: float = 6.0,
+                      out_dtype: torch.dtype = torch.float16, out: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = X W^T under the LLM.int8 decomposition (see include/w8mp.h)."""
+    _dev(x, "x"), _dev(wq, "wq"), _dev(sw, "sw")
+    M, K = x.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K or wq.dtype != torch.int8 or sw.shape != (N,) or sw.dtype != torch.float32:
+        raise ValueError("wq must be int8 [N,K] and sw fp32 [N]")
+    y = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=x.device)
+    need = int8_mixed_linear_workspace_size(M, N, K)
+    ws = workspace if workspace is not None else _workspace(need, x.device)
+    _abi.check(lib().int8_mixed_linear(x.data_ptr(), _dt(x), M, K, wq.data_ptr(), sw.data_ptr(), N,
+                                       float(threshold), y.data_ptr(), _dt(y), ws.data_ptr(), ws.numel(),
+                                       _stream(x)))
+    return y
+
+
+def fp8_w8a8_linear(x: torch.Tensor, wq8: torch.Tensor, sw: torch.Tensor, act_scale: torch.Tensor | None = None,
+                    out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+                    workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = X W^T with E4M3 weights and activations (see include/w8mp.h).
+    act_scale: None (dynamic per token) or a one-element fp32 GPU tensor."""
+    _dev(x, "x"), _dev(wq8, "wq8"), _dev(sw, "sw")
+    M, K = x.shape
+    N = wq8.shape[0]
+    y = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=x.device)
+    need = fp8_w8a8_linear_workspace_size(M, N, K)
+    ws = workspace if workspace is not None else _workspace(need, x.device)
+    sp = 0 if act_scale is None else _dev(act_scale, "act_scale").data_ptr()
+    _abi.check(lib().fp8_w8a8_linear(x.data_ptr(), _dt(x), M, K, wq8.data_ptr(), sw.data_ptr(), N, sp,
+                                     y.data_ptr(), _dt(y), ws.data_ptr(), ws.numel(), _stream(x)))
+    return y
+
+
+def debug_int8_quantize_activations(x: torch.Tensor, threshold: float = 6.0):
+    """(q int8 [M,K], sx fp32 [M], outlier column indices int32 [nO])."""
+    _dev(x, "x")
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    sx = torch.empty((M,), dtype=torch.float32, device=x.device)
+    idx = torch.empty((K,), dtype=torch.int32, device=x.device)
+    n = torch.empty((1,), dtype=torch.int32, device=x.device)
+    ws = _workspace(int(lib().w8dbg_int8_quantize_activations_workspace_size(M, K)), x.device)
+    _abi.check(lib().w8dbg_int8_quantize_activations(x.data_ptr(), _dt(x), M, K, float(threshold), q.data_ptr(),
+                                                     sx.data_ptr(), idx.data_ptr(), n.data_ptr(), ws.data_ptr(),
+                                                     ws.numel(), _stream(x)))
+    return q, sx, idx[: int(n.item())]
+
+
+def debug_int8_gemm_i32(q: torch.Tensor, wq: torch.Tensor) -> torch.Tensor:
+    """acc [M,N] int32 = q . wq^T on the int8 MFMA kernel."""
+    _dev(q, "q"), _dev(wq, "wq")
+    M, K = q.shape
+    N = wq.shape[0]
+    acc = torch.empty((M, N), dtype=torch.int32, device=q.device)
+    _abi.check(lib().w8dbg_int8_gemm_i32(q.data_ptr(), wq.data_ptr(), M, N, K, acc.data_ptr(), _stream(q)))
+    return acc
+
+
+def profile_start(max_calls: int) -> None:
+    """Start recording per-stage GPU times of the linear calls (HIP events)."""
+    _abi.check(lib().w8_profile_start(int(max_calls)))
+
+
+def profile_stop():
+    """Stop recording; returns (stage_ms[3], n_calls): summed milliseconds of
+    the row pass, the outlier fix-up and the GEMM over the recorded calls."""
+    import ctypes
+
+    ms = (ctypes.c_double * 3)()
+    n = ctypes.c_int()
+    _abi.check(lib().w8_profile_stop(ms, ctypes.byref(n)))
+    return [ms[0], ms[1], ms[2]], n.value
+
+
+def debug_fp8_quantize_activations(x: torch.Tensor, act_scale: torch.Tensor | None = None):
+    """(E4M3 codes uint8 [M,K], sx fp32 [M])."""
+    _dev(x, "x")
+    M, K = x.shape
+    xq = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    sx = torch.empty((M,), dtype=torch.float32, device=x.device)
+    sp = 0 if act_scale is None else _dev(act_scale, "act_scale").data_ptr()
+    _abi.check(lib().w8dbg_fp8_quantize_activations(x.data_ptr(), _dt(x), M, K, sp, xq.data_ptr(), sx.data_ptr(),
+                                                    _stream(x)))
+    return xq, sx

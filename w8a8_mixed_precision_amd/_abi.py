@@ -1,0 +1,71 @@
+"""ctypes declarations of libw8mp.so (the C ABI in include/w8mp.h).
+
+Loading fails loudly: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw8mp.so")
+
+W8_OK, W8_ERR_INVALID_ARGUMENT, W8_ERR_UNSUPPORTED, W8_ERR_WORKSPACE, W8_ERR_HIP = range(5)
+W8_DT_F16, W8_DT_BF16, W8_DT_F32 = range(3)
+W8_Q_INT8, W8_Q_FP8_E4M3 = range(2)
+W8_INT8_MAX_K = 133144
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_size = ctypes.c_size_t
+_f = ctypes.c_float
+
+# name -> (restype, argtypes)
+SIGNATURES = {
+    "quantize_weight_rowwise": (_int, [_p, _int, _i64, _i64, _int, _p, _p, _p]),
+    "int8_mixed_linear_workspace_size": (_size, [_i64, _i64, _i64]),
+    "int8_mixed_linear": (_int, [_p, _int, _i64, _i64, _p, _p, _i64, _f, _p, _int, _p, _size, _p]),
+    "fp8_w8a8_linear_workspace_size": (_size, [_i64, _i64, _i64]),
+    "fp8_w8a8_linear": (_int, [_p, _int, _i64, _i64, _p, _p, _i64, _p, _p, _int, _p, _size, _p]),
+    "w8_status_string": (ctypes.c_char_p, [_int]),
+    "w8_last_error": (ctypes.c_char_p, []),
+    "w8dbg_int8_quantize_activations_workspace_size": (_size, [_i64, _i64]),
+    "w8dbg_int8_quantize_activations": (_int, [_p, _int, _i64, _i64, _f, _p, _p, _p, _p, _p, _size, _p]),
+    "w8dbg_int8_gemm_i32": (_int, [_p, _p, _i64, _i64, _i64, _p, _p]),
+    "w8dbg_fp8_quantize_activations": (_int, [_p, _int, _i64, _i64, _p, _p, _p, _p]),
+    "w8_profile_start": (_int, [_int]),
+    "w8_profile_stop": (_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_int)]),
+}
+
+
+class W8Error(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{status_string(status)}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m w8a8_mixed_precision_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().w8_status_string(status).decode()
+
+
+def check(status: int) -> None:
+    if status != W8_OK:
+        raise W8Error(status, lib().w8_last_error().decode())

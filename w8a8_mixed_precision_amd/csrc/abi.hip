@@ -1,0 +1,343 @@
+// C ABI of libw8mp: argument validation, workspace carve-up, kernel dispatch.
+// Declarations and contracts: include/w8mp.h.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include <hip/hip_runtime.h>
+
+#include "w8mp.h"
+
+namespace w8 {
+void launch_clear(uint32_t* p, int n, hipStream_t s);
+void launch_int8_rows(const void* X, bool bf16, int64_t rows, int K, float t, int8_t* q, float* sx, int* amax_col,
+                      uint32_t* mask, bool weight, hipStream_t s);
+size_t outlier_fixup_lds_bytes(int K);
+void launch_outlier_fixup(const void* X, bool bf16, int64_t M, int K, const uint32_t* mask, int8_t* q, float* sx,
+                          const int* amax_col, int* O, int* nO, uint16_t* XO, const int8_t* Wq, int64_t N,
+                          uint16_t* WO, hipStream_t s);
+void launch_fp8_rows(const void* X, bool bf16, int64_t rows, int K, const float* act_scale, uint8_t* xq, float* sx,
+                     int mode, hipStream_t s);
+void launch_int8_gemm(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t K, const float* sx,
+                      const float* sw, const int* nO, const uint16_t* XO, const uint16_t* WO, bool xbf16, void* Y,
+                      int mode, hipStream_t s);
+void launch_fp8_gemm(const uint8_t* A, const uint8_t* B, int64_t M, int64_t N, int64_t K, const float* sx,
+                     const float* sw, void* Y, int ydt, hipStream_t s);
+}  // namespace w8
+
+namespace {
+
+thread_local std::string g_last_error;
+
+w8_status fail(w8_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+w8_status ok() {
+  g_last_error.clear();
+  return W8_OK;
+}
+
+w8_status check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(W8_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Largest dimension the kernels index with 32-bit row counters.
+constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
+
+#define W8_REQUIRE(cond, st, ...) \
+  do {                            \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+w8_status check_mk(int64_t M, int64_t K, int64_t maxK) {
+  W8_REQUIRE(M >= 1 && M <= kMaxDim, W8_ERR_INVALID_ARGUMENT, "M must be in [1, 2^31): got %lld", (long long)M);
+  W8_REQUIRE(K >= 16 && K % 16 == 0, W8_ERR_INVALID_ARGUMENT, "K must be a positive multiple of 16: got %lld",
+             (long long)K);
+  W8_REQUIRE(K <= maxK, W8_ERR_UNSUPPORTED, "K=%lld exceeds the supported maximum %lld", (long long)K,
+             (long long)maxK);
+  W8_REQUIRE(M * K < (int64_t{1} << 46), W8_ERR_UNSUPPORTED, "M*K too large");
+  return W8_OK;
+}
+
+// Workspace layout of int8_mixed_linear (offsets from the 256-aligned base).
+struct Int8Ws {
+  size_t q, sx, amax, mask, O, nO, XO, WO, total;
+};
+
+Int8Ws int8_layout(int64_t M, int64_t N, int64_t K) {
+  Int8Ws w{};
+  const size_t P = static_cast<size_t>((K + 31) / 32 * 32);  // worst case: every column is an outlier
+  size_t off = 0;
+  w.q = off;    off = up(off + static_cast<size_t>(M) * K);
+  w.sx = off;   off = up(off + 4 * static_cast<size_t>(M));
+  w.amax = off; off = up(off + 4 * static_cast<size_t>(M));
+  w.mask = off; off = up(off + 4 * static_cast<size_t>((K + 31) / 32));
+  w.nO = off;   off = up(off + 4);
+  w.O = off;    off = up(off + 4 * static_cast<size_t>(K));
+  w.XO = off;   off = up(off + 2 * static_cast<size_t>(M) * P);
+  w.WO = off;   off = up(off + 2 * static_cast<size_t>(N) * P);
+  w.total = off;
+  return w;
+}
+
+struct Fp8Ws {
+  size_t xq, sx, total;
+};
+
+Fp8Ws fp8_layout(int64_t M, int64_t K) {
+  Fp8Ws w{};
+  size_t off = 0;
+  w.xq = off; off = up(off + static_cast<size_t>(M) * K);
+  w.sx = off; off = up(off + 4 * static_cast<size_t>(M));
+  w.total = off;
+  return w;
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+w8_status check_ws(void* ws, size_t bytes, size_t need) {
+  W8_REQUIRE(ws != nullptr, W8_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  W8_REQUIRE((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) == 0, W8_ERR_WORKSPACE,
+             "workspace must be 256-byte aligned");
+  W8_REQUIRE(bytes >= need, W8_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", bytes, need);
+  return W8_OK;
+}
+
+// Measurement hook state (see w8_profile_start in w8mp.h).
+struct Profile {
+  bool on = false;
+  int cap = 0, n = 0;
+  std::vector<hipEvent_t> ev;  // 4 per call: start, after row pass, after fix-up, after GEMM
+} g_prof;
+
+// Record boundary `b` (0..3) of the current call; a no-op unless profiling.
+void mark(int b, hipStream_t s) {
+  if (!g_prof.on || g_prof.n >= g_prof.cap) return;
+  hipEventRecord(g_prof.ev[4 * g_prof.n + b], s);
+  if (b == 3) ++g_prof.n;
+}
+
+}  // namespace
+
+extern "C" {
+
+w8_status w8_profile_start(int max_calls) {
+  W8_REQUIRE(max_calls >= 1, W8_ERR_INVALID_ARGUMENT, "max_calls must be >= 1");
+  double unused[3];
+  int n;
+  if (g_prof.on) w8_profile_stop(unused, &n);
+  g_prof.ev.assign(4 * static_cast<size_t>(max_calls), nullptr);
+  for (auto& e : g_prof.ev) {
+    if (hipEventCreate(&e) != hipSuccess) return fail(W8_ERR_HIP, "hipEventCreate failed");
+  }
+  g_prof.cap = max_calls;
+  g_prof.n = 0;
+  g_prof.on = true;
+  return ok();
+}
+
+w8_status w8_profile_stop(double* stage_ms, int* n_calls) {
+  W8_REQUIRE(stage_ms && n_calls, W8_ERR_INVALID_ARGUMENT, "null pointer argument");
+  stage_ms[0] = stage_ms[1] = stage_ms[2] = 0.0;
+  *n_calls = 0;
+  if (!g_prof.on) return ok();
+  w8_status st = W8_OK;
+  for (int c = 0; c < g_prof.n; ++c) {
+    hipEvent_t* e = &g_prof.ev[4 * static_cast<size_t>(c)];
+    if (hipEventSynchronize(e[3]) != hipSuccess) st = W8_ERR_HIP;
+    for (int k = 0; k < 3; ++k) {
+      float ms = 0.0f;
+      if (hipEventElapsedTime(&ms, e[k], e[k + 1]) != hipSuccess) st = W8_ERR_HIP;
+      stage_ms[k] += ms;
+    }
+  }
+  *n_calls = g_prof.n;
+  for (auto& e : g_prof.ev)
+    if (e) hipEventDestroy(e);
+  g_prof.ev.clear();
+  g_prof.on = false;
+  g_prof.cap = g_prof.n = 0;
+  return st == W8_OK ? ok() : fail(st, "reading profile events failed");
+}
+
+const char* w8_status_string(int status) {
+  switch (status) {
+    case W8_OK: return "W8_OK";
+    case W8_ERR_INVALID_ARGUMENT: return "W8_ERR_INVALID_ARGUMENT";
+    case W8_ERR_UNSUPPORTED: return "W8_ERR_UNSUPPORTED";
+    case W8_ERR_WORKSPACE: return "W8_ERR_WORKSPACE";
+    case W8_ERR_HIP: return "W8_ERR_HIP";
+    default: return "W8_UNKNOWN_STATUS";
+  }
+}
+
+const char* w8_last_error(void) { return g_last_error.c_str(); }
+
+w8_status quantize_weight_rowwise(const void* W, int w_dt, int64_t N, int64_t K, int fmt, void* Wq, float* sw,
+                                  void* stream) {
+  W8_REQUIRE(W && Wq && sw, W8_ERR_INVALID_ARGUMENT, "null pointer argument");
+  W8_REQUIRE(w_dt == W8_DT_F16 || w_dt == W8_DT_BF16, W8_ERR_UNSUPPORTED, "weights must be f16 or bf16");
+  W8_REQUIRE(fmt == W8_Q_INT8 || fmt == W8_Q_FP8_E4M3, W8_ERR_UNSUPPORTED, "unknown weight format %d", fmt);
+  if (w8_status st = check_mk(N, K, fmt == W8_Q_INT8 ? W8_INT8_MAX_K : 65536); st != W8_OK) return st;
+  W8_REQUIRE(aligned16(W) && aligned16(Wq) && aligned16(sw), W8_ERR_INVALID_ARGUMENT,
+             "pointers must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf = w_dt == W8_DT_BF16;
+  if (fmt == W8_Q_INT8)
+    w8::launch_int8_rows(W, bf, N, (int)K, INFINITY, static_cast<int8_t*>(Wq), sw, nullptr, nullptr, true, s);
+  else
+    w8::launch_fp8_rows(W, bf, N, (int)K, nullptr, static_cast<uint8_t*>(Wq), sw, 2, s);
+  return check_launch("quantize_weight_rowwise");
+}
+
+size_t int8_mixed_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 1) return 0;
+  return int8_layout(M, N, K).total;
+}
+
+static w8_status int8_common_checks(const void* X, int x_dt, int64_t M, int64_t K, float threshold) {
+  W8_REQUIRE(X != nullptr, W8_ERR_INVALID_ARGUMENT, "X is NULL");
+  W8_REQUIRE(x_dt == W8_DT_F16 || x_dt == W8_DT_BF16, W8_ERR_UNSUPPORTED, "X must be f16 or bf16");
+  if (w8_status st = check_mk(M, K, W8_INT8_MAX_K); st != W8_OK) return st;
+  W8_REQUIRE(!std::isnan(threshold) && threshold >= 0.0f, W8_ERR_INVALID_ARGUMENT,
+             "threshold must be >= 0 (+inf allowed), got %g", (double)threshold);
+  W8_REQUIRE(aligned16(X), W8_ERR_INVALID_ARGUMENT, "X must be 16-byte aligned");
+  return W8_OK;
+}
+
+w8_status int8_mixed_linear(const void* X, int x_dt, int64_t M, int64_t K, const int8_t* Wq, const float* sw,
+                            int64_t N, float threshold, void* Y, int y_dt, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (w8_status st = int8_common_checks(X, x_dt, M, K, threshold); st != W8_OK) return st;
+  W8_REQUIRE(Wq && sw && Y, W8_ERR_INVALID_ARGUMENT, "null pointer argument");
+  W8_REQUIRE(N >= 1 && N <= kMaxDim, W8_ERR_INVALID_ARGUMENT, "N must be in [1, 2^31)");
+  W8_REQUIRE(y_dt == W8_DT_F16 || y_dt == W8_DT_F32, W8_ERR_UNSUPPORTED, "Y must be f16 or f32");
+  W8_REQUIRE(aligned16(Wq) && aligned16(sw) && aligned16(Y), W8_ERR_INVALID_ARGUMENT,
+             "pointers must be 16-byte aligned");
+  const Int8Ws L = int8_layout(M, N, K);
+  if (w8_status st = check_ws(workspace, workspace_bytes, L.total); st != W8_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf = x_dt == W8_DT_BF16;
+  int8_t* q = at<int8_t>(workspace, L.q);
+  float* sx = at<float>(workspace, L.sx);
+  int* amax = at<int>(workspace, L.amax);
+  uint32_t* mask = at<uint32_t>(workspace, L.mask);
+  int* nO = at<int>(workspace, L.nO);
+  int* O = at<int>(workspace, L.O);
+  uint16_t* XO = at<uint16_t>(workspace, L.XO);
+  uint16_t* WO = at<uint16_t>(workspace, L.WO);
+
+  mark(0, s);
+  w8::launch_clear(mask, (int)((K + 31) / 32), s);
+  w8::launch_int8_rows(X, bf, M, (int)K, threshold, q, sx, amax, mask, false, s);
+  mark(1, s);
+  w8::launch_outlier_fixup(X, bf, M, (int)K, mask, q, sx, amax, O, nO, XO, Wq, N, WO, s);
+  mark(2, s);
+  w8::launch_int8_gemm(q, Wq, M, N, K, sx, sw, nO, XO, WO, bf, Y, y_dt == W8_DT_F16 ? 1 : 2, s);
+  mark(3, s);
+  return check_launch("int8_mixed_linear");
+}
+
+size_t fp8_w8a8_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
+  (void)N;
+  if (M < 1 || K < 1) return 0;
+  return fp8_layout(M, K).total;
+}
+
+w8_status fp8_w8a8_linear(const void* X, int x_dt, int64_t M, int64_t K, const uint8_t* Wq8, const float* sw,
+                          int64_t N, const float* act_scale, void* Y, int y_dt, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  W8_REQUIRE(X && Wq8 && sw && Y, W8_ERR_INVALID_ARGUMENT, "null pointer argument");
+  W8_REQUIRE(x_dt == W8_DT_F16 || x_dt == W8_DT_BF16, W8_ERR_UNSUPPORTED, "X must be f16 or bf16");
+  W8_REQUIRE(y_dt == W8_DT_BF16 || y_dt == W8_DT_F16 || y_dt == W8_DT_F32, W8_ERR_UNSUPPORTED,
+             "Y must be bf16, f16 or f32");
+  if (w8_status st = check_mk(M, K, 65536); st != W8_OK) return st;
+  W8_REQUIRE(N >= 1 && N <= kMaxDim, W8_ERR_INVALID_ARGUMENT, "N must be in [1, 2^31)");
+  W8_REQUIRE(aligned16(X) && aligned16(Wq8) && aligned16(sw) && aligned16(Y), W8_ERR_INVALID_ARGUMENT,
+             "pointers must be 16-byte aligned");
+  const Fp8Ws L = fp8_layout(M, K);
+  if (w8_status st = check_ws(workspace, workspace_bytes, L.total); st != W8_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* xq = at<uint8_t>(workspace, L.xq);
+  float* sx = at<float>(workspace, L.sx);
+  mark(0, s);
+  w8::launch_fp8_rows(X, x_dt == W8_DT_BF16, M, (int)K, act_scale, xq, sx, act_scale ? 1 : 0, s);
+  mark(1, s);
+  mark(2, s);
+  const int ydt = y_dt == W8_DT_BF16 ? 0 : (y_dt == W8_DT_F16 ? 1 : 2);
+  w8::launch_fp8_gemm(xq, Wq8, M, N, K, sx, sw, Y, ydt, s);
+  mark(3, s);
+  return check_launch("fp8_w8a8_linear");
+}
+
+// ---- parity exports ---------------------------------------------------------
+
+size_t w8dbg_int8_quantize_activations_workspace_size(int64_t M, int64_t K) {
+  if (M < 1 || K < 1) return 0;
+  return up(4 * static_cast<size_t>(M)) + up(4 * static_cast<size_t>((K + 31) / 32));
+}
+
+w8_status w8dbg_int8_quantize_activations(const void* X, int x_dt, int64_t M, int64_t K, float threshold, int8_t* q,
+                                          float* sx, int32_t* outlier_idx, int32_t* n_outliers, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  if (w8_status st = int8_common_checks(X, x_dt, M, K, threshold); st != W8_OK) return st;
+  W8_REQUIRE(q && sx && outlier_idx && n_outliers, W8_ERR_INVALID_ARGUMENT, "null pointer argument");
+  W8_REQUIRE(aligned16(q) && aligned16(sx), W8_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+  const size_t need = w8dbg_int8_quantize_activations_workspace_size(M, K);
+  if (w8_status st = check_ws(workspace, workspace_bytes, need); st != W8_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf = x_dt == W8_DT_BF16;
+  int* amax = at<int>(workspace, 0);
+  uint32_t* mask = at<uint32_t>(workspace, up(4 * static_cast<size_t>(M)));
+  w8::launch_clear(mask, (int)((K + 31) / 32), s);
+  w8::launch_int8_rows(X, bf, M, (int)K, threshold, q, sx, amax, mask, false, s);
+  w8::launch_outlier_fixup(X, bf, M, (int)K, mask, q, sx, amax, outlier_idx, n_outliers, nullptr, nullptr, 0,
+                           nullptr, s);
+  return check_launch("w8dbg_int8_quantize_activations");
+}
+
+w8_status w8dbg_int8_gemm_i32(const int8_t* q, const int8_t* Wq, int64_t M, int64_t N, int64_t K, int32_t* acc,
+                              void* stream) {
+  W8_REQUIRE(q && Wq && acc, W8_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (w8_status st = check_mk(M, K, W8_INT8_MAX_K); st != W8_OK) return st;
+  W8_REQUIRE(N >= 1 && N <= kMaxDim, W8_ERR_INVALID_ARGUMENT, "N must be in [1, 2^31)");
+  W8_REQUIRE(aligned16(q) && aligned16(Wq) && aligned16(acc), W8_ERR_INVALID_ARGUMENT,
+             "pointers must be 16-byte aligned");
+  w8::launch_int8_gemm(q, Wq, M, N, K, nullptr, nullptr, nullptr, nullptr, nullptr, true, acc, 0,
+                       static_cast<hipStream_t>(stream));
+  return check_launch("w8dbg_int8_gemm_i32");
+}
+
+w8_status w8dbg_fp8_quantize_activations(const void* X, int x_dt, int64_t M, int64_t K, const float* act_scale,
+                                         uint8_t* xq, float* sx, void* stream) {
+  W8_REQUIRE(X && xq && sx, W8_ERR_INVALID_ARGUMENT, "null pointer argument");
+  W8_REQUIRE(x_dt == W8_DT_F16 || x_dt == W8_DT_BF16, W8_ERR_UNSUPPORTED, "X must be f16 or bf16");
+  if (w8_status st = check_mk(M, K, 65536); st != W8_OK) return st;
+  W8_REQUIRE(aligned16(X) && aligned16(xq) && aligned16(sx), W8_ERR_INVALID_ARGUMENT,
+             "pointers must be 16-byte aligned");
+  w8::launch_fp8_rows(X, x_dt == W8_DT_BF16, M, (int)K, act_scale, xq, sx, act_scale ? 1 : 0,
+                      static_cast<hipStream_t>(stream));
+  return check_launch("w8dbg_fp8_quantize_activations");
+}
+
+}  // extern "C"
