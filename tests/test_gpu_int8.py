@@ -50,6 +50,7 @@ def _cases():
                               name="ragged_f16_rows")
     yield synth.random_linear(513, 1040, 777, seed=33, x_dtype="bf16", outlier_cols=40, name="many_outliers")
     yield synth.random_linear(70, 16, 33, seed=34, x_dtype="bf16", outlier_cols=0, name="k16_no_outliers")
+    yield synth.random_linear(333, 640, 300, seed=35, x_dtype="bf16", outlier_cols=3, name="ragged_mn_k64")
 
 
 CASES = list(_cases())
@@ -111,6 +112,26 @@ def test_activation_quantisation_long_rows(K):
     assert np.array_equal(q.cpu().numpy(), q_ref)
 
 
+def test_outlier_set_larger_than_the_lds_list():
+    """t = 0 makes every non-zero column an outlier: 8192 of them, more than
+    the fix-up kernel lists in LDS, so its per-row fallback runs."""
+    c = synth.random_linear(40, 8192, 24, seed=45, x_dtype="bf16")
+    x = c.x_bits.copy()
+    x[:, 77] = 0                                   # one all-zero column stays int8
+    xf = o.decode16(x, "bf16")
+    O_ref, sx_ref, q_ref = o.quantize_activations_int8(xf, 0.0)
+    assert O_ref.size == 8191
+    announce("int8 act quant unlisted outliers")
+    q, sx, O = w8.debug_int8_quantize_activations(dev16(x, "bf16"), 0.0)
+    assert np.array_equal(O.cpu().numpy(), O_ref)
+    assert np.array_equal(sx.cpu().numpy(), sx_ref) and np.array_equal(q.cpu().numpy(), q_ref)
+    wq, sw, wq_ref, sw_ref = _quant_weights_both(c)
+    ref = o.int8_mixed_linear(x, "bf16", wq_ref, sw_ref, 0.0, "f32")
+    y = w8.int8_mixed_linear(dev16(x, "bf16"), wq, sw, 0.0, torch.float32)
+    torch.cuda.synchronize()
+    _check_outputs(y, ref["Y"], "f32", "unlisted")
+
+
 def test_every_bf16_value_encodes_like_the_oracle():
     """All finite bf16 patterns, 256 per row, each row with its own scale."""
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
@@ -127,7 +148,8 @@ def test_every_bf16_value_encodes_like_the_oracle():
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 520, 272), (257, 130, 48), (600, 700, 320), (64, 512, 256), (1, 1, 16),
-                                   (256, 256, 16384)])
+                                   (256, 256, 16384), (300, 200, 64), (77, 300, 128), (256, 512, 192),
+                                   (520, 260, 320)])
 def test_int8_gemm_accumulators_bit_exact(M, N, K):
     rng = np.random.default_rng(M * 7 + N * 3 + K)
     q = rng.integers(-127, 128, size=(M, K)).astype(np.int8)

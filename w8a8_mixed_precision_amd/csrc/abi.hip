@@ -13,9 +13,9 @@
 namespace w8 {
 void launch_clear(uint32_t* p, int n, hipStream_t s);
 void launch_int8_rows(const void* X, bool bf16, int64_t rows, int K, float t, int8_t* q, float* sx, int* amax_col,
-                      uint32_t* mask, bool weight, hipStream_t s);
+                      uint8_t* colflag, bool weight, hipStream_t s);
 size_t outlier_fixup_lds_bytes(int K);
-void launch_outlier_fixup(const void* X, bool bf16, int64_t M, int K, const uint32_t* mask, int8_t* q, float* sx,
+void launch_outlier_fixup(const void* X, bool bf16, int64_t M, int K, const uint8_t* colflag, int8_t* q, float* sx,
                           const int* amax_col, int* O, int* nO, uint16_t* XO, const int8_t* Wq, int64_t N,
                           uint16_t* WO, hipStream_t s);
 void launch_fp8_rows(const void* X, bool bf16, int64_t rows, int K, const float* act_scale, uint8_t* xq, float* sx,
@@ -77,7 +77,7 @@ w8_status check_mk(int64_t M, int64_t K, int64_t maxK) {
 
 // Workspace layout of int8_mixed_linear (offsets from the 256-aligned base).
 struct Int8Ws {
-  size_t q, sx, amax, mask, O, nO, XO, WO, total;
+  size_t q, sx, amax, flags, O, nO, XO, WO, total;
 };
 
 Int8Ws int8_layout(int64_t M, int64_t N, int64_t K) {
@@ -87,7 +87,7 @@ Int8Ws int8_layout(int64_t M, int64_t N, int64_t K) {
   w.q = off;    off = up(off + static_cast<size_t>(M) * K);
   w.sx = off;   off = up(off + 4 * static_cast<size_t>(M));
   w.amax = off; off = up(off + 4 * static_cast<size_t>(M));
-  w.mask = off; off = up(off + 4 * static_cast<size_t>((K + 31) / 32));
+  w.flags = off; off = up(off + static_cast<size_t>(K));
   w.nO = off;   off = up(off + 4);
   w.O = off;    off = up(off + 4 * static_cast<size_t>(K));
   w.XO = off;   off = up(off + 2 * static_cast<size_t>(M) * P);
@@ -241,17 +241,17 @@ w8_status int8_mixed_linear(const void* X, int x_dt, int64_t M, int64_t K, const
   int8_t* q = at<int8_t>(workspace, L.q);
   float* sx = at<float>(workspace, L.sx);
   int* amax = at<int>(workspace, L.amax);
-  uint32_t* mask = at<uint32_t>(workspace, L.mask);
+  uint8_t* flags = at<uint8_t>(workspace, L.flags);
   int* nO = at<int>(workspace, L.nO);
   int* O = at<int>(workspace, L.O);
   uint16_t* XO = at<uint16_t>(workspace, L.XO);
   uint16_t* WO = at<uint16_t>(workspace, L.WO);
 
   mark(0, s);
-  w8::launch_clear(mask, (int)((K + 31) / 32), s);
-  w8::launch_int8_rows(X, bf, M, (int)K, threshold, q, sx, amax, mask, false, s);
+  w8::launch_clear(reinterpret_cast<uint32_t*>(flags), (int)(K / 4), s);
+  w8::launch_int8_rows(X, bf, M, (int)K, threshold, q, sx, amax, flags, false, s);
   mark(1, s);
-  w8::launch_outlier_fixup(X, bf, M, (int)K, mask, q, sx, amax, O, nO, XO, Wq, N, WO, s);
+  w8::launch_outlier_fixup(X, bf, M, (int)K, flags, q, sx, amax, O, nO, XO, Wq, N, WO, s);
   mark(2, s);
   w8::launch_int8_gemm(q, Wq, M, N, K, sx, sw, nO, XO, WO, bf, Y, y_dt == W8_DT_F16 ? 1 : 2, s);
   mark(3, s);
@@ -294,7 +294,7 @@ w8_status fp8_w8a8_linear(const void* X, int x_dt, int64_t M, int64_t K, const u
 
 size_t w8dbg_int8_quantize_activations_workspace_size(int64_t M, int64_t K) {
   if (M < 1 || K < 1) return 0;
-  return up(4 * static_cast<size_t>(M)) + up(4 * static_cast<size_t>((K + 31) / 32));
+  return up(4 * static_cast<size_t>(M)) + up(static_cast<size_t>(K));
 }
 
 w8_status w8dbg_int8_quantize_activations(const void* X, int x_dt, int64_t M, int64_t K, float threshold, int8_t* q,
@@ -308,10 +308,10 @@ w8_status w8dbg_int8_quantize_activations(const void* X, int x_dt, int64_t M, in
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = x_dt == W8_DT_BF16;
   int* amax = at<int>(workspace, 0);
-  uint32_t* mask = at<uint32_t>(workspace, up(4 * static_cast<size_t>(M)));
-  w8::launch_clear(mask, (int)((K + 31) / 32), s);
-  w8::launch_int8_rows(X, bf, M, (int)K, threshold, q, sx, amax, mask, false, s);
-  w8::launch_outlier_fixup(X, bf, M, (int)K, mask, q, sx, amax, outlier_idx, n_outliers, nullptr, nullptr, 0,
+  uint8_t* flags = at<uint8_t>(workspace, up(4 * static_cast<size_t>(M)));
+  w8::launch_clear(reinterpret_cast<uint32_t*>(flags), (int)(K / 4), s);
+  w8::launch_int8_rows(X, bf, M, (int)K, threshold, q, sx, amax, flags, false, s);
+  w8::launch_outlier_fixup(X, bf, M, (int)K, flags, q, sx, amax, outlier_idx, n_outliers, nullptr, nullptr, 0,
                            nullptr, s);
   return check_launch("w8dbg_int8_quantize_activations");
 }

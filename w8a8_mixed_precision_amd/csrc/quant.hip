@@ -1,8 +1,8 @@
 // Row quantisation kernels of libw8mp (gfx950).
 //
-//  k_clear            zero the outlier-column bit mask (and the outlier count)
+//  k_clear            zero the outlier-column flags
 //  k_int8_rows        one pass over a row: absmax over the elements with
-//                     |x| <= t and its column, outlier-column bits (|x| > t),
+//                     |x| <= t and its column, outlier-column flags (|x| > t),
 //                     int8 codes with that provisional scale. With t = +inf it
 //                     is the rowwise weight quantiser.
 //  k_outlier_fixup    outlier list, zero codes in outlier columns, gather the
@@ -28,40 +28,68 @@ __global__ void k_clear(uint32_t* __restrict__ p, int n) {
 }
 
 // --------------------------------------------------------------------------
-// One 256-thread block per row. A thread owns 16-byte chunks c = tid + 256*i.
-// CPT > 0: the row stays in registers (K <= 2048*CPT); CPT == 0: two passes.
-template <bool BF16, int CPT, bool WEIGHT>
-__global__ __launch_bounds__(256) void k_int8_rows(const uint16_t* __restrict__ X, int K, float t,
+// Row pass, register-resident form: W waves per row (W = 1, 2, 4), each wave
+// covering a 4096-element slice, 8 chunks of 8 elements per lane; a block of
+// 256 threads therefore holds 4/W rows. With W == 1 the row reduction stays
+// inside one wave (no LDS, no barrier).
+//
+// Outlier columns are flagged with a plain byte store of 1 into colflag[k]
+// (cleared before the pass): many rows flag the same few columns, and equal
+// plain stores need no read-modify-write.
+template <bool BF16, int W, bool WEIGHT>
+__global__ __launch_bounds__(256) void k_int8_rows(const uint16_t* __restrict__ X, int64_t rows, int K, float t,
                                                    int8_t* __restrict__ q, float* __restrict__ sx,
-                                                   int* __restrict__ amax_col,
-                                                   uint32_t* __restrict__ mask) {
+                                                   int* __restrict__ amax_col, uint8_t* __restrict__ colflag) {
+  constexpr int kRows = 4 / W;
   __shared__ MaxLoc red[4];
-  const int64_t row = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRows + wave / W;
+  const bool valid = row < rows;
+  const int part = wave % W;
   const int nch = K >> 3;
-  const uint4* xr = reinterpret_cast<const uint4*>(X + row * K);
-  uint2* qr = reinterpret_cast<uint2*>(q + row * K);
-  const int tid = threadIdx.x;
+  const uint4* xr = reinterpret_cast<const uint4*>(X + (valid ? row : 0) * K);
+  uint2* qr = reinterpret_cast<uint2*>(q + (valid ? row : 0) * K);
 
+  uint4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = part * 512 + lane + 64 * i;
+    if (valid && c < nch) v[i] = xr[c];
+  }
   MaxLoc best{0.0f, -1};
-  auto scan_chunk = [&](const uint4& v, int c) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = part * 512 + lane + 64 * i;
+    if (!(valid && c < nch)) continue;
     float f[8];
-    unpack8<BF16>(v, f);
-    uint32_t obits = 0;
+    unpack8<BF16>(v[i], f);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float a = fabsf(f[j]);
       if (a > t) {
-        obits |= 1u << j;
+        if (!WEIGHT) colflag[8 * c + j] = 1;
       } else if (a > best.v) {
         best.v = a;
         best.k = 8 * c + j;
       }
     }
-    if (!WEIGHT && obits) atomicOr(&mask[c >> 2], obits << ((c & 3) * 8));
-  };
-  auto code_chunk = [&](const uint4& v, int c, float r) {
+  }
+  best = wave_maxloc(best);
+  if constexpr (W > 1) {
+    if (lane == 0) red[wave] = best;
+    __syncthreads();
+    const int w0 = (wave / W) * W;
+    best = red[w0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) best = maxloc_pick(best, red[w0 + w]);
+  }
+  const float r = 127.0f / best.v;  // IEEE division; +inf for an all-zero row
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = part * 512 + lane + 64 * i;
+    if (!(valid && c < nch)) continue;
     float f[8];
-    unpack8<BF16>(v, f);
+    unpack8<BF16>(v[i], f);
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -71,71 +99,115 @@ __global__ __launch_bounds__(256) void k_int8_rows(const uint16_t* __restrict__ 
       else hi |= b << (8 * (j - 4));
     }
     qr[c] = make_uint2(lo, hi);
-  };
+  }
+  if (valid && part == 0 && lane == 0) {
+    sx[row] = best.v;
+    if (!WEIGHT) amax_col[row] = best.k;
+  }
+}
 
-  if constexpr (CPT > 0) {
-    uint4 v[CPT];
+// Row pass, streaming form for K > 16384: one block per row, two passes.
+template <bool BF16, bool WEIGHT>
+__global__ __launch_bounds__(256) void k_int8_rows_long(const uint16_t* __restrict__ X, int K, float t,
+                                                        int8_t* __restrict__ q, float* __restrict__ sx,
+                                                        int* __restrict__ amax_col, uint8_t* __restrict__ colflag) {
+  __shared__ MaxLoc red[4];
+  const int64_t row = blockIdx.x;
+  const int nch = K >> 3;
+  const uint4* xr = reinterpret_cast<const uint4*>(X + row * K);
+  uint2* qr = reinterpret_cast<uint2*>(q + row * K);
+  MaxLoc best{0.0f, -1};
+#pragma unroll 4
+  for (int c = threadIdx.x; c < nch; c += 256) {
+    float f[8];
+    unpack8<BF16>(xr[c], f);
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + 256 * i;
-      if (c < nch) v[i] = xr[c];
+    for (int j = 0; j < 8; ++j) {
+      const float a = fabsf(f[j]);
+      if (a > t) {
+        if (!WEIGHT) colflag[8 * c + j] = 1;
+      } else if (a > best.v) {
+        best.v = a;
+        best.k = 8 * c + j;
+      }
     }
+  }
+  const MaxLoc b = block_maxloc256(best, red);
+  const float r = 127.0f / b.v;
+#pragma unroll 4
+  for (int c = threadIdx.x; c < nch; c += 256) {
+    float f[8];
+    unpack8<BF16>(xr[c], f);
+    uint32_t lo = 0, hi = 0;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + 256 * i;
-      if (c < nch) scan_chunk(v[i], c);
+    for (int j = 0; j < 8; ++j) {
+      const int code = (fabsf(f[j]) > t) ? 0 : absmax_code(f[j], r);
+      const uint32_t bb = static_cast<uint32_t>(code) & 0xFFu;
+      if (j < 4) lo |= bb << (8 * j);
+      else hi |= bb << (8 * (j - 4));
     }
-    const MaxLoc b = block_maxloc256(best, red);
-    const float r = 127.0f / b.v;  // IEEE division; +inf for an all-zero row
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + 256 * i;
-      if (c < nch) code_chunk(v[i], c, r);
-    }
-    if (tid == 0) {
-      sx[row] = b.v;
-      if (!WEIGHT) amax_col[row] = b.k;
-    }
-  } else {
-    for (int c = tid; c < nch; c += 256) scan_chunk(xr[c], c);
-    const MaxLoc b = block_maxloc256(best, red);
-    const float r = 127.0f / b.v;
-    for (int c = tid; c < nch; c += 256) code_chunk(xr[c], c, r);
-    if (tid == 0) {
-      sx[row] = b.v;
-      if (!WEIGHT) amax_col[row] = b.k;
-    }
+    qr[c] = make_uint2(lo, hi);
+  }
+  if (threadIdx.x == 0) {
+    sx[row] = b.v;
+    if (!WEIGHT) amax_col[row] = b.k;
   }
 }
 
 // --------------------------------------------------------------------------
-// Block roles: blocks [0, xblocks) take ROWS rows of X each; the rest take ROWS
-// rows of Wq each (only when WO != nullptr). Dynamic LDS: mask words and their
-// exclusive popcount prefix (2 * nwords ints).
-constexpr int kFixRows = 16;
+// Block roles: blocks [0, xblocks) take kFixRows rows of X each; the rest take
+// kFixRows rows of Wq each (only when WO != nullptr). Every block rebuilds the
+// ascending outlier list from the mask in LDS (prefix of popcounts), then
+// spreads (row, outlier slot) pairs over all threads, so the scattered loads
+// of a block are all in flight together. Dynamic LDS: mask words, their
+// exclusive popcount prefix, and the outlier list (up to kOcap entries; a
+// larger set takes the per-row loop at the end).
+constexpr int kFixRows = 64;
+constexpr int kOcap = 4096;
+
+size_t outlier_fixup_lds_bytes(int K) {
+  return static_cast<size_t>(2) * ((K + 31) / 32) * 4 + static_cast<size_t>(kOcap) * 4;
+}
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_outlier_fixup(
-    const uint16_t* __restrict__ X, int M, int K, const uint32_t* __restrict__ mask,
+    const uint16_t* __restrict__ X, int M, int K, const uint8_t* __restrict__ colflag,
     int8_t* __restrict__ q, float* __restrict__ sx, const int* __restrict__ amax_col,
     int* __restrict__ O, int* __restrict__ nO_out, uint16_t* __restrict__ XO,
     const int8_t* __restrict__ Wq, int N, uint16_t* __restrict__ WO, int xblocks) {
   extern __shared__ uint32_t smem[];
   __shared__ int scan_tot[4];
   __shared__ float fred[4];
+  __shared__ int sredo[kFixRows];
   const int nwords = (K + 31) >> 5;
   uint32_t* smask = smem;
   int* spre = reinterpret_cast<int*>(smem + nwords);
+  int* sO = reinterpret_cast<int*>(smem + 2 * nwords);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
 
-  // mask -> LDS, exclusive prefix of popcounts (block scan in 256-word tiles)
+  // column flags -> bit mask in LDS, exclusive prefix of popcounts
+  // (block scan in 256-word tiles)
   int carry = 0;
   for (int base = 0; base < nwords; base += 256) {
     const int w = base + tid;
-    const uint32_t bits = (w < nwords) ? mask[w] : 0u;
+    uint32_t bits = 0u;
+    if (w < nwords) {
+      const uint4* fp = reinterpret_cast<const uint4*>(colflag + 32 * w);  // K % 32 == 0 region
+      const int avail = min(32, K - 32 * w);
+      if (avail == 32) {
+        const uint4 a = fp[0], b = fp[1];
+        const uint32_t wd[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bits |= ((wd[i] >> (8 * j)) & 1u) << (4 * i + j);
+      } else {
+        for (int j = 0; j < avail; ++j) bits |= static_cast<uint32_t>(colflag[32 * w + j] & 1u) << j;
+      }
+    }
     if (w < nwords) smask[w] = bits;
-    int v = __popc(bits);
+    const int v = __popc(bits);
     int incl = v;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -152,82 +224,129 @@ __global__ __launch_bounds__(256) void k_outlier_fixup(
   }
   const int nO = carry;
   const int P = (nO + 31) & ~31;
+  const bool listed = nO <= kOcap;
 
-  if (blockIdx.x == 0) {
-    for (int w = tid; w < nwords; w += 256) {
-      uint32_t bits = smask[w];
-      int j = spre[w];
-      while (bits) {
-        const int b = __ffs(bits) - 1;
-        bits &= bits - 1;
-        if (O) O[j] = 32 * w + b;
-        ++j;
-      }
+  // ascending outlier list: in LDS for this block, in global memory from block 0
+  for (int w = tid; w < nwords; w += 256) {
+    uint32_t bits = smask[w];
+    int j = spre[w];
+    while (bits) {
+      const int b = __ffs(bits) - 1;
+      bits &= bits - 1;
+      if (listed) sO[j] = 32 * w + b;
+      if (blockIdx.x == 0 && O) O[j] = 32 * w + b;
+      ++j;
     }
-    if (tid == 0) *nO_out = nO;
   }
+  if (blockIdx.x == 0 && tid == 0) *nO_out = nO;
   if (nO == 0) return;
+  __syncthreads();
 
   if (static_cast<int>(blockIdx.x) < xblocks) {
     const int r0 = blockIdx.x * kFixRows;
-    for (int m = r0; m < min(r0 + kFixRows, M); ++m) {
-      const int64_t rowoff = static_cast<int64_t>(m) * K;
-      const int c = amax_col[m];
-      const bool redo = (c >= 0) && ((smask[c >> 5] >> (c & 31)) & 1u);
-      if (redo) {
-        // The provisional absmax sat in an outlier column: recompute the
-        // scale over the non-outlier columns and re-encode the whole row.
-        float best = 0.0f;
-        for (int k = tid; k < K; k += 256) {
-          if (!((smask[k >> 5] >> (k & 31)) & 1u)) best = fmaxf(best, fabsf(to_f32<BF16>(X[rowoff + k])));
+    const int rows = min(kFixRows, M - r0);
+    if (tid < rows) {
+      const int c = amax_col[r0 + tid];
+      sredo[tid] = (c >= 0) && ((smask[c >> 5] >> (c & 31)) & 1u);
+    }
+    if (listed) {
+      // zero the codes of the outlier columns and gather X's outlier columns
+#pragma unroll 8
+      for (int idx = tid; idx < rows * P; idx += 256) {
+        const int r = idx / P, j = idx - r * P;
+        const int64_t m = r0 + r;
+        uint16_t v = 0;
+        if (j < nO) {
+          const int k = sO[j];
+          v = X[m * K + k];
+          q[m * K + k] = 0;
         }
-        best = block_max256(best, fred);
-        const float r = 127.0f / best;
-        for (int k = tid; k < K; k += 256) {
-          const bool out = (smask[k >> 5] >> (k & 31)) & 1u;
-          q[rowoff + k] = out ? 0 : static_cast<int8_t>(absmax_code(to_f32<BF16>(X[rowoff + k]), r));
-        }
-        if (tid == 0) sx[m] = best;
-      } else {
-        for (int w = tid; w < nwords; w += 256) {
-          uint32_t bits = smask[w];
-          while (bits) {
-            const int b = __ffs(bits) - 1;
-            bits &= bits - 1;
-            q[rowoff + 32 * w + b] = 0;
-          }
-        }
+        if (XO) XO[m * P + j] = v;
       }
-      if (XO) {
-        uint16_t* xo = XO + static_cast<int64_t>(m) * P;
+    } else {
+      for (int r = 0; r < rows; ++r) {
+        const int64_t m = r0 + r;
         for (int w = tid; w < nwords; w += 256) {
           uint32_t bits = smask[w];
           int j = spre[w];
           while (bits) {
             const int b = __ffs(bits) - 1;
             bits &= bits - 1;
-            xo[j++] = X[rowoff + 32 * w + b];
+            q[m * K + 32 * w + b] = 0;
+            if (XO) XO[m * P + j] = X[m * K + 32 * w + b];
+            ++j;
           }
         }
-        for (int j = nO + tid; j < P; j += 256) xo[j] = 0;
+        if (XO)
+          for (int j = nO + tid; j < P; j += 256) XO[m * P + j] = 0;
       }
+    }
+    __syncthreads();
+    // Rows whose provisional absmax sat in an outlier column: recompute the
+    // scale over the non-outlier columns and re-encode the whole row.
+    for (int r = 0; r < rows; ++r) {
+      if (!sredo[r]) continue;
+      const int64_t rowoff = static_cast<int64_t>(r0 + r) * K;
+      const uint4* xr = reinterpret_cast<const uint4*>(X + rowoff);
+      uint2* qr = reinterpret_cast<uint2*>(q + rowoff);
+      const int nch = K >> 3;
+      float best = 0.0f;
+#pragma unroll 8
+      for (int c = tid; c < nch; c += 256) {
+        float f[8];
+        unpack8<BF16>(xr[c], f);
+        const uint32_t ob = (smask[c >> 2] >> ((c & 3) * 8)) & 0xFFu;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (!((ob >> j) & 1u)) best = fmaxf(best, fabsf(f[j]));
+      }
+      best = block_max256(best, fred);
+      const float rr = 127.0f / best;
+#pragma unroll 8
+      for (int c = tid; c < nch; c += 256) {
+        float f[8];
+        unpack8<BF16>(xr[c], f);
+        const uint32_t ob = (smask[c >> 2] >> ((c & 3) * 8)) & 0xFFu;
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int code = ((ob >> j) & 1u) ? 0 : absmax_code(f[j], rr);
+          const uint32_t bb = static_cast<uint32_t>(code) & 0xFFu;
+          if (j < 4) lo |= bb << (8 * j);
+          else hi |= bb << (8 * (j - 4));
+        }
+        qr[c] = make_uint2(lo, hi);
+      }
+      if (tid == 0) sx[r0 + r] = best;
     }
   } else if (WO) {
     const int r0 = (blockIdx.x - xblocks) * kFixRows;
-    for (int n = r0; n < min(r0 + kFixRows, N); ++n) {
-      const int8_t* wr = Wq + static_cast<int64_t>(n) * K;
-      uint16_t* wo = WO + static_cast<int64_t>(n) * P;
-      for (int w = tid; w < nwords; w += 256) {
-        uint32_t bits = smask[w];
-        int j = spre[w];
-        while (bits) {
-          const int b = __ffs(bits) - 1;
-          bits &= bits - 1;
-          const float v = static_cast<float>(wr[32 * w + b]);  // |v| <= 127: exact in 16 bits
-          wo[j++] = BF16 ? static_cast<uint16_t>(__float_as_uint(v) >> 16) : f32_to_f16_bits(v);
-        }
+    const int rows = min(kFixRows, N - r0);
+    auto cvt = [](int8_t v) -> uint16_t {
+      const float f = static_cast<float>(v);  // |v| <= 127: exact in both 16-bit types
+      return BF16 ? static_cast<uint16_t>(__float_as_uint(f) >> 16) : f32_to_f16_bits(f);
+    };
+    if (listed) {
+#pragma unroll 8
+      for (int idx = tid; idx < rows * P; idx += 256) {
+        const int r = idx / P, j = idx - r * P;
+        const int64_t n = r0 + r;
+        WO[n * P + j] = (j < nO) ? cvt(Wq[n * K + sO[j]]) : uint16_t(0);
       }
-      for (int j = nO + tid; j < P; j += 256) wo[j] = 0;
+    } else {
+      for (int r = 0; r < rows; ++r) {
+        const int64_t n = r0 + r;
+        for (int w = tid; w < nwords; w += 256) {
+          uint32_t bits = smask[w];
+          int j = spre[w];
+          while (bits) {
+            const int b = __ffs(bits) - 1;
+            bits &= bits - 1;
+            WO[n * P + j++] = cvt(Wq[n * K + 32 * w + b]);
+          }
+        }
+        for (int j = nO + tid; j < P; j += 256) WO[n * P + j] = 0;
+      }
     }
   }
 }
@@ -316,19 +435,18 @@ __global__ __launch_bounds__(256) void k_fp8_rows(const uint16_t* __restrict__ X
 
 template <bool BF16, bool WEIGHT>
 static void launch_int8_rows_t(const uint16_t* X, int64_t rows, int K, float t, int8_t* q, float* sx,
-                               int* amax_col, uint32_t* mask, hipStream_t s) {
-  const int nch = K >> 3;
-  const dim3 grid(static_cast<unsigned>(rows)), block(256);
-  if (nch <= 256)
-    k_int8_rows<BF16, 1, WEIGHT><<<grid, block, 0, s>>>(X, K, t, q, sx, amax_col, mask);
-  else if (nch <= 512)
-    k_int8_rows<BF16, 2, WEIGHT><<<grid, block, 0, s>>>(X, K, t, q, sx, amax_col, mask);
-  else if (nch <= 1024)
-    k_int8_rows<BF16, 4, WEIGHT><<<grid, block, 0, s>>>(X, K, t, q, sx, amax_col, mask);
-  else if (nch <= 2048)
-    k_int8_rows<BF16, 8, WEIGHT><<<grid, block, 0, s>>>(X, K, t, q, sx, amax_col, mask);
+                               int* amax_col, uint8_t* colflag, hipStream_t s) {
+  const dim3 block(256);
+  auto blocks = [&](int rpb) { return dim3(static_cast<unsigned>((rows + rpb - 1) / rpb)); };
+  if (K <= 4096)
+    k_int8_rows<BF16, 1, WEIGHT><<<blocks(4), block, 0, s>>>(X, rows, K, t, q, sx, amax_col, colflag);
+  else if (K <= 8192)
+    k_int8_rows<BF16, 2, WEIGHT><<<blocks(2), block, 0, s>>>(X, rows, K, t, q, sx, amax_col, colflag);
+  else if (K <= 16384)
+    k_int8_rows<BF16, 4, WEIGHT><<<blocks(1), block, 0, s>>>(X, rows, K, t, q, sx, amax_col, colflag);
   else
-    k_int8_rows<BF16, 0, WEIGHT><<<grid, block, 0, s>>>(X, K, t, q, sx, amax_col, mask);
+    k_int8_rows_long<BF16, WEIGHT><<<dim3(static_cast<unsigned>(rows)), block, 0, s>>>(X, K, t, q, sx, amax_col,
+                                                                                       colflag);
 }
 
 void launch_clear(uint32_t* p, int n, hipStream_t s) {
@@ -337,20 +455,18 @@ void launch_clear(uint32_t* p, int n, hipStream_t s) {
 }
 
 void launch_int8_rows(const void* X, bool bf16, int64_t rows, int K, float t, int8_t* q, float* sx,
-                      int* amax_col, uint32_t* mask, bool weight, hipStream_t s) {
+                      int* amax_col, uint8_t* colflag, bool weight, hipStream_t s) {
   const uint16_t* x = static_cast<const uint16_t*>(X);
   if (bf16) {
-    if (weight) launch_int8_rows_t<true, true>(x, rows, K, t, q, sx, amax_col, mask, s);
-    else launch_int8_rows_t<true, false>(x, rows, K, t, q, sx, amax_col, mask, s);
+    if (weight) launch_int8_rows_t<true, true>(x, rows, K, t, q, sx, amax_col, colflag, s);
+    else launch_int8_rows_t<true, false>(x, rows, K, t, q, sx, amax_col, colflag, s);
   } else {
-    if (weight) launch_int8_rows_t<false, true>(x, rows, K, t, q, sx, amax_col, mask, s);
-    else launch_int8_rows_t<false, false>(x, rows, K, t, q, sx, amax_col, mask, s);
+    if (weight) launch_int8_rows_t<false, true>(x, rows, K, t, q, sx, amax_col, colflag, s);
+    else launch_int8_rows_t<false, false>(x, rows, K, t, q, sx, amax_col, colflag, s);
   }
 }
 
-size_t outlier_fixup_lds_bytes(int K) { return static_cast<size_t>(2) * ((K + 31) / 32) * 4; }
-
-void launch_outlier_fixup(const void* X, bool bf16, int64_t M, int K, const uint32_t* mask, int8_t* q,
+void launch_outlier_fixup(const void* X, bool bf16, int64_t M, int K, const uint8_t* colflag, int8_t* q,
                           float* sx, const int* amax_col, int* O, int* nO, uint16_t* XO,
                           const int8_t* Wq, int64_t N, uint16_t* WO, hipStream_t s) {
   const int xblocks = static_cast<int>((M + kFixRows - 1) / kFixRows);
@@ -359,10 +475,10 @@ void launch_outlier_fixup(const void* X, bool bf16, int64_t M, int K, const uint
   const uint16_t* x = static_cast<const uint16_t*>(X);
   const dim3 grid(xblocks + wblocks), block(256);
   if (bf16)
-    k_outlier_fixup<true><<<grid, block, lds, s>>>(x, (int)M, K, mask, q, sx, amax_col, O, nO, XO, Wq,
+    k_outlier_fixup<true><<<grid, block, lds, s>>>(x, (int)M, K, colflag, q, sx, amax_col, O, nO, XO, Wq,
                                                    (int)N, WO, xblocks);
   else
-    k_outlier_fixup<false><<<grid, block, lds, s>>>(x, (int)M, K, mask, q, sx, amax_col, O, nO, XO, Wq,
+    k_outlier_fixup<false><<<grid, block, lds, s>>>(x, (int)M, K, colflag, q, sx, amax_col, O, nO, XO, Wq,
                                                     (int)N, WO, xblocks);
 }
 
