@@ -92,6 +92,9 @@ w8_status quantize_weight_rowwise(const void* W, int w_dt, int64_t N, int64_t K,
  *   Y          [M,N] f16 or f32 (y_dt), device, written in full.
  *   workspace  device scratch of at least int8_mixed_linear_workspace_size()
  *              bytes, 256-byte aligned; contents undefined after the call.
+ *              The size depends on the compute-unit count of the device that
+ *              is current when it is queried (the GEMM grid is planned per
+ *              device); query and call on the same device.
  *
  * What is computed (O = outlier columns, ascending):
  *   sx[m]   = max_{k not in O} |X[m,k]|                     (fp32, exact)
@@ -151,9 +154,13 @@ w8_status w8dbg_int8_quantize_activations(const void* X, int x_dt, int64_t M, in
                                           int32_t* outlier_idx, int32_t* n_outliers,
                                           void* workspace, size_t workspace_bytes, void* stream);
 
-/* The int8 MFMA contraction alone: acc [M,N] int32 = q [M,K] . Wq [N,K]^T. */
+/* The int8 MFMA contraction alone: acc [M,N] int32 = q [M,K] . Wq [N,K]^T,
+ * with the same grid plan (including the K-split of the last wave of tiles)
+ * as int8_mixed_linear. Workspace: w8dbg_int8_gemm_i32_workspace_size(M, N, K)
+ * bytes on the current device (may be 0, then workspace may be NULL). */
+size_t w8dbg_int8_gemm_i32_workspace_size(int64_t M, int64_t N, int64_t K);
 w8_status w8dbg_int8_gemm_i32(const int8_t* q, const int8_t* Wq, int64_t M, int64_t N, int64_t K,
-                              int32_t* acc, void* stream);
+                              int32_t* acc, void* workspace, size_t workspace_bytes, void* stream);
 
 /* The activation half of fp8_w8a8_linear: xq [M,K] E4M3 codes, sx [M] fp32. */
 w8_status w8dbg_fp8_quantize_activations(const void* X, int x_dt, int64_t M, int64_t K,

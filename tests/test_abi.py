@@ -119,8 +119,8 @@ def test_weight_quantisation_rejects(args, status):
 
 def test_debug_exports_reject():
     lib = _abi.lib()
-    assert lib.w8dbg_int8_gemm_i32(A, A, 4, 4, 20, A, None) == _abi.W8_ERR_INVALID_ARGUMENT
-    assert lib.w8dbg_int8_gemm_i32(None, A, 4, 4, 32, A, None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert lib.w8dbg_int8_gemm_i32(A, A, 4, 4, 20, A, None, 0, None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert lib.w8dbg_int8_gemm_i32(None, A, 4, 4, 32, A, None, 0, None) == _abi.W8_ERR_INVALID_ARGUMENT
     assert lib.w8dbg_fp8_quantize_activations(A, _abi.W8_DT_BF16, 4, 20, None, A, A, None) == \
         _abi.W8_ERR_INVALID_ARGUMENT
     assert lib.w8dbg_int8_quantize_activations(A, _abi.W8_DT_BF16, 4, 32, 6.0, A, A, A, A, A, 1,

@@ -51,6 +51,10 @@ def _cases():
     yield synth.random_linear(513, 1040, 777, seed=33, x_dtype="bf16", outlier_cols=40, name="many_outliers")
     yield synth.random_linear(70, 16, 33, seed=34, x_dtype="bf16", outlier_cols=0, name="k16_no_outliers")
     yield synth.random_linear(333, 640, 300, seed=35, x_dtype="bf16", outlier_cols=3, name="ragged_mn_k64")
+    # few tiles, long K: on 256 CUs the GEMM splits them along K (3 slices of
+    # 128 K-steps; 4 uneven slices of 193 K-steps)
+    yield synth.random_linear(300, 8192, 520, seed=36, x_dtype="bf16", outlier_cols=4, name="split_k_bf16")
+    yield synth.random_linear(200, 12352, 300, seed=37, x_dtype="f16", outlier_cols=6, name="split_k_f16_uneven")
 
 
 CASES = list(_cases())
@@ -149,7 +153,9 @@ def test_every_bf16_value_encodes_like_the_oracle():
 
 @pytest.mark.parametrize("M,N,K", [(300, 520, 272), (257, 130, 48), (600, 700, 320), (64, 512, 256), (1, 1, 16),
                                    (256, 256, 16384), (300, 200, 64), (77, 300, 128), (256, 512, 192),
-                                   (520, 260, 320)])
+                                   (520, 260, 320),
+                                   # K-split of the last wave of tiles (even, uneven, many tiles, ragged)
+                                   (300, 520, 16384), (77, 300, 12352), (600, 700, 8192), (513, 1040, 16384)])
 def test_int8_gemm_accumulators_bit_exact(M, N, K):
     rng = np.random.default_rng(M * 7 + N * 3 + K)
     q = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
@@ -235,9 +241,11 @@ def test_dit_1024_full_size(name):
     assert np.array_equal(sx.cpu().numpy(), sx_ref)
     assert np.array_equal(q.cpu().numpy(), q_ref)
     # accumulators and outputs on sampled rows (every injected row included)
+    # and on the whole last 256-row strip, whose tiles the GEMM splits along K
     rng = np.random.default_rng(44)
+    last_strip = np.arange((c.M - 1) // 256 * 256, c.M)
     rows = np.unique(np.concatenate([rng.choice(c.M, 96, replace=False), np.array(c.injected_rows, int),
-                                     [0, c.M - 1]])).astype(int)
+                                     [0, c.M - 1], last_strip])).astype(int)
     acc = w8.debug_int8_gemm_i32(q, wq)
     acc_rows = acc[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.int64)
     assert np.array_equal(acc_rows, o.int8_contract(q_ref[rows], wq_ref))

@@ -126,7 +126,10 @@ def debug_int8_gemm_i32(q: torch.Tensor, wq: torch.Tensor) -> torch.Tensor:
     M, K = q.shape
     N = wq.shape[0]
     acc = torch.empty((M, N), dtype=torch.int32, device=q.device)
-    _abi.check(lib().w8dbg_int8_gemm_i32(q.data_ptr(), wq.data_ptr(), M, N, K, acc.data_ptr(), _stream(q)))
+    n_ws = int(lib().w8dbg_int8_gemm_i32_workspace_size(M, N, K))
+    ws = _workspace(n_ws, q.device) if n_ws else None
+    _abi.check(lib().w8dbg_int8_gemm_i32(q.data_ptr(), wq.data_ptr(), M, N, K, acc.data_ptr(),
+                                         ws.data_ptr() if ws is not None else None, n_ws, _stream(q)))
     return acc
 
 

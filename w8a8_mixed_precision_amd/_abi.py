@@ -31,7 +31,8 @@ SIGNATURES = {
     "w8_last_error": (ctypes.c_char_p, []),
     "w8dbg_int8_quantize_activations_workspace_size": (_size, [_i64, _i64]),
     "w8dbg_int8_quantize_activations": (_int, [_p, _int, _i64, _i64, _f, _p, _p, _p, _p, _p, _size, _p]),
-    "w8dbg_int8_gemm_i32": (_int, [_p, _p, _i64, _i64, _i64, _p, _p]),
+    "w8dbg_int8_gemm_i32_workspace_size": (_size, [_i64, _i64, _i64]),
+    "w8dbg_int8_gemm_i32": (_int, [_p, _p, _i64, _i64, _i64, _p, _p, _size, _p]),
     "w8dbg_fp8_quantize_activations": (_int, [_p, _int, _i64, _i64, _p, _p, _p, _p]),
     "w8_profile_start": (_int, [_int]),
     "w8_profile_stop": (_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_int)]),

@@ -8,24 +8,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include "launch.h"
 #include "w8mp.h"
 
-namespace w8 {
-void launch_clear(uint32_t* p, int n, hipStream_t s);
-void launch_int8_rows(const void* X, bool bf16, int64_t rows, int K, float t, int8_t* q, float* sx, int* amax_col,
-                      uint8_t* colflag, bool weight, hipStream_t s);
-size_t outlier_fixup_lds_bytes(int K);
-void launch_outlier_fixup(const void* X, bool bf16, int64_t M, int K, const uint8_t* colflag, int8_t* q, float* sx,
-                          const int* amax_col, int* O, int* nO, uint16_t* XO, const int8_t* Wq, int64_t N,
-                          uint16_t* WO, hipStream_t s);
-void launch_fp8_rows(const void* X, bool bf16, int64_t rows, int K, const float* act_scale, uint8_t* xq, float* sx,
-                     int mode, hipStream_t s);
-void launch_int8_gemm(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t K, const float* sx,
-                      const float* sw, const int* nO, const uint16_t* XO, const uint16_t* WO, bool xbf16, void* Y,
-                      int mode, hipStream_t s);
-void launch_fp8_gemm(const uint8_t* A, const uint8_t* B, int64_t M, int64_t N, int64_t K, const float* sx,
-                     const float* sw, void* Y, int ydt, hipStream_t s);
-}  // namespace w8
 
 namespace {
 
@@ -75,23 +60,59 @@ w8_status check_mk(int64_t M, int64_t K, int64_t maxK) {
   return W8_OK;
 }
 
+// Compute units of the current device (cached per device); the GEMM plan
+// depends on it, so workspace sizes are per device.
+int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cache[dev] = n;
+  return n;
+}
+
 // Workspace layout of int8_mixed_linear (offsets from the 256-aligned base).
+// flags and cnt are adjacent so one clear covers both.
 struct Int8Ws {
-  size_t q, sx, amax, flags, O, nO, XO, WO, total;
+  size_t q, sx, amax, flags, cnt, nO, O, XO, WO, part, total;
+  size_t clear_words;
+  w8::Int8GemmPlan plan;
 };
 
 Int8Ws int8_layout(int64_t M, int64_t N, int64_t K) {
   Int8Ws w{};
+  w.plan = w8::plan_int8_gemm(M, N, K, cu_count());
   const size_t P = static_cast<size_t>((K + 31) / 32 * 32);  // worst case: every column is an outlier
   size_t off = 0;
   w.q = off;    off = up(off + static_cast<size_t>(M) * K);
   w.sx = off;   off = up(off + 4 * static_cast<size_t>(M));
   w.amax = off; off = up(off + 4 * static_cast<size_t>(M));
   w.flags = off; off = up(off + static_cast<size_t>(K));
+  w.cnt = off;  off = up(off + 4 * static_cast<size_t>(w.plan.counters()));
+  w.clear_words = (off - w.flags) / 4;
   w.nO = off;   off = up(off + 4);
   w.O = off;    off = up(off + 4 * static_cast<size_t>(K));
   w.XO = off;   off = up(off + 2 * static_cast<size_t>(M) * P);
   w.WO = off;   off = up(off + 2 * static_cast<size_t>(N) * P);
+  w.part = off; off = up(off + w.plan.partial_bytes());
+  w.total = off;
+  return w;
+}
+
+// Workspace of the int8 GEMM parity export: counters, then partials.
+struct GemmWs {
+  size_t cnt, part, total;
+  w8::Int8GemmPlan plan;
+};
+
+GemmWs gemm_layout(int64_t M, int64_t N, int64_t K) {
+  GemmWs w{};
+  w.plan = w8::plan_int8_gemm(M, N, K, cu_count());
+  size_t off = 0;
+  w.cnt = off;  off = up(off + 4 * static_cast<size_t>(w.plan.counters()));
+  w.part = off; off = up(off + w.plan.partial_bytes());
   w.total = off;
   return w;
 }
@@ -132,7 +153,7 @@ struct Profile {
 // Record boundary `b` (0..3) of the current call; a no-op unless profiling.
 void mark(int b, hipStream_t s) {
   if (!g_prof.on || g_prof.n >= g_prof.cap) return;
-  hipEventRecord(g_prof.ev[4 * g_prof.n + b], s);
+  (void)hipEventRecord(g_prof.ev[4 * g_prof.n + b], s);
   if (b == 3) ++g_prof.n;
 }
 
@@ -172,7 +193,7 @@ w8_status w8_profile_stop(double* stage_ms, int* n_calls) {
   }
   *n_calls = g_prof.n;
   for (auto& e : g_prof.ev)
-    if (e) hipEventDestroy(e);
+    if (e) (void)hipEventDestroy(e);
   g_prof.ev.clear();
   g_prof.on = false;
   g_prof.cap = g_prof.n = 0;
@@ -246,14 +267,16 @@ w8_status int8_mixed_linear(const void* X, int x_dt, int64_t M, int64_t K, const
   int* O = at<int>(workspace, L.O);
   uint16_t* XO = at<uint16_t>(workspace, L.XO);
   uint16_t* WO = at<uint16_t>(workspace, L.WO);
+  int* cnt = at<int>(workspace, L.cnt);
+  int* part = at<int>(workspace, L.part);
 
   mark(0, s);
-  w8::launch_clear(reinterpret_cast<uint32_t*>(flags), (int)(K / 4), s);
+  w8::launch_clear(reinterpret_cast<uint32_t*>(flags), (int)L.clear_words, s);
   w8::launch_int8_rows(X, bf, M, (int)K, threshold, q, sx, amax, flags, false, s);
   mark(1, s);
   w8::launch_outlier_fixup(X, bf, M, (int)K, flags, q, sx, amax, O, nO, XO, Wq, N, WO, s);
   mark(2, s);
-  w8::launch_int8_gemm(q, Wq, M, N, K, sx, sw, nO, XO, WO, bf, Y, y_dt == W8_DT_F16 ? 1 : 2, s);
+  w8::launch_int8_gemm(q, Wq, M, N, K, sx, sw, nO, XO, WO, bf, Y, y_dt == W8_DT_F16 ? 1 : 2, L.plan, part, cnt, s);
   mark(3, s);
   return check_launch("int8_mixed_linear");
 }
@@ -316,15 +339,28 @@ w8_status w8dbg_int8_quantize_activations(const void* X, int x_dt, int64_t M, in
   return check_launch("w8dbg_int8_quantize_activations");
 }
 
+size_t w8dbg_int8_gemm_i32_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 1) return 0;
+  return gemm_layout(M, N, K).total;
+}
+
 w8_status w8dbg_int8_gemm_i32(const int8_t* q, const int8_t* Wq, int64_t M, int64_t N, int64_t K, int32_t* acc,
-                              void* stream) {
+                              void* workspace, size_t workspace_bytes, void* stream) {
   W8_REQUIRE(q && Wq && acc, W8_ERR_INVALID_ARGUMENT, "null pointer argument");
   if (w8_status st = check_mk(M, K, W8_INT8_MAX_K); st != W8_OK) return st;
   W8_REQUIRE(N >= 1 && N <= kMaxDim, W8_ERR_INVALID_ARGUMENT, "N must be in [1, 2^31)");
   W8_REQUIRE(aligned16(q) && aligned16(Wq) && aligned16(acc), W8_ERR_INVALID_ARGUMENT,
              "pointers must be 16-byte aligned");
-  w8::launch_int8_gemm(q, Wq, M, N, K, nullptr, nullptr, nullptr, nullptr, nullptr, true, acc, 0,
-                       static_cast<hipStream_t>(stream));
+  const GemmWs L = gemm_layout(M, N, K);
+  if (L.total > 0) {
+    if (w8_status st = check_ws(workspace, workspace_bytes, L.total); st != W8_OK) return st;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int* cnt = L.total > 0 ? at<int>(workspace, L.cnt) : nullptr;
+  int* part = L.total > 0 ? at<int>(workspace, L.part) : nullptr;
+  if (L.plan.counters() > 0) w8::launch_clear(reinterpret_cast<uint32_t*>(cnt), L.plan.counters(), s);
+  w8::launch_int8_gemm(q, Wq, M, N, K, nullptr, nullptr, nullptr, nullptr, nullptr, true, acc, 0, L.plan, part, cnt,
+                       s);
   return check_launch("w8dbg_int8_gemm_i32");
 }
 

@@ -17,9 +17,11 @@
 // registers). On gfx950 the 32x32x32 int8 MFMA runs at the full int8 rate
 // (the 16x16x64 form issues at half of it). Both operands are K-contiguous
 // ([M,K] and [N,K]) and staged through LDS with a 16-byte XOR swizzle.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
+#include "launch.h"
 
 namespace w8 {
 
@@ -35,16 +37,19 @@ __device__ __forceinline__ int swz_term(int row) { return ((row >> 1) ^ (row >> 
 __device__ __forceinline__ int swz64(int row, int ch) { return row * kBK + ((ch ^ swz_term(row)) << 4); }
 
 // XCD-aware block order: the hardware deals consecutive workgroups round-robin
-// over the 8 XCDs; renumber so each XCD gets a contiguous range, then walk
-// tiles in groups of kGroupM tile-rows so blocks that run together on one XCD
-// share A rows and B columns in that XCD's L2.
+// over the 8 XCDs; renumber so each XCD gets a contiguous range of ids, then
+// walk tiles in groups of kGroupM tile-rows so blocks that run together on one
+// XCD share A rows and B columns in that XCD's L2.
 constexpr int kXcds = 8, kGroupM = 4;
 
-__device__ __forceinline__ void tile_coords(int bid, int nblocks, int tiles_m, int tiles_n, int& tm, int& tn) {
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   const int per = (nblocks + kXcds - 1) / kXcds;
   const int tall = nblocks - (per - 1) * kXcds;  // XCDs that get `per` blocks
   const int xcd = bid % kXcds, local = bid / kXcds;
-  const int id = (xcd < tall) ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
+  return (xcd < tall) ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
+}
+
+__device__ __forceinline__ void group_tile(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int in_group = kGroupM * tiles_n;
   const int g = id / in_group;
   const int first_m = g * kGroupM;
@@ -52,6 +57,10 @@ __device__ __forceinline__ void tile_coords(int bid, int nblocks, int tiles_m, i
   const int r = id % in_group;
   tm = first_m + r % gm;
   tn = r / gm;
+}
+
+__device__ __forceinline__ void tile_coords(int bid, int nblocks, int tiles_m, int tiles_n, int& tm, int& tn) {
+  group_tile(xcd_remap(bid, nblocks), tiles_m, tiles_n, tm, tn);
 }
 
 // One K step (64 bytes) of the wave's 128x128 tile from LDS: two 32-byte
@@ -79,53 +88,40 @@ __device__ __forceinline__ void mma_step(const int8_t* sa, const int8_t* sb, v16
 //   m = m0 + wm*128 + 32*i + (lane&31),
 //   n = n0 + wn*128 + 32*j + 8*(r>>2) + 4*(lane>>5) + (r&3):
 // one output row per lane and four consecutive columns per group of four
-// registers, stored as one 8-byte (fp16) or 16-byte (fp32 / int32) write.
+// registers. Stored directly, every store instruction would touch 32 rows
+// (32 partial cache lines); instead each wave stages 32 rows x 256 bytes of
+// its results in LDS and writes them back as whole rows, 16 lanes x 16 bytes
+// per row, 4 rows per instruction.
 //
 // rsx[i]: sx[m]/127 for the lane's row of block i (prefetched by the caller);
-// scol: LDS copy of sw[n0 .. n0+256) / 127.
+// scol: LDS copy of sw[n0 .. n0+256) / 127; stg: this wave's staging area.
+constexpr int kStgPitch = 256 + 16;             // staged row: 256 bytes + pad
+constexpr int kStgWave = 32 * kStgPitch;        // one wave's 32 staged rows
+constexpr int kEpiLds = 1024 + 4 * kStgWave;    // column scales + 4 staging areas
+
 template <int MODE, bool XBF16>
 __device__ __forceinline__ void epilogue(v16i (&acc)[4][4], int M, int N, int m0, int n0, int wm, int wn, int lane,
                                          const float (&rsx)[4], const float* scol, int nO,
                                          const uint16_t* __restrict__ XO, const uint16_t* __restrict__ WO,
-                                         void* __restrict__ Y) {
+                                         void* __restrict__ Y, char* stg) {
   const int fr = lane & 31, fh = lane >> 5;
-  const bool vec = (N & 3) == 0;            // 4 consecutive columns are aligned and in one row
-  auto col_of = [&](int j, int g) { return n0 + wn * 128 + 32 * j + 8 * g + 4 * fh; };
-
-  if constexpr (MODE == 0) {
-    int32_t* y = static_cast<int32_t*>(Y);
+  constexpr int EB = MODE == 1 ? 2 : 4;         // bytes per output element
+  constexpr int PJ = 256 / (32 * EB);           // 32-column MFMA tiles per staged row: 4 or 2
+  constexpr int EPC = 16 / EB;                  // elements per 16-byte chunk
+  const bool vec = (static_cast<int64_t>(N) * EB) % 16 == 0;
+  const int P = (nO + 31) & ~31;
+  using V8 = typename std::conditional<XBF16, v8bf, v8h>::type;
+  char* const y = static_cast<char*>(Y);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 4; ++i) {
+    // side product for this 32-row block: o[j] = WO(block j) . XO(rows of block i)^T
+    v16f o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[j][r] = 0.0f;
+    if constexpr (MODE != 0) {
       const int m = m0 + wm * 128 + 32 * i + fr;
-      if (m >= M) continue;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = col_of(j, g);
-          int32_t* dst = y + static_cast<int64_t>(m) * N + n;
-          if (vec && n + 3 < N) {
-            *reinterpret_cast<v4i*>(dst) =
-                v4i{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (n + e < N) dst[e] = acc[i][j][4 * g + e];
-          }
-        }
-    }
-  } else {
-    // side product for one 32-row block at a time: o[j] = WO(block j) . XO(rows of block i)^T
-    const int P = (nO + 31) & ~31;
-    using V8 = typename std::conditional<XBF16, v8bf, v8h>::type;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + wm * 128 + 32 * i + fr;
-      v16f o[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[j][r] = 0.0f;
       const int64_t xrow = static_cast<int64_t>(min(m, M - 1)) * P;
       for (int c = 0; c < P; c += 16) {
         const V8 xb = *reinterpret_cast<const V8*>(XO + xrow + c + 8 * fh);
@@ -139,39 +135,60 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[4][4], int M, int N, int m0
             o[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wa, xb, o[j], 0, 0, 0);
         }
       }
-      if (m >= M) continue;
+    }
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+    for (int h = 0; h < 4 / PJ; ++h) {
+      // registers -> staging: row fr, columns 32*jj + 8*g + 4*fh .. +4 of this pass
+#pragma unroll
+      for (int jj = 0; jj < PJ; ++jj) {
+        const int j = h * PJ + jj;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int n = col_of(j, g);
-          const v4f cs = *reinterpret_cast<const v4f*>(scol + (n - n0));
-          float y[4];
+          char* dst = stg + fr * kStgPitch + (32 * jj + 8 * g + 4 * fh) * EB;
+          if constexpr (MODE == 0) {
+            *reinterpret_cast<v4i*>(dst) =
+                v4i{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          } else {
+            const v4f cs = *reinterpret_cast<const v4f*>(scol + wn * 128 + 32 * j + 8 * g + 4 * fh);
+            float v[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            y[e] = (static_cast<float>(acc[i][j][4 * g + e]) * rsx[i] + o[j][4 * g + e]) * cs[e];
-          if constexpr (MODE == 1) {
-            uint16_t* dst = static_cast<uint16_t*>(Y) + static_cast<int64_t>(m) * N + n;
-            if (vec && n + 3 < N) {
-              const uint32_t lo = f32_to_f16_bits(y[0]) | (static_cast<uint32_t>(f32_to_f16_bits(y[1])) << 16);
-              const uint32_t hi = f32_to_f16_bits(y[2]) | (static_cast<uint32_t>(f32_to_f16_bits(y[3])) << 16);
+            for (int e = 0; e < 4; ++e)
+              v[e] = (static_cast<float>(acc[i][j][4 * g + e]) * rsx[i] + o[j][4 * g + e]) * cs[e];
+            if constexpr (MODE == 1) {
+              const uint32_t lo = f32_to_f16_bits(v[0]) | (static_cast<uint32_t>(f32_to_f16_bits(v[1])) << 16);
+              const uint32_t hi = f32_to_f16_bits(v[2]) | (static_cast<uint32_t>(f32_to_f16_bits(v[3])) << 16);
               *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
             } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (n + e < N) dst[e] = f32_to_f16_bits(y[e]);
-            }
-          } else {
-            float* dst = static_cast<float*>(Y) + static_cast<int64_t>(m) * N + n;
-            if (vec && n + 3 < N) {
-              *reinterpret_cast<v4f*>(dst) = v4f{y[0], y[1], y[2], y[3]};
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (n + e < N) dst[e] = y[e];
+              *reinterpret_cast<v4f*>(dst) = v4f{v[0], v[1], v[2], v[3]};
             }
           }
         }
+      }
+      // staging -> global: 8 instructions of 4 rows x 16 chunks of 16 bytes.
+      // LDS accesses of one wave complete in issue order, so no wait is needed
+      // between the staging writes and these reads, nor before the next pass.
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int r = 4 * t + (lane >> 4), ch = lane & 15;
+        const char* src = stg + r * kStgPitch + ch * 16;
+        const int m = m0 + wm * 128 + 32 * i + r;
+        const int n = n0 + wn * 128 + h * PJ * 32 + ch * EPC;
+        if (m < M) {
+          char* dst = y + (static_cast<int64_t>(m) * N + n) * EB;
+          if (vec && n + EPC <= N) {
+            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+          } else {
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) {
+              if (n + e >= N) break;
+              if constexpr (EB == 2)
+                *reinterpret_cast<uint16_t*>(dst + 2 * e) = *reinterpret_cast<const uint16_t*>(src + 2 * e);
+              else
+                *reinterpret_cast<uint32_t*>(dst + 4 * e) = *reinterpret_cast<const uint32_t*>(src + 4 * e);
+            }
+          }
+        }
+      }
     }
   }
 }
@@ -202,20 +219,22 @@ __device__ __forceinline__ void epi_prefetch(EpiIn& e, int M, int N, int m0, int
   }
 }
 
-// Finishes the prefetch (divides by 127, publishes the column scales in
-// `scol`, 256 floats of LDS no longer used by the K loop) and runs the
-// epilogue. Every wave of the block must call it.
+// Finishes the prefetch (divides by 127, publishes the column scales in LDS)
+// and runs the epilogue. `lds` is at least kEpiLds bytes of LDS that the K loop
+// no longer uses. Every wave of the block must call it.
 template <int MODE, bool XBF16>
-__device__ __forceinline__ void finish_tile(v16i (&acc)[4][4], EpiIn& e, float* scol, int M, int N, int m0, int n0,
+__device__ __forceinline__ void finish_tile(v16i (&acc)[4][4], EpiIn& e, char* lds, int M, int N, int m0, int n0,
                                             int wm, int wn, int lane, const uint16_t* __restrict__ XO,
                                             const uint16_t* __restrict__ WO, void* __restrict__ Y) {
+  float* scol = reinterpret_cast<float*>(lds);
   if constexpr (MODE != 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) e.rsx[i] = e.rsx[i] / 127.0f;
     scol[threadIdx.x] = e.my_sw / 127.0f;
     __syncthreads();
   }
-  epilogue<MODE, XBF16>(acc, M, N, m0, n0, wm, wn, lane, e.rsx, scol, e.nO, XO, WO, Y);
+  epilogue<MODE, XBF16>(acc, M, N, m0, n0, wm, wn, lane, e.rsx, scol, e.nO, XO, WO, Y,
+                        lds + 1024 + (threadIdx.x >> 6) * kStgWave);
 }
 
 __device__ __forceinline__ void zero_acc(v16i (&acc)[4][4]) {
@@ -239,7 +258,7 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm(const int8_t* __restrict__
                                                       const uint16_t* __restrict__ WO, void* __restrict__ Y,
                                                       int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(16))) int8_t lds[2][2][kBM * kBK];
-  __shared__ float scol[kBN];
+  static_assert(sizeof(lds) >= kEpiLds, "epilogue LDS");
 
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
@@ -293,7 +312,7 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm(const int8_t* __restrict__
     if (kt + 1 < nk) lstore(st ^ 1);
     __syncthreads();
   }
-  finish_tile<MODE, XBF16>(acc, ein, scol, M, N, m0, n0, wm, wn, lane, XO, WO, Y);
+  finish_tile<MODE, XBF16>(acc, ein, reinterpret_cast<char*>(&lds[0][0][0]), M, N, m0, n0, wm, wn, lane, XO, WO, Y);
 }
 
 // ---------------------------------------------------------------------------
@@ -347,15 +366,26 @@ __device__ __forceinline__ void mfma_sub(const v4i (&f)[8], v16i (&acc)[4][4]) {
 }
 
 // One 32-byte sub-step as 8 fixed groups of {2 MFMAs on the current
-// fragments, 1 LDS read of the next fragments, [1 DMA of a future K-step]}.
-// sched_barrier keeps the order: the loads are spread over the MFMA
-// shadow instead of stalling the wave's in-order issue in a burst.
+// fragments, LDS reads of the next fragments, [1 DMA of a future K-step]}.
+// sched_barrier keeps the order: the loads are spread over the MFMA shadow
+// instead of stalling the wave's in-order issue in a burst. The next
+// fragments are read in the order the next sub-step consumes them (A0, then
+// B0..B3, then A1..A3). Without DMA (the sub-step before the barrier) the
+// reads go two per group into the first four groups, so they have landed by
+// the time the wave waits for them at the barrier.
 template <bool DMA>
 __device__ __forceinline__ void mma_phase(const v4i (&fm)[8], v16i (&acc)[4][4], const int8_t* sfr, int sub,
                                           int wm, int wn, int lane, v4i (&fl)[8],
                                           const int8_t* const (&a_src)[4], const int8_t* const (&b_src)[4],
                                           int k0, int8_t* st, int wave) {
   const int fr = lane & 31, fh = lane >> 5;
+  constexpr int kOrder[8] = {0, 4, 5, 6, 7, 1, 2, 3};   // fragment index: 0..3 rows of A, 4..7 rows of B
+  auto read = [&](int f) {
+    if (f < 4)
+      fl[f] = *reinterpret_cast<const v4i*>(sfr + swz64(wm * 128 + f * 32 + fr, 2 * sub + fh));
+    else
+      fl[f] = *reinterpret_cast<const v4i*>(sfr + kBM * kBK + swz64(wn * 128 + (f - 4) * 32 + fr, 2 * sub + fh));
+  };
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const int p0 = 2 * t, p1 = 2 * t + 1;
@@ -363,19 +393,29 @@ __device__ __forceinline__ void mma_phase(const v4i (&fm)[8], v16i (&acc)[4][4],
         __builtin_amdgcn_mfma_i32_32x32x32_i8(fm[4 + (p0 & 3)], fm[p0 >> 2], acc[p0 >> 2][p0 & 3], 0, 0, 0);
     acc[p1 >> 2][p1 & 3] =
         __builtin_amdgcn_mfma_i32_32x32x32_i8(fm[4 + (p1 & 3)], fm[p1 >> 2], acc[p1 >> 2][p1 & 3], 0, 0, 0);
-    if (t < 4)
-      fl[t] = *reinterpret_cast<const v4i*>(sfr + swz64(wm * 128 + t * 32 + fr, 2 * sub + fh));
-    else
-      fl[t] = *reinterpret_cast<const v4i*>(sfr + kBM * kBK + swz64(wn * 128 + (t - 4) * 32 + fr, 2 * sub + fh));
     if (DMA) {
+      read(kOrder[t]);
       if (t < 4)
         __builtin_amdgcn_global_load_lds(a_src[t] + k0, st + (wave * 4 + t) * 1024, 16, 0, 0);
       else
         __builtin_amdgcn_global_load_lds(b_src[t - 4] + k0, st + kBM * kBK + (wave * 4 + t - 4) * 1024, 16, 0, 0);
+    } else if (t < 4) {
+      read(kOrder[2 * t]);
+      read(kOrder[2 * t + 1]);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
+
+// Work split for the last, partial wave of tiles (split-K). The first
+// dp_tiles blocks each own a whole 256x256 tile. The remaining blocks are
+// `split` K-slices of each of the R = (gridDim.x - dp_tiles) / split leftover
+// tiles: every slice writes its int32 partial sums to its own slot of `part`,
+// bumps the tile's arrival counter in `cnt` (zero on entry), and the last
+// slice to arrive adds the other slices' partials to its own and runs the
+// epilogue. Integer sums are exact in any order, so the result does not
+// depend on which slice arrives last. No block ever waits for another.
+constexpr int kPartInts = kBM * kBN;          // one 256x256 int32 partial
 
 template <int MODE, bool XBF16, int S>
 __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
@@ -383,13 +423,38 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
                                                           const float* __restrict__ sw, const int* __restrict__ nO_ptr,
                                                           const uint16_t* __restrict__ XO,
                                                           const uint16_t* __restrict__ WO, void* __restrict__ Y,
-                                                          int tiles_m, int tiles_n) {
+                                                          int tiles_m, int tiles_n, int dp_tiles, int split,
+                                                          int* __restrict__ part, int* __restrict__ cnt) {
   constexpr int kStage = 2 * kBM * kBK;       // A then B, 32 KB
   constexpr int kLoads = 8;                   // DMA instructions per wave per step
   __shared__ __attribute__((aligned(1024))) int8_t lds[S * kStage];
+  static_assert(sizeof(lds) >= kEpiLds, "epilogue LDS");
+  // A second __shared__ object would make the compiler guard every LDS read in
+  // the K loop with a full vmcnt wait (it cannot tell the DMA destinations
+  // apart from it); the split-K arrival flag lives in the ring instead, which
+  // the K loop no longer uses by then (past the epilogue's LDS, so the
+  // epilogue cannot overwrite it while a wave still reads it).
+  int* const s_last = reinterpret_cast<int*>(lds + kEpiLds);
+  static_assert(sizeof(lds) >= kEpiLds + 4, "epilogue LDS and arrival flag");
 
-  int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int nk_all = K / kBK;
+  int tm, tn, kb = 0, ke = nk_all;
+  int slot = -1, sk_tile = 0, piece = 0, R = 0;
+  if (static_cast<int>(blockIdx.x) < dp_tiles) {
+    tile_coords(blockIdx.x, dp_tiles, tiles_m, tiles_n, tm, tn);
+  } else {
+    // slices are numbered slice-major per XCD, so the blocks of one XCD share
+    // the K range and the A rows of neighbouring tiles
+    const int nu = gridDim.x - dp_tiles;
+    const int v = xcd_remap(blockIdx.x - dp_tiles, nu);
+    R = nu / split;
+    piece = v / R;
+    sk_tile = v % R;
+    slot = v;
+    group_tile(dp_tiles + sk_tile, tiles_m, tiles_n, tm, tn);
+    kb = piece * nk_all / split;
+    ke = (piece + 1) * nk_all / split;
+  }
   const int m0 = tm * kBM, n0 = tn * kBN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -405,10 +470,10 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
   for (int i = 0; i < 4; ++i) {
     const int r = wave * 64 + 16 * i + (lane >> 2);
     const int ch = (lane & 3) ^ swz_term(r);
-    a_src[i] = A + static_cast<int64_t>(min(m0 + r, M - 1)) * K + ch * 16;
-    b_src[i] = B + static_cast<int64_t>(min(n0 + r, N - 1)) * K + ch * 16;
+    a_src[i] = A + static_cast<int64_t>(min(m0 + r, M - 1)) * K + kb * kBK + ch * 16;
+    b_src[i] = B + static_cast<int64_t>(min(n0 + r, N - 1)) * K + kb * kBK + ch * 16;
   }
-  const int nk = K / kBK;
+  const int nk = ke - kb;
   // DMA of K-step kt into its ring slot. Past the last step the load repeats
   // the last step's data into the slot just retired, which no later step
   // reads: every iteration then issues the same number of loads, so the wait
@@ -448,34 +513,131 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
   mfma_sub(f1, acc);
   wait_vmcnt<0>();                                // retire the trailing repeat loads
   block_barrier();                                // every wave is done with the ring
-  finish_tile<MODE, XBF16>(acc, ein, reinterpret_cast<float*>(lds), M, N, m0, n0, wm, wn, lane, XO, WO, Y);
+
+  if (slot >= 0) {
+    // Partial layout: 16-byte chunk c (0..63) of wave w's 256 accumulators at
+    // byte ((w*64 + c)*64 + lane)*16, so every access is 1 KB contiguous.
+    // Partials are written and read through buffer instructions with the
+    // agent-scope coherence bit (sc1), the form the compiler itself uses for
+    // agent-scope atomic loads and stores: those accesses are coherent across
+    // XCDs on their own, without the whole-L2 write-back / invalidate that a
+    // device-scope fence performs. Once a wave's stores have completed
+    // (vmcnt 0) they are visible to any later sc1 load; the arrival counter is
+    // bumped only after every wave's stores have completed.
+    constexpr int kSc1 = 16;                       // cache-policy bit sc1
+    constexpr int kRawBuffer = 0x00020000;         // word 3 of a raw buffer descriptor (32-bit data format)
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int lane_off = (wv * 64 * 64 + lane) * 16;
+    const __amdgpu_buffer_rsrc_t mine = __builtin_amdgcn_make_buffer_rsrc(
+        part + static_cast<int64_t>(slot) * kPartInts, 0, kPartInts * 4, kRawBuffer);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = (i * 4 + j) * 4 + q;
+          const v4i v{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), mine, lane_off + c * 1024, 0, kSc1);
+        }
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's partial is visible
+    __syncthreads();                                        // ... and every wave's
+    if (tid == 0)
+      *s_last = __hip_atomic_fetch_add(cnt + sk_tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == split - 1;
+    __syncthreads();
+    if (!*s_last) return;
+    // one 32-row block at a time, so only its 64 accumulators leave the AGPRs
+    // and 16 loads of 1 KB per wave are in flight
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      for (int p = 0; p < split; ++p) {
+        if (p == piece) continue;
+        const __amdgpu_buffer_rsrc_t other = __builtin_amdgcn_make_buffer_rsrc(
+            part + static_cast<int64_t>(p * R + sk_tile) * kPartInts, 0, kPartInts * 4, kRawBuffer);
+        v4i w[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t)
+          w[t] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(other, lane_off + (i * 16 + t) * 1024,
+                                                                               0, kSc1));
+#pragma unroll
+        for (int t = 0; t < 16; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][t >> 2][4 * (t & 3) + e] += w[t][e];
+      }
+    }
+  }
+  finish_tile<MODE, XBF16>(acc, ein, reinterpret_cast<char*>(lds), M, N, m0, n0, wm, wn, lane, XO, WO, Y);
 }
 
 // ---------------------------------------------------------------------------
-// mode: 0 int32 acc, 1 fp16 out, 2 fp32 out
+// Launch plan. Whole tiles fill as many complete waves of `cus` blocks as
+// they can; the leftover R = T mod cus tiles may be split along K into
+// `split` slices instead. Cost model in K-steps, fitted to MI355X timings:
+// a sparse last wave of whole tiles runs at ~3/4 of a full tile's time (the
+// few busy CUs clock higher and share the memory system with no one); a split
+// costs its slice, a fixed start-up and, for the last slice, re-reading the
+// other slices. 256 KB partials from another CU (the dominant cost, ~10
+// K-steps each). In practice only long-K shapes split.
+constexpr int kSliceCost = 10;
+constexpr int kSliceFixed = 10;
+constexpr int kMinSliceSteps = 4;
+constexpr int kMaxSplit = 16;
+
+Int8GemmPlan plan_int8_gemm(int64_t M, int64_t N, int64_t K, int cus) {
+  Int8GemmPlan p{};
+  p.tiles_m = static_cast<int>((M + kBM - 1) / kBM);
+  p.tiles_n = static_cast<int>((N + kBN - 1) / kBN);
+  const int T = p.tiles_m * p.tiles_n;
+  p.dp_tiles = T;
+  p.split = 1;
+  p.sk_tiles = 0;
+  if (K % kBK != 0 || cus <= 0) return p;
+  const int R = T % cus;
+  if (R == 0) return p;
+  const int nk = static_cast<int>(K / kBK);
+  const int smax = std::min(std::min(cus / R, nk / kMinSliceSteps), kMaxSplit);
+  int best = 1, best_cost = 3 * nk / 4;
+  for (int s = 2; s <= smax; ++s) {
+    const int cost = (nk + s - 1) / s + kSliceCost * (s - 1) + kSliceFixed;
+    if (cost < best_cost) best = s, best_cost = cost;
+  }
+  if (best == 1) return p;
+  p.dp_tiles = T - R;
+  p.split = best;
+  p.sk_tiles = R;
+  return p;
+}
+
+// ---------------------------------------------------------------------------
+// mode: 0 int32 acc, 1 fp16 out, 2 fp32 out. `part` / `cnt` are needed when
+// plan.split > 1 (plan.sk_tiles * plan.split partials, plan.sk_tiles counters
+// that must be zero).
 void launch_int8_gemm(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t K, const float* sx,
                       const float* sw, const int* nO, const uint16_t* XO, const uint16_t* WO, bool xbf16,
-                      void* Y, int mode, hipStream_t s) {
-  const int tiles_m = static_cast<int>((M + kBM - 1) / kBM);
-  const int tiles_n = static_cast<int>((N + kBN - 1) / kBN);
-  const dim3 grid(tiles_m * tiles_n), block(256);
+                      void* Y, int mode, const Int8GemmPlan& plan, int* part, int* cnt, hipStream_t s) {
+  const int tiles_m = plan.tiles_m, tiles_n = plan.tiles_n;
   const int m = (int)M, n = (int)N, k = (int)K;
-#define W8_GEMM_ARGS A, B, m, n, k, sx, sw, nO, XO, WO, Y, tiles_m, tiles_n
+  const dim3 block(256);
   if (K % kBK == 0) {
     constexpr int S = 4;
+    const dim3 grid(plan.dp_tiles + plan.sk_tiles * plan.split);
+#define W8_GEMM_ARGS A, B, m, n, k, sx, sw, nO, XO, WO, Y, tiles_m, tiles_n, plan.dp_tiles, plan.split, part, cnt
     if (mode == 0) k_int8_gemm_dma<0, true, S><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
     else if (mode == 1 && xbf16) k_int8_gemm_dma<1, true, S><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
     else if (mode == 1) k_int8_gemm_dma<1, false, S><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
     else if (xbf16) k_int8_gemm_dma<2, true, S><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
     else k_int8_gemm_dma<2, false, S><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
+#undef W8_GEMM_ARGS
   } else {
+    const dim3 grid(tiles_m * tiles_n);
+#define W8_GEMM_ARGS A, B, m, n, k, sx, sw, nO, XO, WO, Y, tiles_m, tiles_n
     if (mode == 0) k_int8_gemm<0, true><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
     else if (mode == 1 && xbf16) k_int8_gemm<1, true><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
     else if (mode == 1) k_int8_gemm<1, false><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
     else if (xbf16) k_int8_gemm<2, true><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
     else k_int8_gemm<2, false><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
-  }
 #undef W8_GEMM_ARGS
+  }
 }
 
 }  // namespace w8

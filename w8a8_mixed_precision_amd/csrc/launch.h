@@ -1,0 +1,34 @@
+// Host-side launchers of the libw8mp kernels (internal to the library).
+#pragma once
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+namespace w8 {
+
+// Grid of the int8 GEMM: dp_tiles whole 256x256 tiles, then sk_tiles tiles cut
+// into `split` K-slices each (split == 1: none).
+struct Int8GemmPlan {
+  int tiles_m, tiles_n, dp_tiles, split, sk_tiles;
+  size_t partial_bytes() const { return split > 1 ? size_t(sk_tiles) * split * 256 * 256 * 4 : 0; }
+  int counters() const { return split > 1 ? sk_tiles : 0; }
+};
+Int8GemmPlan plan_int8_gemm(int64_t M, int64_t N, int64_t K, int cus);
+
+void launch_clear(uint32_t* p, int n, hipStream_t s);
+void launch_int8_rows(const void* X, bool bf16, int64_t rows, int K, float t, int8_t* q, float* sx, int* amax_col,
+                      uint8_t* colflag, bool weight, hipStream_t s);
+size_t outlier_fixup_lds_bytes(int K);
+void launch_outlier_fixup(const void* X, bool bf16, int64_t M, int K, const uint8_t* colflag, int8_t* q, float* sx,
+                          const int* amax_col, int* O, int* nO, uint16_t* XO, const int8_t* Wq, int64_t N,
+                          uint16_t* WO, hipStream_t s);
+void launch_fp8_rows(const void* X, bool bf16, int64_t rows, int K, const float* act_scale, uint8_t* xq, float* sx,
+                     int mode, hipStream_t s);
+void launch_int8_gemm(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t K, const float* sx,
+                      const float* sw, const int* nO, const uint16_t* XO, const uint16_t* WO, bool xbf16, void* Y,
+                      int mode, const Int8GemmPlan& plan, int* part, int* cnt, hipStream_t s);
+void launch_fp8_gemm(const uint8_t* A, const uint8_t* B, int64_t M, int64_t N, int64_t K, const float* sx,
+                     const float* sw, void* Y, int ydt, hipStream_t s);
+
+}  // namespace w8
