@@ -96,8 +96,7 @@ def main() -> int:
         wqs.append(wq)
         sws.append(sw)
         ys.append(torch.empty((c.M, c.N), dtype=torch.float16, device="cuda"))
-        wss.append(torch.empty(w8.int8_mixed_linear_workspace_size(c.M, c.N, c.K), dtype=torch.uint8,
-                               device="cuda"))
+        wss.append(w8.new_workspace(w8.int8_mixed_linear_workspace_size(c.M, c.N, c.K)))
     torch.cuda.synchronize()
 
     def step():

@@ -90,11 +90,15 @@ w8_status quantize_weight_rowwise(const void* W, int w_dt, int64_t N, int64_t K,
  *              outlier column when |X[m,k]| > t for some row m of THIS call.
  *              +inf gives plain vector-wise int8; t < 0 or NaN is rejected.
  *   Y          [M,N] f16 or f32 (y_dt), device, written in full.
- *   workspace  device scratch of at least int8_mixed_linear_workspace_size()
- *              bytes, 256-byte aligned; contents undefined after the call.
- *              The size depends on the compute-unit count of the device that
- *              is current when it is queried (the GEMM grid is planned per
- *              device); query and call on the same device.
+ *   workspace  device memory of at least int8_mixed_linear_workspace_size()
+ *              bytes, 256-byte aligned. It must be zero-filled before its
+ *              first use (e.g. hipMemsetAsync); every call leaves the
+ *              bookkeeping it relies on (outlier-column flags, arrival
+ *              counters) zero again, so a workspace is reused without
+ *              clearing. Do not write to it between calls. The size depends
+ *              on the compute-unit count of the device that is current when
+ *              it is queried (the GEMM grid is planned per device); query and
+ *              call on the same device.
  *
  * What is computed (O = outlier columns, ascending):
  *   sx[m]   = max_{k not in O} |X[m,k]|                     (fp32, exact)
@@ -147,7 +151,8 @@ const char* w8_last_error(void);
 /* The activation half of int8_mixed_linear (outlier detection, row scales,
  * int8 codes, outlier fix-up). Outputs (device): q [M,K] int8, sx [M] fp32,
  * outlier_idx [K] int32 (first *n_outliers entries valid, ascending),
- * n_outliers [1] int32. Workspace: w8dbg_int8_quantize_activations_workspace_size(M, K). */
+ * n_outliers [1] int32. Workspace: w8dbg_int8_quantize_activations_workspace_size(M, K)
+ * bytes, zero-filled before first use (left zero by every call). */
 size_t w8dbg_int8_quantize_activations_workspace_size(int64_t M, int64_t K);
 w8_status w8dbg_int8_quantize_activations(const void* X, int x_dt, int64_t M, int64_t K,
                                           float threshold, int8_t* q, float* sx,
@@ -157,7 +162,8 @@ w8_status w8dbg_int8_quantize_activations(const void* X, int x_dt, int64_t M, in
 /* The int8 MFMA contraction alone: acc [M,N] int32 = q [M,K] . Wq [N,K]^T,
  * with the same grid plan (including the K-split of the last wave of tiles)
  * as int8_mixed_linear. Workspace: w8dbg_int8_gemm_i32_workspace_size(M, N, K)
- * bytes on the current device (may be 0, then workspace may be NULL). */
+ * bytes on the current device (may be 0, then workspace may be NULL),
+ * zero-filled before first use (left zero by every call). */
 size_t w8dbg_int8_gemm_i32_workspace_size(int64_t M, int64_t N, int64_t K);
 w8_status w8dbg_int8_gemm_i32(const int8_t* q, const int8_t* Wq, int64_t M, int64_t N, int64_t K,
                               int32_t* acc, void* workspace, size_t workspace_bytes, void* stream);

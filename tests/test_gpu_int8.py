@@ -69,7 +69,9 @@ def test_weight_quantisation_bit_exact(case):
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: c.name)
-@pytest.mark.parametrize("t", [6.0, math.inf, 0.0, 2.0])
+# 6.001 and 1e-6 fall between representable values of both 16-bit formats;
+# 7e4 is above the largest finite f16
+@pytest.mark.parametrize("t", [6.0, math.inf, 0.0, 2.0, 6.001, 1e-6, 7e4])
 def test_activation_quantisation_bit_exact(case, t):
     announce("int8 act quant", case.name, t)
     xf = o.decode16(case.x_bits, case.x_dtype)
@@ -81,8 +83,8 @@ def test_activation_quantisation_bit_exact(case, t):
 
 
 def test_activation_quantisation_fixup_rows():
-    """Rows whose largest |x| <= t sits in a column that another row makes
-    an outlier column must be re-scaled without that column."""
+    """A row's scale ignores a column that another row makes an outlier
+    column, even when that column holds the row's largest |x| <= t."""
     rng = np.random.default_rng(40)
     x = rng.standard_normal((96, 512)).astype(np.float32)
     x[5, 100] = 7.5                   # column 100 becomes an outlier column
@@ -117,8 +119,8 @@ def test_activation_quantisation_long_rows(K):
 
 
 def test_outlier_set_larger_than_the_lds_list():
-    """t = 0 makes every non-zero column an outlier: 8192 of them, more than
-    the fix-up kernel lists in LDS, so its per-row fallback runs."""
+    """t = 0 makes every non-zero column an outlier: 8191 of them, more than
+    the code kernel lists in LDS, so its per-row gather fallback runs."""
     c = synth.random_linear(40, 8192, 24, seed=45, x_dtype="bf16")
     x = c.x_bits.copy()
     x[:, 77] = 0                                   # one all-zero column stays int8
@@ -181,6 +183,30 @@ def test_int8_mixed_linear_matches_oracle(case, out_dtype, t):
                                                                           "f32": torch.float32}[out_dtype])
     torch.cuda.synchronize()
     _check_outputs(y, ref["Y"], out_dtype, (case.name, t))
+
+
+def test_workspace_reuse_leaves_bookkeeping_clean():
+    """The outlier flags and split-K counters live in the workspace and every
+    call leaves them zero: reusing one workspace across calls with different
+    outlier sets (and a K-split GEMM) gives each call its own exact result."""
+    a = synth.random_linear(300, 8192, 520, seed=46, x_dtype="bf16", outlier_cols=5)
+    b = synth.random_linear(300, 8192, 520, seed=47, x_dtype="bf16", outlier_cols=2)
+    wq, sw, wq_ref, sw_ref = _quant_weights_both(a)
+    ws = w8.new_workspace(w8.int8_mixed_linear_workspace_size(300, 520, 8192))
+    announce("int8 workspace reuse")
+    for c in (a, b, a, b):
+        y = w8.int8_mixed_linear(dev16(c.x_bits, "bf16"), wq, sw, 6.0, torch.float32, workspace=ws)
+        ref = o.int8_mixed_linear(c.x_bits, "bf16", wq_ref, sw_ref, 6.0, "f32")
+        _check_outputs(y, ref["Y"], "f32", c.name)
+    # the bookkeeping is zero again after the calls: the outlier-column flags
+    # (K bytes) and the split-K counters (6 tiles), each region 256-byte
+    # aligned after q [M,K] and sx [M]
+    torch.cuda.synchronize()
+    up = lambda n: (n + 255) // 256 * 256
+    flags_off = up(300 * 8192) + up(4 * 300)
+    cnt_off = flags_off + up(8192)
+    assert not ws[flags_off:flags_off + 8192].any()
+    assert not ws[cnt_off:cnt_off + 4 * 6].any()
 
 
 def test_zero_row_gives_zero_output_row():

@@ -16,7 +16,7 @@ _DT = {torch.float16: _abi.W8_DT_F16, torch.bfloat16: _abi.W8_DT_BF16, torch.flo
 __all__ = [
     "quantize_weight_rowwise", "int8_mixed_linear", "fp8_w8a8_linear",
     "debug_int8_quantize_activations", "debug_int8_gemm_i32", "debug_fp8_quantize_activations",
-    "int8_mixed_linear_workspace_size", "fp8_w8a8_linear_workspace_size", "W8Error",
+    "int8_mixed_linear_workspace_size", "fp8_w8a8_linear_workspace_size", "new_workspace", "W8Error",
 ]
 
 
@@ -40,8 +40,14 @@ def _dt(t: torch.Tensor) -> int:
 
 
 def _workspace(nbytes: int, device) -> torch.Tensor:
-    # torch's allocator returns 256-byte aligned blocks
-    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    # torch's allocator returns 256-byte aligned blocks; the library needs the
+    # workspace zero-filled before first use (it leaves its bookkeeping zero)
+    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def new_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A workspace of `nbytes` for repeated calls (zero-filled, as required)."""
+    return _workspace(nbytes, device)
 
 
 def int8_mixed_linear_workspace_size(M: int, N: int, K: int) -> int:

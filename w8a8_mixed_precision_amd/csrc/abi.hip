@@ -1,6 +1,8 @@
 // C ABI of libw8mp: argument validation, workspace carve-up, kernel dispatch.
 // Declarations and contracts: include/w8mp.h.
+#include <algorithm>
 #include <cmath>
+#include <cstring>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -74,10 +76,9 @@ int cu_count() {
 }
 
 // Workspace layout of int8_mixed_linear (offsets from the 256-aligned base).
-// flags and cnt are adjacent so one clear covers both.
+// flags and cnt are the bookkeeping that every call leaves zero again.
 struct Int8Ws {
-  size_t q, sx, amax, flags, cnt, nO, O, XO, WO, part, total;
-  size_t clear_words;
+  size_t q, sx, flags, cnt, nO, O, XO, WO, part, total;
   w8::Int8GemmPlan plan;
 };
 
@@ -86,19 +87,39 @@ Int8Ws int8_layout(int64_t M, int64_t N, int64_t K) {
   w.plan = w8::plan_int8_gemm(M, N, K, cu_count());
   const size_t P = static_cast<size_t>((K + 31) / 32 * 32);  // worst case: every column is an outlier
   size_t off = 0;
-  w.q = off;    off = up(off + static_cast<size_t>(M) * K);
-  w.sx = off;   off = up(off + 4 * static_cast<size_t>(M));
-  w.amax = off; off = up(off + 4 * static_cast<size_t>(M));
+  w.q = off;     off = up(off + static_cast<size_t>(M) * K);
+  w.sx = off;    off = up(off + 4 * static_cast<size_t>(M));
   w.flags = off; off = up(off + static_cast<size_t>(K));
-  w.cnt = off;  off = up(off + 4 * static_cast<size_t>(w.plan.counters()));
-  w.clear_words = (off - w.flags) / 4;
-  w.nO = off;   off = up(off + 4);
-  w.O = off;    off = up(off + 4 * static_cast<size_t>(K));
-  w.XO = off;   off = up(off + 2 * static_cast<size_t>(M) * P);
-  w.WO = off;   off = up(off + 2 * static_cast<size_t>(N) * P);
-  w.part = off; off = up(off + w.plan.partial_bytes());
+  w.cnt = off;   off = up(off + 4 * static_cast<size_t>(w.plan.counters()));
+  w.nO = off;    off = up(off + 4);
+  w.O = off;     off = up(off + 4 * static_cast<size_t>(K));
+  w.XO = off;    off = up(off + 2 * static_cast<size_t>(M) * P);
+  w.WO = off;    off = up(off + 2 * static_cast<size_t>(N) * P);
+  w.part = off;  off = up(off + w.plan.partial_bytes());
   w.total = off;
   return w;
+}
+
+// Magnitude bits (bits & 0x7FFF) of the largest value of the 16-bit format
+// that is <= t: |x| > t exactly when x's magnitude bits exceed it.
+uint32_t threshold_bits(float t, bool bf16) {
+  if (bf16) {
+    uint32_t u;
+    std::memcpy(&u, &t, 4);
+    return std::min<uint32_t>(u >> 16, 0x7F80u);   // truncation = round toward zero for t >= 0
+  }
+  auto f16_value = [](uint32_t h) -> double {        // h: magnitude bits of a non-NaN half
+    const int e = static_cast<int>(h >> 10), m = static_cast<int>(h & 0x3FF);
+    if (e == 31) return INFINITY;
+    return e == 0 ? std::ldexp(static_cast<double>(m), -24) : std::ldexp(1024.0 + m, e - 25);
+  };
+  uint32_t lo = 0, hi = 0x7C00;                        // f16_value(lo) <= t always (t >= 0)
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi + 1) / 2;
+    if (f16_value(mid) <= static_cast<double>(t)) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
 }
 
 // Workspace of the int8 GEMM parity export: counters, then partials.
@@ -224,7 +245,7 @@ w8_status quantize_weight_rowwise(const void* W, int w_dt, int64_t N, int64_t K,
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = w_dt == W8_DT_BF16;
   if (fmt == W8_Q_INT8)
-    w8::launch_int8_rows(W, bf, N, (int)K, INFINITY, static_cast<int8_t*>(Wq), sw, nullptr, nullptr, true, s);
+    w8::launch_int8_rows(W, bf, N, (int)K, 0x7F80u, static_cast<int8_t*>(Wq), sw, nullptr, s);
   else
     w8::launch_fp8_rows(W, bf, N, (int)K, nullptr, static_cast<uint8_t*>(Wq), sw, 2, s);
   return check_launch("quantize_weight_rowwise");
@@ -261,7 +282,6 @@ w8_status int8_mixed_linear(const void* X, int x_dt, int64_t M, int64_t K, const
   const bool bf = x_dt == W8_DT_BF16;
   int8_t* q = at<int8_t>(workspace, L.q);
   float* sx = at<float>(workspace, L.sx);
-  int* amax = at<int>(workspace, L.amax);
   uint8_t* flags = at<uint8_t>(workspace, L.flags);
   int* nO = at<int>(workspace, L.nO);
   int* O = at<int>(workspace, L.O);
@@ -271,12 +291,13 @@ w8_status int8_mixed_linear(const void* X, int x_dt, int64_t M, int64_t K, const
   int* part = at<int>(workspace, L.part);
 
   mark(0, s);
-  w8::launch_clear(reinterpret_cast<uint32_t*>(flags), (int)L.clear_words, s);
-  w8::launch_int8_rows(X, bf, M, (int)K, threshold, q, sx, amax, flags, false, s);
+  const uint32_t tb = threshold_bits(threshold, bf);
+  w8::launch_int8_rows(X, bf, M, (int)K, tb, q, sx, flags, s);
   mark(1, s);
-  w8::launch_outlier_fixup(X, bf, M, (int)K, flags, q, sx, amax, O, nO, XO, Wq, N, WO, s);
+  w8::launch_outlier_fixup(X, bf, M, (int)K, tb, flags, q, sx, O, nO, XO, Wq, N, WO, s);
   mark(2, s);
-  w8::launch_int8_gemm(q, Wq, M, N, K, sx, sw, nO, XO, WO, bf, Y, y_dt == W8_DT_F16 ? 1 : 2, L.plan, part, cnt, s);
+  w8::launch_int8_gemm(q, Wq, M, N, K, sx, sw, nO, XO, WO, bf, Y, y_dt == W8_DT_F16 ? 1 : 2, L.plan, part, cnt,
+                       reinterpret_cast<uint32_t*>(flags), static_cast<int>(K / 4), s);
   mark(3, s);
   return check_launch("int8_mixed_linear");
 }
@@ -317,7 +338,7 @@ w8_status fp8_w8a8_linear(const void* X, int x_dt, int64_t M, int64_t K, const u
 
 size_t w8dbg_int8_quantize_activations_workspace_size(int64_t M, int64_t K) {
   if (M < 1 || K < 1) return 0;
-  return up(4 * static_cast<size_t>(M)) + up(static_cast<size_t>(K));
+  return up(static_cast<size_t>(K));
 }
 
 w8_status w8dbg_int8_quantize_activations(const void* X, int x_dt, int64_t M, int64_t K, float threshold, int8_t* q,
@@ -330,12 +351,12 @@ w8_status w8dbg_int8_quantize_activations(const void* X, int x_dt, int64_t M, in
   if (w8_status st = check_ws(workspace, workspace_bytes, need); st != W8_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = x_dt == W8_DT_BF16;
-  int* amax = at<int>(workspace, 0);
-  uint8_t* flags = at<uint8_t>(workspace, up(4 * static_cast<size_t>(M)));
-  w8::launch_clear(reinterpret_cast<uint32_t*>(flags), (int)(K / 4), s);
-  w8::launch_int8_rows(X, bf, M, (int)K, threshold, q, sx, amax, flags, false, s);
-  w8::launch_outlier_fixup(X, bf, M, (int)K, flags, q, sx, amax, outlier_idx, n_outliers, nullptr, nullptr, 0,
-                           nullptr, s);
+  uint8_t* flags = at<uint8_t>(workspace, 0);
+  const uint32_t tb = threshold_bits(threshold, bf);
+  w8::launch_int8_rows(X, bf, M, (int)K, tb, q, sx, flags, s);
+  w8::launch_outlier_fixup(X, bf, M, (int)K, tb, flags, q, sx, outlier_idx, n_outliers, nullptr, nullptr, 0, nullptr,
+                           s);
+  w8::launch_clear_words(reinterpret_cast<uint32_t*>(flags), static_cast<int>(K / 4), s);
   return check_launch("w8dbg_int8_quantize_activations");
 }
 
@@ -358,9 +379,8 @@ w8_status w8dbg_int8_gemm_i32(const int8_t* q, const int8_t* Wq, int64_t M, int6
   hipStream_t s = static_cast<hipStream_t>(stream);
   int* cnt = L.total > 0 ? at<int>(workspace, L.cnt) : nullptr;
   int* part = L.total > 0 ? at<int>(workspace, L.part) : nullptr;
-  if (L.plan.counters() > 0) w8::launch_clear(reinterpret_cast<uint32_t*>(cnt), L.plan.counters(), s);
   w8::launch_int8_gemm(q, Wq, M, N, K, nullptr, nullptr, nullptr, nullptr, nullptr, true, acc, 0, L.plan, part, cnt,
-                       s);
+                       nullptr, 0, s);
   return check_launch("w8dbg_int8_gemm_i32");
 }
 

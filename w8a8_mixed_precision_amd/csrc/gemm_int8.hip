@@ -256,7 +256,8 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm(const int8_t* __restrict__
                                                       const float* __restrict__ sw, const int* __restrict__ nO_ptr,
                                                       const uint16_t* __restrict__ XO,
                                                       const uint16_t* __restrict__ WO, void* __restrict__ Y,
-                                                      int tiles_m, int tiles_n) {
+                                                      int tiles_m, int tiles_n, uint32_t* __restrict__ clear,
+                                                      int clear_words) {
   __shared__ __attribute__((aligned(16))) int8_t lds[2][2][kBM * kBK];
   static_assert(sizeof(lds) >= kEpiLds, "epilogue LDS");
 
@@ -265,6 +266,8 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm(const int8_t* __restrict__
   const int m0 = tm * kBM, n0 = tn * kBN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  if (blockIdx.x == 0 && clear)                   // see k_int8_gemm_dma
+    for (int i = tid; i < clear_words; i += 256) clear[i] = 0u;
   EpiIn ein;
   epi_prefetch<MODE>(ein, M, N, m0, n0, wm, lane, sx, sw, nO_ptr);
 
@@ -411,9 +414,9 @@ __device__ __forceinline__ void mma_phase(const v4i (&fm)[8], v16i (&acc)[4][4],
 // dp_tiles blocks each own a whole 256x256 tile. The remaining blocks are
 // `split` K-slices of each of the R = (gridDim.x - dp_tiles) / split leftover
 // tiles: every slice writes its int32 partial sums to its own slot of `part`,
-// bumps the tile's arrival counter in `cnt` (zero on entry), and the last
-// slice to arrive adds the other slices' partials to its own and runs the
-// epilogue. Integer sums are exact in any order, so the result does not
+// bumps the tile's arrival counter in `cnt` (zero on entry, left zero on
+// exit), and the last slice to arrive adds the other slices' partials to its
+// own and runs the epilogue. Integer sums are exact in any order, so the result does not
 // depend on which slice arrives last. No block ever waits for another.
 constexpr int kPartInts = kBM * kBN;          // one 256x256 int32 partial
 
@@ -424,7 +427,8 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
                                                           const uint16_t* __restrict__ XO,
                                                           const uint16_t* __restrict__ WO, void* __restrict__ Y,
                                                           int tiles_m, int tiles_n, int dp_tiles, int split,
-                                                          int* __restrict__ part, int* __restrict__ cnt) {
+                                                          int* __restrict__ part, int* __restrict__ cnt,
+                                                          uint32_t* __restrict__ clear, int clear_words) {
   constexpr int kStage = 2 * kBM * kBK;       // A then B, 32 KB
   constexpr int kLoads = 8;                   // DMA instructions per wave per step
   __shared__ __attribute__((aligned(1024))) int8_t lds[S * kStage];
@@ -458,6 +462,10 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
   const int m0 = tm * kBM, n0 = tn * kBN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  // The quantisation pass before this kernel is complete, so its outlier-column
+  // mask can be cleared here for the next call.
+  if (blockIdx.x == 0 && clear)
+    for (int i = tid; i < clear_words; i += 256) clear[i] = 0u;
   EpiIn ein;
   epi_prefetch<MODE>(ein, M, N, m0, n0, wm, lane, sx, sw, nO_ptr);
 
@@ -546,6 +554,7 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
       *s_last = __hip_atomic_fetch_add(cnt + sk_tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == split - 1;
     __syncthreads();
     if (!*s_last) return;
+    if (tid == 0) cnt[sk_tile] = 0;               // every slice has arrived: leave the counter zero
     // one 32-row block at a time, so only its 64 accumulators leave the AGPRs
     // and 16 loads of 1 KB per wave are in flight
 #pragma unroll
@@ -611,17 +620,20 @@ Int8GemmPlan plan_int8_gemm(int64_t M, int64_t N, int64_t K, int cus) {
 // ---------------------------------------------------------------------------
 // mode: 0 int32 acc, 1 fp16 out, 2 fp32 out. `part` / `cnt` are needed when
 // plan.split > 1 (plan.sk_tiles * plan.split partials, plan.sk_tiles counters
-// that must be zero).
+// that must be zero; they are left zero). `clear` (may be null): clear_words
+// words that the kernel zeroes (the outlier-column mask of the pass before).
 void launch_int8_gemm(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t K, const float* sx,
                       const float* sw, const int* nO, const uint16_t* XO, const uint16_t* WO, bool xbf16,
-                      void* Y, int mode, const Int8GemmPlan& plan, int* part, int* cnt, hipStream_t s) {
+                      void* Y, int mode, const Int8GemmPlan& plan, int* part, int* cnt, uint32_t* clear,
+                      int clear_words, hipStream_t s) {
   const int tiles_m = plan.tiles_m, tiles_n = plan.tiles_n;
   const int m = (int)M, n = (int)N, k = (int)K;
   const dim3 block(256);
   if (K % kBK == 0) {
     constexpr int S = 4;
     const dim3 grid(plan.dp_tiles + plan.sk_tiles * plan.split);
-#define W8_GEMM_ARGS A, B, m, n, k, sx, sw, nO, XO, WO, Y, tiles_m, tiles_n, plan.dp_tiles, plan.split, part, cnt
+#define W8_GEMM_ARGS A, B, m, n, k, sx, sw, nO, XO, WO, Y, tiles_m, tiles_n, plan.dp_tiles, plan.split, part, cnt, \
+    clear, clear_words
     if (mode == 0) k_int8_gemm_dma<0, true, S><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
     else if (mode == 1 && xbf16) k_int8_gemm_dma<1, true, S><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
     else if (mode == 1) k_int8_gemm_dma<1, false, S><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
@@ -630,7 +642,7 @@ void launch_int8_gemm(const int8_t* A, const int8_t* B, int64_t M, int64_t N, in
 #undef W8_GEMM_ARGS
   } else {
     const dim3 grid(tiles_m * tiles_n);
-#define W8_GEMM_ARGS A, B, m, n, k, sx, sw, nO, XO, WO, Y, tiles_m, tiles_n
+#define W8_GEMM_ARGS A, B, m, n, k, sx, sw, nO, XO, WO, Y, tiles_m, tiles_n, clear, clear_words
     if (mode == 0) k_int8_gemm<0, true><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
     else if (mode == 1 && xbf16) k_int8_gemm<1, true><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
     else if (mode == 1) k_int8_gemm<1, false><<<grid, block, 0, s>>>(W8_GEMM_ARGS);

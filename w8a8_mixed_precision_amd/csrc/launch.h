@@ -16,18 +16,19 @@ struct Int8GemmPlan {
 };
 Int8GemmPlan plan_int8_gemm(int64_t M, int64_t N, int64_t K, int cus);
 
-void launch_clear(uint32_t* p, int n, hipStream_t s);
-void launch_int8_rows(const void* X, bool bf16, int64_t rows, int K, float t, int8_t* q, float* sx, int* amax_col,
-                      uint8_t* colflag, bool weight, hipStream_t s);
+void launch_int8_rows(const void* X, bool bf16, int64_t rows, int K, uint32_t tbits, int8_t* q, float* sx,
+                      uint8_t* flags, hipStream_t s);
 size_t outlier_fixup_lds_bytes(int K);
-void launch_outlier_fixup(const void* X, bool bf16, int64_t M, int K, const uint8_t* colflag, int8_t* q, float* sx,
-                          const int* amax_col, int* O, int* nO, uint16_t* XO, const int8_t* Wq, int64_t N,
+void launch_outlier_fixup(const void* X, bool bf16, int64_t M, int K, uint32_t tbits, const uint8_t* colflag,
+                          int8_t* q, float* sx, int* O, int* nO, uint16_t* XO, const int8_t* Wq, int64_t N,
                           uint16_t* WO, hipStream_t s);
+void launch_clear_words(uint32_t* p, int n, hipStream_t s);
 void launch_fp8_rows(const void* X, bool bf16, int64_t rows, int K, const float* act_scale, uint8_t* xq, float* sx,
                      int mode, hipStream_t s);
 void launch_int8_gemm(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t K, const float* sx,
                       const float* sw, const int* nO, const uint16_t* XO, const uint16_t* WO, bool xbf16, void* Y,
-                      int mode, const Int8GemmPlan& plan, int* part, int* cnt, hipStream_t s);
+                      int mode, const Int8GemmPlan& plan, int* part, int* cnt, uint32_t* clear, int clear_words,
+                      hipStream_t s);
 void launch_fp8_gemm(const uint8_t* A, const uint8_t* B, int64_t M, int64_t N, int64_t K, const float* sx,
                      const float* sw, void* Y, int ydt, hipStream_t s);
 

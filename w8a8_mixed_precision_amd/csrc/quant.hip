@@ -1,167 +1,203 @@
 // Row quantisation kernels of libw8mp (gfx950).
 //
-//  k_clear            zero the outlier-column flags
-//  k_int8_rows        one pass over a row: absmax over the elements with
-//                     |x| <= t and its column, outlier-column flags (|x| > t),
-//                     int8 codes with that provisional scale. With t = +inf it
-//                     is the rowwise weight quantiser.
-//  k_outlier_fixup    outlier list, zero codes in outlier columns, gather the
-//                     outlier columns of X and Wq for the 16-bit side product,
-//                     and redo the rare rows whose provisional absmax sat in an
-//                     outlier column.
-//  k_fp8_rows         per-row (or static) scale and E4M3 codes.
+//  k_int8_rows       one pass over each row: outlier-column flags (|x| > t),
+//                    the provisional scale s' = max |x| over the elements with
+//                    |x| <= t, and int8 codes with it. Without flags (t = inf)
+//                    it is the rowwise weight quantiser.
+//  k_outlier_fixup   the outlier set from the flags; zero the codes of the
+//                    outlier columns, gather those columns of X (XO) and of Wq
+//                    as 16-bit values (WO), and re-encode the rare rows whose
+//                    scale must change.
+//  k_fp8_rows        per-row (or static) scale and E4M3 codes.
 //
 // The LLM.int8 decomposition ("Image21-INT8" card, section "Quantization":
-// threshold 6.0, outliers in floating point): a row's scale must ignore every
-// column that is an outlier column in ANY row of the call. One pass cannot know
-// that set, so k_int8_rows takes the max over |x| <= t. That equals the true
-// scale unless the max sat in a column another row made an outlier;
-// k_outlier_fixup detects exactly those rows through the recorded column and
-// re-encodes them once the whole set is known.
+// threshold 6.0, outliers in floating point): a row's scale ignores every
+// column that is an outlier column in ANY row of the call. One pass cannot
+// know that set, so the row pass takes s' over |x| <= t. The true scale
+// differs from s' only when s' is reached in outlier columns alone; the
+// fix-up sees exactly those values when it gathers XO, so it re-encodes a row
+// when its largest gathered |x| <= t equals s'.
+//
+// Both 16-bit formats store a sign bit and a magnitude whose bit patterns
+// order like the magnitudes, so maxima and threshold tests run on packed
+// 16-bit integers (bits & 0x7FFF): |x| > t exactly when the magnitude bits
+// exceed those of the largest representable value <= t. Non-finite values
+// have the largest patterns: with a finite t they are outliers.
 #include "common.h"
 
 namespace w8 {
 
-// --------------------------------------------------------------------------
-__global__ void k_clear(uint32_t* __restrict__ p, int n) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+typedef short ss2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(us2, a), __builtin_bit_cast(us2, b)));
+}
+
+// per 16-bit half: 0xFFFF where the magnitude m exceeds t2's half, else 0
+// (t - m as a signed 16-bit difference is negative exactly then; both are
+// 15-bit magnitudes)
+__device__ __forceinline__ uint32_t pk_gt_mask(uint32_t m, uint32_t t2) {
+  const ss2 d = __builtin_bit_cast(ss2, t2) - __builtin_bit_cast(ss2, m);
+  return __builtin_bit_cast(uint32_t, static_cast<ss2>(d >> static_cast<short>(15)));
+}
+
+// 8 codes of one 16-byte chunk: q = rne(fl32(x * r)) as a byte. Adding
+// 1.5 * 2^23 rounds fl32(x * r) (|.| <= 127.x) to the nearest integer, ties
+// to even, and leaves it in the low mantissa bits. A row scale below
+// 127/FLT_MAX makes r = +inf: then every non-zero x saturates to +-127 and
+// zero stays 0. (Outlier elements, |x| > t, get arbitrary bytes here: the
+// fix-up zeroes every code of an outlier column.)
+template <bool BF16>
+__device__ __forceinline__ uint2 encode8(const uint4& v, float r) {
+#pragma clang fp contract(off)  // the product is rounded before the add: no FMA
+  float f[8];
+  unpack8<BF16>(v, f);
+  uint32_t b[8];
+  if (__builtin_isinf(r)) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) b[j] = f[j] > 0.0f ? 0x7Fu : (f[j] < 0.0f ? 0x81u : 0u);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p = f[j] * r;
+      b[j] = __float_as_uint(p + 12582912.0f) & 0xFFu;
+    }
+  }
+  return make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24), b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
+}
+
+// Packed maximum of the magnitudes <= t of one chunk; the columns of the
+// magnitudes > t get a flag byte of 1 (a plain store: many rows flag the same
+// few columns, and equal plain stores need no atomics).
+template <bool ACT>
+__device__ __forceinline__ uint32_t chunk_scan(const uint4& v, uint32_t t2, uint8_t* __restrict__ flags, int c) {
+  uint32_t w[4] = {v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu, v.z & 0x7FFF7FFFu, v.w & 0x7FFF7FFFu};
+  if constexpr (ACT) {
+    uint32_t gt[4], any = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      gt[i] = pk_gt_mask(w[i], t2);
+      any |= gt[i];
+      w[i] &= ~gt[i];
+    }
+    if (any) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (gt[i] & 0xFFFFu) flags[8 * c + 2 * i] = 1;
+        if (gt[i] >> 16) flags[8 * c + 2 * i + 1] = 1;
+      }
+    }
+  }
+  return pk_max_u16(pk_max_u16(w[0], w[1]), pk_max_u16(w[2], w[3]));
+}
+
+template <bool BF16>
+__device__ __forceinline__ float decode_mag(uint32_t bits) {
+  if constexpr (BF16) return __uint_as_float(bits << 16);
+  else return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+}
+
+template <bool BF16>
+__device__ __forceinline__ uint32_t mag_bits(float s) {   // s is a value of the 16-bit format
+  if constexpr (BF16) return __float_as_uint(s) >> 16;
+  else return __builtin_bit_cast(uint16_t, static_cast<_Float16>(s));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), off, 64)));
+  return v;
 }
 
 // --------------------------------------------------------------------------
-// Row pass, register-resident form: W waves per row (W = 1, 2, 4), each wave
-// covering a 4096-element slice, 8 chunks of 8 elements per lane; a block of
-// 256 threads therefore holds 4/W rows. With W == 1 the row reduction stays
-// inside one wave (no LDS, no barrier).
-//
-// Outlier columns are flagged with a plain byte store of 1 into colflag[k]
-// (cleared before the pass): many rows flag the same few columns, and equal
-// plain stores need no read-modify-write.
-template <bool BF16, int W, bool WEIGHT>
-__global__ __launch_bounds__(256) void k_int8_rows(const uint16_t* __restrict__ X, int64_t rows, int K, float t,
-                                                   int8_t* __restrict__ q, float* __restrict__ sx,
-                                                   int* __restrict__ amax_col, uint8_t* __restrict__ colflag) {
+// Row pass, register form (K <= 16384): W = ceil(K / 4096) waves per row, each
+// covering a 4096-column slice, 8 chunks of 8 elements per lane; a block of
+// 256 threads holds 4/W rows. With W == 1 the row reduction stays inside one
+// wave (no LDS, no barrier).
+template <bool BF16, int W, bool ACT>
+__global__ __launch_bounds__(256) void k_int8_rows(const uint16_t* __restrict__ X, int64_t rows, int K,
+                                                   uint32_t tbits, int8_t* __restrict__ q, float* __restrict__ sx,
+                                                   uint8_t* __restrict__ flags) {
   constexpr int kRows = 4 / W;
-  __shared__ MaxLoc red[4];
+  __shared__ uint32_t red[4];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * kRows + wave / W;
   const bool valid = row < rows;
   const int part = wave % W;
   const int nch = K >> 3;
-  const uint4* xr = reinterpret_cast<const uint4*>(X + (valid ? row : 0) * K);
-  uint2* qr = reinterpret_cast<uint2*>(q + (valid ? row : 0) * K);
-
+  const uint32_t t2 = tbits | (tbits << 16);
   uint4 v[8];
+  if (valid) {
+    const uint4* xr = reinterpret_cast<const uint4*>(X + row * K);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int c = part * 512 + lane + 64 * i;
-    if (valid && c < nch) v[i] = xr[c];
-  }
-  MaxLoc best{0.0f, -1};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int c = part * 512 + lane + 64 * i;
-    if (!(valid && c < nch)) continue;
-    float f[8];
-    unpack8<BF16>(v[i], f);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float a = fabsf(f[j]);
-      if (a > t) {
-        if (!WEIGHT) colflag[8 * c + j] = 1;
-      } else if (a > best.v) {
-        best.v = a;
-        best.k = 8 * c + j;
-      }
+    for (int i = 0; i < 8; ++i) {
+      const int c = part * 512 + lane + 64 * i;
+      if (c < nch) v[i] = xr[c];
     }
   }
-  best = wave_maxloc(best);
+  uint32_t mx = 0;
+  if (valid) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = part * 512 + lane + 64 * i;
+      if (c < nch) mx = pk_max_u16(mx, chunk_scan<ACT>(v[i], t2, flags, c));
+    }
+  }
+  mx = wave_max_u32(max(mx & 0xFFFFu, mx >> 16));
   if constexpr (W > 1) {
-    if (lane == 0) red[wave] = best;
+    if (lane == 0) red[wave] = mx;
     __syncthreads();
     const int w0 = (wave / W) * W;
-    best = red[w0];
 #pragma unroll
-    for (int w = 1; w < W; ++w) best = maxloc_pick(best, red[w0 + w]);
+    for (int w = 0; w < W; ++w) mx = max(mx, red[w0 + w]);
   }
-  const float r = 127.0f / best.v;  // IEEE division; +inf for an all-zero row
+  if (!valid) return;
+  const float s = decode_mag<BF16>(mx);
+  const float r = s > 0.0f ? 127.0f / s : 0.0f;   // IEEE division; an all-zero row codes to 0
+  uint2* qr = reinterpret_cast<uint2*>(q + row * K);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int c = part * 512 + lane + 64 * i;
-    if (!(valid && c < nch)) continue;
-    float f[8];
-    unpack8<BF16>(v[i], f);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int code = (fabsf(f[j]) > t) ? 0 : absmax_code(f[j], r);
-      const uint32_t b = static_cast<uint32_t>(code) & 0xFFu;
-      if (j < 4) lo |= b << (8 * j);
-      else hi |= b << (8 * (j - 4));
-    }
-    qr[c] = make_uint2(lo, hi);
+    if (c < nch) qr[c] = encode8<BF16>(v[i], r);
   }
-  if (valid && part == 0 && lane == 0) {
-    sx[row] = best.v;
-    if (!WEIGHT) amax_col[row] = best.k;
-  }
+  if (part == 0 && lane == 0) sx[row] = s;
 }
 
 // Row pass, streaming form for K > 16384: one block per row, two passes.
-template <bool BF16, bool WEIGHT>
-__global__ __launch_bounds__(256) void k_int8_rows_long(const uint16_t* __restrict__ X, int K, float t,
+template <bool BF16, bool ACT>
+__global__ __launch_bounds__(256) void k_int8_rows_long(const uint16_t* __restrict__ X, int K, uint32_t tbits,
                                                         int8_t* __restrict__ q, float* __restrict__ sx,
-                                                        int* __restrict__ amax_col, uint8_t* __restrict__ colflag) {
-  __shared__ MaxLoc red[4];
+                                                        uint8_t* __restrict__ flags) {
+  __shared__ uint32_t red[4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t row = blockIdx.x;
   const int nch = K >> 3;
+  const uint32_t t2 = tbits | (tbits << 16);
   const uint4* xr = reinterpret_cast<const uint4*>(X + row * K);
+  uint32_t mx = 0;
+#pragma unroll 4
+  for (int c = threadIdx.x; c < nch; c += 256) mx = pk_max_u16(mx, chunk_scan<ACT>(xr[c], t2, flags, c));
+  mx = wave_max_u32(max(mx & 0xFFFFu, mx >> 16));
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  mx = max(max(red[0], red[1]), max(red[2], red[3]));
+  const float s = decode_mag<BF16>(mx);
+  const float r = s > 0.0f ? 127.0f / s : 0.0f;
   uint2* qr = reinterpret_cast<uint2*>(q + row * K);
-  MaxLoc best{0.0f, -1};
 #pragma unroll 4
-  for (int c = threadIdx.x; c < nch; c += 256) {
-    float f[8];
-    unpack8<BF16>(xr[c], f);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float a = fabsf(f[j]);
-      if (a > t) {
-        if (!WEIGHT) colflag[8 * c + j] = 1;
-      } else if (a > best.v) {
-        best.v = a;
-        best.k = 8 * c + j;
-      }
-    }
-  }
-  const MaxLoc b = block_maxloc256(best, red);
-  const float r = 127.0f / b.v;
-#pragma unroll 4
-  for (int c = threadIdx.x; c < nch; c += 256) {
-    float f[8];
-    unpack8<BF16>(xr[c], f);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int code = (fabsf(f[j]) > t) ? 0 : absmax_code(f[j], r);
-      const uint32_t bb = static_cast<uint32_t>(code) & 0xFFu;
-      if (j < 4) lo |= bb << (8 * j);
-      else hi |= bb << (8 * (j - 4));
-    }
-    qr[c] = make_uint2(lo, hi);
-  }
-  if (threadIdx.x == 0) {
-    sx[row] = b.v;
-    if (!WEIGHT) amax_col[row] = b.k;
-  }
+  for (int c = threadIdx.x; c < nch; c += 256) qr[c] = encode8<BF16>(xr[c], r);
+  if (threadIdx.x == 0) sx[row] = s;
 }
 
 // --------------------------------------------------------------------------
 // Block roles: blocks [0, xblocks) take kFixRows rows of X each; the rest take
 // kFixRows rows of Wq each (only when WO != nullptr). Every block rebuilds the
-// ascending outlier list from the mask in LDS (prefix of popcounts), then
-// spreads (row, outlier slot) pairs over all threads, so the scattered loads
-// of a block are all in flight together. Dynamic LDS: mask words, their
-// exclusive popcount prefix, and the outlier list (up to kOcap entries; a
-// larger set takes the per-row loop at the end).
+// ascending outlier list from the flags (a bit mask and its popcount prefix in
+// LDS), then spreads (row, outlier slot) pairs over all threads, so the
+// scattered loads of a block are all in flight together. Dynamic LDS: mask
+// words, their exclusive popcount prefix, and the outlier list (up to kOcap
+// entries; a larger set takes the per-row loops).
 constexpr int kFixRows = 64;
 constexpr int kOcap = 4096;
 
@@ -171,14 +207,14 @@ size_t outlier_fixup_lds_bytes(int K) {
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_outlier_fixup(
-    const uint16_t* __restrict__ X, int M, int K, const uint8_t* __restrict__ colflag,
-    int8_t* __restrict__ q, float* __restrict__ sx, const int* __restrict__ amax_col,
-    int* __restrict__ O, int* __restrict__ nO_out, uint16_t* __restrict__ XO,
-    const int8_t* __restrict__ Wq, int N, uint16_t* __restrict__ WO, int xblocks) {
+    const uint16_t* __restrict__ X, int M, int K, uint32_t tbits, const uint8_t* __restrict__ colflag,
+    int8_t* __restrict__ q, float* __restrict__ sx, int* __restrict__ O, int* __restrict__ nO_out,
+    uint16_t* __restrict__ XO, const int8_t* __restrict__ Wq, int N, uint16_t* __restrict__ WO, int xblocks) {
   extern __shared__ uint32_t smem[];
   __shared__ int scan_tot[4];
   __shared__ float fred[4];
-  __shared__ int sredo[kFixRows];
+  __shared__ uint32_t somax[kFixRows];       // per row: largest gathered magnitude <= t
+  __shared__ float ssx[kFixRows];            // per row: provisional scale
   const int nwords = (K + 31) >> 5;
   uint32_t* smask = smem;
   int* spre = reinterpret_cast<int*>(smem + nwords);
@@ -193,9 +229,8 @@ __global__ __launch_bounds__(256) void k_outlier_fixup(
     const int w = base + tid;
     uint32_t bits = 0u;
     if (w < nwords) {
-      const uint4* fp = reinterpret_cast<const uint4*>(colflag + 32 * w);  // K % 32 == 0 region
-      const int avail = min(32, K - 32 * w);
-      if (avail == 32) {
+      if (32 * w + 32 <= K) {
+        const uint4* fp = reinterpret_cast<const uint4*>(colflag + 32 * w);
         const uint4 a = fp[0], b = fp[1];
         const uint32_t wd[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
@@ -203,10 +238,10 @@ __global__ __launch_bounds__(256) void k_outlier_fixup(
 #pragma unroll
           for (int j = 0; j < 4; ++j) bits |= ((wd[i] >> (8 * j)) & 1u) << (4 * i + j);
       } else {
-        for (int j = 0; j < avail; ++j) bits |= static_cast<uint32_t>(colflag[32 * w + j] & 1u) << j;
+        for (int j = 0; 32 * w + j < K; ++j) bits |= static_cast<uint32_t>(colflag[32 * w + j] & 1u) << j;
       }
+      smask[w] = bits;
     }
-    if (w < nwords) smask[w] = bits;
     const int v = __popc(bits);
     int incl = v;
 #pragma unroll
@@ -240,27 +275,30 @@ __global__ __launch_bounds__(256) void k_outlier_fixup(
   }
   if (blockIdx.x == 0 && tid == 0) *nO_out = nO;
   if (nO == 0) return;
+  if (tid < kFixRows) somax[tid] = 0u;
+  const bool xblock = static_cast<int>(blockIdx.x) < xblocks;
+  if (xblock && tid < kFixRows && static_cast<int>(blockIdx.x) * kFixRows + tid < M)
+    ssx[tid] = sx[blockIdx.x * kFixRows + tid];
   __syncthreads();
 
-  if (static_cast<int>(blockIdx.x) < xblocks) {
+  if (xblock) {
     const int r0 = blockIdx.x * kFixRows;
     const int rows = min(kFixRows, M - r0);
-    if (tid < rows) {
-      const int c = amax_col[r0 + tid];
-      sredo[tid] = (c >= 0) && ((smask[c >> 5] >> (c & 31)) & 1u);
-    }
+    // zero the codes of the outlier columns, gather X's outlier columns, and
+    // note per row the largest gathered magnitude <= t
+    auto take = [&](int r, int64_t m, int k) -> uint16_t {
+      const uint16_t v = X[m * K + k];
+      q[m * K + k] = 0;
+      const uint32_t mag = v & 0x7FFFu;
+      if (mag <= tbits) atomicMax(&somax[r], mag);
+      return v;
+    };
     if (listed) {
-      // zero the codes of the outlier columns and gather X's outlier columns
 #pragma unroll 8
       for (int idx = tid; idx < rows * P; idx += 256) {
         const int r = idx / P, j = idx - r * P;
         const int64_t m = r0 + r;
-        uint16_t v = 0;
-        if (j < nO) {
-          const int k = sO[j];
-          v = X[m * K + k];
-          q[m * K + k] = 0;
-        }
+        const uint16_t v = (j < nO) ? take(r, m, sO[j]) : uint16_t(0);
         if (XO) XO[m * P + j] = v;
       }
     } else {
@@ -272,8 +310,8 @@ __global__ __launch_bounds__(256) void k_outlier_fixup(
           while (bits) {
             const int b = __ffs(bits) - 1;
             bits &= bits - 1;
-            q[m * K + 32 * w + b] = 0;
-            if (XO) XO[m * P + j] = X[m * K + 32 * w + b];
+            const uint16_t v = take(r, m, 32 * w + b);
+            if (XO) XO[m * P + j] = v;
             ++j;
           }
         }
@@ -282,10 +320,12 @@ __global__ __launch_bounds__(256) void k_outlier_fixup(
       }
     }
     __syncthreads();
-    // Rows whose provisional absmax sat in an outlier column: recompute the
-    // scale over the non-outlier columns and re-encode the whole row.
+    // A row whose provisional scale is also reached in an outlier column may
+    // have a smaller true scale: recompute it over the non-outlier columns
+    // and re-encode the whole row.
     for (int r = 0; r < rows; ++r) {
-      if (!sredo[r]) continue;
+      const float sp = ssx[r];
+      if (!(sp > 0.0f) || somax[r] != mag_bits<BF16>(sp)) continue;   // block-uniform
       const int64_t rowoff = static_cast<int64_t>(r0 + r) * K;
       const uint4* xr = reinterpret_cast<const uint4*>(X + rowoff);
       uint2* qr = reinterpret_cast<uint2*>(q + rowoff);
@@ -433,53 +473,56 @@ __global__ __launch_bounds__(256) void k_fp8_rows(const uint16_t* __restrict__ X
 // --------------------------------------------------------------------------
 // Host-side launchers (called by the ABI layer after validation).
 
-template <bool BF16, bool WEIGHT>
-static void launch_int8_rows_t(const uint16_t* X, int64_t rows, int K, float t, int8_t* q, float* sx,
-                               int* amax_col, uint8_t* colflag, hipStream_t s) {
+__global__ void k_clear_words(uint32_t* __restrict__ p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+void launch_clear_words(uint32_t* p, int n, hipStream_t s) {
+  k_clear_words<<<dim3((n + 255) / 256 < 64 ? (n + 255) / 256 : 64), dim3(256), 0, s>>>(p, n);
+}
+
+template <bool BF16, bool ACT>
+static void launch_int8_rows_t(const uint16_t* X, int64_t rows, int K, uint32_t tbits, int8_t* q, float* sx,
+                               uint8_t* flags, hipStream_t s) {
   const dim3 block(256);
   auto blocks = [&](int rpb) { return dim3(static_cast<unsigned>((rows + rpb - 1) / rpb)); };
   if (K <= 4096)
-    k_int8_rows<BF16, 1, WEIGHT><<<blocks(4), block, 0, s>>>(X, rows, K, t, q, sx, amax_col, colflag);
+    k_int8_rows<BF16, 1, ACT><<<blocks(4), block, 0, s>>>(X, rows, K, tbits, q, sx, flags);
   else if (K <= 8192)
-    k_int8_rows<BF16, 2, WEIGHT><<<blocks(2), block, 0, s>>>(X, rows, K, t, q, sx, amax_col, colflag);
+    k_int8_rows<BF16, 2, ACT><<<blocks(2), block, 0, s>>>(X, rows, K, tbits, q, sx, flags);
   else if (K <= 16384)
-    k_int8_rows<BF16, 4, WEIGHT><<<blocks(1), block, 0, s>>>(X, rows, K, t, q, sx, amax_col, colflag);
+    k_int8_rows<BF16, 4, ACT><<<blocks(1), block, 0, s>>>(X, rows, K, tbits, q, sx, flags);
   else
-    k_int8_rows_long<BF16, WEIGHT><<<dim3(static_cast<unsigned>(rows)), block, 0, s>>>(X, K, t, q, sx, amax_col,
-                                                                                       colflag);
+    k_int8_rows_long<BF16, ACT><<<dim3(static_cast<unsigned>(rows)), block, 0, s>>>(X, K, tbits, q, sx, flags);
 }
 
-void launch_clear(uint32_t* p, int n, hipStream_t s) {
-  const int blocks = (n + 255) / 256 < 64 ? (n + 255) / 256 : 64;
-  k_clear<<<dim3(blocks > 0 ? blocks : 1), dim3(256), 0, s>>>(p, n);
-}
-
-void launch_int8_rows(const void* X, bool bf16, int64_t rows, int K, float t, int8_t* q, float* sx,
-                      int* amax_col, uint8_t* colflag, bool weight, hipStream_t s) {
+// flags == nullptr: weight pass (no threshold)
+void launch_int8_rows(const void* X, bool bf16, int64_t rows, int K, uint32_t tbits, int8_t* q, float* sx,
+                      uint8_t* flags, hipStream_t s) {
   const uint16_t* x = static_cast<const uint16_t*>(X);
   if (bf16) {
-    if (weight) launch_int8_rows_t<true, true>(x, rows, K, t, q, sx, amax_col, colflag, s);
-    else launch_int8_rows_t<true, false>(x, rows, K, t, q, sx, amax_col, colflag, s);
+    if (flags) launch_int8_rows_t<true, true>(x, rows, K, tbits, q, sx, flags, s);
+    else launch_int8_rows_t<true, false>(x, rows, K, tbits, q, sx, flags, s);
   } else {
-    if (weight) launch_int8_rows_t<false, true>(x, rows, K, t, q, sx, amax_col, colflag, s);
-    else launch_int8_rows_t<false, false>(x, rows, K, t, q, sx, amax_col, colflag, s);
+    if (flags) launch_int8_rows_t<false, true>(x, rows, K, tbits, q, sx, flags, s);
+    else launch_int8_rows_t<false, false>(x, rows, K, tbits, q, sx, flags, s);
   }
 }
 
-void launch_outlier_fixup(const void* X, bool bf16, int64_t M, int K, const uint8_t* colflag, int8_t* q,
-                          float* sx, const int* amax_col, int* O, int* nO, uint16_t* XO,
-                          const int8_t* Wq, int64_t N, uint16_t* WO, hipStream_t s) {
+void launch_outlier_fixup(const void* X, bool bf16, int64_t M, int K, uint32_t tbits, const uint8_t* colflag,
+                          int8_t* q, float* sx, int* O, int* nO, uint16_t* XO, const int8_t* Wq, int64_t N,
+                          uint16_t* WO, hipStream_t s) {
   const int xblocks = static_cast<int>((M + kFixRows - 1) / kFixRows);
   const int wblocks = WO ? static_cast<int>((N + kFixRows - 1) / kFixRows) : 0;
   const size_t lds = outlier_fixup_lds_bytes(K);
   const uint16_t* x = static_cast<const uint16_t*>(X);
   const dim3 grid(xblocks + wblocks), block(256);
   if (bf16)
-    k_outlier_fixup<true><<<grid, block, lds, s>>>(x, (int)M, K, colflag, q, sx, amax_col, O, nO, XO, Wq,
-                                                   (int)N, WO, xblocks);
+    k_outlier_fixup<true><<<grid, block, lds, s>>>(x, (int)M, K, tbits, colflag, q, sx, O, nO, XO, Wq, (int)N, WO,
+                                                   xblocks);
   else
-    k_outlier_fixup<false><<<grid, block, lds, s>>>(x, (int)M, K, colflag, q, sx, amax_col, O, nO, XO, Wq,
-                                                    (int)N, WO, xblocks);
+    k_outlier_fixup<false><<<grid, block, lds, s>>>(x, (int)M, K, tbits, colflag, q, sx, O, nO, XO, Wq, (int)N, WO,
+                                                    xblocks);
 }
 
 template <bool BF16, int MODE>
