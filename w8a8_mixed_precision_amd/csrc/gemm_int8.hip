@@ -40,7 +40,7 @@ __device__ __forceinline__ int swz64(int row, int ch) { return row * kBK + ((ch 
 // over the 8 XCDs; renumber so each XCD gets a contiguous range of ids, then
 // walk tiles in groups of kGroupM tile-rows so blocks that run together on one
 // XCD share A rows and B columns in that XCD's L2.
-constexpr int kXcds = 8, kGroupM = 4;
+constexpr int kXcds = 8, kGroupM = 8;
 
 __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   const int per = (nblocks + kXcds - 1) / kXcds;
@@ -98,6 +98,16 @@ __device__ __forceinline__ void mma_step(const int8_t* sa, const int8_t* sb, v16
 constexpr int kStgPitch = 256 + 16;             // staged row: 256 bytes + pad
 constexpr int kStgWave = 32 * kStgPitch;        // one wave's 32 staged rows
 constexpr int kEpiLds = 1024 + 4 * kStgWave;    // column scales + 4 staging areas
+
+// Lanes of a wave exchange data through the staging area. The hardware runs a
+// wave's LDS accesses in issue order, but the compiler reasons per thread and
+// may move one lane's read ahead of another lane's write (or a write ahead of
+// another lane's read) to the same bytes: a wavefront-scope fence keeps the
+// program order, at no cost in instructions.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
 
 template <int MODE, bool XBF16>
 __device__ __forceinline__ void epilogue(v16i (&acc)[4][4], int M, int N, int m0, int n0, int wm, int wn, int lane,
@@ -164,9 +174,8 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[4][4], int M, int N, int m0
           }
         }
       }
-      // staging -> global: 8 instructions of 4 rows x 16 chunks of 16 bytes.
-      // LDS accesses of one wave complete in issue order, so no wait is needed
-      // between the staging writes and these reads, nor before the next pass.
+      // staging -> global: 8 instructions of 4 rows x 16 chunks of 16 bytes
+      wave_lds_fence();
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const int r = 4 * t + (lane >> 4), ch = lane & 15;
@@ -189,6 +198,7 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[4][4], int M, int N, int m0
           }
         }
       }
+      wave_lds_fence();                         // staging reads done before the next pass writes
     }
   }
 }
