@@ -26,6 +26,7 @@ if ROOT not in sys.path:
 
 METRIC = "int8 mixed-precision linear TOPS at 1024^2 DiT shapes; % of MFMA peak"
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, published
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 THRESHOLD = 6.0
 
@@ -65,6 +66,72 @@ def cpu_baseline(cases, rows: int):
                       f"{ops / 1e9:.1f} G ops in {dt:.1f} s"}
 
 
+def fp8_layers(torch, w8, steps: int) -> dict:
+    """FP8-E4M3 W8A8 text-encoder linears at 512 tokens, per layer and
+    activation-scale mode: whole-call, row-pass and GEMM time from the HIP-event
+    hook, GEMM TFLOP/s and the GEMM's fraction of its roofline
+    max(2MNK / 5.0 PFLOP/s, bytes / 8 TB/s), bytes = M K + N K + 2 M N."""
+    import synth
+
+    res = {}
+    for layer in synth.FP8_TEXT_LAYERS:
+        c = synth.fp8_text_encoder(layer)
+        x = _dev16(c.x_bits, torch)
+        wq, sw = w8.quantize_weight_rowwise(_dev16(c.w_bits, torch), "fp8")
+        y = torch.empty((c.M, c.N), dtype=torch.bfloat16, device="cuda")
+        ws = w8.new_workspace(w8.fp8_w8a8_linear_workspace_size(c.M, c.N, c.K))
+        # static per-tensor input scale: "max" calibration on an independent draw
+        xcal = _dev16(c.extra["x_cal_bits"], torch).float()
+        scale = (xcal.abs().max() / 448.0).reshape(1).contiguous()
+        for mode, act in (("dynamic", None), ("static", scale)):
+            for _ in range(3):
+                w8.fp8_w8a8_linear(x, wq, sw, act, out=y, workspace=ws)
+            w8.profile_start(steps)
+            for _ in range(steps):
+                w8.fp8_w8a8_linear(x, wq, sw, act, out=y, workspace=ws)
+            ms, n = w8.profile_stop()
+            gemm_us = ms[2] / n * 1e3
+            rows_us = ms[0] / n * 1e3
+            gbytes = c.M * c.K + c.N * c.K + 2 * c.M * c.N
+            t_roof = max(c.ops / (PEAK_FP8_TFLOPS * 1e12), gbytes / (PEAK_HBM_GBS * 1e9)) * 1e6
+            res[f"{layer}_{c.M}x{c.K}x{c.N}_{mode}"] = {
+                "call_us": round(sum(ms) / n * 1e3, 2),
+                "act_quant_us": round(rows_us, 2),
+                "act_quant_GBs": round(3 * c.M * c.K / (rows_us * 1e-6) / 1e9, 1),
+                "gemm_us": round(gemm_us, 2),
+                "gemm_tflops": round(c.ops / (gemm_us * 1e-6) / 1e12, 1),
+                "gemm_roofline_us": round(t_roof, 2),
+                "gemm_roofline_frac": round(t_roof / gemm_us, 3),
+            }
+            print(f"[bench] fp8 {layer} {mode}: {res[f'{layer}_{c.M}x{c.K}x{c.N}_{mode}']}", file=sys.stderr, flush=True)
+    return res
+
+
+def weight_quant(torch, w8, cases, steps: int) -> dict:
+    """Offline weight quantisation (int8 rowwise and FP8 per-channel) on the
+    step's weights: time per call from events on the stream the kernels run on
+    (torch's current stream), and HBM GB/s against 3 N K bytes (read 16-bit W,
+    write 8-bit codes)."""
+    res = {}
+    for c in cases:
+        w = _dev16(c.w_bits, torch)
+        for fmt in ("int8", "fp8"):
+            w8.quantize_weight_rowwise(w, fmt)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                w8.quantize_weight_rowwise(w, fmt)
+            e1.record()
+            e1.synchronize()
+            us = e0.elapsed_time(e1) / steps * 1e3
+            gbs = 3 * c.N * c.K / (us * 1e-6) / 1e9
+            res[f"{fmt}_{c.N}x{c.K}"] = {"us": round(us, 2), "GBs": round(gbs, 1),
+                                         "hbm_frac": round(gbs / PEAK_HBM_GBS, 3)}
+        del w
+    print(f"[bench] weight quantisation: {res}", file=sys.stderr, flush=True)
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -72,6 +139,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-rows", type=int, default=4352, help="token rows per shape for the oracle baseline (4352 = the whole step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 W8A8 text-encoder layer timings")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the sharding design is "
@@ -179,6 +247,13 @@ def main() -> int:
         },
         "per_shape": per_shape,
     }
+    if not args.no_fp8:
+        out["weight_quant"] = weight_quant(torch, w8, cases, max(1, args.steps // 4))
+        out["fp8_w8a8"] = {
+            "workload": "FP8-E4M3 W8A8 text-encoder linears, 512 tokens, hidden 4096, bf16 in/out, "
+                        "per-channel weight scale; dynamic per-token and static per-tensor activation scale",
+            "layers": fp8_layers(torch, w8, args.steps),
+        }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cases, args.cpu_rows)

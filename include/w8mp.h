@@ -126,10 +126,16 @@ w8_status int8_mixed_linear(const void* X, int x_dt, int64_t M, int64_t K,
  *              Otherwise a DEVICE pointer to one fp32 static per-tensor input
  *              scale (must be finite and >= 0; 0 gives zero codes).
  *   Y          [M,N] bf16, f16 or f32, device.
- *   workspace  at least fp8_w8a8_linear_workspace_size() bytes.
+ *   workspace  device memory of at least fp8_w8a8_linear_workspace_size()
+ *              bytes (which depends on M, N, K and the current device's
+ *              compute-unit count), 256-byte aligned, zero-filled before its
+ *              first use. Every call leaves its bookkeeping (split-K arrival
+ *              counters) zero again, so a workspace is reused without
+ *              clearing; the rest of its contents are scratch.
  * Codes: xq[m,k] = E4M3FN(fl32(X[m,k] / sx[m])) (saturating), all zero when
  * sx[m] = 0. Y[m,n] = sx[m] * sw[n] * sum_k xq*wq, fp32 accumulation on FP8
- * MFMA, rounded to nearest even into Y.
+ * MFMA, rounded to nearest even into Y. Results are bitwise reproducible for
+ * a given device: split-K partial sums are added in a fixed order.
  * Requires M, N >= 1, 16 <= K <= 65536, K % 16 == 0.
  */
 size_t fp8_w8a8_linear_workspace_size(int64_t M, int64_t N, int64_t K);
@@ -172,6 +178,19 @@ w8_status w8dbg_int8_gemm_i32(const int8_t* q, const int8_t* Wq, int64_t M, int6
 w8_status w8dbg_fp8_quantize_activations(const void* X, int x_dt, int64_t M, int64_t K,
                                          const float* act_scale, uint8_t* xq, float* sx,
                                          void* stream);
+
+/* The GEMM half of fp8_w8a8_linear on given codes and scales: Y [M,N] =
+ * sx[m] * sw[n] * sum_k xq[m,k] * Wq8[n,k] (E4M3 codes, fp32 accumulation).
+ * split = 0: the output tiling and K-slicing fp8_w8a8_linear would choose
+ * (tile ignored). split >= 1: output tiles of tile x tile (128 or 256; 0 means
+ * 256), each with its K range cut into `split` slices; needs K % 64 == 0 and
+ * split <= K / 64 (else W8_ERR_UNSUPPORTED) unless split is 1. Workspace:
+ * w8dbg_fp8_gemm_workspace_size(M, N, K, split, tile) bytes (0 means none,
+ * then workspace may be NULL), zero-filled before first use (left zero). */
+size_t w8dbg_fp8_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int split, int tile);
+w8_status w8dbg_fp8_gemm(const uint8_t* xq, const float* sx, const uint8_t* Wq8, const float* sw,
+                         int64_t M, int64_t N, int64_t K, int split, int tile, void* Y, int y_dt,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Measurement hook (process-wide, for benchmarks; not for concurrent use).

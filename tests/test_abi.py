@@ -125,6 +125,20 @@ def test_debug_exports_reject():
         _abi.W8_ERR_INVALID_ARGUMENT
     assert lib.w8dbg_int8_quantize_activations(A, _abi.W8_DT_BF16, 4, 32, 6.0, A, A, A, A, A, 1,
                                                None) == _abi.W8_ERR_WORKSPACE
+    f8 = lib.w8dbg_fp8_gemm
+    bf = _abi.W8_DT_BF16
+    assert f8(None, A, A, A, 4, 4, 64, 1, 0, A, bf, None, 0, None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert f8(A, A, A, A, 4, 4, 64, -1, 0, A, bf, None, 0, None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert f8(A, A, A, A, 4, 4, 64, 1, 64, A, bf, None, 0, None) == _abi.W8_ERR_INVALID_ARGUMENT   # tile
+    assert f8(A, A, A, A, 4, 4, 80, 2, 0, A, bf, None, 0, None) == _abi.W8_ERR_UNSUPPORTED     # K % 64 != 0
+    assert f8(A, A, A, A, 4, 4, 80, 1, 128, A, bf, None, 0, None) == _abi.W8_ERR_UNSUPPORTED   # K % 64 != 0
+    assert f8(A, A, A, A, 4, 4, 128, 3, 0, A, bf, None, 0, None) == _abi.W8_ERR_UNSUPPORTED    # > K / 64 slices
+    assert f8(A, A, A, A, 4, 4, 64, 1, 0, A, 9, None, 0, None) == _abi.W8_ERR_UNSUPPORTED
+    need = lib.w8dbg_fp8_gemm_workspace_size(4, 4, 128, 2, 256)
+    assert need >= 2 * 256 * 256 * 4                                                        # two fp32 partials
+    assert lib.w8dbg_fp8_gemm_workspace_size(4, 4, 128, 2, 128) >= 2 * 128 * 128 * 4
+    assert f8(A, A, A, A, 4, 4, 128, 2, 256, A, bf, A, need - 256, None) == _abi.W8_ERR_WORKSPACE
+    assert lib.w8dbg_fp8_gemm_workspace_size(4, 4, 128, 1, 0) == 0
 
 
 def test_binding_refuses_without_library(monkeypatch, tmp_path):

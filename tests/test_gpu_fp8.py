@@ -116,3 +116,69 @@ def test_fp8_text_encoder_full_size(layer, static):
     ref = o.fp8_w8a8_linear(c.x_bits, "bf16", wq_ref, sw_ref, s, "bf16")
     y = w8.fp8_w8a8_linear(x, wq, sw, sp, torch.bfloat16)
     _check(y, ref["Y"], "bf16", c.name)
+
+
+def _random_codes(rng, shape):
+    """E4M3 codes without the two NaN patterns (0x7F, 0xFF)."""
+    c = rng.integers(0, 254, size=shape, dtype=np.int64)
+    c = np.where(c >= 0x7F, c + 1, c)                       # skip 0x7F
+    return c.astype(np.uint8)
+
+
+# (M, K, N): K % 64 == 0 takes the pipelined kernel; ragged M and N, a single
+# row, one tile, and grids of 1..6 tiles that the K-slicing spreads over.
+GEMM_SHAPES = [(300, 4096, 520), (77, 2048, 300), (512, 1024, 256), (1, 640, 16), (257, 4160, 513),
+               (512, 12288, 1024)]
+
+
+@pytest.mark.parametrize("shape", GEMM_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("tile,split", [(0, 0), (256, 1), (256, 2), (256, 3), (256, 5), (256, 8),
+                                        (128, 1), (128, 2), (128, 3), (128, 8)])
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+def test_fp8_gemm_tiling_and_k_slicing_match_oracle(shape, tile, split, out_dtype):
+    """The FP8 GEMM for both block sizes and several K-slicings against the
+    exact contraction; the sliced result is bitwise the same on a repeated call
+    (fixed summation order) and the bookkeeping counters are left zero."""
+    M, K, N = shape
+    if split > K // 64:
+        pytest.skip("more slices than K steps")
+    rng = np.random.default_rng(7000 + M + K + N + split + tile)
+    xq, wq = _random_codes(rng, (M, K)), _random_codes(rng, (N, K))
+    sx = rng.uniform(0.5, 2.0, size=M).astype(np.float32) / np.float32(448.0)
+    sw = rng.uniform(0.5, 2.0, size=N).astype(np.float32) / np.float32(448.0)
+    acc = o.fp8_contract(xq, wq)
+    want = o.stored_to_f64(o.round_output(sx[:, None].astype(np.float64) * sw[None, :] * acc, out_dtype), out_dtype)
+    announce("fp8 gemm", shape, "tile", tile, "split", split, out_dtype)
+    t = [torch.from_numpy(a).cuda() for a in (xq, sx, wq, sw)]
+    n_ws = w8.debug_fp8_gemm_workspace_size(M, N, K, split, tile)
+    ws = w8.new_workspace(max(n_ws, 256))
+    y1 = w8.debug_fp8_gemm(*t, split=split, tile=tile, out_dtype=OUT[out_dtype], workspace=ws)
+    y2 = w8.debug_fp8_gemm(*t, split=split, tile=tile, out_dtype=OUT[out_dtype], workspace=ws)
+    torch.cuda.synchronize()
+    got = o.stored_to_f64(host_stored(y1, out_dtype), out_dtype)
+    e, er = rel_fro(got, want), row_rel_fro(got, want).max()
+    assert e <= TOL[out_dtype] and er <= TOL[out_dtype], (e, er)
+    assert torch.equal(y1.view(torch.uint8), y2.view(torch.uint8))
+    if n_ws:
+        assert int(ws[:256].view(torch.int32).abs().sum().item()) == 0     # counters left zero
+
+
+def test_fp8_linear_workspace_reuse_is_bitwise_stable():
+    """Two text-encoder calls (K-sliced on this grid) through one workspace give
+    identical bits, and the split-K counters are zero again after each."""
+    c = synth.fp8_text_encoder("q")
+    wq, sw = w8.quantize_weight_rowwise(dev16(c.w_bits, "bf16"), "fp8")
+    x = dev16(c.x_bits, "bf16")
+    n = w8.fp8_w8a8_linear_workspace_size(c.M, c.N, c.K)
+    ws = w8.new_workspace(n)
+    announce("fp8 workspace reuse", c.name)
+    y1 = w8.fp8_w8a8_linear(x, wq, sw, None, torch.bfloat16, workspace=ws).clone()
+    y2 = w8.fp8_w8a8_linear(x, wq, sw, None, torch.bfloat16, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    cnt_off = _up(c.M * c.K) + _up(4 * c.M)                   # codes, scales, then the counters
+    assert int(ws[cnt_off:cnt_off + 256].view(torch.int32).abs().sum().item()) == 0
+
+
+def _up(x: int) -> int:
+    return (x + 255) // 256 * 256

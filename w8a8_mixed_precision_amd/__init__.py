@@ -15,7 +15,7 @@ _DT = {torch.float16: _abi.W8_DT_F16, torch.bfloat16: _abi.W8_DT_BF16, torch.flo
 
 __all__ = [
     "quantize_weight_rowwise", "int8_mixed_linear", "fp8_w8a8_linear",
-    "debug_int8_quantize_activations", "debug_int8_gemm_i32", "debug_fp8_quantize_activations",
+    "debug_int8_quantize_activations", "debug_int8_gemm_i32", "debug_fp8_quantize_activations", "debug_fp8_gemm",
     "int8_mixed_linear_workspace_size", "fp8_w8a8_linear_workspace_size", "new_workspace", "W8Error",
 ]
 
@@ -165,3 +165,26 @@ def debug_fp8_quantize_activations(x: torch.Tensor, act_scale: torch.Tensor | No
     _abi.check(lib().w8dbg_fp8_quantize_activations(x.data_ptr(), _dt(x), M, K, sp, xq.data_ptr(), sx.data_ptr(),
                                                     _stream(x)))
     return xq, sx
+
+
+def debug_fp8_gemm(xq: torch.Tensor, sx: torch.Tensor, wq8: torch.Tensor, sw: torch.Tensor, split: int = 0,
+                   tile: int = 0, out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Y [M,N] = sx[m] sw[n] (xq . wq8^T) on the FP8 MFMA kernel: `tile` x
+    `tile` output blocks with `split` K-slices each (split 0: the linear's own
+    choice of both)."""
+    _dev(xq, "xq"), _dev(sx, "sx"), _dev(wq8, "wq8"), _dev(sw, "sw")
+    M, K = xq.shape
+    N = wq8.shape[0]
+    y = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=xq.device)
+    n_ws = debug_fp8_gemm_workspace_size(M, N, K, split, tile)
+    ws = workspace if workspace is not None else (_workspace(n_ws, xq.device) if n_ws else None)
+    _abi.check(lib().w8dbg_fp8_gemm(xq.data_ptr(), sx.data_ptr(), wq8.data_ptr(), sw.data_ptr(), M, N, K,
+                                    int(split), int(tile), y.data_ptr(), _dt(y),
+                                    ws.data_ptr() if ws is not None else None,
+                                    ws.numel() if ws is not None else 0, _stream(xq)))
+    return y
+
+
+def debug_fp8_gemm_workspace_size(M: int, N: int, K: int, split: int = 0, tile: int = 0) -> int:
+    return int(lib().w8dbg_fp8_gemm_workspace_size(M, N, K, int(split), int(tile)))

@@ -79,7 +79,7 @@ int cu_count() {
 // flags and cnt are the bookkeeping that every call leaves zero again.
 struct Int8Ws {
   size_t q, sx, flags, cnt, nO, O, XO, WO, part, total;
-  w8::Int8GemmPlan plan;
+  w8::GemmPlan plan;
 };
 
 Int8Ws int8_layout(int64_t M, int64_t N, int64_t K) {
@@ -125,7 +125,7 @@ uint32_t threshold_bits(float t, bool bf16) {
 // Workspace of the int8 GEMM parity export: counters, then partials.
 struct GemmWs {
   size_t cnt, part, total;
-  w8::Int8GemmPlan plan;
+  w8::GemmPlan plan;
 };
 
 GemmWs gemm_layout(int64_t M, int64_t N, int64_t K) {
@@ -138,17 +138,30 @@ GemmWs gemm_layout(int64_t M, int64_t N, int64_t K) {
   return w;
 }
 
+// Workspace layout of fp8_w8a8_linear: codes, scales, then the GEMM's split-K
+// counters (left zero by every call) and partials.
 struct Fp8Ws {
-  size_t xq, sx, total;
+  size_t xq, sx, cnt, part, total;
+  w8::GemmPlan plan;
 };
 
-Fp8Ws fp8_layout(int64_t M, int64_t K) {
+Fp8Ws fp8_layout(int64_t M, int64_t N, int64_t K) {
   Fp8Ws w{};
+  w.plan = w8::plan_fp8_gemm(M, N, K, cu_count());
   size_t off = 0;
-  w.xq = off; off = up(off + static_cast<size_t>(M) * K);
-  w.sx = off; off = up(off + 4 * static_cast<size_t>(M));
+  w.xq = off;   off = up(off + static_cast<size_t>(M) * K);
+  w.sx = off;   off = up(off + 4 * static_cast<size_t>(M));
+  w.cnt = off;  off = up(off + 4 * static_cast<size_t>(w.plan.counters()));
+  w.part = off; off = up(off + w.plan.partial_bytes());
   w.total = off;
   return w;
+}
+
+// Grid of the FP8 GEMM parity export: the linear's own plan (split 0) or the
+// given block size and K-slicing.
+w8::GemmPlan fp8_debug_plan(int64_t M, int64_t N, int64_t K, int split, int tile) {
+  return split == 0 ? w8::plan_fp8_gemm(M, N, K, cu_count())
+                    : w8::plan_fp8_gemm_split(M, N, split, tile == 128 ? 128 : 256);
 }
 
 template <typename T>
@@ -303,9 +316,8 @@ w8_status int8_mixed_linear(const void* X, int x_dt, int64_t M, int64_t K, const
 }
 
 size_t fp8_w8a8_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
-  (void)N;
-  if (M < 1 || K < 1) return 0;
-  return fp8_layout(M, K).total;
+  if (M < 1 || N < 1 || K < 1) return 0;
+  return fp8_layout(M, N, K).total;
 }
 
 w8_status fp8_w8a8_linear(const void* X, int x_dt, int64_t M, int64_t K, const uint8_t* Wq8, const float* sw,
@@ -319,7 +331,7 @@ w8_status fp8_w8a8_linear(const void* X, int x_dt, int64_t M, int64_t K, const u
   W8_REQUIRE(N >= 1 && N <= kMaxDim, W8_ERR_INVALID_ARGUMENT, "N must be in [1, 2^31)");
   W8_REQUIRE(aligned16(X) && aligned16(Wq8) && aligned16(sw) && aligned16(Y), W8_ERR_INVALID_ARGUMENT,
              "pointers must be 16-byte aligned");
-  const Fp8Ws L = fp8_layout(M, K);
+  const Fp8Ws L = fp8_layout(M, N, K);
   if (w8_status st = check_ws(workspace, workspace_bytes, L.total); st != W8_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* xq = at<uint8_t>(workspace, L.xq);
@@ -329,7 +341,8 @@ w8_status fp8_w8a8_linear(const void* X, int x_dt, int64_t M, int64_t K, const u
   mark(1, s);
   mark(2, s);
   const int ydt = y_dt == W8_DT_BF16 ? 0 : (y_dt == W8_DT_F16 ? 1 : 2);
-  w8::launch_fp8_gemm(xq, Wq8, M, N, K, sx, sw, Y, ydt, s);
+  w8::launch_fp8_gemm(xq, Wq8, M, N, K, sx, sw, Y, ydt, L.plan, at<float>(workspace, L.part),
+                      at<int>(workspace, L.cnt), s);
   mark(3, s);
   return check_launch("fp8_w8a8_linear");
 }
@@ -382,6 +395,39 @@ w8_status w8dbg_int8_gemm_i32(const int8_t* q, const int8_t* Wq, int64_t M, int6
   w8::launch_int8_gemm(q, Wq, M, N, K, nullptr, nullptr, nullptr, nullptr, nullptr, true, acc, 0, L.plan, part, cnt,
                        nullptr, 0, s);
   return check_launch("w8dbg_int8_gemm_i32");
+}
+
+size_t w8dbg_fp8_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int split, int tile) {
+  if (M < 1 || N < 1 || K < 1 || split < 0) return 0;
+  const w8::GemmPlan plan = fp8_debug_plan(M, N, K, split, tile);
+  return up(4 * static_cast<size_t>(plan.counters())) + up(plan.partial_bytes());
+}
+
+w8_status w8dbg_fp8_gemm(const uint8_t* xq, const float* sx, const uint8_t* Wq8, const float* sw, int64_t M,
+                         int64_t N, int64_t K, int split, int tile, void* Y, int y_dt, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  W8_REQUIRE(xq && sx && Wq8 && sw && Y, W8_ERR_INVALID_ARGUMENT, "null pointer argument");
+  W8_REQUIRE(y_dt == W8_DT_BF16 || y_dt == W8_DT_F16 || y_dt == W8_DT_F32, W8_ERR_UNSUPPORTED,
+             "Y must be bf16, f16 or f32");
+  if (w8_status st = check_mk(M, K, 65536); st != W8_OK) return st;
+  W8_REQUIRE(N >= 1 && N <= kMaxDim, W8_ERR_INVALID_ARGUMENT, "N must be in [1, 2^31)");
+  W8_REQUIRE(split >= 0, W8_ERR_INVALID_ARGUMENT, "split must be >= 0");
+  W8_REQUIRE(tile == 0 || tile == 128 || tile == 256, W8_ERR_INVALID_ARGUMENT, "tile must be 0, 128 or 256");
+  W8_REQUIRE(split == 0 || tile == 0 || K % 64 == 0, W8_ERR_UNSUPPORTED, "a tile size needs K %% 64 == 0");
+  W8_REQUIRE(split <= 1 || (K % 64 == 0 && split <= K / 64), W8_ERR_UNSUPPORTED,
+             "split %d needs K %% 64 == 0 and at most K / 64 slices", split);
+  W8_REQUIRE(aligned16(xq) && aligned16(sx) && aligned16(Wq8) && aligned16(sw) && aligned16(Y),
+             W8_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+  const w8::GemmPlan plan = fp8_debug_plan(M, N, K, split, tile);
+  const size_t cnt_bytes = up(4 * static_cast<size_t>(plan.counters()));
+  const size_t need = cnt_bytes + up(plan.partial_bytes());
+  if (need > 0) {
+    if (w8_status st = check_ws(workspace, workspace_bytes, need); st != W8_OK) return st;
+  }
+  const int ydt = y_dt == W8_DT_BF16 ? 0 : (y_dt == W8_DT_F16 ? 1 : 2);
+  w8::launch_fp8_gemm(xq, Wq8, M, N, K, sx, sw, Y, ydt, plan, need > 0 ? at<float>(workspace, cnt_bytes) : nullptr,
+                      need > 0 ? at<int>(workspace, 0) : nullptr, static_cast<hipStream_t>(stream));
+  return check_launch("w8dbg_fp8_gemm");
 }
 
 w8_status w8dbg_fp8_quantize_activations(const void* X, int x_dt, int64_t M, int64_t K, const float* act_scale,

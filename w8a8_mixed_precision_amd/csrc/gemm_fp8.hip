@@ -8,13 +8,22 @@
 // per-tensor input scale arrives as the same sx vector ("Darkstar ... ModelOpt
 // FP8" card, section "Precision map").
 //
-// The contraction uses v_mfma_scale_f32_16x16x128_f8f6f4 with both block
-// scales at 2^0 (E8M0 code 127) and format E4M3 on both sides: 16x16 output,
-// K = 128 per instruction, 32 bytes of each operand per lane.
-// Tiling: 256 threads = 4 waves as 2x2, block tile 128x128, K step 128 bytes,
-// each wave 64x64 = 4x4 MFMA tiles. LDS: 2 stages x (16 + 16) KB, 16-byte XOR
-// swizzle over the 8 chunks of a 128-byte row.
-#include "common.h"
+// Main kernel (K % 64 == 0): the int8 GEMM's LDS-DMA ring and swizzle
+// (tile.h) with 256x256 or 128x128 blocks, and v_mfma_scale_f32_32x32x64_f8f6f4 (both block scales 2^0,
+// E8M0 code 127; format E4M3 on both sides), which issues at the full fp8 rate
+// on gfx950 (the 16x16x128 form does not). One MFMA covers a whole 64-byte K
+// step: lane l supplies row (l & 31) and the 32 bytes made of 16-byte chunks
+// (l >> 5) and 2 + (l >> 5) of the step, the same chunks for both operands, so
+// every k of the step is multiplied exactly once.
+//
+// Text-encoder shapes have few tokens (M = 512), so their grids use the
+// smaller blocks and may be split along K to occupy the chip; the slices' fp32
+// partials are summed in slice order 0, 1, ..., whichever slice adds them up,
+// so results do not depend on arrival order.
+#include <algorithm>
+
+#include "launch.h"
+#include "tile.h"
 
 namespace w8 {
 
@@ -22,12 +31,14 @@ constexpr int kFBM = 128, kFBN = 128, kFBK = 128;
 
 __device__ __forceinline__ int swz128(int row, int ch) { return row * kFBK + ((ch ^ ((row >> 1) & 7)) << 4); }
 
-// YDT: 0 bf16, 1 fp16, 2 fp32
+// General kernel (any K % 16 == 0): register-staged loads with zero fill past
+// K, two LDS stages, 128x128 tiles of v_mfma_scale_f32_16x16x128_f8f6f4.
+// YDT: 0 bf16, 1 fp16, 2 fp32.
 template <int YDT>
-__global__ __launch_bounds__(256, 2) void k_fp8_gemm(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
-                                                     int M, int N, int K, const float* __restrict__ sx,
-                                                     const float* __restrict__ sw, void* __restrict__ Y,
-                                                     int tiles_m) {
+__global__ __launch_bounds__(256, 2) void k_fp8_gemm_any(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
+                                                         int M, int N, int K, const float* __restrict__ sx,
+                                                         const float* __restrict__ sw, void* __restrict__ Y,
+                                                         int tiles_m) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kFBM * kFBK];
   const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
   const int m0 = tm * kFBM, n0 = tn * kFBN;
@@ -124,15 +135,398 @@ __global__ __launch_bounds__(256, 2) void k_fp8_gemm(const uint8_t* __restrict__
   }
 }
 
-// ydt: 0 bf16, 1 fp16, 2 fp32
+
+// ---------------------------------------------------------------------------
+// Pipelined kernel (K % 64 == 0). Block = 2x2 waves; each wave owns WT x WT
+// MFMA tiles of 32x32 outputs: WT = 4 gives 256x256 blocks (one per CU: 256
+// accumulator registers per wave), WT = 2 gives 128x128 blocks (two per CU),
+// which suit grids with few 256x256 tiles (the 512-token text encoder).
+template <int WT>
+struct Fp8Tile {
+  static constexpr int BM = 64 * WT;                  // block rows = block columns
+  static constexpr int kStage = 2 * BM * kBK;         // one K step of A then B in LDS
+  static constexpr int kLoads = 2 * WT;               // DMA instructions per wave per step
+  static constexpr int kFrags = 2 * WT;               // 32-byte fragments per wave per step
+  static constexpr int kMfma = WT * WT;               // MFMAs per wave per step
+  static constexpr int kChunks = 4 * WT * WT;         // 16-byte accumulator chunks per lane
+  static constexpr int kPartBytes = BM * BM * 4;      // one fp32 partial
+};
+
+// The two builtins of the K loop behind plain (non-template) wrappers: called
+// with template-dependent arguments directly, the host compilation pass drops
+// the kernel templates that use them.
+__device__ __forceinline__ void lds_dma16(const uint8_t* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+__device__ __forceinline__ v16f mfma_fp8(v8i a, v8i b, v16f c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// One fragment: both 16-byte halves of a 32x64-byte operand block for this
+// lane (chunks fh and 2 + fh of its row).
+__device__ __forceinline__ v8i frag_pair(const uint8_t* base, int row, int fh) {
+  const v4i lo = *reinterpret_cast<const v4i*>(base + swz64(row, fh));
+  const v4i hi = *reinterpret_cast<const v4i*>(base + swz64(row, 2 + fh));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// LDS row of fragment f of wave (wm, wn): f < WT are A row blocks, the rest B.
+template <int WT>
+__device__ __forceinline__ const uint8_t* frag_base(const uint8_t* slot, int f) {
+  return f < WT ? slot : slot + Fp8Tile<WT>::BM * kBK;
+}
+template <int WT>
+__device__ __forceinline__ int frag_row(int f, int wm, int wn, int fr) {
+  return f < WT ? wm * 32 * WT + f * 32 + fr : wn * 32 * WT + (f - WT) * 32 + fr;
+}
+
+// One K step: the wave's WT*WT MFMAs on fragments fc, while the next step's
+// fragments are read into fn (in the order the next step consumes them: A0,
+// B0.., A1..) and the step's DMAs of a future K step go out, both spread evenly
+// over the MFMAs; sched_barrier keeps that interleaving.
+template <int WT>
+__device__ __forceinline__ void fp8_step(const v8i* fc, v8i* fn, v16f (*acc)[WT], const uint8_t* sn, int wm, int wn,
+                                         int lane, const uint8_t* const* a_src, const uint8_t* const* b_src, int k0,
+                                         uint8_t* st, int wave) {
+  using T = Fp8Tile<WT>;
+  const int fr = lane & 31, fh = lane >> 5;
+  constexpr int kReads = 2 * T::kFrags;
+  v4i lo;
+#pragma unroll
+  for (int t = 0; t < T::kMfma; ++t) {
+    const int i = t / WT, j = t % WT;
+    acc[i][j] = mfma_fp8(fc[WT + j], fc[i], acc[i][j]);
+#pragma unroll
+    for (int q = t * kReads / T::kMfma; q < (t + 1) * kReads / T::kMfma; ++q) {
+      const int o = q >> 1;                              // o-th fragment in consumption order
+      const int f = o == 0 ? 0 : (o <= WT ? WT + o - 1 : o - WT);
+      const uint8_t* base = frag_base<WT>(sn, f);
+      const int row = frag_row<WT>(f, wm, wn, fr);
+      if ((q & 1) == 0) {
+        lo = *reinterpret_cast<const v4i*>(base + swz64(row, fh));
+      } else {
+        const v4i hi = *reinterpret_cast<const v4i*>(base + swz64(row, 2 + fh));
+        fn[f] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    }
+#pragma unroll
+    for (int d = t * T::kLoads / T::kMfma; d < (t + 1) * T::kLoads / T::kMfma; ++d) {
+      if (d < WT)
+        lds_dma16(a_src[d] + k0, st + (wave * WT + d) * 1024);
+      else
+        lds_dma16(b_src[d - WT] + k0, st + T::BM * kBK + (wave * WT + d - WT) * 1024);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// DMA of K-step kt into its ring slot; past the last step the load repeats the
+// last step into the slot just retired (read by no later step), so every step
+// issues the same number of loads and one constant wait fits all.
+template <int WT, int S>
+__device__ __forceinline__ void fp8_issue(uint8_t* lds, int kt, int nk, const uint8_t* const* a_src,
+                                          const uint8_t* const* b_src, int wave) {
+  using T = Fp8Tile<WT>;
+  uint8_t* st = lds + (kt % S) * T::kStage;
+  const int k0 = min(kt, nk - 1) * kBK;
+#pragma unroll
+  for (int i = 0; i < WT; ++i) {
+    lds_dma16(a_src[i] + k0, st + (wave * WT + i) * 1024);
+    lds_dma16(b_src[i] + k0, st + T::BM * kBK + (wave * WT + i) * 1024);
+  }
+}
+
+// K step kt of the loop: wait until step kt+1 has landed everywhere and every
+// wave has read step kt's fragments (so its slot can be refilled with step
+// kt+S), then multiply step kt while reading step kt+1's fragments. The last
+// step runs the same code: its reads of the following slot (in the ring, never
+// used) and its repeat DMA of the last step into its own, retired slot are
+// harmless, and one loop body keeps register use at the loop's.
+template <int WT, int S>
+__device__ __forceinline__ void fp8_body(const v8i* fc, v8i* fn, v16f (*acc)[WT], uint8_t* lds, int kt, int nk,
+                                         int wm, int wn, int lane, const uint8_t* const* a_src,
+                                         const uint8_t* const* b_src, int wave) {
+  using T = Fp8Tile<WT>;
+  wait_lgkmcnt<0>();
+  wait_vmcnt<(S - 2) * T::kLoads>();
+  block_barrier();
+  fp8_step<WT>(fc, fn, acc, lds + ((kt + 1) % S) * T::kStage, wm, wn, lane, a_src, b_src, min(kt + S, nk - 1) * kBK,
+               lds + (kt % S) * T::kStage, wave);
+}
+
+// YDT: 0 bf16, 1 fp16, 2 fp32. Grid and split-K protocol as in the int8
+// kernel: blocks below dp_tiles own whole tiles; the rest are `split` K-slices
+// of each of R = (gridDim.x - dp_tiles) / split tiles. Each slice writes its
+// fp32 partial to its own slot of `part`, bumps the tile's counter in `cnt`
+// (zero on entry, left zero), and the last to arrive sums all slices' partials
+// in slice order and runs the epilogue.
+template <int YDT, int S, int WT>
+__global__ __launch_bounds__(256, 4 / WT) void k_fp8_gemm_dma(const uint8_t* __restrict__ A,
+                                                              const uint8_t* __restrict__ B, int M, int N, int K,
+                                                              const float* __restrict__ sx,
+                                                              const float* __restrict__ sw, void* __restrict__ Y,
+                                                              int tiles_m, int tiles_n, int dp_tiles, int split,
+                                                              float* __restrict__ part, int* __restrict__ cnt) {
+  using T = Fp8Tile<WT>;
+  constexpr int BM = T::BM;
+  // One LDS object only (a second one would make the compiler put a full vmcnt
+  // wait before every LDS read of the K loop); the arrival flag lives in the
+  // ring past the epilogue's area.
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[S * T::kStage];
+  static_assert(sizeof(lds) >= kEpiLds + 4, "epilogue LDS and arrival flag");
+  int* const s_last = reinterpret_cast<int*>(lds + kEpiLds);
+
+  const int nk_all = K / kBK;
+  int tm, tn, kb = 0, ke = nk_all;
+  int slot = -1, sk_tile = 0, piece = 0, R = 0;
+  if (static_cast<int>(blockIdx.x) < dp_tiles) {
+    tile_coords(blockIdx.x, dp_tiles, tiles_m, tiles_n, tm, tn);
+  } else {
+    // slice-major per XCD: the blocks of one XCD share a K range
+    const int nu = gridDim.x - dp_tiles;
+    const int v = xcd_remap(blockIdx.x - dp_tiles, nu);
+    R = nu / split;
+    piece = v / R;
+    sk_tile = v % R;
+    slot = v;
+    group_tile(dp_tiles + sk_tile, tiles_m, tiles_n, tm, tn);
+    kb = piece * nk_all / split;
+    ke = (piece + 1) * nk_all / split;
+  }
+  const int m0 = tm * BM, n0 = tn * BM;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int fr = lane & 31, fh = lane >> 5;
+  // epilogue inputs, fetched now so their latency hides under the K loop
+  float rsx[WT];
+#pragma unroll
+  for (int i = 0; i < WT; ++i) rsx[i] = sx[min(m0 + wm * 32 * WT + 32 * i + fr, M - 1)];
+  const float my_sw = sw[min(n0 + (tid & (BM - 1)), N - 1)];
+
+  // DMA source of this lane for load instruction i of each operand: tile row
+  // r = wave*16*WT + 16*i + lane/4 lands in LDS slot (lane & 3) of that row,
+  // which holds logical 16-byte chunk (lane & 3) ^ swz_term(r).
+  const uint8_t* a_src[WT];
+  const uint8_t* b_src[WT];
+#pragma unroll
+  for (int i = 0; i < WT; ++i) {
+    const int r = wave * 16 * WT + 16 * i + (lane >> 2);
+    const int ch = (lane & 3) ^ swz_term(r);
+    a_src[i] = A + static_cast<int64_t>(min(m0 + r, M - 1)) * K + kb * kBK + ch * 16;
+    b_src[i] = B + static_cast<int64_t>(min(n0 + r, N - 1)) * K + kb * kBK + ch * 16;
+  }
+  const int nk = ke - kb;
+
+  v16f acc[WT][WT];
+#pragma unroll
+  for (int i = 0; i < WT; ++i)
+#pragma unroll
+    for (int j = 0; j < WT; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  for (int s = 0; s < S; ++s) fp8_issue<WT, S>(lds, s, nk, a_src, b_src, wave);
+  wait_vmcnt<(S - 1) * T::kLoads>();            // step 0 landed (this wave)
+  block_barrier();                              // ... for every wave
+  v8i fa[2 * WT], fb[2 * WT];
+#pragma unroll
+  for (int f = 0; f < 2 * WT; ++f) fa[f] = frag_pair(frag_base<WT>(lds, f), frag_row<WT>(f, wm, wn, fr), fh);
+
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    fp8_body<WT, S>(fa, fb, acc, lds, kt, nk, wm, wn, lane, a_src, b_src, wave);
+    fp8_body<WT, S>(fb, fa, acc, lds, kt + 1, nk, wm, wn, lane, a_src, b_src, wave);
+  }
+  if (kt < nk) fp8_body<WT, S>(fa, fb, acc, lds, kt, nk, wm, wn, lane, a_src, b_src, wave);
+  wait_lgkmcnt<0>();
+  wait_vmcnt<0>();                              // retire the trailing repeat loads
+  block_barrier();                              // every wave is done with the ring
+
+  if (slot >= 0) {
+    // partial layout: 16-byte chunk c of wave w's accumulators at byte
+    // ((w * kChunks + c) * 64 + lane) * 16: every access is 1 KB contiguous
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int lane_off = (wv * T::kChunks * 64 + lane) * 16;
+    const __amdgpu_buffer_rsrc_t mine = partial_rsrc(part, slot, T::kPartBytes);
+#pragma unroll
+    for (int i = 0; i < WT; ++i)
+#pragma unroll
+      for (int j = 0; j < WT; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = (i * WT + j) * 4 + q;
+          const v4f v{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), mine, lane_off + c * 1024, 0, kSc1);
+        }
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's partial is visible
+    __syncthreads();                                        // ... and every wave's
+    if (tid == 0)
+      *s_last = __hip_atomic_fetch_add(cnt + sk_tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == split - 1;
+    __syncthreads();
+    if (!*s_last) return;
+    if (tid == 0) cnt[sk_tile] = 0;             // every slice has arrived: leave the counter zero
+    // Sum all slices' partials in slice order (this slice's own included, read
+    // back from its slot: summing from registers instead makes the compiler
+    // spill), one 32-row block at a time, 4*WT loads of 1 KB per wave in flight.
+#pragma unroll
+    for (int i = 0; i < WT; ++i) {
+      for (int p = 0; p < split; ++p) {
+        const __amdgpu_buffer_rsrc_t src = partial_rsrc(part, p * R + sk_tile, T::kPartBytes);
+        v4f w[4 * WT];
+#pragma unroll
+        for (int t = 0; t < 4 * WT; ++t)
+          w[t] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                                             src, lane_off + (i * 4 * WT + t) * 1024, 0, kSc1));
+#pragma unroll
+        for (int t = 0; t < 4 * WT; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[i][t >> 2][4 * (t & 3) + e] = p == 0 ? w[t][e] : acc[i][t >> 2][4 * (t & 3) + e] + w[t][e];
+      }
+    }
+  }
+
+  // Epilogue: Y = acc * sx[m] * sw[n], rounded to the output type, staged
+  // through LDS a 32-row block at a time (element r of tile (i, j) of a lane is
+  // row m0 + wm*32*WT + 32i + (lane&31), column n0 + wn*32*WT + 32j + 8(r>>2)
+  // + 4(lane>>5) + (r&3): the Wq fragment is the MFMA's first operand).
+  float* scol = reinterpret_cast<float*>(lds);
+  if (tid < BM) scol[tid] = my_sw;
+  __syncthreads();
+  constexpr int EB = YDT == 2 ? 4 : 2;          // bytes per output element
+  constexpr int ROWB = 32 * WT * EB;            // bytes of one output row of the wave's tile
+  constexpr int H = ROWB > 256 ? ROWB / 256 : 1;   // staging passes per 32-row block
+  constexpr int PJ = WT / H;                    // 32-column tiles per pass
+  constexpr int RB = 32 * PJ * EB;              // staged row bytes: 256 or 128
+  const bool vec = (static_cast<int64_t>(N) * EB) % 16 == 0;
+  char* const stg = reinterpret_cast<char*>(lds) + 1024 + wave * kStgWave;
+  char* const y = static_cast<char*>(Y);
+#pragma unroll
+  for (int i = 0; i < WT; ++i) {
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+#pragma unroll
+      for (int jj = 0; jj < PJ; ++jj) {
+        const int j = h * PJ + jj;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          char* dst = stg + fr * kStgPitch + (32 * jj + 8 * g + 4 * fh) * EB;
+          const v4f cs = *reinterpret_cast<const v4f*>(scol + wn * 32 * WT + 32 * j + 8 * g + 4 * fh);
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] * rsx[i] * cs[e];
+          if constexpr (YDT == 0) {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16),
+                                                        bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16));
+          } else if constexpr (YDT == 1) {
+            const uint32_t lo = f32_to_f16_bits(v[0]) | (static_cast<uint32_t>(f32_to_f16_bits(v[1])) << 16);
+            const uint32_t hi = f32_to_f16_bits(v[2]) | (static_cast<uint32_t>(f32_to_f16_bits(v[3])) << 16);
+            *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+          } else {
+            *reinterpret_cast<v4f*>(dst) = v4f{v[0], v[1], v[2], v[3]};
+          }
+        }
+      }
+      wave_lds_fence();
+      flush_staged<EB, RB>(stg, y, M, N, m0 + wm * 32 * WT + 32 * i, n0 + wn * 32 * WT + h * PJ * 32, lane, vec);
+      wave_lds_fence();                         // staging reads done before the next pass writes
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launch plan: block size (256 or 128) and K-slicing, all tiles alike, chosen
+// by a bandwidth model of MI355X fitted to measured timings (microseconds):
+//  * a 256x256 block step (32 KB of operands, 1024 MFMA cycles) takes
+//    kStep256 on one CU;
+//  * a 128x128 block step moves 16 KB, and one CU streams at most kCuRate
+//    bytes/us into LDS (two blocks share a CU); its MFMAs take kMfma128;
+//  * all CUs together stream at most kL2Rate bytes/us from L2;
+//  * K-slicing writes every slice's fp32 partial and re-reads them all for the
+//    last slice (through memory, kPartRate bytes/us) after a latency kSplitLat;
+//  * kFixed per launch (start-up, epilogue).
+constexpr double kStep256 = 0.65;
+constexpr double kCuRate = 62e3;
+constexpr double kMfma128 = 0.13;
+constexpr double kL2Rate = 12e6;
+constexpr double kPartRate = 5e6;
+constexpr double kSplitLat = 2.0;
+constexpr double kFixed = 3.0;
+constexpr int kFp8MinSliceSteps = 4;
+constexpr int kFp8MaxSplit = 16;
+
+double fp8_plan_time(int64_t M, int64_t N, int64_t nk, int bm, int s, int cus) {
+  const int64_t T = ((M + bm - 1) / bm) * ((N + bm - 1) / bm);
+  const int64_t units = T * s;
+  const double per_cu = static_cast<double>((units + cus - 1) / cus);      // blocks on the busiest CU
+  const double steps = static_cast<double>((nk + s - 1) / s);
+  const double step_bytes = 2.0 * bm * kBK;
+  const double total = static_cast<double>(units) * steps * step_bytes;
+  double t = total / kL2Rate;
+  if (bm == 256) t = std::max(t, per_cu * steps * kStep256);
+  else t = std::max(t, per_cu * steps * std::max(step_bytes / kCuRate, kMfma128));
+  if (s > 1) {
+    const double part = 4.0 * bm * bm;
+    t += (static_cast<double>(units) + static_cast<double>(T) * s) * part / kPartRate + kSplitLat;
+  }
+  return t + kFixed;
+}
+
+GemmPlan plan_fp8_gemm_split(int64_t M, int64_t N, int split, int bm) {
+  GemmPlan p{};
+  p.bm = bm;
+  p.tiles_m = static_cast<int>((M + bm - 1) / bm);
+  p.tiles_n = static_cast<int>((N + bm - 1) / bm);
+  const int T = p.tiles_m * p.tiles_n;
+  p.split = split;
+  p.dp_tiles = split > 1 ? 0 : T;
+  p.sk_tiles = split > 1 ? T : 0;
+  return p;
+}
+
+GemmPlan plan_fp8_gemm(int64_t M, int64_t N, int64_t K, int cus) {
+  if (K % kBK != 0 || cus <= 0) return plan_fp8_gemm_split(M, N, 1, 256);
+  const int64_t nk = K / kBK;
+  double best_t = 0.0;
+  int best_bm = 256, best_s = 1;
+  bool have = false;
+  for (int bm : {256, 128}) {
+    for (int s = 1; s == 1 || (s <= kFp8MaxSplit && s * kFp8MinSliceSteps <= nk); ++s) {
+      const double t = fp8_plan_time(M, N, nk, bm, s, cus);
+      if (!have || t < best_t) have = true, best_t = t, best_bm = bm, best_s = s;
+    }
+  }
+  return plan_fp8_gemm_split(M, N, best_s, best_bm);
+}
+
+// ydt: 0 bf16, 1 fp16, 2 fp32. `part` / `cnt`: plan.partial_bytes() of fp32
+// partials and plan.counters() zeroed counters (left zero), when plan.split > 1.
 void launch_fp8_gemm(const uint8_t* A, const uint8_t* B, int64_t M, int64_t N, int64_t K, const float* sx,
-                     const float* sw, void* Y, int ydt, hipStream_t s) {
+                     const float* sw, void* Y, int ydt, const GemmPlan& plan, float* part, int* cnt, hipStream_t s) {
+  const dim3 block(256);
+  if (K % kBK == 0) {
+    constexpr int S = 4;
+    const dim3 grid(plan.dp_tiles + plan.sk_tiles * plan.split);
+#define W8_FP8_ARGS A, B, (int)M, (int)N, (int)K, sx, sw, Y, plan.tiles_m, plan.tiles_n, plan.dp_tiles, plan.split, \
+    part, cnt
+    if (plan.bm == 256) {
+      if (ydt == 0) k_fp8_gemm_dma<0, S, 4><<<grid, block, 0, s>>>(W8_FP8_ARGS);
+      else if (ydt == 1) k_fp8_gemm_dma<1, S, 4><<<grid, block, 0, s>>>(W8_FP8_ARGS);
+      else k_fp8_gemm_dma<2, S, 4><<<grid, block, 0, s>>>(W8_FP8_ARGS);
+    } else {
+      if (ydt == 0) k_fp8_gemm_dma<0, S, 2><<<grid, block, 0, s>>>(W8_FP8_ARGS);
+      else if (ydt == 1) k_fp8_gemm_dma<1, S, 2><<<grid, block, 0, s>>>(W8_FP8_ARGS);
+      else k_fp8_gemm_dma<2, S, 2><<<grid, block, 0, s>>>(W8_FP8_ARGS);
+    }
+#undef W8_FP8_ARGS
+    return;
+  }
   const int tiles_m = static_cast<int>((M + kFBM - 1) / kFBM);
   const int tiles_n = static_cast<int>((N + kFBN - 1) / kFBN);
-  const dim3 grid(tiles_m * tiles_n), block(256);
-  if (ydt == 0) k_fp8_gemm<0><<<grid, block, 0, s>>>(A, B, (int)M, (int)N, (int)K, sx, sw, Y, tiles_m);
-  else if (ydt == 1) k_fp8_gemm<1><<<grid, block, 0, s>>>(A, B, (int)M, (int)N, (int)K, sx, sw, Y, tiles_m);
-  else k_fp8_gemm<2><<<grid, block, 0, s>>>(A, B, (int)M, (int)N, (int)K, sx, sw, Y, tiles_m);
+  const dim3 grid(tiles_m * tiles_n);
+  if (ydt == 0) k_fp8_gemm_any<0><<<grid, block, 0, s>>>(A, B, (int)M, (int)N, (int)K, sx, sw, Y, tiles_m);
+  else if (ydt == 1) k_fp8_gemm_any<1><<<grid, block, 0, s>>>(A, B, (int)M, (int)N, (int)K, sx, sw, Y, tiles_m);
+  else k_fp8_gemm_any<2><<<grid, block, 0, s>>>(A, B, (int)M, (int)N, (int)K, sx, sw, Y, tiles_m);
 }
 
 }  // namespace w8

@@ -20,48 +20,10 @@
 #include <algorithm>
 #include <type_traits>
 
-#include "common.h"
 #include "launch.h"
+#include "tile.h"
 
 namespace w8 {
-
-typedef int v16i __attribute__((ext_vector_type(16)));
-typedef float v16f __attribute__((ext_vector_type(16)));
-
-constexpr int kBM = 256, kBN = 256, kBK = 64;
-
-// LDS byte offset of logical 16-byte chunk `ch` (0..3) of tile row `row`
-// (64 bytes per row). The XOR term makes the fragment reads (32 rows at one
-// chunk per half-wave) hit distinct banks in every 8- and 16-lane group.
-__device__ __forceinline__ int swz_term(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
-__device__ __forceinline__ int swz64(int row, int ch) { return row * kBK + ((ch ^ swz_term(row)) << 4); }
-
-// XCD-aware block order: the hardware deals consecutive workgroups round-robin
-// over the 8 XCDs; renumber so each XCD gets a contiguous range of ids, then
-// walk tiles in groups of kGroupM tile-rows so blocks that run together on one
-// XCD share A rows and B columns in that XCD's L2.
-constexpr int kXcds = 8, kGroupM = 8;
-
-__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
-  const int per = (nblocks + kXcds - 1) / kXcds;
-  const int tall = nblocks - (per - 1) * kXcds;  // XCDs that get `per` blocks
-  const int xcd = bid % kXcds, local = bid / kXcds;
-  return (xcd < tall) ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
-}
-
-__device__ __forceinline__ void group_tile(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int in_group = kGroupM * tiles_n;
-  const int g = id / in_group;
-  const int first_m = g * kGroupM;
-  const int gm = min(tiles_m - first_m, kGroupM);
-  const int r = id % in_group;
-  tm = first_m + r % gm;
-  tn = r / gm;
-}
-
-__device__ __forceinline__ void tile_coords(int bid, int nblocks, int tiles_m, int tiles_n, int& tm, int& tn) {
-  group_tile(xcd_remap(bid, nblocks), tiles_m, tiles_n, tm, tn);
-}
 
 // One K step (64 bytes) of the wave's 128x128 tile from LDS: two 32-byte
 // sub-steps; lane l supplies row (l & 31), chunk 2*s + (l >> 5).
@@ -86,29 +48,11 @@ __device__ __forceinline__ void mma_step(const int8_t* sa, const int8_t* sb, v16
 // transposed (Wq fragment as the first operand), so element r of tile (i, j)
 // of a lane is
 //   m = m0 + wm*128 + 32*i + (lane&31),
-//   n = n0 + wn*128 + 32*j + 8*(r>>2) + 4*(lane>>5) + (r&3):
-// one output row per lane and four consecutive columns per group of four
-// registers. Stored directly, every store instruction would touch 32 rows
-// (32 partial cache lines); instead each wave stages 32 rows x 256 bytes of
-// its results in LDS and writes them back as whole rows, 16 lanes x 16 bytes
-// per row, 4 rows per instruction.
+//   n = n0 + wn*128 + 32*j + 8*(r>>2) + 4*(lane>>5) + (r&3),
+// staged through LDS a row block at a time (flush_staged).
 //
 // rsx[i]: sx[m]/127 for the lane's row of block i (prefetched by the caller);
 // scol: LDS copy of sw[n0 .. n0+256) / 127; stg: this wave's staging area.
-constexpr int kStgPitch = 256 + 16;             // staged row: 256 bytes + pad
-constexpr int kStgWave = 32 * kStgPitch;        // one wave's 32 staged rows
-constexpr int kEpiLds = 1024 + 4 * kStgWave;    // column scales + 4 staging areas
-
-// Lanes of a wave exchange data through the staging area. The hardware runs a
-// wave's LDS accesses in issue order, but the compiler reasons per thread and
-// may move one lane's read ahead of another lane's write (or a write ahead of
-// another lane's read) to the same bytes: a wavefront-scope fence keeps the
-// program order, at no cost in instructions.
-__device__ __forceinline__ void wave_lds_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-}
-
 template <int MODE, bool XBF16>
 __device__ __forceinline__ void epilogue(v16i (&acc)[4][4], int M, int N, int m0, int n0, int wm, int wn, int lane,
                                          const float (&rsx)[4], const float* scol, int nO,
@@ -117,7 +61,6 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[4][4], int M, int N, int m0
   const int fr = lane & 31, fh = lane >> 5;
   constexpr int EB = MODE == 1 ? 2 : 4;         // bytes per output element
   constexpr int PJ = 256 / (32 * EB);           // 32-column MFMA tiles per staged row: 4 or 2
-  constexpr int EPC = 16 / EB;                  // elements per 16-byte chunk
   const bool vec = (static_cast<int64_t>(N) * EB) % 16 == 0;
   const int P = (nO + 31) & ~31;
   using V8 = typename std::conditional<XBF16, v8bf, v8h>::type;
@@ -176,28 +119,7 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[4][4], int M, int N, int m0
       }
       // staging -> global: 8 instructions of 4 rows x 16 chunks of 16 bytes
       wave_lds_fence();
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int r = 4 * t + (lane >> 4), ch = lane & 15;
-        const char* src = stg + r * kStgPitch + ch * 16;
-        const int m = m0 + wm * 128 + 32 * i + r;
-        const int n = n0 + wn * 128 + h * PJ * 32 + ch * EPC;
-        if (m < M) {
-          char* dst = y + (static_cast<int64_t>(m) * N + n) * EB;
-          if (vec && n + EPC <= N) {
-            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
-          } else {
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) {
-              if (n + e >= N) break;
-              if constexpr (EB == 2)
-                *reinterpret_cast<uint16_t*>(dst + 2 * e) = *reinterpret_cast<const uint16_t*>(src + 2 * e);
-              else
-                *reinterpret_cast<uint32_t*>(dst + 4 * e) = *reinterpret_cast<const uint32_t*>(src + 4 * e);
-            }
-          }
-        }
-      }
+      flush_staged<EB>(stg, y, M, N, m0 + wm * 128 + 32 * i, n0 + wn * 128 + h * PJ * 32, lane, vec);
       wave_lds_fence();                         // staging reads done before the next pass writes
     }
   }
@@ -342,25 +264,6 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm(const int8_t* __restrict__
 //    between the two sub-steps, publishes the next stage and retires the
 //    current one (whose slot the next DMA refills).
 
-// s_waitcnt with only a vmcnt limit (expcnt/lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
-
-// s_waitcnt with only an lgkmcnt limit.
-template <int N>
-__device__ __forceinline__ void wait_lgkmcnt() {
-  static_assert(N >= 0 && N < 16, "lgkmcnt range");
-  __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));
-}
-
-__device__ __forceinline__ void block_barrier() {
-  // a scheduling/memory fence for the compiler, and the hardware barrier
-  __asm__ volatile("s_barrier" ::: "memory");
-}
-
 // A and B fragments of one 32-byte sub-step: f[0..3] rows of A, f[4..7] of B.
 __device__ __forceinline__ void load_frags(const int8_t* sa, int sub, int wm, int wn, int lane, v4i (&f)[8]) {
   const int fr = lane & 31, fh = lane >> 5;
@@ -428,7 +331,6 @@ __device__ __forceinline__ void mma_phase(const v4i (&fm)[8], v16i (&acc)[4][4],
 // exit), and the last slice to arrive adds the other slices' partials to its
 // own and runs the epilogue. Integer sums are exact in any order, so the result does not
 // depend on which slice arrives last. No block ever waits for another.
-constexpr int kPartInts = kBM * kBN;          // one 256x256 int32 partial
 
 template <int MODE, bool XBF16, int S>
 __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
@@ -533,21 +435,13 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
   block_barrier();                                // every wave is done with the ring
 
   if (slot >= 0) {
-    // Partial layout: 16-byte chunk c (0..63) of wave w's 256 accumulators at
-    // byte ((w*64 + c)*64 + lane)*16, so every access is 1 KB contiguous.
-    // Partials are written and read through buffer instructions with the
-    // agent-scope coherence bit (sc1), the form the compiler itself uses for
-    // agent-scope atomic loads and stores: those accesses are coherent across
-    // XCDs on their own, without the whole-L2 write-back / invalidate that a
-    // device-scope fence performs. Once a wave's stores have completed
-    // (vmcnt 0) they are visible to any later sc1 load; the arrival counter is
-    // bumped only after every wave's stores have completed.
-    constexpr int kSc1 = 16;                       // cache-policy bit sc1
-    constexpr int kRawBuffer = 0x00020000;         // word 3 of a raw buffer descriptor (32-bit data format)
+    // Partials go through sc1 buffer accesses (partial_rsrc). Once a wave's
+    // stores have completed (vmcnt 0) they are visible to any later sc1 load;
+    // the arrival counter is bumped only after every wave's stores have
+    // completed.
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     const int lane_off = (wv * 64 * 64 + lane) * 16;
-    const __amdgpu_buffer_rsrc_t mine = __builtin_amdgcn_make_buffer_rsrc(
-        part + static_cast<int64_t>(slot) * kPartInts, 0, kPartInts * 4, kRawBuffer);
+    const __amdgpu_buffer_rsrc_t mine = partial_rsrc(part, slot);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -571,8 +465,7 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
     for (int i = 0; i < 4; ++i) {
       for (int p = 0; p < split; ++p) {
         if (p == piece) continue;
-        const __amdgpu_buffer_rsrc_t other = __builtin_amdgcn_make_buffer_rsrc(
-            part + static_cast<int64_t>(p * R + sk_tile) * kPartInts, 0, kPartInts * 4, kRawBuffer);
+        const __amdgpu_buffer_rsrc_t other = partial_rsrc(part, p * R + sk_tile);
         v4i w[16];
 #pragma unroll
         for (int t = 0; t < 16; ++t)
@@ -602,8 +495,8 @@ constexpr int kSliceFixed = 10;
 constexpr int kMinSliceSteps = 4;
 constexpr int kMaxSplit = 16;
 
-Int8GemmPlan plan_int8_gemm(int64_t M, int64_t N, int64_t K, int cus) {
-  Int8GemmPlan p{};
+GemmPlan plan_int8_gemm(int64_t M, int64_t N, int64_t K, int cus) {
+  GemmPlan p{};
   p.tiles_m = static_cast<int>((M + kBM - 1) / kBM);
   p.tiles_n = static_cast<int>((N + kBN - 1) / kBN);
   const int T = p.tiles_m * p.tiles_n;
@@ -634,7 +527,7 @@ Int8GemmPlan plan_int8_gemm(int64_t M, int64_t N, int64_t K, int cus) {
 // words that the kernel zeroes (the outlier-column mask of the pass before).
 void launch_int8_gemm(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t K, const float* sx,
                       const float* sw, const int* nO, const uint16_t* XO, const uint16_t* WO, bool xbf16,
-                      void* Y, int mode, const Int8GemmPlan& plan, int* part, int* cnt, uint32_t* clear,
+                      void* Y, int mode, const GemmPlan& plan, int* part, int* cnt, uint32_t* clear,
                       int clear_words, hipStream_t s) {
   const int tiles_m = plan.tiles_m, tiles_n = plan.tiles_n;
   const int m = (int)M, n = (int)N, k = (int)K;

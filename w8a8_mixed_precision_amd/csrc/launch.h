@@ -7,14 +7,16 @@
 
 namespace w8 {
 
-// Grid of the int8 GEMM: dp_tiles whole 256x256 tiles, then sk_tiles tiles cut
-// into `split` K-slices each (split == 1: none).
-struct Int8GemmPlan {
+// Grid of the tiled GEMMs: dp_tiles whole tiles of bm x bm outputs, then
+// sk_tiles tiles cut into `split` K-slices each (split == 1: none). The int8
+// GEMM always uses bm = 256; the FP8 GEMM uses 256 or 128.
+struct GemmPlan {
   int tiles_m, tiles_n, dp_tiles, split, sk_tiles;
-  size_t partial_bytes() const { return split > 1 ? size_t(sk_tiles) * split * 256 * 256 * 4 : 0; }
+  int bm = 256;
+  size_t partial_bytes() const { return split > 1 ? size_t(sk_tiles) * split * bm * bm * 4 : 0; }
   int counters() const { return split > 1 ? sk_tiles : 0; }
 };
-Int8GemmPlan plan_int8_gemm(int64_t M, int64_t N, int64_t K, int cus);
+GemmPlan plan_int8_gemm(int64_t M, int64_t N, int64_t K, int cus);
 
 void launch_int8_rows(const void* X, bool bf16, int64_t rows, int K, uint32_t tbits, int8_t* q, float* sx,
                       uint8_t* flags, hipStream_t s);
@@ -27,9 +29,11 @@ void launch_fp8_rows(const void* X, bool bf16, int64_t rows, int K, const float*
                      int mode, hipStream_t s);
 void launch_int8_gemm(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t K, const float* sx,
                       const float* sw, const int* nO, const uint16_t* XO, const uint16_t* WO, bool xbf16, void* Y,
-                      int mode, const Int8GemmPlan& plan, int* part, int* cnt, uint32_t* clear, int clear_words,
+                      int mode, const GemmPlan& plan, int* part, int* cnt, uint32_t* clear, int clear_words,
                       hipStream_t s);
+GemmPlan plan_fp8_gemm(int64_t M, int64_t N, int64_t K, int cus);
+GemmPlan plan_fp8_gemm_split(int64_t M, int64_t N, int split, int bm);
 void launch_fp8_gemm(const uint8_t* A, const uint8_t* B, int64_t M, int64_t N, int64_t K, const float* sx,
-                     const float* sw, void* Y, int ydt, hipStream_t s);
+                     const float* sw, void* Y, int ydt, const GemmPlan& plan, float* part, int* cnt, hipStream_t s);
 
 }  // namespace w8
