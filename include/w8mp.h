@@ -165,14 +165,20 @@ w8_status w8dbg_int8_quantize_activations(const void* X, int x_dt, int64_t M, in
                                           int32_t* outlier_idx, int32_t* n_outliers,
                                           void* workspace, size_t workspace_bytes, void* stream);
 
-/* The int8 MFMA contraction alone: acc [M,N] int32 = q [M,K] . Wq [N,K]^T,
- * with the same grid plan (including the K-split of the last wave of tiles)
- * as int8_mixed_linear. Workspace: w8dbg_int8_gemm_i32_workspace_size(M, N, K)
- * bytes on the current device (may be 0, then workspace may be NULL),
- * zero-filled before first use (left zero by every call). */
-size_t w8dbg_int8_gemm_i32_workspace_size(int64_t M, int64_t N, int64_t K);
+/* The int8 MFMA contraction alone: acc [M,N] int32 = q [M,K] . Wq [N,K]^T.
+ * tail = 0: the grid int8_mixed_linear would use (split ignored). Otherwise
+ * the leftover 256x256 tiles of the last, partial wave of the device (every
+ * tile when there are fewer tiles than compute units) run as `split` K-slices
+ * of whole tiles (tail = 1; split = 1 runs every tile whole) or of 128x128
+ * quarters (tail = 2); tail 1 with split > 1 and tail 2 need K % 64 == 0 and
+ * split <= K / 64 (else W8_ERR_UNSUPPORTED). Workspace:
+ * w8dbg_int8_gemm_i32_workspace_size(M, N, K, tail, split) bytes on the
+ * current device (may be 0, then workspace may be NULL), zero-filled before
+ * first use (left zero by every call). */
+size_t w8dbg_int8_gemm_i32_workspace_size(int64_t M, int64_t N, int64_t K, int tail, int split);
 w8_status w8dbg_int8_gemm_i32(const int8_t* q, const int8_t* Wq, int64_t M, int64_t N, int64_t K,
-                              int32_t* acc, void* workspace, size_t workspace_bytes, void* stream);
+                              int tail, int split, int32_t* acc, void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 /* The activation half of fp8_w8a8_linear: xq [M,K] E4M3 codes, sx [M] fp32. */
 w8_status w8dbg_fp8_quantize_activations(const void* X, int x_dt, int64_t M, int64_t K,

@@ -119,8 +119,15 @@ def test_weight_quantisation_rejects(args, status):
 
 def test_debug_exports_reject():
     lib = _abi.lib()
-    assert lib.w8dbg_int8_gemm_i32(A, A, 4, 4, 20, A, None, 0, None) == _abi.W8_ERR_INVALID_ARGUMENT
-    assert lib.w8dbg_int8_gemm_i32(None, A, 4, 4, 32, A, None, 0, None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert lib.w8dbg_int8_gemm_i32(A, A, 4, 4, 20, 0, 1, A, None, 0, None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert lib.w8dbg_int8_gemm_i32(None, A, 4, 4, 32, 0, 1, A, None, 0, None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert lib.w8dbg_int8_gemm_i32(A, A, 4, 4, 64, 3, 1, A, None, 0, None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert lib.w8dbg_int8_gemm_i32(A, A, 4, 4, 64, 2, 0, A, None, 0, None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert lib.w8dbg_int8_gemm_i32(A, A, 4, 4, 80, 2, 1, A, None, 0, None) == _abi.W8_ERR_UNSUPPORTED
+    assert lib.w8dbg_int8_gemm_i32(A, A, 4, 4, 128, 1, 3, A, None, 0, None) == _abi.W8_ERR_UNSUPPORTED
+    assert lib.w8dbg_int8_gemm_i32_workspace_size(4, 4, 128, 2, 2) >= 4 * 2 * 128 * 128 * 4
+    assert lib.w8dbg_int8_gemm_i32_workspace_size(4, 4, 128, 1, 2) >= 2 * 256 * 256 * 4
+    assert lib.w8dbg_int8_gemm_i32(A, A, 4, 4, 128, 2, 2, A, A, 1024, None) == _abi.W8_ERR_WORKSPACE
     assert lib.w8dbg_fp8_quantize_activations(A, _abi.W8_DT_BF16, 4, 20, None, A, A, None) == \
         _abi.W8_ERR_INVALID_ARGUMENT
     assert lib.w8dbg_int8_quantize_activations(A, _abi.W8_DT_BF16, 4, 32, 6.0, A, A, A, A, A, 1,

@@ -172,6 +172,36 @@ def test_int8_gemm_accumulators_bit_exact(M, N, K):
     assert np.array_equal(acc.cpu().numpy().astype(np.int64), ref)
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 520, 4096), (77, 300, 2048), (513, 1040, 1024), (256, 512, 192),
+                                   (1, 16, 640)])
+@pytest.mark.parametrize("tail,split", [(1, 1), (1, 2), (1, 3), (2, 1), (2, 2), (2, 5)])
+def test_int8_gemm_tail_treatments_bit_exact(M, N, K, tail, split):
+    """Every treatment of the leftover tiles of a partial wave (here all tiles:
+    fewer tiles than compute units): whole 256x256 tiles, K-sliced 256x256
+    tiles, and 128x128 quarters whole or K-sliced (quarters outside [M, N)
+    included). Repeated calls through one workspace stay exact and leave the
+    split-K counters zero."""
+    if split > K // 64:
+        pytest.skip("more slices than K steps")
+    rng = np.random.default_rng(M * 5 + N + K + 10 * tail + split)
+    q = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    w = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    if M > 2 and N > 2:
+        q[0, :] = 127
+        w[0, :] = 127
+        w[1, :] = -127
+    ref = o.int8_contract(q, w)
+    announce("int8 gemm i32 tail", M, N, K, tail, split)
+    n_ws = w8.debug_int8_gemm_i32_workspace_size(M, N, K, tail, split)
+    ws = w8.new_workspace(max(n_ws, 256))
+    tq, tw = torch.from_numpy(q).cuda(), torch.from_numpy(w).cuda()
+    for _ in range(2):
+        acc = w8.debug_int8_gemm_i32(tq, tw, tail, split, workspace=ws)
+        assert np.array_equal(acc.cpu().numpy().astype(np.int64), ref)
+    if n_ws:
+        assert int(ws[:256].view(torch.int32).abs().sum().item()) == 0     # counters left zero
+
+
 @pytest.mark.parametrize("case", CASES, ids=lambda c: c.name)
 @pytest.mark.parametrize("out_dtype", ["f16", "f32"])
 @pytest.mark.parametrize("t", [6.0, math.inf, 0.0])

@@ -126,17 +126,25 @@ def debug_int8_quantize_activations(x: torch.Tensor, threshold: float = 6.0):
     return q, sx, idx[: int(n.item())]
 
 
-def debug_int8_gemm_i32(q: torch.Tensor, wq: torch.Tensor) -> torch.Tensor:
-    """acc [M,N] int32 = q . wq^T on the int8 MFMA kernel."""
+def debug_int8_gemm_i32(q: torch.Tensor, wq: torch.Tensor, tail: int = 0, split: int = 1,
+                        workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """acc [M,N] int32 = q . wq^T on the int8 MFMA kernel. tail 0: the linear's
+    own grid; 1: leftover tiles as `split` 256x256 K-slices (1: all whole);
+    2: as `split` K-slices of 128x128 quarters (see include/w8mp.h)."""
     _dev(q, "q"), _dev(wq, "wq")
     M, K = q.shape
     N = wq.shape[0]
     acc = torch.empty((M, N), dtype=torch.int32, device=q.device)
-    n_ws = int(lib().w8dbg_int8_gemm_i32_workspace_size(M, N, K))
-    ws = _workspace(n_ws, q.device) if n_ws else None
-    _abi.check(lib().w8dbg_int8_gemm_i32(q.data_ptr(), wq.data_ptr(), M, N, K, acc.data_ptr(),
-                                         ws.data_ptr() if ws is not None else None, n_ws, _stream(q)))
+    n_ws = debug_int8_gemm_i32_workspace_size(M, N, K, tail, split)
+    ws = workspace if workspace is not None else (_workspace(n_ws, q.device) if n_ws else None)
+    _abi.check(lib().w8dbg_int8_gemm_i32(q.data_ptr(), wq.data_ptr(), M, N, K, int(tail), int(split), acc.data_ptr(),
+                                         ws.data_ptr() if ws is not None else None,
+                                         ws.numel() if ws is not None else 0, _stream(q)))
     return acc
+
+
+def debug_int8_gemm_i32_workspace_size(M: int, N: int, K: int, tail: int = 0, split: int = 1) -> int:
+    return int(lib().w8dbg_int8_gemm_i32_workspace_size(M, N, K, int(tail), int(split)))
 
 
 def profile_start(max_calls: int) -> None:

@@ -31,8 +31,8 @@ SIGNATURES = {
     "w8_last_error": (ctypes.c_char_p, []),
     "w8dbg_int8_quantize_activations_workspace_size": (_size, [_i64, _i64]),
     "w8dbg_int8_quantize_activations": (_int, [_p, _int, _i64, _i64, _f, _p, _p, _p, _p, _p, _size, _p]),
-    "w8dbg_int8_gemm_i32_workspace_size": (_size, [_i64, _i64, _i64]),
-    "w8dbg_int8_gemm_i32": (_int, [_p, _p, _i64, _i64, _i64, _p, _p, _size, _p]),
+    "w8dbg_int8_gemm_i32_workspace_size": (_size, [_i64, _i64, _i64, _int, _int]),
+    "w8dbg_int8_gemm_i32": (_int, [_p, _p, _i64, _i64, _i64, _int, _int, _p, _p, _size, _p]),
     "w8dbg_fp8_quantize_activations": (_int, [_p, _int, _i64, _i64, _p, _p, _p, _p]),
     "w8dbg_fp8_gemm_workspace_size": (_size, [_i64, _i64, _i64, _int, _int]),
     "w8dbg_fp8_gemm": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _int, _int, _p, _int, _p, _size, _p]),

@@ -128,9 +128,12 @@ struct GemmWs {
   w8::GemmPlan plan;
 };
 
-GemmWs gemm_layout(int64_t M, int64_t N, int64_t K) {
+// tail: 0 the linear's own plan; 1 leftover tiles as `split` 256x256 slices
+// (split 1: every tile whole); 2 as `split` slices of 128x128 quarters.
+GemmWs gemm_layout(int64_t M, int64_t N, int64_t K, int tail = 0, int split = 1) {
   GemmWs w{};
-  w.plan = w8::plan_int8_gemm(M, N, K, cu_count());
+  w.plan = tail == 0 ? w8::plan_int8_gemm(M, N, K, cu_count())
+                     : w8::plan_int8_gemm_forced(M, N, cu_count(), tail == 2, split);
   size_t off = 0;
   w.cnt = off;  off = up(off + 4 * static_cast<size_t>(w.plan.counters()));
   w.part = off; off = up(off + w.plan.partial_bytes());
@@ -373,19 +376,22 @@ w8_status w8dbg_int8_quantize_activations(const void* X, int x_dt, int64_t M, in
   return check_launch("w8dbg_int8_quantize_activations");
 }
 
-size_t w8dbg_int8_gemm_i32_workspace_size(int64_t M, int64_t N, int64_t K) {
-  if (M < 1 || N < 1 || K < 1) return 0;
-  return gemm_layout(M, N, K).total;
+size_t w8dbg_int8_gemm_i32_workspace_size(int64_t M, int64_t N, int64_t K, int tail, int split) {
+  if (M < 1 || N < 1 || K < 1 || tail < 0 || tail > 2 || split < 1) return 0;
+  return gemm_layout(M, N, K, tail, split).total;
 }
 
-w8_status w8dbg_int8_gemm_i32(const int8_t* q, const int8_t* Wq, int64_t M, int64_t N, int64_t K, int32_t* acc,
-                              void* workspace, size_t workspace_bytes, void* stream) {
+w8_status w8dbg_int8_gemm_i32(const int8_t* q, const int8_t* Wq, int64_t M, int64_t N, int64_t K, int tail,
+                              int split, int32_t* acc, void* workspace, size_t workspace_bytes, void* stream) {
   W8_REQUIRE(q && Wq && acc, W8_ERR_INVALID_ARGUMENT, "null pointer argument");
   if (w8_status st = check_mk(M, K, W8_INT8_MAX_K); st != W8_OK) return st;
   W8_REQUIRE(N >= 1 && N <= kMaxDim, W8_ERR_INVALID_ARGUMENT, "N must be in [1, 2^31)");
+  W8_REQUIRE(tail >= 0 && tail <= 2 && split >= 1, W8_ERR_INVALID_ARGUMENT, "tail must be 0..2 and split >= 1");
+  W8_REQUIRE(tail == 0 || (tail == 1 && split == 1) || (K % 64 == 0 && split <= K / 64), W8_ERR_UNSUPPORTED,
+             "this tail treatment needs K %% 64 == 0 and split <= K / 64");
   W8_REQUIRE(aligned16(q) && aligned16(Wq) && aligned16(acc), W8_ERR_INVALID_ARGUMENT,
              "pointers must be 16-byte aligned");
-  const GemmWs L = gemm_layout(M, N, K);
+  const GemmWs L = gemm_layout(M, N, K, tail, split);
   if (L.total > 0) {
     if (w8_status st = check_ws(workspace, workspace_bytes, L.total); st != W8_OK) return st;
   }

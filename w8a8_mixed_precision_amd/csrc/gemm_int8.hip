@@ -44,53 +44,64 @@ __device__ __forceinline__ void mma_step(const int8_t* sa, const int8_t* sb, v16
   }
 }
 
-// Epilogue shared by both GEMM kernels. The MFMAs compute each 32x32 tile
-// transposed (Wq fragment as the first operand), so element r of tile (i, j)
-// of a lane is
-//   m = m0 + wm*128 + 32*i + (lane&31),
-//   n = n0 + wn*128 + 32*j + 8*(r>>2) + 4*(lane>>5) + (r&3),
+// The 16-bit side-product MFMA behind a plain function (a target builtin with
+// template-dependent arguments can make the host compilation pass drop the
+// kernel templates that use it).
+template <bool XBF16, typename V8>
+__device__ __forceinline__ v16f mfma_side(V8 a, V8 b, v16f c) {
+  if constexpr (XBF16) return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  else return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Epilogue shared by the GEMM kernels, for a wave tile of WT x WT 32x32 MFMA
+// tiles (WT = 4: 256x256 blocks, 2: 128x128 blocks). The MFMAs compute each
+// tile transposed (Wq fragment as the first operand), so element r of tile
+// (i, j) of a lane is
+//   m = m0 + wm*32*WT + 32*i + (lane&31),
+//   n = n0 + wn*32*WT + 32*j + 8*(r>>2) + 4*(lane>>5) + (r&3),
 // staged through LDS a row block at a time (flush_staged).
 //
 // rsx[i]: sx[m]/127 for the lane's row of block i (prefetched by the caller);
-// scol: LDS copy of sw[n0 .. n0+256) / 127; stg: this wave's staging area.
-template <int MODE, bool XBF16>
-__device__ __forceinline__ void epilogue(v16i (&acc)[4][4], int M, int N, int m0, int n0, int wm, int wn, int lane,
+// scol: LDS copy of sw[n0 .. n0+64*WT) / 127; stg: this wave's staging area.
+template <int MODE, bool XBF16, int WT = 4>
+__device__ __forceinline__ void epilogue(v16i (&acc)[WT][WT], int M, int N, int m0, int n0, int wm, int wn, int lane,
                                          const float (&rsx)[4], const float* scol, int nO,
                                          const uint16_t* __restrict__ XO, const uint16_t* __restrict__ WO,
                                          void* __restrict__ Y, char* stg) {
   const int fr = lane & 31, fh = lane >> 5;
   constexpr int EB = MODE == 1 ? 2 : 4;         // bytes per output element
-  constexpr int PJ = 256 / (32 * EB);           // 32-column MFMA tiles per staged row: 4 or 2
+  constexpr int ROWB = 32 * WT * EB;            // bytes of one output row of the wave tile
+  constexpr int H = ROWB > 256 ? ROWB / 256 : 1;   // staging passes per 32-row block
+  constexpr int PJ = WT / H;                    // 32-column MFMA tiles per pass
+  constexpr int RB = 32 * PJ * EB;              // staged row bytes: 256 or 128
+  constexpr int WR = 32 * WT;                   // rows (= columns) of the wave tile
   const bool vec = (static_cast<int64_t>(N) * EB) % 16 == 0;
   const int P = (nO + 31) & ~31;
   using V8 = typename std::conditional<XBF16, v8bf, v8h>::type;
   char* const y = static_cast<char*>(Y);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < WT; ++i) {
     // side product for this 32-row block: o[j] = WO(block j) . XO(rows of block i)^T
-    v16f o[4];
+    v16f o[WT];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < WT; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[j][r] = 0.0f;
     if constexpr (MODE != 0) {
-      const int m = m0 + wm * 128 + 32 * i + fr;
+      const int m = m0 + wm * WR + 32 * i + fr;
       const int64_t xrow = static_cast<int64_t>(min(m, M - 1)) * P;
       for (int c = 0; c < P; c += 16) {
         const V8 xb = *reinterpret_cast<const V8*>(XO + xrow + c + 8 * fh);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < WT; ++j) {
           const V8 wa = *reinterpret_cast<const V8*>(
-              WO + static_cast<int64_t>(min(n0 + wn * 128 + 32 * j + fr, N - 1)) * P + c + 8 * fh);
-          if constexpr (XBF16)
-            o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, xb, o[j], 0, 0, 0);
-          else
-            o[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wa, xb, o[j], 0, 0, 0);
+              WO + static_cast<int64_t>(min(n0 + wn * WR + 32 * j + fr, N - 1)) * P + c + 8 * fh);
+          o[j] = mfma_side<XBF16>(wa, xb, o[j]);
         }
       }
     }
 #pragma unroll
-    for (int h = 0; h < 4 / PJ; ++h) {
+    for (int h = 0; h < H; ++h) {
       // registers -> staging: row fr, columns 32*jj + 8*g + 4*fh .. +4 of this pass
 #pragma unroll
       for (int jj = 0; jj < PJ; ++jj) {
@@ -102,7 +113,7 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[4][4], int M, int N, int m0
             *reinterpret_cast<v4i*>(dst) =
                 v4i{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
           } else {
-            const v4f cs = *reinterpret_cast<const v4f*>(scol + wn * 128 + 32 * j + 8 * g + 4 * fh);
+            const v4f cs = *reinterpret_cast<const v4f*>(scol + wn * WR + 32 * j + 8 * g + 4 * fh);
             float v[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -119,7 +130,7 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[4][4], int M, int N, int m0
       }
       // staging -> global: 8 instructions of 4 rows x 16 chunks of 16 bytes
       wave_lds_fence();
-      flush_staged<EB>(stg, y, M, N, m0 + wm * 128 + 32 * i, n0 + wn * 128 + h * PJ * 32, lane, vec);
+      flush_staged<EB, RB>(stg, y, M, N, m0 + wm * WR + 32 * i, n0 + wn * WR + h * PJ * 32, lane, vec);
       wave_lds_fence();                         // staging reads done before the next pass writes
     }
   }
@@ -134,13 +145,13 @@ struct EpiIn {
   int nO;
 };
 
-template <int MODE>
+template <int MODE, int WT = 4>
 __device__ __forceinline__ void epi_prefetch(EpiIn& e, int M, int N, int m0, int n0, int wm, int lane,
                                              const float* __restrict__ sx, const float* __restrict__ sw,
                                              const int* __restrict__ nO_ptr) {
   if constexpr (MODE != 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) e.rsx[i] = sx[min(m0 + wm * 128 + 32 * i + (lane & 31), M - 1)];
+    for (int i = 0; i < 4; ++i) e.rsx[i] = sx[min(m0 + wm * 32 * WT + 32 * i + (lane & 31), M - 1)];
     e.my_sw = sw[min(n0 + static_cast<int>(threadIdx.x), N - 1)];
     e.nO = *nO_ptr;
   } else {
@@ -154,8 +165,8 @@ __device__ __forceinline__ void epi_prefetch(EpiIn& e, int M, int N, int m0, int
 // Finishes the prefetch (divides by 127, publishes the column scales in LDS)
 // and runs the epilogue. `lds` is at least kEpiLds bytes of LDS that the K loop
 // no longer uses. Every wave of the block must call it.
-template <int MODE, bool XBF16>
-__device__ __forceinline__ void finish_tile(v16i (&acc)[4][4], EpiIn& e, char* lds, int M, int N, int m0, int n0,
+template <int MODE, bool XBF16, int WT = 4>
+__device__ __forceinline__ void finish_tile(v16i (&acc)[WT][WT], EpiIn& e, char* lds, int M, int N, int m0, int n0,
                                             int wm, int wn, int lane, const uint16_t* __restrict__ XO,
                                             const uint16_t* __restrict__ WO, void* __restrict__ Y) {
   float* scol = reinterpret_cast<float*>(lds);
@@ -165,8 +176,8 @@ __device__ __forceinline__ void finish_tile(v16i (&acc)[4][4], EpiIn& e, char* l
     scol[threadIdx.x] = e.my_sw / 127.0f;
     __syncthreads();
   }
-  epilogue<MODE, XBF16>(acc, M, N, m0, n0, wm, wn, lane, e.rsx, scol, e.nO, XO, WO, Y,
-                        lds + 1024 + (threadIdx.x >> 6) * kStgWave);
+  epilogue<MODE, XBF16, WT>(acc, M, N, m0, n0, wm, wn, lane, e.rsx, scol, e.nO, XO, WO, Y,
+                            lds + 1024 + (threadIdx.x >> 6) * kStgWave);
 }
 
 __device__ __forceinline__ void zero_acc(v16i (&acc)[4][4]) {
@@ -323,6 +334,194 @@ __device__ __forceinline__ void mma_phase(const v4i (&fm)[8], v16i (&acc)[4][4],
   }
 }
 
+// ---------------------------------------------------------------------------
+// 128x128 blocks for the leftover tiles of a last, partial wave. A 256x256
+// tile takes the same time on its CU however few tiles share the wave, so a
+// wave of R < cus tiles costs as much as a full one; each leftover tile is
+// instead covered by four 128x128 blocks (2x2 waves of 64x64 outputs, 2x2
+// MFMA tiles each), optionally cut into `split` K-slices. The smaller block
+// streams twice the operand bytes per MFMA, but it runs alone on its CU while
+// the chip is otherwise idle. Ring: 2*S stages of 16 KB in the same LDS.
+constexpr int kSmall = 128;
+constexpr int kSmallStage = 2 * kSmall * kBK;   // one K step of A then B, 16 KB
+constexpr int kSmallLoads = 4;                  // DMA instructions per wave per step
+constexpr int kSmallPartBytes = kSmall * kSmall * 4;
+
+// The builtins of the small-block loop behind plain functions (with
+// template-dependent arguments the host compilation pass can drop the kernel
+// templates that use them).
+__device__ __forceinline__ v16i mfma_i8(v4i a, v4i b, v16i c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_dma16(const int8_t* src, int8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+__device__ __forceinline__ v4i lo4(v8i v) { return __builtin_shufflevector(v, v, 0, 1, 2, 3); }
+__device__ __forceinline__ v4i hi4(v8i v) { return __builtin_shufflevector(v, v, 4, 5, 6, 7); }
+
+// LDS row of small-block fragment f (0, 1: A row blocks; 2, 3: B row blocks).
+__device__ __forceinline__ const int8_t* small_frag(const int8_t* slot, int f, int wm, int wn, int fr, int ch) {
+  return f < 2 ? slot + swz64(wm * 64 + f * 32 + fr, ch) : slot + kSmall * kBK + swz64(wn * 64 + (f - 2) * 32 + fr, ch);
+}
+
+template <int SS>
+__device__ __forceinline__ void small_issue(int8_t* lds, int kt, int nk, const int8_t* const* a_src,
+                                            const int8_t* const* b_src, int wave) {
+  int8_t* st = lds + (kt % SS) * kSmallStage;
+  const int k0 = min(kt, nk - 1) * kBK;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    lds_dma16(a_src[i] + k0, st + (wave * 2 + i) * 1024);
+    lds_dma16(b_src[i] + k0, st + kSmall * kBK + (wave * 2 + i) * 1024);
+  }
+}
+
+// K step kt of the small-block loop: wait for step kt+1 (all waves) and for
+// every wave to be done with step kt's slot; then 8 MFMAs (both 32-byte halves
+// of the 2x2 tiles, half-major so back-to-back MFMAs are independent) on fc,
+// one 16-byte read of step kt+1's fragments per MFMA (order A0, B0, B1, A1)
+// and one DMA of step kt+SS into the retired slot per two MFMAs. The last step
+// runs the same code: its reads stay in the ring and its DMA repeats the last
+// step into its own, retired slot.
+template <int SS>
+__device__ __forceinline__ void small_body(const v8i* fc, v8i* fn, v16i (*acc)[2], int8_t* lds, int kt, int nk,
+                                           int wm, int wn, int lane, const int8_t* const* a_src,
+                                           const int8_t* const* b_src, int wave) {
+  wait_lgkmcnt<0>();
+  wait_vmcnt<(SS - 2) * kSmallLoads>();
+  block_barrier();
+  const int fr = lane & 31, fh = lane >> 5;
+  const int8_t* sn = lds + ((kt + 1) % SS) * kSmallStage;
+  int8_t* st = lds + (kt % SS) * kSmallStage;
+  const int k0 = min(kt + SS, nk - 1) * kBK;
+  constexpr int kOrd[4] = {0, 2, 3, 1};
+  v4i lo;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int half = t >> 2, i = (t >> 1) & 1, j = t & 1;
+    const v4i a = half ? hi4(fc[i]) : lo4(fc[i]);
+    const v4i b = half ? hi4(fc[2 + j]) : lo4(fc[2 + j]);
+    acc[i][j] = mfma_i8(b, a, acc[i][j]);
+    const int f = kOrd[t >> 1];
+    if ((t & 1) == 0) {
+      lo = *reinterpret_cast<const v4i*>(small_frag(sn, f, wm, wn, fr, fh));
+      const int d = t >> 1;
+      if (d < 2) lds_dma16(a_src[d] + k0, st + (wave * 2 + d) * 1024);
+      else lds_dma16(b_src[d - 2] + k0, st + kSmall * kBK + (wave * 2 + d - 2) * 1024);
+    } else {
+      const v4i hi = *reinterpret_cast<const v4i*>(small_frag(sn, f, wm, wn, fr, 2 + fh));
+      fn[f] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// One 128x128 block of the leftover tiles: blocks dp_tiles.. of the grid are
+// `split` K-slices of 4*R quarter tiles (R leftover 256x256 tiles, numbered
+// slice-major per XCD like the big split). A quarter outside [M, N) returns at
+// once (its other slices do too). With split > 1 the slices exchange int32
+// partials and counters as the big split-K does (exact sums, any order).
+template <int MODE, bool XBF16, int S>
+__device__ __forceinline__ void small_block(int8_t* lds, const int8_t* __restrict__ A, const int8_t* __restrict__ B,
+                                            int M, int N, int K, const float* __restrict__ sx,
+                                            const float* __restrict__ sw, const int* __restrict__ nO_ptr,
+                                            const uint16_t* __restrict__ XO, const uint16_t* __restrict__ WO,
+                                            void* __restrict__ Y, int tiles_m, int tiles_n, int dp_tiles, int split,
+                                            int* __restrict__ part, int* __restrict__ cnt) {
+  constexpr int SS = 2 * S;                     // the same LDS as S big stages
+  int* const s_last = reinterpret_cast<int*>(lds + kEpiLds);
+  const int nu = gridDim.x - dp_tiles;
+  const int v = xcd_remap(blockIdx.x - dp_tiles, nu);
+  const int Q = nu / split;                     // quarter tiles
+  const int piece = v / Q, sub = v % Q;
+  int tm, tn;
+  group_tile(dp_tiles + sub / 4, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * kBM + (sub & 2) * 64, n0 = tn * kBN + (sub & 1) * 128;
+  if (m0 >= M || n0 >= N) return;
+  const int nk_all = K / kBK;
+  const int kb = piece * nk_all / split, ke = (piece + 1) * nk_all / split, nk = ke - kb;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int fr = lane & 31, fh = lane >> 5;
+  EpiIn ein;
+  epi_prefetch<MODE, 2>(ein, M, N, m0, n0, wm, lane, sx, sw, nO_ptr);
+
+  // DMA source of this lane for load i (0, 1) of each operand: block row
+  // r = wave*32 + 16*i + lane/4 lands in LDS slot (lane & 3) of that row.
+  const int8_t* a_src[2];
+  const int8_t* b_src[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = wave * 32 + 16 * i + (lane >> 2);
+    const int ch = (lane & 3) ^ swz_term(r);
+    a_src[i] = A + static_cast<int64_t>(min(m0 + r, M - 1)) * K + kb * kBK + ch * 16;
+    b_src[i] = B + static_cast<int64_t>(min(n0 + r, N - 1)) * K + kb * kBK + ch * 16;
+  }
+  v16i acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+
+  for (int st = 0; st < SS; ++st) small_issue<SS>(lds, st, nk, a_src, b_src, wave);
+  wait_vmcnt<(SS - 1) * kSmallLoads>();
+  block_barrier();
+  v8i fa[4], fb[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const v4i lo = *reinterpret_cast<const v4i*>(small_frag(lds, f, wm, wn, fr, fh));
+    const v4i hi = *reinterpret_cast<const v4i*>(small_frag(lds, f, wm, wn, fr, 2 + fh));
+    fa[f] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    small_body<SS>(fa, fb, acc, lds, kt, nk, wm, wn, lane, a_src, b_src, wave);
+    small_body<SS>(fb, fa, acc, lds, kt + 1, nk, wm, wn, lane, a_src, b_src, wave);
+  }
+  if (kt < nk) small_body<SS>(fa, fb, acc, lds, kt, nk, wm, wn, lane, a_src, b_src, wave);
+  wait_lgkmcnt<0>();
+  wait_vmcnt<0>();
+  block_barrier();
+
+  if (split > 1) {
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int lane_off = (wv * 16 * 64 + lane) * 16;
+    const __amdgpu_buffer_rsrc_t mine = partial_rsrc(part, v, kSmallPartBytes);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const v4i val{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, val), mine,
+                                                 lane_off + ((i * 2 + j) * 4 + q) * 1024, 0, kSc1);
+        }
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0)
+      *s_last = __hip_atomic_fetch_add(cnt + sub, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == split - 1;
+    __syncthreads();
+    if (!*s_last) return;
+    if (tid == 0) cnt[sub] = 0;
+    for (int p = 0; p < split; ++p) {
+      if (p == piece) continue;
+      const __amdgpu_buffer_rsrc_t other = partial_rsrc(part, p * Q + sub, kSmallPartBytes);
+      v4i w[16];
+#pragma unroll
+      for (int t = 0; t < 16; ++t)
+        w[t] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(other, lane_off + t * 1024, 0, kSc1));
+#pragma unroll
+      for (int t = 0; t < 16; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[t >> 3][(t >> 2) & 1][4 * (t & 3) + e] += w[t][e];
+    }
+  }
+  finish_tile<MODE, XBF16, 2>(acc, ein, reinterpret_cast<char*>(lds), M, N, m0, n0, wm, wn, lane, XO, WO, Y);
+}
+
 // Work split for the last, partial wave of tiles (split-K). The first
 // dp_tiles blocks each own a whole 256x256 tile. The remaining blocks are
 // `split` K-slices of each of the R = (gridDim.x - dp_tiles) / split leftover
@@ -339,7 +538,7 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
                                                           const uint16_t* __restrict__ XO,
                                                           const uint16_t* __restrict__ WO, void* __restrict__ Y,
                                                           int tiles_m, int tiles_n, int dp_tiles, int split,
-                                                          int* __restrict__ part, int* __restrict__ cnt,
+                                                          int small, int* __restrict__ part, int* __restrict__ cnt,
                                                           uint32_t* __restrict__ clear, int clear_words) {
   constexpr int kStage = 2 * kBM * kBK;       // A then B, 32 KB
   constexpr int kLoads = 8;                   // DMA instructions per wave per step
@@ -353,6 +552,15 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
   int* const s_last = reinterpret_cast<int*>(lds + kEpiLds);
   static_assert(sizeof(lds) >= kEpiLds + 4, "epilogue LDS and arrival flag");
 
+  // The quantisation pass before this kernel is complete, so its outlier-column
+  // mask can be cleared here for the next call.
+  if (blockIdx.x == 0 && clear)
+    for (int i = threadIdx.x; i < clear_words; i += 256) clear[i] = 0u;
+  if (small && static_cast<int>(blockIdx.x) >= dp_tiles) {
+    small_block<MODE, XBF16, S>(lds, A, B, M, N, K, sx, sw, nO_ptr, XO, WO, Y, tiles_m, tiles_n, dp_tiles, split,
+                                part, cnt);
+    return;
+  }
   const int nk_all = K / kBK;
   int tm, tn, kb = 0, ke = nk_all;
   int slot = -1, sk_tile = 0, piece = 0, R = 0;
@@ -374,10 +582,6 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
   const int m0 = tm * kBM, n0 = tn * kBN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  // The quantisation pass before this kernel is complete, so its outlier-column
-  // mask can be cleared here for the next call.
-  if (blockIdx.x == 0 && clear)
-    for (int i = tid; i < clear_words; i += 256) clear[i] = 0u;
   EpiIn ein;
   epi_prefetch<MODE>(ein, M, N, m0, n0, wm, lane, sx, sw, nO_ptr);
 
@@ -482,18 +686,26 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// Launch plan. Whole tiles fill as many complete waves of `cus` blocks as
-// they can; the leftover R = T mod cus tiles may be split along K into
-// `split` slices instead. Cost model in K-steps, fitted to MI355X timings:
-// a sparse last wave of whole tiles runs at ~3/4 of a full tile's time (the
-// few busy CUs clock higher and share the memory system with no one); a split
-// costs its slice, a fixed start-up and, for the last slice, re-reading the
-// other slices. 256 KB partials from another CU (the dominant cost, ~10
-// K-steps each). In practice only long-K shapes split.
+// Launch plan. Whole tiles fill as many complete waves of `cus` blocks as they
+// can; the leftover R = T mod cus tiles of the last, partial wave run either
+// whole, cut into `split` K-slices, or as four 128x128 blocks each (optionally
+// sliced), whichever a cost model in units of one 256x256 K step says is
+// cheapest, fitted to MI355X timings:
+//  * a sparse wave of whole tiles runs at ~3/4 of a full tile's time (the few
+//    busy CUs clock higher and share the memory system with no one);
+//  * a 256x256 slice costs its K steps, kSliceFixed of start-up and epilogue
+//    and kSliceCost per extra slice (the last slice re-reads the others' 256 KB
+//    partials from another CU);
+//  * a 128x128 block step costs kSmallStep of a 256x256 step, plus
+//    kSmallFixed, plus kSmallSlice per extra slice (64 KB partials); with more
+//    than one block per CU the CU's blocks run back to back.
 constexpr int kSliceCost = 10;
 constexpr int kSliceFixed = 10;
 constexpr int kMinSliceSteps = 4;
 constexpr int kMaxSplit = 16;
+constexpr double kSmallStep = 0.30;
+constexpr double kSmallFixed = 6.0;
+constexpr double kSmallSlice = 3.0;
 
 GemmPlan plan_int8_gemm(int64_t M, int64_t N, int64_t K, int cus) {
   GemmPlan p{};
@@ -507,16 +719,45 @@ GemmPlan plan_int8_gemm(int64_t M, int64_t N, int64_t K, int cus) {
   const int R = T % cus;
   if (R == 0) return p;
   const int nk = static_cast<int>(K / kBK);
-  const int smax = std::min(std::min(cus / R, nk / kMinSliceSteps), kMaxSplit);
-  int best = 1, best_cost = 3 * nk / 4;
-  for (int s = 2; s <= smax; ++s) {
-    const int cost = (nk + s - 1) / s + kSliceCost * (s - 1) + kSliceFixed;
-    if (cost < best_cost) best = s, best_cost = cost;
+  double best_cost = 0.75 * nk;
+  int best_split = 1;
+  bool best_small = false;
+  const int smax = std::min(nk / kMinSliceSteps, kMaxSplit);
+  for (int s = 2; s <= std::min(cus / R, smax); ++s) {
+    const double cost = (nk + s - 1) / s + kSliceCost * (s - 1) + kSliceFixed;
+    if (cost < best_cost) best_cost = cost, best_split = s, best_small = false;
   }
-  if (best == 1) return p;
+  for (int s = 1; s <= smax; ++s) {
+    const int per_cu = (4 * R * s + cus - 1) / cus;
+    const double cost = per_cu * (kSmallStep * ((nk + s - 1) / s) + kSmallFixed) + kSmallSlice * (s - 1);
+    if (cost < best_cost) best_cost = cost, best_split = s, best_small = true;
+  }
+  if (best_split == 1 && !best_small) return p;
   p.dp_tiles = T - R;
-  p.split = best;
+  p.split = best_split;
   p.sk_tiles = R;
+  p.small = best_small;
+  return p;
+}
+
+// The same grid with a given treatment of the leftover tiles: small = false
+// and split = 1 runs every tile whole; otherwise the R = T mod cus leftover
+// tiles (all tiles when T < cus) run as `split` slices of 256x256 tiles or, with
+// small, of 128x128 quarters. split must be in [1, K / 64] and K % 64 == 0.
+GemmPlan plan_int8_gemm_forced(int64_t M, int64_t N, int cus, bool small, int split) {
+  GemmPlan p{};
+  p.tiles_m = static_cast<int>((M + kBM - 1) / kBM);
+  p.tiles_n = static_cast<int>((N + kBN - 1) / kBN);
+  const int T = p.tiles_m * p.tiles_n;
+  const int R = cus > 0 ? T % cus : T;
+  p.dp_tiles = T;
+  p.split = 1;
+  p.sk_tiles = 0;
+  if ((split <= 1 && !small) || R == 0) return p;
+  p.dp_tiles = T - R;
+  p.split = split;
+  p.sk_tiles = R;
+  p.small = small;
   return p;
 }
 
@@ -534,9 +775,9 @@ void launch_int8_gemm(const int8_t* A, const int8_t* B, int64_t M, int64_t N, in
   const dim3 block(256);
   if (K % kBK == 0) {
     constexpr int S = 4;
-    const dim3 grid(plan.dp_tiles + plan.sk_tiles * plan.split);
-#define W8_GEMM_ARGS A, B, m, n, k, sx, sw, nO, XO, WO, Y, tiles_m, tiles_n, plan.dp_tiles, plan.split, part, cnt, \
-    clear, clear_words
+    const dim3 grid(plan.grid());
+#define W8_GEMM_ARGS A, B, m, n, k, sx, sw, nO, XO, WO, Y, tiles_m, tiles_n, plan.dp_tiles, plan.split, \
+    plan.small ? 1 : 0, part, cnt, clear, clear_words
     if (mode == 0) k_int8_gemm_dma<0, true, S><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
     else if (mode == 1 && xbf16) k_int8_gemm_dma<1, true, S><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
     else if (mode == 1) k_int8_gemm_dma<1, false, S><<<grid, block, 0, s>>>(W8_GEMM_ARGS);

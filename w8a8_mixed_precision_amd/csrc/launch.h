@@ -9,14 +9,23 @@ namespace w8 {
 
 // Grid of the tiled GEMMs: dp_tiles whole tiles of bm x bm outputs, then
 // sk_tiles tiles cut into `split` K-slices each (split == 1: none). The int8
-// GEMM always uses bm = 256; the FP8 GEMM uses 256 or 128.
+// GEMM uses bm = 256, and with `small` runs each of the sk_tiles leftover
+// tiles as four 128x128 blocks (each cut into `split` slices); the FP8 GEMM
+// uses bm = 256 or 128.
 struct GemmPlan {
   int tiles_m, tiles_n, dp_tiles, split, sk_tiles;
   int bm = 256;
-  size_t partial_bytes() const { return split > 1 ? size_t(sk_tiles) * split * bm * bm * 4 : 0; }
-  int counters() const { return split > 1 ? sk_tiles : 0; }
+  bool small = false;
+  int units() const { return small ? 4 * sk_tiles : sk_tiles; }       // blocks per K-slice past dp_tiles
+  int grid() const { return dp_tiles + units() * split; }
+  size_t partial_bytes() const {
+    const size_t b = small ? 128 * 128 * 4 : size_t(bm) * bm * 4;
+    return split > 1 ? size_t(units()) * split * b : 0;
+  }
+  int counters() const { return split > 1 ? units() : 0; }
 };
 GemmPlan plan_int8_gemm(int64_t M, int64_t N, int64_t K, int cus);
+GemmPlan plan_int8_gemm_forced(int64_t M, int64_t N, int cus, bool small, int split);
 
 void launch_int8_rows(const void* X, bool bf16, int64_t rows, int K, uint32_t tbits, int8_t* q, float* sx,
                       uint8_t* flags, hipStream_t s);
