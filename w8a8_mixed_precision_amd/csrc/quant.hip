@@ -200,6 +200,7 @@ __global__ __launch_bounds__(256) void k_int8_rows_long(const uint16_t* __restri
 // entries; a larger set takes the per-row loops).
 constexpr int kFixRows = 64;
 constexpr int kOcap = 4096;
+constexpr int kGatherUnroll = 8;
 
 size_t outlier_fixup_lds_bytes(int K) {
   return static_cast<size_t>(2) * ((K + 31) / 32) * 4 + static_cast<size_t>(kOcap) * 4;
@@ -294,12 +295,34 @@ __global__ __launch_bounds__(256) void k_outlier_fixup(
       return v;
     };
     if (listed) {
-#pragma unroll 8
-      for (int idx = tid; idx < rows * P; idx += 256) {
-        const int r = idx / P, j = idx - r * P;
-        const int64_t m = r0 + r;
-        const uint16_t v = (j < nO) ? take(r, m, sO[j]) : uint16_t(0);
-        if (XO) XO[m * P + j] = v;
+      // 8 entries per thread per round: all 8 loads go out before any store
+      // (loads of padding entries read X[0] and are discarded), so a round
+      // costs one memory latency, not eight
+      const int total = rows * P;
+      for (int base = 0; base < total; base += 256 * kGatherUnroll) {
+        uint16_t v[kGatherUnroll];
+#pragma unroll
+        for (int u = 0; u < kGatherUnroll; ++u) {
+          const int idx = base + tid + 256 * u;
+          const int r = idx / P, j = idx - r * P;
+          const bool live = idx < total && j < nO;
+          v[u] = X[live ? static_cast<int64_t>(r0 + r) * K + sO[j] : 0];
+        }
+#pragma unroll
+        for (int u = 0; u < kGatherUnroll; ++u) {
+          const int idx = base + tid + 256 * u;
+          if (idx >= total) break;
+          const int r = idx / P, j = idx - r * P;
+          const int64_t m = r0 + r;
+          uint16_t val = 0;
+          if (j < nO) {
+            val = v[u];
+            q[m * K + sO[j]] = 0;
+            const uint32_t mag = val & 0x7FFFu;
+            if (mag <= tbits) atomicMax(&somax[r], mag);
+          }
+          if (XO) XO[m * P + j] = val;
+        }
       }
     } else {
       for (int r = 0; r < rows; ++r) {
@@ -367,11 +390,24 @@ __global__ __launch_bounds__(256) void k_outlier_fixup(
       return BF16 ? static_cast<uint16_t>(__float_as_uint(f) >> 16) : f32_to_f16_bits(f);
     };
     if (listed) {
-#pragma unroll 8
-      for (int idx = tid; idx < rows * P; idx += 256) {
-        const int r = idx / P, j = idx - r * P;
-        const int64_t n = r0 + r;
-        WO[n * P + j] = (j < nO) ? cvt(Wq[n * K + sO[j]]) : uint16_t(0);
+      // as for XO: the round's loads go out together (padding reads Wq[0])
+      const int total = rows * P;
+      for (int base = 0; base < total; base += 256 * kGatherUnroll) {
+        int8_t v[kGatherUnroll];
+#pragma unroll
+        for (int u = 0; u < kGatherUnroll; ++u) {
+          const int idx = base + tid + 256 * u;
+          const int r = idx / P, j = idx - r * P;
+          const bool live = idx < total && j < nO;
+          v[u] = Wq[live ? static_cast<int64_t>(r0 + r) * K + sO[j] : 0];
+        }
+#pragma unroll
+        for (int u = 0; u < kGatherUnroll; ++u) {
+          const int idx = base + tid + 256 * u;
+          if (idx >= total) break;
+          const int r = idx / P, j = idx - r * P;
+          WO[static_cast<int64_t>(r0 + r) * P + j] = j < nO ? cvt(v[u]) : uint16_t(0);
+        }
       }
     } else {
       for (int r = 0; r < rows; ++r) {
