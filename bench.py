@@ -132,6 +132,69 @@ def weight_quant(torch, w8, cases, steps: int) -> dict:
     return res
 
 
+def counter_workload(torch, w8, cases, steps: int, copy_mib: int) -> None:
+    """Minimal run for hardware-counter collection: `steps` int8 steps (after
+    one warm-up step), then three plain device copies of `copy_mib` MiB, the
+    calibration for the byte counters (a copy reads and writes exactly that
+    many bytes)."""
+    xs, wqs, sws, ys, wss = _prepare(torch, w8, cases)
+    for _ in range(1 + steps):
+        for i in range(len(cases)):
+            w8.int8_mixed_linear(xs[i], wqs[i], sws[i], THRESHOLD, out=ys[i], workspace=wss[i])
+    torch.cuda.synchronize()
+    n = copy_mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[bench] counter workload done: {steps} steps, 3 copies of {copy_mib} MiB", file=sys.stderr, flush=True)
+
+
+def _prepare(torch, w8, cases):
+    """Inputs resident in HBM, weights quantized once (untimed)."""
+    xs, wqs, sws, ys, wss = [], [], [], [], []
+    for c in cases:
+        xs.append(_dev16(c.x_bits, torch))
+        wq, sw = w8.quantize_weight_rowwise(_dev16(c.w_bits, torch), "int8")
+        wqs.append(wq)
+        sws.append(sw)
+        ys.append(torch.empty((c.M, c.N), dtype=torch.float16, device="cuda"))
+        wss.append(w8.new_workspace(w8.int8_mixed_linear_workspace_size(c.M, c.N, c.K)))
+    torch.cuda.synchronize()
+    return xs, wqs, sws, ys, wss
+
+
+def recorded_traffic(w8) -> float | None:
+    """HBM bytes per launch of the int8 GEMM from the committed counter record
+    (profiles/k_int8_gemm_dit1024_traffic.md), or None when there is none or
+    the GEMM sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "k_int8_gemm_dit1024_traffic.md")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if line.startswith("traffic_bytes_per_launch:") or line.startswith("sources_sha256:"):
+            k, v = line.split(":", 1)
+            rec[k] = v.strip()
+    if "traffic_bytes_per_launch" not in rec or "sources_sha256" not in rec:
+        return None
+    if rec["sources_sha256"] != gemm_sources_sha256():
+        return None
+    return float(rec["traffic_bytes_per_launch"])
+
+
+def gemm_sources_sha256() -> str:
+    """Digest of the sources the int8 GEMM kernel is built from."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in ("gemm_int8.hip", "tile.h", "common.h"):
+        with open(os.path.join(ROOT, "w8a8_mixed_precision_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +203,8 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=4352, help="token rows per shape for the oracle baseline (4352 = the whole step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 W8A8 text-encoder layer timings")
+    ap.add_argument("--counters", type=int, default=0, metavar="MIB",
+                    help="counter-collection mode: a few int8 steps, then plain copies of MIB MiB; no JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the sharding design is "
@@ -156,16 +221,12 @@ def main() -> int:
     cases = synth.dit_1024_block()
     print(f"[bench] workload: {[c.name for c in cases]}", file=sys.stderr, flush=True)
 
+    if args.counters:
+        counter_workload(torch, w8, cases, args.steps, args.counters)
+        return 0
+
     # inputs resident in HBM, weights quantized once (untimed)
-    xs, wqs, sws, ys, wss = [], [], [], [], []
-    for c in cases:
-        xs.append(_dev16(c.x_bits, torch))
-        wq, sw = w8.quantize_weight_rowwise(_dev16(c.w_bits, torch), "int8")
-        wqs.append(wq)
-        sws.append(sw)
-        ys.append(torch.empty((c.M, c.N), dtype=torch.float16, device="cuda"))
-        wss.append(w8.new_workspace(w8.int8_mixed_linear_workspace_size(c.M, c.N, c.K)))
-    torch.cuda.synchronize()
+    xs, wqs, sws, ys, wss = _prepare(torch, w8, cases)
 
     def step():
         for i in range(len(cases)):
@@ -242,7 +303,7 @@ def main() -> int:
             "peak": PEAK_INT8_TOPS,
             "unit": "TFLOP/s",
             "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(w8),
             "avg_launch_us": round(gemm_avg_ms * 1e3, 2),
         },
         "per_shape": per_shape,
