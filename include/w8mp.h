@@ -117,6 +117,53 @@ w8_status int8_mixed_linear(const void* X, int x_dt, int64_t M, int64_t K,
                             void* stream);
 
 /*
+ * The op that produces X, for int8_mixed_linear_fused. X is made from H in the
+ * quantisation pass itself and never stored. Each producer is a fixed sequence
+ * of fp32 operations, each rounded to nearest even and none fused, so X is
+ * well defined element by element. X = that fp32 result rounded to nearest
+ * even in H's 16-bit type:
+ *   W8_PRODUCER_RMSNORM: RMSNorm (Zhang and Sennrich, 2019) with the
+ *     x(1+scale)+shift modulation of adaptive layer norm (Peebles and Xie,
+ *     2023). Per row:
+ *       ss   = sum_k H[m,k]^2 in fp64 (each square is exact);
+ *       rstd = fl32(1 / fl32(sqrt(fl32(fl32(ss/K) + eps))));
+ *       x    = fl32(fl32(H*rstd) * fl32(gamma[k] * fl32(1 + scale[k]))) + shift[k].
+ *     gamma (NULL: 1), scale (NULL: 0) and shift (NULL: no addition) are fp32
+ *     [K] device vectors.
+ *   W8_PRODUCER_GELU_TANH: GELU, tanh form (Hendrycks and Gimpel, 2016),
+ *     evaluated as H / (1 + exp(-2u)) with u = sqrt(2/pi)(H + 0.044715 H^3).
+ *     This equals 0.5 H (1 + tanh u). exp uses Cody-Waite reduction and a
+ *     degree-6 Taylor polynomial (about 2 ulp).
+ */
+typedef enum { W8_PRODUCER_NONE = 0, W8_PRODUCER_RMSNORM = 1, W8_PRODUCER_GELU_TANH = 2 } w8_producer_kind;
+typedef struct w8_producer {
+  int kind;              /* w8_producer_kind */
+  const float* gamma;    /* RMSNorm gain [K], device, or NULL */
+  const float* scale;    /* modulation scale [K], device, or NULL */
+  const float* shift;    /* modulation shift [K], device, or NULL */
+  float eps;             /* RMSNorm epsilon: finite, >= 0 */
+} w8_producer;
+
+/*
+ * int8_mixed_linear_fused -- Y = producer(H) W^T + bias, with the LLM.int8
+ * decomposition of int8_mixed_linear applied to X = producer(H).
+ *
+ *   H          [M,K] f16 or bf16 (h_dt), device: the producer's input. X has
+ *              H's type.
+ *   producer   NULL or kind W8_PRODUCER_NONE: X = H (this call is then
+ *              int8_mixed_linear plus the bias). A producer needs
+ *              K <= 16384 (else W8_ERR_UNSUPPORTED).
+ *   bias       NULL or fp32 [N], device: added to the fp32 epilogue result
+ *              before the rounding into Y.
+ * All other arguments, the workspace (int8_mixed_linear_workspace_size) and
+ * the result are as for int8_mixed_linear.
+ */
+w8_status int8_mixed_linear_fused(const void* H, int h_dt, int64_t M, int64_t K,
+                                  const w8_producer* producer, const int8_t* Wq, const float* sw,
+                                  const float* bias, int64_t N, float threshold, void* Y, int y_dt,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * fp8_w8a8_linear -- Y = X W^T with E4M3 weights and activations.
  *
  *   X          [M,K] f16 or bf16, device.
@@ -154,16 +201,23 @@ const char* w8_last_error(void);
  * written to caller buffers. Used by the test suite.
  * ------------------------------------------------------------------------ */
 
-/* The activation half of int8_mixed_linear (outlier detection, row scales,
- * int8 codes, outlier fix-up). Outputs (device): q [M,K] int8, sx [M] fp32,
- * outlier_idx [K] int32 (first *n_outliers entries valid, ascending),
- * n_outliers [1] int32. Workspace: w8dbg_int8_quantize_activations_workspace_size(M, K)
- * bytes, zero-filled before first use (left zero by every call). */
+/* The activation half of int8_mixed_linear_fused (X from H by `producer`, NULL
+ * for none; outlier detection, row scales, int8 codes, outlier fix-up).
+ * Outputs (device): q [M,K] int8, sx [M] fp32, outlier_idx [K] int32 (first
+ * *n_outliers entries valid, ascending), n_outliers [1] int32. Workspace:
+ * w8dbg_int8_quantize_activations_workspace_size(M, K) bytes, zero-filled
+ * before first use (left zero by every call). */
 size_t w8dbg_int8_quantize_activations_workspace_size(int64_t M, int64_t K);
 w8_status w8dbg_int8_quantize_activations(const void* X, int x_dt, int64_t M, int64_t K,
-                                          float threshold, int8_t* q, float* sx,
-                                          int32_t* outlier_idx, int32_t* n_outliers,
-                                          void* workspace, size_t workspace_bytes, void* stream);
+                                          const w8_producer* producer, float threshold,
+                                          int8_t* q, float* sx, int32_t* outlier_idx,
+                                          int32_t* n_outliers, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
+/* X = producer(H) written out [M,K] in H's 16-bit type (the values the fused
+ * quantisation pass makes in registers). */
+w8_status w8dbg_produce(const void* H, int h_dt, int64_t M, int64_t K, const w8_producer* producer,
+                        void* X, void* stream);
 
 /* The int8 MFMA contraction alone: acc [M,N] int32 = q [M,K] . Wq [N,K]^T.
  * tail = 0: the grid int8_mixed_linear would use (split ignored). Otherwise

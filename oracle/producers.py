@@ -122,13 +122,15 @@ def produce(h_bits, h_dtype: str, kind: str, gamma=None, scale=None, shift=None,
 
 
 def fused_int8_linear(h_bits, h_dtype, kind, wq, sw, threshold, bias=None, out_dtype="f16", rows=None,
-                      gamma=None, scale=None, shift=None, eps: float = 1e-6):
+                      gamma=None, scale=None, shift=None, eps: float = 1e-6, x_bits=None):
     """Y = producer(H) W^T + bias under the LLM.int8 decomposition.
 
     The producer gives X exactly as a separate producer op would store it (16-bit);
     the linear is ``w8ref.int8_mixed_linear``; bias (float32 [N]) is added to the
-    float64 result before the single final rounding."""
-    x_bits = produce(h_bits, h_dtype, kind, gamma, scale, shift, eps)
+    float64 result before the single final rounding. ``x_bits``: X already made
+    by ``produce`` with the same arguments (saves recomputing it)."""
+    if x_bits is None:
+        x_bits = produce(h_bits, h_dtype, kind, gamma, scale, shift, eps)
     ref = w8ref.int8_mixed_linear(x_bits, h_dtype, wq, sw, threshold, out_dtype, rows=rows)
     y = ref["y"]
     if bias is not None:

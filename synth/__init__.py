@@ -220,3 +220,73 @@ def dit_2048(part: str, m_rows: int | None = None) -> LinearCase:
 def dit_1024_block() -> list[LinearCase]:
     """The three quantized linears of one DiT block at 1024^2."""
     return [dit_qkv_1024(), dit_mlp_1024("up"), dit_mlp_1024("down")]
+
+
+@dataclass
+class FusedCase:
+    """One producer-fused linear: H [M,K] (16-bit patterns) is the producer's
+    input, X = producer(H) the linear's. RMSNorm cases carry float32 gain,
+    modulation scale and shift vectors [K]; every case a float32 bias [N]."""
+
+    name: str
+    kind: str                # "rmsnorm" or "gelu"
+    M: int
+    K: int
+    N: int
+    h_bits: np.ndarray
+    h_dtype: str
+    w_bits: np.ndarray
+    w_dtype: str
+    bias: np.ndarray
+    gamma: np.ndarray | None = None
+    scale: np.ndarray | None = None
+    shift: np.ndarray | None = None
+    eps: float = 1e-6
+    threshold: float = THRESHOLD
+
+    @property
+    def ops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+
+def fused_case(kind: str, M: int, K: int, N: int, seed: int, dtype: str = "bf16", name: str | None = None,
+               outlier_cols: int = 4, massive: bool = False) -> FusedCase:
+    """Seeded producer-fused linear.
+
+    rmsnorm: H is a residual stream ~N(0,1) whose ``outlier_cols`` channels run
+    at +-U(20,60) (they stay above the threshold after normalisation), with
+    optional massive activations (~9000 in channel 2276 of 8 text-token rows,
+    as in ``_dit_x``); gain ~U(0.5,1.5), modulation scale ~U(-0.5,0.5), shift
+    ~U(-1,1). gelu: H is an MLP hidden state ~N(0,1.5^2) whose ``outlier_cols``
+    channels run at +-U(6,60) (GELU keeps the positive ones, zeroes the
+    negative ones). Weights ~N(0,0.02), bias ~N(0,0.1)."""
+    rng = np.random.default_rng(seed)
+    std = 1.0 if kind == "rmsnorm" else 1.5
+    h = _normal(rng, (M, K), std)
+    lo, hi = (20.0, 60.0) if kind == "rmsnorm" else (6.0, 60.0)
+    if outlier_cols:
+        for c in rng.choice(K, size=min(outlier_cols, K), replace=False):
+            h[:, int(c)] = _signed_uniform(rng, M, lo, hi)
+    if massive and K > 2276:
+        rows = [4096 + 32 * r for r in range(8) if 4096 + 32 * r < M]
+        h[rows, 2276] = rng.uniform(8500.0, 9500.0, size=len(rows)).astype(np.float32)
+    w = _normal(np.random.default_rng(seed + 1), (N, K), 0.02)
+    prng = np.random.default_rng(seed + 2)
+    bias = (prng.standard_normal(N) * 0.1).astype(np.float32)
+    gamma = scale = shift = None
+    if kind == "rmsnorm":
+        gamma = prng.uniform(0.5, 1.5, K).astype(np.float32)
+        scale = prng.uniform(-0.5, 0.5, K).astype(np.float32)
+        shift = prng.uniform(-1.0, 1.0, K).astype(np.float32)
+    return FusedCase(name or f"{kind}_{M}x{K}x{N}_s{seed}", kind, M, K, N, encode16(h, dtype), dtype,
+                     encode16(w, dtype), dtype, bias, gamma, scale, shift)
+
+
+def dit_mlp_fused_1024() -> list[FusedCase]:
+    """The DiT 1024^2 MLP with its producers: up = (RMSNorm + modulation of the
+    residual stream) -> 4096 x 16384, down = GELU(hidden) -> 16384 x 4096."""
+    i = 5
+    return [fused_case("rmsnorm", 4352, 4096, 16384, 1000 * i + 1, name="dit1024_mlp_up_rmsnorm_4352x4096x16384",
+                       massive=True),
+            fused_case("gelu", 4352, 16384, 4096, 1000 * i + 11, name="dit1024_mlp_down_gelu_4352x16384x4096",
+                       outlier_cols=16)]

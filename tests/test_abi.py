@@ -72,6 +72,37 @@ def test_int8_mixed_linear_rejects(kw, status):
     assert _abi.lib().w8_last_error().decode() != ""
 
 
+def _fused(prod=None, **kw):
+    a = dict(X=A, x_dt=_abi.W8_DT_BF16, M=64, K=256, Wq=A, sw=A, bias=None, N=32, t=6.0, Y=A,
+             y_dt=_abi.W8_DT_F16, ws=A, ws_bytes=WS_BIG, stream=None)
+    a.update(kw)
+    p = ctypes.byref(prod) if prod is not None else None
+    return _abi.lib().int8_mixed_linear_fused(a["X"], a["x_dt"], a["M"], a["K"], p, a["Wq"], a["sw"], a["bias"],
+                                              a["N"], a["t"], a["Y"], a["y_dt"], a["ws"], a["ws_bytes"],
+                                              a["stream"])
+
+
+@pytest.mark.parametrize("prod,kw,status", [
+    (_abi.Producer(7, None, None, None, 0.0), {}, _abi.W8_ERR_INVALID_ARGUMENT),            # unknown kind
+    (_abi.Producer(_abi.W8_PRODUCER_RMSNORM, None, None, None, -1.0), {}, _abi.W8_ERR_INVALID_ARGUMENT),
+    (_abi.Producer(_abi.W8_PRODUCER_RMSNORM, None, None, None, math.nan), {}, _abi.W8_ERR_INVALID_ARGUMENT),
+    (_abi.Producer(_abi.W8_PRODUCER_GELU_TANH, None, None, None, 0.0), dict(K=16400), _abi.W8_ERR_UNSUPPORTED),
+    (None, dict(X=None), _abi.W8_ERR_INVALID_ARGUMENT),
+    (None, dict(ws_bytes=1024), _abi.W8_ERR_WORKSPACE),
+])
+def test_int8_fused_linear_rejects(prod, kw, status):
+    assert _fused(prod, **kw) == status
+    assert _abi.lib().w8_last_error().decode() != ""
+
+
+def test_debug_produce_rejects():
+    lib = _abi.lib()
+    gelu = _abi.Producer(_abi.W8_PRODUCER_GELU_TANH, None, None, None, 0.0)
+    assert lib.w8dbg_produce(None, _abi.W8_DT_BF16, 4, 64, ctypes.byref(gelu), A, None) == \
+        _abi.W8_ERR_INVALID_ARGUMENT
+    assert lib.w8dbg_produce(A, _abi.W8_DT_BF16, 4, 32768, ctypes.byref(gelu), A, None) == _abi.W8_ERR_UNSUPPORTED
+
+
 def test_workspace_size_is_exact_boundary():
     lib = _abi.lib()
     need = lib.int8_mixed_linear_workspace_size(64, 32, 256)
@@ -130,7 +161,7 @@ def test_debug_exports_reject():
     assert lib.w8dbg_int8_gemm_i32(A, A, 4, 4, 128, 2, 2, A, A, 1024, None) == _abi.W8_ERR_WORKSPACE
     assert lib.w8dbg_fp8_quantize_activations(A, _abi.W8_DT_BF16, 4, 20, None, A, A, None) == \
         _abi.W8_ERR_INVALID_ARGUMENT
-    assert lib.w8dbg_int8_quantize_activations(A, _abi.W8_DT_BF16, 4, 32, 6.0, A, A, A, A, A, 1,
+    assert lib.w8dbg_int8_quantize_activations(A, _abi.W8_DT_BF16, 4, 32, None, 6.0, A, A, A, A, A, 1,
                                                None) == _abi.W8_ERR_WORKSPACE
     f8 = lib.w8dbg_fp8_gemm
     bf = _abi.W8_DT_BF16

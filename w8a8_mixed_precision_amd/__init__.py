@@ -14,7 +14,7 @@ from ._abi import W8Error, lib  # noqa: F401
 _DT = {torch.float16: _abi.W8_DT_F16, torch.bfloat16: _abi.W8_DT_BF16, torch.float32: _abi.W8_DT_F32}
 
 __all__ = [
-    "quantize_weight_rowwise", "int8_mixed_linear", "fp8_w8a8_linear",
+    "quantize_weight_rowwise", "int8_mixed_linear", "fp8_w8a8_linear", "Producer", "debug_produce",
     "debug_int8_quantize_activations", "debug_int8_gemm_i32", "debug_fp8_quantize_activations", "debug_fp8_gemm",
     "int8_mixed_linear_workspace_size", "fp8_w8a8_linear_workspace_size", "new_workspace", "W8Error",
 ]
@@ -76,21 +76,68 @@ def quantize_weight_rowwise(w: torch.Tensor, fmt: str = "int8"):
     return wq, sw
 
 
+class Producer:
+    """The op that produces X from H, fused into the int8 quantisation pass
+    (struct w8_producer in include/w8mp.h): kind "rmsnorm" (RMSNorm with the
+    optional gain gamma, modulation scale and shift, fp32 [K] GPU tensors, and
+    eps) or "gelu" (tanh form)."""
+
+    KINDS = {"none": _abi.W8_PRODUCER_NONE, "rmsnorm": _abi.W8_PRODUCER_RMSNORM, "gelu": _abi.W8_PRODUCER_GELU_TANH}
+
+    def __init__(self, kind: str, gamma: torch.Tensor | None = None, scale: torch.Tensor | None = None,
+                 shift: torch.Tensor | None = None, eps: float = 1e-6):
+        if kind not in self.KINDS:
+            raise ValueError(f"producer kind {kind!r}")
+        for name, v in (("gamma", gamma), ("scale", scale), ("shift", shift)):
+            if v is not None:
+                _dev(v, name)
+                if v.dtype != torch.float32 or v.dim() != 1:
+                    raise ValueError(f"{name} must be a 1-D fp32 tensor")
+        self.kind, self.gamma, self.scale, self.shift, self.eps = kind, gamma, scale, shift, float(eps)
+
+    def struct(self, K: int) -> "_abi.Producer":
+        for name, v in (("gamma", self.gamma), ("scale", self.scale), ("shift", self.shift)):
+            if v is not None and v.numel() != K:
+                raise ValueError(f"{name} must have K = {K} entries")
+        ptr = lambda v: v.data_ptr() if v is not None else None
+        return _abi.Producer(self.KINDS[self.kind], ptr(self.gamma), ptr(self.scale), ptr(self.shift), self.eps)
+
+
+def _producer_arg(producer: "Producer | None", K: int):
+    import ctypes
+
+    return None if producer is None else ctypes.byref(producer.struct(K))
+
+
 def int8_mixed_linear(x: torch.Tensor, wq: torch.Tensor, sw: torch.Tensor, threshold: float = 6.0,
                       out_dtype: torch.dtype = torch.float16, out: torch.Tensor | None = None,
-                      workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """Y = X W^T under the LLM.int8 decomposition (see include/w8mp.h)."""
+                      workspace: torch.Tensor | None = None, bias: torch.Tensor | None = None,
+                      producer: Producer | None = None) -> torch.Tensor:
+    """Y = X W^T (+ bias) under the LLM.int8 decomposition (see include/w8mp.h).
+    With `producer`, x is the producer's input H and X = producer(H) is made in
+    the quantisation pass (int8_mixed_linear_fused)."""
     _dev(x, "x"), _dev(wq, "wq"), _dev(sw, "sw")
     M, K = x.shape
     N = wq.shape[0]
     if wq.shape[1] != K or wq.dtype != torch.int8 or sw.shape != (N,) or sw.dtype != torch.float32:
         raise ValueError("wq must be int8 [N,K] and sw fp32 [N]")
+    if bias is not None:
+        _dev(bias, "bias")
+        if bias.shape != (N,) or bias.dtype != torch.float32:
+            raise ValueError("bias must be fp32 [N]")
     y = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=x.device)
     need = int8_mixed_linear_workspace_size(M, N, K)
     ws = workspace if workspace is not None else _workspace(need, x.device)
-    _abi.check(lib().int8_mixed_linear(x.data_ptr(), _dt(x), M, K, wq.data_ptr(), sw.data_ptr(), N,
-                                       float(threshold), y.data_ptr(), _dt(y), ws.data_ptr(), ws.numel(),
-                                       _stream(x)))
+    if bias is None and producer is None:
+        _abi.check(lib().int8_mixed_linear(x.data_ptr(), _dt(x), M, K, wq.data_ptr(), sw.data_ptr(), N,
+                                           float(threshold), y.data_ptr(), _dt(y), ws.data_ptr(), ws.numel(),
+                                           _stream(x)))
+    else:
+        _abi.check(lib().int8_mixed_linear_fused(x.data_ptr(), _dt(x), M, K, _producer_arg(producer, K),
+                                                 wq.data_ptr(), sw.data_ptr(),
+                                                 bias.data_ptr() if bias is not None else None, N,
+                                                 float(threshold), y.data_ptr(), _dt(y), ws.data_ptr(), ws.numel(),
+                                                 _stream(x)))
     return y
 
 
@@ -111,8 +158,9 @@ def fp8_w8a8_linear(x: torch.Tensor, wq8: torch.Tensor, sw: torch.Tensor, act_sc
     return y
 
 
-def debug_int8_quantize_activations(x: torch.Tensor, threshold: float = 6.0):
-    """(q int8 [M,K], sx fp32 [M], outlier column indices int32 [nO])."""
+def debug_int8_quantize_activations(x: torch.Tensor, threshold: float = 6.0, producer: Producer | None = None):
+    """(q int8 [M,K], sx fp32 [M], outlier column indices int32 [nO]) of X, or of
+    X = producer(x)."""
     _dev(x, "x")
     M, K = x.shape
     q = torch.empty((M, K), dtype=torch.int8, device=x.device)
@@ -120,10 +168,20 @@ def debug_int8_quantize_activations(x: torch.Tensor, threshold: float = 6.0):
     idx = torch.empty((K,), dtype=torch.int32, device=x.device)
     n = torch.empty((1,), dtype=torch.int32, device=x.device)
     ws = _workspace(int(lib().w8dbg_int8_quantize_activations_workspace_size(M, K)), x.device)
-    _abi.check(lib().w8dbg_int8_quantize_activations(x.data_ptr(), _dt(x), M, K, float(threshold), q.data_ptr(),
-                                                     sx.data_ptr(), idx.data_ptr(), n.data_ptr(), ws.data_ptr(),
-                                                     ws.numel(), _stream(x)))
+    _abi.check(lib().w8dbg_int8_quantize_activations(x.data_ptr(), _dt(x), M, K, _producer_arg(producer, K),
+                                                     float(threshold), q.data_ptr(), sx.data_ptr(), idx.data_ptr(),
+                                                     n.data_ptr(), ws.data_ptr(), ws.numel(), _stream(x)))
     return q, sx, idx[: int(n.item())]
+
+
+def debug_produce(h: torch.Tensor, producer: Producer) -> torch.Tensor:
+    """X = producer(H), [M,K] in H's 16-bit type."""
+    _dev(h, "h")
+    M, K = h.shape
+    x = torch.empty_like(h)
+    _abi.check(lib().w8dbg_produce(h.data_ptr(), _dt(h), M, K, _producer_arg(producer, K), x.data_ptr(),
+                                   _stream(h)))
+    return x
 
 
 def debug_int8_gemm_i32(q: torch.Tensor, wq: torch.Tensor, tail: int = 0, split: int = 1,

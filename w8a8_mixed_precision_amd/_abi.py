@@ -13,6 +13,7 @@ W8_OK, W8_ERR_INVALID_ARGUMENT, W8_ERR_UNSUPPORTED, W8_ERR_WORKSPACE, W8_ERR_HIP
 W8_DT_F16, W8_DT_BF16, W8_DT_F32 = range(3)
 W8_Q_INT8, W8_Q_FP8_E4M3 = range(2)
 W8_INT8_MAX_K = 133144
+W8_PRODUCER_NONE, W8_PRODUCER_RMSNORM, W8_PRODUCER_GELU_TANH = range(3)
 
 _p = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -20,17 +21,26 @@ _int = ctypes.c_int
 _size = ctypes.c_size_t
 _f = ctypes.c_float
 
+
+class Producer(ctypes.Structure):
+    """struct w8_producer of include/w8mp.h."""
+    _fields_ = [("kind", ctypes.c_int), ("gamma", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                ("shift", ctypes.c_void_p), ("eps", ctypes.c_float)]
+
+
 # name -> (restype, argtypes)
 SIGNATURES = {
     "quantize_weight_rowwise": (_int, [_p, _int, _i64, _i64, _int, _p, _p, _p]),
     "int8_mixed_linear_workspace_size": (_size, [_i64, _i64, _i64]),
     "int8_mixed_linear": (_int, [_p, _int, _i64, _i64, _p, _p, _i64, _f, _p, _int, _p, _size, _p]),
+    "int8_mixed_linear_fused": (_int, [_p, _int, _i64, _i64, _p, _p, _p, _p, _i64, _f, _p, _int, _p, _size, _p]),
     "fp8_w8a8_linear_workspace_size": (_size, [_i64, _i64, _i64]),
     "fp8_w8a8_linear": (_int, [_p, _int, _i64, _i64, _p, _p, _i64, _p, _p, _int, _p, _size, _p]),
     "w8_status_string": (ctypes.c_char_p, [_int]),
     "w8_last_error": (ctypes.c_char_p, []),
     "w8dbg_int8_quantize_activations_workspace_size": (_size, [_i64, _i64]),
-    "w8dbg_int8_quantize_activations": (_int, [_p, _int, _i64, _i64, _f, _p, _p, _p, _p, _p, _size, _p]),
+    "w8dbg_int8_quantize_activations": (_int, [_p, _int, _i64, _i64, _p, _f, _p, _p, _p, _p, _p, _size, _p]),
+    "w8dbg_produce": (_int, [_p, _int, _i64, _i64, _p, _p, _p]),
     "w8dbg_int8_gemm_i32_workspace_size": (_size, [_i64, _i64, _i64, _int, _int]),
     "w8dbg_int8_gemm_i32": (_int, [_p, _p, _i64, _i64, _i64, _int, _int, _p, _p, _size, _p]),
     "w8dbg_fp8_quantize_activations": (_int, [_p, _int, _i64, _i64, _p, _p, _p, _p]),

@@ -78,7 +78,7 @@ int cu_count() {
 // Workspace layout of int8_mixed_linear (offsets from the 256-aligned base).
 // flags and cnt are the bookkeeping that every call leaves zero again.
 struct Int8Ws {
-  size_t q, sx, flags, cnt, nO, O, XO, WO, part, total;
+  size_t q, sx, rstd, flags, cnt, nO, O, XO, WO, part, total;
   w8::GemmPlan plan;
 };
 
@@ -89,6 +89,7 @@ Int8Ws int8_layout(int64_t M, int64_t N, int64_t K) {
   size_t off = 0;
   w.q = off;     off = up(off + static_cast<size_t>(M) * K);
   w.sx = off;    off = up(off + 4 * static_cast<size_t>(M));
+  w.rstd = off;  off = up(off + 4 * static_cast<size_t>(M));
   w.flags = off; off = up(off + static_cast<size_t>(K));
   w.cnt = off;   off = up(off + 4 * static_cast<size_t>(w.plan.counters()));
   w.nO = off;    off = up(off + 4);
@@ -261,7 +262,8 @@ w8_status quantize_weight_rowwise(const void* W, int w_dt, int64_t N, int64_t K,
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = w_dt == W8_DT_BF16;
   if (fmt == W8_Q_INT8)
-    w8::launch_int8_rows(W, bf, N, (int)K, 0x7F80u, static_cast<int8_t*>(Wq), sw, nullptr, s);
+    w8::launch_int8_rows(W, bf, N, (int)K, 0x7F80u, static_cast<int8_t*>(Wq), sw, nullptr, w8::kProdNone,
+                         w8::ProdArgs{}, s);
   else
     w8::launch_fp8_rows(W, bf, N, (int)K, nullptr, static_cast<uint8_t*>(Wq), sw, 2, s);
   return check_launch("quantize_weight_rowwise");
@@ -282,15 +284,37 @@ static w8_status int8_common_checks(const void* X, int x_dt, int64_t M, int64_t 
   return W8_OK;
 }
 
-w8_status int8_mixed_linear(const void* X, int x_dt, int64_t M, int64_t K, const int8_t* Wq, const float* sw,
-                            int64_t N, float threshold, void* Y, int y_dt, void* workspace, size_t workspace_bytes,
-                            void* stream) {
+// Producer descriptor -> kernel arguments; NULL means none.
+static w8_status producer_args(const w8_producer* p, int64_t K, int* kind, w8::ProdArgs* pa) {
+  *kind = w8::kProdNone;
+  *pa = w8::ProdArgs{nullptr, nullptr, nullptr, 0.0f, nullptr};
+  if (!p || p->kind == W8_PRODUCER_NONE) return W8_OK;
+  W8_REQUIRE(p->kind == W8_PRODUCER_RMSNORM || p->kind == W8_PRODUCER_GELU_TANH, W8_ERR_INVALID_ARGUMENT,
+             "unknown producer kind %d", p->kind);
+  W8_REQUIRE(K <= 16384, W8_ERR_UNSUPPORTED, "a producer needs K <= 16384, got %lld", (long long)K);
+  if (p->kind == W8_PRODUCER_RMSNORM) {
+    W8_REQUIRE(std::isfinite(p->eps) && p->eps >= 0.0f, W8_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+    *kind = w8::kProdRms;
+    *pa = w8::ProdArgs{p->gamma, p->scale, p->shift, p->eps, nullptr};
+  } else {
+    *kind = w8::kProdGelu;
+  }
+  return W8_OK;
+}
+
+static w8_status int8_linear_impl(const void* X, int x_dt, int64_t M, int64_t K, const w8_producer* producer,
+                                  const int8_t* Wq, const float* sw, const float* bias, int64_t N, float threshold,
+                                  void* Y, int y_dt, void* workspace, size_t workspace_bytes, void* stream,
+                                  const char* what) {
   if (w8_status st = int8_common_checks(X, x_dt, M, K, threshold); st != W8_OK) return st;
   W8_REQUIRE(Wq && sw && Y, W8_ERR_INVALID_ARGUMENT, "null pointer argument");
   W8_REQUIRE(N >= 1 && N <= kMaxDim, W8_ERR_INVALID_ARGUMENT, "N must be in [1, 2^31)");
   W8_REQUIRE(y_dt == W8_DT_F16 || y_dt == W8_DT_F32, W8_ERR_UNSUPPORTED, "Y must be f16 or f32");
   W8_REQUIRE(aligned16(Wq) && aligned16(sw) && aligned16(Y), W8_ERR_INVALID_ARGUMENT,
              "pointers must be 16-byte aligned");
+  int kind = 0;
+  w8::ProdArgs pa{};
+  if (w8_status st = producer_args(producer, K, &kind, &pa); st != W8_OK) return st;
   const Int8Ws L = int8_layout(M, N, K);
   if (w8_status st = check_ws(workspace, workspace_bytes, L.total); st != W8_OK) return st;
 
@@ -305,17 +329,32 @@ w8_status int8_mixed_linear(const void* X, int x_dt, int64_t M, int64_t K, const
   uint16_t* WO = at<uint16_t>(workspace, L.WO);
   int* cnt = at<int>(workspace, L.cnt);
   int* part = at<int>(workspace, L.part);
+  pa.rstd = at<float>(workspace, L.rstd);
 
   mark(0, s);
   const uint32_t tb = threshold_bits(threshold, bf);
-  w8::launch_int8_rows(X, bf, M, (int)K, tb, q, sx, flags, s);
+  w8::launch_int8_rows(X, bf, M, (int)K, tb, q, sx, flags, kind, pa, s);
   mark(1, s);
-  w8::launch_outlier_fixup(X, bf, M, (int)K, tb, flags, q, sx, O, nO, XO, Wq, N, WO, s);
+  w8::launch_outlier_fixup(X, bf, M, (int)K, tb, flags, q, sx, O, nO, XO, Wq, N, WO, kind, pa, s);
   mark(2, s);
-  w8::launch_int8_gemm(q, Wq, M, N, K, sx, sw, nO, XO, WO, bf, Y, y_dt == W8_DT_F16 ? 1 : 2, L.plan, part, cnt,
-                       reinterpret_cast<uint32_t*>(flags), static_cast<int>(K / 4), s);
+  w8::launch_int8_gemm(q, Wq, M, N, K, sx, sw, nO, XO, WO, bf, bias, Y, y_dt == W8_DT_F16 ? 1 : 2, L.plan, part,
+                       cnt, reinterpret_cast<uint32_t*>(flags), static_cast<int>(K / 4), s);
   mark(3, s);
-  return check_launch("int8_mixed_linear");
+  return check_launch(what);
+}
+
+w8_status int8_mixed_linear(const void* X, int x_dt, int64_t M, int64_t K, const int8_t* Wq, const float* sw,
+                            int64_t N, float threshold, void* Y, int y_dt, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  return int8_linear_impl(X, x_dt, M, K, nullptr, Wq, sw, nullptr, N, threshold, Y, y_dt, workspace,
+                          workspace_bytes, stream, "int8_mixed_linear");
+}
+
+w8_status int8_mixed_linear_fused(const void* H, int h_dt, int64_t M, int64_t K, const w8_producer* producer,
+                                  const int8_t* Wq, const float* sw, const float* bias, int64_t N, float threshold,
+                                  void* Y, int y_dt, void* workspace, size_t workspace_bytes, void* stream) {
+  return int8_linear_impl(H, h_dt, M, K, producer, Wq, sw, bias, N, threshold, Y, y_dt, workspace, workspace_bytes,
+                          stream, "int8_mixed_linear_fused");
 }
 
 size_t fp8_w8a8_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
@@ -354,24 +393,29 @@ w8_status fp8_w8a8_linear(const void* X, int x_dt, int64_t M, int64_t K, const u
 
 size_t w8dbg_int8_quantize_activations_workspace_size(int64_t M, int64_t K) {
   if (M < 1 || K < 1) return 0;
-  return up(static_cast<size_t>(K));
+  return up(static_cast<size_t>(K)) + up(4 * static_cast<size_t>(M));
 }
 
-w8_status w8dbg_int8_quantize_activations(const void* X, int x_dt, int64_t M, int64_t K, float threshold, int8_t* q,
-                                          float* sx, int32_t* outlier_idx, int32_t* n_outliers, void* workspace,
+w8_status w8dbg_int8_quantize_activations(const void* X, int x_dt, int64_t M, int64_t K,
+                                          const w8_producer* producer, float threshold, int8_t* q, float* sx,
+                                          int32_t* outlier_idx, int32_t* n_outliers, void* workspace,
                                           size_t workspace_bytes, void* stream) {
   if (w8_status st = int8_common_checks(X, x_dt, M, K, threshold); st != W8_OK) return st;
   W8_REQUIRE(q && sx && outlier_idx && n_outliers, W8_ERR_INVALID_ARGUMENT, "null pointer argument");
   W8_REQUIRE(aligned16(q) && aligned16(sx), W8_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+  int kind = 0;
+  w8::ProdArgs pa{};
+  if (w8_status st = producer_args(producer, K, &kind, &pa); st != W8_OK) return st;
   const size_t need = w8dbg_int8_quantize_activations_workspace_size(M, K);
   if (w8_status st = check_ws(workspace, workspace_bytes, need); st != W8_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = x_dt == W8_DT_BF16;
   uint8_t* flags = at<uint8_t>(workspace, 0);
+  pa.rstd = at<float>(workspace, up(static_cast<size_t>(K)));
   const uint32_t tb = threshold_bits(threshold, bf);
-  w8::launch_int8_rows(X, bf, M, (int)K, tb, q, sx, flags, s);
+  w8::launch_int8_rows(X, bf, M, (int)K, tb, q, sx, flags, kind, pa, s);
   w8::launch_outlier_fixup(X, bf, M, (int)K, tb, flags, q, sx, outlier_idx, n_outliers, nullptr, nullptr, 0, nullptr,
-                           s);
+                           kind, pa, s);
   w8::launch_clear_words(reinterpret_cast<uint32_t*>(flags), static_cast<int>(K / 4), s);
   return check_launch("w8dbg_int8_quantize_activations");
 }
@@ -398,7 +442,8 @@ w8_status w8dbg_int8_gemm_i32(const int8_t* q, const int8_t* Wq, int64_t M, int6
   hipStream_t s = static_cast<hipStream_t>(stream);
   int* cnt = L.total > 0 ? at<int>(workspace, L.cnt) : nullptr;
   int* part = L.total > 0 ? at<int>(workspace, L.part) : nullptr;
-  w8::launch_int8_gemm(q, Wq, M, N, K, nullptr, nullptr, nullptr, nullptr, nullptr, true, acc, 0, L.plan, part, cnt,
+  w8::launch_int8_gemm(q, Wq, M, N, K, nullptr, nullptr, nullptr, nullptr, nullptr, true, nullptr, acc, 0, L.plan,
+                       part, cnt,
                        nullptr, 0, s);
   return check_launch("w8dbg_int8_gemm_i32");
 }
@@ -434,6 +479,19 @@ w8_status w8dbg_fp8_gemm(const uint8_t* xq, const float* sx, const uint8_t* Wq8,
   w8::launch_fp8_gemm(xq, Wq8, M, N, K, sx, sw, Y, ydt, plan, need > 0 ? at<float>(workspace, cnt_bytes) : nullptr,
                       need > 0 ? at<int>(workspace, 0) : nullptr, static_cast<hipStream_t>(stream));
   return check_launch("w8dbg_fp8_gemm");
+}
+
+w8_status w8dbg_produce(const void* H, int h_dt, int64_t M, int64_t K, const w8_producer* producer, void* X,
+                        void* stream) {
+  W8_REQUIRE(H && X, W8_ERR_INVALID_ARGUMENT, "null pointer argument");
+  W8_REQUIRE(h_dt == W8_DT_F16 || h_dt == W8_DT_BF16, W8_ERR_UNSUPPORTED, "H must be f16 or bf16");
+  if (w8_status st = check_mk(M, K, W8_INT8_MAX_K); st != W8_OK) return st;
+  W8_REQUIRE(aligned16(H) && aligned16(X), W8_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+  int kind = 0;
+  w8::ProdArgs pa{};
+  if (w8_status st = producer_args(producer, K, &kind, &pa); st != W8_OK) return st;
+  w8::launch_produce(H, h_dt == W8_DT_BF16, M, (int)K, kind, pa, X, static_cast<hipStream_t>(stream));
+  return check_launch("w8dbg_produce");
 }
 
 w8_status w8dbg_fp8_quantize_activations(const void* X, int x_dt, int64_t M, int64_t K, const float* act_scale,

@@ -62,10 +62,11 @@ __device__ __forceinline__ v16f mfma_side(V8 a, V8 b, v16f c) {
 // staged through LDS a row block at a time (flush_staged).
 //
 // rsx[i]: sx[m]/127 for the lane's row of block i (prefetched by the caller);
-// scol: LDS copy of sw[n0 .. n0+64*WT) / 127; stg: this wave's staging area.
+// scol: LDS copy of sw[n0 .. n0+64*WT) / 127; sbias: LDS copy of the bias
+// there (null: no bias); stg: this wave's staging area.
 template <int MODE, bool XBF16, int WT = 4>
 __device__ __forceinline__ void epilogue(v16i (&acc)[WT][WT], int M, int N, int m0, int n0, int wm, int wn, int lane,
-                                         const float (&rsx)[4], const float* scol, int nO,
+                                         const float (&rsx)[4], const float* scol, const float* sbias, int nO,
                                          const uint16_t* __restrict__ XO, const uint16_t* __restrict__ WO,
                                          void* __restrict__ Y, char* stg) {
   const int fr = lane & 31, fh = lane >> 5;
@@ -118,6 +119,11 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[WT][WT], int M, int N, int 
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               v[e] = (static_cast<float>(acc[i][j][4 * g + e]) * rsx[i] + o[j][4 * g + e]) * cs[e];
+            if (sbias) {
+              const v4f bs = *reinterpret_cast<const v4f*>(sbias + wn * WR + 32 * j + 8 * g + 4 * fh);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = v[e] + bs[e];
+            }
             if constexpr (MODE == 1) {
               const uint32_t lo = f32_to_f16_bits(v[0]) | (static_cast<uint32_t>(f32_to_f16_bits(v[1])) << 16);
               const uint32_t hi = f32_to_f16_bits(v[2]) | (static_cast<uint32_t>(f32_to_f16_bits(v[3])) << 16);
@@ -142,22 +148,25 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[WT][WT], int M, int N, int 
 struct EpiIn {
   float rsx[4];
   float my_sw;
+  float my_bias;
   int nO;
 };
 
 template <int MODE, int WT = 4>
 __device__ __forceinline__ void epi_prefetch(EpiIn& e, int M, int N, int m0, int n0, int wm, int lane,
                                              const float* __restrict__ sx, const float* __restrict__ sw,
-                                             const int* __restrict__ nO_ptr) {
+                                             const float* __restrict__ bias, const int* __restrict__ nO_ptr) {
   if constexpr (MODE != 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) e.rsx[i] = sx[min(m0 + wm * 32 * WT + 32 * i + (lane & 31), M - 1)];
     e.my_sw = sw[min(n0 + static_cast<int>(threadIdx.x), N - 1)];
+    e.my_bias = bias ? bias[min(n0 + static_cast<int>(threadIdx.x), N - 1)] : 0.0f;
     e.nO = *nO_ptr;
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) e.rsx[i] = 0.0f;
     e.my_sw = 0.0f;
+    e.my_bias = 0.0f;
     e.nO = 0;
   }
 }
@@ -168,16 +177,19 @@ __device__ __forceinline__ void epi_prefetch(EpiIn& e, int M, int N, int m0, int
 template <int MODE, bool XBF16, int WT = 4>
 __device__ __forceinline__ void finish_tile(v16i (&acc)[WT][WT], EpiIn& e, char* lds, int M, int N, int m0, int n0,
                                             int wm, int wn, int lane, const uint16_t* __restrict__ XO,
-                                            const uint16_t* __restrict__ WO, void* __restrict__ Y) {
+                                            const uint16_t* __restrict__ WO, const float* __restrict__ bias,
+                                            void* __restrict__ Y) {
   float* scol = reinterpret_cast<float*>(lds);
+  float* sbias = scol + 256;
   if constexpr (MODE != 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) e.rsx[i] = e.rsx[i] / 127.0f;
     scol[threadIdx.x] = e.my_sw / 127.0f;
+    if (bias) sbias[threadIdx.x] = e.my_bias;
     __syncthreads();
   }
-  epilogue<MODE, XBF16, WT>(acc, M, N, m0, n0, wm, wn, lane, e.rsx, scol, e.nO, XO, WO, Y,
-                            lds + 1024 + (threadIdx.x >> 6) * kStgWave);
+  epilogue<MODE, XBF16, WT>(acc, M, N, m0, n0, wm, wn, lane, e.rsx, scol, MODE != 0 && bias ? sbias : nullptr,
+                            e.nO, XO, WO, Y, lds + kEpiCols + (threadIdx.x >> 6) * kStgWave);
 }
 
 __device__ __forceinline__ void zero_acc(v16i (&acc)[4][4]) {
@@ -198,7 +210,8 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm(const int8_t* __restrict__
                                                       int M, int N, int K, const float* __restrict__ sx,
                                                       const float* __restrict__ sw, const int* __restrict__ nO_ptr,
                                                       const uint16_t* __restrict__ XO,
-                                                      const uint16_t* __restrict__ WO, void* __restrict__ Y,
+                                                      const uint16_t* __restrict__ WO,
+                                                      const float* __restrict__ bias, void* __restrict__ Y,
                                                       int tiles_m, int tiles_n, uint32_t* __restrict__ clear,
                                                       int clear_words) {
   __shared__ __attribute__((aligned(16))) int8_t lds[2][2][kBM * kBK];
@@ -212,7 +225,7 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm(const int8_t* __restrict__
   if (blockIdx.x == 0 && clear)                   // see k_int8_gemm_dma
     for (int i = tid; i < clear_words; i += 256) clear[i] = 0u;
   EpiIn ein;
-  epi_prefetch<MODE>(ein, M, N, m0, n0, wm, lane, sx, sw, nO_ptr);
+  epi_prefetch<MODE>(ein, M, N, m0, n0, wm, lane, sx, sw, bias, nO_ptr);
 
   // this thread moves logical chunk (tid & 3) of rows tid/4 + 64*i
   const int ld_ch = tid & 3;
@@ -258,7 +271,8 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm(const int8_t* __restrict__
     if (kt + 1 < nk) lstore(st ^ 1);
     __syncthreads();
   }
-  finish_tile<MODE, XBF16>(acc, ein, reinterpret_cast<char*>(&lds[0][0][0]), M, N, m0, n0, wm, wn, lane, XO, WO, Y);
+  finish_tile<MODE, XBF16>(acc, ein, reinterpret_cast<char*>(&lds[0][0][0]), M, N, m0, n0, wm, wn, lane, XO, WO, bias,
+                           Y);
 }
 
 // ---------------------------------------------------------------------------
@@ -426,8 +440,9 @@ __device__ __forceinline__ void small_block(int8_t* lds, const int8_t* __restric
                                             int M, int N, int K, const float* __restrict__ sx,
                                             const float* __restrict__ sw, const int* __restrict__ nO_ptr,
                                             const uint16_t* __restrict__ XO, const uint16_t* __restrict__ WO,
-                                            void* __restrict__ Y, int tiles_m, int tiles_n, int dp_tiles, int split,
-                                            int* __restrict__ part, int* __restrict__ cnt) {
+                                            const float* __restrict__ bias, void* __restrict__ Y, int tiles_m,
+                                            int tiles_n, int dp_tiles, int split, int* __restrict__ part,
+                                            int* __restrict__ cnt) {
   constexpr int SS = 2 * S;                     // the same LDS as S big stages
   int* const s_last = reinterpret_cast<int*>(lds + kEpiLds);
   const int nu = gridDim.x - dp_tiles;
@@ -444,7 +459,7 @@ __device__ __forceinline__ void small_block(int8_t* lds, const int8_t* __restric
   const int wm = wave >> 1, wn = wave & 1;
   const int fr = lane & 31, fh = lane >> 5;
   EpiIn ein;
-  epi_prefetch<MODE, 2>(ein, M, N, m0, n0, wm, lane, sx, sw, nO_ptr);
+  epi_prefetch<MODE, 2>(ein, M, N, m0, n0, wm, lane, sx, sw, bias, nO_ptr);
 
   // DMA source of this lane for load i (0, 1) of each operand: block row
   // r = wave*32 + 16*i + lane/4 lands in LDS slot (lane & 3) of that row.
@@ -519,7 +534,7 @@ __device__ __forceinline__ void small_block(int8_t* lds, const int8_t* __restric
         for (int e = 0; e < 4; ++e) acc[t >> 3][(t >> 2) & 1][4 * (t & 3) + e] += w[t][e];
     }
   }
-  finish_tile<MODE, XBF16, 2>(acc, ein, reinterpret_cast<char*>(lds), M, N, m0, n0, wm, wn, lane, XO, WO, Y);
+  finish_tile<MODE, XBF16, 2>(acc, ein, reinterpret_cast<char*>(lds), M, N, m0, n0, wm, wn, lane, XO, WO, bias, Y);
 }
 
 // Work split for the last, partial wave of tiles (split-K). The first
@@ -536,7 +551,8 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
                                                           int M, int N, int K, const float* __restrict__ sx,
                                                           const float* __restrict__ sw, const int* __restrict__ nO_ptr,
                                                           const uint16_t* __restrict__ XO,
-                                                          const uint16_t* __restrict__ WO, void* __restrict__ Y,
+                                                          const uint16_t* __restrict__ WO,
+                                                          const float* __restrict__ bias, void* __restrict__ Y,
                                                           int tiles_m, int tiles_n, int dp_tiles, int split,
                                                           int small, int* __restrict__ part, int* __restrict__ cnt,
                                                           uint32_t* __restrict__ clear, int clear_words) {
@@ -557,8 +573,8 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
   if (blockIdx.x == 0 && clear)
     for (int i = threadIdx.x; i < clear_words; i += 256) clear[i] = 0u;
   if (small && static_cast<int>(blockIdx.x) >= dp_tiles) {
-    small_block<MODE, XBF16, S>(lds, A, B, M, N, K, sx, sw, nO_ptr, XO, WO, Y, tiles_m, tiles_n, dp_tiles, split,
-                                part, cnt);
+    small_block<MODE, XBF16, S>(lds, A, B, M, N, K, sx, sw, nO_ptr, XO, WO, bias, Y, tiles_m, tiles_n, dp_tiles,
+                                split, part, cnt);
     return;
   }
   const int nk_all = K / kBK;
@@ -583,7 +599,7 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   EpiIn ein;
-  epi_prefetch<MODE>(ein, M, N, m0, n0, wm, lane, sx, sw, nO_ptr);
+  epi_prefetch<MODE>(ein, M, N, m0, n0, wm, lane, sx, sw, bias, nO_ptr);
 
   // DMA source of this lane for load instruction i (0..3) of each operand:
   // tile row r = wave*64 + 16*i + lane/4 lands in LDS slot (lane & 3) of that
@@ -682,7 +698,7 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
       }
     }
   }
-  finish_tile<MODE, XBF16>(acc, ein, reinterpret_cast<char*>(lds), M, N, m0, n0, wm, wn, lane, XO, WO, Y);
+  finish_tile<MODE, XBF16>(acc, ein, reinterpret_cast<char*>(lds), M, N, m0, n0, wm, wn, lane, XO, WO, bias, Y);
 }
 
 // ---------------------------------------------------------------------------
@@ -768,15 +784,15 @@ GemmPlan plan_int8_gemm_forced(int64_t M, int64_t N, int cus, bool small, int sp
 // words that the kernel zeroes (the outlier-column mask of the pass before).
 void launch_int8_gemm(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t K, const float* sx,
                       const float* sw, const int* nO, const uint16_t* XO, const uint16_t* WO, bool xbf16,
-                      void* Y, int mode, const GemmPlan& plan, int* part, int* cnt, uint32_t* clear,
-                      int clear_words, hipStream_t s) {
+                      const float* bias, void* Y, int mode, const GemmPlan& plan, int* part, int* cnt,
+                      uint32_t* clear, int clear_words, hipStream_t s) {
   const int tiles_m = plan.tiles_m, tiles_n = plan.tiles_n;
   const int m = (int)M, n = (int)N, k = (int)K;
   const dim3 block(256);
   if (K % kBK == 0) {
     constexpr int S = 4;
     const dim3 grid(plan.grid());
-#define W8_GEMM_ARGS A, B, m, n, k, sx, sw, nO, XO, WO, Y, tiles_m, tiles_n, plan.dp_tiles, plan.split, \
+#define W8_GEMM_ARGS A, B, m, n, k, sx, sw, nO, XO, WO, bias, Y, tiles_m, tiles_n, plan.dp_tiles, plan.split, \
     plan.small ? 1 : 0, part, cnt, clear, clear_words
     if (mode == 0) k_int8_gemm_dma<0, true, S><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
     else if (mode == 1 && xbf16) k_int8_gemm_dma<1, true, S><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
@@ -786,7 +802,7 @@ void launch_int8_gemm(const int8_t* A, const int8_t* B, int64_t M, int64_t N, in
 #undef W8_GEMM_ARGS
   } else {
     const dim3 grid(tiles_m * tiles_n);
-#define W8_GEMM_ARGS A, B, m, n, k, sx, sw, nO, XO, WO, Y, tiles_m, tiles_n, clear, clear_words
+#define W8_GEMM_ARGS A, B, m, n, k, sx, sw, nO, XO, WO, bias, Y, tiles_m, tiles_n, clear, clear_words
     if (mode == 0) k_int8_gemm<0, true><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
     else if (mode == 1 && xbf16) k_int8_gemm<1, true><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
     else if (mode == 1) k_int8_gemm<1, false><<<grid, block, 0, s>>>(W8_GEMM_ARGS);

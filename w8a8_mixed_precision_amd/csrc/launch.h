@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "producer.h"
+
 namespace w8 {
 
 // Grid of the tiled GEMMs: dp_tiles whole tiles of bm x bm outputs, then
@@ -27,19 +29,23 @@ struct GemmPlan {
 GemmPlan plan_int8_gemm(int64_t M, int64_t N, int64_t K, int cus);
 GemmPlan plan_int8_gemm_forced(int64_t M, int64_t N, int cus, bool small, int split);
 
+// prod: producer of X from H (kProdNone / kProdRms / kProdGelu of producer.h;
+// rows with a producer need K <= 16384); pa: its parameters.
 void launch_int8_rows(const void* X, bool bf16, int64_t rows, int K, uint32_t tbits, int8_t* q, float* sx,
-                      uint8_t* flags, hipStream_t s);
+                      uint8_t* flags, int prod, const ProdArgs& pa, hipStream_t s);
 size_t outlier_fixup_lds_bytes(int K);
 void launch_outlier_fixup(const void* X, bool bf16, int64_t M, int K, uint32_t tbits, const uint8_t* colflag,
                           int8_t* q, float* sx, int* O, int* nO, uint16_t* XO, const int8_t* Wq, int64_t N,
-                          uint16_t* WO, hipStream_t s);
+                          uint16_t* WO, int prod, const ProdArgs& pa, hipStream_t s);
+void launch_produce(const void* H, bool bf16, int64_t M, int K, int prod, const ProdArgs& pa, void* X,
+                    hipStream_t s);
 void launch_clear_words(uint32_t* p, int n, hipStream_t s);
 void launch_fp8_rows(const void* X, bool bf16, int64_t rows, int K, const float* act_scale, uint8_t* xq, float* sx,
                      int mode, hipStream_t s);
 void launch_int8_gemm(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t K, const float* sx,
-                      const float* sw, const int* nO, const uint16_t* XO, const uint16_t* WO, bool xbf16, void* Y,
-                      int mode, const GemmPlan& plan, int* part, int* cnt, uint32_t* clear, int clear_words,
-                      hipStream_t s);
+                      const float* sw, const int* nO, const uint16_t* XO, const uint16_t* WO, bool xbf16,
+                      const float* bias, void* Y, int mode, const GemmPlan& plan, int* part, int* cnt,
+                      uint32_t* clear, int clear_words, hipStream_t s);
 GemmPlan plan_fp8_gemm(int64_t M, int64_t N, int64_t K, int cus);
 GemmPlan plan_fp8_gemm_split(int64_t M, int64_t N, int split, int bm);
 void launch_fp8_gemm(const uint8_t* A, const uint8_t* B, int64_t M, int64_t N, int64_t K, const float* sx,

@@ -24,6 +24,7 @@
 // exceed those of the largest representable value <= t. Non-finite values
 // have the largest patterns: with a finite t they are outliers.
 #include "common.h"
+#include "producer.h"
 
 namespace w8 {
 
@@ -115,12 +116,17 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // covering a 4096-column slice, 8 chunks of 8 elements per lane; a block of
 // 256 threads holds 4/W rows. With W == 1 the row reduction stays inside one
 // wave (no LDS, no barrier).
-template <bool BF16, int W, bool ACT>
+//
+// With a producer (PROD != kProdNone) the loaded values are H, and X is made
+// from them in registers (producer.h) before anything else; RMSNorm first
+// reduces the row's sum of squares and stores the row's rstd for the fix-up.
+template <bool BF16, int W, bool ACT, int PROD>
 __global__ __launch_bounds__(256) void k_int8_rows(const uint16_t* __restrict__ X, int64_t rows, int K,
                                                    uint32_t tbits, int8_t* __restrict__ q, float* __restrict__ sx,
-                                                   uint8_t* __restrict__ flags) {
+                                                   uint8_t* __restrict__ flags, ProdArgs pa) {
   constexpr int kRows = 4 / W;
   __shared__ uint32_t red[4];
+  __shared__ double red64[4];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * kRows + wave / W;
   const bool valid = row < rows;
@@ -134,6 +140,37 @@ __global__ __launch_bounds__(256) void k_int8_rows(const uint16_t* __restrict__ 
     for (int i = 0; i < 8; ++i) {
       const int c = part * 512 + lane + 64 * i;
       if (c < nch) v[i] = xr[c];
+    }
+  }
+  if constexpr (PROD != kProdNone) {
+    float rstd = 0.0f;
+    if constexpr (PROD == kProdRms) {
+      double ss = 0.0;
+      if (valid) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int c = part * 512 + lane + 64 * i;
+          if (c < nch) ss += sumsq8<BF16>(v[i]);
+        }
+      }
+      ss = wave_sum_f64(ss);
+      if constexpr (W > 1) {
+        if (lane == 0) red64[wave] = ss;
+        __syncthreads();
+        const int w0 = (wave / W) * W;
+        ss = red64[w0];
+#pragma unroll
+        for (int w = 1; w < W; ++w) ss += red64[w0 + w];
+      }
+      rstd = rms_rstd(ss, K, pa.eps);
+      if (valid && part == 0 && lane == 0) pa.rstd[row] = rstd;
+    }
+    if (valid) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int c = part * 512 + lane + 64 * i;
+        if (c < nch) v[i] = produce8<BF16, PROD>(v[i], c, rstd, pa);
+      }
     }
   }
   uint32_t mx = 0;
@@ -206,16 +243,22 @@ size_t outlier_fixup_lds_bytes(int K) {
   return static_cast<size_t>(2) * ((K + 31) / 32) * 4 + static_cast<size_t>(kOcap) * 4;
 }
 
-template <bool BF16>
+//
+// With a producer, X is never stored: the gathers read H and make X values from
+// it (with the row's rstd from the row pass), and re-encoded rows are made
+// from H again.
+template <bool BF16, int PROD>
 __global__ __launch_bounds__(256) void k_outlier_fixup(
     const uint16_t* __restrict__ X, int M, int K, uint32_t tbits, const uint8_t* __restrict__ colflag,
     int8_t* __restrict__ q, float* __restrict__ sx, int* __restrict__ O, int* __restrict__ nO_out,
-    uint16_t* __restrict__ XO, const int8_t* __restrict__ Wq, int N, uint16_t* __restrict__ WO, int xblocks) {
+    uint16_t* __restrict__ XO, const int8_t* __restrict__ Wq, int N, uint16_t* __restrict__ WO, int xblocks,
+    ProdArgs pa) {
   extern __shared__ uint32_t smem[];
   __shared__ int scan_tot[4];
   __shared__ float fred[4];
   __shared__ uint32_t somax[kFixRows];       // per row: largest gathered magnitude <= t
   __shared__ float ssx[kFixRows];            // per row: provisional scale
+  __shared__ float srstd[kFixRows];          // per row: RMSNorm rstd (producer kProdRms)
   const int nwords = (K + 31) >> 5;
   uint32_t* smask = smem;
   int* spre = reinterpret_cast<int*>(smem + nwords);
@@ -278,8 +321,10 @@ __global__ __launch_bounds__(256) void k_outlier_fixup(
   if (nO == 0) return;
   if (tid < kFixRows) somax[tid] = 0u;
   const bool xblock = static_cast<int>(blockIdx.x) < xblocks;
-  if (xblock && tid < kFixRows && static_cast<int>(blockIdx.x) * kFixRows + tid < M)
+  if (xblock && tid < kFixRows && static_cast<int>(blockIdx.x) * kFixRows + tid < M) {
     ssx[tid] = sx[blockIdx.x * kFixRows + tid];
+    if constexpr (PROD == kProdRms) srstd[tid] = pa.rstd[blockIdx.x * kFixRows + tid];
+  }
   __syncthreads();
 
   if (xblock) {
@@ -288,7 +333,8 @@ __global__ __launch_bounds__(256) void k_outlier_fixup(
     // zero the codes of the outlier columns, gather X's outlier columns, and
     // note per row the largest gathered magnitude <= t
     auto take = [&](int r, int64_t m, int k) -> uint16_t {
-      const uint16_t v = X[m * K + k];
+      const uint16_t v = static_cast<uint16_t>(produce1<BF16, PROD>(X[m * K + k], k,
+                                                                   PROD == kProdRms ? srstd[r] : 0.0f, pa));
       q[m * K + k] = 0;
       const uint32_t mag = v & 0x7FFFu;
       if (mag <= tbits) atomicMax(&somax[r], mag);
@@ -316,7 +362,7 @@ __global__ __launch_bounds__(256) void k_outlier_fixup(
           const int64_t m = r0 + r;
           uint16_t val = 0;
           if (j < nO) {
-            val = v[u];
+            val = static_cast<uint16_t>(produce1<BF16, PROD>(v[u], sO[j], PROD == kProdRms ? srstd[r] : 0.0f, pa));
             q[m * K + sO[j]] = 0;
             const uint32_t mag = val & 0x7FFFu;
             if (mag <= tbits) atomicMax(&somax[r], mag);
@@ -353,11 +399,12 @@ __global__ __launch_bounds__(256) void k_outlier_fixup(
       const uint4* xr = reinterpret_cast<const uint4*>(X + rowoff);
       uint2* qr = reinterpret_cast<uint2*>(q + rowoff);
       const int nch = K >> 3;
+      const float rr_std = PROD == kProdRms ? srstd[r] : 0.0f;
       float best = 0.0f;
 #pragma unroll 8
       for (int c = tid; c < nch; c += 256) {
         float f[8];
-        unpack8<BF16>(xr[c], f);
+        unpack8<BF16>(produce8<BF16, PROD>(xr[c], c, rr_std, pa), f);
         const uint32_t ob = (smask[c >> 2] >> ((c & 3) * 8)) & 0xFFu;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
@@ -368,7 +415,7 @@ __global__ __launch_bounds__(256) void k_outlier_fixup(
 #pragma unroll 8
       for (int c = tid; c < nch; c += 256) {
         float f[8];
-        unpack8<BF16>(xr[c], f);
+        unpack8<BF16>(produce8<BF16, PROD>(xr[c], c, rr_std, pa), f);
         const uint32_t ob = (smask[c >> 2] >> ((c & 3) * 8)) & 0xFFu;
         uint32_t lo = 0, hi = 0;
 #pragma unroll
@@ -517,48 +564,104 @@ void launch_clear_words(uint32_t* p, int n, hipStream_t s) {
   k_clear_words<<<dim3((n + 255) / 256 < 64 ? (n + 255) / 256 : 64), dim3(256), 0, s>>>(p, n);
 }
 
-template <bool BF16, bool ACT>
+template <bool BF16, bool ACT, int PROD>
 static void launch_int8_rows_t(const uint16_t* X, int64_t rows, int K, uint32_t tbits, int8_t* q, float* sx,
-                               uint8_t* flags, hipStream_t s) {
+                               uint8_t* flags, const ProdArgs& pa, hipStream_t s) {
   const dim3 block(256);
   auto blocks = [&](int rpb) { return dim3(static_cast<unsigned>((rows + rpb - 1) / rpb)); };
   if (K <= 4096)
-    k_int8_rows<BF16, 1, ACT><<<blocks(4), block, 0, s>>>(X, rows, K, tbits, q, sx, flags);
+    k_int8_rows<BF16, 1, ACT, PROD><<<blocks(4), block, 0, s>>>(X, rows, K, tbits, q, sx, flags, pa);
   else if (K <= 8192)
-    k_int8_rows<BF16, 2, ACT><<<blocks(2), block, 0, s>>>(X, rows, K, tbits, q, sx, flags);
+    k_int8_rows<BF16, 2, ACT, PROD><<<blocks(2), block, 0, s>>>(X, rows, K, tbits, q, sx, flags, pa);
   else if (K <= 16384)
-    k_int8_rows<BF16, 4, ACT><<<blocks(1), block, 0, s>>>(X, rows, K, tbits, q, sx, flags);
-  else
+    k_int8_rows<BF16, 4, ACT, PROD><<<blocks(1), block, 0, s>>>(X, rows, K, tbits, q, sx, flags, pa);
+  else if constexpr (PROD == kProdNone)
     k_int8_rows_long<BF16, ACT><<<dim3(static_cast<unsigned>(rows)), block, 0, s>>>(X, K, tbits, q, sx, flags);
 }
 
-// flags == nullptr: weight pass (no threshold)
+template <bool BF16>
+static void launch_int8_rows_b(const uint16_t* X, int64_t rows, int K, uint32_t tbits, int8_t* q, float* sx,
+                               uint8_t* flags, int prod, const ProdArgs& pa, hipStream_t s) {
+  if (!flags) launch_int8_rows_t<BF16, false, kProdNone>(X, rows, K, tbits, q, sx, flags, pa, s);
+  else if (prod == kProdRms) launch_int8_rows_t<BF16, true, kProdRms>(X, rows, K, tbits, q, sx, flags, pa, s);
+  else if (prod == kProdGelu) launch_int8_rows_t<BF16, true, kProdGelu>(X, rows, K, tbits, q, sx, flags, pa, s);
+  else launch_int8_rows_t<BF16, true, kProdNone>(X, rows, K, tbits, q, sx, flags, pa, s);
+}
+
+// flags == nullptr: weight pass (no threshold, no producer). A producer needs
+// K <= 16384 (checked by the caller).
 void launch_int8_rows(const void* X, bool bf16, int64_t rows, int K, uint32_t tbits, int8_t* q, float* sx,
-                      uint8_t* flags, hipStream_t s) {
+                      uint8_t* flags, int prod, const ProdArgs& pa, hipStream_t s) {
   const uint16_t* x = static_cast<const uint16_t*>(X);
-  if (bf16) {
-    if (flags) launch_int8_rows_t<true, true>(x, rows, K, tbits, q, sx, flags, s);
-    else launch_int8_rows_t<true, false>(x, rows, K, tbits, q, sx, flags, s);
-  } else {
-    if (flags) launch_int8_rows_t<false, true>(x, rows, K, tbits, q, sx, flags, s);
-    else launch_int8_rows_t<false, false>(x, rows, K, tbits, q, sx, flags, s);
+  if (bf16) launch_int8_rows_b<true>(x, rows, K, tbits, q, sx, flags, prod, pa, s);
+  else launch_int8_rows_b<false>(x, rows, K, tbits, q, sx, flags, prod, pa, s);
+}
+
+// X = producer(H) written out (parity export): one block per row.
+template <bool BF16, int PROD>
+__global__ __launch_bounds__(256) void k_produce(const uint16_t* __restrict__ H, int K, ProdArgs pa,
+                                                 uint16_t* __restrict__ X) {
+  __shared__ double red64[4];
+  const int64_t row = blockIdx.x;
+  const int nch = K >> 3;
+  const uint4* hr = reinterpret_cast<const uint4*>(H + row * K);
+  uint4* xr = reinterpret_cast<uint4*>(X + row * K);
+  float rstd = 0.0f;
+  if constexpr (PROD == kProdRms) {
+    double ss = 0.0;
+    for (int c = threadIdx.x; c < nch; c += 256) ss += sumsq8<BF16>(hr[c]);
+    ss = wave_sum_f64(ss);
+    if ((threadIdx.x & 63) == 0) red64[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    ss = ((red64[0] + red64[1]) + red64[2]) + red64[3];
+    rstd = rms_rstd(ss, K, pa.eps);
   }
+  for (int c = threadIdx.x; c < nch; c += 256) xr[c] = produce8<BF16, PROD>(hr[c], c, rstd, pa);
+}
+
+void launch_produce(const void* H, bool bf16, int64_t M, int K, int prod, const ProdArgs& pa, void* X,
+                    hipStream_t s) {
+  const uint16_t* h = static_cast<const uint16_t*>(H);
+  uint16_t* x = static_cast<uint16_t*>(X);
+  const dim3 grid(static_cast<unsigned>(M)), block(256);
+  if (bf16) {
+    if (prod == kProdRms) k_produce<true, kProdRms><<<grid, block, 0, s>>>(h, K, pa, x);
+    else if (prod == kProdGelu) k_produce<true, kProdGelu><<<grid, block, 0, s>>>(h, K, pa, x);
+    else k_produce<true, kProdNone><<<grid, block, 0, s>>>(h, K, pa, x);
+  } else {
+    if (prod == kProdRms) k_produce<false, kProdRms><<<grid, block, 0, s>>>(h, K, pa, x);
+    else if (prod == kProdGelu) k_produce<false, kProdGelu><<<grid, block, 0, s>>>(h, K, pa, x);
+    else k_produce<false, kProdNone><<<grid, block, 0, s>>>(h, K, pa, x);
+  }
+}
+
+template <bool BF16, int PROD>
+static void launch_fixup_t(const uint16_t* X, int64_t M, int K, uint32_t tbits, const uint8_t* colflag, int8_t* q,
+                           float* sx, int* O, int* nO, uint16_t* XO, const int8_t* Wq, int64_t N, uint16_t* WO,
+                           const ProdArgs& pa, hipStream_t s) {
+  const int xblocks = static_cast<int>((M + kFixRows - 1) / kFixRows);
+  const int wblocks = WO ? static_cast<int>((N + kFixRows - 1) / kFixRows) : 0;
+  const size_t lds = outlier_fixup_lds_bytes(K);
+  const dim3 grid(xblocks + wblocks), block(256);
+  k_outlier_fixup<BF16, PROD><<<grid, block, lds, s>>>(X, (int)M, K, tbits, colflag, q, sx, O, nO, XO, Wq, (int)N, WO,
+                                                       xblocks, pa);
 }
 
 void launch_outlier_fixup(const void* X, bool bf16, int64_t M, int K, uint32_t tbits, const uint8_t* colflag,
                           int8_t* q, float* sx, int* O, int* nO, uint16_t* XO, const int8_t* Wq, int64_t N,
-                          uint16_t* WO, hipStream_t s) {
-  const int xblocks = static_cast<int>((M + kFixRows - 1) / kFixRows);
-  const int wblocks = WO ? static_cast<int>((N + kFixRows - 1) / kFixRows) : 0;
-  const size_t lds = outlier_fixup_lds_bytes(K);
+                          uint16_t* WO, int prod, const ProdArgs& pa, hipStream_t s) {
   const uint16_t* x = static_cast<const uint16_t*>(X);
-  const dim3 grid(xblocks + wblocks), block(256);
-  if (bf16)
-    k_outlier_fixup<true><<<grid, block, lds, s>>>(x, (int)M, K, tbits, colflag, q, sx, O, nO, XO, Wq, (int)N, WO,
-                                                   xblocks);
-  else
-    k_outlier_fixup<false><<<grid, block, lds, s>>>(x, (int)M, K, tbits, colflag, q, sx, O, nO, XO, Wq, (int)N, WO,
-                                                    xblocks);
+#define W8_FIX_ARGS x, M, K, tbits, colflag, q, sx, O, nO, XO, Wq, N, WO, pa, s
+  if (bf16) {
+    if (prod == kProdRms) launch_fixup_t<true, kProdRms>(W8_FIX_ARGS);
+    else if (prod == kProdGelu) launch_fixup_t<true, kProdGelu>(W8_FIX_ARGS);
+    else launch_fixup_t<true, kProdNone>(W8_FIX_ARGS);
+  } else {
+    if (prod == kProdRms) launch_fixup_t<false, kProdRms>(W8_FIX_ARGS);
+    else if (prod == kProdGelu) launch_fixup_t<false, kProdGelu>(W8_FIX_ARGS);
+    else launch_fixup_t<false, kProdNone>(W8_FIX_ARGS);
+  }
+#undef W8_FIX_ARGS
 }
 
 template <bool BF16, int MODE>

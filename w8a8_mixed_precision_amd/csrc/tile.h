@@ -83,7 +83,8 @@ __device__ __forceinline__ void wave_lds_fence() {
 // 16 lanes x 16 bytes per row, 4 rows per instruction.
 constexpr int kStgPitch = 256 + 16;             // staged row: 256 bytes + pad
 constexpr int kStgWave = 32 * kStgPitch;        // one wave's 32 staged rows
-constexpr int kEpiLds = 1024 + 4 * kStgWave;    // column scales + 4 staging areas
+constexpr int kEpiCols = 2048;                  // column scales and bias, 256 floats each
+constexpr int kEpiLds = kEpiCols + 4 * kStgWave;   // + 4 staging areas
 
 // Writes the wave's 32 staged rows (RB bytes each: 256 or 128; EB bytes per
 // element) to Y rows m_base.. and columns n_base.., clipped to [M, N). `vec`:
