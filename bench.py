@@ -132,6 +132,70 @@ def weight_quant(torch, w8, cases, steps: int) -> dict:
     return res
 
 
+def fused_mlp(torch, w8, steps: int) -> dict:
+    """DiT 1024^2 MLP pair with its producers (up after RMSNorm+modulation,
+    down after tanh-GELU), bias in the epilogue. Fused: one
+    int8_mixed_linear_fused call per layer. Unfused: the library's one-pass
+    producer kernel writes X, then the linear reads it. Both timed with events
+    on the launch stream over `steps` calls, alternating, best of 3 rounds; the
+    row pass (quantisation) and GEMM stages from the library's HIP-event hook."""
+    import synth
+
+    res = {}
+    for c in synth.dit_mlp_fused_1024():
+        h = _dev16(c.h_bits, torch)
+        wq, sw = w8.quantize_weight_rowwise(_dev16(c.w_bits, torch), "int8")
+        bias = torch.from_numpy(c.bias).cuda()
+        if c.kind == "rmsnorm":
+            t = lambda v: torch.from_numpy(v).cuda()
+            prod = w8.Producer("rmsnorm", t(c.gamma), t(c.scale), t(c.shift), c.eps)
+        else:
+            prod = w8.Producer("gelu")
+        y = torch.empty((c.M, c.N), dtype=torch.float16, device="cuda")
+        ws = w8.new_workspace(w8.int8_mixed_linear_workspace_size(c.M, c.N, c.K))
+
+        def fused():
+            w8.int8_mixed_linear(h, wq, sw, THRESHOLD, out=y, workspace=ws, bias=bias, producer=prod)
+
+        def unfused():
+            w8.int8_mixed_linear(w8.debug_produce(h, prod), wq, sw, THRESHOLD, out=y, workspace=ws, bias=bias)
+
+        out = {}
+        for fn in (fused, unfused):
+            for _ in range(3):
+                fn()
+        # the two variants alternate over 3 rounds (the clock drifts under a
+        # long GEMM run); each keeps its fastest round
+        for _ in range(3):
+            for name, fn in (("fused", fused), ("unfused", unfused)):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(steps):
+                    fn()
+                e1.record()
+                e1.synchronize()
+                us = round(e0.elapsed_time(e1) / steps * 1e3, 2)
+                out[f"{name}_us"] = min(us, out.get(f"{name}_us", us))
+        for name, fn in (("fused", fused), ("unfused", unfused)):
+            w8.profile_start(steps)
+            for _ in range(steps):
+                fn()
+            ms, n = w8.profile_stop()
+            out[f"{name}_quant_us"] = round(ms[0] / n * 1e3, 2)
+            out[f"{name}_fixup_us"] = round(ms[1] / n * 1e3, 2)
+            out[f"{name}_gemm_us"] = round(ms[2] / n * 1e3, 2)
+        # HBM bytes of the quantisation stage: fused reads H and writes codes;
+        # unfused also writes X and reads it back
+        out["quant_bytes_fused"] = 3 * c.M * c.K
+        out["quant_bytes_unfused"] = 7 * c.M * c.K
+        out["saved_us"] = round(out["unfused_us"] - out["fused_us"], 2)
+        out["fused_tops"] = round(c.ops / (out["fused_us"] * 1e-6) / 1e12, 1)
+        res[c.name] = out
+        print(f"[bench] fused {c.name}: {out}", file=sys.stderr, flush=True)
+        del h, y, ws, wq
+    return res
+
+
 def counter_workload(torch, w8, cases, steps: int, copy_mib: int) -> None:
     """Minimal run for hardware-counter collection: `steps` int8 steps (after
     one warm-up step), then three plain device copies of `copy_mib` MiB, the
@@ -203,6 +267,7 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=4352, help="token rows per shape for the oracle baseline (4352 = the whole step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 W8A8 text-encoder layer timings")
+    ap.add_argument("--no-fused", action="store_true", help="skip the producer-fused DiT MLP timings")
     ap.add_argument("--counters", type=int, default=0, metavar="MIB",
                     help="counter-collection mode: a few int8 steps, then plain copies of MIB MiB; no JSON line")
     args = ap.parse_args()
@@ -314,6 +379,12 @@ def main() -> int:
             "workload": "FP8-E4M3 W8A8 text-encoder linears, 512 tokens, hidden 4096, bf16 in/out, "
                         "per-channel weight scale; dynamic per-token and static per-tensor activation scale",
             "layers": fp8_layers(torch, w8, args.steps),
+        }
+    if not args.no_fused:
+        out["fused_mlp"] = {
+            "workload": "DiT 1024^2 MLP with producers: up = RMSNorm+modulation(H [4352,4096]) x W [16384,4096], "
+                        "down = GELU(H [4352,16384]) x W [4096,16384]; bias, threshold 6.0, bf16 in, fp16 out",
+            "layers": fused_mlp(torch, w8, args.steps),
         }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

@@ -129,7 +129,7 @@ w8_status int8_mixed_linear(const void* X, int x_dt, int64_t M, int64_t K,
  *       rstd = fl32(1 / fl32(sqrt(fl32(fl32(ss/K) + eps))));
  *       x    = fl32(fl32(H*rstd) * fl32(gamma[k] * fl32(1 + scale[k]))) + shift[k].
  *     gamma (NULL: 1), scale (NULL: 0) and shift (NULL: no addition) are fp32
- *     [K] device vectors.
+ *     [K] device vectors, 16-byte aligned.
  *   W8_PRODUCER_GELU_TANH: GELU, tanh form (Hendrycks and Gimpel, 2016),
  *     evaluated as H / (1 + exp(-2u)) with u = sqrt(2/pi)(H + 0.044715 H^3).
  *     This equals 0.5 H (1 + tanh u). exp uses Cody-Waite reduction and a

@@ -256,13 +256,14 @@ def fused_case(kind: str, M: int, K: int, N: int, seed: int, dtype: str = "bf16"
     rmsnorm: H is a residual stream ~N(0,1) whose ``outlier_cols`` channels run
     at +-U(20,60) (they stay above the threshold after normalisation), with
     optional massive activations (~9000 in channel 2276 of 8 text-token rows,
-    as in ``_dit_x``); gain ~U(0.5,1.5), modulation scale ~U(-0.5,0.5), shift
-    ~U(-1,1). gelu: H is an MLP hidden state ~N(0,1.5^2) whose ``outlier_cols``
+    as in ``_dit_x``); gain ~U(0.8,1.2), modulation scale ~U(-0.2,0.2), shift
+    ~U(-0.2,0.2), so the normalised bulk stays far below the threshold and the
+    outlier columns are the planted ones (about 0.1%, the regime the threshold
+    is about). gelu: H is an MLP hidden state ~N(0,1) whose ``outlier_cols``
     channels run at +-U(6,60) (GELU keeps the positive ones, zeroes the
     negative ones). Weights ~N(0,0.02), bias ~N(0,0.1)."""
     rng = np.random.default_rng(seed)
-    std = 1.0 if kind == "rmsnorm" else 1.5
-    h = _normal(rng, (M, K), std)
+    h = _normal(rng, (M, K))
     lo, hi = (20.0, 60.0) if kind == "rmsnorm" else (6.0, 60.0)
     if outlier_cols:
         for c in rng.choice(K, size=min(outlier_cols, K), replace=False):
@@ -275,9 +276,9 @@ def fused_case(kind: str, M: int, K: int, N: int, seed: int, dtype: str = "bf16"
     bias = (prng.standard_normal(N) * 0.1).astype(np.float32)
     gamma = scale = shift = None
     if kind == "rmsnorm":
-        gamma = prng.uniform(0.5, 1.5, K).astype(np.float32)
-        scale = prng.uniform(-0.5, 0.5, K).astype(np.float32)
-        shift = prng.uniform(-1.0, 1.0, K).astype(np.float32)
+        gamma = prng.uniform(0.8, 1.2, K).astype(np.float32)
+        scale = prng.uniform(-0.2, 0.2, K).astype(np.float32)
+        shift = prng.uniform(-0.2, 0.2, K).astype(np.float32)
     return FusedCase(name or f"{kind}_{M}x{K}x{N}_s{seed}", kind, M, K, N, encode16(h, dtype), dtype,
                      encode16(w, dtype), dtype, bias, gamma, scale, shift)
 

@@ -294,6 +294,8 @@ static w8_status producer_args(const w8_producer* p, int64_t K, int* kind, w8::P
   W8_REQUIRE(K <= 16384, W8_ERR_UNSUPPORTED, "a producer needs K <= 16384, got %lld", (long long)K);
   if (p->kind == W8_PRODUCER_RMSNORM) {
     W8_REQUIRE(std::isfinite(p->eps) && p->eps >= 0.0f, W8_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+    W8_REQUIRE(aligned16(p->gamma) && aligned16(p->scale) && aligned16(p->shift), W8_ERR_INVALID_ARGUMENT,
+               "gamma, scale and shift must be 16-byte aligned");
     *kind = w8::kProdRms;
     *pa = w8::ProdArgs{p->gamma, p->scale, p->shift, p->eps, nullptr};
   } else {

@@ -107,21 +107,48 @@ __device__ __forceinline__ uint32_t produce1(uint32_t hbits, int k, float rstd, 
   }
 }
 
-// Eight elements of X (chunk c: columns 8c .. 8c+7) from eight of H.
+// Eight consecutive floats of an optional [K] vector (16-byte aligned).
+__device__ __forceinline__ void load8(const float* v, int c, float (&out)[8], float dflt) {
+  if (v) {
+    const float4 a = reinterpret_cast<const float4*>(v)[2 * c];
+    const float4 b = reinterpret_cast<const float4*>(v)[2 * c + 1];
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) out[j] = dflt;
+  }
+}
+
+// Eight elements of X (chunk c: columns 8c .. 8c+7) from eight of H; the
+// RMSNorm vectors are read as 16-byte loads, the same values produce1 reads.
 template <bool BF16, int PROD>
 __device__ __forceinline__ uint4 produce8(const uint4& hv, int c, float rstd, const ProdArgs& pa) {
+#pragma clang fp contract(off)
   if constexpr (PROD == kProdNone) {
     return hv;
   } else {
-    const uint32_t w[4] = {hv.x, hv.y, hv.z, hv.w};
-    uint32_t o[4];
+    float h[8];
+    unpack8<BF16>(hv, h);
+    uint32_t b[8];
+    if constexpr (PROD == kProdGelu) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t lo = produce1<BF16, PROD>(w[i] & 0xFFFFu, 8 * c + 2 * i, rstd, pa);
-      const uint32_t hi = produce1<BF16, PROD>(w[i] >> 16, 8 * c + 2 * i + 1, rstd, pa);
-      o[i] = lo | (hi << 16);
+      for (int j = 0; j < 8; ++j) b[j] = round16<BF16>(gelu32(h[j]));
+    } else {
+      float g[8], sc[8], sh[8];
+      load8(pa.gamma, c, g, 1.0f);
+      load8(pa.scale, c, sc, 0.0f);
+      load8(pa.shift, c, sh, 0.0f);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float gain = g[j] * (pa.scale ? 1.0f + sc[j] : 1.0f);
+        float x = h[j] * rstd;
+        x = x * gain;
+        if (pa.shift) x = x + sh[j];
+        b[j] = round16<BF16>(x);
+      }
     }
-    return make_uint4(o[0], o[1], o[2], o[3]);
+    return make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16));
   }
 }
 

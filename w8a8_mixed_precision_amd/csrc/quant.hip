@@ -401,21 +401,8 @@ __global__ __launch_bounds__(256) void k_outlier_fixup(
       const int nch = K >> 3;
       const float rr_std = PROD == kProdRms ? srstd[r] : 0.0f;
       float best = 0.0f;
-#pragma unroll 8
-      for (int c = tid; c < nch; c += 256) {
-        float f[8];
-        unpack8<BF16>(produce8<BF16, PROD>(xr[c], c, rr_std, pa), f);
-        const uint32_t ob = (smask[c >> 2] >> ((c & 3) * 8)) & 0xFFu;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (!((ob >> j) & 1u)) best = fmaxf(best, fabsf(f[j]));
-      }
-      best = block_max256(best, fred);
-      const float rr = 127.0f / best;
-#pragma unroll 8
-      for (int c = tid; c < nch; c += 256) {
-        float f[8];
-        unpack8<BF16>(produce8<BF16, PROD>(xr[c], c, rr_std, pa), f);
+      // the 8 codes of chunk c (outlier columns 0) with reciprocal scale rr
+      auto code8 = [&](const float (&f)[8], int c, float rr) {
         const uint32_t ob = (smask[c >> 2] >> ((c & 3) * 8)) & 0xFFu;
         uint32_t lo = 0, hi = 0;
 #pragma unroll
@@ -426,6 +413,53 @@ __global__ __launch_bounds__(256) void k_outlier_fixup(
           else hi |= bb << (8 * (j - 4));
         }
         qr[c] = make_uint2(lo, hi);
+      };
+      auto chunk_best = [&](const float (&f)[8], int c) {
+        const uint32_t ob = (smask[c >> 2] >> ((c & 3) * 8)) & 0xFFu;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (!((ob >> j) & 1u)) best = fmaxf(best, fabsf(f[j]));
+      };
+      if constexpr (PROD != kProdNone) {
+        // K <= 16384 with a producer: the row's X is made once and held in
+        // registers (8 chunks per thread) for both passes
+        uint4 xv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int c = tid + 256 * i;
+          if (c < nch) {
+            xv[i] = produce8<BF16, PROD>(xr[c], c, rr_std, pa);
+            float f[8];
+            unpack8<BF16>(xv[i], f);
+            chunk_best(f, c);
+          }
+        }
+        best = block_max256(best, fred);
+        const float rr = 127.0f / best;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int c = tid + 256 * i;
+          if (c < nch) {
+            float f[8];
+            unpack8<BF16>(xv[i], f);
+            code8(f, c, rr);
+          }
+        }
+      } else {
+#pragma unroll 8
+        for (int c = tid; c < nch; c += 256) {
+          float f[8];
+          unpack8<BF16>(xr[c], f);
+          chunk_best(f, c);
+        }
+        best = block_max256(best, fred);
+        const float rr = 127.0f / best;
+#pragma unroll 8
+        for (int c = tid; c < nch; c += 256) {
+          float f[8];
+          unpack8<BF16>(xr[c], f);
+          code8(f, c, rr);
+        }
       }
       if (tid == 0) sx[r0 + r] = best;
     }
