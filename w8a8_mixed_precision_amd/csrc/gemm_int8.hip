@@ -53,92 +53,178 @@ __device__ __forceinline__ v16f mfma_side(V8 a, V8 b, v16f c) {
   else return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// The 16-bit outlier operands of a 256x256 tile, copied into LDS at tile
+// start when the padded outlier count P is 32 (at most 32 outlier columns, the
+// usual case): XO rows m0 .. m0+255, then WO rows n0 .. n0+255, 64 bytes (32
+// values) per row. The four 16-byte chunks of row r are XOR-permuted by
+// (r >> 2) & 3, so eight consecutive rows read at one chunk hit distinct banks.
+constexpr int kSideRows = 256;
+constexpr int kSideLds = 2 * kSideRows * 64;    // 32 KB
+__device__ __forceinline__ int side_off(int row, int ch) { return row * 64 + ((ch ^ ((row >> 2) & 3)) << 4); }
+
+// Epilogue staging, one 32-column block of the wave tile at a time: all its
+// 32*WT rows x 32 columns go to the wave's staging area (row pitch
+// kStgPitchJ), then out as row segments of 32 elements. Every element of a
+// column block shares the lane's 16 column scales and biases, so these are
+// read from LDS once per block.
+constexpr int kStgPitchJ = 128 + 16;            // a staged row: 32 x 4 bytes + pad
+constexpr int kStgWaveJ = 128 * kStgPitchJ;     // one wave's staged rows (WT <= 4)
+constexpr int kEpiLds8 = kEpiCols + 4 * kStgWaveJ;
+
+// Column block j of the wave tile, registers -> staging area:
+// y = fl(acc) * rsx[i] (+ o[i]) then * cs + bias, per element; SIDE: o holds
+// the block's 16-bit outlier product per 32-row block i. MODE 0 stages the raw
+// int32 accumulators. ncol: first column of the block within the block tile.
+template <int MODE, bool SIDE, int WT>
+__device__ __forceinline__ void stage_cols(const v16i (&acc)[WT][WT], const v16f* o, int j, const float (&rsx)[4],
+                                           const float* __restrict__ scol, const float* __restrict__ sbias,
+                                           int ncol, int lane, char* __restrict__ stg) {
+  const int fr = lane & 31, fh = lane >> 5;
+  constexpr int EB = MODE == 1 ? 2 : 4;         // bytes per output element
+  v4f cs[4], bs[4];
+  if constexpr (MODE != 0) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      cs[g] = *reinterpret_cast<const v4f*>(scol + ncol + 8 * g + 4 * fh);
+      bs[g] = *reinterpret_cast<const v4f*>(sbias + ncol + 8 * g + 4 * fh);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < WT; ++i)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      char* dst = stg + (32 * i + fr) * kStgPitchJ + (8 * g + 4 * fh) * EB;
+      if constexpr (MODE == 0) {
+        *reinterpret_cast<v4i*>(dst) =
+            v4i{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+      } else {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a = static_cast<float>(acc[i][j][4 * g + e]);
+          const float t = SIDE ? __builtin_fmaf(a, rsx[i], o[i][4 * g + e]) : a * rsx[i];
+          v[e] = __builtin_fmaf(t, cs[g][e], bs[g][e]);
+        }
+        if constexpr (MODE == 1) {
+          const uint32_t lo = f32_to_f16_bits(v[0]) | (static_cast<uint32_t>(f32_to_f16_bits(v[1])) << 16);
+          const uint32_t hi = f32_to_f16_bits(v[2]) | (static_cast<uint32_t>(f32_to_f16_bits(v[3])) << 16);
+          *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+        } else {
+          *reinterpret_cast<v4f*>(dst) = v4f{v[0], v[1], v[2], v[3]};
+        }
+      }
+    }
+}
+
+// Writes the R staged rows of a column block (32 elements of EB bytes each) to
+// Y rows m_base.. and columns n_base.. (clipped to [M, N)): every lane stores
+// 16-byte chunks, 64 / (32 * EB / 16) rows per instruction, reading at most 8
+// chunks from LDS ahead of their stores. vec: rows of Y are 16-byte aligned.
+template <int EB, int R>
+__device__ __forceinline__ void flush_cols(const char* stg, char* __restrict__ y, int M, int N, int m_base,
+                                           int n_base, int lane, bool vec) {
+  constexpr int EPC = 16 / EB;                  // elements per 16-byte chunk
+  constexpr int CPR = 32 / EPC;                 // chunks per staged row: 4 or 8
+  constexpr int RPI = 64 / CPR;                 // rows per instruction: 16 or 8
+  constexpr int T = R / RPI;                    // store instructions
+  constexpr int TB = T > 8 ? 8 : T;             // chunks read ahead
+  const int ch = lane % CPR;
+  const int n = n_base + ch * EPC;
+#pragma unroll
+  for (int t0 = 0; t0 < T; t0 += TB) {
+    uint4 v[TB];
+#pragma unroll
+    for (int t = 0; t < TB; ++t)
+      v[t] = *reinterpret_cast<const uint4*>(stg + (RPI * (t0 + t) + lane / CPR) * kStgPitchJ + ch * 16);
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+      const int m = m_base + RPI * (t0 + t) + lane / CPR;
+      if (m < M) {
+        char* dst = y + (static_cast<int64_t>(m) * N + n) * EB;
+        if (vec && n + EPC <= N) {
+          *reinterpret_cast<uint4*>(dst) = v[t];
+        } else {
+          const uint32_t w[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) {
+            if (n + e >= N) break;
+            if constexpr (EB == 2)
+              *reinterpret_cast<uint16_t*>(dst + 2 * e) = static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)));
+            else
+              *reinterpret_cast<uint32_t*>(dst + 4 * e) = w[e];
+          }
+        }
+      }
+    }
+  }
+}
+
 // Epilogue shared by the GEMM kernels, for a wave tile of WT x WT 32x32 MFMA
 // tiles (WT = 4: 256x256 blocks, 2: 128x128 blocks). The MFMAs compute each
 // tile transposed (Wq fragment as the first operand), so element r of tile
 // (i, j) of a lane is
 //   m = m0 + wm*32*WT + 32*i + (lane&31),
-//   n = n0 + wn*32*WT + 32*j + 8*(r>>2) + 4*(lane>>5) + (r&3),
-// staged through LDS a row block at a time (flush_staged).
+//   n = n0 + wn*32*WT + 32*j + 8*(r>>2) + 4*(lane>>5) + (r&3).
+// Written one column block j at a time (stage_cols, flush_cols).
 //
 // rsx[i]: sx[m]/127 for the lane's row of block i (prefetched by the caller);
-// scol: LDS copy of sw[n0 .. n0+64*WT) / 127; sbias: LDS copy of the bias
-// there (null: no bias); stg: this wave's staging area.
+// scol, sbias: LDS copies of sw[n0 .. n0+64*WT) / 127 and of the bias there
+// (zeros without one); side: the tile's outlier operands in LDS (side_off
+// layout; null: none were staged); stg: this wave's staging area (kStgWaveJ).
 template <int MODE, bool XBF16, int WT = 4>
 __device__ __forceinline__ void epilogue(v16i (&acc)[WT][WT], int M, int N, int m0, int n0, int wm, int wn, int lane,
                                          const float (&rsx)[4], const float* scol, const float* sbias, int nO,
                                          const uint16_t* __restrict__ XO, const uint16_t* __restrict__ WO,
-                                         void* __restrict__ Y, char* stg) {
+                                         const char* side, void* __restrict__ Y, char* stg) {
   const int fr = lane & 31, fh = lane >> 5;
   constexpr int EB = MODE == 1 ? 2 : 4;         // bytes per output element
-  constexpr int ROWB = 32 * WT * EB;            // bytes of one output row of the wave tile
-  constexpr int H = ROWB > 256 ? ROWB / 256 : 1;   // staging passes per 32-row block
-  constexpr int PJ = WT / H;                    // 32-column MFMA tiles per pass
-  constexpr int RB = 32 * PJ * EB;              // staged row bytes: 256 or 128
   constexpr int WR = 32 * WT;                   // rows (= columns) of the wave tile
-  const bool vec = (static_cast<int64_t>(N) * EB) % 16 == 0;
   const int P = (nO + 31) & ~31;
+  const bool vec = (static_cast<int64_t>(N) * EB) % 16 == 0;
   using V8 = typename std::conditional<XBF16, v8bf, v8h>::type;
   char* const y = static_cast<char*>(Y);
+  const int row0 = m0 + wm * WR;
 #pragma unroll
-  for (int i = 0; i < WT; ++i) {
-    // side product for this 32-row block: o[j] = WO(block j) . XO(rows of block i)^T
-    v16f o[WT];
+  for (int j = 0; j < WT; ++j) {
+    const int ncol = wn * WR + 32 * j;
+    if (MODE == 0 || P == 0) {
+      stage_cols<MODE, false, WT>(acc, nullptr, j, rsx, scol, sbias, ncol, lane, stg);
+    } else {
+      // side product for this column block: o[i] = WO(block j) . XO(rows of block i)^T
+      v16f o[WT];
 #pragma unroll
-    for (int j = 0; j < WT; ++j)
+      for (int i = 0; i < WT; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[j][r] = 0.0f;
-    if constexpr (MODE != 0) {
-      const int m = m0 + wm * WR + 32 * i + fr;
-      const int64_t xrow = static_cast<int64_t>(min(m, M - 1)) * P;
-      for (int c = 0; c < P; c += 16) {
-        const V8 xb = *reinterpret_cast<const V8*>(XO + xrow + c + 8 * fh);
+        for (int r = 0; r < 16; ++r) o[i][r] = 0.0f;
+      if (side && P == 32) {
+        const char* sx_rows = side;
+        const char* sw_rows = side + kSideRows * 64;
 #pragma unroll
-        for (int j = 0; j < WT; ++j) {
-          const V8 wa = *reinterpret_cast<const V8*>(
-              WO + static_cast<int64_t>(min(n0 + wn * WR + 32 * j + fr, N - 1)) * P + c + 8 * fh);
-          o[j] = mfma_side<XBF16>(wa, xb, o[j]);
+        for (int c = 0; c < 2; ++c) {
+          const V8 wa = *reinterpret_cast<const V8*>(sw_rows + side_off(ncol + fr, 2 * c + fh));
+#pragma unroll
+          for (int i = 0; i < WT; ++i) {
+            const V8 xb = *reinterpret_cast<const V8*>(sx_rows + side_off(wm * WR + 32 * i + fr, 2 * c + fh));
+            o[i] = mfma_side<XBF16>(wa, xb, o[i]);
+          }
         }
-      }
-    }
+      } else {
+        const int64_t wrow = static_cast<int64_t>(min(n0 + ncol + fr, N - 1)) * P;
+        for (int c = 0; c < P; c += 16) {
+          const V8 wa = *reinterpret_cast<const V8*>(WO + wrow + c + 8 * fh);
 #pragma unroll
-    for (int h = 0; h < H; ++h) {
-      // registers -> staging: row fr, columns 32*jj + 8*g + 4*fh .. +4 of this pass
-#pragma unroll
-      for (int jj = 0; jj < PJ; ++jj) {
-        const int j = h * PJ + jj;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          char* dst = stg + fr * kStgPitch + (32 * jj + 8 * g + 4 * fh) * EB;
-          if constexpr (MODE == 0) {
-            *reinterpret_cast<v4i*>(dst) =
-                v4i{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-          } else {
-            const v4f cs = *reinterpret_cast<const v4f*>(scol + wn * WR + 32 * j + 8 * g + 4 * fh);
-            float v[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              v[e] = (static_cast<float>(acc[i][j][4 * g + e]) * rsx[i] + o[j][4 * g + e]) * cs[e];
-            if (sbias) {
-              const v4f bs = *reinterpret_cast<const v4f*>(sbias + wn * WR + 32 * j + 8 * g + 4 * fh);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] = v[e] + bs[e];
-            }
-            if constexpr (MODE == 1) {
-              const uint32_t lo = f32_to_f16_bits(v[0]) | (static_cast<uint32_t>(f32_to_f16_bits(v[1])) << 16);
-              const uint32_t hi = f32_to_f16_bits(v[2]) | (static_cast<uint32_t>(f32_to_f16_bits(v[3])) << 16);
-              *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
-            } else {
-              *reinterpret_cast<v4f*>(dst) = v4f{v[0], v[1], v[2], v[3]};
-            }
+          for (int i = 0; i < WT; ++i) {
+            const V8 xb = *reinterpret_cast<const V8*>(
+                XO + static_cast<int64_t>(min(row0 + 32 * i + fr, M - 1)) * P + c + 8 * fh);
+            o[i] = mfma_side<XBF16>(wa, xb, o[i]);
           }
         }
       }
-      // staging -> global: 8 instructions of 4 rows x 16 chunks of 16 bytes
-      wave_lds_fence();
-      flush_staged<EB, RB>(stg, y, M, N, m0 + wm * WR + 32 * i, n0 + wn * WR + h * PJ * 32, lane, vec);
-      wave_lds_fence();                         // staging reads done before the next pass writes
+      stage_cols<MODE, true, WT>(acc, o, j, rsx, scol, sbias, ncol, lane, stg);
     }
+    wave_lds_fence();
+    flush_cols<EB, WR>(stg, y, M, N, row0, n0 + ncol, lane, vec);
+    wave_lds_fence();                           // staging reads done before the next block writes
   }
 }
 
@@ -172,12 +258,12 @@ __device__ __forceinline__ void epi_prefetch(EpiIn& e, int M, int N, int m0, int
 }
 
 // Finishes the prefetch (divides by 127, publishes the column scales in LDS)
-// and runs the epilogue. `lds` is at least kEpiLds bytes of LDS that the K loop
+// and runs the epilogue. `lds` is at least kEpiLds8 bytes of LDS that the K loop
 // no longer uses. Every wave of the block must call it.
 template <int MODE, bool XBF16, int WT = 4>
 __device__ __forceinline__ void finish_tile(v16i (&acc)[WT][WT], EpiIn& e, char* lds, int M, int N, int m0, int n0,
                                             int wm, int wn, int lane, const uint16_t* __restrict__ XO,
-                                            const uint16_t* __restrict__ WO, const float* __restrict__ bias,
+                                            const uint16_t* __restrict__ WO, const char* side,
                                             void* __restrict__ Y) {
   float* scol = reinterpret_cast<float*>(lds);
   float* sbias = scol + 256;
@@ -185,11 +271,11 @@ __device__ __forceinline__ void finish_tile(v16i (&acc)[WT][WT], EpiIn& e, char*
 #pragma unroll
     for (int i = 0; i < 4; ++i) e.rsx[i] = e.rsx[i] / 127.0f;
     scol[threadIdx.x] = e.my_sw / 127.0f;
-    if (bias) sbias[threadIdx.x] = e.my_bias;
+    sbias[threadIdx.x] = e.my_bias;             // 0 without a bias
     __syncthreads();
   }
-  epilogue<MODE, XBF16, WT>(acc, M, N, m0, n0, wm, wn, lane, e.rsx, scol, MODE != 0 && bias ? sbias : nullptr,
-                            e.nO, XO, WO, Y, lds + kEpiCols + (threadIdx.x >> 6) * kStgWave);
+  epilogue<MODE, XBF16, WT>(acc, M, N, m0, n0, wm, wn, lane, e.rsx, scol, sbias, e.nO, XO, WO, side, Y,
+                            lds + kEpiCols + (threadIdx.x >> 6) * kStgWaveJ);
 }
 
 __device__ __forceinline__ void zero_acc(v16i (&acc)[4][4]) {
@@ -214,8 +300,10 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm(const int8_t* __restrict__
                                                       const float* __restrict__ bias, void* __restrict__ Y,
                                                       int tiles_m, int tiles_n, uint32_t* __restrict__ clear,
                                                       int clear_words) {
-  __shared__ __attribute__((aligned(16))) int8_t lds[2][2][kBM * kBK];
-  static_assert(sizeof(lds) >= kEpiLds, "epilogue LDS");
+  // two stages of A and B, and the epilogue's LDS after the K loop
+  constexpr int kLdsBytes = 4 * kBM * kBK > kEpiLds8 ? 4 * kBM * kBK : kEpiLds8;
+  __shared__ __attribute__((aligned(16))) int8_t lds_raw[kLdsBytes];
+  int8_t (*lds)[2][kBM * kBK] = reinterpret_cast<int8_t (*)[2][kBM * kBK]>(lds_raw);
 
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
@@ -271,8 +359,8 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm(const int8_t* __restrict__
     if (kt + 1 < nk) lstore(st ^ 1);
     __syncthreads();
   }
-  finish_tile<MODE, XBF16>(acc, ein, reinterpret_cast<char*>(&lds[0][0][0]), M, N, m0, n0, wm, wn, lane, XO, WO, bias,
-                           Y);
+  finish_tile<MODE, XBF16>(acc, ein, reinterpret_cast<char*>(&lds[0][0][0]), M, N, m0, n0, wm, wn, lane, XO, WO,
+                           nullptr, Y);
 }
 
 // ---------------------------------------------------------------------------
@@ -444,7 +532,7 @@ __device__ __forceinline__ void small_block(int8_t* lds, const int8_t* __restric
                                             int tiles_n, int dp_tiles, int split, int* __restrict__ part,
                                             int* __restrict__ cnt) {
   constexpr int SS = 2 * S;                     // the same LDS as S big stages
-  int* const s_last = reinterpret_cast<int*>(lds + kEpiLds);
+  int* const s_last = reinterpret_cast<int*>(lds + kEpiLds8);
   const int nu = gridDim.x - dp_tiles;
   const int v = xcd_remap(blockIdx.x - dp_tiles, nu);
   const int Q = nu / split;                     // quarter tiles
@@ -534,7 +622,7 @@ __device__ __forceinline__ void small_block(int8_t* lds, const int8_t* __restric
         for (int e = 0; e < 4; ++e) acc[t >> 3][(t >> 2) & 1][4 * (t & 3) + e] += w[t][e];
     }
   }
-  finish_tile<MODE, XBF16, 2>(acc, ein, reinterpret_cast<char*>(lds), M, N, m0, n0, wm, wn, lane, XO, WO, bias, Y);
+  finish_tile<MODE, XBF16, 2>(acc, ein, reinterpret_cast<char*>(lds), M, N, m0, n0, wm, wn, lane, XO, WO, nullptr, Y);
 }
 
 // Work split for the last, partial wave of tiles (split-K). The first
@@ -558,15 +646,16 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
                                                           uint32_t* __restrict__ clear, int clear_words) {
   constexpr int kStage = 2 * kBM * kBK;       // A then B, 32 KB
   constexpr int kLoads = 8;                   // DMA instructions per wave per step
-  __shared__ __attribute__((aligned(1024))) int8_t lds[S * kStage];
-  static_assert(sizeof(lds) >= kEpiLds, "epilogue LDS");
+  // the ring, then the tile's outlier operands (kSideLds)
+  __shared__ __attribute__((aligned(1024))) int8_t lds[S * kStage + kSideLds];
+  static_assert(S * kStage >= kEpiLds8, "epilogue LDS");
   // A second __shared__ object would make the compiler guard every LDS read in
   // the K loop with a full vmcnt wait (it cannot tell the DMA destinations
   // apart from it); the split-K arrival flag lives in the ring instead, which
   // the K loop no longer uses by then (past the epilogue's LDS, so the
   // epilogue cannot overwrite it while a wave still reads it).
-  int* const s_last = reinterpret_cast<int*>(lds + kEpiLds);
-  static_assert(sizeof(lds) >= kEpiLds + 4, "epilogue LDS and arrival flag");
+  int* const s_last = reinterpret_cast<int*>(lds + kEpiLds8);
+  static_assert(S * kStage >= kEpiLds8 + 4, "epilogue LDS and arrival flag");
 
   // The quantisation pass before this kernel is complete, so its outlier-column
   // mask can be cleared here for the next call.
@@ -632,7 +721,27 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
   zero_acc(acc);
 
   for (int s = 0; s < S; ++s) issue(s);
-  wait_vmcnt<(S - 1) * kLoads>();                 // step 0 landed (this wave)
+  // The outlier operands of the tile for a padded outlier count of 32 (the
+  // count is not known yet; the epilogue uses them only for that count), after
+  // the ring's first stages so that step 0 does not wait for them. XO and WO
+  // hold at least 32 values per row, so the clamped rows are in bounds.
+  const bool side = MODE != 0 && XO != nullptr && WO != nullptr;
+  if (side) {
+    int8_t* sl = lds + S * kStage;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int r = (wave * 4 + t) * 16 + (lane >> 2);
+      const int ch = (lane & 3) ^ ((r >> 2) & 3);
+      __builtin_amdgcn_global_load_lds(XO + static_cast<int64_t>(min(m0 + r, M - 1)) * 32 + ch * 8,
+                                       sl + (wave * 4 + t) * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(WO + static_cast<int64_t>(min(n0 + r, N - 1)) * 32 + ch * 8,
+                                       sl + kSideRows * 64 + (wave * 4 + t) * 1024, 16, 0, 0);
+    }
+  }
+  // step 0 landed (this wave); the waits of the first K steps also cover
+  // the 8 side loads, in flight behind the ring's
+  if (side) wait_vmcnt<(S - 1) * kLoads + 8>();
+  else wait_vmcnt<(S - 1) * kLoads>();
   block_barrier();                                // ... for every wave
   v4i f0[8], f1[8];
   load_frags(lds, 0, wm, wn, lane, f0);
@@ -698,7 +807,8 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
       }
     }
   }
-  finish_tile<MODE, XBF16>(acc, ein, reinterpret_cast<char*>(lds), M, N, m0, n0, wm, wn, lane, XO, WO, bias, Y);
+  finish_tile<MODE, XBF16>(acc, ein, reinterpret_cast<char*>(lds), M, N, m0, n0, wm, wn, lane, XO, WO,
+                           side ? reinterpret_cast<const char*>(lds) + S * kStage : nullptr, Y);
 }
 
 // ---------------------------------------------------------------------------
@@ -782,6 +892,8 @@ GemmPlan plan_int8_gemm_forced(int64_t M, int64_t N, int cus, bool small, int sp
 // plan.split > 1 (plan.sk_tiles * plan.split partials, plan.sk_tiles counters
 // that must be zero; they are left zero). `clear` (may be null): clear_words
 // words that the kernel zeroes (the outlier-column mask of the pass before).
+// XO [M, P] and WO [N, P] (P = the outlier count nO padded to 32) may be null
+// when mode is 0; otherwise their buffers hold at least 32 values per row.
 void launch_int8_gemm(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t K, const float* sx,
                       const float* sw, const int* nO, const uint16_t* XO, const uint16_t* WO, bool xbf16,
                       const float* bias, void* Y, int mode, const GemmPlan& plan, int* part, int* cnt,

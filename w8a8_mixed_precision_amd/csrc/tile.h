@@ -89,7 +89,8 @@ constexpr int kEpiLds = kEpiCols + 4 * kStgWave;   // + 4 staging areas
 // Writes the wave's 32 staged rows (RB bytes each: 256 or 128; EB bytes per
 // element) to Y rows m_base.. and columns n_base.., clipped to [M, N). `vec`:
 // rows of Y are 16-byte aligned (N * EB % 16 == 0), so whole chunks can be
-// stored. One instruction covers 64 / (RB / 16) rows.
+// stored. One instruction covers 64 / (RB / 16) rows. All the lane's chunks
+// are read from the staging area first (one LDS round trip), then stored.
 template <int EB, int RB = 256>
 __device__ __forceinline__ void flush_staged(const char* stg, char* __restrict__ y, int M, int N, int m_base,
                                              int n_base, int lane, bool vec) {
@@ -97,24 +98,29 @@ __device__ __forceinline__ void flush_staged(const char* stg, char* __restrict__
   constexpr int EPC = 16 / EB;                  // elements per 16-byte chunk
   constexpr int CPR = RB / 16;                  // chunks per staged row
   constexpr int RPI = 64 / CPR;                 // rows per instruction
+  constexpr int T = 32 / RPI;                   // store instructions
+  const int ch = lane % CPR;
+  const int n = n_base + ch * EPC;
+  uint4 v[T];
 #pragma unroll
-  for (int t = 0; t < 32 / RPI; ++t) {
-    const int r = RPI * t + lane / CPR, ch = lane % CPR;
-    const char* src = stg + r * kStgPitch + ch * 16;
-    const int m = m_base + r;
-    const int n = n_base + ch * EPC;
+  for (int t = 0; t < T; ++t)
+    v[t] = *reinterpret_cast<const uint4*>(stg + (RPI * t + lane / CPR) * kStgPitch + ch * 16);
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int m = m_base + RPI * t + lane / CPR;
     if (m < M) {
       char* dst = y + (static_cast<int64_t>(m) * N + n) * EB;
       if (vec && n + EPC <= N) {
-        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+        *reinterpret_cast<uint4*>(dst) = v[t];
       } else {
+        const uint32_t w[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
 #pragma unroll
         for (int e = 0; e < EPC; ++e) {
           if (n + e >= N) break;
           if constexpr (EB == 2)
-            *reinterpret_cast<uint16_t*>(dst + 2 * e) = *reinterpret_cast<const uint16_t*>(src + 2 * e);
+            *reinterpret_cast<uint16_t*>(dst + 2 * e) = static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)));
           else
-            *reinterpret_cast<uint32_t*>(dst + 4 * e) = *reinterpret_cast<const uint32_t*>(src + 4 * e);
+            *reinterpret_cast<uint32_t*>(dst + 4 * e) = w[e];
         }
       }
     }
