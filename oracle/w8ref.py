@@ -25,7 +25,9 @@ first of them names):
   [FP8D]  "Qwen-Image-2.1 Text Encoder: FP8" card, section "Format": E4M3
           weights with one bf16 scale per output channel ([out, 1]);
           activations quantised per token at run time; the dequantised weight
-          is the FP8 value times its scale.
+          is the FP8 value times its scale, in bf16, for a weight-only
+          loader that computes in bf16 (section "How it was tested" measures
+          that weight-only mode beside W8A8).
   [FP8S]  "Darkstar-Qwen-Image-2.1-Base-ModelOpt-FP8" card, sections
           "Precision map" and "Provenance": E4M3 with static fp32 per-tensor
           weight and input scales, calibrated with the "max" algorithm.
@@ -335,6 +337,35 @@ def fp8_w8a8_linear(x_bits, x_dtype, wq8, sw, act_scale=None, out_dtype="bf16"):
     acc = fp8_contract(xq, wq8)
     y = sx.astype(np.float64)[:, None] * np.asarray(sw, np.float32).astype(np.float64)[None, :] * acc
     return {"xq": xq, "sx": sx, "acc": acc, "y": y, "Y": round_output(y, out_dtype)}
+
+
+# ---------------------------------------------------------------------------
+# FP8 weight-only (W8A16) [FP8D]: the card's weight-only loader dequantises
+# each weight to bf16 as the FP8 value times its channel scale and runs the
+# linear in bf16.
+# ---------------------------------------------------------------------------
+
+
+def dequantize_weight_fp8_bf16(wq8: np.ndarray, sw: np.ndarray) -> np.ndarray:
+    """bfloat16 bits of the dequantised weight, rne_bf16(dec(wq8[n,k]) * sw[n]).
+
+    sw holds bf16 values. An E4M3 value has at most 4 significant bits and a
+    bf16 scale 8, so the float64 product is exact and this is the one rounding
+    of a bf16 multiply (float product, rounded to bf16)."""
+    w = e4m3_decode(wq8) * np.asarray(sw, dtype=F32).astype(np.float64)[:, None]
+    return round_to_bf16(w)
+
+
+def fp8_w8a16_linear(x_bits, x_dtype, wq8, sw, out_dtype="bf16", rows=None):
+    """Y = X W_deq^T with W_deq = dequantize_weight_fp8_bf16(wq8, sw): the
+    16-bit X times the bf16 weights, summed in float64, one final rounding.
+    ``rows``: compute only these rows of Y."""
+    w_bits = dequantize_weight_fp8_bf16(wq8, sw)
+    xf = decode16(x_bits, x_dtype).astype(np.float64)
+    if rows is not None:
+        xf = xf[np.asarray(rows)]
+    y = xf @ decode16(w_bits, "bf16").astype(np.float64).T
+    return {"w_bits": w_bits, "y": y, "Y": round_output(y, out_dtype)}
 
 
 # ---------------------------------------------------------------------------
