@@ -27,6 +27,7 @@ if ROOT not in sys.path:
 METRIC = "int8 mixed-precision linear TOPS at 1024^2 DiT shapes; % of MFMA peak"
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, published
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, published
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 THRESHOLD = 6.0
 
@@ -104,6 +105,40 @@ def fp8_layers(torch, w8, steps: int) -> dict:
                 "gemm_roofline_frac": round(t_roof / gemm_us, 3),
             }
             print(f"[bench] fp8 {layer} {mode}: {res[f'{layer}_{c.M}x{c.K}x{c.N}_{mode}']}", file=sys.stderr, flush=True)
+    return res
+
+
+def w8a16_layers(torch, w8, steps: int) -> dict:
+    """FP8 weight-only (W8A16) text-encoder linears at 512 tokens: GEMM time
+    from the HIP-event hook (the whole call is the one GEMM kernel), TFLOP/s
+    and the fraction of its roofline max(2MNK / 2.5 PFLOP/s bf16,
+    bytes / 8 TB/s), bytes = 2 M K + N K + 2 M N (bf16 X, E4M3 W, bf16 Y)."""
+    import synth
+
+    res = {}
+    for layer in synth.FP8_TEXT_LAYERS:
+        c = synth.fp8_text_encoder(layer)
+        x = _dev16(c.x_bits, torch)
+        wq, sw = w8.quantize_weight_rowwise(_dev16(c.w_bits, torch), "fp8")
+        y = torch.empty((c.M, c.N), dtype=torch.bfloat16, device="cuda")
+        ws = w8.new_workspace(w8.fp8_w8a16_linear_workspace_size(c.M, c.N, c.K))
+        for _ in range(3):
+            w8.fp8_w8a16_linear(x, wq, sw, out=y, workspace=ws)
+        w8.profile_start(steps)
+        for _ in range(steps):
+            w8.fp8_w8a16_linear(x, wq, sw, out=y, workspace=ws)
+        ms, n = w8.profile_stop()
+        gemm_us = ms[2] / n * 1e3
+        gbytes = 2 * c.M * c.K + c.N * c.K + 2 * c.M * c.N
+        t_roof = max(c.ops / (PEAK_BF16_TFLOPS * 1e12), gbytes / (PEAK_HBM_GBS * 1e9)) * 1e6
+        key = f"{layer}_{c.M}x{c.K}x{c.N}"
+        res[key] = {
+            "gemm_us": round(gemm_us, 2),
+            "gemm_tflops": round(c.ops / (gemm_us * 1e-6) / 1e12, 1),
+            "gemm_roofline_us": round(t_roof, 2),
+            "gemm_roofline_frac": round(t_roof / gemm_us, 3),
+        }
+        print(f"[bench] w8a16 {layer}: {res[key]}", file=sys.stderr, flush=True)
     return res
 
 
@@ -266,7 +301,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-rows", type=int, default=4352, help="token rows per shape for the oracle baseline (4352 = the whole step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 W8A8 text-encoder layer timings")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 text-encoder layer timings (W8A8 and weight-only)")
     ap.add_argument("--no-fused", action="store_true", help="skip the producer-fused DiT MLP timings")
     ap.add_argument("--counters", type=int, default=0, metavar="MIB",
                     help="counter-collection mode: a few int8 steps, then plain copies of MIB MiB; no JSON line")
@@ -379,6 +414,11 @@ def main() -> int:
             "workload": "FP8-E4M3 W8A8 text-encoder linears, 512 tokens, hidden 4096, bf16 in/out, "
                         "per-channel weight scale; dynamic per-token and static per-tensor activation scale",
             "layers": fp8_layers(torch, w8, args.steps),
+        }
+        out["fp8_w8a16"] = {
+            "workload": "FP8-E4M3 weight-only text-encoder linears, 512 tokens, hidden 4096: bf16 X, E4M3 weights "
+                        "widened to bf16 (value x channel scale) in the GEMM, bf16 MFMA, bf16 out",
+            "layers": w8a16_layers(torch, w8, args.steps),
         }
     if not args.no_fused:
         out["fused_mlp"] = {

@@ -17,6 +17,10 @@
  *     quantised per token at run time; "Darkstar-Qwen-Image-2.1-Base-ModelOpt-
  *     FP8" card, section "Precision map": static per-tensor input scale).
  *
+ *  3. FP8-E4M3 weight-only (W8A16): the same E4M3 weights, widened to bf16
+ *     inside the GEMM, with bf16 activations (the same card's weight-only
+ *     loader).
+ *
  * Conventions for every entry point
  *  - Layouts are row-major and dense: X [M,K], W and Wq [N,K] (the [out,in]
  *    order of a linear layer), Y [M,N]. Base pointers must be 16-byte aligned.
@@ -191,6 +195,39 @@ w8_status fp8_w8a8_linear(const void* X, int x_dt, int64_t M, int64_t K,
                           const float* act_scale, void* Y, int y_dt,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fp8_w8a16_linear -- Y = X W_deq^T with E4M3 weights and bf16 activations
+ * (weight-only FP8).
+ *
+ * The weight-only loader of the FP8 text-encoder card ("Qwen-Image-2.1 Text
+ * Encoder: FP8", section "Format"; measured as "weight-only" in section "How
+ * it was tested") turns each weight into bf16 as its FP8 value times the bf16
+ * scale of its output channel, and computes in bf16:
+ *   W_deq[n,k] = rne_bf16(e4m3(Wq8[n,k]) * sw[n])   (the product is exact)
+ *   Y[m,n]     = sum_k X[m,k] * W_deq[n,k], fp32 accumulation on bf16 MFMA,
+ *                rounded to nearest even into Y.
+ * The weights stay E4M3 in memory: they are widened to bf16 on the way from
+ * LDS to the matrix cores, never written out.
+ *
+ *   X          [M,K] bf16, device (other types: W8_ERR_UNSUPPORTED).
+ *   Wq8, sw    the W8_Q_FP8_E4M3 output of quantize_weight_rowwise (sw holds
+ *              bf16 values); codes 0x7F / 0xFF (NaN) are outside the contract.
+ *   Y          [M,N] bf16, f16 or f32, device.
+ *   workspace  device memory of at least fp8_w8a16_linear_workspace_size()
+ *              bytes (depends on M, N, K and the current device's
+ *              compute-unit count; at least 256), 256-byte aligned,
+ *              zero-filled before its first use; every call leaves its split-K
+ *              arrival counters zero again, the rest is scratch.
+ * Results are bitwise reproducible for a given device (split-K partial sums
+ * are added in a fixed order).
+ * Requires M, N >= 1, 64 <= K <= 65536, K % 64 == 0 (else W8_ERR_UNSUPPORTED).
+ */
+size_t fp8_w8a16_linear_workspace_size(int64_t M, int64_t N, int64_t K);
+w8_status fp8_w8a16_linear(const void* X, int x_dt, int64_t M, int64_t K,
+                           const uint8_t* Wq8, const float* sw, int64_t N,
+                           void* Y, int y_dt, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 /* Readable name of a status; never NULL. */
 const char* w8_status_string(int status);
 /* Detail of the last failed call on this host thread ("" if none). */
@@ -251,6 +288,17 @@ size_t w8dbg_fp8_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int split,
 w8_status w8dbg_fp8_gemm(const uint8_t* xq, const float* sx, const uint8_t* Wq8, const float* sw,
                          int64_t M, int64_t N, int64_t K, int split, int tile, void* Y, int y_dt,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* fp8_w8a16_linear with a given output tiling: split = 0 is the linear's own
+ * choice (tile ignored); split >= 1 uses tile x tile output blocks (128 or
+ * 256; 0 means 256) with each K range cut into `split` slices, split <= K / 64
+ * (else W8_ERR_UNSUPPORTED). Same requirements as fp8_w8a16_linear otherwise;
+ * workspace: w8dbg_fp8_w8a16_linear_workspace_size(M, N, K, split, tile) bytes
+ * (at least 256), zero-filled before first use (left zero). */
+size_t w8dbg_fp8_w8a16_linear_workspace_size(int64_t M, int64_t N, int64_t K, int split, int tile);
+w8_status w8dbg_fp8_w8a16_linear(const void* X, int x_dt, int64_t M, int64_t K, const uint8_t* Wq8,
+                                 const float* sw, int64_t N, int split, int tile, void* Y, int y_dt,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Measurement hook (process-wide, for benchmarks; not for concurrent use).

@@ -137,6 +137,46 @@ def test_fp8_linear_rejects(kw, status):
     assert _fp8(**kw) == status
 
 
+def _w16(**kw):
+    a = dict(X=A, x_dt=_abi.W8_DT_BF16, M=512, K=4096, Wq=A, sw=A, N=1024, Y=A, y_dt=_abi.W8_DT_BF16,
+             ws=A, ws_bytes=WS_BIG, stream=None)
+    a.update(kw)
+    return _abi.lib().fp8_w8a16_linear(a["X"], a["x_dt"], a["M"], a["K"], a["Wq"], a["sw"], a["N"], a["Y"],
+                                       a["y_dt"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), _abi.W8_ERR_INVALID_ARGUMENT),
+    (dict(sw=None), _abi.W8_ERR_INVALID_ARGUMENT),
+    (dict(M=0), _abi.W8_ERR_INVALID_ARGUMENT),
+    (dict(K=100), _abi.W8_ERR_INVALID_ARGUMENT),                 # K % 16 != 0
+    (dict(K=4112), _abi.W8_ERR_UNSUPPORTED),                     # K % 64 != 0
+    (dict(K=65600), _abi.W8_ERR_UNSUPPORTED),
+    (dict(x_dt=_abi.W8_DT_F16), _abi.W8_ERR_UNSUPPORTED),        # bf16 activations only
+    (dict(y_dt=7), _abi.W8_ERR_UNSUPPORTED),
+    (dict(Wq=A + 8), _abi.W8_ERR_INVALID_ARGUMENT),
+    (dict(ws=None), _abi.W8_ERR_WORKSPACE),
+    (dict(ws_bytes=16), _abi.W8_ERR_WORKSPACE),
+])
+def test_w8a16_linear_rejects(kw, status):
+    assert _w16(**kw) == status
+
+
+def test_w8a16_workspace_and_debug_rejects():
+    lib = _abi.lib()
+    assert lib.fp8_w8a16_linear_workspace_size(512, 4096, 4096) >= 256
+    assert lib.fp8_w8a16_linear_workspace_size(0, 4096, 4096) == 0
+    assert lib.w8dbg_fp8_w8a16_linear_workspace_size(4, 4, 128, 2, 256) >= 2 * 256 * 256 * 4
+    assert lib.w8dbg_fp8_w8a16_linear_workspace_size(4, 4, 128, 1, 0) == 256
+    g = lib.w8dbg_fp8_w8a16_linear
+    bf = _abi.W8_DT_BF16
+    assert g(A, bf, 4, 128, A, A, 4, -1, 0, A, bf, A, WS_BIG, None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert g(A, bf, 4, 128, A, A, 4, 1, 64, A, bf, A, WS_BIG, None) == _abi.W8_ERR_INVALID_ARGUMENT   # tile
+    assert g(A, bf, 4, 128, A, A, 4, 3, 0, A, bf, A, WS_BIG, None) == _abi.W8_ERR_UNSUPPORTED         # > K/64
+    need = lib.w8dbg_fp8_w8a16_linear_workspace_size(4, 4, 128, 2, 128)
+    assert g(A, bf, 4, 128, A, A, 4, 2, 128, A, bf, A, need - 256, None) == _abi.W8_ERR_WORKSPACE
+
+
 @pytest.mark.parametrize("args,status", [
     ((None, _abi.W8_DT_BF16, 16, 64, _abi.W8_Q_INT8, A, A, None), _abi.W8_ERR_INVALID_ARGUMENT),
     ((A, _abi.W8_DT_F32, 16, 64, _abi.W8_Q_INT8, A, A, None), _abi.W8_ERR_UNSUPPORTED),

@@ -14,7 +14,8 @@ from ._abi import W8Error, lib  # noqa: F401
 _DT = {torch.float16: _abi.W8_DT_F16, torch.bfloat16: _abi.W8_DT_BF16, torch.float32: _abi.W8_DT_F32}
 
 __all__ = [
-    "quantize_weight_rowwise", "int8_mixed_linear", "fp8_w8a8_linear", "Producer", "debug_produce",
+    "quantize_weight_rowwise", "int8_mixed_linear", "fp8_w8a8_linear", "fp8_w8a16_linear", "Producer",
+    "debug_produce", "debug_fp8_w8a16_linear", "fp8_w8a16_linear_workspace_size",
     "debug_int8_quantize_activations", "debug_int8_gemm_i32", "debug_fp8_quantize_activations", "debug_fp8_gemm",
     "int8_mixed_linear_workspace_size", "fp8_w8a8_linear_workspace_size", "new_workspace", "W8Error",
 ]
@@ -56,6 +57,10 @@ def int8_mixed_linear_workspace_size(M: int, N: int, K: int) -> int:
 
 def fp8_w8a8_linear_workspace_size(M: int, N: int, K: int) -> int:
     return int(lib().fp8_w8a8_linear_workspace_size(M, N, K))
+
+
+def fp8_w8a16_linear_workspace_size(M: int, N: int, K: int) -> int:
+    return int(lib().fp8_w8a16_linear_workspace_size(M, N, K))
 
 
 def quantize_weight_rowwise(w: torch.Tensor, fmt: str = "int8"):
@@ -155,6 +160,36 @@ def fp8_w8a8_linear(x: torch.Tensor, wq8: torch.Tensor, sw: torch.Tensor, act_sc
     sp = 0 if act_scale is None else _dev(act_scale, "act_scale").data_ptr()
     _abi.check(lib().fp8_w8a8_linear(x.data_ptr(), _dt(x), M, K, wq8.data_ptr(), sw.data_ptr(), N, sp,
                                      y.data_ptr(), _dt(y), ws.data_ptr(), ws.numel(), _stream(x)))
+    return y
+
+
+def fp8_w8a16_linear(x: torch.Tensor, wq8: torch.Tensor, sw: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+                     out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = X W_deq^T, W_deq = bf16(E4M3 value * channel scale), bf16 compute
+    (weight-only FP8; see include/w8mp.h). x must be bf16."""
+    _dev(x, "x"), _dev(wq8, "wq8"), _dev(sw, "sw")
+    M, K = x.shape
+    N = wq8.shape[0]
+    y = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=x.device)
+    ws = workspace if workspace is not None else _workspace(fp8_w8a16_linear_workspace_size(M, N, K), x.device)
+    _abi.check(lib().fp8_w8a16_linear(x.data_ptr(), _dt(x), M, K, wq8.data_ptr(), sw.data_ptr(), N, y.data_ptr(),
+                                      _dt(y), ws.data_ptr(), ws.numel(), _stream(x)))
+    return y
+
+
+def debug_fp8_w8a16_linear(x: torch.Tensor, wq8: torch.Tensor, sw: torch.Tensor, split: int = 0, tile: int = 0,
+                           out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+                           workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """fp8_w8a16_linear with `tile` x `tile` output blocks and `split`
+    K-slices (split 0: the linear's own choice)."""
+    _dev(x, "x"), _dev(wq8, "wq8"), _dev(sw, "sw")
+    M, K = x.shape
+    N = wq8.shape[0]
+    y = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=x.device)
+    n_ws = int(lib().w8dbg_fp8_w8a16_linear_workspace_size(M, N, K, int(split), int(tile)))
+    ws = workspace if workspace is not None else _workspace(n_ws, x.device)
+    _abi.check(lib().w8dbg_fp8_w8a16_linear(x.data_ptr(), _dt(x), M, K, wq8.data_ptr(), sw.data_ptr(), N, int(split),
+                                            int(tile), y.data_ptr(), _dt(y), ws.data_ptr(), ws.numel(), _stream(x)))
     return y
 
 

@@ -36,6 +36,8 @@ SIGNATURES = {
     "int8_mixed_linear_fused": (_int, [_p, _int, _i64, _i64, _p, _p, _p, _p, _i64, _f, _p, _int, _p, _size, _p]),
     "fp8_w8a8_linear_workspace_size": (_size, [_i64, _i64, _i64]),
     "fp8_w8a8_linear": (_int, [_p, _int, _i64, _i64, _p, _p, _i64, _p, _p, _int, _p, _size, _p]),
+    "fp8_w8a16_linear_workspace_size": (_size, [_i64, _i64, _i64]),
+    "fp8_w8a16_linear": (_int, [_p, _int, _i64, _i64, _p, _p, _i64, _p, _int, _p, _size, _p]),
     "w8_status_string": (ctypes.c_char_p, [_int]),
     "w8_last_error": (ctypes.c_char_p, []),
     "w8dbg_int8_quantize_activations_workspace_size": (_size, [_i64, _i64]),
@@ -46,6 +48,8 @@ SIGNATURES = {
     "w8dbg_fp8_quantize_activations": (_int, [_p, _int, _i64, _i64, _p, _p, _p, _p]),
     "w8dbg_fp8_gemm_workspace_size": (_size, [_i64, _i64, _i64, _int, _int]),
     "w8dbg_fp8_gemm": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _int, _int, _p, _int, _p, _size, _p]),
+    "w8dbg_fp8_w8a16_linear_workspace_size": (_size, [_i64, _i64, _i64, _int, _int]),
+    "w8dbg_fp8_w8a16_linear": (_int, [_p, _int, _i64, _i64, _p, _p, _i64, _int, _int, _p, _int, _p, _size, _p]),
     "w8_profile_start": (_int, [_int]),
     "w8_profile_stop": (_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_int)]),
 }

@@ -391,7 +391,87 @@ w8_status fp8_w8a8_linear(const void* X, int x_dt, int64_t M, int64_t K, const u
   return check_launch("fp8_w8a8_linear");
 }
 
+// FP8 weight-only: split-K counters and partials of the plan (at least one
+// aligned unit, so a workspace is always passed).
+struct W16Ws {
+  size_t cnt, part, total;
+  w8::GemmPlan plan;
+};
+
+W16Ws w16_layout(const w8::GemmPlan& plan) {
+  W16Ws w{};
+  w.plan = plan;
+  size_t off = 0;
+  w.cnt = off;  off = up(off + 4 * static_cast<size_t>(plan.counters()));
+  w.part = off; off = up(off + plan.partial_bytes());
+  w.total = std::max<size_t>(off, kAlign);
+  return w;
+}
+
+w8::GemmPlan w16_plan(int64_t M, int64_t N, int64_t K, int split, int tile) {
+  return split == 0 ? w8::plan_w8a16_gemm(M, N, K, cu_count())
+                    : w8::plan_w8a16_gemm_split(M, N, split, tile == 128 ? 128 : 256);
+}
+
+static w8_status w16_checks(const void* X, int x_dt, int64_t M, int64_t K, const uint8_t* Wq8, const float* sw,
+                            int64_t N, void* Y, int y_dt) {
+  W8_REQUIRE(X && Wq8 && sw && Y, W8_ERR_INVALID_ARGUMENT, "null pointer argument");
+  W8_REQUIRE(x_dt == W8_DT_BF16, W8_ERR_UNSUPPORTED, "X must be bf16 (the weight-only path computes in bf16)");
+  W8_REQUIRE(y_dt == W8_DT_BF16 || y_dt == W8_DT_F16 || y_dt == W8_DT_F32, W8_ERR_UNSUPPORTED,
+             "Y must be bf16, f16 or f32");
+  if (w8_status st = check_mk(M, K, 65536); st != W8_OK) return st;
+  W8_REQUIRE(K % 64 == 0, W8_ERR_UNSUPPORTED, "K must be a multiple of 64, got %lld", (long long)K);
+  W8_REQUIRE(N >= 1 && N <= kMaxDim, W8_ERR_INVALID_ARGUMENT, "N must be in [1, 2^31)");
+  W8_REQUIRE(aligned16(X) && aligned16(Wq8) && aligned16(sw) && aligned16(Y), W8_ERR_INVALID_ARGUMENT,
+             "pointers must be 16-byte aligned");
+  return W8_OK;
+}
+
+static w8_status w16_run(const void* X, int64_t M, int64_t K, const uint8_t* Wq8, const float* sw, int64_t N,
+                         void* Y, int y_dt, const W16Ws& L, void* workspace, size_t workspace_bytes, void* stream,
+                         const char* what) {
+  if (w8_status st = check_ws(workspace, workspace_bytes, L.total); st != W8_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int ydt = y_dt == W8_DT_BF16 ? 0 : (y_dt == W8_DT_F16 ? 1 : 2);
+  mark(0, s);
+  mark(1, s);
+  mark(2, s);
+  w8::launch_w8a16_gemm(static_cast<const uint16_t*>(X), Wq8, M, N, K, sw, Y, ydt, L.plan,
+                        at<float>(workspace, L.part), at<int>(workspace, L.cnt), s);
+  mark(3, s);
+  return check_launch(what);
+}
+
+size_t fp8_w8a16_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 1) return 0;
+  return w16_layout(w16_plan(M, N, K, 0, 0)).total;
+}
+
+w8_status fp8_w8a16_linear(const void* X, int x_dt, int64_t M, int64_t K, const uint8_t* Wq8, const float* sw,
+                           int64_t N, void* Y, int y_dt, void* workspace, size_t workspace_bytes, void* stream) {
+  if (w8_status st = w16_checks(X, x_dt, M, K, Wq8, sw, N, Y, y_dt); st != W8_OK) return st;
+  return w16_run(X, M, K, Wq8, sw, N, Y, y_dt, w16_layout(w16_plan(M, N, K, 0, 0)), workspace, workspace_bytes,
+                 stream, "fp8_w8a16_linear");
+}
+
 // ---- parity exports ---------------------------------------------------------
+
+size_t w8dbg_fp8_w8a16_linear_workspace_size(int64_t M, int64_t N, int64_t K, int split, int tile) {
+  if (M < 1 || N < 1 || K < 1 || split < 0) return 0;
+  return w16_layout(w16_plan(M, N, K, split, tile)).total;
+}
+
+w8_status w8dbg_fp8_w8a16_linear(const void* X, int x_dt, int64_t M, int64_t K, const uint8_t* Wq8,
+                                 const float* sw, int64_t N, int split, int tile, void* Y, int y_dt,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (w8_status st = w16_checks(X, x_dt, M, K, Wq8, sw, N, Y, y_dt); st != W8_OK) return st;
+  W8_REQUIRE(split >= 0, W8_ERR_INVALID_ARGUMENT, "split must be >= 0");
+  W8_REQUIRE(tile == 0 || tile == 128 || tile == 256, W8_ERR_INVALID_ARGUMENT, "tile must be 0, 128 or 256");
+  W8_REQUIRE(split <= K / 64, W8_ERR_UNSUPPORTED, "split %d needs at most K / 64 slices", split);
+  return w16_run(X, M, K, Wq8, sw, N, Y, y_dt, w16_layout(w16_plan(M, N, K, split, tile)), workspace,
+                 workspace_bytes, stream, "w8dbg_fp8_w8a16_linear");
+}
+
 
 size_t w8dbg_int8_quantize_activations_workspace_size(int64_t M, int64_t K) {
   if (M < 1 || K < 1) return 0;
