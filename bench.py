@@ -142,6 +142,43 @@ def w8a16_layers(torch, w8, steps: int) -> dict:
     return res
 
 
+def w4a8_layers(torch, w8, steps: int) -> dict:
+    """W4A8 (int4 per-group weights, int8 per-token activations) on the
+    512-token text-encoder shapes: whole-call, activation-pass and GEMM time
+    from the HIP-event hook, GEMM TOPS and its fraction of the roofline
+    max(2MNK / 5.0 POPS int8, bytes / 8 TB/s), bytes = M K + N K / 2 + 2 M N
+    + 4 N K / 128 (codes, packed weights, fp16 Y, group scales)."""
+    import synth
+
+    res = {}
+    for layer in synth.FP8_TEXT_LAYERS:
+        c = synth.fp8_text_encoder(layer)
+        x = _dev16(c.x_bits, torch)
+        wq, sw = w8.quantize_weight_rowwise(_dev16(c.w_bits, torch), "int4")
+        y = torch.empty((c.M, c.N), dtype=torch.float16, device="cuda")
+        ws = w8.new_workspace(w8.w4a8_linear_workspace_size(c.M, c.N, c.K))
+        for _ in range(3):
+            w8.w4a8_linear(x, wq, sw, out=y, workspace=ws)
+        w8.profile_start(steps)
+        for _ in range(steps):
+            w8.w4a8_linear(x, wq, sw, out=y, workspace=ws)
+        ms, n = w8.profile_stop()
+        gemm_us = ms[2] / n * 1e3
+        gbytes = c.M * c.K + c.N * c.K // 2 + 2 * c.M * c.N + 4 * c.N * c.K // 128
+        t_roof = max(c.ops / (PEAK_INT8_TOPS * 1e12), gbytes / (PEAK_HBM_GBS * 1e9)) * 1e6
+        key = f"{layer}_{c.M}x{c.K}x{c.N}"
+        res[key] = {
+            "call_us": round(sum(ms) / n * 1e3, 2),
+            "act_quant_us": round(ms[0] / n * 1e3, 2),
+            "gemm_us": round(gemm_us, 2),
+            "gemm_tops": round(c.ops / (gemm_us * 1e-6) / 1e12, 1),
+            "gemm_roofline_us": round(t_roof, 2),
+            "gemm_roofline_frac": round(t_roof / gemm_us, 3),
+        }
+        print(f"[bench] w4a8 {layer}: {res[key]}", file=sys.stderr, flush=True)
+    return res
+
+
 def weight_quant(torch, w8, cases, steps: int) -> dict:
     """Offline weight quantisation (int8 rowwise and FP8 per-channel) on the
     step's weights: time per call from events on the stream the kernels run on
@@ -301,7 +338,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-rows", type=int, default=4352, help="token rows per shape for the oracle baseline (4352 = the whole step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 text-encoder layer timings (W8A8 and weight-only)")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the text-encoder layer timings (FP8 W8A8, FP8 weight-only, W4A8)")
     ap.add_argument("--no-fused", action="store_true", help="skip the producer-fused DiT MLP timings")
     ap.add_argument("--counters", type=int, default=0, metavar="MIB",
                     help="counter-collection mode: a few int8 steps, then plain copies of MIB MiB; no JSON line")
@@ -419,6 +456,11 @@ def main() -> int:
             "workload": "FP8-E4M3 weight-only text-encoder linears, 512 tokens, hidden 4096: bf16 X, E4M3 weights "
                         "widened to bf16 (value x channel scale) in the GEMM, bf16 MFMA, bf16 out",
             "layers": w8a16_layers(torch, w8, args.steps),
+        }
+        out["w4a8"] = {
+            "workload": "W4A8 text-encoder linears, 512 tokens, hidden 4096: int4 weights with one fp32 scale per "
+                        "128 inputs, int8 per-token activations, int8 MFMA, fp16 out",
+            "layers": w4a8_layers(torch, w8, args.steps),
         }
     if not args.no_fused:
         out["fused_mlp"] = {

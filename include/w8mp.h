@@ -21,6 +21,9 @@
  *     inside the GEMM, with bf16 activations (the same card's weight-only
  *     loader).
  *
+ *  4. W4A8: int4 weights with one scale per group of 128 input values and
+ *     int8 per-token activations ("Qwen-Image-fni8" card, section "Format").
+ *
  * Conventions for every entry point
  *  - Layouts are row-major and dense: X [M,K], W and Wq [N,K] (the [out,in]
  *    order of a linear layer), Y [M,N]. Base pointers must be 16-byte aligned.
@@ -56,7 +59,7 @@ typedef enum {
 
 typedef enum { W8_DT_F16 = 0, W8_DT_BF16 = 1, W8_DT_F32 = 2 } w8_dtype;
 
-typedef enum { W8_Q_INT8 = 0, W8_Q_FP8_E4M3 = 1 } w8_qformat;
+typedef enum { W8_Q_INT8 = 0, W8_Q_FP8_E4M3 = 1, W8_Q_INT4_G128 = 2 } w8_qformat;
 
 /* Largest K the int8 contraction accepts: K * 127^2 < 2^31, so the int32
  * accumulator cannot overflow. */
@@ -78,8 +81,18 @@ typedef enum { W8_Q_INT8 = 0, W8_Q_FP8_E4M3 = 1 } w8_qformat;
  *                       Wq[n,k] = E4M3FN(fl32(W[n,k] / sw[n])), round to nearest
  *                       even, saturating at +-448, sign of zero kept; rows with
  *                       sw = 0 are all zero.
- *   Wq   [N,K] int8 / uint8 E4M3 codes (output, device).
- *   sw   [N] fp32 (output, device).
+ *        W8_Q_INT4_G128: int4 codes with one fp32 scale per group of 128 values
+ *                       of a row (the per-group int4 weights of the
+ *                       "Qwen-Image-fni8" card, section "Format"): for group g
+ *                       of row n, sw[g*N + n] = max |W| over the group,
+ *                       q = clamp(rne(fl32(W * fl32(7/sw))), +-7), 0 when sw = 0.
+ *                       Wq holds the codes packed two per byte, [N, K/2] uint8:
+ *                       byte b (0..3) of the 32-bit little-endian word c of a
+ *                       row holds k = 8c+b in its low nibble and k = 8c+b+4 in
+ *                       its high nibble (4-bit two's complement). Needs
+ *                       K % 128 == 0.
+ *   Wq   [N,K] int8 / uint8 E4M3 codes, or [N,K/2] packed int4 (output, device).
+ *   sw   [N] fp32, or [K/128, N] fp32 for int4 groups (output, device).
  * Requires N >= 1, 16 <= K, K % 16 == 0.
  */
 w8_status quantize_weight_rowwise(const void* W, int w_dt, int64_t N, int64_t K, int fmt,
@@ -228,6 +241,28 @@ w8_status fp8_w8a16_linear(const void* X, int x_dt, int64_t M, int64_t K,
                            void* Y, int y_dt, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/*
+ * w4a8_linear -- Y = X W^T with int4 per-group weights and int8 per-token
+ * activations ("Qwen-Image-fni8" card, section "Format"), on int8 MFMA.
+ *
+ *   X          [M,K] f16 or bf16, device.
+ *   Wq4, sw4   the W8_Q_INT4_G128 output of quantize_weight_rowwise.
+ *   Y          [M,N] bf16, f16 or f32, device.
+ *   workspace  at least w4a8_linear_workspace_size() bytes (depends on M, N,
+ *              K and the device's CU count), 256-byte aligned, zero-filled
+ *              before its first use; calls leave their split-K counters zero.
+ * Activations are coded per token like int8_mixed_linear with no outlier
+ * columns: sx[m] = max_k |X[m,k]|, q = rne(fl32(X * fl32(127/sx))). Each
+ * group's int8 x int4 products are summed exactly (int32), the group sum
+ * scaled by sw4[g*N + n] / 7 and the total by sx[m] / 127 (fp32), rounded to
+ * nearest even into Y. Results are bitwise reproducible for a given device.
+ * Requires M, N >= 1, K % 128 == 0, K <= 65536, M*K and N*K/2 below 2^32.
+ */
+size_t w4a8_linear_workspace_size(int64_t M, int64_t N, int64_t K);
+w8_status w4a8_linear(const void* X, int x_dt, int64_t M, int64_t K,
+                      const uint8_t* Wq4, const float* sw4, int64_t N,
+                      void* Y, int y_dt, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Readable name of a status; never NULL. */
 const char* w8_status_string(int status);
 /* Detail of the last failed call on this host thread ("" if none). */
@@ -295,6 +330,15 @@ w8_status w8dbg_fp8_gemm(const uint8_t* xq, const float* sx, const uint8_t* Wq8,
  * (else W8_ERR_UNSUPPORTED). Same requirements as fp8_w8a16_linear otherwise;
  * workspace: w8dbg_fp8_w8a16_linear_workspace_size(M, N, K, split, tile) bytes
  * (at least 256), zero-filled before first use (left zero). */
+/* w4a8_linear with its K range cut into `split` slices of whole groups
+ * (split = 0: the linear's own choice; 1 <= split <= K / 128, else
+ * W8_ERR_UNSUPPORTED). Workspace: w8dbg_w4a8_linear_workspace_size(M, N, K,
+ * split) bytes, zero-filled before first use (left zero). */
+size_t w8dbg_w4a8_linear_workspace_size(int64_t M, int64_t N, int64_t K, int split);
+w8_status w8dbg_w4a8_linear(const void* X, int x_dt, int64_t M, int64_t K, const uint8_t* Wq4,
+                            const float* sw4, int64_t N, int split, void* Y, int y_dt,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 size_t w8dbg_fp8_w8a16_linear_workspace_size(int64_t M, int64_t N, int64_t K, int split, int tile);
 w8_status w8dbg_fp8_w8a16_linear(const void* X, int x_dt, int64_t M, int64_t K, const uint8_t* Wq8,
                                  const float* sw, int64_t N, int split, int tile, void* Y, int y_dt,

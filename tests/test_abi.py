@@ -162,6 +162,45 @@ def test_w8a16_linear_rejects(kw, status):
     assert _w16(**kw) == status
 
 
+def _w4(**kw):
+    a = dict(X=A, x_dt=_abi.W8_DT_BF16, M=512, K=4096, Wq=A, sw=A, N=1024, Y=A, y_dt=_abi.W8_DT_F16,
+             ws=A, ws_bytes=WS_BIG, stream=None)
+    a.update(kw)
+    return _abi.lib().w4a8_linear(a["X"], a["x_dt"], a["M"], a["K"], a["Wq"], a["sw"], a["N"], a["Y"], a["y_dt"],
+                                  a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), _abi.W8_ERR_INVALID_ARGUMENT),
+    (dict(Wq=None), _abi.W8_ERR_INVALID_ARGUMENT),
+    (dict(N=0), _abi.W8_ERR_INVALID_ARGUMENT),
+    (dict(K=4160), _abi.W8_ERR_UNSUPPORTED),                     # K % 128 != 0
+    (dict(K=100), _abi.W8_ERR_INVALID_ARGUMENT),
+    (dict(x_dt=_abi.W8_DT_F32), _abi.W8_ERR_UNSUPPORTED),
+    (dict(y_dt=9), _abi.W8_ERR_UNSUPPORTED),
+    (dict(M=1 << 21, K=4096), _abi.W8_ERR_UNSUPPORTED),          # codes above 4 GiB
+    (dict(sw=A + 4), _abi.W8_ERR_INVALID_ARGUMENT),
+    (dict(ws_bytes=1024), _abi.W8_ERR_WORKSPACE),
+])
+def test_w4a8_linear_rejects(kw, status):
+    assert _w4(**kw) == status
+
+
+def test_w4a8_weight_format_and_debug_rejects():
+    lib = _abi.lib()
+    q = lib.quantize_weight_rowwise
+    assert q(A, _abi.W8_DT_BF16, 16, 192, _abi.W8_Q_INT4_G128, A, A, None) == _abi.W8_ERR_UNSUPPORTED  # K % 128
+    assert q(A, _abi.W8_DT_BF16, 16, 192, 3, A, A, None) == _abi.W8_ERR_UNSUPPORTED
+    need = lib.w4a8_linear_workspace_size(512, 1024, 4096)
+    assert need >= 512 * 4096 + 4 * 512
+    assert _w4(ws_bytes=need - 1) == _abi.W8_ERR_WORKSPACE
+    g = lib.w8dbg_w4a8_linear
+    bf, f16 = _abi.W8_DT_BF16, _abi.W8_DT_F16
+    assert g(A, bf, 4, 256, A, A, 4, -1, A, f16, A, WS_BIG, None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert g(A, bf, 4, 256, A, A, 4, 3, A, f16, A, WS_BIG, None) == _abi.W8_ERR_UNSUPPORTED          # > K/128
+    assert lib.w8dbg_w4a8_linear_workspace_size(4, 4, 256, 2) >= 2 * 128 * 128 * 4
+
+
 def test_w8a16_workspace_and_debug_rejects():
     lib = _abi.lib()
     assert lib.fp8_w8a16_linear_workspace_size(512, 4096, 4096) >= 256

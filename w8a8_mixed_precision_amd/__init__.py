@@ -15,7 +15,8 @@ _DT = {torch.float16: _abi.W8_DT_F16, torch.bfloat16: _abi.W8_DT_BF16, torch.flo
 
 __all__ = [
     "quantize_weight_rowwise", "int8_mixed_linear", "fp8_w8a8_linear", "fp8_w8a16_linear", "Producer",
-    "debug_produce", "debug_fp8_w8a16_linear", "fp8_w8a16_linear_workspace_size",
+    "debug_produce", "debug_fp8_w8a16_linear", "fp8_w8a16_linear_workspace_size", "w4a8_linear",
+    "w4a8_linear_workspace_size",
     "debug_int8_quantize_activations", "debug_int8_gemm_i32", "debug_fp8_quantize_activations", "debug_fp8_gemm",
     "int8_mixed_linear_workspace_size", "fp8_w8a8_linear_workspace_size", "new_workspace", "W8Error",
 ]
@@ -64,7 +65,9 @@ def fp8_w8a16_linear_workspace_size(M: int, N: int, K: int) -> int:
 
 
 def quantize_weight_rowwise(w: torch.Tensor, fmt: str = "int8"):
-    """W [N,K] f16/bf16 -> (Wq [N,K] int8 or uint8 E4M3 codes, sw [N] fp32)."""
+    """W [N,K] f16/bf16 -> (Wq, sw): "int8" gives int8 codes [N,K] and sw [N];
+    "fp8" E4M3 codes [N,K] (uint8) and sw [N]; "int4" packed int4 codes
+    [N,K/2] (uint8) and group scales [K/128, N] (see include/w8mp.h)."""
     _dev(w, "w")
     N, K = w.shape
     if fmt == "int8":
@@ -73,9 +76,12 @@ def quantize_weight_rowwise(w: torch.Tensor, fmt: str = "int8"):
     elif fmt == "fp8":
         wq = torch.empty((N, K), dtype=torch.uint8, device=w.device)
         f = _abi.W8_Q_FP8_E4M3
+    elif fmt == "int4":
+        wq = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+        f = _abi.W8_Q_INT4_G128
     else:
         raise ValueError(fmt)
-    sw = torch.empty((N,), dtype=torch.float32, device=w.device)
+    sw = torch.empty((K // 128, N) if fmt == "int4" else (N,), dtype=torch.float32, device=w.device)
     _abi.check(lib().quantize_weight_rowwise(w.data_ptr(), _dt(w), N, K, f, wq.data_ptr(), sw.data_ptr(),
                                              _stream(w)))
     return wq, sw
@@ -174,6 +180,32 @@ def fp8_w8a16_linear(x: torch.Tensor, wq8: torch.Tensor, sw: torch.Tensor, out_d
     ws = workspace if workspace is not None else _workspace(fp8_w8a16_linear_workspace_size(M, N, K), x.device)
     _abi.check(lib().fp8_w8a16_linear(x.data_ptr(), _dt(x), M, K, wq8.data_ptr(), sw.data_ptr(), N, y.data_ptr(),
                                       _dt(y), ws.data_ptr(), ws.numel(), _stream(x)))
+    return y
+
+
+def w4a8_linear_workspace_size(M: int, N: int, K: int) -> int:
+    return int(lib().w4a8_linear_workspace_size(M, N, K))
+
+
+def w4a8_linear(x: torch.Tensor, wq4: torch.Tensor, sw4: torch.Tensor, out_dtype: torch.dtype = torch.float16,
+                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, split: int | None = None
+                ) -> torch.Tensor:
+    """Y = X W^T with int4 per-group weights (quantize_weight_rowwise(w,
+    "int4")) and int8 per-token activations. `split`: force the number of
+    K-slices (parity export), None for the library's choice."""
+    _dev(x, "x"), _dev(wq4, "wq4"), _dev(sw4, "sw4")
+    M, K = x.shape
+    N = wq4.shape[0]
+    y = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=x.device)
+    if split is None:
+        ws = workspace if workspace is not None else _workspace(w4a8_linear_workspace_size(M, N, K), x.device)
+        _abi.check(lib().w4a8_linear(x.data_ptr(), _dt(x), M, K, wq4.data_ptr(), sw4.data_ptr(), N, y.data_ptr(),
+                                     _dt(y), ws.data_ptr(), ws.numel(), _stream(x)))
+    else:
+        n_ws = int(lib().w8dbg_w4a8_linear_workspace_size(M, N, K, int(split)))
+        ws = workspace if workspace is not None else _workspace(n_ws, x.device)
+        _abi.check(lib().w8dbg_w4a8_linear(x.data_ptr(), _dt(x), M, K, wq4.data_ptr(), sw4.data_ptr(), N,
+                                           int(split), y.data_ptr(), _dt(y), ws.data_ptr(), ws.numel(), _stream(x)))
     return y
 
 

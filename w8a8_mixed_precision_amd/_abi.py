@@ -11,7 +11,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw8mp.so"
 
 W8_OK, W8_ERR_INVALID_ARGUMENT, W8_ERR_UNSUPPORTED, W8_ERR_WORKSPACE, W8_ERR_HIP = range(5)
 W8_DT_F16, W8_DT_BF16, W8_DT_F32 = range(3)
-W8_Q_INT8, W8_Q_FP8_E4M3 = range(2)
+W8_Q_INT8, W8_Q_FP8_E4M3, W8_Q_INT4_G128 = range(3)
 W8_INT8_MAX_K = 133144
 W8_PRODUCER_NONE, W8_PRODUCER_RMSNORM, W8_PRODUCER_GELU_TANH = range(3)
 
@@ -37,6 +37,10 @@ SIGNATURES = {
     "fp8_w8a8_linear_workspace_size": (_size, [_i64, _i64, _i64]),
     "fp8_w8a8_linear": (_int, [_p, _int, _i64, _i64, _p, _p, _i64, _p, _p, _int, _p, _size, _p]),
     "fp8_w8a16_linear_workspace_size": (_size, [_i64, _i64, _i64]),
+    "w4a8_linear_workspace_size": (_size, [_i64, _i64, _i64]),
+    "w4a8_linear": (_int, [_p, _int, _i64, _i64, _p, _p, _i64, _p, _int, _p, _size, _p]),
+    "w8dbg_w4a8_linear_workspace_size": (_size, [_i64, _i64, _i64, _int]),
+    "w8dbg_w4a8_linear": (_int, [_p, _int, _i64, _i64, _p, _p, _i64, _int, _p, _int, _p, _size, _p]),
     "fp8_w8a16_linear": (_int, [_p, _int, _i64, _i64, _p, _p, _i64, _p, _int, _p, _size, _p]),
     "w8_status_string": (ctypes.c_char_p, [_int]),
     "w8_last_error": (ctypes.c_char_p, []),

@@ -255,8 +255,10 @@ w8_status quantize_weight_rowwise(const void* W, int w_dt, int64_t N, int64_t K,
                                   void* stream) {
   W8_REQUIRE(W && Wq && sw, W8_ERR_INVALID_ARGUMENT, "null pointer argument");
   W8_REQUIRE(w_dt == W8_DT_F16 || w_dt == W8_DT_BF16, W8_ERR_UNSUPPORTED, "weights must be f16 or bf16");
-  W8_REQUIRE(fmt == W8_Q_INT8 || fmt == W8_Q_FP8_E4M3, W8_ERR_UNSUPPORTED, "unknown weight format %d", fmt);
+  W8_REQUIRE(fmt == W8_Q_INT8 || fmt == W8_Q_FP8_E4M3 || fmt == W8_Q_INT4_G128, W8_ERR_UNSUPPORTED,
+             "unknown weight format %d", fmt);
   if (w8_status st = check_mk(N, K, fmt == W8_Q_INT8 ? W8_INT8_MAX_K : 65536); st != W8_OK) return st;
+  W8_REQUIRE(fmt != W8_Q_INT4_G128 || K % 128 == 0, W8_ERR_UNSUPPORTED, "int4 groups need K %% 128 == 0");
   W8_REQUIRE(aligned16(W) && aligned16(Wq) && aligned16(sw), W8_ERR_INVALID_ARGUMENT,
              "pointers must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -264,6 +266,8 @@ w8_status quantize_weight_rowwise(const void* W, int w_dt, int64_t N, int64_t K,
   if (fmt == W8_Q_INT8)
     w8::launch_int8_rows(W, bf, N, (int)K, 0x7F80u, static_cast<int8_t*>(Wq), sw, nullptr, w8::kProdNone,
                          w8::ProdArgs{}, s);
+  else if (fmt == W8_Q_INT4_G128)
+    w8::launch_int4_weights(W, bf, N, (int)K, static_cast<uint8_t*>(Wq), sw, s);
   else
     w8::launch_fp8_rows(W, bf, N, (int)K, nullptr, static_cast<uint8_t*>(Wq), sw, 2, s);
   return check_launch("quantize_weight_rowwise");
@@ -454,7 +458,89 @@ w8_status fp8_w8a16_linear(const void* X, int x_dt, int64_t M, int64_t K, const 
                  stream, "fp8_w8a16_linear");
 }
 
+// W4A8: activation codes and row scales, split-K counters and partials.
+struct W4Ws {
+  size_t q, sx, cnt, part, total;
+  w8::GemmPlan plan;
+};
+
+W4Ws w4_layout(int64_t M, int64_t N, int64_t K, int split) {
+  W4Ws w{};
+  w.plan = split == 0 ? w8::plan_w4a8_gemm(M, N, K, cu_count()) : w8::plan_w4a8_gemm_split(M, N, split);
+  size_t off = 0;
+  w.q = off;    off = up(off + static_cast<size_t>(M) * K);
+  w.sx = off;   off = up(off + 4 * static_cast<size_t>(M));
+  w.cnt = off;  off = up(off + 4 * static_cast<size_t>(w.plan.counters()));
+  w.part = off; off = up(off + w.plan.partial_bytes());
+  w.total = off;
+  return w;
+}
+
+static w8_status w4_checks(const void* X, int x_dt, int64_t M, int64_t K, const uint8_t* Wq4, const float* sw4,
+                           int64_t N, void* Y, int y_dt) {
+  W8_REQUIRE(X && Wq4 && sw4 && Y, W8_ERR_INVALID_ARGUMENT, "null pointer argument");
+  W8_REQUIRE(x_dt == W8_DT_F16 || x_dt == W8_DT_BF16, W8_ERR_UNSUPPORTED, "X must be f16 or bf16");
+  W8_REQUIRE(y_dt == W8_DT_BF16 || y_dt == W8_DT_F16 || y_dt == W8_DT_F32, W8_ERR_UNSUPPORTED,
+             "Y must be bf16, f16 or f32");
+  if (w8_status st = check_mk(M, K, 65536); st != W8_OK) return st;
+  W8_REQUIRE(K % 128 == 0, W8_ERR_UNSUPPORTED, "K must be a multiple of 128 (the int4 group), got %lld",
+             (long long)K);
+  W8_REQUIRE(N >= 1 && N <= kMaxDim, W8_ERR_INVALID_ARGUMENT, "N must be in [1, 2^31)");
+  W8_REQUIRE(M * K < (int64_t(1) << 32) && N * (K / 2) < (int64_t(1) << 32), W8_ERR_UNSUPPORTED,
+             "X codes and packed weights must each be smaller than 4 GiB");
+  W8_REQUIRE(aligned16(X) && aligned16(Wq4) && aligned16(sw4) && aligned16(Y), W8_ERR_INVALID_ARGUMENT,
+             "pointers must be 16-byte aligned");
+  return W8_OK;
+}
+
+static w8_status w4_run(const void* X, int x_dt, int64_t M, int64_t K, const uint8_t* Wq4, const float* sw4,
+                        int64_t N, void* Y, int y_dt, const W4Ws& L, void* workspace, size_t workspace_bytes,
+                        void* stream, const char* what) {
+  if (w8_status st = check_ws(workspace, workspace_bytes, L.total); st != W8_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int8_t* q = at<int8_t>(workspace, L.q);
+  float* sx = at<float>(workspace, L.sx);
+  mark(0, s);
+  // per-token absmax int8 codes: the int8 row pass with no outlier columns
+  w8::launch_int8_rows(X, x_dt == W8_DT_BF16, M, (int)K, 0x7F80u, q, sx, nullptr, w8::kProdNone, w8::ProdArgs{}, s);
+  mark(1, s);
+  mark(2, s);
+  const int ydt = y_dt == W8_DT_BF16 ? 0 : (y_dt == W8_DT_F16 ? 1 : 2);
+  w8::launch_w4a8_gemm(q, Wq4, M, N, K, sx, sw4, Y, ydt, L.plan, at<float>(workspace, L.part),
+                       at<int>(workspace, L.cnt), s);
+  mark(3, s);
+  return check_launch(what);
+}
+
+size_t w4a8_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 1) return 0;
+  return w4_layout(M, N, K, 0).total;
+}
+
+w8_status w4a8_linear(const void* X, int x_dt, int64_t M, int64_t K, const uint8_t* Wq4, const float* sw4, int64_t N,
+                      void* Y, int y_dt, void* workspace, size_t workspace_bytes, void* stream) {
+  if (w8_status st = w4_checks(X, x_dt, M, K, Wq4, sw4, N, Y, y_dt); st != W8_OK) return st;
+  return w4_run(X, x_dt, M, K, Wq4, sw4, N, Y, y_dt, w4_layout(M, N, K, 0), workspace, workspace_bytes, stream,
+                "w4a8_linear");
+}
+
 // ---- parity exports ---------------------------------------------------------
+
+size_t w8dbg_w4a8_linear_workspace_size(int64_t M, int64_t N, int64_t K, int split) {
+  if (M < 1 || N < 1 || K < 1 || split < 0) return 0;
+  return w4_layout(M, N, K, split).total;
+}
+
+w8_status w8dbg_w4a8_linear(const void* X, int x_dt, int64_t M, int64_t K, const uint8_t* Wq4, const float* sw4,
+                            int64_t N, int split, void* Y, int y_dt, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (w8_status st = w4_checks(X, x_dt, M, K, Wq4, sw4, N, Y, y_dt); st != W8_OK) return st;
+  W8_REQUIRE(split >= 0, W8_ERR_INVALID_ARGUMENT, "split must be >= 0");
+  W8_REQUIRE(split <= K / 128, W8_ERR_UNSUPPORTED, "split %d needs at most K / 128 slices", split);
+  return w4_run(X, x_dt, M, K, Wq4, sw4, N, Y, y_dt, w4_layout(M, N, K, split), workspace, workspace_bytes, stream,
+                "w8dbg_w4a8_linear");
+}
+
 
 size_t w8dbg_fp8_w8a16_linear_workspace_size(int64_t M, int64_t N, int64_t K, int split, int tile) {
   if (M < 1 || N < 1 || K < 1 || split < 0) return 0;

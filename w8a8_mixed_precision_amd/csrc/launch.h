@@ -13,7 +13,7 @@ namespace w8 {
 // sk_tiles tiles cut into `split` K-slices each (split == 1: none). The int8
 // GEMM uses bm = 256, and with `small` runs each of the sk_tiles leftover
 // tiles as four 128x128 blocks (each cut into `split` slices); the FP8 GEMM
-// and the FP8 weight-only GEMMs use bm = 256 or 128.
+// and the FP8 weight-only GEMMs use bm = 256 or 128, the W4A8 GEMM 128.
 struct GemmPlan {
   int tiles_m, tiles_n, dp_tiles, split, sk_tiles;
   int bm = 256;
@@ -50,6 +50,14 @@ GemmPlan plan_fp8_gemm(int64_t M, int64_t N, int64_t K, int cus);
 GemmPlan plan_fp8_gemm_split(int64_t M, int64_t N, int split, int bm);
 void launch_fp8_gemm(const uint8_t* A, const uint8_t* B, int64_t M, int64_t N, int64_t K, const float* sx,
                      const float* sw, void* Y, int ydt, const GemmPlan& plan, float* part, int* cnt, hipStream_t s);
+// W4A8: int4 weight codes packed two per byte with one fp32 scale per group of
+// kW4Group values of K (group-major scales sw[g, n]).
+constexpr int kW4Group = 128;
+void launch_int4_weights(const void* W, bool bf16, int64_t N, int K, uint8_t* packed, float* sw, hipStream_t s);
+GemmPlan plan_w4a8_gemm(int64_t M, int64_t N, int64_t K, int cus);
+GemmPlan plan_w4a8_gemm_split(int64_t M, int64_t N, int split);
+void launch_w4a8_gemm(const int8_t* A, const uint8_t* B, int64_t M, int64_t N, int64_t K, const float* sx,
+                      const float* sw, void* Y, int ydt, const GemmPlan& plan, float* part, int* cnt, hipStream_t s);
 GemmPlan plan_w8a16_gemm(int64_t M, int64_t N, int64_t K, int cus);
 GemmPlan plan_w8a16_gemm_split(int64_t M, int64_t N, int split, int bm);
 void launch_w8a16_gemm(const uint16_t* A, const uint8_t* B, int64_t M, int64_t N, int64_t K, const float* sw,
