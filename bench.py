@@ -179,6 +179,50 @@ def w4a8_layers(torch, w8, steps: int) -> dict:
     return res
 
 
+def dit_block(torch, w8, steps: int) -> dict:
+    """One DiT 1024^2 block through the library's driver (M = 4352 tokens,
+    D = 4096, F = 16384: QKV, attention stub, output projection, residual, MLP
+    up after RMSNorm, GELU, MLP down, residual), with the MLP down-projection
+    int8 or kept in fp16 as a massive-activation writer. Time per block from
+    events on the launch stream, and the block's linears' ops per second."""
+    g = torch.Generator(device="cuda").manual_seed(11)
+    M, D, F = 4352, 4096, 16384
+    x = torch.randn(M, D, device="cuda", generator=g)
+    x[4096::32, 2276] = 9000.0
+    x = x.to(torch.float16)
+
+    def lin(n, k):
+        w = (torch.randn(n, k, device="cuda", generator=g) * 0.02).to(torch.float16)
+        b = torch.randn(n, device="cuda", generator=g) * 0.1
+        wq, sw = w8.quantize_weight_rowwise(w, "int8")
+        return wq, sw, b, w
+
+    qkv, o_, up, down = lin(3 * D, D), lin(D, D), lin(F, D), lin(D, F)
+    norm = lambda: w8.Producer("rmsnorm", torch.rand(D, device="cuda", generator=g) * 0.4 + 0.8)
+    ops = 2.0 * M * D * (3 * D + D + F) + 2.0 * M * F * D
+    res = {}
+    for name, with16 in (("int8_down", False), ("fp16_down", True)):
+        blk = w8.DitBlock(D, F, qkv[0], qkv[1], o_[0], o_[1], up[0], up[1],
+                          w_down=None if with16 else down[0], s_down=None if with16 else down[1],
+                          b_qkv=qkv[2], b_o=o_[2], b_up=up[2], b_down=down[2], norm1=norm(), norm2=norm(),
+                          w_down16=down[3] if with16 else None)
+        y = torch.empty_like(x)
+        ws = w8.new_workspace(blk.workspace_size(M))
+        for _ in range(2):
+            blk.forward(x, out=y, workspace=ws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            blk.forward(x, out=y, workspace=ws)
+        e1.record()
+        e1.synchronize()
+        us = e0.elapsed_time(e1) / steps * 1e3
+        res[name] = {"us_per_block": round(us, 1), "linear_tops": round(ops / (us * 1e-6) / 1e12, 1)}
+        print(f"[bench] dit block {name}: {res[name]}", file=sys.stderr, flush=True)
+        del ws, blk
+    return res
+
+
 def weight_quant(torch, w8, cases, steps: int) -> dict:
     """Offline weight quantisation (int8 rowwise and FP8 per-channel) on the
     step's weights: time per call from events on the stream the kernels run on
@@ -340,6 +384,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the text-encoder layer timings (FP8 W8A8, FP8 weight-only, W4A8)")
     ap.add_argument("--no-fused", action="store_true", help="skip the producer-fused DiT MLP timings")
+    ap.add_argument("--no-block", action="store_true", help="skip the DiT block driver timings")
     ap.add_argument("--counters", type=int, default=0, metavar="MIB",
                     help="counter-collection mode: a few int8 steps, then plain copies of MIB MiB; no JSON line")
     args = ap.parse_args()
@@ -467,6 +512,13 @@ def main() -> int:
             "workload": "DiT 1024^2 MLP with producers: up = RMSNorm+modulation(H [4352,4096]) x W [16384,4096], "
                         "down = GELU(H [4352,16384]) x W [4096,16384]; bias, threshold 6.0, bf16 in, fp16 out",
             "layers": fused_mlp(torch, w8, args.steps),
+        }
+    if not args.no_block:
+        out["dit_block"] = {
+            "workload": "DiT 1024^2 block through the driver: X fp16 [4352,4096], QKV [12288,4096], O [4096,4096], "
+                        "up [16384,4096], down [4096,16384] int8 (LLM.int8, t = 6.0) or fp16 (exclusion policy); "
+                        "RMSNorm and GELU producers, biases, residuals, attention stub",
+            "modes": dit_block(torch, w8, max(1, args.steps // 2)),
         }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

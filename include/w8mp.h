@@ -24,6 +24,9 @@
  *  4. W4A8: int4 weights with one scale per group of 128 input values and
  *     int8 per-token activations ("Qwen-Image-fni8" card, section "Format").
  *
+ * and a block driver that chains one DiT block's int8 linears with the fp16
+ * exclusion policy for massive-activation writers.
+ *
  * Conventions for every entry point
  *  - Layouts are row-major and dense: X [M,K], W and Wq [N,K] (the [out,in]
  *    order of a linear layer), Y [M,N]. Base pointers must be 16-byte aligned.
@@ -263,6 +266,52 @@ w8_status w4a8_linear(const void* X, int x_dt, int64_t M, int64_t K,
                       const uint8_t* Wq4, const float* sw4, int64_t N,
                       void* Y, int y_dt, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * w8_dit_block_forward -- one DiT block's quantized linears, chained on
+ * `stream` (a driver over the calls above; fp16 activations throughout):
+ *
+ *   qkv = LLM.int8 linear of RMSNorm1(X), + b_qkv          [M, 3D]
+ *   a   = qkv[:, 2D:3D]                                     attention stub
+ *   o   = LLM.int8 linear of a, + b_o                       [M, D]
+ *   h   = X + o
+ *   u   = LLM.int8 linear of RMSNorm2(h), + b_up            [M, F]
+ *   d   = LLM.int8 linear of GELU(u), + b_down              [M, D]
+ *   Y   = h + d
+ *
+ * The "Image21-INT8" card ("Quantization") quantizes the block's linears with
+ * LLM.int8; the "Image21-Turbo-OrbitQuant-W4A4" card ("What 4-bit breaks here
+ * and what stays in fp16") keeps the MLP output projections that write the
+ * near-9000 text-token values in fp16. That is the exclusion policy here:
+ * with w_down16 set, d = GELU(u) w_down16^T + b_down is computed in fp16 (fp32
+ * sums) from unquantized weights. Attention is outside the quantized path;
+ * the stub passes each token's value vector through (as if each token
+ * attended only to itself). Every linear's output and each residual sum is
+ * rounded once to fp16 (round to nearest even).
+ *
+ * Weights are the W8_Q_INT8 output of quantize_weight_rowwise; biases are
+ * fp32 [N] or NULL; norm1 / norm2 are RMSNorm producers (kind
+ * W8_PRODUCER_RMSNORM, or W8_PRODUCER_NONE to skip the norm). Requires
+ * M >= 1, D and F multiples of 64 in [64, 16384], 16-byte aligned X, Y,
+ * w_down16 and b_down. The workspace (w8_dit_block_workspace_size bytes,
+ * 256-byte aligned, zero-filled before its first use, left reusable) holds
+ * the intermediates and one workspace per linear.
+ */
+typedef struct w8_dit_block {
+  int64_t D;                   /* model width: X, Y [M, D] fp16 */
+  int64_t F;                   /* MLP hidden size */
+  float threshold;             /* LLM.int8 outlier threshold (6.0 on the card) */
+  const int8_t* w_qkv;   const float* s_qkv;  const float* b_qkv;    /* [3D, D], [3D], [3D] */
+  const int8_t* w_o;     const float* s_o;    const float* b_o;      /* [D, D], [D], [D] */
+  const int8_t* w_up;    const float* s_up;   const float* b_up;     /* [F, D], [F], [F] */
+  const int8_t* w_down;  const float* s_down; const float* b_down;   /* [D, F], [D], [D] */
+  const uint16_t* w_down16;    /* [D, F] fp16: the excluded writer, or NULL */
+  w8_producer norm1, norm2;
+} w8_dit_block;
+
+size_t w8_dit_block_workspace_size(int64_t M, int64_t D, int64_t F);
+w8_status w8_dit_block_forward(const w8_dit_block* blk, const void* X, int64_t M, void* Y,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Readable name of a status; never NULL. */
 const char* w8_status_string(int status);
 /* Detail of the last failed call on this host thread ("" if none). */
@@ -334,6 +383,16 @@ w8_status w8dbg_fp8_gemm(const uint8_t* xq, const float* sx, const uint8_t* Wq8,
  * (split = 0: the linear's own choice; 1 <= split <= K / 128, else
  * W8_ERR_UNSUPPORTED). Workspace: w8dbg_w4a8_linear_workspace_size(M, N, K,
  * split) bytes, zero-filled before first use (left zero). */
+/* The plain 16-bit linear of the block driver's exclusion policy:
+ * Y [M,N] = X [M,K] . W [N,K]^T, X and W both f16 or both bf16 (x_dt), fp32
+ * accumulation on 16-bit MFMA, rounded into Y (bf16/f16/f32). K % 64 == 0,
+ * K <= 65536. split = 0: the driver's own K-slicing; else `split` slices of
+ * 128x128 blocks (<= K / 64). Workspace: w8dbg_linear16_workspace_size bytes
+ * (at least 256), zero-filled before first use (left zero). */
+size_t w8dbg_linear16_workspace_size(int64_t M, int64_t N, int64_t K, int split);
+w8_status w8dbg_linear16(const void* X, int x_dt, int64_t M, int64_t K, const void* W, int64_t N, int split,
+                         void* Y, int y_dt, void* workspace, size_t workspace_bytes, void* stream);
+
 size_t w8dbg_w4a8_linear_workspace_size(int64_t M, int64_t N, int64_t K, int split);
 w8_status w8dbg_w4a8_linear(const void* X, int x_dt, int64_t M, int64_t K, const uint8_t* Wq4,
                             const float* sw4, int64_t N, int split, void* Y, int y_dt,

@@ -201,6 +201,32 @@ def test_w4a8_weight_format_and_debug_rejects():
     assert lib.w8dbg_w4a8_linear_workspace_size(4, 4, 256, 2) >= 2 * 128 * 128 * 4
 
 
+def test_dit_block_and_linear16_reject():
+    lib = _abi.lib()
+    blk = _abi.DitBlock(256, 1024, 6.0, *([A] * 12), None, _abi.Producer(), _abi.Producer())
+    fwd = lambda b, X=A, M=64, Y=A, ws=A, n=WS_BIG: lib.w8_dit_block_forward(
+        ctypes.byref(b) if b is not None else None, X, M, Y, ws, n, None)
+    assert fwd(None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert fwd(blk, X=None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert fwd(blk, M=0) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert fwd(blk, Y=A + 2) == _abi.W8_ERR_INVALID_ARGUMENT
+    need = lib.w8_dit_block_workspace_size(64, 256, 1024)
+    assert need > 64 * 256 * 2 * 8
+    assert fwd(blk, n=need - 1) == _abi.W8_ERR_WORKSPACE
+    bad = _abi.DitBlock(200, 1024, 6.0, *([A] * 12), None, _abi.Producer(), _abi.Producer())
+    assert fwd(bad) == _abi.W8_ERR_INVALID_ARGUMENT                    # D % 64 != 0
+    nodown = _abi.DitBlock(256, 1024, 6.0, *([A] * 9), None, None, A, None, _abi.Producer(), _abi.Producer())
+    assert fwd(nodown) == _abi.W8_ERR_INVALID_ARGUMENT                 # neither int8 nor fp16 down weights
+    assert "down projection" in _abi.lib().w8_last_error().decode()
+    f16, f32 = _abi.W8_DT_F16, _abi.W8_DT_F32
+    l16 = lib.w8dbg_linear16
+    assert l16(A, f16, 4, 96, A, 4, 0, A, f32, A, WS_BIG, None) == _abi.W8_ERR_UNSUPPORTED        # K % 64
+    assert l16(A, f32, 4, 128, A, 4, 0, A, f32, A, WS_BIG, None) == _abi.W8_ERR_UNSUPPORTED       # X type
+    assert l16(A, f16, 4, 128, A, 4, 3, A, f32, A, WS_BIG, None) == _abi.W8_ERR_UNSUPPORTED       # split > K/64
+    assert l16(None, f16, 4, 128, A, 4, 0, A, f32, A, WS_BIG, None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert l16(A, f16, 4, 128, A, 4, 2, A, f32, A, 256, None) == _abi.W8_ERR_WORKSPACE
+
+
 def test_w8a16_workspace_and_debug_rejects():
     lib = _abi.lib()
     assert lib.fp8_w8a16_linear_workspace_size(512, 4096, 4096) >= 256

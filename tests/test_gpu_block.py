@@ -1,0 +1,121 @@
+"""GPU parity of the block driver (w8_dit_block_forward) and its plain 16-bit
+linear against the CPU oracle (oracle/block.py).
+
+The 16-bit linear: relative Frobenius error <= 1e-5 for fp32 output (fp32
+sums against float64) and <= 1e-2 for 16-bit output. The block: Y within
+1e-2 relative Frobenius, globally and per row (each of the chained linears
+meets 1e-2 on its own output, and Y is dominated by the residual stream);
+at full DiT size, where the oracle's chain is out of reach, Y is checked to be
+finite and not constant (the "Qwen-Image-fni8" card's sanity test).
+"""
+import numpy as np
+import pytest
+import torch
+
+import w8a8_mixed_precision_amd as w8
+from oracle import block as B
+from oracle import w8ref as o
+from tests.gpu_util import OUT, announce, dev16, host_stored, rel_fro, row_rel_fro
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("M,K,N,dtype,split", [(300, 1024, 520, "f16", 0), (300, 1024, 520, "bf16", 2),
+                                               (64, 256, 96, "f16", 4), (1, 64, 1, "bf16", 1),
+                                               (257, 4096, 129, "f16", 8)])
+@pytest.mark.parametrize("out_dtype", ["f32", "f16"])
+def test_linear16_matches_oracle(M, K, N, dtype, split, out_dtype):
+    rng = np.random.default_rng(M + K + N)
+    enc = o.round_to_f16 if dtype == "f16" else o.round_to_bf16
+    x_bits, w_bits = enc(rng.standard_normal((M, K))), enc(rng.standard_normal((N, K)) * 0.05)
+    ref = B.linear16(x_bits, dtype, w_bits, dtype, out_dtype)
+    announce("linear16", M, K, N, dtype, split, out_dtype)
+    y = w8.debug_linear16(dev16(x_bits, dtype), dev16(w_bits, dtype), split, OUT[out_dtype])
+    torch.cuda.synchronize()
+    got = o.stored_to_f64(host_stored(y, out_dtype), out_dtype)
+    e, er = rel_fro(got, ref["y"]), row_rel_fro(got, ref["y"]).max()
+    tol = 1e-5 if out_dtype == "f32" else 1e-2
+    assert e <= tol and er <= tol, (e, er)
+
+
+def _block(rng, D, F, with16, massive_rows=()):
+    blk, dev = {}, {}
+    for name, (n, k) in {"qkv": (3 * D, D), "o": (D, D), "up": (F, D), "down": (D, F)}.items():
+        w = rng.standard_normal((n, k)).astype(np.float32) * 0.02
+        w_bits = o.round_to_f16(w)
+        wq, sw = o.quantize_weight_int8(o.decode16(w_bits, "f16"))
+        b = (rng.standard_normal(n) * 0.1).astype(np.float32)
+        blk[f"wq_{name}"], blk[f"sw_{name}"], blk[f"b_{name}"] = wq, sw, b
+        dev[name] = (torch.from_numpy(wq).cuda(), torch.from_numpy(sw).cuda(), torch.from_numpy(b).cuda())
+    norms = []
+    for _ in range(2):
+        g = rng.uniform(0.8, 1.2, D).astype(np.float32)
+        sc = rng.uniform(-0.2, 0.2, D).astype(np.float32)
+        sh = rng.uniform(-0.2, 0.2, D).astype(np.float32)
+        norms.append((dict(gamma=g, scale=sc, shift=sh, eps=1e-6),
+                      w8.Producer("rmsnorm", torch.from_numpy(g).cuda(), torch.from_numpy(sc).cuda(),
+                                  torch.from_numpy(sh).cuda(), 1e-6)))
+    blk["norm1"], blk["norm2"] = norms[0][0], norms[1][0]
+    w16 = o.round_to_f16(rng.standard_normal((D, F)) * 0.02) if with16 else None
+    blk["w16_down"] = w16
+    gpu = w8.DitBlock(D, F, *dev["qkv"][:2], *dev["o"][:2], *dev["up"][:2],
+                      w_down=None if with16 else dev["down"][0], s_down=None if with16 else dev["down"][1],
+                      b_qkv=dev["qkv"][2], b_o=dev["o"][2], b_up=dev["up"][2], b_down=dev["down"][2],
+                      norm1=norms[0][1], norm2=norms[1][1],
+                      w_down16=dev16(w16, "f16") if with16 else None)
+    return blk, gpu
+
+
+@pytest.mark.parametrize("with16", [False, True], ids=["int8_down", "fp16_down"])
+@pytest.mark.parametrize("M", [300, 64])
+def test_block_matches_oracle(with16, M):
+    rng = np.random.default_rng(90 + M + with16)
+    D, F = 256, 1024
+    x = rng.standard_normal((M, D))
+    x[M - 8:, 37] = rng.uniform(8500, 9500, 8)     # massive activations in a few text rows
+    x[:, 101] *= 20.0                              # an outlier channel
+    x_bits = o.round_to_f16(x)
+    blk, gpu = _block(rng, D, F, with16)
+    ref = B.dit_block(x_bits, blk)
+    announce("block", M, D, F, with16)
+    y = gpu.forward(dev16(x_bits, "f16"))
+    torch.cuda.synchronize()
+    got = o.stored_to_f64(host_stored(y, "f16"), "f16")
+    want = o.stored_to_f64(ref["Y"], "f16")
+    e, er = rel_fro(got, want), row_rel_fro(got, want).max()
+    assert e <= 1e-2 and er <= 1e-2, (e, er)
+    # the workspace is reused without clearing: a second call repeats bit for bit
+    ws = w8.new_workspace(gpu.workspace_size(M))
+    y1 = gpu.forward(dev16(x_bits, "f16"), workspace=ws)
+    y2 = gpu.forward(dev16(x_bits, "f16"), workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(y1, y)
+
+
+@pytest.mark.parametrize("with16", [False, True], ids=["int8_down", "fp16_down"])
+def test_block_full_size_is_finite_and_not_constant(with16):
+    """The DiT 1024^2 block (M = 4352, D = 4096, F = 16384) with random
+    weights and the massive text-token activations of the MLP workload."""
+    g = torch.Generator(device="cuda").manual_seed(7)
+    M, D, F = 4352, 4096, 16384
+    x = torch.randn(M, D, device="cuda", generator=g)
+    x[4096::32, 2276] = 9000.0
+    x = x.to(torch.float16)
+
+    def lin(n, k):
+        w = (torch.randn(n, k, device="cuda", generator=g) * 0.02).to(torch.float16)
+        wq, sw = w8.quantize_weight_rowwise(w, "int8")
+        return wq, sw, w
+
+    qkv, o_, up, down = lin(3 * D, D), lin(D, D), lin(F, D), lin(D, F)
+    blk = w8.DitBlock(D, F, qkv[0], qkv[1], o_[0], o_[1], up[0], up[1],
+                      w_down=None if with16 else down[0], s_down=None if with16 else down[1],
+                      norm1=w8.Producer("rmsnorm"), norm2=w8.Producer("rmsnorm"),
+                      w_down16=down[2] if with16 else None)
+    announce("block full size", with16)
+    y = blk.forward(x)
+    torch.cuda.synchronize()
+    yf = y.float()
+    assert torch.isfinite(yf).all() and float(yf.std()) > 0
+    # the massive channel survives the block (residual stream)
+    assert float(yf[4096, 2276]) > 4000

@@ -16,7 +16,7 @@ _DT = {torch.float16: _abi.W8_DT_F16, torch.bfloat16: _abi.W8_DT_BF16, torch.flo
 __all__ = [
     "quantize_weight_rowwise", "int8_mixed_linear", "fp8_w8a8_linear", "fp8_w8a16_linear", "Producer",
     "debug_produce", "debug_fp8_w8a16_linear", "fp8_w8a16_linear_workspace_size", "w4a8_linear",
-    "w4a8_linear_workspace_size",
+    "w4a8_linear_workspace_size", "DitBlock", "debug_linear16",
     "debug_int8_quantize_activations", "debug_int8_gemm_i32", "debug_fp8_quantize_activations", "debug_fp8_gemm",
     "int8_mixed_linear_workspace_size", "fp8_w8a8_linear_workspace_size", "new_workspace", "W8Error",
 ]
@@ -206,6 +206,71 @@ def w4a8_linear(x: torch.Tensor, wq4: torch.Tensor, sw4: torch.Tensor, out_dtype
         ws = workspace if workspace is not None else _workspace(n_ws, x.device)
         _abi.check(lib().w8dbg_w4a8_linear(x.data_ptr(), _dt(x), M, K, wq4.data_ptr(), sw4.data_ptr(), N,
                                            int(split), y.data_ptr(), _dt(y), ws.data_ptr(), ws.numel(), _stream(x)))
+    return y
+
+
+class DitBlock:
+    """One DiT block's quantized linears chained by the library's driver
+    (w8_dit_block_forward in include/w8mp.h): QKV after RMSNorm1, an attention
+    stub (each token's value vector), the output projection, residual, MLP up
+    after RMSNorm2, GELU, MLP down (int8, or fp16 with `w_down16` for a
+    massive-activation writer), residual. fp16 activations; int8 weights and
+    scales from quantize_weight_rowwise; biases fp32 or None; norms are
+    Producer("rmsnorm", ...) or None."""
+
+    def __init__(self, D: int, F: int, w_qkv, s_qkv, w_o, s_o, w_up, s_up, w_down=None, s_down=None, b_qkv=None,
+                 b_o=None, b_up=None, b_down=None, norm1: Producer | None = None, norm2: Producer | None = None,
+                 w_down16: torch.Tensor | None = None, threshold: float = 6.0):
+        self.D, self.F = int(D), int(F)
+        self.t = dict(qkv=(w_qkv, s_qkv, b_qkv), o=(w_o, s_o, b_o), up=(w_up, s_up, b_up), down=(w_down, s_down, b_down))
+        for name, trio in self.t.items():
+            for v in trio:
+                if v is not None:
+                    _dev(v, name)
+        if w_down16 is not None:
+            _dev(w_down16, "w_down16")
+            if w_down16.dtype != torch.float16 or tuple(w_down16.shape) != (self.D, self.F):
+                raise ValueError("w_down16 must be fp16 [D, F]")
+        self.w_down16 = w_down16
+        self.norm1, self.norm2, self.threshold = norm1, norm2, float(threshold)
+        ptr = lambda v: v.data_ptr() if v is not None else None
+        none = Producer("none")
+        self._s = _abi.DitBlock(self.D, self.F, self.threshold,
+                                *[ptr(v) for n in ("qkv", "o", "up", "down") for v in self.t[n]],
+                                ptr(w_down16), (norm1 or none).struct(self.D), (norm2 or none).struct(self.D))
+
+    def workspace_size(self, M: int) -> int:
+        return int(lib().w8_dit_block_workspace_size(M, self.D, self.F))
+
+    def forward(self, x: torch.Tensor, out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None) -> torch.Tensor:
+        import ctypes
+
+        _dev(x, "x")
+        if x.dtype != torch.float16 or x.dim() != 2 or x.shape[1] != self.D:
+            raise ValueError("x must be fp16 [M, D]")
+        M = x.shape[0]
+        y = out if out is not None else torch.empty_like(x)
+        ws = workspace if workspace is not None else _workspace(self.workspace_size(M), x.device)
+        _abi.check(lib().w8_dit_block_forward(ctypes.byref(self._s), x.data_ptr(), M, y.data_ptr(), ws.data_ptr(),
+                                              ws.numel(), _stream(x)))
+        return y
+
+
+def debug_linear16(x: torch.Tensor, w: torch.Tensor, split: int = 0, out_dtype: torch.dtype = torch.float32,
+                   workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """The block driver's plain 16-bit linear: Y = X W^T (x and w both fp16
+    or both bf16), `split` K-slices of 128x128 blocks (0: the driver's own)."""
+    _dev(x, "x"), _dev(w, "w")
+    M, K = x.shape
+    N = w.shape[0]
+    if w.dtype != x.dtype or w.shape[1] != K:
+        raise ValueError("w must be [N, K] of x's dtype")
+    y = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    n_ws = int(lib().w8dbg_linear16_workspace_size(M, N, K, int(split)))
+    ws = workspace if workspace is not None else _workspace(n_ws, x.device)
+    _abi.check(lib().w8dbg_linear16(x.data_ptr(), _dt(x), M, K, w.data_ptr(), N, int(split), y.data_ptr(), _dt(y),
+                                    ws.data_ptr(), ws.numel(), _stream(x)))
     return y
 
 

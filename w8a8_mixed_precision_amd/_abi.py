@@ -28,6 +28,13 @@ class Producer(ctypes.Structure):
                 ("shift", ctypes.c_void_p), ("eps", ctypes.c_float)]
 
 
+class DitBlock(ctypes.Structure):
+    """struct w8_dit_block of include/w8mp.h."""
+    _fields_ = [("D", ctypes.c_int64), ("F", ctypes.c_int64), ("threshold", ctypes.c_float)] + [
+        (f"{k}_{n}", ctypes.c_void_p) for n in ("qkv", "o", "up", "down") for k in ("w", "s", "b")] + [
+        ("w_down16", ctypes.c_void_p), ("norm1", Producer), ("norm2", Producer)]
+
+
 # name -> (restype, argtypes)
 SIGNATURES = {
     "quantize_weight_rowwise": (_int, [_p, _int, _i64, _i64, _int, _p, _p, _p]),
@@ -38,6 +45,10 @@ SIGNATURES = {
     "fp8_w8a8_linear": (_int, [_p, _int, _i64, _i64, _p, _p, _i64, _p, _p, _int, _p, _size, _p]),
     "fp8_w8a16_linear_workspace_size": (_size, [_i64, _i64, _i64]),
     "w4a8_linear_workspace_size": (_size, [_i64, _i64, _i64]),
+    "w8_dit_block_workspace_size": (_size, [_i64, _i64, _i64]),
+    "w8_dit_block_forward": (_int, [_p, _p, _i64, _p, _p, _size, _p]),
+    "w8dbg_linear16_workspace_size": (_size, [_i64, _i64, _i64, _int]),
+    "w8dbg_linear16": (_int, [_p, _int, _i64, _i64, _p, _i64, _int, _p, _int, _p, _size, _p]),
     "w4a8_linear": (_int, [_p, _int, _i64, _i64, _p, _p, _i64, _p, _int, _p, _size, _p]),
     "w8dbg_w4a8_linear_workspace_size": (_size, [_i64, _i64, _i64, _int]),
     "w8dbg_w4a8_linear": (_int, [_p, _int, _i64, _i64, _p, _p, _i64, _int, _p, _int, _p, _size, _p]),

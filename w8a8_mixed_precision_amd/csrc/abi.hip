@@ -75,6 +75,19 @@ int cu_count() {
   return n;
 }
 
+}  // namespace
+
+namespace w8 {
+// Error and device queries for the other translation units of the library.
+int report_status(int status, const char* detail) {
+  g_last_error = detail ? detail : "";
+  return status;
+}
+int device_cus() { return cu_count(); }
+}  // namespace w8
+
+namespace {
+
 // Workspace layout of int8_mixed_linear (offsets from the 256-aligned base).
 // flags and cnt are the bookkeeping that every call leaves zero again.
 struct Int8Ws {

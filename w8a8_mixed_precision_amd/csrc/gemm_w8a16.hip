@@ -28,20 +28,30 @@
 
 namespace w8 {
 
-template <int WT>
+// B operand kinds: E4M3 codes widened to bf16 with the channel scale (the
+// weight-only FP8 linear), or 16-bit weights used as they are (the plain
+// 16-bit linear: bf16 x bf16 or f16 x f16). A has B's 16-bit type.
+enum : int { kBE4M3 = 0, kBBF16 = 1, kBF16 = 2 };
+
+template <int WT, int BK>
 struct W16Tile {
   static constexpr int BM = 64 * WT;                  // block rows = block columns
-  static constexpr int kABytes = BM * 128;            // A of one K step (bf16)
-  static constexpr int kStage = BM * 192;             // A then B (E4M3)
+  static constexpr int kBRow = BK == kBE4M3 ? 64 : 128;   // bytes of a B row per K step
+  static constexpr int kABytes = BM * 128;            // A of one K step (16-bit)
+  static constexpr int kStage = kABytes + BM * kBRow; // A then B
   static constexpr int kALoads = BM / 32;             // DMA instructions per wave per step (A)
-  static constexpr int kBLoads = BM / 64;             // ... (B)
+  static constexpr int kBLoads = BM * kBRow / 4096;   // ... (B)
   static constexpr int kLoads = kALoads + kBLoads;
   static constexpr int kMfma = 2 * WT * WT;           // MFMAs per wave per sub-step
-  static constexpr int kReads = 3 * WT;               // 16-byte LDS reads per wave per sub-step
+  static constexpr int kBReads = BK == kBE4M3 ? WT : 2 * WT;   // 16-byte B reads per sub-step
+  static constexpr int kReads = kBReads + 2 * WT;     // 16-byte LDS reads per wave per sub-step
   static constexpr int kChunks = 4 * WT * WT;         // 16-byte accumulator chunks per lane
   static constexpr int kPartBytes = BM * BM * 4;      // one fp32 partial
 };
-constexpr int kW16Stages = 3;
+// Ring stages: 3 (E4M3 B: 144 KB at WT = 4, 72 KB at WT = 2, two blocks per
+// CU); 16-bit B: 3 at WT = 2 (96 KB, one block per CU), 2 at WT = 4 (128 KB).
+template <int WT, int BK>
+constexpr int w16_stages() { return BK == kBE4M3 ? 3 : (WT == 4 ? 2 : 3); }
 
 // A rows: 8 chunks of 16 bytes, XOR-permuted by (row >> 1) & 7 so that the 32
 // rows a half-wave reads at one chunk spread over the banks.
@@ -57,13 +67,22 @@ __device__ __forceinline__ int swz_a128(int row, int ch) { return row * 128 + ((
 __device__ __forceinline__ void w16_dma(__amdgpu_buffer_rsrc_t r, uint8_t* dst, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
 }
-__device__ __forceinline__ v16f mfma_bf16(v8bf a, v8bf b, v16f c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ v16f mfma_bf16(v4i a, v4i b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0,
+                                                 0);
+}
+__device__ __forceinline__ v16f mfma_f16(v4i a, v4i b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+}
+template <int BK>
+__device__ __forceinline__ v16f mfma16(v4i a, v4i b, v16f c) {
+  if constexpr (BK == kBF16) return mfma_f16(a, b, c);
+  else return mfma_bf16(a, b, c);
 }
 
 // Eight E4M3 codes (bytes of w0, then w1) -> eight bf16 weights
 // rne_bf16(value * s); the float product of a code and a bf16 scale is exact.
-__device__ __forceinline__ v8bf widen8(uint32_t w0, uint32_t w1, float s) {
+__device__ __forceinline__ v4i widen8(uint32_t w0, uint32_t w1, float s) {
   const v2f p0 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w0), false);
   const v2f p1 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w0), true);
   const v2f p2 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w1), false);
@@ -72,30 +91,37 @@ __device__ __forceinline__ v8bf widen8(uint32_t w0, uint32_t w1, float s) {
   v8bf r;
 #pragma unroll
   for (int e = 0; e < 8; ++e) r[e] = static_cast<__bf16>(f[e]);
-  return r;
+  return __builtin_bit_cast(v4i, r);
 }
 
-// Fragments of one sub-step: a[i][q] (row block i, MFMA q), b[j][q].
+// Fragments of one sub-step (16 bytes each, kept as plain vectors): a[i][q]
+// (row block i, MFMA q), b[j][q], and for E4M3 the B chunks before widening.
 template <int WT>
 struct W16Frags {
-  v8bf a[WT][2];
-  v8bf b[WT][2];
-  v4u raw[WT];                                        // B chunks before widening
+  v4i a[WT][2];
+  v4i b[WT][2];
+  v4u raw[WT];
 };
 
-// Read number o (0 .. 3*WT-1) of a sub-step's fragments from stage `sl`: the
-// B chunks first (they still need widening), then A in consumption order.
-template <int WT>
+// Read number o (0 .. kReads-1) of a sub-step's fragments from stage `sl`: B
+// first (E4M3 chunks still need widening), then A in consumption order.
+template <int WT, int BK>
 __device__ __forceinline__ void w16_read(W16Frags<WT>& F, const uint8_t* sl, int o, int h, int wm, int wn, int fr,
                                          int fh) {
-  using T = W16Tile<WT>;
-  if (o < WT) {
-    const int row = wn * 32 * WT + 32 * o + fr;
-    F.raw[o] = *reinterpret_cast<const v4u*>(sl + T::kABytes + swz64(row, 2 * h + fh));
+  using T = W16Tile<WT, BK>;
+  if (o < T::kBReads) {
+    if constexpr (BK == kBE4M3) {
+      const int row = wn * 32 * WT + 32 * o + fr;
+      F.raw[o] = *reinterpret_cast<const v4u*>(sl + T::kABytes + swz64(row, 2 * h + fh));
+    } else {
+      const int j = o >> 1, q = o & 1;
+      const int row = wn * 32 * WT + 32 * j + fr;
+      F.b[j][q] = *reinterpret_cast<const v4i*>(sl + T::kABytes + swz_a128(row, 4 * h + 2 * fh + q));
+    }
   } else {
-    const int a = o - WT, i = a >> 1, q = a & 1;
+    const int a = o - T::kBReads, i = a >> 1, q = a & 1;
     const int row = wm * 32 * WT + 32 * i + fr;
-    F.a[i][q] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(sl + swz_a128(row, 4 * h + 2 * fh + q)));
+    F.a[i][q] = *reinterpret_cast<const v4i*>(sl + swz_a128(row, 4 * h + 2 * fh + q));
   }
 }
 
@@ -108,17 +134,18 @@ __device__ __forceinline__ void w16_widen(W16Frags<WT>& F, int j, float s) {
 // DMA of K-step kt into its ring slot (past the last step the last step is
 // loaded again into the slot just retired, which no later step reads, so every
 // step issues the same number of loads).
-template <int WT, int S>
+template <int WT, int BK, int S>
 __device__ __forceinline__ void w16_issue_one(uint8_t* lds, int kt, int nk, int d, __amdgpu_buffer_rsrc_t ra,
                                               __amdgpu_buffer_rsrc_t rb, const uint32_t* a_off,
                                               const uint32_t* b_off, int wave) {
-  using T = W16Tile<WT>;
+  using T = W16Tile<WT, BK>;
   uint8_t* st = lds + (kt % S) * T::kStage;
   const uint32_t k0 = static_cast<uint32_t>(min(kt, nk - 1));
   if (d < T::kALoads)
     w16_dma(ra, st + (wave * T::kALoads + d) * 1024, a_off[d], k0 * 128u);
   else
-    w16_dma(rb, st + T::kABytes + (wave * T::kBLoads + d - T::kALoads) * 1024, b_off[d - T::kALoads], k0 * 64u);
+    w16_dma(rb, st + T::kABytes + (wave * T::kBLoads + d - T::kALoads) * 1024, b_off[d - T::kALoads],
+            k0 * static_cast<uint32_t>(T::kBRow));
 }
 
 // One sub-step: the wave's 2*WT*WT MFMAs on fragments C, while the next
@@ -126,46 +153,50 @@ __device__ __forceinline__ void w16_issue_one(uint8_t* lds, int kt, int nk, int 
 // widened, and (DMA) the loads of K-step kt_dma go out into the retired slot.
 // Each MFMA is followed by its share of the reads, widenings and loads;
 // sched_barrier keeps that order.
-template <int WT, int S, bool DMA>
+template <int WT, int BK, int S, bool DMA>
 __device__ __forceinline__ void w16_phase(const W16Frags<WT>& C, W16Frags<WT>& N, v16f (*acc)[WT], const uint8_t* sn,
                                           int hn, int wm, int wn, int fr, int fh, const float* sc, uint8_t* lds,
                                           int kt_dma, int nk, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                           const uint32_t* a_off, const uint32_t* b_off, int wave) {
-  using T = W16Tile<WT>;
+  using T = W16Tile<WT, BK>;
   constexpr int kT = T::kMfma;
 #pragma unroll
   for (int t = 0; t < kT; ++t) {
     const int i = t / (2 * WT), j = (t / 2) % WT, q = t & 1;
-    acc[i][j] = mfma_bf16(C.b[j][q], C.a[i][q], acc[i][j]);
+    acc[i][j] = mfma16<BK>(C.b[j][q], C.a[i][q], acc[i][j]);
 #pragma unroll
-    for (int o = t * T::kReads / kT; o < (t + 1) * T::kReads / kT; ++o) w16_read<WT>(N, sn, o, hn, wm, wn, fr, fh);
-    // widen B chunk j' at MFMA kT/2 + j' * kT/(2*WT), long after its read
-    if (t >= kT / 2 && (t - kT / 2) % (kT / (2 * WT)) == 0) {
-      const int jw = (t - kT / 2) / (kT / (2 * WT));
-      w16_widen<WT>(N, jw, sc[jw]);
+    for (int o = t * T::kReads / kT; o < (t + 1) * T::kReads / kT; ++o)
+      w16_read<WT, BK>(N, sn, o, hn, wm, wn, fr, fh);
+    // widen E4M3 chunk j' at MFMA kT/2 + j' * kT/(2*WT), long after its read
+    if constexpr (BK == kBE4M3) {
+      if (t >= kT / 2 && (t - kT / 2) % (kT / (2 * WT)) == 0) {
+        const int jw = (t - kT / 2) / (kT / (2 * WT));
+        w16_widen<WT>(N, jw, sc[jw]);
+      }
     }
     if constexpr (DMA) {
 #pragma unroll
       for (int d = t * T::kLoads / kT; d < (t + 1) * T::kLoads / kT; ++d)
-        w16_issue_one<WT, S>(lds, kt_dma, nk, d, ra, rb, a_off, b_off, wave);
+        w16_issue_one<WT, BK, S>(lds, kt_dma, nk, d, ra, rb, a_off, b_off, wave);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// YDT: 0 bf16, 1 fp16, 2 fp32. Grid and split-K protocol of the FP8 W8A8
+// YDT: 0 bf16, 1 fp16, 2 fp32; BK: the B operand kind. sw: channel scales
+// (E4M3 only; unused otherwise). Grid and split-K protocol of the FP8 W8A8
 // kernel: blocks below dp_tiles own whole tiles; the rest are `split`
 // K-slices of R = (gridDim.x - dp_tiles) / split tiles, whose fp32 partials go
 // to their own slots of `part`; the last slice of a tile to arrive (counter in
 // `cnt`, zero on entry and left zero) sums all partials in slice order.
-template <int YDT, int WT>
-__global__ __launch_bounds__(256, 4 / WT) void k_w8a16_gemm(const uint16_t* __restrict__ A,
+template <int YDT, int WT, int BK>
+__global__ __launch_bounds__(256, BK == kBE4M3 ? 4 / WT : 1) void k_w8a16_gemm(const uint16_t* __restrict__ A,
                                                             const uint8_t* __restrict__ B, int M, int N, int K,
                                                             const float* __restrict__ sw, void* __restrict__ Y,
                                                             int tiles_m, int tiles_n, int dp_tiles, int split,
                                                             float* __restrict__ part, int* __restrict__ cnt) {
-  using T = W16Tile<WT>;
-  constexpr int S = kW16Stages;
+  using T = W16Tile<WT, BK>;
+  constexpr int S = w16_stages<WT, BK>();
   constexpr int BM = T::BM;
   // one LDS object (see the int8 kernel); the arrival flag lives past the
   // epilogue's area
@@ -197,7 +228,7 @@ __global__ __launch_bounds__(256, 4 / WT) void k_w8a16_gemm(const uint16_t* __re
   // channel scales of the lane's B rows (output columns), one per column block
   float sc[WT];
 #pragma unroll
-  for (int j = 0; j < WT; ++j) sc[j] = sw[min(n0 + wn * 32 * WT + 32 * j + fr, N - 1)];
+  for (int j = 0; j < WT; ++j) sc[j] = BK == kBE4M3 ? sw[min(n0 + wn * 32 * WT + 32 * j + fr, N - 1)] : 1.0f;
 
   // DMA sources, as byte offsets into X and Wq8. A: load d of wave w covers
   // rows (w*kALoads + d)*8 + lane/8, LDS slot (lane & 7) holding chunk
@@ -207,7 +238,8 @@ __global__ __launch_bounds__(256, 4 / WT) void k_w8a16_gemm(const uint16_t* __re
       const_cast<uint16_t*>(A), 0, static_cast<int>(static_cast<uint32_t>(M) * static_cast<uint32_t>(K) * 2u),
       kRawBuffer);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(B), 0, static_cast<int>(static_cast<uint32_t>(N) * static_cast<uint32_t>(K)), kRawBuffer);
+      const_cast<uint8_t*>(B), 0,
+      static_cast<int>(static_cast<uint32_t>(N) * static_cast<uint32_t>(K) * (BK == kBE4M3 ? 1u : 2u)), kRawBuffer);
   uint32_t a_off[T::kALoads], b_off[T::kBLoads];
 #pragma unroll
   for (int d = 0; d < T::kALoads; ++d) {
@@ -217,9 +249,15 @@ __global__ __launch_bounds__(256, 4 / WT) void k_w8a16_gemm(const uint16_t* __re
   }
 #pragma unroll
   for (int d = 0; d < T::kBLoads; ++d) {
-    const int r = (wave * T::kBLoads + d) * 16 + (lane >> 2);
-    const int ch = (lane & 3) ^ swz_term(r);
-    b_off[d] = static_cast<uint32_t>(min(n0 + r, N - 1)) * static_cast<uint32_t>(K) + kb * 64 + ch * 16;
+    if constexpr (BK == kBE4M3) {
+      const int r = (wave * T::kBLoads + d) * 16 + (lane >> 2);
+      const int ch = (lane & 3) ^ swz_term(r);
+      b_off[d] = static_cast<uint32_t>(min(n0 + r, N - 1)) * static_cast<uint32_t>(K) + kb * 64 + ch * 16;
+    } else {                                    // 16-bit rows: the layout of A
+      const int r = (wave * T::kBLoads + d) * 8 + (lane >> 3);
+      const int ch = (lane & 7) ^ ((r >> 1) & 7);
+      b_off[d] = (static_cast<uint32_t>(min(n0 + r, N - 1)) * static_cast<uint32_t>(K) + kb * 64) * 2u + ch * 16;
+    }
   }
   const int nk = ke - kb;
 
@@ -233,42 +271,46 @@ __global__ __launch_bounds__(256, 4 / WT) void k_w8a16_gemm(const uint16_t* __re
 
   for (int s = 0; s < S; ++s)
 #pragma unroll
-    for (int d = 0; d < T::kLoads; ++d) w16_issue_one<WT, S>(lds, s, nk, d, ra, rb, a_off, b_off, wave);
+    for (int d = 0; d < T::kLoads; ++d) w16_issue_one<WT, BK, S>(lds, s, nk, d, ra, rb, a_off, b_off, wave);
   wait_vmcnt<(S - 1) * T::kLoads>();            // step 0 landed (this wave)
   block_barrier();                              // ... for every wave
   W16Frags<WT> f0, f1;
 #pragma unroll
-  for (int o = 0; o < T::kReads; ++o) w16_read<WT>(f0, lds, o, 0, wm, wn, fr, fh);
+  for (int o = 0; o < T::kReads; ++o) w16_read<WT, BK>(f0, lds, o, 0, wm, wn, fr, fh);
+  if constexpr (BK == kBE4M3) {
 #pragma unroll
-  for (int j = 0; j < WT; ++j) w16_widen<WT>(f0, j, sc[j]);
+    for (int j = 0; j < WT; ++j) w16_widen<WT>(f0, j, sc[j]);
+  }
 
   for (int kt = 0; kt < nk - 1; ++kt) {
     const uint8_t* sa = lds + (kt % S) * T::kStage;
     // sub-step 0 multiplies while sub-step 1's fragments are read
-    w16_phase<WT, S, false>(f0, f1, acc, sa, 1, wm, wn, fr, fh, sc, lds, 0, nk, ra, rb, a_off, b_off, wave);
+    w16_phase<WT, BK, S, false>(f0, f1, acc, sa, 1, wm, wn, fr, fh, sc, lds, 0, nk, ra, rb, a_off, b_off, wave);
     wait_lgkmcnt<0>();                          // this slot is fully read
     wait_vmcnt<(S - 2) * T::kLoads>();          // step kt+1 landed (this wave)
     block_barrier();                            // ... for every wave; slot kt retired
     // sub-step 1 multiplies while step kt+1's first fragments are read and
     // step kt+S is fetched into the retired slot
-    w16_phase<WT, S, true>(f1, f0, acc, lds + ((kt + 1) % S) * T::kStage, 0, wm, wn, fr, fh, sc, lds, kt + S, nk,
-                           ra, rb, a_off, b_off, wave);
+    w16_phase<WT, BK, S, true>(f1, f0, acc, lds + ((kt + 1) % S) * T::kStage, 0, wm, wn, fr, fh, sc, lds, kt + S,
+                               nk, ra, rb, a_off, b_off, wave);
   }
   {
     const uint8_t* sa = lds + ((nk - 1) % S) * T::kStage;
 #pragma unroll
-    for (int o = 0; o < T::kReads; ++o) w16_read<WT>(f1, sa, o, 1, wm, wn, fr, fh);
+    for (int o = 0; o < T::kReads; ++o) w16_read<WT, BK>(f1, sa, o, 1, wm, wn, fr, fh);
+    if constexpr (BK == kBE4M3) {
 #pragma unroll
-    for (int j = 0; j < WT; ++j) w16_widen<WT>(f1, j, sc[j]);
-#pragma unroll
-    for (int t = 0; t < T::kMfma; ++t) {
-      const int i = t / (2 * WT), j = (t / 2) % WT, q = t & 1;
-      acc[i][j] = mfma_bf16(f0.b[j][q], f0.a[i][q], acc[i][j]);
+      for (int j = 0; j < WT; ++j) w16_widen<WT>(f1, j, sc[j]);
     }
 #pragma unroll
     for (int t = 0; t < T::kMfma; ++t) {
       const int i = t / (2 * WT), j = (t / 2) % WT, q = t & 1;
-      acc[i][j] = mfma_bf16(f1.b[j][q], f1.a[i][q], acc[i][j]);
+      acc[i][j] = mfma16<BK>(f0.b[j][q], f0.a[i][q], acc[i][j]);
+    }
+#pragma unroll
+    for (int t = 0; t < T::kMfma; ++t) {
+      const int i = t / (2 * WT), j = (t / 2) % WT, q = t & 1;
+      acc[i][j] = mfma16<BK>(f1.b[j][q], f1.a[i][q], acc[i][j]);
     }
   }
   wait_lgkmcnt<0>();
@@ -432,22 +474,38 @@ GemmPlan plan_w8a16_gemm(int64_t M, int64_t N, int64_t K, int cus) {
 
 // K % 64 == 0 (checked by the caller). ydt: 0 bf16, 1 fp16, 2 fp32. `part` /
 // `cnt`: plan.partial_bytes() of fp32 partials and plan.counters() zeroed
-// counters (left zero), when plan.split > 1.
-void launch_w8a16_gemm(const uint16_t* A, const uint8_t* B, int64_t M, int64_t N, int64_t K, const float* sw,
-                       void* Y, int ydt, const GemmPlan& plan, float* part, int* cnt, hipStream_t s) {
+// counters (left zero), when plan.split > 1. bk: kBE4M3 (B = E4M3 codes, sw
+// their channel scales, A bf16), kBBF16 / kBF16 (B and A 16-bit, sw unused).
+template <int BK>
+static void launch_w16(const uint16_t* A, const uint8_t* B, int64_t M, int64_t N, int64_t K, const float* sw, void* Y,
+                       int ydt, const GemmPlan& plan, float* part, int* cnt, hipStream_t s) {
   const dim3 block(256);
   const dim3 grid(plan.dp_tiles + plan.sk_tiles * plan.split);
 #define W8_W16_ARGS A, B, (int)M, (int)N, (int)K, sw, Y, plan.tiles_m, plan.tiles_n, plan.dp_tiles, plan.split, part, cnt
   if (plan.bm == 256) {
-    if (ydt == 0) k_w8a16_gemm<0, 4><<<grid, block, 0, s>>>(W8_W16_ARGS);
-    else if (ydt == 1) k_w8a16_gemm<1, 4><<<grid, block, 0, s>>>(W8_W16_ARGS);
-    else k_w8a16_gemm<2, 4><<<grid, block, 0, s>>>(W8_W16_ARGS);
+    if (ydt == 0) k_w8a16_gemm<0, 4, BK><<<grid, block, 0, s>>>(W8_W16_ARGS);
+    else if (ydt == 1) k_w8a16_gemm<1, 4, BK><<<grid, block, 0, s>>>(W8_W16_ARGS);
+    else k_w8a16_gemm<2, 4, BK><<<grid, block, 0, s>>>(W8_W16_ARGS);
   } else {
-    if (ydt == 0) k_w8a16_gemm<0, 2><<<grid, block, 0, s>>>(W8_W16_ARGS);
-    else if (ydt == 1) k_w8a16_gemm<1, 2><<<grid, block, 0, s>>>(W8_W16_ARGS);
-    else k_w8a16_gemm<2, 2><<<grid, block, 0, s>>>(W8_W16_ARGS);
+    if (ydt == 0) k_w8a16_gemm<0, 2, BK><<<grid, block, 0, s>>>(W8_W16_ARGS);
+    else if (ydt == 1) k_w8a16_gemm<1, 2, BK><<<grid, block, 0, s>>>(W8_W16_ARGS);
+    else k_w8a16_gemm<2, 2, BK><<<grid, block, 0, s>>>(W8_W16_ARGS);
   }
 #undef W8_W16_ARGS
+}
+
+void launch_w8a16_gemm(const uint16_t* A, const uint8_t* B, int64_t M, int64_t N, int64_t K, const float* sw,
+                       void* Y, int ydt, const GemmPlan& plan, float* part, int* cnt, hipStream_t s) {
+  launch_w16<kBE4M3>(A, B, M, N, K, sw, Y, ydt, plan, part, cnt, s);
+}
+
+// The plain 16-bit linear Y = X W^T (X and W both bf16, or both f16), on the
+// same kernel with the 16-bit weights used as they are.
+void launch_linear16(const uint16_t* A, const uint16_t* B, bool bf16, int64_t M, int64_t N, int64_t K, void* Y,
+                     int ydt, const GemmPlan& plan, float* part, int* cnt, hipStream_t s) {
+  const uint8_t* b = reinterpret_cast<const uint8_t*>(B);
+  if (bf16) launch_w16<kBBF16>(A, b, M, N, K, nullptr, Y, ydt, plan, part, cnt, s);
+  else launch_w16<kBF16>(A, b, M, N, K, nullptr, Y, ydt, plan, part, cnt, s);
 }
 
 }  // namespace w8

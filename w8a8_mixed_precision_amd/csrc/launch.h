@@ -9,6 +9,11 @@
 
 namespace w8 {
 
+// Sets the detail w8_last_error() returns on this thread; returns `status`.
+int report_status(int status, const char* detail);
+// Compute units of the current device (0 if it cannot be queried).
+int device_cus();
+
 // Grid of the tiled GEMMs: dp_tiles whole tiles of bm x bm outputs, then
 // sk_tiles tiles cut into `split` K-slices each (split == 1: none). The int8
 // GEMM uses bm = 256, and with `small` runs each of the sk_tiles leftover
@@ -62,5 +67,10 @@ GemmPlan plan_w8a16_gemm(int64_t M, int64_t N, int64_t K, int cus);
 GemmPlan plan_w8a16_gemm_split(int64_t M, int64_t N, int split, int bm);
 void launch_w8a16_gemm(const uint16_t* A, const uint8_t* B, int64_t M, int64_t N, int64_t K, const float* sw,
                        void* Y, int ydt, const GemmPlan& plan, float* part, int* cnt, hipStream_t s);
+// Plain 16-bit linear (X and W both bf16 or both f16), K % 64 == 0, on the
+// weight-only kernel; plans from plan_w8a16_gemm* (the operand bytes differ
+// but the tiling trade-offs are alike).
+void launch_linear16(const uint16_t* A, const uint16_t* B, bool bf16, int64_t M, int64_t N, int64_t K, void* Y,
+                     int ydt, const GemmPlan& plan, float* part, int* cnt, hipStream_t s);
 
 }  // namespace w8
