@@ -408,6 +408,10 @@ w8_status fp8_w8a8_linear(const void* X, int x_dt, int64_t M, int64_t K, const u
   return check_launch("fp8_w8a8_linear");
 }
 
+}  // extern "C"
+
+namespace {
+
 // FP8 weight-only: split-K counters and partials of the plan (at least one
 // aligned unit, so a workspace is always passed).
 struct W16Ws {
@@ -429,6 +433,10 @@ w8::GemmPlan w16_plan(int64_t M, int64_t N, int64_t K, int split, int tile) {
   return split == 0 ? w8::plan_w8a16_gemm(M, N, K, cu_count())
                     : w8::plan_w8a16_gemm_split(M, N, split, tile == 128 ? 128 : 256);
 }
+
+}  // namespace
+
+extern "C" {
 
 static w8_status w16_checks(const void* X, int x_dt, int64_t M, int64_t K, const uint8_t* Wq8, const float* sw,
                             int64_t N, void* Y, int y_dt) {
@@ -471,6 +479,10 @@ w8_status fp8_w8a16_linear(const void* X, int x_dt, int64_t M, int64_t K, const 
                  stream, "fp8_w8a16_linear");
 }
 
+}  // extern "C"
+
+namespace {
+
 // W4A8: activation codes and row scales, split-K counters and partials.
 struct W4Ws {
   size_t q, sx, cnt, part, total;
@@ -488,6 +500,10 @@ W4Ws w4_layout(int64_t M, int64_t N, int64_t K, int split) {
   w.total = off;
   return w;
 }
+
+}  // namespace
+
+extern "C" {
 
 static w8_status w4_checks(const void* X, int x_dt, int64_t M, int64_t K, const uint8_t* Wq4, const float* sw4,
                            int64_t N, void* Y, int y_dt) {

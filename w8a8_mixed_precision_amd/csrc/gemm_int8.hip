@@ -64,7 +64,10 @@ __device__ __forceinline__ int side_off(int row, int ch) { return row * 64 + ((c
 
 // Epilogue staging, one 32-column block of the wave tile at a time: all its
 // 32*WT rows x 32 columns go to the wave's staging area (row pitch
-// kStgPitchJ), then out as row segments of 32 elements. Every element of a
+// kStgPitchJ), then out as 128-byte row segments, whole cache lines: one
+// block of 32-bit outputs, or two neighbouring blocks of fp16 outputs staged
+// side by side (a line written in two halves at different times can be
+// evicted in between and then costs two line writes). Every element of a
 // column block shares the lane's 16 column scales and biases, so these are
 // read from LDS once per block.
 constexpr int kStgPitchJ = 128 + 16;            // a staged row: 32 x 4 bytes + pad
@@ -116,16 +119,16 @@ __device__ __forceinline__ void stage_cols(const v16i (&acc)[WT][WT], const v16f
     }
 }
 
-// Writes the R staged rows of a column block (32 elements of EB bytes each) to
-// Y rows m_base.. and columns n_base.. (clipped to [M, N)): every lane stores
-// 16-byte chunks, 64 / (32 * EB / 16) rows per instruction, reading at most 8
-// chunks from LDS ahead of their stores. vec: rows of Y are 16-byte aligned.
+// Writes the R staged rows (128 bytes each: 128 / EB elements) to Y rows
+// m_base.. and columns n_base.. (clipped to [M, N)): every lane stores
+// 16-byte chunks, 8 rows per instruction, reading at most 8 chunks from LDS
+// ahead of their stores. vec: rows of Y are 16-byte aligned.
 template <int EB, int R>
 __device__ __forceinline__ void flush_cols(const char* stg, char* __restrict__ y, int M, int N, int m_base,
                                            int n_base, int lane, bool vec) {
   constexpr int EPC = 16 / EB;                  // elements per 16-byte chunk
-  constexpr int CPR = 32 / EPC;                 // chunks per staged row: 4 or 8
-  constexpr int RPI = 64 / CPR;                 // rows per instruction: 16 or 8
+  constexpr int CPR = 8;                        // chunks per staged row
+  constexpr int RPI = 64 / CPR;                 // rows per instruction
   constexpr int T = R / RPI;                    // store instructions
   constexpr int TB = T > 8 ? 8 : T;             // chunks read ahead
   const int ch = lane % CPR;
@@ -165,7 +168,8 @@ __device__ __forceinline__ void flush_cols(const char* stg, char* __restrict__ y
 // (i, j) of a lane is
 //   m = m0 + wm*32*WT + 32*i + (lane&31),
 //   n = n0 + wn*32*WT + 32*j + 8*(r>>2) + 4*(lane>>5) + (r&3).
-// Written one column block j at a time (stage_cols, flush_cols).
+// Staged one column block j at a time (stage_cols) and written in whole
+// 128-byte row segments (flush_cols).
 //
 // rsx[i]: sx[m]/127 for the lane's row of block i (prefetched by the caller);
 // scol, sbias: LDS copies of sw[n0 .. n0+64*WT) / 127 and of the bias there
@@ -179,6 +183,8 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[WT][WT], int M, int N, int 
   const int fr = lane & 31, fh = lane >> 5;
   constexpr int EB = MODE == 1 ? 2 : 4;         // bytes per output element
   constexpr int WR = 32 * WT;                   // rows (= columns) of the wave tile
+  constexpr bool PAIR = EB == 2;                // two column blocks per staged row
+  static_assert(WT % 2 == 0, "column blocks pair up");
   const int P = (nO + 31) & ~31;
   const bool vec = (static_cast<int64_t>(N) * EB) % 16 == 0;
   using V8 = typename std::conditional<XBF16, v8bf, v8h>::type;
@@ -187,8 +193,9 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[WT][WT], int M, int N, int 
 #pragma unroll
   for (int j = 0; j < WT; ++j) {
     const int ncol = wn * WR + 32 * j;
+    const int soff = PAIR ? (j & 1) * 64 : 0;   // byte offset of the block in a staged row
     if (MODE == 0 || P == 0) {
-      stage_cols<MODE, false, WT>(acc, nullptr, j, rsx, scol, sbias, ncol, lane, stg);
+      stage_cols<MODE, false, WT>(acc, nullptr, j, rsx, scol, sbias, ncol, lane, stg + soff);
     } else {
       // side product for this column block: o[i] = WO(block j) . XO(rows of block i)^T
       v16f o[WT];
@@ -220,10 +227,11 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[WT][WT], int M, int N, int 
           }
         }
       }
-      stage_cols<MODE, true, WT>(acc, o, j, rsx, scol, sbias, ncol, lane, stg);
+      stage_cols<MODE, true, WT>(acc, o, j, rsx, scol, sbias, ncol, lane, stg + soff);
     }
+    if (PAIR && (j & 1) == 0) continue;         // the pair's second block completes the lines
     wave_lds_fence();
-    flush_cols<EB, WR>(stg, y, M, N, row0, n0 + ncol, lane, vec);
+    flush_cols<EB, WR>(stg, y, M, N, row0, n0 + ncol - (PAIR ? 32 : 0), lane, vec);
     wave_lds_fence();                           // staging reads done before the next block writes
   }
 }
