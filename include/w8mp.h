@@ -386,11 +386,16 @@ w8_status w8dbg_fp8_gemm(const uint8_t* xq, const float* sx, const uint8_t* Wq8,
 /* The plain 16-bit linear of the block driver's exclusion policy:
  * Y [M,N] = X [M,K] . W [N,K]^T, X and W both f16 or both bf16 (x_dt), fp32
  * accumulation on 16-bit MFMA, rounded into Y (bf16/f16/f32). K % 64 == 0,
- * K <= 65536. split = 0: the driver's own K-slicing; else `split` slices of
- * 128x128 blocks (<= K / 64). Workspace: w8dbg_linear16_workspace_size bytes
- * (at least 256), zero-filled before first use (left zero). */
-size_t w8dbg_linear16_workspace_size(int64_t M, int64_t N, int64_t K, int split);
-w8_status w8dbg_linear16(const void* X, int x_dt, int64_t M, int64_t K, const void* W, int64_t N, int split,
+ * K <= 65536. split = 0: the driver's own tiling (tile ignored); else
+ * 1 <= split <= K / 64 and tile = 256: 256x256 blocks, the tiles of the
+ * device's full waves whole and the leftover tiles of the last partial wave
+ * (every tile when there are fewer tiles than compute units) in `split`
+ * K-slices; tile = 128: 128x128 blocks, every one in `split` K-slices (other
+ * tiles: W8_ERR_INVALID_ARGUMENT). Workspace:
+ * w8dbg_linear16_workspace_size(M, N, K, split, tile) bytes (at least 256) on
+ * the current device, zero-filled before first use (left zero). */
+size_t w8dbg_linear16_workspace_size(int64_t M, int64_t N, int64_t K, int split, int tile);
+w8_status w8dbg_linear16(const void* X, int x_dt, int64_t M, int64_t K, const void* W, int64_t N, int split, int tile,
                          void* Y, int y_dt, void* workspace, size_t workspace_bytes, void* stream);
 
 size_t w8dbg_w4a8_linear_workspace_size(int64_t M, int64_t N, int64_t K, int split);

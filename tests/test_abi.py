@@ -220,11 +220,14 @@ def test_dit_block_and_linear16_reject():
     assert "down projection" in _abi.lib().w8_last_error().decode()
     f16, f32 = _abi.W8_DT_F16, _abi.W8_DT_F32
     l16 = lib.w8dbg_linear16
-    assert l16(A, f16, 4, 96, A, 4, 0, A, f32, A, WS_BIG, None) == _abi.W8_ERR_UNSUPPORTED        # K % 64
-    assert l16(A, f32, 4, 128, A, 4, 0, A, f32, A, WS_BIG, None) == _abi.W8_ERR_UNSUPPORTED       # X type
-    assert l16(A, f16, 4, 128, A, 4, 3, A, f32, A, WS_BIG, None) == _abi.W8_ERR_UNSUPPORTED       # split > K/64
-    assert l16(None, f16, 4, 128, A, 4, 0, A, f32, A, WS_BIG, None) == _abi.W8_ERR_INVALID_ARGUMENT
-    assert l16(A, f16, 4, 128, A, 4, 2, A, f32, A, 256, None) == _abi.W8_ERR_WORKSPACE
+    assert l16(A, f16, 4, 96, A, 4, 0, 0, A, f32, A, WS_BIG, None) == _abi.W8_ERR_UNSUPPORTED        # K % 64
+    assert l16(A, f32, 4, 128, A, 4, 0, 0, A, f32, A, WS_BIG, None) == _abi.W8_ERR_UNSUPPORTED       # X type
+    assert l16(A, f16, 4, 128, A, 4, 3, 128, A, f32, A, WS_BIG, None) == _abi.W8_ERR_UNSUPPORTED     # split > K/64
+    assert l16(A, f16, 4, 128, A, 4, 1, 64, A, f32, A, WS_BIG, None) == _abi.W8_ERR_INVALID_ARGUMENT  # tile
+    assert l16(None, f16, 4, 128, A, 4, 0, 0, A, f32, A, WS_BIG, None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert l16(A, f16, 4, 128, A, 4, 2, 128, A, f32, A, 256, None) == _abi.W8_ERR_WORKSPACE
+    assert l16(A, f16, 4, 128, A, 4, 2, 256, A, f32, A, 128, None) == _abi.W8_ERR_WORKSPACE     # < 256 bytes
+    assert lib.w8dbg_linear16_workspace_size(4, 4, 128, 2, 128) >= 2 * 128 * 128 * 4
 
 
 def test_w8a16_workspace_and_debug_rejects():

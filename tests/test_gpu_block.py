@@ -21,17 +21,19 @@ from tests.gpu_util import OUT, announce, dev16, host_stored, rel_fro, row_rel_f
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("M,K,N,dtype,split", [(300, 1024, 520, "f16", 0), (300, 1024, 520, "bf16", 2),
-                                               (64, 256, 96, "f16", 4), (1, 64, 1, "bf16", 1),
-                                               (257, 4096, 129, "f16", 8)])
+@pytest.mark.parametrize("M,K,N,dtype,split,tile", [(300, 1024, 520, "f16", 0, 0), (300, 1024, 520, "bf16", 2, 128),
+                                                    (64, 256, 96, "f16", 4, 128), (1, 64, 1, "bf16", 1, 128),
+                                                    (257, 4096, 129, "f16", 8, 128),
+                                                    (300, 1024, 520, "bf16", 1, 256), (300, 1024, 520, "f16", 3, 256),
+                                                    (1, 64, 1, "f16", 1, 256), (513, 2048, 777, "bf16", 16, 256)])
 @pytest.mark.parametrize("out_dtype", ["f32", "f16"])
-def test_linear16_matches_oracle(M, K, N, dtype, split, out_dtype):
+def test_linear16_matches_oracle(M, K, N, dtype, split, tile, out_dtype):
     rng = np.random.default_rng(M + K + N)
     enc = o.round_to_f16 if dtype == "f16" else o.round_to_bf16
     x_bits, w_bits = enc(rng.standard_normal((M, K))), enc(rng.standard_normal((N, K)) * 0.05)
     ref = B.linear16(x_bits, dtype, w_bits, dtype, out_dtype)
-    announce("linear16", M, K, N, dtype, split, out_dtype)
-    y = w8.debug_linear16(dev16(x_bits, dtype), dev16(w_bits, dtype), split, OUT[out_dtype])
+    announce("linear16", M, K, N, dtype, split, tile, out_dtype)
+    y = w8.debug_linear16(dev16(x_bits, dtype), dev16(w_bits, dtype), split, OUT[out_dtype], tile=tile)
     torch.cuda.synchronize()
     got = o.stored_to_f64(host_stored(y, out_dtype), out_dtype)
     e, er = rel_fro(got, ref["y"]), row_rel_fro(got, ref["y"]).max()
@@ -65,6 +67,23 @@ def _block(rng, D, F, with16, massive_rows=()):
                       norm1=norms[0][1], norm2=norms[1][1],
                       w_down16=dev16(w16, "f16") if with16 else None)
     return blk, gpu
+
+
+@pytest.mark.parametrize("split", [0, 2, 8])
+def test_linear16_whole_waves_and_sliced_tail(split):
+    """More 256x256 tiles than compute units: the full waves' tiles whole and
+    the leftover tiles in K-slices (split 0: the driver's own plan), at the
+    DiT 1024^2 output shape with a short K; every output checked."""
+    rng = np.random.default_rng(97 + split)
+    M, K, N = 4352, 1024, 4096
+    x_bits, w_bits = o.round_to_f16(rng.standard_normal((M, K))), o.round_to_f16(rng.standard_normal((N, K)) * 0.05)
+    ref = B.linear16(x_bits, "f16", w_bits, "f16", "f32")
+    announce("linear16 tail", M, K, N, split)
+    y = w8.debug_linear16(dev16(x_bits, "f16"), dev16(w_bits, "f16"), split, torch.float32, tile=256)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    e, er = rel_fro(got, ref["y"]), row_rel_fro(got, ref["y"]).max()
+    assert e <= 1e-5 and er <= 1e-5, (e, er)
 
 
 @pytest.mark.parametrize("with16", [False, True], ids=["int8_down", "fp16_down"])

@@ -258,18 +258,21 @@ class DitBlock:
 
 
 def debug_linear16(x: torch.Tensor, w: torch.Tensor, split: int = 0, out_dtype: torch.dtype = torch.float32,
-                   workspace: torch.Tensor | None = None) -> torch.Tensor:
+                   workspace: torch.Tensor | None = None, tile: int = 128) -> torch.Tensor:
     """The block driver's plain 16-bit linear: Y = X W^T (x and w both fp16
-    or both bf16), `split` K-slices of 128x128 blocks (0: the driver's own)."""
+    or both bf16). split 0: the driver's own tiling; else tile 128: 128x128
+    blocks each in `split` K-slices; tile 256: 256x256 blocks with the last
+    partial wave's tiles in `split` K-slices."""
     _dev(x, "x"), _dev(w, "w")
     M, K = x.shape
     N = w.shape[0]
     if w.dtype != x.dtype or w.shape[1] != K:
         raise ValueError("w must be [N, K] of x's dtype")
     y = torch.empty((M, N), dtype=out_dtype, device=x.device)
-    n_ws = int(lib().w8dbg_linear16_workspace_size(M, N, K, int(split)))
+    n_ws = int(lib().w8dbg_linear16_workspace_size(M, N, K, int(split), int(tile)))
     ws = workspace if workspace is not None else _workspace(n_ws, x.device)
-    _abi.check(lib().w8dbg_linear16(x.data_ptr(), _dt(x), M, K, w.data_ptr(), N, int(split), y.data_ptr(), _dt(y),
+    _abi.check(lib().w8dbg_linear16(x.data_ptr(), _dt(x), M, K, w.data_ptr(), N, int(split), int(tile), y.data_ptr(),
+                                    _dt(y),
                                     ws.data_ptr(), ws.numel(), _stream(x)))
     return y
 

@@ -47,8 +47,8 @@ SIGNATURES = {
     "w4a8_linear_workspace_size": (_size, [_i64, _i64, _i64]),
     "w8_dit_block_workspace_size": (_size, [_i64, _i64, _i64]),
     "w8_dit_block_forward": (_int, [_p, _p, _i64, _p, _p, _size, _p]),
-    "w8dbg_linear16_workspace_size": (_size, [_i64, _i64, _i64, _int]),
-    "w8dbg_linear16": (_int, [_p, _int, _i64, _i64, _p, _i64, _int, _p, _int, _p, _size, _p]),
+    "w8dbg_linear16_workspace_size": (_size, [_i64, _i64, _i64, _int, _int]),
+    "w8dbg_linear16": (_int, [_p, _int, _i64, _i64, _p, _i64, _int, _int, _p, _int, _p, _size, _p]),
     "w4a8_linear": (_int, [_p, _int, _i64, _i64, _p, _p, _i64, _p, _int, _p, _size, _p]),
     "w8dbg_w4a8_linear_workspace_size": (_size, [_i64, _i64, _i64, _int]),
     "w8dbg_w4a8_linear": (_int, [_p, _int, _i64, _i64, _p, _p, _i64, _int, _p, _int, _p, _size, _p]),

@@ -86,14 +86,6 @@ static void launch_residual(const uint16_t* h, const void* d, bool f32d, const f
   else k_residual<false><<<grid, block, 0, s>>>(h, d, bias, M, D, y);
 }
 
-// The plain 16-bit linear's tiling: the weight-only planner's K-slicing on
-// 128x128 blocks (the 16-bit operands leave room for only two ring stages
-// of 256x256).
-GemmPlan plan_linear16(int64_t M, int64_t N, int64_t K, int cus) {
-  const GemmPlan p = plan_w8a16_gemm(M, N, K, cus);
-  return plan_w8a16_gemm_split(M, N, p.split, 128);
-}
-
 }  // namespace w8
 
 namespace {
@@ -214,14 +206,23 @@ w8_status w8_dit_block_forward(const w8_dit_block* blk, const void* X, int64_t M
   return static_cast<w8_status>(w8::report_status(W8_OK, ""));
 }
 
-size_t w8dbg_linear16_workspace_size(int64_t M, int64_t N, int64_t K, int split) {
+// The parity export's tiling: the driver's own plan (split 0), 256x256 blocks
+// with the last partial wave's tiles in `split` K-slices, or 128x128 blocks
+// all in `split` K-slices.
+static w8::GemmPlan linear16_debug_plan(int64_t M, int64_t N, int64_t K, int split, int tile) {
+  if (split == 0) return w8::plan_linear16(M, N, K, block_cus());
+  if (tile == 256) return w8::plan_linear16_tail(M, N, split, block_cus());
+  return w8::plan_w8a16_gemm_split(M, N, split, 128);
+}
+
+size_t w8dbg_linear16_workspace_size(int64_t M, int64_t N, int64_t K, int split, int tile) {
   if (M < 1 || N < 1 || K < 1 || split < 0) return 0;
-  const w8::GemmPlan p = split == 0 ? w8::plan_linear16(M, N, K, block_cus()) : w8::plan_w8a16_gemm_split(M, N, split, 128);
+  const w8::GemmPlan p = linear16_debug_plan(M, N, K, split, tile);
   return std::max<size_t>(upb(4 * static_cast<size_t>(p.counters())) + upb(p.partial_bytes()), kAlignB);
 }
 
-w8_status w8dbg_linear16(const void* X, int x_dt, int64_t M, int64_t K, const void* W, int64_t N, int split, void* Y,
-                         int y_dt, void* workspace, size_t workspace_bytes, void* stream) {
+w8_status w8dbg_linear16(const void* X, int x_dt, int64_t M, int64_t K, const void* W, int64_t N, int split, int tile,
+                         void* Y, int y_dt, void* workspace, size_t workspace_bytes, void* stream) {
   if (!X || !W || !Y) return block_fail(W8_ERR_INVALID_ARGUMENT, "null pointer argument");
   if (x_dt != W8_DT_F16 && x_dt != W8_DT_BF16) return block_fail(W8_ERR_UNSUPPORTED, "X must be f16 or bf16");
   if (y_dt != W8_DT_BF16 && y_dt != W8_DT_F16 && y_dt != W8_DT_F32)
@@ -232,8 +233,9 @@ w8_status w8dbg_linear16(const void* X, int x_dt, int64_t M, int64_t K, const vo
   if (M * K * 2 >= (int64_t(1) << 32) || N * K * 2 >= (int64_t(1) << 32))
     return block_fail(W8_ERR_UNSUPPORTED, "X and W must each be smaller than 4 GiB");
   if (split < 0 || split > K / 64) return block_fail(W8_ERR_UNSUPPORTED, "split must be in [0, K / 64]");
+  if (split > 0 && tile != 128 && tile != 256) return block_fail(W8_ERR_INVALID_ARGUMENT, "tile must be 128 or 256");
   if (!al16(X) || !al16(W) || !al16(Y)) return block_fail(W8_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
-  const w8::GemmPlan p = split == 0 ? w8::plan_linear16(M, N, K, block_cus()) : w8::plan_w8a16_gemm_split(M, N, split, 128);
+  const w8::GemmPlan p = linear16_debug_plan(M, N, K, split, tile);
   const size_t cnt_bytes = upb(4 * static_cast<size_t>(p.counters()));
   const size_t need = std::max<size_t>(cnt_bytes + upb(p.partial_bytes()), kAlignB);
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & (kAlignB - 1)) != 0 || workspace_bytes < need)

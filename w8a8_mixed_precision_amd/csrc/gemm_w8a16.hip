@@ -21,6 +21,13 @@
 // (8 bf16 each, one per MFMA) and B chunk 2h + fh (16 codes, widened into the
 // two matching bf16 fragments). Both operands use the same k, so every k of
 // the step is multiplied exactly once.
+//
+// The plain 16-bit linear on 256x256 blocks takes K steps of 32 values
+// instead: 64-byte rows of both operands (the int8 GEMM's layout), one
+// sub-step per step, A and B chunks 2fh and 2fh + 1, through a 4-stage ring of
+// 32 KB. It streams the same 32 KB per 1024 MFMA cycles as the int8 GEMM; the
+// 64-value step would leave room for only two 64 KB stages, one step of
+// look-ahead, too little to cover the load latency.
 #include <algorithm>
 
 #include "launch.h"
@@ -36,10 +43,13 @@ enum : int { kBE4M3 = 0, kBBF16 = 1, kBF16 = 2 };
 template <int WT, int BK>
 struct W16Tile {
   static constexpr int BM = 64 * WT;                  // block rows = block columns
-  static constexpr int kBRow = BK == kBE4M3 ? 64 : 128;   // bytes of a B row per K step
-  static constexpr int kABytes = BM * 128;            // A of one K step (16-bit)
+  static constexpr int kKS = BK != kBE4M3 && WT == 4 ? 32 : 64;   // K values per step
+  static constexpr int kSub = kKS / 32;               // sub-steps per K step
+  static constexpr int kARow = 2 * kKS;               // bytes of an A row per K step (16-bit)
+  static constexpr int kBRow = BK == kBE4M3 ? kKS : 2 * kKS;   // bytes of a B row per K step
+  static constexpr int kABytes = BM * kARow;          // A of one K step
   static constexpr int kStage = kABytes + BM * kBRow; // A then B
-  static constexpr int kALoads = BM / 32;             // DMA instructions per wave per step (A)
+  static constexpr int kALoads = kABytes / 4096;      // DMA instructions per wave per step (A)
   static constexpr int kBLoads = BM * kBRow / 4096;   // ... (B)
   static constexpr int kLoads = kALoads + kBLoads;
   static constexpr int kMfma = 2 * WT * WT;           // MFMAs per wave per sub-step
@@ -49,9 +59,10 @@ struct W16Tile {
   static constexpr int kPartBytes = BM * BM * 4;      // one fp32 partial
 };
 // Ring stages: 3 (E4M3 B: 144 KB at WT = 4, 72 KB at WT = 2, two blocks per
-// CU); 16-bit B: 3 at WT = 2 (96 KB, one block per CU), 2 at WT = 4 (128 KB).
+// CU); 16-bit B: 3 at WT = 2 (96 KB, one block per CU), 4 at WT = 4 (32-value
+// steps, 128 KB).
 template <int WT, int BK>
-constexpr int w16_stages() { return BK == kBE4M3 ? 3 : (WT == 4 ? 2 : 3); }
+constexpr int w16_stages() { return BK == kBE4M3 ? 3 : (WT == 4 ? 4 : 3); }
 
 // A rows: 8 chunks of 16 bytes, XOR-permuted by (row >> 1) & 7 so that the 32
 // rows a half-wave reads at one chunk spread over the banks.
@@ -109,6 +120,10 @@ template <int WT, int BK>
 __device__ __forceinline__ void w16_read(W16Frags<WT>& F, const uint8_t* sl, int o, int h, int wm, int wn, int fr,
                                          int fh) {
   using T = W16Tile<WT, BK>;
+  // byte offset of chunk (2h + fh) * 2 + q of a 16-bit row
+  auto at16 = [](int row, int q, int h, int fh) {
+    return T::kKS == 32 ? swz64(row, 2 * fh + q) : swz_a128(row, 4 * h + 2 * fh + q);
+  };
   if (o < T::kBReads) {
     if constexpr (BK == kBE4M3) {
       const int row = wn * 32 * WT + 32 * o + fr;
@@ -116,12 +131,12 @@ __device__ __forceinline__ void w16_read(W16Frags<WT>& F, const uint8_t* sl, int
     } else {
       const int j = o >> 1, q = o & 1;
       const int row = wn * 32 * WT + 32 * j + fr;
-      F.b[j][q] = *reinterpret_cast<const v4i*>(sl + T::kABytes + swz_a128(row, 4 * h + 2 * fh + q));
+      F.b[j][q] = *reinterpret_cast<const v4i*>(sl + T::kABytes + at16(row, q, h, fh));
     }
   } else {
     const int a = o - T::kBReads, i = a >> 1, q = a & 1;
     const int row = wm * 32 * WT + 32 * i + fr;
-    F.a[i][q] = *reinterpret_cast<const v4i*>(sl + swz_a128(row, 4 * h + 2 * fh + q));
+    F.a[i][q] = *reinterpret_cast<const v4i*>(sl + at16(row, q, h, fh));
   }
 }
 
@@ -142,7 +157,7 @@ __device__ __forceinline__ void w16_issue_one(uint8_t* lds, int kt, int nk, int 
   uint8_t* st = lds + (kt % S) * T::kStage;
   const uint32_t k0 = static_cast<uint32_t>(min(kt, nk - 1));
   if (d < T::kALoads)
-    w16_dma(ra, st + (wave * T::kALoads + d) * 1024, a_off[d], k0 * 128u);
+    w16_dma(ra, st + (wave * T::kALoads + d) * 1024, a_off[d], k0 * static_cast<uint32_t>(T::kARow));
   else
     w16_dma(rb, st + T::kABytes + (wave * T::kBLoads + d - T::kALoads) * 1024, b_off[d - T::kALoads],
             k0 * static_cast<uint32_t>(T::kBRow));
@@ -204,7 +219,8 @@ __global__ __launch_bounds__(256, BK == kBE4M3 ? 4 / WT : 1) void k_w8a16_gemm(c
   static_assert(sizeof(lds) >= kEpiLds + 4, "epilogue LDS and arrival flag");
   int* const s_last = reinterpret_cast<int*>(lds + kEpiLds);
 
-  const int nk_all = K / 64;
+  constexpr int KS = T::kKS;
+  const int nk_all = K / KS;
   int tm, tn, kb = 0, ke = nk_all;
   int slot = -1, sk_tile = 0, R = 0;
   if (static_cast<int>(blockIdx.x) < dp_tiles) {
@@ -230,23 +246,32 @@ __global__ __launch_bounds__(256, BK == kBE4M3 ? 4 / WT : 1) void k_w8a16_gemm(c
 #pragma unroll
   for (int j = 0; j < WT; ++j) sc[j] = BK == kBE4M3 ? sw[min(n0 + wn * 32 * WT + 32 * j + fr, N - 1)] : 1.0f;
 
-  // DMA sources, as byte offsets into X and Wq8. A: load d of wave w covers
-  // rows (w*kALoads + d)*8 + lane/8, LDS slot (lane & 7) holding chunk
-  // (lane & 7) ^ ((row >> 1) & 7). B: rows (w*kBLoads + d)*16 + lane/4, slot
-  // (lane & 3) holding chunk (lane & 3) ^ swz_term(row).
+  // DMA sources, as byte offsets into X and Wq8. 128-byte rows (16-bit, 64
+  // values per step): load d of wave w covers rows (w*loads + d)*8 + lane/8,
+  // LDS slot (lane & 7) holding chunk (lane & 7) ^ ((row >> 1) & 7). 64-byte
+  // rows (E4M3 B, or 16-bit at 32 values per step): rows (w*loads + d)*16 +
+  // lane/4, slot (lane & 3) holding chunk (lane & 3) ^ swz_term(row).
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(A), 0, static_cast<int>(static_cast<uint32_t>(M) * static_cast<uint32_t>(K) * 2u),
       kRawBuffer);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(B), 0,
       static_cast<int>(static_cast<uint32_t>(N) * static_cast<uint32_t>(K) * (BK == kBE4M3 ? 1u : 2u)), kRawBuffer);
+  // byte offset of this lane's 16-byte chunk for load d of a 16-bit operand
+  auto off16 = [&](int row0, int rows, int d, int loads) -> uint32_t {
+    int r, ch;
+    if constexpr (KS == 32) {
+      r = (wave * loads + d) * 16 + (lane >> 2);
+      ch = (lane & 3) ^ swz_term(r);
+    } else {
+      r = (wave * loads + d) * 8 + (lane >> 3);
+      ch = (lane & 7) ^ ((r >> 1) & 7);
+    }
+    return (static_cast<uint32_t>(min(row0 + r, rows - 1)) * static_cast<uint32_t>(K) + kb * KS) * 2u + ch * 16;
+  };
   uint32_t a_off[T::kALoads], b_off[T::kBLoads];
 #pragma unroll
-  for (int d = 0; d < T::kALoads; ++d) {
-    const int r = (wave * T::kALoads + d) * 8 + (lane >> 3);
-    const int ch = (lane & 7) ^ ((r >> 1) & 7);
-    a_off[d] = (static_cast<uint32_t>(min(m0 + r, M - 1)) * static_cast<uint32_t>(K) + kb * 64) * 2u + ch * 16;
-  }
+  for (int d = 0; d < T::kALoads; ++d) a_off[d] = off16(m0, M, d, T::kALoads);
 #pragma unroll
   for (int d = 0; d < T::kBLoads; ++d) {
     if constexpr (BK == kBE4M3) {
@@ -254,9 +279,7 @@ __global__ __launch_bounds__(256, BK == kBE4M3 ? 4 / WT : 1) void k_w8a16_gemm(c
       const int ch = (lane & 3) ^ swz_term(r);
       b_off[d] = static_cast<uint32_t>(min(n0 + r, N - 1)) * static_cast<uint32_t>(K) + kb * 64 + ch * 16;
     } else {                                    // 16-bit rows: the layout of A
-      const int r = (wave * T::kBLoads + d) * 8 + (lane >> 3);
-      const int ch = (lane & 7) ^ ((r >> 1) & 7);
-      b_off[d] = (static_cast<uint32_t>(min(n0 + r, N - 1)) * static_cast<uint32_t>(K) + kb * 64) * 2u + ch * 16;
+      b_off[d] = off16(n0, N, d, T::kBLoads);
     }
   }
   const int nk = ke - kb;
@@ -282,6 +305,26 @@ __global__ __launch_bounds__(256, BK == kBE4M3 ? 4 / WT : 1) void k_w8a16_gemm(c
     for (int j = 0; j < WT; ++j) w16_widen<WT>(f0, j, sc[j]);
   }
 
+  if constexpr (T::kSub == 1) {
+    // one sub-step per K step: wait for step kt+1 (all waves) and for every
+    // wave to be done reading step kt's slot, then multiply step kt while
+    // reading step kt+1's fragments and loading step kt+S into the retired
+    // slot. The last step runs the same code: its reads stay in the ring, and
+    // its loads repeat the last step into its own slot, which no later step reads.
+    auto body = [&](const W16Frags<WT>& C, W16Frags<WT>& Nx, int kt) {
+      wait_lgkmcnt<0>();
+      wait_vmcnt<(S - 2) * T::kLoads>();
+      block_barrier();
+      w16_phase<WT, BK, S, true>(C, Nx, acc, lds + ((kt + 1) % S) * T::kStage, 0, wm, wn, fr, fh, sc, lds, kt + S,
+                                 nk, ra, rb, a_off, b_off, wave);
+    };
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      body(f0, f1, kt);
+      body(f1, f0, kt + 1);
+    }
+    if (kt < nk) body(f0, f1, kt);
+  } else {
   for (int kt = 0; kt < nk - 1; ++kt) {
     const uint8_t* sa = lds + (kt % S) * T::kStage;
     // sub-step 0 multiplies while sub-step 1's fragments are read
@@ -312,6 +355,7 @@ __global__ __launch_bounds__(256, BK == kBE4M3 ? 4 / WT : 1) void k_w8a16_gemm(c
       const int i = t / (2 * WT), j = (t / 2) % WT, q = t & 1;
       acc[i][j] = mfma16<BK>(f1.b[j][q], f1.a[i][q], acc[i][j]);
     }
+  }
   }
   wait_lgkmcnt<0>();
   wait_vmcnt<0>();                              // retire the trailing repeat loads
@@ -470,6 +514,65 @@ GemmPlan plan_w8a16_gemm(int64_t M, int64_t N, int64_t K, int cus) {
     }
   }
   return plan_w8a16_gemm_split(M, N, best_s, best_bm);
+}
+
+// Plain 16-bit linear. 256x256 blocks (32-value K steps): the tiles of the
+// device's full waves run whole and the R leftover tiles of the last, partial
+// wave (every tile when there are fewer than the CUs) run as `split` K-slices,
+// so the tail costs 1/split of a tile plus the partial exchange. Model
+// (microseconds, measured at 4352x16384 -> 4096): a 32-value step of a
+// 256x256 block takes kL16Step on its CU while every CU streams, kL16TailStep
+// in a sparse tail wave; the last slice of a cut tile reads the split fp32
+// partials of 256 KB at kL16Part each, after kL16SplitLat. The 128x128 plan
+// of the weight-only model (its byte terms scaled by 4/3 for the 16-bit B
+// rows) is taken when it is cheaper (small outputs).
+constexpr double kL16Step = 1.1;
+constexpr double kL16TailStep = 0.75;
+constexpr double kL16Part = 6.0;
+constexpr double kL16SplitLat = 3.0;
+
+GemmPlan plan_linear16_tail(int64_t M, int64_t N, int split, int cus) {
+  GemmPlan p = plan_w8a16_gemm_split(M, N, 1, 256);
+  const int T = p.tiles_m * p.tiles_n;
+  if (split <= 1) return p;
+  const int R = T % std::max(cus, 1);
+  p.split = split;
+  p.dp_tiles = T - R;
+  p.sk_tiles = R;
+  if (R == 0) p.split = 1;
+  return p;
+}
+
+static double l16_tail_time(int64_t T, int64_t nk, int s, int cus) {
+  const int64_t R = T % cus, full = T / cus;
+  double t = static_cast<double>(full) * nk * kL16Step;
+  if (R > 0) {
+    const double rounds = static_cast<double>((R * s + cus - 1) / cus);
+    t += rounds * static_cast<double>((nk + s - 1) / s) * (R * s >= cus ? kL16Step : kL16TailStep);
+    if (s > 1) t += kL16SplitLat + s * kL16Part;
+  }
+  return t + kW16Fixed;
+}
+
+GemmPlan plan_linear16(int64_t M, int64_t N, int64_t K, int cus) {
+  cus = std::max(cus, 1);
+  const int64_t nk = K / 32;
+  const int64_t T = ((M + 255) / 256) * ((N + 255) / 256);
+  double best_t = 0.0;
+  int best_s = 1;
+  for (int s = 1; s == 1 || (s <= kW16MaxSplit && s * kW16MinSliceSteps <= nk); ++s) {
+    const double t = l16_tail_time(T, nk, s, cus);
+    if (s == 1 || t < best_t) best_t = t, best_s = s;
+  }
+  const int64_t nk64 = K / 64;
+  double best128 = 0.0;
+  int s128 = 1;
+  for (int s = 1; s == 1 || (s <= kW16MaxSplit && s * kW16MinSliceSteps <= nk64); ++s) {
+    const double t = w16_plan_time(M, N, nk64, 128, s, cus) * (4.0 / 3.0);
+    if (s == 1 || t < best128) best128 = t, s128 = s;
+  }
+  if (best128 < best_t) return plan_w8a16_gemm_split(M, N, s128, 128);
+  return plan_linear16_tail(M, N, best_s, cus);
 }
 
 // K % 64 == 0 (checked by the caller). ydt: 0 bf16, 1 fp16, 2 fp32. `part` /

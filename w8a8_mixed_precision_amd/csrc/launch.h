@@ -68,8 +68,11 @@ GemmPlan plan_w8a16_gemm_split(int64_t M, int64_t N, int split, int bm);
 void launch_w8a16_gemm(const uint16_t* A, const uint8_t* B, int64_t M, int64_t N, int64_t K, const float* sw,
                        void* Y, int ydt, const GemmPlan& plan, float* part, int* cnt, hipStream_t s);
 // Plain 16-bit linear (X and W both bf16 or both f16), K % 64 == 0, on the
-// weight-only kernel; plans from plan_w8a16_gemm* (the operand bytes differ
-// but the tiling trade-offs are alike).
+// weight-only kernel: plan_linear16 (the device's own choice), or
+// plan_linear16_tail (256x256 blocks, the leftover tiles of the last partial
+// wave in `split` K-slices) / plan_w8a16_gemm_split(.., 128).
+GemmPlan plan_linear16(int64_t M, int64_t N, int64_t K, int cus);
+GemmPlan plan_linear16_tail(int64_t M, int64_t N, int split, int cus);
 void launch_linear16(const uint16_t* A, const uint16_t* B, bool bf16, int64_t M, int64_t N, int64_t K, void* Y,
                      int ydt, const GemmPlan& plan, float* part, int* cnt, hipStream_t s);
 
