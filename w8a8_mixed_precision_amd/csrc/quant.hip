@@ -259,6 +259,7 @@ __global__ __launch_bounds__(256) void k_outlier_fixup(
   __shared__ uint32_t somax[kFixRows];       // per row: largest gathered magnitude <= t
   __shared__ float ssx[kFixRows];            // per row: provisional scale
   __shared__ float srstd[kFixRows];          // per row: RMSNorm rstd (producer kProdRms)
+  __shared__ uint64_t sredo[1];              // rows to re-encode (bit r: row r of the block)
   const int nwords = (K + 31) >> 5;
   uint32_t* smask = smem;
   int* spre = reinterpret_cast<int*>(smem + nwords);
@@ -391,10 +392,19 @@ __global__ __launch_bounds__(256) void k_outlier_fixup(
     __syncthreads();
     // A row whose provisional scale is also reached in an outlier column may
     // have a smaller true scale: recompute it over the non-outlier columns
-    // and re-encode the whole row.
-    for (int r = 0; r < rows; ++r) {
-      const float sp = ssx[r];
-      if (!(sp > 0.0f) || somax[r] != mag_bits<BF16>(sp)) continue;   // block-uniform
+    // and re-encode the whole row. The rows are tested all at once (one lane
+    // per row, kFixRows == 64 == one wave's ballot); the loop visits only the
+    // rows found, instead of paying two dependent LDS reads for every row.
+    static_assert(kFixRows == 64, "one ballot bit per row");
+    if (wave == 0) {
+      const float sp = lane < rows ? ssx[lane] : 0.0f;
+      const bool redo = sp > 0.0f && somax[lane] == mag_bits<BF16>(sp);
+      const uint64_t m = __ballot(redo);
+      if (lane == 0) sredo[0] = m;
+    }
+    __syncthreads();
+    for (uint64_t todo = sredo[0]; todo != 0; todo &= todo - 1) {
+      const int r = __builtin_ctzll(todo);       // block-uniform
       const int64_t rowoff = static_cast<int64_t>(r0 + r) * K;
       const uint4* xr = reinterpret_cast<const uint4*>(X + rowoff);
       uint2* qr = reinterpret_cast<uint2*>(q + rowoff);
