@@ -229,13 +229,16 @@ __global__ __launch_bounds__(256) void k_int8_rows_long(const uint16_t* __restri
 
 // --------------------------------------------------------------------------
 // Block roles: blocks [0, xblocks) take kFixRows rows of X each; the rest take
-// kFixRows rows of Wq each (only when WO != nullptr). Every block rebuilds the
+// kFixWRows rows of Wq each (only when WO != nullptr). X blocks are small so
+// that the rare rows to re-encode (a full pass over the row each, about 12 us
+// on one CU with a GELU producer at K = 16384) seldom share a block. Every block rebuilds the
 // ascending outlier list from the flags (a bit mask and its popcount prefix in
 // LDS), then spreads (row, outlier slot) pairs over all threads, so the
 // scattered loads of a block are all in flight together. Dynamic LDS: mask
 // words, their exclusive popcount prefix, and the outlier list (up to kOcap
 // entries; a larger set takes the per-row loops).
-constexpr int kFixRows = 64;
+constexpr int kFixRows = 16;
+constexpr int kFixWRows = 64;
 constexpr int kOcap = 4096;
 constexpr int kGatherUnroll = 8;
 
@@ -393,12 +396,15 @@ __global__ __launch_bounds__(256) void k_outlier_fixup(
     // A row whose provisional scale is also reached in an outlier column may
     // have a smaller true scale: recompute it over the non-outlier columns
     // and re-encode the whole row. The rows are tested all at once (one lane
-    // per row, kFixRows == 64 == one wave's ballot); the loop visits only the
-    // rows found, instead of paying two dependent LDS reads for every row.
-    static_assert(kFixRows == 64, "one ballot bit per row");
+    // per row, one wave's ballot); the loop visits only the rows found,
+    // instead of paying two dependent LDS reads for every row.
+    static_assert(kFixRows <= 64, "one ballot bit per row");
     if (wave == 0) {
-      const float sp = lane < rows ? ssx[lane] : 0.0f;
-      const bool redo = sp > 0.0f && somax[lane] == mag_bits<BF16>(sp);
+      bool redo = false;
+      if (lane < rows) {
+        const float sp = ssx[lane];
+        redo = sp > 0.0f && somax[lane] == mag_bits<BF16>(sp);
+      }
       const uint64_t m = __ballot(redo);
       if (lane == 0) sredo[0] = m;
     }
@@ -474,8 +480,8 @@ __global__ __launch_bounds__(256) void k_outlier_fixup(
       if (tid == 0) sx[r0 + r] = best;
     }
   } else if (WO) {
-    const int r0 = (blockIdx.x - xblocks) * kFixRows;
-    const int rows = min(kFixRows, N - r0);
+    const int r0 = (blockIdx.x - xblocks) * kFixWRows;
+    const int rows = min(kFixWRows, N - r0);
     auto cvt = [](int8_t v) -> uint16_t {
       const float f = static_cast<float>(v);  // |v| <= 127: exact in both 16-bit types
       return BF16 ? static_cast<uint16_t>(__float_as_uint(f) >> 16) : f32_to_f16_bits(f);
@@ -684,7 +690,7 @@ static void launch_fixup_t(const uint16_t* X, int64_t M, int K, uint32_t tbits, 
                            float* sx, int* O, int* nO, uint16_t* XO, const int8_t* Wq, int64_t N, uint16_t* WO,
                            const ProdArgs& pa, hipStream_t s) {
   const int xblocks = static_cast<int>((M + kFixRows - 1) / kFixRows);
-  const int wblocks = WO ? static_cast<int>((N + kFixRows - 1) / kFixRows) : 0;
+  const int wblocks = WO ? static_cast<int>((N + kFixWRows - 1) / kFixWRows) : 0;
   const size_t lds = outlier_fixup_lds_bytes(K);
   const dim3 grid(xblocks + wblocks), block(256);
   k_outlier_fixup<BF16, PROD><<<grid, block, lds, s>>>(X, (int)M, K, tbits, colflag, q, sx, O, nO, XO, Wq, (int)N, WO,
