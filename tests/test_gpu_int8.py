@@ -271,18 +271,22 @@ def test_deterministic_non_default_stream_and_no_out_of_bounds_writes():
 
 
 # ----------------------------------------------------------------------------
-# the DiT workloads at full size, in the configuration bench.py times
+# the DiT workloads at full size: 1024^2 in the configuration bench.py times,
+# and 2048^2 (16640 tokens)
 # ----------------------------------------------------------------------------
 
 FULL = {
     "dit1024_qkv": synth.dit_qkv_1024,
     "dit1024_mlp_up": lambda: synth.dit_mlp_1024("up"),
     "dit1024_mlp_down": lambda: synth.dit_mlp_1024("down"),
+    "dit2048_qkv": lambda: synth.dit_2048("qkv"),
+    "dit2048_mlp_up": lambda: synth.dit_2048("up"),
+    "dit2048_mlp_down": lambda: synth.dit_2048("down"),
 }
 
 
 @pytest.mark.parametrize("name", list(FULL))
-def test_dit_1024_full_size(name):
+def test_dit_full_size(name):
     c = FULL[name]()
     announce("full-size", c.name)
     xf = o.decode16(c.x_bits, "bf16")
