@@ -15,9 +15,12 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int kBM = 256, kBN = 256, kBK = 64;
 
 // LDS byte offset of logical 16-byte chunk `ch` (0..3) of tile row `row`
-// (64 bytes per row). The XOR term makes the fragment reads (32 rows at one
-// chunk per half-wave) hit distinct banks in every 8- and 16-lane group.
-__device__ __forceinline__ int swz_term(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// (64 bytes per row). The fragment reads take 32 consecutive rows at one
+// chunk per half-wave; XOR-ing the chunk with (row >> 2) & 3 makes them free
+// of bank conflicts on gfx950 (measured with the SQ_LDS_BANK_CONFLICT counter:
+// 0% of the LDS-active cycles, against 50% for ((row >> 1) ^ (row >> 3)) & 3,
+// 50% for (row >> 1) & 3 and 75% for row & 3 or no XOR).
+__device__ __forceinline__ int swz_term(int row) { return (row >> 2) & 3; }
 __device__ __forceinline__ int swz64(int row, int ch) { return row * kBK + ((ch ^ swz_term(row)) << 4); }
 
 // XCD-aware block order: the hardware deals consecutive workgroups round-robin
