@@ -389,8 +389,8 @@ def main() -> int:
                     help="counter-collection mode: a few int8 steps, then plain copies of MIB MiB; no JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the sharding design is "
-              "described in DESIGN.md, not built).", file=sys.stderr)
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported: the library has no "
+              "multi-GPU path (the linear would shard along N with no exchange).", file=sys.stderr)
         return 2
 
     import numpy as np

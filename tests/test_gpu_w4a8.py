@@ -5,7 +5,7 @@ Bit-exact: the packed int4 codes and group scales of quantize_weight_rowwise
 (fmt "int4"), and the whole contraction on inputs whose result is exact in
 fp32 (integer codes, power-of-two scales). Outputs otherwise: relative
 Frobenius error, globally and per row, <= 1e-2 for 16-bit outputs and
-<= 2e-3 for fp32 (the benchmark spec's bounds), fp32 also within 1e-5.
+<= 2e-3 for fp32 (the stated output bounds of the linear), fp32 also within 1e-5.
 """
 import numpy as np
 import pytest

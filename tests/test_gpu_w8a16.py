@@ -5,7 +5,7 @@ Bit-exact: the dequantised bf16 weight of every finite E4M3 code (read back
 through one-hot activation rows, where each output is a single product).
 Outputs: relative Frobenius error, globally and per row, <= 1e-2 for 16-bit
 outputs (their rounding alone is 2^-9 relative per element for bf16) and
-<= 2e-3 for fp32 (the benchmark spec's bounds); fp32 outputs additionally within 1e-5,
+<= 2e-3 for fp32 (the stated output bounds of the linear); fp32 outputs additionally within 1e-5,
 the size of fp32 accumulation error over these K.
 """
 import numpy as np
