@@ -1,6 +1,7 @@
 // C ABI of libw8mp: argument validation, workspace carve-up, kernel dispatch.
 // Declarations and contracts: include/w8mp.h.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <cstdarg>
@@ -63,15 +64,19 @@ w8_status check_mk(int64_t M, int64_t K, int64_t maxK) {
 }
 
 // Compute units of the current device (cached per device); the GEMM plan
-// depends on it, so workspace sizes are per device.
+// depends on it, so workspace sizes are per device. Threads may race to fill
+// an entry; they all store the same value, and the atomics keep that defined.
 int cu_count() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (dev < 64) cache[dev] = n;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
