@@ -311,7 +311,7 @@ def quantize_activations_fp8(xf: np.ndarray, act_scale=None):
     all zero on rows whose scale is 0."""
     xf = np.asarray(xf, dtype=F32)
     sx = fp8_activation_scales(xf, act_scale)
-    with np.errstate(divide="ignore", invalid="ignore"):
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
         ratio = xf / sx[:, None]
     ratio = np.where((sx == 0)[:, None], F32(0.0), ratio).astype(F32)
     codes = e4m3_encode(ratio)
