@@ -169,3 +169,36 @@ def test_error_metric_definitions():
     assert math.isclose(o.relative_l2(2 * a, a), 1.0)
     assert math.isclose(o.mean_token_cosine(a, 3 * a), 1.0)
     assert math.isclose(o.mean_token_cosine(a, -a), -1.0)
+
+
+def test_weight_scale_is_rounded_to_nearest_even_bf16():
+    """The per-channel scale is stored as bf16 ("Qwen-Image-2.1 Text Encoder:
+    FP8" card, section "Format"): sw = bf16(fl32(amax / 448)), round to
+    nearest even, and the codes use that rounded scale.
+
+    amax = 65/64 gives fl32(amax/448) = 0x3B149249, whose low half is above
+    the bf16 midpoint: round to nearest gives 0x3B15 (0.0022735595703125),
+    truncation would give 0x3B14. A row of amax = 1.0 has fl32(1/448) =
+    0x3B12_4925 (below the midpoint, rounds down either way). The expected
+    scales come from exact rationals and from torch's own fp32 -> bf16 cast;
+    the expected codes from torch's float8_e4m3fn cast of fl32(w / sw)."""
+    from fractions import Fraction
+    from tests.exact import to_bf16, to_f32
+
+    w_rows = np.array([[65 / 64, 0.002197265625, 0.002685546875, -0.00439453125, 0.0087890625, 0.0],
+                       [1.0, 0.5, -0.25, 0.125, -0.0625, 2.0 ** -12]], np.float32)
+    codes, sw = o.quantize_weight_fp8(w_rows)
+    want = []
+    for row in w_rows:
+        amax = Fraction(float(np.abs(row).max()))
+        want.append(float(to_bf16(to_f32(amax / 448))))
+    assert sw.tolist() == want
+    assert sw[0] == np.float32(0.0022735595703125)               # 0x3B15, not the truncated 0x3B14
+    s32 = (np.abs(w_rows).max(axis=1) / np.float32(448)).astype(np.float32)
+    tb = torch.from_numpy(s32).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(sw, tb)
+    ratio = (w_rows / sw[:, None]).astype(np.float32)
+    assert np.array_equal(codes, torch_e4m3(ratio))
+    # with the rounded scale these weights take the codes below; a truncated
+    # scale would move each of the four non-top entries up by one code
+    assert codes[0, :5].tolist() == [0x7E, 0x37, 0x39, 0xBF, 0x47]
