@@ -32,6 +32,76 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 THRESHOLD = 6.0
 
 
+class HipEvents:
+    """A pool of HIP events (host objects made with hipEventCreate through
+    ctypes) for the library's event-recording exports, which record them on
+    the stream their kernels run on."""
+
+    def __init__(self, n: int):
+        import ctypes
+
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(e.value)
+
+    def group(self, i: int, k: int = 4):
+        return self.ev[k * i: k * i + k]
+
+    def ms(self, a, b) -> float:
+        t = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(t), self.ct.c_void_p(a), self.ct.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(t.value)
+
+    def sync(self, e) -> None:
+        self.hip.hipEventSynchronize(self.ct.c_void_p(e))
+
+    def close(self) -> None:
+        for e in self.ev:
+            self.hip.hipEventDestroy(self.ct.c_void_p(e))
+        self.ev = []
+
+
+def staged_int8(w8, ev, args_list, steps: int):
+    """`steps` rounds over the calls in args_list (x, wq, sw, y, ws), each call
+    recording 4 events (start, after the row pass, after the fix-up, after the
+    GEMM). Returns per call index a list of [row, fixup, gemm] ms per round."""
+    n = len(args_list)
+    for r in range(steps):
+        for i, (x, wq, sw, y, ws) in enumerate(args_list):
+            w8.debug_int8_mixed_linear_events(x, wq, sw, THRESHOLD, ev.group(r * n + i), y, ws)
+    ev.sync(ev.ev[4 * steps * n - 1])
+    out = [[] for _ in range(n)]
+    for r in range(steps):
+        for i in range(n):
+            e = ev.group(r * n + i)
+            out[i].append([ev.ms(e[0], e[1]), ev.ms(e[1], e[2]), ev.ms(e[2], e[3])])
+    return out
+
+
+def _median(v):
+    import numpy as np
+
+    return float(np.median(np.asarray(v, dtype=np.float64)))
+
+
+def _call_ms(torch, fn, steps: int):
+    """Per-call GPU time (ms) of `steps` calls of fn, each bracketed by events
+    on torch's current stream (where the library launches)."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    ev[-1][1].synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
 def _dev16(bits, torch):
     import numpy as np
 
@@ -68,49 +138,61 @@ def cpu_baseline(cases, rows: int):
 
 
 def fp8_layers(torch, w8, steps: int) -> dict:
-    """FP8-E4M3 W8A8 text-encoder linears at 512 tokens, per layer and
-    activation-scale mode: whole-call, row-pass and GEMM time from the HIP-event
-    hook, GEMM TFLOP/s and the GEMM's fraction of its roofline
-    max(2MNK / 5.0 PFLOP/s, bytes / 8 TB/s), bytes = M K + N K + 2 M N."""
+    """FP8-E4M3 W8A8 linears, per layer and activation-scale mode: medians over
+    `steps` calls of the whole call, the activation pass and the GEMM, from
+    HIP events the library records between its kernels; GEMM TFLOP/s and the
+    GEMM's fraction of its roofline max(2MNK / 5.0 PFLOP/s, bytes / 8 TB/s),
+    bytes = M K + N K + 2 M N. The 512-token text-encoder layers, and the DiT
+    1024^2 QKV and MLP-up shapes (4352 tokens) under a static per-tensor scale
+    (the ModelOpt FP8 card's DiT recipe)."""
     import synth
 
     res = {}
-    for layer in synth.FP8_TEXT_LAYERS:
-        c = synth.fp8_text_encoder(layer)
+    cases = [(synth.fp8_text_encoder(layer), ("dynamic", "static")) for layer in synth.FP8_TEXT_LAYERS]
+    cases += [(synth.dit_qkv_1024(), ("static",)), (synth.dit_mlp_1024("up"), ("static",))]
+    ev = HipEvents(4 * steps)
+    for c, modes in cases:
         x = _dev16(c.x_bits, torch)
         wq, sw = w8.quantize_weight_rowwise(_dev16(c.w_bits, torch), "fp8")
         y = torch.empty((c.M, c.N), dtype=torch.bfloat16, device="cuda")
         ws = w8.new_workspace(w8.fp8_w8a8_linear_workspace_size(c.M, c.N, c.K))
         # static per-tensor input scale: "max" calibration on an independent draw
-        xcal = _dev16(c.extra["x_cal_bits"], torch).float()
+        cal = c.extra["x_cal_bits"] if "x_cal_bits" in c.extra else synth.calibration_draw(c.M, c.K, seed=3001)
+        xcal = _dev16(cal, torch).float()
         scale = (xcal.abs().max() / 448.0).reshape(1).contiguous()
-        for mode, act in (("dynamic", None), ("static", scale)):
+        del xcal
+        for mode in modes:
+            act = scale if mode == "static" else None
             for _ in range(3):
                 w8.fp8_w8a8_linear(x, wq, sw, act, out=y, workspace=ws)
-            w8.profile_start(steps)
-            for _ in range(steps):
-                w8.fp8_w8a8_linear(x, wq, sw, act, out=y, workspace=ws)
-            ms, n = w8.profile_stop()
-            gemm_us = ms[2] / n * 1e3
-            rows_us = ms[0] / n * 1e3
+            for i in range(steps):
+                w8.debug_fp8_w8a8_linear_events(x, wq, sw, act, ev.group(i), y, ws)
+            ev.sync(ev.ev[4 * steps - 1])
+            st = [[ev.ms(e[0], e[1]), ev.ms(e[2], e[3])] for e in (ev.group(i) for i in range(steps))]
+            rows_us = _median([a for a, _ in st]) * 1e3
+            gemm_us = _median([b for _, b in st]) * 1e3
             gbytes = c.M * c.K + c.N * c.K + 2 * c.M * c.N
             t_roof = max(c.ops / (PEAK_FP8_TFLOPS * 1e12), gbytes / (PEAK_HBM_GBS * 1e9)) * 1e6
-            res[f"{layer}_{c.M}x{c.K}x{c.N}_{mode}"] = {
-                "call_us": round(sum(ms) / n * 1e3, 2),
+            key = f"{c.name}_{mode}"
+            res[key] = {
+                "call_us": round(_median([a + b for a, b in st]) * 1e3, 2),
                 "act_quant_us": round(rows_us, 2),
                 "act_quant_GBs": round(3 * c.M * c.K / (rows_us * 1e-6) / 1e9, 1),
                 "gemm_us": round(gemm_us, 2),
                 "gemm_tflops": round(c.ops / (gemm_us * 1e-6) / 1e12, 1),
+                "gemm_pct_fp8_peak": round(100 * c.ops / (gemm_us * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 2),
                 "gemm_roofline_us": round(t_roof, 2),
                 "gemm_roofline_frac": round(t_roof / gemm_us, 3),
             }
-            print(f"[bench] fp8 {layer} {mode}: {res[f'{layer}_{c.M}x{c.K}x{c.N}_{mode}']}", file=sys.stderr, flush=True)
+            print(f"[bench] fp8 {key}: {res[key]}", file=sys.stderr, flush=True)
+        del x, wq, y, ws
+    ev.close()
     return res
 
 
 def w8a16_layers(torch, w8, steps: int) -> dict:
-    """FP8 weight-only (W8A16) text-encoder linears at 512 tokens: GEMM time
-    from the HIP-event hook (the whole call is the one GEMM kernel), TFLOP/s
+    """FP8 weight-only (W8A16) text-encoder linears at 512 tokens: median GEMM
+    time from events around each call (the call is the one GEMM kernel), TFLOP/s
     and the fraction of its roofline max(2MNK / 2.5 PFLOP/s bf16,
     bytes / 8 TB/s), bytes = 2 M K + N K + 2 M N (bf16 X, E4M3 W, bf16 Y)."""
     import synth
@@ -124,11 +206,7 @@ def w8a16_layers(torch, w8, steps: int) -> dict:
         ws = w8.new_workspace(w8.fp8_w8a16_linear_workspace_size(c.M, c.N, c.K))
         for _ in range(3):
             w8.fp8_w8a16_linear(x, wq, sw, out=y, workspace=ws)
-        w8.profile_start(steps)
-        for _ in range(steps):
-            w8.fp8_w8a16_linear(x, wq, sw, out=y, workspace=ws)
-        ms, n = w8.profile_stop()
-        gemm_us = ms[2] / n * 1e3
+        gemm_us = _median(_call_ms(torch, lambda: w8.fp8_w8a16_linear(x, wq, sw, out=y, workspace=ws), steps)) * 1e3
         gbytes = 2 * c.M * c.K + c.N * c.K + 2 * c.M * c.N
         t_roof = max(c.ops / (PEAK_BF16_TFLOPS * 1e12), gbytes / (PEAK_HBM_GBS * 1e9)) * 1e6
         key = f"{layer}_{c.M}x{c.K}x{c.N}"
@@ -144,8 +222,8 @@ def w8a16_layers(torch, w8, steps: int) -> dict:
 
 def w4a8_layers(torch, w8, steps: int) -> dict:
     """W4A8 (int4 per-group weights, int8 per-token activations) on the
-    512-token text-encoder shapes: whole-call, activation-pass and GEMM time
-    from the HIP-event hook, GEMM TOPS and its fraction of the roofline
+    512-token text-encoder shapes: median whole-call time (activation pass and
+    GEMM) from events around each call, TOPS and its fraction of the roofline
     max(2MNK / 5.0 POPS int8, bytes / 8 TB/s), bytes = M K + N K / 2 + 2 M N
     + 4 N K / 128 (codes, packed weights, fp16 Y, group scales)."""
     import synth
@@ -159,21 +237,15 @@ def w4a8_layers(torch, w8, steps: int) -> dict:
         ws = w8.new_workspace(w8.w4a8_linear_workspace_size(c.M, c.N, c.K))
         for _ in range(3):
             w8.w4a8_linear(x, wq, sw, out=y, workspace=ws)
-        w8.profile_start(steps)
-        for _ in range(steps):
-            w8.w4a8_linear(x, wq, sw, out=y, workspace=ws)
-        ms, n = w8.profile_stop()
-        gemm_us = ms[2] / n * 1e3
+        call_us = _median(_call_ms(torch, lambda: w8.w4a8_linear(x, wq, sw, out=y, workspace=ws), steps)) * 1e3
         gbytes = c.M * c.K + c.N * c.K // 2 + 2 * c.M * c.N + 4 * c.N * c.K // 128
         t_roof = max(c.ops / (PEAK_INT8_TOPS * 1e12), gbytes / (PEAK_HBM_GBS * 1e9)) * 1e6
         key = f"{layer}_{c.M}x{c.K}x{c.N}"
         res[key] = {
-            "call_us": round(sum(ms) / n * 1e3, 2),
-            "act_quant_us": round(ms[0] / n * 1e3, 2),
-            "gemm_us": round(gemm_us, 2),
-            "gemm_tops": round(c.ops / (gemm_us * 1e-6) / 1e12, 1),
-            "gemm_roofline_us": round(t_roof, 2),
-            "gemm_roofline_frac": round(t_roof / gemm_us, 3),
+            "call_us": round(call_us, 2),
+            "call_tops": round(c.ops / (call_us * 1e-6) / 1e12, 1),
+            "roofline_us": round(t_roof, 2),
+            "call_roofline_frac": round(t_roof / call_us, 3),
         }
         print(f"[bench] w4a8 {layer}: {res[key]}", file=sys.stderr, flush=True)
     return res
@@ -254,7 +326,8 @@ def fused_mlp(torch, w8, steps: int) -> dict:
     int8_mixed_linear_fused call per layer. Unfused: the library's one-pass
     producer kernel writes X, then the linear reads it. Both timed with events
     on the launch stream over `steps` calls, alternating, best of 3 rounds; the
-    row pass (quantisation) and GEMM stages from the library's HIP-event hook."""
+    fused call's stages (medians) from HIP events the library records between
+    its kernels."""
     import synth
 
     res = {}
@@ -292,14 +365,16 @@ def fused_mlp(torch, w8, steps: int) -> dict:
                 e1.synchronize()
                 us = round(e0.elapsed_time(e1) / steps * 1e3, 2)
                 out[f"{name}_us"] = min(us, out.get(f"{name}_us", us))
-        for name, fn in (("fused", fused), ("unfused", unfused)):
-            w8.profile_start(steps)
-            for _ in range(steps):
-                fn()
-            ms, n = w8.profile_stop()
-            out[f"{name}_quant_us"] = round(ms[0] / n * 1e3, 2)
-            out[f"{name}_fixup_us"] = round(ms[1] / n * 1e3, 2)
-            out[f"{name}_gemm_us"] = round(ms[2] / n * 1e3, 2)
+        ev = HipEvents(4 * steps)
+        for i in range(steps):
+            w8.debug_int8_mixed_linear_events(h, wq, sw, THRESHOLD, ev.group(i), y, ws, bias=bias, producer=prod)
+        ev.sync(ev.ev[-1])
+        st = [[ev.ms(e[0], e[1]), ev.ms(e[1], e[2]), ev.ms(e[2], e[3])] for e in (ev.group(i) for i in range(steps))]
+        ev.close()
+        out["fused_quant_us"] = round(_median([a for a, _, _ in st]) * 1e3, 2)
+        out["fused_fixup_us"] = round(_median([b for _, b, _ in st]) * 1e3, 2)
+        out["fused_gemm_us"] = round(_median([g for _, _, g in st]) * 1e3, 2)
+        out["fused_quant_GBs"] = round(3 * c.M * c.K / (out["fused_quant_us"] * 1e-6) / 1e9, 1)
         # HBM bytes of the quantisation stage: fused reads H and writes codes;
         # unfused also writes X and reads it back
         out["quant_bytes_fused"] = 3 * c.M * c.K
@@ -375,6 +450,113 @@ def gemm_sources_sha256() -> str:
     return h.hexdigest()
 
 
+def shape_timing(torch, w8, c, call, step_stages, steps: int) -> dict:
+    """One shape: stage medians inside the step (the three shapes in turn, so
+    each call finds the last-level cache (MALL, 256 MB) holding the other
+    shapes' data); then the call alone, repeated on the same buffers ("hot")
+    and rotated over three copies of X, Wq and Y whose combined size exceeds
+    the MALL ("cold"), medians of events around each call."""
+    x, wq, sw, y, ws = call
+    rows_bytes = 3 * c.M * c.K            # read X (2 B) + write codes (1 B)
+
+    def med(stages, k):
+        return _median([r[k] for r in stages]) * 1e3
+
+    call_us = _median([sum(r) for r in step_stages]) * 1e3
+    out = {
+        "call_us": round(call_us, 2),
+        "tops": round(c.ops / (call_us * 1e-6) / 1e12, 1),
+        "pct_of_mfma_peak": round(100 * c.ops / (call_us * 1e-6) / 1e12 / PEAK_INT8_TOPS, 2),
+        "row_pass_us": round(med(step_stages, 0), 2),
+        "row_pass_GBs": round(rows_bytes / (med(step_stages, 0) * 1e-6) / 1e9, 1),
+        "fixup_us": round(med(step_stages, 1), 2),
+        "gemm_us": round(med(step_stages, 2), 2),
+        "gemm_tops": round(c.ops / (med(step_stages, 2) * 1e-6) / 1e12, 1),
+    }
+    ev = HipEvents(4 * steps)
+    hot = staged_int8(w8, ev, [call], steps)[0]
+    copies = [(x.clone(), wq.clone(), sw, torch.empty_like(y), ws) for _ in range(3)]
+    cold = []
+    for r in range(0, steps, 3):
+        n = min(3, steps - r)
+        cold += [v[0] for v in staged_int8(w8, ev, copies[:n], 1)]
+    ev.close()
+    del copies
+    for name, stages in (("hot", hot), ("cold", cold)):
+        t = _median([sum(r) for r in stages]) * 1e3
+        out[f"{name}_call_us"] = round(t, 2)
+        out[f"{name}_pct_of_mfma_peak"] = round(100 * c.ops / (t * 1e-6) / 1e12 / PEAK_INT8_TOPS, 2)
+        out[f"{name}_gemm_us"] = round(med(stages, 2), 2)
+    return out
+
+
+def extra_shapes(torch, w8, steps: int) -> dict:
+    """The other int8 workloads, each call timed alone (medians of events
+    around the stages): the DiT 2048^2 linears (16640 tokens) and the tiny
+    64 x 256 -> 512 fp16 linear, which is bound by launch latency."""
+    import synth
+
+    res = {}
+    for c in [synth.dit_2048("qkv"), synth.dit_2048("up"), synth.dit_2048("down"), synth.tiny_int8()]:
+        enc = torch.float16 if c.x_dtype == "f16" else torch.bfloat16
+        import numpy as np
+
+        x = torch.from_numpy(np.ascontiguousarray(c.x_bits).view(np.int16)).view(enc).cuda()
+        w = torch.from_numpy(np.ascontiguousarray(c.w_bits).view(np.int16)).view(enc).cuda()
+        wq, sw = w8.quantize_weight_rowwise(w, "int8")
+        del w
+        y = torch.empty((c.M, c.N), dtype=torch.float16, device="cuda")
+        ws = w8.new_workspace(w8.int8_mixed_linear_workspace_size(c.M, c.N, c.K))
+        ev = HipEvents(4 * steps)
+        staged_int8(w8, ev, [(x, wq, sw, y, ws)], 2)
+        st = staged_int8(w8, ev, [(x, wq, sw, y, ws)], steps)[0]
+        ev.close()
+        t = _median([sum(r) for r in st]) * 1e3
+        g = _median([r[2] for r in st]) * 1e3
+        res[c.name] = {"call_us": round(t, 2), "tops": round(c.ops / (t * 1e-6) / 1e12, 2),
+                       "pct_of_mfma_peak": round(100 * c.ops / (t * 1e-6) / 1e12 / PEAK_INT8_TOPS, 2),
+                       "gemm_us": round(g, 2), "row_pass_us": round(_median([r[0] for r in st]) * 1e3, 2),
+                       "fixup_us": round(_median([r[1] for r in st]) * 1e3, 2)}
+        print(f"[bench] {c.name}: {res[c.name]}", file=sys.stderr, flush=True)
+        del x, wq, y, ws
+    return res
+
+
+def measured_peaks(torch, w8) -> dict:
+    """The chip's attainable rates, measured here: dense MFMA issue (int8,
+    fp8, bf16) with every SIMD busy (the library's peak kernel, median of 5
+    launches) and a device-to-device copy of 2 GiB (median of 5)."""
+    res = {}
+    blocks = 4 * max(torch.cuda.get_device_properties(0).multi_processor_count, 1)
+    for kind, iters in (("int8", 20000), ("fp8", 10000), ("bf16", 20000)):
+        w8.debug_mfma_peak(kind, blocks, 100)
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            _, ops = w8.debug_mfma_peak(kind, blocks, iters)
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        res[f"{kind}_mfma_tops"] = round(ops / _median(ts) / 1e12, 1)
+    n = 2 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ts = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    res["copy_GBs"] = round(2 * n / _median(ts) / 1e9, 1)
+    del src, dst
+    print(f"[bench] measured peaks: {res}", file=sys.stderr, flush=True)
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -385,6 +567,8 @@ def main() -> int:
     ap.add_argument("--no-fp8", action="store_true", help="skip the text-encoder layer timings (FP8 W8A8, FP8 weight-only, W4A8)")
     ap.add_argument("--no-fused", action="store_true", help="skip the producer-fused DiT MLP timings")
     ap.add_argument("--no-block", action="store_true", help="skip the DiT block driver timings")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the measured peaks and the DiT 2048^2 and tiny int8 shapes")
     ap.add_argument("--counters", type=int, default=0, metavar="MIB",
                     help="counter-collection mode: a few int8 steps, then plain copies of MIB MiB; no JSON line")
     args = ap.parse_args()
@@ -430,32 +614,20 @@ def main() -> int:
     tops = ops_step * args.steps / dt / 1e12
     print(f"[bench] timed {args.steps} steps in {dt * 1e3:.2f} ms", file=sys.stderr, flush=True)
 
-    # Second pass over the same K steps with the library's HIP-event hook on:
-    # per-stage GPU time of every call, on the stream the kernels run on.
-    w8.profile_start(args.steps * len(cases))
-    for _ in range(args.steps):
-        step()
-    stage_ms, ncalls = w8.profile_stop()
-    gemm_avg_ms = stage_ms[2] / ncalls
+    # Second pass over the same K steps, every call recording HIP events
+    # between its kernels on the stream they run on: per-stage GPU times.
+    ev = HipEvents(4 * args.steps * len(cases))
+    calls = [(xs[i], wqs[i], sws[i], ys[i], wss[i]) for i in range(len(cases))]
+    st = staged_int8(w8, ev, calls, args.steps)
+    ev.close()
+    gemm_all = [r[2] for per in st for r in per]
+    gemm_avg_ms = sum(gemm_all) / len(gemm_all)
     gemm_tops = (ops_step / len(cases)) / (gemm_avg_ms * 1e-3) / 1e12
     per_shape = {}
     for i, c in enumerate(cases):
-        w8.profile_start(args.steps)
-        for _ in range(args.steps):
-            w8.int8_mixed_linear(xs[i], wqs[i], sws[i], THRESHOLD, out=ys[i], workspace=wss[i])
-        ms, n = w8.profile_stop()
-        call_us = sum(ms) / n * 1e3
-        rows_bytes = 3 * c.M * c.K            # read X (2 B) + write codes (1 B)
-        per_shape[c.name] = {
-            "call_us": round(call_us, 2),
-            "tops": round(c.ops / (call_us * 1e-6) / 1e12, 1),
-            "row_pass_us": round(ms[0] / n * 1e3, 2),
-            "row_pass_GBs": round(rows_bytes / (ms[0] / n * 1e-3) / 1e9, 1),
-            "fixup_us": round(ms[1] / n * 1e3, 2),
-            "gemm_us": round(ms[2] / n * 1e3, 2),
-            "gemm_tops": round(c.ops / (ms[2] / n * 1e-3) / 1e12, 1),
-        }
+        per_shape[c.name] = shape_timing(torch, w8, c, calls[i], st[i], args.steps)
         print(f"[bench] {c.name}: {per_shape[c.name]}", file=sys.stderr, flush=True)
+    del st
 
     out = {
         "metric": METRIC,
@@ -490,6 +662,11 @@ def main() -> int:
         },
         "per_shape": per_shape,
     }
+    if not args.no_extra:
+        out["measured_peak"] = measured_peaks(torch, w8)
+        out["roofline"]["frac_of_measured_peak"] = round(gemm_tops / out["measured_peak"]["int8_mfma_tops"], 4)
+        out["pct_of_measured_mfma_peak"] = round(100.0 * tops / out["measured_peak"]["int8_mfma_tops"], 2)
+        out["other_int8_shapes"] = extra_shapes(torch, w8, max(5, args.steps // 2))
     if not args.no_fp8:
         out["weight_quant"] = weight_quant(torch, w8, cases, max(1, args.steps // 4))
         out["fp8_w8a8"] = {

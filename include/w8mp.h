@@ -40,7 +40,27 @@
  *    w8_last_error() gives a readable detail (thread-local).
  *  - Input values are not inspected: finite inputs are a precondition.
  *  - Results are deterministic: the same inputs give the same bits.
- *  - Concurrent calls on different streams need distinct workspaces.
+ *
+ * Workspaces (every entry point that takes one)
+ *  - A workspace is caller-owned device memory, 256-byte aligned, at least as
+ *    large as the entry point's size query, which depends on (M, N, K) only.
+ *    It must be zero-filled before its first use (e.g. hipMemsetAsync).
+ *  - Every workspace starts with the same fixed region: split-K arrival
+ *    counters, left zero by every call, and the outlier-column flag words of
+ *    the int8 linears, which each call marks with a stamp of its own (a
+ *    per-process call counter, never 0) and never clears. One workspace may
+ *    therefore serve calls of any shapes and entry points one after another,
+ *    without clearing, if it is as large as each call's size query.
+ *  - After a call that returns an error before launching anything (a
+ *    validation status), the workspace is untouched. After W8_ERR_HIP (a
+ *    launch that failed), the workspace still serves later calls: a kernel
+ *    that never ran touched no counter, and flags left by the failed call
+ *    carry its stamp, which no later call uses (until 2^32 - 1 further int8
+ *    calls). A kernel fault leaves the device unusable anyway.
+ *  - Sizes are planned for a 256-CU device (MI355X). On a device whose GEMM
+ *    plan needs more split-K partials than the workspace holds, the call runs
+ *    the same tiles without K-slicing (same results).
+ *  - Calls that may overlap (different streams) need distinct workspaces.
  */
 #ifndef W8MP_H
 #define W8MP_H
@@ -111,14 +131,11 @@ w8_status quantize_weight_rowwise(const void* W, int w_dt, int64_t N, int64_t K,
  *              +inf gives plain vector-wise int8; t < 0 or NaN is rejected.
  *   Y          [M,N] f16 or f32 (y_dt), device, written in full.
  *   workspace  device memory of at least int8_mixed_linear_workspace_size()
- *              bytes, 256-byte aligned. It must be zero-filled before its
- *              first use (e.g. hipMemsetAsync); every call leaves the
- *              bookkeeping it relies on (outlier-column flags, arrival
- *              counters) zero again, so a workspace is reused without
- *              clearing. Do not write to it between calls. The size depends
- *              on the compute-unit count of the device that is current when
- *              it is queried (the GEMM grid is planned per device); query and
- *              call on the same device.
+ *              bytes (see "Workspaces" above). It holds the codes [M,K], the
+ *              scales, the outlier list and the 16-bit outlier operands of up
+ *              to 256 outlier columns; a call with more outlier columns reads
+ *              them from X and Wq in the GEMM instead (same results, slower).
+ *              Do not write to it between calls.
  *
  * What is computed (O = outlier columns, ascending):
  *   sx[m]   = max_{k not in O} |X[m,k]|                     (fp32, exact)
@@ -138,22 +155,26 @@ w8_status int8_mixed_linear(const void* X, int x_dt, int64_t M, int64_t K,
 
 /*
  * The op that produces X, for int8_mixed_linear_fused. X is made from H in the
- * quantisation pass itself and never stored. Each producer is a fixed sequence
- * of fp32 operations, each rounded to nearest even and none fused, so X is
- * well defined element by element. X = that fp32 result rounded to nearest
- * even in H's 16-bit type:
+ * quantisation pass itself and never stored; it is the 16-bit value (H's type)
+ * that a separate producer op would store:
  *   W8_PRODUCER_RMSNORM: RMSNorm (Zhang and Sennrich, 2019) with the
  *     x(1+scale)+shift modulation of adaptive layer norm (Peebles and Xie,
- *     2023). Per row:
+ *     2023), a fixed sequence of fp32 operations, each rounded to nearest
+ *     even and none fused, then rounded to nearest even in H's type. Per row:
  *       ss   = sum_k H[m,k]^2 in fp64 (each square is exact);
  *       rstd = fl32(1 / fl32(sqrt(fl32(fl32(ss/K) + eps))));
  *       x    = fl32(fl32(H*rstd) * fl32(gamma[k] * fl32(1 + scale[k]))) + shift[k].
  *     gamma (NULL: 1), scale (NULL: 0) and shift (NULL: no addition) are fp32
  *     [K] device vectors, 16-byte aligned.
- *   W8_PRODUCER_GELU_TANH: GELU, tanh form (Hendrycks and Gimpel, 2016),
- *     evaluated as H / (1 + exp(-2u)) with u = sqrt(2/pi)(H + 0.044715 H^3).
- *     This equals 0.5 H (1 + tanh u). exp uses Cody-Waite reduction and a
- *     degree-6 Taylor polynomial (about 2 ulp).
+ *     The kernel adds the float64 squares in its own order, which can differ
+ *     from the exactly rounded sum in the last bit of ss; rstd then differs
+ *     from the exact reading only when fl32(ss / K) sits at a rounding
+ *     boundary (both values are correct readings of the definition).
+ *   W8_PRODUCER_GELU_TANH: GELU, tanh form (Hendrycks and Gimpel, 2016):
+ *     X = 0.5 H (1 + tanh(sqrt(2/pi)(H + 0.044715 H^3))) correctly rounded
+ *     (to nearest, ties to even) in H's type. X is a function of the 16-bit
+ *     pattern of H alone; the library reads it from a table of all 65536
+ *     results per format, made when the library is built.
  */
 typedef enum { W8_PRODUCER_NONE = 0, W8_PRODUCER_RMSNORM = 1, W8_PRODUCER_GELU_TANH = 2 } w8_producer_kind;
 typedef struct w8_producer {
@@ -194,11 +215,7 @@ w8_status int8_mixed_linear_fused(const void* H, int h_dt, int64_t M, int64_t K,
  *              scale (must be finite and >= 0; 0 gives zero codes).
  *   Y          [M,N] bf16, f16 or f32, device.
  *   workspace  device memory of at least fp8_w8a8_linear_workspace_size()
- *              bytes (which depends on M, N, K and the current device's
- *              compute-unit count), 256-byte aligned, zero-filled before its
- *              first use. Every call leaves its bookkeeping (split-K arrival
- *              counters) zero again, so a workspace is reused without
- *              clearing; the rest of its contents are scratch.
+ *              bytes (see "Workspaces" above).
  * Codes: xq[m,k] = E4M3FN(fl32(X[m,k] / sx[m])) (saturating), all zero when
  * sx[m] = 0. Y[m,n] = sx[m] * sw[n] * sum_k xq*wq, fp32 accumulation on FP8
  * MFMA, rounded to nearest even into Y. Results are bitwise reproducible for
@@ -230,10 +247,7 @@ w8_status fp8_w8a8_linear(const void* X, int x_dt, int64_t M, int64_t K,
  *              bf16 values); codes 0x7F / 0xFF (NaN) are outside the contract.
  *   Y          [M,N] bf16, f16 or f32, device.
  *   workspace  device memory of at least fp8_w8a16_linear_workspace_size()
- *              bytes (depends on M, N, K and the current device's
- *              compute-unit count; at least 256), 256-byte aligned,
- *              zero-filled before its first use; every call leaves its split-K
- *              arrival counters zero again, the rest is scratch.
+ *              bytes (see "Workspaces" above).
  * Results are bitwise reproducible for a given device (split-K partial sums
  * are added in a fixed order).
  * Requires M, N >= 1, 64 <= K <= 65536, K % 64 == 0 (else W8_ERR_UNSUPPORTED).
@@ -251,9 +265,8 @@ w8_status fp8_w8a16_linear(const void* X, int x_dt, int64_t M, int64_t K,
  *   X          [M,K] f16 or bf16, device.
  *   Wq4, sw4   the W8_Q_INT4_G128 output of quantize_weight_rowwise.
  *   Y          [M,N] bf16, f16 or f32, device.
- *   workspace  at least w4a8_linear_workspace_size() bytes (depends on M, N,
- *              K and the device's CU count), 256-byte aligned, zero-filled
- *              before its first use; calls leave their split-K counters zero.
+ *   workspace  at least w4a8_linear_workspace_size() bytes (see
+ *              "Workspaces" above).
  * Activations are coded per token like int8_mixed_linear with no outlier
  * columns: sx[m] = max_k |X[m,k]|, q = rne(fl32(X * fl32(127/sx))). Each
  * group's int8 x int4 products are summed exactly (int32), the group sum
@@ -292,9 +305,9 @@ w8_status w4a8_linear(const void* X, int x_dt, int64_t M, int64_t K,
  * fp32 [N] or NULL; norm1 / norm2 are RMSNorm producers (kind
  * W8_PRODUCER_RMSNORM, or W8_PRODUCER_NONE to skip the norm). Requires
  * M >= 1, D and F multiples of 64 in [64, 16384], 16-byte aligned X, Y,
- * w_down16 and b_down. The workspace (w8_dit_block_workspace_size bytes,
- * 256-byte aligned, zero-filled before its first use, left reusable) holds
- * the intermediates and one workspace per linear.
+ * w_down16 and b_down. The workspace (w8_dit_block_workspace_size bytes, see
+ * "Workspaces" above) holds one int8 workspace that the four linears share in
+ * turn, then the intermediates.
  */
 typedef struct w8_dit_block {
   int64_t D;                   /* model width: X, Y [M, D] fp16 */
@@ -326,8 +339,8 @@ const char* w8_last_error(void);
  * for none; outlier detection, row scales, int8 codes, outlier fix-up).
  * Outputs (device): q [M,K] int8, sx [M] fp32, outlier_idx [K] int32 (first
  * *n_outliers entries valid, ascending), n_outliers [1] int32. Workspace:
- * w8dbg_int8_quantize_activations_workspace_size(M, K) bytes, zero-filled
- * before first use (left zero by every call). */
+ * w8dbg_int8_quantize_activations_workspace_size(M, K) bytes (the common
+ * front, then the RMSNorm rstd [M] fp32). */
 size_t w8dbg_int8_quantize_activations_workspace_size(int64_t M, int64_t K);
 w8_status w8dbg_int8_quantize_activations(const void* X, int x_dt, int64_t M, int64_t K,
                                           const w8_producer* producer, float threshold,
@@ -408,22 +421,41 @@ w8_status w8dbg_fp8_w8a16_linear(const void* X, int x_dt, int64_t M, int64_t K, 
                                  const float* sw, int64_t N, int split, int tile, void* Y, int y_dt,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
-/* ------------------------------------------------------------------------
- * Measurement hook (process-wide, for benchmarks; not for concurrent use).
- *
- * w8_profile_start(max_calls): from now on, each int8_mixed_linear and
- * fp8_w8a8_linear call (up to max_calls of them) records HIP events on its own
- * stream at its kernel boundaries. Creates the events (host-side HIP objects,
- * no device memory). Returns W8_ERR_INVALID_ARGUMENT if max_calls < 1.
- *
- * w8_profile_stop(stage_ms, n_calls): waits for the recorded events, writes
- * the summed GPU time of each stage in milliseconds -- stage_ms[0]: outlier
- * mask clear + row quantisation pass, stage_ms[1]: outlier fix-up and gather
- * (0 for FP8), stage_ms[2]: the GEMM -- and the number of calls recorded,
- * then destroys the events and turns the hook off.
- * ------------------------------------------------------------------------ */
-w8_status w8_profile_start(int max_calls);
-w8_status w8_profile_stop(double* stage_ms /*[3]*/, int* n_calls);
+/* int8_mixed_linear_fused that also records the caller's HIP events
+ * events[0..3] (hipEvent_t, created by the caller; NULL entries are skipped)
+ * on `stream`: before the row pass, after it, after the outlier fix-up and
+ * after the GEMM. Same arguments, workspace and results otherwise. */
+w8_status w8dbg_int8_mixed_linear_events(const void* H, int h_dt, int64_t M, int64_t K, const w8_producer* producer,
+                                         const int8_t* Wq, const float* sw, const float* bias, int64_t N,
+                                         float threshold, void* Y, int y_dt, void* workspace, size_t workspace_bytes,
+                                         void* const* events, void* stream);
+
+/* fp8_w8a8_linear recording events[0..3]: before the activation pass, after
+ * it (events 1 and 2), after the GEMM. */
+w8_status w8dbg_fp8_w8a8_linear_events(const void* X, int x_dt, int64_t M, int64_t K, const uint8_t* Wq8,
+                                       const float* sw, int64_t N, const float* act_scale, void* Y, int y_dt,
+                                       void* workspace, size_t workspace_bytes, void* const* events, void* stream);
+
+/* Byte offsets in an int8_mixed_linear workspace of shape (M, N, K):
+ * offsets[0..10] = split-K counters, flag words (uint32 [K]), nO (int32), the
+ * outlier list O (int32 [K]), codes q (int8 [M,K]), sx (fp32 [M]), rstd
+ * (fp32 [M]), XO (16-bit [M, P]), WO (16-bit [N, P]), split-K partials, and
+ * the outlier columns XO/WO hold (P = nO padded to 32 when it fits). */
+w8_status w8dbg_int8_workspace_layout(int64_t M, int64_t N, int64_t K, size_t* offsets);
+
+/* Byte offsets in a w8_dit_block workspace of the block's intermediates after
+ * w8_dit_block_forward: offsets[0..6] = qkv, a, o, h, u (fp16), g = GELU(u)
+ * (fp16, written only with the 16-bit down-projection), d (fp16; fp32 with
+ * the 16-bit down-projection). */
+w8_status w8dbg_dit_block_layout(int64_t M, int64_t D, int64_t F, size_t* offsets);
+
+/* Measured MFMA peak (measurement export): `blocks` blocks of 4 waves each
+ * issue `iters` rounds of 4 independent back-to-back MFMAs on register
+ * operands -- kind 0: v_mfma_i32_32x32x32_i8, 1: v_mfma_scale_f32_32x32x64_f8f6f4
+ * (E4M3), 2: v_mfma_f32_32x32x16_bf16 -- and store a checksum per thread in
+ * out[blocks * 256] (device). *ops (host) receives the operations launched
+ * (2 M N K per instruction); the caller times the launch. */
+w8_status w8dbg_mfma_peak(int kind, int blocks, int iters, unsigned* out, double* ops, void* stream);
 
 #ifdef __cplusplus
 }

@@ -202,6 +202,12 @@ def fp8_text_encoder(layer: str, massive: bool = False) -> LinearCase:
                       extra={"x_cal_bits": encode16(x_cal, "bf16")})
 
 
+def calibration_draw(M: int, K: int, seed: int) -> np.ndarray:
+    """An independent N(0,1) bf16 draw [M, K]: the data a per-tensor "max"
+    calibration of a static input scale runs on."""
+    return encode16(_normal(np.random.default_rng(seed), (M, K)), "bf16")
+
+
 def dit_2048(part: str, m_rows: int | None = None) -> LinearCase:
     """DiT at 2048^2: M = 16640 tokens; QKV, MLP up and MLP down; ~0.1% outlier columns.
 

@@ -17,6 +17,9 @@ HEADER = os.path.join(ROOT, "include", "w8mp.h")
 # anything dereferences them.
 A = 0x10000
 WS_BIG = 1 << 40
+# the region every workspace starts with: 4096 split-K counters, then one
+# outlier-flag word per column up to the largest int8 K (256-byte aligned)
+FRONT = 4 * 4096 + (4 * _abi.W8_INT8_MAX_K + 255) // 256 * 256
 
 
 def declared_functions():
@@ -106,7 +109,7 @@ def test_debug_produce_rejects():
 def test_workspace_size_is_exact_boundary():
     lib = _abi.lib()
     need = lib.int8_mixed_linear_workspace_size(64, 32, 256)
-    assert need >= 64 * 256 + 2 * (64 + 32) * 256
+    assert need >= FRONT + 64 * 256 + 2 * (64 + 32) * 256
     assert _int8(ws_bytes=need - 1) == _abi.W8_ERR_WORKSPACE
     assert lib.int8_mixed_linear_workspace_size(0, 32, 256) == 0
     # grows with every dimension
@@ -235,7 +238,7 @@ def test_w8a16_workspace_and_debug_rejects():
     assert lib.fp8_w8a16_linear_workspace_size(512, 4096, 4096) >= 256
     assert lib.fp8_w8a16_linear_workspace_size(0, 4096, 4096) == 0
     assert lib.w8dbg_fp8_w8a16_linear_workspace_size(4, 4, 128, 2, 256) >= 2 * 256 * 256 * 4
-    assert lib.w8dbg_fp8_w8a16_linear_workspace_size(4, 4, 128, 1, 0) == 256
+    assert lib.w8dbg_fp8_w8a16_linear_workspace_size(4, 4, 128, 1, 0) == FRONT    # the common front only
     g = lib.w8dbg_fp8_w8a16_linear
     bf = _abi.W8_DT_BF16
     assert g(A, bf, 4, 128, A, A, 4, -1, 0, A, bf, A, WS_BIG, None) == _abi.W8_ERR_INVALID_ARGUMENT
@@ -284,7 +287,7 @@ def test_debug_exports_reject():
     assert need >= 2 * 256 * 256 * 4                                                        # two fp32 partials
     assert lib.w8dbg_fp8_gemm_workspace_size(4, 4, 128, 2, 128) >= 2 * 128 * 128 * 4
     assert f8(A, A, A, A, 4, 4, 128, 2, 256, A, bf, A, need - 256, None) == _abi.W8_ERR_WORKSPACE
-    assert lib.w8dbg_fp8_gemm_workspace_size(4, 4, 128, 1, 0) == 0
+    assert lib.w8dbg_fp8_gemm_workspace_size(4, 4, 128, 1, 0) == FRONT
 
 
 def test_binding_refuses_without_library(monkeypatch, tmp_path):
@@ -292,3 +295,60 @@ def test_binding_refuses_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_abi, "_lib", None)
     with pytest.raises(ImportError):
         _abi.lib()
+
+
+def test_workspace_layout_has_a_fixed_front():
+    """The split-K counters and the outlier flags sit at the same offsets for
+    every shape (so one workspace serves calls of different shapes), before
+    every shape-dependent region; XO/WO hold a bounded number of outlier
+    columns (not K), so WO of a large weight no longer dwarfs the codes."""
+    lib = _abi.lib()
+    shapes = [(64, 32, 256), (4352, 12288, 4096), (4352, 4096, 16384), (1, 1, 16), (16640, 16384, 4096)]
+    lays = []
+    for M, N, K in shapes:
+        v = (ctypes.c_size_t * 11)()
+        assert lib.w8dbg_int8_workspace_layout(M, N, K, v) == _abi.W8_OK
+        lays.append(list(v))
+    for (M, N, K), (cnt, flags, nO, O, q, sx, rstd, XO, WO, part, cap) in zip(shapes, lays):
+        assert cnt == 0 and flags == 4 * 4096 and nO == FRONT
+        assert flags + 4 * _abi.W8_INT8_MAX_K <= nO
+        assert O >= nO + 4 and q >= O + 4 * K and sx >= q + M * K and rstd >= sx + 4 * M
+        assert XO >= rstd + 4 * M and WO >= XO + 2 * M * cap and part >= WO + 2 * N * cap
+        assert cap == 256
+        assert all(x % 256 == 0 for x in (cnt, flags, nO, O, q, sx, rstd, XO, WO, part))
+        assert lib.int8_mixed_linear_workspace_size(M, N, K) >= part
+    # the 1024^2 MLP-up workspace: about the codes plus 10 MB, not 2 (M + N) K bytes
+    M, N, K = 4352, 16384, 4096
+    assert lib.int8_mixed_linear_workspace_size(M, N, K) < M * K + FRONT + 2 * (M + N) * 256 + 40 * 2 ** 20
+    assert lib.w8dbg_int8_workspace_layout(0, 1, 16, (ctypes.c_size_t * 11)()) == _abi.W8_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_sizes_are_shape_functions():
+    """Size queries depend on (M, N, K) only: they answer without a device
+    (here there is none) and cover the shape's own regions."""
+    lib = _abi.lib()
+    M, N, K = 512, 4096, 4096
+    assert lib.int8_mixed_linear_workspace_size(M, N, K) >= FRONT + M * K + 2 * (M + N) * 256
+    assert lib.fp8_w8a8_linear_workspace_size(M, N, K) >= FRONT + M * K + 4 * M
+    assert lib.fp8_w8a16_linear_workspace_size(M, N, K) >= FRONT
+    assert lib.w4a8_linear_workspace_size(M, N, K) >= FRONT + M * K + 4 * M
+    assert lib.w8_dit_block_workspace_size(4352, 4096, 16384) > lib.int8_mixed_linear_workspace_size(4352, 4096, 16384)
+
+
+def test_events_exports_validate_like_the_linears():
+    lib = _abi.lib()
+    ev = (ctypes.c_void_p * 4)()
+    bf, f16 = _abi.W8_DT_BF16, _abi.W8_DT_F16
+    assert lib.w8dbg_int8_mixed_linear_events(None, bf, 4, 64, None, A, A, None, 4, 6.0, A, f16, A, WS_BIG, ev,
+                                              None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert lib.w8dbg_int8_mixed_linear_events(A, bf, 4, 64, None, A, A, None, 4, 6.0, A, f16, A, 256, ev,
+                                              None) == _abi.W8_ERR_WORKSPACE
+    assert lib.w8dbg_fp8_w8a8_linear_events(A, bf, 4, 64, A, A, 4, None, A, bf, A, 256, ev, None) == \
+        _abi.W8_ERR_WORKSPACE
+    v = (ctypes.c_size_t * 7)()
+    assert lib.w8dbg_dit_block_layout(4352, 4096, 16384, v) == _abi.W8_OK
+    qkv, a, o, h, u, g, d = list(v)
+    M, D, F = 4352, 4096, 16384
+    assert qkv >= lib.int8_mixed_linear_workspace_size(M, D, F)
+    assert a >= qkv + 2 * M * 3 * D and o >= a + 2 * M * D and h >= o + 2 * M * D and u >= h + 2 * M * D
+    assert g >= u + 2 * M * F and d >= g + 2 * M * F

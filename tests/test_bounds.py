@@ -1,0 +1,65 @@
+"""The element-wise bounds of tests/bounds.py on the CPU: they accept the
+oracle's own single rounding and reject an output whose one column carries a
+small scale error (the kind of mistake a norm over a row would miss)."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import w8ref as o
+from tests import bounds as B
+
+
+def _case():
+    c = synth.random_linear(48, 320, 96, seed=71, x_dtype="bf16", outlier_cols=3)
+    wq, sw = o.quantize_weight_int8(o.decode16(c.w_bits, "bf16"))
+    return c, wq, sw
+
+
+def test_half_ulp_values():
+    assert B.half_ulp(np.array([1.0]), "f16")[0] == 2.0 ** -11
+    assert B.half_ulp(np.array([1.5]), "bf16")[0] == 2.0 ** -8
+    assert B.half_ulp(np.array([3.0]), "f32")[0] == 2.0 ** -23
+    assert B.half_ulp(np.array([2.0 ** -20]), "f16")[0] == 2.0 ** -25          # subnormal spacing 2^-24
+    assert B.half_ulp(np.array([0.0]), "bf16")[0] == 2.0 ** -134
+
+
+@pytest.mark.parametrize("out_dtype", ["f16", "f32"])
+def test_int8_bound_accepts_rounding_and_rejects_a_column_error(out_dtype):
+    c, wq, sw = _case()
+    ref = o.int8_mixed_linear(c.x_bits, "bf16", wq, sw, 6.0, out_dtype)
+    assert len(ref["O"]) == 3
+    err = B.int8_err32(ref, c.x_bits, "bf16", wq, sw)
+    B.assert_elementwise(ref["Y"], out_dtype, ref["y"], err, "oracle itself")
+    # one column's weight scale off by 0.8 percent (a norm over a 96-wide
+    # row moves by about 0.1 percent)
+    bad = ref["y"].copy()
+    bad[:, 17] *= 1.008
+    with pytest.raises(AssertionError):
+        B.assert_elementwise(o.round_output(bad, out_dtype), out_dtype, ref["y"], err, "column error")
+
+
+def test_fp8_bound_accepts_rounding_and_rejects_a_column_error():
+    c = synth.random_linear(32, 256, 40, seed=72, x_dtype="bf16")
+    wq8, sw = o.quantize_weight_fp8(o.decode16(c.w_bits, "bf16"))
+    ref = o.fp8_w8a8_linear(c.x_bits, "bf16", wq8, sw, None, "bf16")
+    err = B.fp8_err32(ref, wq8, sw, 256)
+    B.assert_elementwise(ref["Y"], "bf16", ref["y"], err, "oracle itself")
+    bad = ref["y"].copy()
+    bad[:, 3] *= 1.5
+    with pytest.raises(AssertionError):
+        B.assert_elementwise(o.round_output(bad, "bf16"), "bf16", ref["y"], err, "column error")
+
+
+def test_w4a8_and_dense_bounds_accept_the_oracle_rounding():
+    from oracle import w4a8 as o4
+    rng = np.random.default_rng(73)
+    M, K, N = 16, 512, 24
+    x_bits = o.round_to_bf16(rng.standard_normal((M, K)))
+    packed, sw4 = o4.quantize_weight_int4(rng.standard_normal((N, K)).astype(np.float32) * 0.02)
+    ref = o4.w4a8_linear(x_bits, "bf16", packed, sw4, "f16")
+    B.assert_elementwise(ref["Y"], "f16", ref["y"], B.w4a8_err32(ref, sw4), "w4a8")
+    codes, sw = o.quantize_weight_fp8(rng.standard_normal((N, K)).astype(np.float32) * 0.02)
+    r16 = o.fp8_w8a16_linear(x_bits, "bf16", codes, sw, "bf16")
+    err = B.dense_err32(np.abs(o.decode16(x_bits, "bf16").astype(np.float64)),
+                        np.abs(o.decode16(r16["w_bits"], "bf16").astype(np.float64)), r16["y"], K)
+    B.assert_elementwise(r16["Y"], "bf16", r16["y"], err, "w8a16")

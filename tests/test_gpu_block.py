@@ -3,11 +3,13 @@ linear against the CPU oracle (oracle/block.py).
 
 The 16-bit linear: relative Frobenius error <= 1e-5 for fp32 output (fp32
 sums against float64) and <= 1e-2 for 16-bit output. The block: Y within
-1e-2 relative Frobenius, globally and per row (each of the chained linears
-meets 1e-2 on its own output, and Y is dominated by the residual stream),
-at small sizes and at the full DiT 1024^2 size; the full size with the
-library's own weight quantisation is also checked to be finite and not
-constant (the "Qwen-Image-fni8" card's sanity test).
+1e-2 relative Frobenius, globally and per row, at small sizes and at the full
+DiT 1024^2 size; and step by step: every intermediate the driver leaves in its
+workspace (qkv, a, o, h, u, GELU(u) or d) against the oracle's step applied to
+the driver's own input of that step, element by element (tests/bounds.py),
+the attention stub bit-exact. The full size with the library's own weight
+quantisation is also checked to be finite and not constant (the
+"Qwen-Image-fni8" card's sanity test).
 """
 import numpy as np
 import pytest
@@ -15,7 +17,9 @@ import torch
 
 import w8a8_mixed_precision_amd as w8
 from oracle import block as B
+from oracle import producers as P
 from oracle import w8ref as o
+from tests import bounds
 from tests.gpu_util import OUT, announce, dev16, host_stored, rel_fro, row_rel_fro
 
 pytestmark = pytest.mark.gpu
@@ -162,3 +166,114 @@ def test_block_full_size_is_finite_and_not_constant(with16):
     assert torch.isfinite(yf).all() and float(yf.std()) > 0
     # the massive channel survives the block (residual stream)
     assert float(yf[4096, 2276]) > 4000
+
+
+def _f16(t):
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def _check_linear_step(got_bits, h_bits, kind, blk, name, norm, label, rows, rstd=None):
+    """One int8 linear of the block: the oracle's fused linear on the
+    driver's own input h_bits, element by element on `rows`. RMSNorm: with
+    the given rstd (checked against the allowed readings), or with each
+    reading when a row has two."""
+    kw = dict(norm) if norm else {}
+    wq, sw, b = blk[f"wq_{name}"], blk[f"sw_{name}"], blk[f"b_{name}"]
+    cands = [None]
+    if kind == "rmsnorm":
+        h = o.decode16(h_bits, "f16")
+        a, bb = P.rstd_alternatives(h, kw.get("eps", 1e-6))
+        if rstd is not None:
+            assert np.all((rstd == a) | (rstd == bb))
+            cands = [rstd]
+        else:
+            cands = [a] if np.array_equal(a, bb) else [a, bb]
+    ok = np.zeros(len(rows), bool)
+    errs = []
+    for r in cands:
+        x_bits = P.produce(h_bits, "f16", kind, rstd=r, **kw) if kind != "none" else h_bits
+        ref = P.fused_int8_linear(h_bits, "f16", kind, wq, sw, 6.0, b, "f16", rows=rows, x_bits=x_bits, **kw)
+        err = bounds.int8_err32(ref, x_bits[rows], "f16", wq, sw, bias=b)
+        g = o.stored_to_f64(got_bits[rows], "f16")
+        big = np.maximum(np.abs(g), np.abs(ref["y"]))
+        bound = bounds.half_ulp(big, "f16") + 2 * err + 1e-12 * big
+        ok |= np.all(np.abs(g - ref["y"]) <= bound, axis=1)
+        errs.append(float(np.max(np.abs(g - ref["y"]) / bound)))
+    assert ok.all(), (label, np.flatnonzero(~ok)[:10], errs)
+
+
+def _check_residual(got_bits, a_bits, d_values, label):
+    """y = rne16(fl32(a) + fl32(d)): within half an fp16 ulp plus one float32
+    rounding of the exact sum."""
+    s = o.decode16(a_bits, "f16").astype(np.float64) + d_values
+    bounds.assert_elementwise(got_bits, "f16", s, bounds.U * np.abs(s), label)
+
+
+def _check_block_steps(x_bits, blk, gpu, ws, M, rows):
+    D, F = gpu.D, gpu.F
+    it = gpu.intermediates(ws, M)
+    qkv, a, o_, h, u = (_f16(it[k]) for k in ("qkv", "a", "o", "h", "u"))
+    _check_linear_step(qkv, x_bits, "rmsnorm", blk, "qkv", blk["norm1"], "qkv", rows)
+    assert np.array_equal(a, qkv[:, 2 * D:3 * D])                       # the attention stub
+    _check_linear_step(o_, a, "none", blk, "o", None, "o", rows)
+    _check_residual(h, x_bits, o.decode16(o_, "f16").astype(np.float64), "h")
+    # the up projection's rstd is the last one the shared int8 workspace holds
+    lay = w8.int8_workspace_layout(M, F, D)
+    rstd2 = ws[lay["rstd"]:lay["rstd"] + 4 * M].view(torch.float32).cpu().numpy()
+    _check_linear_step(u, h, "rmsnorm", blk, "up", blk["norm2"], "u", rows, rstd=rstd2)
+    if blk.get("w16_down") is not None:
+        g = _f16(it["g"])
+        assert np.array_equal(g, P.gelu16(u, "f16"))
+        d = it["d"].cpu().numpy().astype(np.float64)
+        ref = B.linear16(g[rows], "f16", blk["w16_down"], "f16", "f32")
+        err = bounds.dense_err32(np.abs(o.decode16(g[rows], "f16").astype(np.float64)),
+                                 np.abs(o.decode16(blk["w16_down"], "f16").astype(np.float64)), ref["y"], F)
+        bounds.assert_elementwise(d[rows].astype(np.float32), "f32", ref["y"], err, "d16")
+        dv = d + blk["b_down"].astype(np.float64)[None, :]
+    else:
+        d = _f16(it["d"])
+        _check_linear_step(d, u, "gelu", blk, "down", None, "d", rows)
+        dv = o.decode16(d, "f16").astype(np.float64)
+    return h, dv
+
+
+@pytest.mark.parametrize("with16", [False, True], ids=["int8_down", "fp16_down"])
+def test_block_every_step_matches_oracle(with16):
+    """Every intermediate of a small block, each against the oracle's step on
+    the driver's own input of that step, and Y against the residual of the
+    driver's h and d."""
+    M = 300
+    rng = np.random.default_rng(190 + with16)
+    D, F = 256, 1024
+    x = rng.standard_normal((M, D))
+    x[M - 8:, 37] = rng.uniform(8500, 9500, 8)
+    x[:, 101] *= 20.0
+    x_bits = o.round_to_f16(x)
+    blk, gpu = _block(rng, D, F, with16)
+    ws = w8.new_workspace(gpu.workspace_size(M))
+    announce("block steps", M, D, F, with16)
+    y = gpu.forward(dev16(x_bits, "f16"), workspace=ws)
+    torch.cuda.synchronize()
+    h, dv = _check_block_steps(x_bits, blk, gpu, ws, M, np.arange(M))
+    _check_residual(_f16(y), h, dv, "Y")
+
+
+@pytest.mark.parametrize("with16", [False, True], ids=["int8_down", "fp16_down"])
+def test_block_full_size_every_step(with16):
+    """The DiT 1024^2 block, every intermediate on sampled rows (the massive
+    text-token rows and the ragged last strip among them)."""
+    rng = np.random.default_rng(195 + with16)
+    M, D, F = 4352, 4096, 16384
+    x = rng.standard_normal((M, D))
+    x[4096::32, 2276] = rng.uniform(8500, 9500, 8)
+    x[:, 101] *= 20.0
+    x_bits = o.round_to_f16(x)
+    blk, gpu = _block(rng, D, F, with16)
+    ws = w8.new_workspace(gpu.workspace_size(M))
+    announce("block full size steps", with16)
+    y = gpu.forward(dev16(x_bits, "f16"), workspace=ws)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.random.default_rng(196).choice(M, 40, replace=False),
+                                     np.arange(4096, M, 32), np.arange(4352 - 12, M)]))
+    h, dv = _check_block_steps(x_bits, blk, gpu, ws, M, rows)
+    _check_residual(_f16(y)[rows], h[rows], dv[rows], "Y")

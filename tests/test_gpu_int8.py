@@ -2,7 +2,9 @@
 
 Bit-exact: int8 weight codes and scales, activation codes, row scales, the
 outlier-column set, int32 accumulators. Outputs: relative Frobenius error
-<= 1e-2 for fp16 output and <= 2e-3 for fp32 output, globally and per row.
+<= 1e-2 for fp16 output and <= 2e-3 for fp32 output, globally and per row,
+and element by element within half an output ulp plus the float32 epilogue's
+own error (tests/bounds.py).
 """
 import math
 
@@ -13,6 +15,7 @@ import torch
 import synth
 import w8a8_mixed_precision_amd as w8
 from oracle import w8ref as o
+from tests import bounds
 from tests.gpu_util import announce, dev16, host_stored, rel_fro, row_rel_fro
 
 pytestmark = pytest.mark.gpu
@@ -28,14 +31,20 @@ def _quant_weights_both(case):
     return wq, sw, wq_ref, sw_ref
 
 
-def _check_outputs(y_gpu, ref, out_dtype, label):
-    got = o.stored_to_f64(host_stored(y_gpu, out_dtype), out_dtype)
-    want = o.stored_to_f64(ref, out_dtype)
+def _check_outputs(y_gpu, ref, out_dtype, label, x_bits=None, x_dtype="bf16", wq=None, sw=None, rows=None):
+    """ref: the oracle's result dict. With x_bits, wq and sw (the oracle's
+    operands) the element-wise bound is checked too."""
+    stored = host_stored(y_gpu, out_dtype)
+    got = o.stored_to_f64(stored, out_dtype)
+    want = o.stored_to_f64(ref["Y"], out_dtype)
     assert np.all(np.isfinite(got)), label
     assert np.std(got) > 0, label          # finite and non-constant
     e = rel_fro(got, want)
     er = row_rel_fro(got, want).max()
     assert e <= TOL[out_dtype] and er <= TOL[out_dtype], (label, e, er)
+    if x_bits is not None:
+        err = bounds.int8_err32(ref, x_bits, x_dtype, wq, sw, rows=rows)
+        bounds.assert_elementwise(stored, out_dtype, ref["y"], err, label)
     return e, er
 
 
@@ -135,19 +144,22 @@ def test_outlier_set_larger_than_the_lds_list():
     ref = o.int8_mixed_linear(x, "bf16", wq_ref, sw_ref, 0.0, "f32")
     y = w8.int8_mixed_linear(dev16(x, "bf16"), wq, sw, 0.0, torch.float32)
     torch.cuda.synchronize()
-    _check_outputs(y, ref["Y"], "f32", "unlisted")
+    _check_outputs(y, ref, "f32", "unlisted", x, "bf16", wq_ref, sw_ref)
 
 
-def test_every_bf16_value_encodes_like_the_oracle():
-    """All finite bf16 patterns, 256 per row, each row with its own scale."""
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_every_16bit_value_encodes_like_the_oracle(dtype):
+    """All finite patterns of the format, 256 per row, each row with its own
+    scale (the last row padded with zeros)."""
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
-    vals = o.decode16(bits, "bf16")
-    keep = np.isfinite(vals)
-    rows = bits[keep][: (keep.sum() // 256) * 256].reshape(-1, 256)
-    xf = o.decode16(rows, "bf16")
+    vals = o.decode16(bits, dtype)
+    fin = bits[np.isfinite(vals)]
+    pad = (-fin.size) % 256
+    rows = np.concatenate([fin, np.zeros(pad, np.uint16)]).reshape(-1, 256)
+    xf = o.decode16(rows, dtype)
     O_ref, sx_ref, q_ref = o.quantize_activations_int8(xf, math.inf)
-    announce("int8 exhaustive bf16 encode")
-    q, sx, O = w8.debug_int8_quantize_activations(dev16(rows, "bf16"), math.inf)
+    announce("int8 exhaustive encode", dtype)
+    q, sx, O = w8.debug_int8_quantize_activations(dev16(rows, dtype), math.inf)
     assert O.numel() == 0
     assert np.array_equal(sx.cpu().numpy(), sx_ref)
     assert np.array_equal(q.cpu().numpy(), q_ref)
@@ -212,31 +224,78 @@ def test_int8_mixed_linear_matches_oracle(case, out_dtype, t):
     y = w8.int8_mixed_linear(dev16(case.x_bits, case.x_dtype), wq, sw, t, {"f16": torch.float16,
                                                                           "f32": torch.float32}[out_dtype])
     torch.cuda.synchronize()
-    _check_outputs(y, ref["Y"], out_dtype, (case.name, t))
+    _check_outputs(y, ref, out_dtype, (case.name, t), case.x_bits, case.x_dtype, wq_ref, sw_ref)
 
 
 def test_workspace_reuse_leaves_bookkeeping_clean():
-    """The outlier flags and split-K counters live in the workspace and every
-    call leaves them zero: reusing one workspace across calls with different
-    outlier sets (and a K-split GEMM) gives each call its own exact result."""
+    """The outlier flags and split-K counters live in the workspace's fixed
+    front: reusing one workspace across calls with different outlier sets (and
+    a K-split GEMM) gives each call its own exact result, and the counters are
+    zero again after every call."""
     a = synth.random_linear(300, 8192, 520, seed=46, x_dtype="bf16", outlier_cols=5)
     b = synth.random_linear(300, 8192, 520, seed=47, x_dtype="bf16", outlier_cols=2)
     wq, sw, wq_ref, sw_ref = _quant_weights_both(a)
     ws = w8.new_workspace(w8.int8_mixed_linear_workspace_size(300, 520, 8192))
+    lay = w8.int8_workspace_layout(300, 520, 8192)
     announce("int8 workspace reuse")
     for c in (a, b, a, b):
         y = w8.int8_mixed_linear(dev16(c.x_bits, "bf16"), wq, sw, 6.0, torch.float32, workspace=ws)
         ref = o.int8_mixed_linear(c.x_bits, "bf16", wq_ref, sw_ref, 6.0, "f32")
-        _check_outputs(y, ref["Y"], "f32", c.name)
-    # the bookkeeping is zero again after the calls: the outlier-column flags
-    # (K bytes) and the split-K counters (6 tiles), each region 256-byte
-    # aligned after q [M,K] and sx [M]
+        _check_outputs(y, ref, "f32", c.name, c.x_bits, "bf16", wq_ref, sw_ref)
+        torch.cuda.synchronize()
+        assert not ws[lay["cnt"]:lay["flags"]].any()          # every split-K counter zero
+    # the flags carry the last call's stamp on exactly its outlier columns
+    flags = ws[lay["flags"]:lay["flags"] + 4 * 8192].view(torch.int32).cpu().numpy().view(np.uint32)
+    O_b = o.quantize_activations_int8(o.decode16(b.x_bits, "bf16"), 6.0)[0]
+    stamped = np.flatnonzero(flags == flags[O_b[0]])
+    assert np.array_equal(stamped, O_b)
+
+
+def test_one_workspace_serves_shapes_of_both_kinds():
+    """One zero-filled workspace, large enough for both, runs a K = 4096 linear,
+    a K = 16384 linear (whose flags and codes span what the first used for
+    other regions), the first again and an FP8 linear, each with the result
+    of a fresh workspace."""
+    up = synth.random_linear(520, 4096, 700, seed=48, x_dtype="bf16", outlier_cols=4)
+    down = synth.random_linear(520, 16384, 300, seed=49, x_dtype="bf16", outlier_cols=3)
+    sizes = [w8.int8_mixed_linear_workspace_size(520, 700, 4096), w8.int8_mixed_linear_workspace_size(520, 300, 16384),
+             w8.fp8_w8a8_linear_workspace_size(520, 700, 4096)]
+    ws = w8.new_workspace(max(sizes))
+    wu, su, wu_ref, su_ref = _quant_weights_both(up)
+    wd, sd, wd_ref, sd_ref = _quant_weights_both(down)
+    w8q, s8 = w8.quantize_weight_rowwise(dev16(up.w_bits, "bf16"), "fp8")
+    announce("int8 one workspace, two shapes")
+    xu, xd = dev16(up.x_bits, "bf16"), dev16(down.x_bits, "bf16")
+    for c, x, wq, sw, wq_ref, sw_ref in ((up, xu, wu, su, wu_ref, su_ref), (down, xd, wd, sd, wd_ref, sd_ref),
+                                         (up, xu, wu, su, wu_ref, su_ref)):
+        y = w8.int8_mixed_linear(x, wq, sw, 6.0, torch.float16, workspace=ws)
+        fresh = w8.int8_mixed_linear(x, wq, sw, 6.0, torch.float16)
+        assert torch.equal(y, fresh), c.name
+        ref = o.int8_mixed_linear(c.x_bits, "bf16", wq_ref, sw_ref, 6.0, "f16")
+        _check_outputs(y, ref, "f16", c.name, c.x_bits, "bf16", wq_ref, sw_ref)
+    y8 = w8.fp8_w8a8_linear(xu, w8q, s8, None, torch.bfloat16, workspace=ws)
+    assert torch.equal(y8, w8.fp8_w8a8_linear(xu, w8q, s8, None, torch.bfloat16))
+    y = w8.int8_mixed_linear(xd, wd, sd, 6.0, torch.float16, workspace=ws)
+    assert torch.equal(y, w8.int8_mixed_linear(xd, wd, sd, 6.0, torch.float16))
+
+
+@pytest.mark.parametrize("n_out,t", [(40, 6.0), (300, 6.0), (600, 0.0)], ids=["staged_global", "gathered",
+                                                                                "all_gathered"])
+@pytest.mark.parametrize("x_dtype", ["bf16", "f16"])
+def test_outlier_counts_past_the_lds_staging(n_out, t, x_dtype):
+    """More than 32 outlier columns: the epilogue reads the staged XO/WO from
+    global memory (up to 256 columns), or, past that, gathers the outlier
+    columns from X and Wq itself; t = 0 makes every column an outlier."""
+    K = 640 if n_out < 600 else 600
+    c = synth.random_linear(300, K, 520, seed=50 + n_out, x_dtype=x_dtype, outlier_cols=min(n_out, K))
+    wq, sw, wq_ref, sw_ref = _quant_weights_both(c)
+    ref = o.int8_mixed_linear(c.x_bits, x_dtype, wq_ref, sw_ref, t, "f32")
+    if t > 0:
+        assert len(ref["O"]) >= n_out - 2
+    announce("int8 outlier count", n_out, t, x_dtype, len(ref["O"]))
+    y = w8.int8_mixed_linear(dev16(c.x_bits, x_dtype), wq, sw, t, torch.float32)
     torch.cuda.synchronize()
-    up = lambda n: (n + 255) // 256 * 256
-    flags_off = up(300 * 8192) + up(4 * 300)
-    cnt_off = flags_off + up(8192)
-    assert not ws[flags_off:flags_off + 8192].any()
-    assert not ws[cnt_off:cnt_off + 4 * 6].any()
+    _check_outputs(y, ref, "f32", ("outliers", n_out, t), c.x_bits, x_dtype, wq_ref, sw_ref)
 
 
 def test_zero_row_gives_zero_output_row():
@@ -267,7 +326,7 @@ def test_deterministic_non_default_stream_and_no_out_of_bounds_writes():
     b = buf.cpu().numpy()
     assert np.all(b[:guard] == 12345.0) and np.all(b[guard + M * N:] == 12345.0)
     ref = o.int8_mixed_linear(c.x_bits, "bf16", wq_ref, sw_ref, 6.0, "f32")
-    _check_outputs(y2, ref["Y"], "f32", "stream")
+    _check_outputs(y2, ref, "f32", "stream", c.x_bits, "bf16", wq_ref, sw_ref)
 
 
 # ----------------------------------------------------------------------------
@@ -312,4 +371,4 @@ def test_dit_full_size(name):
     del acc
     y = w8.int8_mixed_linear(x, wq, sw, 6.0, torch.float16)
     ref = o.int8_mixed_linear(c.x_bits, "bf16", wq_ref, sw_ref, 6.0, "f16", rows=rows)
-    _check_outputs(y[torch.from_numpy(rows).cuda()], ref["Y"], "f16", c.name)
+    _check_outputs(y[torch.from_numpy(rows).cuda()], ref, "f16", c.name, c.x_bits, "bf16", wq_ref, sw_ref, rows)

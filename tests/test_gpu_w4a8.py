@@ -15,6 +15,7 @@ import synth
 import w8a8_mixed_precision_amd as w8
 from oracle import w4a8 as o4
 from oracle import w8ref as o
+from tests import bounds
 from tests.gpu_util import OUT, announce, dev16, host_stored, rel_fro, row_rel_fro
 
 pytestmark = pytest.mark.gpu
@@ -88,12 +89,14 @@ def test_w4a8_linear_matches_oracle(M, K, N, seed, out_dtype, split):
     y = w8.w4a8_linear(dev16(x_bits, x_dtype), torch.from_numpy(packed).cuda(), torch.from_numpy(sw).cuda(),
                        OUT[out_dtype], split=split)
     torch.cuda.synchronize()
-    got = o.stored_to_f64(host_stored(y, out_dtype), out_dtype)
+    stored = host_stored(y, out_dtype)
+    got = o.stored_to_f64(stored, out_dtype)
     e, er = rel_fro(got, ref["y"]), row_rel_fro(got, ref["y"]).max()
     assert np.all(np.isfinite(got))
     assert e <= TOL[out_dtype] and er <= TOL[out_dtype], (e, er)
     if out_dtype == "f32":
         assert e <= 1e-5, e
+    bounds.assert_elementwise(stored, out_dtype, ref["y"], bounds.w4a8_err32(ref, sw), (M, K, N, split))
 
 
 def test_workspace_reuse_and_determinism():
@@ -122,6 +125,8 @@ def test_text_encoder_layers_full_size(layer):
     announce("w4a8 full size", c.name)
     y = w8.w4a8_linear(dev16(c.x_bits, c.x_dtype), torch.from_numpy(packed).cuda(), torch.from_numpy(sw).cuda())
     torch.cuda.synchronize()
-    got = o.stored_to_f64(host_stored(y[torch.from_numpy(rows).cuda()], "f16"), "f16")
+    stored = host_stored(y[torch.from_numpy(rows).cuda()], "f16")
+    got = o.stored_to_f64(stored, "f16")
     e, er = rel_fro(got, ref["y"]), row_rel_fro(got, ref["y"]).max()
     assert e <= TOL["f16"] and er <= TOL["f16"], (e, er)
+    bounds.assert_elementwise(stored, "f16", ref["y"], bounds.w4a8_err32(ref, sw), c.name)

@@ -15,6 +15,7 @@ import torch
 import synth
 import w8a8_mixed_precision_amd as w8
 from oracle import w8ref as o
+from tests import bounds
 from tests.gpu_util import OUT, announce, dev16, host_stored, rel_fro, row_rel_fro
 
 pytestmark = pytest.mark.gpu
@@ -80,13 +81,17 @@ def test_w8a16_linear_matches_oracle(M, K, N, seed, out_dtype, split, tile):
     y = w8.debug_fp8_w8a16_linear(dev16(x_bits, "bf16"), torch.from_numpy(codes).cuda(),
                                   torch.from_numpy(sw).cuda(), split, tile, OUT[out_dtype])
     torch.cuda.synchronize()
-    got = o.stored_to_f64(host_stored(y, out_dtype), out_dtype)
+    stored = host_stored(y, out_dtype)
+    got = o.stored_to_f64(stored, out_dtype)
     want = ref["y"]
     assert np.all(np.isfinite(got))
     e, er = rel_fro(got, want), row_rel_fro(got, want).max()
     assert e <= TOL[out_dtype] and er <= TOL[out_dtype], (e, er)
     if out_dtype == "f32":
         assert e <= 1e-5, e
+    err = bounds.dense_err32(np.abs(o.decode16(x_bits, "bf16").astype(np.float64)),
+                             np.abs(o.decode16(ref["w_bits"], "bf16").astype(np.float64)), want, K)
+    bounds.assert_elementwise(stored, out_dtype, want, err, (M, K, N, split, tile))
 
 
 def test_workspace_reuse_and_determinism():
@@ -120,6 +125,10 @@ def test_text_encoder_layers_full_size(layer):
     announce("w8a16 full size", c.name)
     y = w8.fp8_w8a16_linear(dev16(c.x_bits, c.x_dtype), torch.from_numpy(codes).cuda(), torch.from_numpy(sw).cuda())
     torch.cuda.synchronize()
-    got = o.stored_to_f64(host_stored(y[torch.from_numpy(rows).cuda()], "bf16"), "bf16")
+    stored = host_stored(y[torch.from_numpy(rows).cuda()], "bf16")
+    got = o.stored_to_f64(stored, "bf16")
     e, er = rel_fro(got, ref["y"]), row_rel_fro(got, ref["y"]).max()
     assert e <= TOL["bf16"] and er <= TOL["bf16"], (e, er)
+    err = bounds.dense_err32(np.abs(o.decode16(c.x_bits[rows], c.x_dtype).astype(np.float64)),
+                             np.abs(o.decode16(ref["w_bits"], "bf16").astype(np.float64)), ref["y"], c.K)
+    bounds.assert_elementwise(stored, "bf16", ref["y"], err, c.name)

@@ -11,36 +11,99 @@ from oracle import producers as P
 from oracle import w8ref as o
 
 
-def test_exp32_is_accurate_and_exact_at_zero():
-    x = np.linspace(-87.0, 88.0, 400001).astype(np.float32)
-    got = P.exp32(x).astype(np.float64)
-    ref = np.exp(x.astype(np.float64))
-    assert np.max(np.abs(got - ref) / ref) < 2.0 ** -21          # about 2 ulp of float32
-    assert P.exp32(np.float32(0.0)) == 1.0
-    assert P.exp32(np.float32(1.0)) == np.float32(math.e)        # e rounded to float32
-    assert P.exp32(np.float32(89.0)) == np.inf                   # past FLT_MAX
-    assert P.exp32(np.float32(-110.0)) == 0.0                    # below the subnormals
+def _all_finite(dtype):
+    bits = np.arange(65536, dtype=np.uint16)
+    return bits[np.isfinite(o.decode16(bits, dtype))]
 
 
-def test_gelu32_matches_float64_reference():
-    h = np.linspace(-12.0, 12.0, 200001).astype(np.float32)
-    got = P.gelu32(h).astype(np.float64)
-    ref = torch.nn.functional.gelu(torch.from_numpy(h.astype(np.float64)), approximate="tanh").numpy()
-    assert np.max(np.abs(got - ref)) < 2e-6
-    big = np.abs(ref) > 1e-3
-    assert np.max(np.abs(got - ref)[big] / np.abs(ref[big])) < 4e-6
-    # the same function as 0.5 h (1 + tanh u), written independently in float64
-    u = math.sqrt(2.0 / math.pi) * (h.astype(np.float64) + 0.044715 * h.astype(np.float64) ** 3)
-    assert np.max(np.abs(got - 0.5 * h * (1.0 + np.tanh(u)))) < 2e-6
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_gelu16_is_float64_gelu_rounded_once(dtype):
+    """Every finite 16-bit input: the oracle's X equals the float64 value
+    h * sigmoid(2u) (scipy's expit, which stays accurate where 1 + tanh(u)
+    cancels) rounded once to the 16-bit type, and lies within one 16-bit step
+    of torch's float64 tanh-form GELU where that is not in cancellation. The
+    exact values stay at least 2.6e-8 (relative) away from every 16-bit
+    rounding midpoint, far more than float64's error, with one class of
+    exceptions: bf16 inputs with |h| < 2^-125, where gelu(h) = h/2 +
+    sqrt(2/pi) h^2 / 2 + O(h^4) sits just above h/2 and h/2 (a subnormal) can
+    be a midpoint. float64 loses the h^2 term there, so those inputs are
+    checked against the series: h/2 rounded with ties toward +inf."""
+    from scipy.special import expit
+    bits = _all_finite(dtype)
+    got = P.gelu16(bits, dtype)
+    h = o.decode16(bits, dtype).astype(np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        u = np.sqrt(2.0 / np.pi) * (h + 0.044715 * h ** 3)
+        ref = h * expit(2.0 * u)
+    ref = np.where(np.isnan(ref), np.copysign(0.0, h), ref)       # h^3 overflow at the bf16 extremes
+    r16 = o.round_to_f16(ref) if dtype == "f16" else o.round_to_bf16(ref)
+    tg = torch.nn.functional.gelu(torch.from_numpy(h), approximate="tanh").numpy()
+    ok = np.abs(tg) > 1e-3
+    gv = o.decode16(got, dtype).astype(np.float64)
+    step = 2.0 ** -10 if dtype == "f16" else 2.0 ** -7
+    assert np.all(np.abs(gv[ok] - tg[ok]) <= step * np.abs(tg[ok]))
+    tiny = np.abs(h) < 2.0 ** -125
+    if dtype == "f16":
+        assert np.array_equal(got, r16)
+        return
+    assert np.array_equal(got[~tiny], r16[~tiny])
+    # series form for the subnormal inputs, with exact rationals
+    from fractions import Fraction
+    from tests.exact import to_bf16
+    for b, g in zip(bits[tiny].tolist(), got[tiny].tolist()):
+        hv = Fraction(float(o.decode16(np.array([b], np.uint16), "bf16")[0]))
+        half = hv / 2
+        want = to_bf16(half + abs(half) * Fraction(1, 2 ** 40))   # just above h/2
+        gv = Fraction(float(o.decode16(np.array([g], np.uint16), "bf16")[0]))
+        assert gv == want, (b, g, float(want))
+        assert (g >> 15) == (b >> 15)                              # sign kept, -0 included
 
 
-def test_gelu32_special_values():
-    g = P.gelu32(np.array([0.0, 20.0, -20.0, 1.0, -1.0], dtype=np.float32))
-    assert g[0] == 0.0
-    assert g[1] == 20.0                                          # exp(-2u) vanishes
-    assert g[2] == 0.0 and np.signbit(g[2])                      # -20 / inf
-    assert abs(g[3] - 0.8411919906082768) < 1e-6                 # tanh-form GELU(1)
-    assert abs(g[4] + 0.15880800939172324) < 1e-6
+def test_gelu16_special_values():
+    f16 = o.round_to_f16(np.array([0.0, -0.0, 1.0, -1.0, 20.0, -20.0, 65504.0, -65504.0, 3.0, -9.5]))
+    g = o.decode16(P.gelu16(f16, "f16"), "f16")
+    assert g[0] == 0.0 and not np.signbit(g[0])
+    assert g[1] == 0.0 and np.signbit(g[1])
+    assert g[2] == np.float16(0.8411919906082768)                # tanh-form GELU(1) in fp16
+    assert g[3] == np.float16(-0.15880800939172324)
+    assert g[4] == 20.0 and g[6] == 65504.0                      # large positive h: h itself
+    assert g[5] == 0.0 and np.signbit(g[5]) and np.signbit(g[7])  # large negative h: -0
+    assert g[8] == np.float16(2.9963627)                          # 3 Phi-like: just below 3
+    bf = o.round_to_bf16(np.array([1.0, -3.0e38, 3.0e38]))
+    gb = o.decode16(P.gelu16(bf, "bf16"), "bf16")
+    assert gb[0] == o.decode16(o.round_to_bf16(np.array([0.8411919906082768])), "bf16")[0]
+    assert gb[1] == 0.0 and np.signbit(gb[1]) and gb[2] == o.decode16(bf[2:], "bf16")[0]
+
+
+def test_gelu16_odd_part_identity():
+    """gelu(h) - gelu(-h) = h exactly for the tanh form (sigma(z) + sigma(-z)
+    = 1): checked on the decimal values before rounding."""
+    for h in [0.5, 1.0, 2.75, 4.0, 0.001, 7.5]:
+        d = P.gelu_decimal(h) - P.gelu_decimal(-h)
+        assert abs(float(d) - h) <= 1e-40 * max(1.0, h)
+
+
+def test_decimal_rounding_matches_exact_rationals():
+    """round_decimal_to16 (the oracle's last step) against the Fraction-based
+    rounding of tests/exact.py, at midpoints, just off them and at random."""
+    import decimal
+    from decimal import Decimal
+    from fractions import Fraction
+    from tests.exact import to_bf16, to_f16
+    rng = np.random.default_rng(5)
+    vals = [Fraction(1) + Fraction(1, 2 ** 11), Fraction(1) + Fraction(3, 2 ** 11), Fraction(1, 2 ** 25),
+            Fraction(3, 2 ** 25), Fraction(65504) + Fraction(16), Fraction(65520), Fraction(1, 2 ** 134)]
+    vals += [Fraction(float(v)) for v in rng.standard_normal(200) * 10.0 ** rng.integers(-8, 5, 200)]
+    for v in vals:
+        for dtype, ref in (("f16", to_f16), ("bf16", to_bf16)):
+            for sgn in (1, -1):
+                fr = sgn * v
+                with decimal.localcontext(decimal.Context(prec=2000)):
+                    d = Decimal(fr.numerator) / Decimal(fr.denominator)   # exact: a dyadic rational
+                got = P.round_decimal_to16(d, dtype)
+                gv = float(o.decode16(np.array([got], np.uint16), dtype)[0])
+                want = ref(fr)
+                assert gv == float(want), (dtype, float(fr), gv, float(want))
 
 
 @pytest.mark.parametrize("K", [64, 4096])
@@ -116,3 +179,26 @@ def test_fused_gelu_feeds_its_output_to_the_linear():
     keep = np.ones(K, bool)
     keep[7] = False
     assert np.array_equal(ref["sx"], np.abs(x[:, keep]).max(axis=1))
+
+
+def test_rstd_alternatives_cover_every_summation_order():
+    """A float64 sum of the squares in numpy's pairwise order, in row order,
+    in reverse and sorted ascending all give one of the two rstd readings;
+    the exactly rounded sum's rstd is one of them."""
+    rng = np.random.default_rng(9)
+    K = 4096
+    h = (rng.standard_normal((64, K)) * rng.uniform(0.01, 50.0, size=(64, 1))).astype(np.float32)
+    h = o.decode16(o.round_to_bf16(h), "bf16")
+    a, b = P.rstd_alternatives(h, 1e-6)
+    _, exact = P.rmsnorm_modulate32(h, eps=1e-6)
+    assert np.all((exact == a) | (exact == b))
+    sq = h.astype(np.float64) ** 2
+    orders = [sq.sum(axis=1), np.array([sum(r.tolist()) for r in sq]), np.array([sum(r[::-1].tolist()) for r in sq]),
+              np.array([sum(np.sort(r).tolist()) for r in sq])]
+    for ss in orders:
+        r = P._rstd_of_ss(ss, K, 1e-6)
+        assert np.all((r == a) | (r == b))
+    # a reading applied through the override gives the same X as the default
+    x1, _ = P.rmsnorm_modulate32(h, eps=1e-6)
+    x2, _ = P.rmsnorm_modulate32(h, eps=1e-6, rstd=exact)
+    assert np.array_equal(x1, x2)

@@ -19,6 +19,7 @@ __all__ = [
     "w4a8_linear_workspace_size", "DitBlock", "debug_linear16",
     "debug_int8_quantize_activations", "debug_int8_gemm_i32", "debug_fp8_quantize_activations", "debug_fp8_gemm",
     "int8_mixed_linear_workspace_size", "fp8_w8a8_linear_workspace_size", "new_workspace", "W8Error",
+    "int8_workspace_layout", "debug_int8_mixed_linear_events", "debug_fp8_w8a8_linear_events",
 ]
 
 
@@ -48,8 +49,23 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
 
 
 def new_workspace(nbytes: int, device="cuda") -> torch.Tensor:
-    """A workspace of `nbytes` for repeated calls (zero-filled, as required)."""
+    """A workspace of `nbytes` for repeated calls (zero-filled, as required).
+    One workspace may serve calls of any shapes and entry points in turn, as
+    long as it is as large as each call's size query (calls on different
+    streams that may overlap need distinct workspaces)."""
     return _workspace(nbytes, device)
+
+
+def int8_workspace_layout(M: int, N: int, K: int) -> dict:
+    """Byte offsets of the regions of an int8_mixed_linear workspace (parity
+    export): cnt, flags, nO, O, q, sx, rstd, XO, WO, part, and out_cap (the
+    outlier columns XO/WO hold)."""
+    import ctypes
+
+    v = (ctypes.c_size_t * 11)()
+    _abi.check(lib().w8dbg_int8_workspace_layout(M, N, K, v))
+    names = ["cnt", "flags", "nO", "O", "q", "sx", "rstd", "XO", "WO", "part", "out_cap"]
+    return {k: int(v[i]) for i, k in enumerate(names)}
 
 
 def int8_mixed_linear_workspace_size(M: int, N: int, K: int) -> int:
@@ -152,6 +168,43 @@ def int8_mixed_linear(x: torch.Tensor, wq: torch.Tensor, sw: torch.Tensor, thres
     return y
 
 
+def _events_arg(events):
+    import ctypes
+
+    if events is None:
+        return None
+    arr = (ctypes.c_void_p * 4)(*[int(e) if e else None for e in events])
+    return arr
+
+
+def debug_int8_mixed_linear_events(x: torch.Tensor, wq: torch.Tensor, sw: torch.Tensor, threshold: float, events,
+                                   out: torch.Tensor, workspace: torch.Tensor, bias: torch.Tensor | None = None,
+                                   producer: Producer | None = None) -> torch.Tensor:
+    """int8_mixed_linear_fused that also records the four HIP events `events`
+    (raw hipEvent_t handles) on its stream: before the row pass and after the
+    row pass, the fix-up and the GEMM."""
+    M, K = x.shape
+    N = wq.shape[0]
+    _abi.check(lib().w8dbg_int8_mixed_linear_events(
+        x.data_ptr(), _dt(x), M, K, _producer_arg(producer, K), wq.data_ptr(), sw.data_ptr(),
+        bias.data_ptr() if bias is not None else None, N, float(threshold), out.data_ptr(), _dt(out),
+        workspace.data_ptr(), workspace.numel(), _events_arg(events), _stream(x)))
+    return out
+
+
+def debug_fp8_w8a8_linear_events(x: torch.Tensor, wq8: torch.Tensor, sw: torch.Tensor, act_scale, events,
+                                 out: torch.Tensor, workspace: torch.Tensor) -> torch.Tensor:
+    """fp8_w8a8_linear that records `events` (before the activation pass, after
+    it twice, after the GEMM)."""
+    M, K = x.shape
+    N = wq8.shape[0]
+    sp = 0 if act_scale is None else act_scale.data_ptr()
+    _abi.check(lib().w8dbg_fp8_w8a8_linear_events(x.data_ptr(), _dt(x), M, K, wq8.data_ptr(), sw.data_ptr(), N, sp,
+                                                  out.data_ptr(), _dt(out), workspace.data_ptr(), workspace.numel(),
+                                                  _events_arg(events), _stream(x)))
+    return out
+
+
 def fp8_w8a8_linear(x: torch.Tensor, wq8: torch.Tensor, sw: torch.Tensor, act_scale: torch.Tensor | None = None,
                     out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
                     workspace: torch.Tensor | None = None) -> torch.Tensor:
@@ -242,6 +295,26 @@ class DitBlock:
     def workspace_size(self, M: int) -> int:
         return int(lib().w8_dit_block_workspace_size(M, self.D, self.F))
 
+    def intermediates(self, workspace: torch.Tensor, M: int) -> dict:
+        """Views of the block's intermediates in `workspace` after forward()
+        (parity export): qkv, a, o, h, u as fp16 [M, .]; d as fp16 [M, D], or
+        fp32 with the 16-bit down-projection, which also writes g = GELU(u)."""
+        import ctypes
+
+        v = (ctypes.c_size_t * 7)()
+        _abi.check(lib().w8dbg_dit_block_layout(M, self.D, self.F, v))
+        off = dict(zip(["qkv", "a", "o", "h", "u", "g", "d"], [int(x) for x in v]))
+        D, F = self.D, self.F
+        cols = dict(qkv=3 * D, a=D, o=D, h=D, u=F, g=F)
+
+        def view(name, n, dtype, esize):
+            b = workspace[off[name]: off[name] + M * n * esize]
+            return b.view(dtype).view(M, n)
+
+        out = {k: view(k, n, torch.float16, 2) for k, n in cols.items()}
+        out["d"] = view("d", D, torch.float32, 4) if self.w_down16 is not None else view("d", D, torch.float16, 2)
+        return out
+
     def forward(self, x: torch.Tensor, out: torch.Tensor | None = None,
                 workspace: torch.Tensor | None = None) -> torch.Tensor:
         import ctypes
@@ -293,9 +366,10 @@ def debug_fp8_w8a16_linear(x: torch.Tensor, wq8: torch.Tensor, sw: torch.Tensor,
     return y
 
 
-def debug_int8_quantize_activations(x: torch.Tensor, threshold: float = 6.0, producer: Producer | None = None):
+def debug_int8_quantize_activations(x: torch.Tensor, threshold: float = 6.0, producer: Producer | None = None,
+                                    with_rstd: bool = False):
     """(q int8 [M,K], sx fp32 [M], outlier column indices int32 [nO]) of X, or of
-    X = producer(x)."""
+    X = producer(x); with_rstd adds the RMSNorm producer's per-row rstd [M]."""
     _dev(x, "x")
     M, K = x.shape
     q = torch.empty((M, K), dtype=torch.int8, device=x.device)
@@ -306,6 +380,11 @@ def debug_int8_quantize_activations(x: torch.Tensor, threshold: float = 6.0, pro
     _abi.check(lib().w8dbg_int8_quantize_activations(x.data_ptr(), _dt(x), M, K, _producer_arg(producer, K),
                                                      float(threshold), q.data_ptr(), sx.data_ptr(), idx.data_ptr(),
                                                      n.data_ptr(), ws.data_ptr(), ws.numel(), _stream(x)))
+    if with_rstd:
+        # the rstd region follows the workspace's common front (counters, flags)
+        front = int8_workspace_layout(M, 1, K)["nO"]
+        rstd = ws[front: front + 4 * M].view(torch.float32).clone()
+        return q, sx, idx[: int(n.item())], rstd
     return q, sx, idx[: int(n.item())]
 
 
@@ -340,20 +419,18 @@ def debug_int8_gemm_i32_workspace_size(M: int, N: int, K: int, tail: int = 0, sp
     return int(lib().w8dbg_int8_gemm_i32_workspace_size(M, N, K, int(tail), int(split)))
 
 
-def profile_start(max_calls: int) -> None:
-    """Start recording per-stage GPU times of the linear calls (HIP events)."""
-    _abi.check(lib().w8_profile_start(int(max_calls)))
-
-
-def profile_stop():
-    """Stop recording; returns (stage_ms[3], n_calls): summed milliseconds of
-    the row pass, the outlier fix-up and the GEMM over the recorded calls."""
+def debug_mfma_peak(kind: str, blocks: int, iters: int, device="cuda"):
+    """Launch the measured-peak MFMA kernel ("int8", "fp8" or "bf16") on the
+    current stream; returns (checksum tensor, operations launched). The caller
+    times it."""
     import ctypes
 
-    ms = (ctypes.c_double * 3)()
-    n = ctypes.c_int()
-    _abi.check(lib().w8_profile_stop(ms, ctypes.byref(n)))
-    return [ms[0], ms[1], ms[2]], n.value
+    k = {"int8": 0, "fp8": 1, "bf16": 2}[kind]
+    out = torch.empty(blocks * 256, dtype=torch.int32, device=device)
+    ops = ctypes.c_double()
+    _abi.check(lib().w8dbg_mfma_peak(k, int(blocks), int(iters), out.data_ptr(), ctypes.byref(ops),
+                                     torch.cuda.current_stream(out.device).cuda_stream))
+    return out, ops.value
 
 
 def debug_fp8_quantize_activations(x: torch.Tensor, act_scale: torch.Tensor | None = None):

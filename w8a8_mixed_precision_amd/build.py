@@ -2,8 +2,10 @@
 
     python -m w8a8_mixed_precision_amd.build
 
-Every source is compiled every time this runs: one hipcc process per source
-(in parallel), then one link.
+Every source is compiled every time this runs. First the host program
+csrc/gelu_table_gen.cpp is built and run: it writes the GELU tables that the
+kernels include (gelu_table.inc, in the build's temporary folder). Then one
+hipcc process per HIP source (in parallel), then one link.
 """
 from __future__ import annotations
 
@@ -19,6 +21,7 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libw8mp.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CXX = os.environ.get("CXX", "g++")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed-fp32 instructions (v_pk_*_f32) in any kernel
@@ -40,8 +43,14 @@ def _jobs() -> int:
 
 
 def build(verbose: bool = False) -> str:
-    inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc")]
     with tempfile.TemporaryDirectory(prefix="w8mp_build_") as tmpdir:
+        gen = os.path.join(tmpdir, "gelu_table_gen")
+        cmd = [CXX, "-O2", "-std=c++17", os.path.join(PKG, "csrc", "gelu_table_gen.cpp"), "-o", gen]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        subprocess.run([gen, os.path.join(tmpdir, "gelu_table.inc")], check=True)
+        inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"), "-I", tmpdir]
         def compile_one(src: str) -> str:
             obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
             cmd = [HIPCC, *FLAGS, *inc, "-c", src, "-o", obj]

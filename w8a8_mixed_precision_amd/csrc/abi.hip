@@ -63,9 +63,9 @@ w8_status check_mk(int64_t M, int64_t K, int64_t maxK) {
   return W8_OK;
 }
 
-// Compute units of the current device (cached per device); the GEMM plan
-// depends on it, so workspace sizes are per device. Threads may race to fill
-// an entry; they all store the same value, and the atomics keep that defined.
+// Compute units of the current device (cached per device); the GEMM plans
+// depend on it. Threads may race to fill an entry; they all store the same
+// value, and the atomics keep that defined.
 int cu_count() {
   static std::atomic<int> cache[64] = {};
   int dev = 0;
@@ -78,6 +78,42 @@ int cu_count() {
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
   return n;
+}
+
+// Every workspace starts with the same two regions, at fixed offsets whatever
+// the shape of the call, so that one workspace can serve calls of different
+// shapes one after another:
+//  * kCntCap split-K arrival counters, zero between calls (each tile's last
+//    slice resets its counter);
+//  * the outlier-column flag words of the int8 linears, one per column up to
+//    W8_INT8_MAX_K. A call marks its outlier columns with a stamp of its own
+//    (never 0), so flags are never cleared and a flag left by an earlier or a
+//    failed call does not match.
+// Shape-dependent regions follow. Sizes are planned for kPlanCus compute
+// units (MI355X); a device whose GEMM plan needs more split-K partials or
+// counters than a workspace holds runs the plan without K-slicing instead.
+using w8::kCntBytes;
+using w8::kCntCap;
+using w8::kFlagBytes;
+using w8::kFront;
+static_assert(kFlagBytes >= 4 * static_cast<size_t>(W8_INT8_MAX_K), "a flag word per column");
+static_assert(kFront % kAlign == 0, "aligned front");
+constexpr int kPlanCus = 256;
+
+// The next call stamp (process-wide, thread-safe, skips 0). A stale flag can
+// match again only after 2^32 - 1 further int8 calls.
+uint32_t next_stamp() {
+  static std::atomic<uint32_t> counter{0};
+  uint32_t s = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+  while (s == 0) s = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+  return s;
+}
+
+// The plan when it fits the workspace's partials and the counter region,
+// else the same grid without K-slicing (`whole`).
+w8::GemmPlan fit_plan(const w8::GemmPlan& p, size_t part_bytes_avail, const w8::GemmPlan& whole) {
+  if (p.counters() <= kCntCap && p.partial_bytes() <= part_bytes_avail) return p;
+  return whole;
 }
 
 }  // namespace
@@ -93,30 +129,42 @@ int device_cus() { return cu_count(); }
 
 namespace {
 
-// Workspace layout of int8_mixed_linear (offsets from the 256-aligned base).
-// flags and cnt are the bookkeeping that every call leaves zero again.
+// Workspace layout of int8_mixed_linear (offsets from the 256-aligned base):
+// the common front (counters, flags), then nO, the outlier list O [K], the
+// codes q [M,K], sx [M], the RMSNorm rstd [M] of the fused path, the staged
+// outlier operands XO [M, kOutCap] and WO [N, kOutCap], and the split-K
+// partials of the plan.
 struct Int8Ws {
-  size_t q, sx, rstd, flags, cnt, nO, O, XO, WO, part, total;
-  w8::GemmPlan plan;
+  size_t cnt, flags, nO, O, q, sx, rstd, XO, WO, part, base;
 };
 
 Int8Ws int8_layout(int64_t M, int64_t N, int64_t K) {
   Int8Ws w{};
-  w.plan = w8::plan_int8_gemm(M, N, K, cu_count());
-  const size_t P = static_cast<size_t>((K + 31) / 32 * 32);  // worst case: every column is an outlier
   size_t off = 0;
+  w.cnt = off;   off += kCntBytes;
+  w.flags = off; off += kFlagBytes;
+  w.nO = off;    off = up(off + 4);
+  w.O = off;     off = up(off + 4 * static_cast<size_t>(K));
   w.q = off;     off = up(off + static_cast<size_t>(M) * K);
   w.sx = off;    off = up(off + 4 * static_cast<size_t>(M));
   w.rstd = off;  off = up(off + 4 * static_cast<size_t>(M));
-  w.flags = off; off = up(off + static_cast<size_t>(K));
-  w.cnt = off;   off = up(off + 4 * static_cast<size_t>(w.plan.counters()));
-  w.nO = off;    off = up(off + 4);
-  w.O = off;     off = up(off + 4 * static_cast<size_t>(K));
-  w.XO = off;    off = up(off + 2 * static_cast<size_t>(M) * P);
-  w.WO = off;    off = up(off + 2 * static_cast<size_t>(N) * P);
-  w.part = off;  off = up(off + w.plan.partial_bytes());
-  w.total = off;
+  w.XO = off;    off = up(off + 2 * static_cast<size_t>(M) * w8::kOutCap);
+  w.WO = off;    off = up(off + 2 * static_cast<size_t>(N) * w8::kOutCap);
+  w.part = off;
+  w.base = off;
   return w;
+}
+
+size_t int8_ws_size(int64_t M, int64_t N, int64_t K) {
+  const w8::GemmPlan p = w8::plan_int8_gemm(M, N, K, kPlanCus);
+  const size_t part = p.counters() <= kCntCap ? p.partial_bytes() : 0;
+  return int8_layout(M, N, K).base + up(part);
+}
+
+// The int8 GEMM plan of this device that fits `avail` bytes of partials.
+w8::GemmPlan int8_plan(int64_t M, int64_t N, int64_t K, size_t avail) {
+  return fit_plan(w8::plan_int8_gemm(M, N, K, cu_count()), avail,
+                  w8::plan_int8_gemm_forced(M, N, cu_count(), true, 1));
 }
 
 // Magnitude bits (bits & 0x7FFF) of the largest value of the 16-bit format
@@ -141,48 +189,40 @@ uint32_t threshold_bits(float t, bool bf16) {
   return lo;
 }
 
-// Workspace of the int8 GEMM parity export: counters, then partials.
-struct GemmWs {
-  size_t cnt, part, total;
-  w8::GemmPlan plan;
+// Grid of the int8 GEMM parity export. tail: 0 the linear's own plan; 1
+// leftover tiles as `split` 256x256 slices (split 1: every tile whole); 2 as
+// `split` slices of 128x128 quarters. Workspace: the front, then partials.
+w8::GemmPlan int8_debug_plan(int64_t M, int64_t N, int64_t K, int tail, int split, int cus) {
+  return tail == 0 ? w8::plan_int8_gemm(M, N, K, cus) : w8::plan_int8_gemm_forced(M, N, cus, tail == 2, split);
+}
+
+// Workspace layout of fp8_w8a8_linear: the front, codes [M,K], scales [M],
+// split-K partials.
+struct Fp8Ws {
+  size_t xq, sx, part, base;
 };
 
-// tail: 0 the linear's own plan; 1 leftover tiles as `split` 256x256 slices
-// (split 1: every tile whole); 2 as `split` slices of 128x128 quarters.
-GemmWs gemm_layout(int64_t M, int64_t N, int64_t K, int tail = 0, int split = 1) {
-  GemmWs w{};
-  w.plan = tail == 0 ? w8::plan_int8_gemm(M, N, K, cu_count())
-                     : w8::plan_int8_gemm_forced(M, N, cu_count(), tail == 2, split);
-  size_t off = 0;
-  w.cnt = off;  off = up(off + 4 * static_cast<size_t>(w.plan.counters()));
-  w.part = off; off = up(off + w.plan.partial_bytes());
-  w.total = off;
+Fp8Ws fp8_layout(int64_t M, int64_t K) {
+  Fp8Ws w{};
+  size_t off = kFront;
+  w.xq = off;   off = up(off + static_cast<size_t>(M) * K);
+  w.sx = off;   off = up(off + 4 * static_cast<size_t>(M));
+  w.part = off;
+  w.base = off;
   return w;
 }
 
-// Workspace layout of fp8_w8a8_linear: codes, scales, then the GEMM's split-K
-// counters (left zero by every call) and partials.
-struct Fp8Ws {
-  size_t xq, sx, cnt, part, total;
-  w8::GemmPlan plan;
-};
+size_t plan_part(const w8::GemmPlan& p) { return p.counters() <= kCntCap ? up(p.partial_bytes()) : 0; }
 
-Fp8Ws fp8_layout(int64_t M, int64_t N, int64_t K) {
-  Fp8Ws w{};
-  w.plan = w8::plan_fp8_gemm(M, N, K, cu_count());
-  size_t off = 0;
-  w.xq = off;   off = up(off + static_cast<size_t>(M) * K);
-  w.sx = off;   off = up(off + 4 * static_cast<size_t>(M));
-  w.cnt = off;  off = up(off + 4 * static_cast<size_t>(w.plan.counters()));
-  w.part = off; off = up(off + w.plan.partial_bytes());
-  w.total = off;
-  return w;
+w8::GemmPlan fp8_plan(int64_t M, int64_t N, int64_t K, size_t avail) {
+  const w8::GemmPlan p = w8::plan_fp8_gemm(M, N, K, cu_count());
+  return fit_plan(p, avail, w8::plan_fp8_gemm_split(M, N, 1, p.bm));
 }
 
 // Grid of the FP8 GEMM parity export: the linear's own plan (split 0) or the
 // given block size and K-slicing.
-w8::GemmPlan fp8_debug_plan(int64_t M, int64_t N, int64_t K, int split, int tile) {
-  return split == 0 ? w8::plan_fp8_gemm(M, N, K, cu_count())
+w8::GemmPlan fp8_debug_plan(int64_t M, int64_t N, int64_t K, int split, int tile, int cus) {
+  return split == 0 ? w8::plan_fp8_gemm(M, N, K, cus)
                     : w8::plan_fp8_gemm_split(M, N, split, tile == 128 ? 128 : 256);
 }
 
@@ -199,62 +239,16 @@ w8_status check_ws(void* ws, size_t bytes, size_t need) {
   return W8_OK;
 }
 
-// Measurement hook state (see w8_profile_start in w8mp.h).
-struct Profile {
-  bool on = false;
-  int cap = 0, n = 0;
-  std::vector<hipEvent_t> ev;  // 4 per call: start, after row pass, after fix-up, after GEMM
-} g_prof;
-
-// Record boundary `b` (0..3) of the current call; a no-op unless profiling.
-void mark(int b, hipStream_t s) {
-  if (!g_prof.on || g_prof.n >= g_prof.cap) return;
-  (void)hipEventRecord(g_prof.ev[4 * g_prof.n + b], s);
-  if (b == 3) ++g_prof.n;
+// Records event `b` (0..3) of a parity-export call on its stream: events[0]
+// before the first kernel, then one after each stage (row pass, fix-up,
+// GEMM). Product calls pass no events.
+void mark(void* const* events, int b, hipStream_t s) {
+  if (events && events[b]) (void)hipEventRecord(static_cast<hipEvent_t>(events[b]), s);
 }
 
 }  // namespace
 
 extern "C" {
-
-w8_status w8_profile_start(int max_calls) {
-  W8_REQUIRE(max_calls >= 1, W8_ERR_INVALID_ARGUMENT, "max_calls must be >= 1");
-  double unused[3];
-  int n;
-  if (g_prof.on) w8_profile_stop(unused, &n);
-  g_prof.ev.assign(4 * static_cast<size_t>(max_calls), nullptr);
-  for (auto& e : g_prof.ev) {
-    if (hipEventCreate(&e) != hipSuccess) return fail(W8_ERR_HIP, "hipEventCreate failed");
-  }
-  g_prof.cap = max_calls;
-  g_prof.n = 0;
-  g_prof.on = true;
-  return ok();
-}
-
-w8_status w8_profile_stop(double* stage_ms, int* n_calls) {
-  W8_REQUIRE(stage_ms && n_calls, W8_ERR_INVALID_ARGUMENT, "null pointer argument");
-  stage_ms[0] = stage_ms[1] = stage_ms[2] = 0.0;
-  *n_calls = 0;
-  if (!g_prof.on) return ok();
-  w8_status st = W8_OK;
-  for (int c = 0; c < g_prof.n; ++c) {
-    hipEvent_t* e = &g_prof.ev[4 * static_cast<size_t>(c)];
-    if (hipEventSynchronize(e[3]) != hipSuccess) st = W8_ERR_HIP;
-    for (int k = 0; k < 3; ++k) {
-      float ms = 0.0f;
-      if (hipEventElapsedTime(&ms, e[k], e[k + 1]) != hipSuccess) st = W8_ERR_HIP;
-      stage_ms[k] += ms;
-    }
-  }
-  *n_calls = g_prof.n;
-  for (auto& e : g_prof.ev)
-    if (e) (void)hipEventDestroy(e);
-  g_prof.ev.clear();
-  g_prof.on = false;
-  g_prof.cap = g_prof.n = 0;
-  return st == W8_OK ? ok() : fail(st, "reading profile events failed");
-}
 
 const char* w8_status_string(int status) {
   switch (status) {
@@ -282,7 +276,7 @@ w8_status quantize_weight_rowwise(const void* W, int w_dt, int64_t N, int64_t K,
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = w_dt == W8_DT_BF16;
   if (fmt == W8_Q_INT8)
-    w8::launch_int8_rows(W, bf, N, (int)K, 0x7F80u, static_cast<int8_t*>(Wq), sw, nullptr, w8::kProdNone,
+    w8::launch_int8_rows(W, bf, N, (int)K, 0x7F80u, static_cast<int8_t*>(Wq), sw, nullptr, 0u, w8::kProdNone,
                          w8::ProdArgs{}, s);
   else if (fmt == W8_Q_INT4_G128)
     w8::launch_int4_weights(W, bf, N, (int)K, static_cast<uint8_t*>(Wq), sw, s);
@@ -293,7 +287,7 @@ w8_status quantize_weight_rowwise(const void* W, int w_dt, int64_t N, int64_t K,
 
 size_t int8_mixed_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
   if (M < 1 || N < 1 || K < 1) return 0;
-  return int8_layout(M, N, K).total;
+  return int8_ws_size(M, N, K);
 }
 
 static w8_status int8_common_checks(const void* X, int x_dt, int64_t M, int64_t K, float threshold) {
@@ -326,27 +320,30 @@ static w8_status producer_args(const w8_producer* p, int64_t K, int* kind, w8::P
   return W8_OK;
 }
 
+// The three kernels of one int8 call on a validated workspace. `events`: the
+// parity export's stage events (NULL for product calls).
 static w8_status int8_linear_impl(const void* X, int x_dt, int64_t M, int64_t K, const w8_producer* producer,
                                   const int8_t* Wq, const float* sw, const float* bias, int64_t N, float threshold,
                                   void* Y, int y_dt, void* workspace, size_t workspace_bytes, void* stream,
-                                  const char* what) {
+                                  void* const* events, const char* what) {
   if (w8_status st = int8_common_checks(X, x_dt, M, K, threshold); st != W8_OK) return st;
   W8_REQUIRE(Wq && sw && Y, W8_ERR_INVALID_ARGUMENT, "null pointer argument");
   W8_REQUIRE(N >= 1 && N <= kMaxDim, W8_ERR_INVALID_ARGUMENT, "N must be in [1, 2^31)");
   W8_REQUIRE(y_dt == W8_DT_F16 || y_dt == W8_DT_F32, W8_ERR_UNSUPPORTED, "Y must be f16 or f32");
-  W8_REQUIRE(aligned16(Wq) && aligned16(sw) && aligned16(Y), W8_ERR_INVALID_ARGUMENT,
+  W8_REQUIRE(aligned16(Wq) && aligned16(sw) && aligned16(Y) && aligned16(bias), W8_ERR_INVALID_ARGUMENT,
              "pointers must be 16-byte aligned");
   int kind = 0;
   w8::ProdArgs pa{};
   if (w8_status st = producer_args(producer, K, &kind, &pa); st != W8_OK) return st;
   const Int8Ws L = int8_layout(M, N, K);
-  if (w8_status st = check_ws(workspace, workspace_bytes, L.total); st != W8_OK) return st;
+  if (w8_status st = check_ws(workspace, workspace_bytes, int8_ws_size(M, N, K)); st != W8_OK) return st;
+  const w8::GemmPlan plan = int8_plan(M, N, K, workspace_bytes - L.base);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = x_dt == W8_DT_BF16;
   int8_t* q = at<int8_t>(workspace, L.q);
   float* sx = at<float>(workspace, L.sx);
-  uint8_t* flags = at<uint8_t>(workspace, L.flags);
+  uint32_t* flags = at<uint32_t>(workspace, L.flags);
   int* nO = at<int>(workspace, L.nO);
   int* O = at<int>(workspace, L.O);
   uint16_t* XO = at<uint16_t>(workspace, L.XO);
@@ -354,16 +351,18 @@ static w8_status int8_linear_impl(const void* X, int x_dt, int64_t M, int64_t K,
   int* cnt = at<int>(workspace, L.cnt);
   int* part = at<int>(workspace, L.part);
   pa.rstd = at<float>(workspace, L.rstd);
+  const uint32_t stamp = next_stamp();
+  const w8::SideSrc src{static_cast<const uint16_t*>(X), Wq, O, static_cast<int>(K), kind, pa};
 
-  mark(0, s);
+  mark(events, 0, s);
   const uint32_t tb = threshold_bits(threshold, bf);
-  w8::launch_int8_rows(X, bf, M, (int)K, tb, q, sx, flags, kind, pa, s);
-  mark(1, s);
-  w8::launch_outlier_fixup(X, bf, M, (int)K, tb, flags, q, sx, O, nO, XO, Wq, N, WO, kind, pa, s);
-  mark(2, s);
-  w8::launch_int8_gemm(q, Wq, M, N, K, sx, sw, nO, XO, WO, bf, bias, Y, y_dt == W8_DT_F16 ? 1 : 2, L.plan, part,
-                       cnt, reinterpret_cast<uint32_t*>(flags), static_cast<int>(K / 4), s);
-  mark(3, s);
+  w8::launch_int8_rows(X, bf, M, (int)K, tb, q, sx, flags, stamp, kind, pa, s);
+  mark(events, 1, s);
+  w8::launch_outlier_fixup(X, bf, M, (int)K, tb, flags, stamp, q, sx, O, nO, XO, Wq, N, WO, kind, pa, s);
+  mark(events, 2, s);
+  w8::launch_int8_gemm(q, Wq, M, N, K, sx, sw, nO, XO, WO, bf, bias, Y, y_dt == W8_DT_F16 ? 1 : 2, plan, part, cnt,
+                       src, s);
+  mark(events, 3, s);
   return check_launch(what);
 }
 
@@ -371,24 +370,24 @@ w8_status int8_mixed_linear(const void* X, int x_dt, int64_t M, int64_t K, const
                             int64_t N, float threshold, void* Y, int y_dt, void* workspace, size_t workspace_bytes,
                             void* stream) {
   return int8_linear_impl(X, x_dt, M, K, nullptr, Wq, sw, nullptr, N, threshold, Y, y_dt, workspace,
-                          workspace_bytes, stream, "int8_mixed_linear");
+                          workspace_bytes, stream, nullptr, "int8_mixed_linear");
 }
 
 w8_status int8_mixed_linear_fused(const void* H, int h_dt, int64_t M, int64_t K, const w8_producer* producer,
                                   const int8_t* Wq, const float* sw, const float* bias, int64_t N, float threshold,
                                   void* Y, int y_dt, void* workspace, size_t workspace_bytes, void* stream) {
   return int8_linear_impl(H, h_dt, M, K, producer, Wq, sw, bias, N, threshold, Y, y_dt, workspace, workspace_bytes,
-                          stream, "int8_mixed_linear_fused");
+                          stream, nullptr, "int8_mixed_linear_fused");
 }
 
 size_t fp8_w8a8_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
   if (M < 1 || N < 1 || K < 1) return 0;
-  return fp8_layout(M, N, K).total;
+  return fp8_layout(M, K).base + plan_part(w8::plan_fp8_gemm(M, N, K, kPlanCus));
 }
 
-w8_status fp8_w8a8_linear(const void* X, int x_dt, int64_t M, int64_t K, const uint8_t* Wq8, const float* sw,
+static w8_status fp8_impl(const void* X, int x_dt, int64_t M, int64_t K, const uint8_t* Wq8, const float* sw,
                           int64_t N, const float* act_scale, void* Y, int y_dt, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+                          size_t workspace_bytes, void* stream, void* const* events, const char* what) {
   W8_REQUIRE(X && Wq8 && sw && Y, W8_ERR_INVALID_ARGUMENT, "null pointer argument");
   W8_REQUIRE(x_dt == W8_DT_F16 || x_dt == W8_DT_BF16, W8_ERR_UNSUPPORTED, "X must be f16 or bf16");
   W8_REQUIRE(y_dt == W8_DT_BF16 || y_dt == W8_DT_F16 || y_dt == W8_DT_F32, W8_ERR_UNSUPPORTED,
@@ -397,45 +396,37 @@ w8_status fp8_w8a8_linear(const void* X, int x_dt, int64_t M, int64_t K, const u
   W8_REQUIRE(N >= 1 && N <= kMaxDim, W8_ERR_INVALID_ARGUMENT, "N must be in [1, 2^31)");
   W8_REQUIRE(aligned16(X) && aligned16(Wq8) && aligned16(sw) && aligned16(Y), W8_ERR_INVALID_ARGUMENT,
              "pointers must be 16-byte aligned");
-  const Fp8Ws L = fp8_layout(M, N, K);
-  if (w8_status st = check_ws(workspace, workspace_bytes, L.total); st != W8_OK) return st;
+  const Fp8Ws L = fp8_layout(M, K);
+  if (w8_status st = check_ws(workspace, workspace_bytes, fp8_w8a8_linear_workspace_size(M, N, K)); st != W8_OK)
+    return st;
+  const w8::GemmPlan plan = fp8_plan(M, N, K, workspace_bytes - L.base);
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* xq = at<uint8_t>(workspace, L.xq);
   float* sx = at<float>(workspace, L.sx);
-  mark(0, s);
+  mark(events, 0, s);
   w8::launch_fp8_rows(X, x_dt == W8_DT_BF16, M, (int)K, act_scale, xq, sx, act_scale ? 1 : 0, s);
-  mark(1, s);
-  mark(2, s);
+  mark(events, 1, s);
+  mark(events, 2, s);
   const int ydt = y_dt == W8_DT_BF16 ? 0 : (y_dt == W8_DT_F16 ? 1 : 2);
-  w8::launch_fp8_gemm(xq, Wq8, M, N, K, sx, sw, Y, ydt, L.plan, at<float>(workspace, L.part),
-                      at<int>(workspace, L.cnt), s);
-  mark(3, s);
-  return check_launch("fp8_w8a8_linear");
+  w8::launch_fp8_gemm(xq, Wq8, M, N, K, sx, sw, Y, ydt, plan, at<float>(workspace, L.part), at<int>(workspace, 0), s);
+  mark(events, 3, s);
+  return check_launch(what);
+}
+
+w8_status fp8_w8a8_linear(const void* X, int x_dt, int64_t M, int64_t K, const uint8_t* Wq8, const float* sw,
+                          int64_t N, const float* act_scale, void* Y, int y_dt, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return fp8_impl(X, x_dt, M, K, Wq8, sw, N, act_scale, Y, y_dt, workspace, workspace_bytes, stream, nullptr,
+                  "fp8_w8a8_linear");
 }
 
 }  // extern "C"
 
 namespace {
 
-// FP8 weight-only: split-K counters and partials of the plan (at least one
-// aligned unit, so a workspace is always passed).
-struct W16Ws {
-  size_t cnt, part, total;
-  w8::GemmPlan plan;
-};
-
-W16Ws w16_layout(const w8::GemmPlan& plan) {
-  W16Ws w{};
-  w.plan = plan;
-  size_t off = 0;
-  w.cnt = off;  off = up(off + 4 * static_cast<size_t>(plan.counters()));
-  w.part = off; off = up(off + plan.partial_bytes());
-  w.total = std::max<size_t>(off, kAlign);
-  return w;
-}
-
-w8::GemmPlan w16_plan(int64_t M, int64_t N, int64_t K, int split, int tile) {
-  return split == 0 ? w8::plan_w8a16_gemm(M, N, K, cu_count())
+// FP8 weight-only: the front, then the plan's split-K partials.
+w8::GemmPlan w16_plan(int64_t M, int64_t N, int64_t K, int split, int tile, int cus) {
+  return split == 0 ? w8::plan_w8a16_gemm(M, N, K, cus)
                     : w8::plan_w8a16_gemm_split(M, N, split, tile == 128 ? 128 : 256);
 }
 
@@ -457,53 +448,56 @@ static w8_status w16_checks(const void* X, int x_dt, int64_t M, int64_t K, const
   return W8_OK;
 }
 
+// `plan`: the grid to run; `whole`: the same grid unsliced, taken when the
+// plan's partials do not fit the workspace.
 static w8_status w16_run(const void* X, int64_t M, int64_t K, const uint8_t* Wq8, const float* sw, int64_t N,
-                         void* Y, int y_dt, const W16Ws& L, void* workspace, size_t workspace_bytes, void* stream,
-                         const char* what) {
-  if (w8_status st = check_ws(workspace, workspace_bytes, L.total); st != W8_OK) return st;
+                         void* Y, int y_dt, const w8::GemmPlan& want, const w8::GemmPlan& whole, void* workspace,
+                         size_t workspace_bytes, void* stream, const char* what) {
+  if (w8_status st = check_ws(workspace, workspace_bytes, kFront); st != W8_OK) return st;
+  const w8::GemmPlan plan = fit_plan(want, workspace_bytes - kFront, whole);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int ydt = y_dt == W8_DT_BF16 ? 0 : (y_dt == W8_DT_F16 ? 1 : 2);
-  mark(0, s);
-  mark(1, s);
-  mark(2, s);
-  w8::launch_w8a16_gemm(static_cast<const uint16_t*>(X), Wq8, M, N, K, sw, Y, ydt, L.plan,
-                        at<float>(workspace, L.part), at<int>(workspace, L.cnt), s);
-  mark(3, s);
+  w8::launch_w8a16_gemm(static_cast<const uint16_t*>(X), Wq8, M, N, K, sw, Y, ydt, plan, at<float>(workspace, kFront),
+                        at<int>(workspace, 0), s);
   return check_launch(what);
 }
 
 size_t fp8_w8a16_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
   if (M < 1 || N < 1 || K < 1) return 0;
-  return w16_layout(w16_plan(M, N, K, 0, 0)).total;
+  return kFront + plan_part(w16_plan(M, N, K, 0, 0, kPlanCus));
 }
 
 w8_status fp8_w8a16_linear(const void* X, int x_dt, int64_t M, int64_t K, const uint8_t* Wq8, const float* sw,
                            int64_t N, void* Y, int y_dt, void* workspace, size_t workspace_bytes, void* stream) {
   if (w8_status st = w16_checks(X, x_dt, M, K, Wq8, sw, N, Y, y_dt); st != W8_OK) return st;
-  return w16_run(X, M, K, Wq8, sw, N, Y, y_dt, w16_layout(w16_plan(M, N, K, 0, 0)), workspace, workspace_bytes,
-                 stream, "fp8_w8a16_linear");
+  if (w8_status st = check_ws(workspace, workspace_bytes, fp8_w8a16_linear_workspace_size(M, N, K)); st != W8_OK)
+    return st;
+  const w8::GemmPlan p = w16_plan(M, N, K, 0, 0, cu_count());
+  return w16_run(X, M, K, Wq8, sw, N, Y, y_dt, p, w8::plan_w8a16_gemm_split(M, N, 1, p.bm), workspace,
+                 workspace_bytes, stream, "fp8_w8a16_linear");
 }
 
 }  // extern "C"
 
 namespace {
 
-// W4A8: activation codes and row scales, split-K counters and partials.
+// W4A8: the front, activation codes [M,K], row scales [M], split-K partials.
 struct W4Ws {
-  size_t q, sx, cnt, part, total;
-  w8::GemmPlan plan;
+  size_t q, sx, part, base;
 };
 
-W4Ws w4_layout(int64_t M, int64_t N, int64_t K, int split) {
+W4Ws w4_layout(int64_t M, int64_t K) {
   W4Ws w{};
-  w.plan = split == 0 ? w8::plan_w4a8_gemm(M, N, K, cu_count()) : w8::plan_w4a8_gemm_split(M, N, split);
-  size_t off = 0;
+  size_t off = kFront;
   w.q = off;    off = up(off + static_cast<size_t>(M) * K);
   w.sx = off;   off = up(off + 4 * static_cast<size_t>(M));
-  w.cnt = off;  off = up(off + 4 * static_cast<size_t>(w.plan.counters()));
-  w.part = off; off = up(off + w.plan.partial_bytes());
-  w.total = off;
+  w.part = off;
+  w.base = off;
   return w;
+}
+
+w8::GemmPlan w4_plan(int64_t M, int64_t N, int64_t K, int split, int cus) {
+  return split == 0 ? w8::plan_w4a8_gemm(M, N, K, cus) : w8::plan_w4a8_gemm_split(M, N, split);
 }
 
 }  // namespace
@@ -528,41 +522,66 @@ static w8_status w4_checks(const void* X, int x_dt, int64_t M, int64_t K, const 
 }
 
 static w8_status w4_run(const void* X, int x_dt, int64_t M, int64_t K, const uint8_t* Wq4, const float* sw4,
-                        int64_t N, void* Y, int y_dt, const W4Ws& L, void* workspace, size_t workspace_bytes,
-                        void* stream, const char* what) {
-  if (w8_status st = check_ws(workspace, workspace_bytes, L.total); st != W8_OK) return st;
+                        int64_t N, void* Y, int y_dt, const w8::GemmPlan& want, void* workspace,
+                        size_t workspace_bytes, void* stream, const char* what) {
+  const W4Ws L = w4_layout(M, K);
+  if (w8_status st = check_ws(workspace, workspace_bytes, L.base); st != W8_OK) return st;
+  const w8::GemmPlan plan = fit_plan(want, workspace_bytes - L.base, w8::plan_w4a8_gemm_split(M, N, 1));
   hipStream_t s = static_cast<hipStream_t>(stream);
   int8_t* q = at<int8_t>(workspace, L.q);
   float* sx = at<float>(workspace, L.sx);
-  mark(0, s);
   // per-token absmax int8 codes: the int8 row pass with no outlier columns
-  w8::launch_int8_rows(X, x_dt == W8_DT_BF16, M, (int)K, 0x7F80u, q, sx, nullptr, w8::kProdNone, w8::ProdArgs{}, s);
-  mark(1, s);
-  mark(2, s);
+  w8::launch_int8_rows(X, x_dt == W8_DT_BF16, M, (int)K, 0x7F80u, q, sx, nullptr, 0u, w8::kProdNone, w8::ProdArgs{},
+                       s);
   const int ydt = y_dt == W8_DT_BF16 ? 0 : (y_dt == W8_DT_F16 ? 1 : 2);
-  w8::launch_w4a8_gemm(q, Wq4, M, N, K, sx, sw4, Y, ydt, L.plan, at<float>(workspace, L.part),
-                       at<int>(workspace, L.cnt), s);
-  mark(3, s);
+  w8::launch_w4a8_gemm(q, Wq4, M, N, K, sx, sw4, Y, ydt, plan, at<float>(workspace, L.part), at<int>(workspace, 0), s);
   return check_launch(what);
 }
 
 size_t w4a8_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
   if (M < 1 || N < 1 || K < 1) return 0;
-  return w4_layout(M, N, K, 0).total;
+  return w4_layout(M, K).base + plan_part(w4_plan(M, N, K, 0, kPlanCus));
 }
 
 w8_status w4a8_linear(const void* X, int x_dt, int64_t M, int64_t K, const uint8_t* Wq4, const float* sw4, int64_t N,
                       void* Y, int y_dt, void* workspace, size_t workspace_bytes, void* stream) {
   if (w8_status st = w4_checks(X, x_dt, M, K, Wq4, sw4, N, Y, y_dt); st != W8_OK) return st;
-  return w4_run(X, x_dt, M, K, Wq4, sw4, N, Y, y_dt, w4_layout(M, N, K, 0), workspace, workspace_bytes, stream,
-                "w4a8_linear");
+  if (w8_status st = check_ws(workspace, workspace_bytes, w4a8_linear_workspace_size(M, N, K)); st != W8_OK)
+    return st;
+  return w4_run(X, x_dt, M, K, Wq4, sw4, N, Y, y_dt, w4_plan(M, N, K, 0, cu_count()), workspace, workspace_bytes,
+                stream, "w4a8_linear");
 }
 
 // ---- parity exports ---------------------------------------------------------
 
+w8_status w8dbg_int8_mixed_linear_events(const void* H, int h_dt, int64_t M, int64_t K, const w8_producer* producer,
+                                         const int8_t* Wq, const float* sw, const float* bias, int64_t N,
+                                         float threshold, void* Y, int y_dt, void* workspace, size_t workspace_bytes,
+                                         void* const* events, void* stream) {
+  return int8_linear_impl(H, h_dt, M, K, producer, Wq, sw, bias, N, threshold, Y, y_dt, workspace, workspace_bytes,
+                          stream, events, "w8dbg_int8_mixed_linear_events");
+}
+
+w8_status w8dbg_fp8_w8a8_linear_events(const void* X, int x_dt, int64_t M, int64_t K, const uint8_t* Wq8,
+                                       const float* sw, int64_t N, const float* act_scale, void* Y, int y_dt,
+                                       void* workspace, size_t workspace_bytes, void* const* events, void* stream) {
+  return fp8_impl(X, x_dt, M, K, Wq8, sw, N, act_scale, Y, y_dt, workspace, workspace_bytes, stream, events,
+                  "w8dbg_fp8_w8a8_linear_events");
+}
+
+w8_status w8dbg_int8_workspace_layout(int64_t M, int64_t N, int64_t K, size_t* offsets) {
+  W8_REQUIRE(offsets, W8_ERR_INVALID_ARGUMENT, "null pointer argument");
+  W8_REQUIRE(M >= 1 && N >= 1 && K >= 1, W8_ERR_INVALID_ARGUMENT, "M, N, K must be >= 1");
+  const Int8Ws L = int8_layout(M, N, K);
+  const size_t v[11] = {L.cnt, L.flags, L.nO, L.O, L.q, L.sx, L.rstd, L.XO, L.WO, L.part,
+                        static_cast<size_t>(w8::kOutCap)};
+  std::memcpy(offsets, v, sizeof v);
+  return ok();
+}
+
 size_t w8dbg_w4a8_linear_workspace_size(int64_t M, int64_t N, int64_t K, int split) {
   if (M < 1 || N < 1 || K < 1 || split < 0) return 0;
-  return w4_layout(M, N, K, split).total;
+  return w4_layout(M, K).base + up(w4_plan(M, N, K, split, cu_count()).partial_bytes());
 }
 
 w8_status w8dbg_w4a8_linear(const void* X, int x_dt, int64_t M, int64_t K, const uint8_t* Wq4, const float* sw4,
@@ -571,14 +590,16 @@ w8_status w8dbg_w4a8_linear(const void* X, int x_dt, int64_t M, int64_t K, const
   if (w8_status st = w4_checks(X, x_dt, M, K, Wq4, sw4, N, Y, y_dt); st != W8_OK) return st;
   W8_REQUIRE(split >= 0, W8_ERR_INVALID_ARGUMENT, "split must be >= 0");
   W8_REQUIRE(split <= K / 128, W8_ERR_UNSUPPORTED, "split %d needs at most K / 128 slices", split);
-  return w4_run(X, x_dt, M, K, Wq4, sw4, N, Y, y_dt, w4_layout(M, N, K, split), workspace, workspace_bytes, stream,
-                "w8dbg_w4a8_linear");
+  const w8::GemmPlan p = w4_plan(M, N, K, split, cu_count());
+  W8_REQUIRE(p.counters() <= kCntCap, W8_ERR_UNSUPPORTED, "too many split tiles (%d > %d)", p.counters(), kCntCap);
+  const W4Ws L = w4_layout(M, K);
+  if (w8_status st = check_ws(workspace, workspace_bytes, L.base + up(p.partial_bytes())); st != W8_OK) return st;
+  return w4_run(X, x_dt, M, K, Wq4, sw4, N, Y, y_dt, p, workspace, workspace_bytes, stream, "w8dbg_w4a8_linear");
 }
-
 
 size_t w8dbg_fp8_w8a16_linear_workspace_size(int64_t M, int64_t N, int64_t K, int split, int tile) {
   if (M < 1 || N < 1 || K < 1 || split < 0) return 0;
-  return w16_layout(w16_plan(M, N, K, split, tile)).total;
+  return kFront + up(w16_plan(M, N, K, split, tile, cu_count()).partial_bytes());
 }
 
 w8_status w8dbg_fp8_w8a16_linear(const void* X, int x_dt, int64_t M, int64_t K, const uint8_t* Wq8,
@@ -588,14 +609,15 @@ w8_status w8dbg_fp8_w8a16_linear(const void* X, int x_dt, int64_t M, int64_t K, 
   W8_REQUIRE(split >= 0, W8_ERR_INVALID_ARGUMENT, "split must be >= 0");
   W8_REQUIRE(tile == 0 || tile == 128 || tile == 256, W8_ERR_INVALID_ARGUMENT, "tile must be 0, 128 or 256");
   W8_REQUIRE(split <= K / 64, W8_ERR_UNSUPPORTED, "split %d needs at most K / 64 slices", split);
-  return w16_run(X, M, K, Wq8, sw, N, Y, y_dt, w16_layout(w16_plan(M, N, K, split, tile)), workspace,
-                 workspace_bytes, stream, "w8dbg_fp8_w8a16_linear");
+  const w8::GemmPlan p = w16_plan(M, N, K, split, tile, cu_count());
+  W8_REQUIRE(p.counters() <= kCntCap, W8_ERR_UNSUPPORTED, "too many split tiles (%d > %d)", p.counters(), kCntCap);
+  if (w8_status st = check_ws(workspace, workspace_bytes, kFront + up(p.partial_bytes())); st != W8_OK) return st;
+  return w16_run(X, M, K, Wq8, sw, N, Y, y_dt, p, p, workspace, workspace_bytes, stream, "w8dbg_fp8_w8a16_linear");
 }
-
 
 size_t w8dbg_int8_quantize_activations_workspace_size(int64_t M, int64_t K) {
   if (M < 1 || K < 1) return 0;
-  return up(static_cast<size_t>(K)) + up(4 * static_cast<size_t>(M));
+  return kFront + up(4 * static_cast<size_t>(M));
 }
 
 w8_status w8dbg_int8_quantize_activations(const void* X, int x_dt, int64_t M, int64_t K,
@@ -612,19 +634,19 @@ w8_status w8dbg_int8_quantize_activations(const void* X, int x_dt, int64_t M, in
   if (w8_status st = check_ws(workspace, workspace_bytes, need); st != W8_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = x_dt == W8_DT_BF16;
-  uint8_t* flags = at<uint8_t>(workspace, 0);
-  pa.rstd = at<float>(workspace, up(static_cast<size_t>(K)));
+  uint32_t* flags = at<uint32_t>(workspace, kCntBytes);
+  pa.rstd = at<float>(workspace, kFront);
+  const uint32_t stamp = next_stamp();
   const uint32_t tb = threshold_bits(threshold, bf);
-  w8::launch_int8_rows(X, bf, M, (int)K, tb, q, sx, flags, kind, pa, s);
-  w8::launch_outlier_fixup(X, bf, M, (int)K, tb, flags, q, sx, outlier_idx, n_outliers, nullptr, nullptr, 0, nullptr,
-                           kind, pa, s);
-  w8::launch_clear_words(reinterpret_cast<uint32_t*>(flags), static_cast<int>(K / 4), s);
+  w8::launch_int8_rows(X, bf, M, (int)K, tb, q, sx, flags, stamp, kind, pa, s);
+  w8::launch_outlier_fixup(X, bf, M, (int)K, tb, flags, stamp, q, sx, outlier_idx, n_outliers, nullptr, nullptr, 0,
+                           nullptr, kind, pa, s);
   return check_launch("w8dbg_int8_quantize_activations");
 }
 
 size_t w8dbg_int8_gemm_i32_workspace_size(int64_t M, int64_t N, int64_t K, int tail, int split) {
   if (M < 1 || N < 1 || K < 1 || tail < 0 || tail > 2 || split < 1) return 0;
-  return gemm_layout(M, N, K, tail, split).total;
+  return kFront + up(int8_debug_plan(M, N, K, tail, split, cu_count()).partial_bytes());
 }
 
 w8_status w8dbg_int8_gemm_i32(const int8_t* q, const int8_t* Wq, int64_t M, int64_t N, int64_t K, int tail,
@@ -637,23 +659,19 @@ w8_status w8dbg_int8_gemm_i32(const int8_t* q, const int8_t* Wq, int64_t M, int6
              "this tail treatment needs K %% 64 == 0 and split <= K / 64");
   W8_REQUIRE(aligned16(q) && aligned16(Wq) && aligned16(acc), W8_ERR_INVALID_ARGUMENT,
              "pointers must be 16-byte aligned");
-  const GemmWs L = gemm_layout(M, N, K, tail, split);
-  if (L.total > 0) {
-    if (w8_status st = check_ws(workspace, workspace_bytes, L.total); st != W8_OK) return st;
-  }
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  int* cnt = L.total > 0 ? at<int>(workspace, L.cnt) : nullptr;
-  int* part = L.total > 0 ? at<int>(workspace, L.part) : nullptr;
-  w8::launch_int8_gemm(q, Wq, M, N, K, nullptr, nullptr, nullptr, nullptr, nullptr, true, nullptr, acc, 0, L.plan,
-                       part, cnt,
-                       nullptr, 0, s);
+  const w8::GemmPlan plan = int8_debug_plan(M, N, K, tail, split, cu_count());
+  W8_REQUIRE(plan.counters() <= kCntCap, W8_ERR_UNSUPPORTED, "too many split tiles (%d > %d)", plan.counters(),
+             kCntCap);
+  if (w8_status st = check_ws(workspace, workspace_bytes, kFront + up(plan.partial_bytes())); st != W8_OK) return st;
+  const w8::SideSrc none{nullptr, nullptr, nullptr, 0, w8::kProdNone, w8::ProdArgs{}};
+  w8::launch_int8_gemm(q, Wq, M, N, K, nullptr, nullptr, nullptr, nullptr, nullptr, true, nullptr, acc, 0, plan,
+                       at<int>(workspace, kFront), at<int>(workspace, 0), none, static_cast<hipStream_t>(stream));
   return check_launch("w8dbg_int8_gemm_i32");
 }
 
 size_t w8dbg_fp8_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int split, int tile) {
   if (M < 1 || N < 1 || K < 1 || split < 0) return 0;
-  const w8::GemmPlan plan = fp8_debug_plan(M, N, K, split, tile);
-  return up(4 * static_cast<size_t>(plan.counters())) + up(plan.partial_bytes());
+  return kFront + up(fp8_debug_plan(M, N, K, split, tile, cu_count()).partial_bytes());
 }
 
 w8_status w8dbg_fp8_gemm(const uint8_t* xq, const float* sx, const uint8_t* Wq8, const float* sw, int64_t M,
@@ -671,15 +689,13 @@ w8_status w8dbg_fp8_gemm(const uint8_t* xq, const float* sx, const uint8_t* Wq8,
              "split %d needs K %% 64 == 0 and at most K / 64 slices", split);
   W8_REQUIRE(aligned16(xq) && aligned16(sx) && aligned16(Wq8) && aligned16(sw) && aligned16(Y),
              W8_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
-  const w8::GemmPlan plan = fp8_debug_plan(M, N, K, split, tile);
-  const size_t cnt_bytes = up(4 * static_cast<size_t>(plan.counters()));
-  const size_t need = cnt_bytes + up(plan.partial_bytes());
-  if (need > 0) {
-    if (w8_status st = check_ws(workspace, workspace_bytes, need); st != W8_OK) return st;
-  }
+  const w8::GemmPlan plan = fp8_debug_plan(M, N, K, split, tile, cu_count());
+  W8_REQUIRE(plan.counters() <= kCntCap, W8_ERR_UNSUPPORTED, "too many split tiles (%d > %d)", plan.counters(),
+             kCntCap);
+  if (w8_status st = check_ws(workspace, workspace_bytes, kFront + up(plan.partial_bytes())); st != W8_OK) return st;
   const int ydt = y_dt == W8_DT_BF16 ? 0 : (y_dt == W8_DT_F16 ? 1 : 2);
-  w8::launch_fp8_gemm(xq, Wq8, M, N, K, sx, sw, Y, ydt, plan, need > 0 ? at<float>(workspace, cnt_bytes) : nullptr,
-                      need > 0 ? at<int>(workspace, 0) : nullptr, static_cast<hipStream_t>(stream));
+  w8::launch_fp8_gemm(xq, Wq8, M, N, K, sx, sw, Y, ydt, plan, at<float>(workspace, kFront), at<int>(workspace, 0),
+                      static_cast<hipStream_t>(stream));
   return check_launch("w8dbg_fp8_gemm");
 }
 

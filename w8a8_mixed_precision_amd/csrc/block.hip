@@ -22,6 +22,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "common.h"
 #include "launch.h"
 #include "w8mp.h"
 
@@ -95,22 +96,26 @@ size_t upb(size_t x) { return (x + kAlignB - 1) / kAlignB * kAlignB; }
 
 int block_cus() { return std::max(w8::device_cus(), 1); }
 
+// Block workspace: one int8 linear workspace, shared by the four linears
+// (its front and int8 layout serve calls of any shape in turn), then the
+// intermediates, then the 16-bit down-projection's split-K partials (its
+// counters are the front's).
 struct BlockWs {
-  size_t qkv, a, o, h, u, g, d, ws_qkv, ws_o, ws_up, ws_down, ws16, total;
-  size_t n_qkv, n_o, n_up, n_down, n16;
+  size_t ws8, qkv, a, o, h, u, g, d, part16, total;
+  size_t n8;
   w8::GemmPlan plan16;
 };
 
 BlockWs block_layout(int64_t M, int64_t D, int64_t F) {
   BlockWs w{};
-  w.n_qkv = int8_mixed_linear_workspace_size(M, 3 * D, D);
-  w.n_o = int8_mixed_linear_workspace_size(M, D, D);
-  w.n_up = int8_mixed_linear_workspace_size(M, F, D);
-  w.n_down = int8_mixed_linear_workspace_size(M, D, F);
-  w.plan16 = w8::plan_linear16(M, D, F, block_cus());
-  w.n16 = upb(4 * static_cast<size_t>(w.plan16.counters())) + upb(w.plan16.partial_bytes());
+  w.n8 = std::max({int8_mixed_linear_workspace_size(M, 3 * D, D), int8_mixed_linear_workspace_size(M, D, D),
+                   int8_mixed_linear_workspace_size(M, F, D), int8_mixed_linear_workspace_size(M, D, F)});
+  // sized for a 256-CU device; forward() runs this device's plan when it fits
+  w.plan16 = w8::plan_linear16(M, D, F, 256);
+  if (w.plan16.counters() > w8::kCntCap) w.plan16 = w8::plan_linear16_tail(M, D, 1, 256);
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t at = off; off = upb(off + bytes); return at; };
+  w.ws8 = take(w.n8);
   w.qkv = take(2 * static_cast<size_t>(M) * 3 * D);
   w.a = take(2 * static_cast<size_t>(M) * D);
   w.o = take(2 * static_cast<size_t>(M) * D);
@@ -118,13 +123,7 @@ BlockWs block_layout(int64_t M, int64_t D, int64_t F) {
   w.u = take(2 * static_cast<size_t>(M) * F);
   w.g = take(2 * static_cast<size_t>(M) * F);
   w.d = take(4 * static_cast<size_t>(M) * D);
-  // each linear keeps its own workspace: their bookkeeping (outlier flags,
-  // split-K counters) sits at shape-dependent offsets and must start zero
-  w.ws_qkv = take(w.n_qkv);
-  w.ws_o = take(w.n_o);
-  w.ws_up = take(w.n_up);
-  w.ws_down = take(w.n_down);
-  w.ws16 = take(w.n16);
+  w.part16 = take(w.plan16.partial_bytes());
   w.total = off;
   return w;
 }
@@ -174,29 +173,31 @@ w8_status w8_dit_block_forward(const w8_dit_block* blk, const void* X, int64_t M
 
   // qkv = Linear8(RMSNorm1(X))
   st = int8_mixed_linear_fused(X, W8_DT_F16, M, D, &blk->norm1, blk->w_qkv, blk->s_qkv, blk->b_qkv, 3 * D, t,
-                               at(L.qkv), W8_DT_F16, at(L.ws_qkv), L.n_qkv, stream);
+                               at(L.qkv), W8_DT_F16, at(L.ws8), L.n8, stream);
   if (st != W8_OK) return block_fail(st, "qkv: %s", w8_last_error());
   w8::launch_take_value(static_cast<const uint16_t*>(at(L.qkv)), M, static_cast<int>(D),
                         static_cast<uint16_t*>(at(L.a)), s);
   st = int8_mixed_linear_fused(at(L.a), W8_DT_F16, M, D, &none, blk->w_o, blk->s_o, blk->b_o, D, t, at(L.o),
-                               W8_DT_F16, at(L.ws_o), L.n_o, stream);
+                               W8_DT_F16, at(L.ws8), L.n8, stream);
   if (st != W8_OK) return block_fail(st, "o: %s", w8_last_error());
   w8::launch_residual(static_cast<const uint16_t*>(X), at(L.o), false, nullptr, M, static_cast<int>(D),
                       static_cast<uint16_t*>(at(L.h)), s);
   st = int8_mixed_linear_fused(at(L.h), W8_DT_F16, M, D, &blk->norm2, blk->w_up, blk->s_up, blk->b_up, F, t,
-                               at(L.u), W8_DT_F16, at(L.ws_up), L.n_up, stream);
+                               at(L.u), W8_DT_F16, at(L.ws8), L.n8, stream);
   if (st != W8_OK) return block_fail(st, "up: %s", w8_last_error());
   if (blk->w_down16) {
     // the massive-activation writer, unquantized: GELU(u) W16^T in 16 bit
     w8::launch_produce(at(L.u), false, M, static_cast<int>(F), w8::kProdGelu, w8::ProdArgs{}, at(L.g), s);
-    const size_t cnt_bytes = upb(4 * static_cast<size_t>(L.plan16.counters()));
-    w8::launch_linear16(static_cast<const uint16_t*>(at(L.g)), blk->w_down16, false, M, D, F, at(L.d), 2, L.plan16,
-                        reinterpret_cast<float*>(ws + L.ws16 + cnt_bytes), reinterpret_cast<int*>(ws + L.ws16), s);
+    w8::GemmPlan p16 = w8::plan_linear16(M, D, F, block_cus());
+    if (p16.counters() > w8::kCntCap || p16.partial_bytes() > L.plan16.partial_bytes())
+      p16 = w8::plan_linear16_tail(M, D, 1, block_cus());
+    w8::launch_linear16(static_cast<const uint16_t*>(at(L.g)), blk->w_down16, false, M, D, F, at(L.d), 2, p16,
+                        reinterpret_cast<float*>(ws + L.part16), reinterpret_cast<int*>(ws + L.ws8), s);
     w8::launch_residual(static_cast<const uint16_t*>(at(L.h)), at(L.d), true, blk->b_down, M, static_cast<int>(D),
                         static_cast<uint16_t*>(Y), s);
   } else {
     st = int8_mixed_linear_fused(at(L.u), W8_DT_F16, M, F, &gelu, blk->w_down, blk->s_down, blk->b_down, D, t,
-                                 at(L.d), W8_DT_F16, at(L.ws_down), L.n_down, stream);
+                                 at(L.d), W8_DT_F16, at(L.ws8), L.n8, stream);
     if (st != W8_OK) return block_fail(st, "down: %s", w8_last_error());
     w8::launch_residual(static_cast<const uint16_t*>(at(L.h)), at(L.d), false, nullptr, M, static_cast<int>(D),
                         static_cast<uint16_t*>(Y), s);
@@ -218,7 +219,18 @@ static w8::GemmPlan linear16_debug_plan(int64_t M, int64_t N, int64_t K, int spl
 size_t w8dbg_linear16_workspace_size(int64_t M, int64_t N, int64_t K, int split, int tile) {
   if (M < 1 || N < 1 || K < 1 || split < 0) return 0;
   const w8::GemmPlan p = linear16_debug_plan(M, N, K, split, tile);
-  return std::max<size_t>(upb(4 * static_cast<size_t>(p.counters())) + upb(p.partial_bytes()), kAlignB);
+  return w8::kFront + upb(p.partial_bytes());
+}
+
+// The offsets of the block's intermediates in its workspace (parity export):
+// qkv, a, o, h, u, g (GELU(u), written only with the 16-bit down-projection),
+// d (fp16, or fp32 with the 16-bit down-projection).
+w8_status w8dbg_dit_block_layout(int64_t M, int64_t D, int64_t F, size_t* offsets) {
+  if (!offsets || M < 1 || D < 1 || F < 1) return block_fail(W8_ERR_INVALID_ARGUMENT, "bad arguments");
+  const BlockWs L = block_layout(M, D, F);
+  const size_t v[7] = {L.qkv, L.a, L.o, L.h, L.u, L.g, L.d};
+  for (int i = 0; i < 7; ++i) offsets[i] = v[i];
+  return static_cast<w8_status>(w8::report_status(W8_OK, ""));
 }
 
 w8_status w8dbg_linear16(const void* X, int x_dt, int64_t M, int64_t K, const void* W, int64_t N, int split, int tile,
@@ -236,14 +248,14 @@ w8_status w8dbg_linear16(const void* X, int x_dt, int64_t M, int64_t K, const vo
   if (split > 0 && tile != 128 && tile != 256) return block_fail(W8_ERR_INVALID_ARGUMENT, "tile must be 128 or 256");
   if (!al16(X) || !al16(W) || !al16(Y)) return block_fail(W8_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
   const w8::GemmPlan p = linear16_debug_plan(M, N, K, split, tile);
-  const size_t cnt_bytes = upb(4 * static_cast<size_t>(p.counters()));
-  const size_t need = std::max<size_t>(cnt_bytes + upb(p.partial_bytes()), kAlignB);
+  if (p.counters() > w8::kCntCap) return block_fail(W8_ERR_UNSUPPORTED, "too many split tiles");
+  const size_t need = w8::kFront + upb(p.partial_bytes());
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & (kAlignB - 1)) != 0 || workspace_bytes < need)
     return block_fail(W8_ERR_WORKSPACE, "workspace must be 256-byte aligned and at least %zu bytes", need);
   const int ydt = y_dt == W8_DT_BF16 ? 0 : (y_dt == W8_DT_F16 ? 1 : 2);
   char* ws = static_cast<char*>(workspace);
   w8::launch_linear16(static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(W), x_dt == W8_DT_BF16, M, N, K,
-                      Y, ydt, p, reinterpret_cast<float*>(ws + cnt_bytes), reinterpret_cast<int*>(ws),
+                      Y, ydt, p, reinterpret_cast<float*>(ws + w8::kFront), reinterpret_cast<int*>(ws),
                       static_cast<hipStream_t>(stream));
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return block_fail(W8_ERR_HIP, "w8dbg_linear16: %s", hipGetErrorString(e));

@@ -21,6 +21,7 @@
 #include <type_traits>
 
 #include "launch.h"
+#include "produce.h"
 #include "tile.h"
 
 namespace w8 {
@@ -162,6 +163,42 @@ __device__ __forceinline__ void flush_cols(const char* stg, char* __restrict__ y
   }
 }
 
+// More outlier columns than the XO/WO staging holds (kOutCap): the side
+// product gathers them one by one, from X (made from H by the producer) and
+// from Wq, through the ascending outlier list. o[i] += the outlier product of
+// weight row n and rows m_base + 32 i (clamped into [M, N); rows past M are
+// computed and not stored).
+template <bool XBF16, int WT>
+__device__ __noinline__ void side_gather(v16f* o, const SideSrc& src, int M, int N, int n, int m_base, int nO, int P,
+                                         int fh) {
+  using V8 = typename std::conditional<XBF16, v8bf, v8h>::type;
+  using E = typename std::conditional<XBF16, __bf16, _Float16>::type;
+  const int8_t* wrow = src.Wq + static_cast<int64_t>(min(n, N - 1)) * src.K;
+  for (int c = 0; c < P; c += 16) {
+    int idx[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = c + 8 * fh + e;
+      idx[e] = j < nO ? src.O[j] : -1;
+    }
+    V8 wa;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wa[e] = static_cast<E>(idx[e] >= 0 ? static_cast<float>(wrow[idx[e]]) : 0.0f);
+    for (int i = 0; i < WT; ++i) {
+      const int m = min(m_base + 32 * i, M - 1);
+      const uint16_t* hrow = src.H + static_cast<int64_t>(m) * src.K;
+      const float rstd = src.prod == kProdRms ? src.pa.rstd[m] : 0.0f;
+      V8 xb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t b = idx[e] >= 0 ? produce1_any<XBF16>(src.prod, hrow[idx[e]], idx[e], rstd, src.pa) : 0u;
+        xb[e] = __builtin_bit_cast(E, static_cast<uint16_t>(b));
+      }
+      o[i] = mfma_side<XBF16>(wa, xb, o[i]);
+    }
+  }
+}
+
 // Epilogue shared by the GEMM kernels, for a wave tile of WT x WT 32x32 MFMA
 // tiles (WT = 4: 256x256 blocks, 2: 128x128 blocks). The MFMAs compute each
 // tile transposed (Wq fragment as the first operand), so element r of tile
@@ -179,7 +216,7 @@ template <int MODE, bool XBF16, int WT = 4>
 __device__ __forceinline__ void epilogue(v16i (&acc)[WT][WT], int M, int N, int m0, int n0, int wm, int wn, int lane,
                                          const float (&rsx)[4], const float* scol, const float* sbias, int nO,
                                          const uint16_t* __restrict__ XO, const uint16_t* __restrict__ WO,
-                                         const char* side, void* __restrict__ Y, char* stg) {
+                                         const SideSrc& src, const char* side, void* __restrict__ Y, char* stg) {
   const int fr = lane & 31, fh = lane >> 5;
   constexpr int EB = MODE == 1 ? 2 : 4;         // bytes per output element
   constexpr int WR = 32 * WT;                   // rows (= columns) of the wave tile
@@ -215,7 +252,7 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[WT][WT], int M, int N, int 
             o[i] = mfma_side<XBF16>(wa, xb, o[i]);
           }
         }
-      } else {
+      } else if (P <= kOutCap) {
         const int64_t wrow = static_cast<int64_t>(min(n0 + ncol + fr, N - 1)) * P;
         for (int c = 0; c < P; c += 16) {
           const V8 wa = *reinterpret_cast<const V8*>(WO + wrow + c + 8 * fh);
@@ -226,6 +263,8 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[WT][WT], int M, int N, int 
             o[i] = mfma_side<XBF16>(wa, xb, o[i]);
           }
         }
+      } else {
+        side_gather<XBF16, WT>(o, src, M, N, n0 + ncol + fr, row0 + fr, nO, P, fh);
       }
       stage_cols<MODE, true, WT>(acc, o, j, rsx, scol, sbias, ncol, lane, stg + soff);
     }
@@ -271,7 +310,7 @@ __device__ __forceinline__ void epi_prefetch(EpiIn& e, int M, int N, int m0, int
 template <int MODE, bool XBF16, int WT = 4>
 __device__ __forceinline__ void finish_tile(v16i (&acc)[WT][WT], EpiIn& e, char* lds, int M, int N, int m0, int n0,
                                             int wm, int wn, int lane, const uint16_t* __restrict__ XO,
-                                            const uint16_t* __restrict__ WO, const char* side,
+                                            const uint16_t* __restrict__ WO, const SideSrc& src, const char* side,
                                             void* __restrict__ Y) {
   float* scol = reinterpret_cast<float*>(lds);
   float* sbias = scol + 256;
@@ -282,7 +321,7 @@ __device__ __forceinline__ void finish_tile(v16i (&acc)[WT][WT], EpiIn& e, char*
     sbias[threadIdx.x] = e.my_bias;             // 0 without a bias
     __syncthreads();
   }
-  epilogue<MODE, XBF16, WT>(acc, M, N, m0, n0, wm, wn, lane, e.rsx, scol, sbias, e.nO, XO, WO, side, Y,
+  epilogue<MODE, XBF16, WT>(acc, M, N, m0, n0, wm, wn, lane, e.rsx, scol, sbias, e.nO, XO, WO, src, side, Y,
                             lds + kEpiCols + (threadIdx.x >> 6) * kStgWaveJ);
 }
 
@@ -306,8 +345,7 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm(const int8_t* __restrict__
                                                       const uint16_t* __restrict__ XO,
                                                       const uint16_t* __restrict__ WO,
                                                       const float* __restrict__ bias, void* __restrict__ Y,
-                                                      int tiles_m, int tiles_n, uint32_t* __restrict__ clear,
-                                                      int clear_words) {
+                                                      int tiles_m, int tiles_n, SideSrc src) {
   // two stages of A and B, and the epilogue's LDS after the K loop
   constexpr int kLdsBytes = 4 * kBM * kBK > kEpiLds8 ? 4 * kBM * kBK : kEpiLds8;
   __shared__ __attribute__((aligned(16))) int8_t lds_raw[kLdsBytes];
@@ -318,8 +356,6 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm(const int8_t* __restrict__
   const int m0 = tm * kBM, n0 = tn * kBN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  if (blockIdx.x == 0 && clear)                   // see k_int8_gemm_dma
-    for (int i = tid; i < clear_words; i += 256) clear[i] = 0u;
   EpiIn ein;
   epi_prefetch<MODE>(ein, M, N, m0, n0, wm, lane, sx, sw, bias, nO_ptr);
 
@@ -368,7 +404,7 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm(const int8_t* __restrict__
     __syncthreads();
   }
   finish_tile<MODE, XBF16>(acc, ein, reinterpret_cast<char*>(&lds[0][0][0]), M, N, m0, n0, wm, wn, lane, XO, WO,
-                           nullptr, Y);
+                           src, nullptr, Y);
 }
 
 // ---------------------------------------------------------------------------
@@ -538,7 +574,7 @@ __device__ __forceinline__ void small_block(int8_t* lds, const int8_t* __restric
                                             const uint16_t* __restrict__ XO, const uint16_t* __restrict__ WO,
                                             const float* __restrict__ bias, void* __restrict__ Y, int tiles_m,
                                             int tiles_n, int dp_tiles, int split, int* __restrict__ part,
-                                            int* __restrict__ cnt) {
+                                            int* __restrict__ cnt, const SideSrc& src) {
   constexpr int SS = 2 * S;                     // the same LDS as S big stages
   int* const s_last = reinterpret_cast<int*>(lds + kEpiLds8);
   const int nu = gridDim.x - dp_tiles;
@@ -630,7 +666,8 @@ __device__ __forceinline__ void small_block(int8_t* lds, const int8_t* __restric
         for (int e = 0; e < 4; ++e) acc[t >> 3][(t >> 2) & 1][4 * (t & 3) + e] += w[t][e];
     }
   }
-  finish_tile<MODE, XBF16, 2>(acc, ein, reinterpret_cast<char*>(lds), M, N, m0, n0, wm, wn, lane, XO, WO, nullptr, Y);
+  finish_tile<MODE, XBF16, 2>(acc, ein, reinterpret_cast<char*>(lds), M, N, m0, n0, wm, wn, lane, XO, WO, src, nullptr,
+                              Y);
 }
 
 // Work split for the last, partial wave of tiles (split-K). The first
@@ -651,7 +688,7 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
                                                           const float* __restrict__ bias, void* __restrict__ Y,
                                                           int tiles_m, int tiles_n, int dp_tiles, int split,
                                                           int small, int* __restrict__ part, int* __restrict__ cnt,
-                                                          uint32_t* __restrict__ clear, int clear_words) {
+                                                          SideSrc src) {
   constexpr int kStage = 2 * kBM * kBK;       // A then B, 32 KB
   constexpr int kLoads = 8;                   // DMA instructions per wave per step
   // the ring, then the tile's outlier operands (kSideLds)
@@ -665,13 +702,9 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
   int* const s_last = reinterpret_cast<int*>(lds + kEpiLds8);
   static_assert(S * kStage >= kEpiLds8 + 4, "epilogue LDS and arrival flag");
 
-  // The quantisation pass before this kernel is complete, so its outlier-column
-  // mask can be cleared here for the next call.
-  if (blockIdx.x == 0 && clear)
-    for (int i = threadIdx.x; i < clear_words; i += 256) clear[i] = 0u;
   if (small && static_cast<int>(blockIdx.x) >= dp_tiles) {
     small_block<MODE, XBF16, S>(lds, A, B, M, N, K, sx, sw, nO_ptr, XO, WO, bias, Y, tiles_m, tiles_n, dp_tiles,
-                                split, part, cnt);
+                                split, part, cnt, src);
     return;
   }
   const int nk_all = K / kBK;
@@ -815,7 +848,7 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
       }
     }
   }
-  finish_tile<MODE, XBF16>(acc, ein, reinterpret_cast<char*>(lds), M, N, m0, n0, wm, wn, lane, XO, WO,
+  finish_tile<MODE, XBF16>(acc, ein, reinterpret_cast<char*>(lds), M, N, m0, n0, wm, wn, lane, XO, WO, src,
                            side ? reinterpret_cast<const char*>(lds) + S * kStage : nullptr, Y);
 }
 
@@ -897,15 +930,15 @@ GemmPlan plan_int8_gemm_forced(int64_t M, int64_t N, int cus, bool small, int sp
 
 // ---------------------------------------------------------------------------
 // mode: 0 int32 acc, 1 fp16 out, 2 fp32 out. `part` / `cnt` are needed when
-// plan.split > 1 (plan.sk_tiles * plan.split partials, plan.sk_tiles counters
-// that must be zero; they are left zero). `clear` (may be null): clear_words
-// words that the kernel zeroes (the outlier-column mask of the pass before).
-// XO [M, P] and WO [N, P] (P = the outlier count nO padded to 32) may be null
-// when mode is 0; otherwise their buffers hold at least 32 values per row.
+// plan.split > 1 (plan.partial_bytes() of partials, plan.counters() counters
+// that must be zero; they are left zero). XO [M, P] and WO [N, P] (P = the
+// outlier count nO padded to 32) may be null when mode is 0; otherwise their
+// buffers hold kOutCap values per row. `src`: where the epilogue gathers the
+// outlier columns when P > kOutCap (unused in mode 0).
 void launch_int8_gemm(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t K, const float* sx,
                       const float* sw, const int* nO, const uint16_t* XO, const uint16_t* WO, bool xbf16,
                       const float* bias, void* Y, int mode, const GemmPlan& plan, int* part, int* cnt,
-                      uint32_t* clear, int clear_words, hipStream_t s) {
+                      const SideSrc& src, hipStream_t s) {
   const int tiles_m = plan.tiles_m, tiles_n = plan.tiles_n;
   const int m = (int)M, n = (int)N, k = (int)K;
   const dim3 block(256);
@@ -913,7 +946,7 @@ void launch_int8_gemm(const int8_t* A, const int8_t* B, int64_t M, int64_t N, in
     constexpr int S = 4;
     const dim3 grid(plan.grid());
 #define W8_GEMM_ARGS A, B, m, n, k, sx, sw, nO, XO, WO, bias, Y, tiles_m, tiles_n, plan.dp_tiles, plan.split, \
-    plan.small ? 1 : 0, part, cnt, clear, clear_words
+    plan.small ? 1 : 0, part, cnt, src
     if (mode == 0) k_int8_gemm_dma<0, true, S><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
     else if (mode == 1 && xbf16) k_int8_gemm_dma<1, true, S><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
     else if (mode == 1) k_int8_gemm_dma<1, false, S><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
@@ -922,7 +955,7 @@ void launch_int8_gemm(const int8_t* A, const int8_t* B, int64_t M, int64_t N, in
 #undef W8_GEMM_ARGS
   } else {
     const dim3 grid(tiles_m * tiles_n);
-#define W8_GEMM_ARGS A, B, m, n, k, sx, sw, nO, XO, WO, bias, Y, tiles_m, tiles_n, clear, clear_words
+#define W8_GEMM_ARGS A, B, m, n, k, sx, sw, nO, XO, WO, bias, Y, tiles_m, tiles_n, src
     if (mode == 0) k_int8_gemm<0, true><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
     else if (mode == 1 && xbf16) k_int8_gemm<1, true><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
     else if (mode == 1) k_int8_gemm<1, false><<<grid, block, 0, s>>>(W8_GEMM_ARGS);

@@ -34,23 +34,50 @@ struct GemmPlan {
 GemmPlan plan_int8_gemm(int64_t M, int64_t N, int64_t K, int cus);
 GemmPlan plan_int8_gemm_forced(int64_t M, int64_t N, int cus, bool small, int split);
 
+// The front of every workspace (abi.hip): kCntCap split-K arrival counters
+// (zero between calls), then the int8 outlier-column flag words, one per
+// column up to the largest int8 K, 133144 (stamped per call, never cleared).
+// Shape-dependent regions follow it.
+constexpr int kCntCap = 4096;
+constexpr size_t kCntBytes = 4 * static_cast<size_t>(kCntCap);
+constexpr size_t kFlagBytes = (4 * static_cast<size_t>(133144) + 255) / 256 * 256;
+constexpr size_t kFront = kCntBytes + kFlagBytes;
+
+// Outlier columns whose 16-bit values the fix-up stages for the GEMM (XO
+// [M, kOutCap], WO [N, kOutCap] in the workspace); a call with more gathers
+// them in the GEMM's epilogue instead.
+constexpr int kOutCap = 256;
+
+// Where the GEMM epilogue gathers the outlier columns when they do not fit
+// the staging: X is made from H [M, K] by the producer `prod` (pa.rstd: the
+// row pass's RMSNorm rstd), the weights come from Wq [N, K], the columns from
+// the ascending list O.
+struct SideSrc {
+  const uint16_t* H;
+  const int8_t* Wq;
+  const int* O;
+  int K;
+  int prod;
+  ProdArgs pa;
+};
+
 // prod: producer of X from H (kProdNone / kProdRms / kProdGelu of producer.h;
-// rows with a producer need K <= 16384); pa: its parameters.
+// rows with a producer need K <= 16384); pa: its parameters. flags: one word
+// per column, set to `stamp` where some |x| > t (null: weight pass).
 void launch_int8_rows(const void* X, bool bf16, int64_t rows, int K, uint32_t tbits, int8_t* q, float* sx,
-                      uint8_t* flags, int prod, const ProdArgs& pa, hipStream_t s);
+                      uint32_t* flags, uint32_t stamp, int prod, const ProdArgs& pa, hipStream_t s);
 size_t outlier_fixup_lds_bytes(int K);
-void launch_outlier_fixup(const void* X, bool bf16, int64_t M, int K, uint32_t tbits, const uint8_t* colflag,
-                          int8_t* q, float* sx, int* O, int* nO, uint16_t* XO, const int8_t* Wq, int64_t N,
-                          uint16_t* WO, int prod, const ProdArgs& pa, hipStream_t s);
+void launch_outlier_fixup(const void* X, bool bf16, int64_t M, int K, uint32_t tbits, const uint32_t* colflag,
+                          uint32_t stamp, int8_t* q, float* sx, int* O, int* nO, uint16_t* XO, const int8_t* Wq,
+                          int64_t N, uint16_t* WO, int prod, const ProdArgs& pa, hipStream_t s);
 void launch_produce(const void* H, bool bf16, int64_t M, int K, int prod, const ProdArgs& pa, void* X,
                     hipStream_t s);
-void launch_clear_words(uint32_t* p, int n, hipStream_t s);
 void launch_fp8_rows(const void* X, bool bf16, int64_t rows, int K, const float* act_scale, uint8_t* xq, float* sx,
                      int mode, hipStream_t s);
 void launch_int8_gemm(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t K, const float* sx,
                       const float* sw, const int* nO, const uint16_t* XO, const uint16_t* WO, bool xbf16,
                       const float* bias, void* Y, int mode, const GemmPlan& plan, int* part, int* cnt,
-                      uint32_t* clear, int clear_words, hipStream_t s);
+                      const SideSrc& src, hipStream_t s);
 GemmPlan plan_fp8_gemm(int64_t M, int64_t N, int64_t K, int cus);
 GemmPlan plan_fp8_gemm_split(int64_t M, int64_t N, int split, int bm);
 void launch_fp8_gemm(const uint8_t* A, const uint8_t* B, int64_t M, int64_t N, int64_t K, const float* sx,

@@ -1,0 +1,102 @@
+// Measured peaks of the matrix cores (parity/measurement export of libw8mp):
+// every wave issues `iters` rounds of back-to-back MFMAs on register
+// operands, four independent accumulators in turn so that no instruction
+// waits for the previous one's result, and stores a checksum so that nothing
+// is optimised away. The rate this reaches with every SIMD busy is the
+// chip's attainable dense MFMA peak at the clock it holds under that load;
+// GEMM fractions can be read against it beside the published figure.
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+#include "w8mp.h"
+
+namespace w8 {
+
+namespace {
+
+typedef int v16i_ __attribute__((ext_vector_type(16)));
+typedef float v16f_ __attribute__((ext_vector_type(16)));
+
+// kind 0: v_mfma_i32_32x32x32_i8 (2*32*32*32 ops); 1: v_mfma_scale_f32_32x32x64_f8f6f4
+// with E4M3 operands (2*32*32*64 flops); 2: v_mfma_f32_32x32x16_bf16 (2*32*32*16).
+template <int KIND>
+__global__ __launch_bounds__(256) void k_mfma_peak(int iters, int seed, unsigned* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  unsigned sum = 0;
+  if constexpr (KIND == 0) {
+    v4i a = {seed + lane, 3, 5, 7}, b = {seed ^ lane, 11, 13, 17};
+    v16i_ c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) c[j][r] = 0;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c[j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sum += static_cast<unsigned>(c[j][r]);
+  } else if constexpr (KIND == 1) {
+    v8i a = {0x38383838 + lane, 0x38383838, 0x30303030, 0x38383838, 0x38383838, 0x30303030, 0x38383838, 0x38383838};
+    v8i b = a;
+    v16f_ c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) c[j][r] = 0.0f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        c[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c[j], 0, 0, 0, 127, 0, 127);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sum += __float_as_uint(c[j][r]);
+  } else {
+    v8bf a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[e] = static_cast<__bf16>(static_cast<float>(e + lane) * 0.125f);
+      b[e] = static_cast<__bf16>(static_cast<float>(e ^ seed) * 0.25f);
+    }
+    v16f_ c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) c[j][r] = 0.0f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sum += __float_as_uint(c[j][r]);
+  }
+  out[blockIdx.x * blockDim.x + threadIdx.x] = sum;
+}
+
+}  // namespace
+
+}  // namespace w8
+
+extern "C" {
+
+// See include/w8mp.h.
+w8_status w8dbg_mfma_peak(int kind, int blocks, int iters, unsigned* out, double* ops, void* stream) {
+  if (!out || !ops || kind < 0 || kind > 2 || blocks < 1 || iters < 1)
+    return W8_ERR_INVALID_ARGUMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(blocks), block(256);
+  if (kind == 0) w8::k_mfma_peak<0><<<grid, block, 0, s>>>(iters, 1, out);
+  else if (kind == 1) w8::k_mfma_peak<1><<<grid, block, 0, s>>>(iters, 1, out);
+  else w8::k_mfma_peak<2><<<grid, block, 0, s>>>(iters, 1, out);
+  const double per_inst = kind == 0 ? 2.0 * 32 * 32 * 32 : (kind == 1 ? 2.0 * 32 * 32 * 64 : 2.0 * 32 * 32 * 16);
+  *ops = per_inst * 4.0 * iters * (static_cast<double>(blocks) * 4.0);   // 4 waves per block, 4 per round
+  return hipGetLastError() == hipSuccess ? W8_OK : W8_ERR_HIP;
+}
+
+}  // extern "C"

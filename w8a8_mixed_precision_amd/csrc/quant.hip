@@ -23,8 +23,11 @@
 // 16-bit integers (bits & 0x7FFF): |x| > t exactly when the magnitude bits
 // exceed those of the largest representable value <= t. Non-finite values
 // have the largest patterns: with a finite t they are outliers.
+#include <algorithm>
+
 #include "common.h"
-#include "producer.h"
+#include "launch.h"
+#include "produce.h"
 
 namespace w8 {
 
@@ -69,10 +72,11 @@ __device__ __forceinline__ uint2 encode8(const uint4& v, float r) {
 }
 
 // Packed maximum of the magnitudes <= t of one chunk; the columns of the
-// magnitudes > t get a flag byte of 1 (a plain store: many rows flag the same
-// few columns, and equal plain stores need no atomics).
+// magnitudes > t get this call's stamp in their flag word (a plain store: many
+// rows flag the same few columns, and equal plain stores need no atomics).
 template <bool ACT>
-__device__ __forceinline__ uint32_t chunk_scan(const uint4& v, uint32_t t2, uint8_t* __restrict__ flags, int c) {
+__device__ __forceinline__ uint32_t chunk_scan(const uint4& v, uint32_t t2, uint32_t* __restrict__ flags, int c,
+                                               uint32_t stamp) {
   uint32_t w[4] = {v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu, v.z & 0x7FFF7FFFu, v.w & 0x7FFF7FFFu};
   if constexpr (ACT) {
     uint32_t gt[4], any = 0;
@@ -85,8 +89,8 @@ __device__ __forceinline__ uint32_t chunk_scan(const uint4& v, uint32_t t2, uint
     if (any) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (gt[i] & 0xFFFFu) flags[8 * c + 2 * i] = 1;
-        if (gt[i] >> 16) flags[8 * c + 2 * i + 1] = 1;
+        if (gt[i] & 0xFFFFu) flags[8 * c + 2 * i] = stamp;
+        if (gt[i] >> 16) flags[8 * c + 2 * i + 1] = stamp;
       }
     }
   }
@@ -113,22 +117,21 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 
 // --------------------------------------------------------------------------
 // Row pass, register form (K <= 16384): W = ceil(K / 4096) waves per row, each
-// covering a 4096-column slice, 8 chunks of 8 elements per lane; a block of
-// 256 threads holds 4/W rows. With W == 1 the row reduction stays inside one
-// wave (no LDS, no barrier).
+// covering a 4096-column slice, 8 chunks of 8 elements per lane; a block of NW
+// waves holds NW/W rows per iteration. With W == 1 the row reduction stays
+// inside one wave (no LDS, no barrier).
 //
 // With a producer (PROD != kProdNone) the loaded values are H, and X is made
-// from them in registers (producer.h) before anything else; RMSNorm first
+// from them in registers (produce.h) before anything else; RMSNorm first
 // reduces the row's sum of squares and stores the row's rstd for the fix-up.
-template <bool BF16, int W, bool ACT, int PROD>
-__global__ __launch_bounds__(256) void k_int8_rows(const uint16_t* __restrict__ X, int64_t rows, int K,
-                                                   uint32_t tbits, int8_t* __restrict__ q, float* __restrict__ sx,
-                                                   uint8_t* __restrict__ flags, ProdArgs pa) {
-  constexpr int kRows = 4 / W;
-  __shared__ uint32_t red[4];
-  __shared__ double red64[4];
+// flags: one word per column; a column with some |x| > t gets `stamp`.
+template <bool BF16, int W, int NW, bool ACT, int PROD>
+__device__ __forceinline__ void rows_iter(const uint16_t* __restrict__ X, int64_t rows, int K, uint32_t tbits,
+                                          int8_t* __restrict__ q, float* __restrict__ sx,
+                                          uint32_t* __restrict__ flags, uint32_t stamp, const ProdArgs& pa,
+                                          int64_t row0, uint32_t* red, double* red64, const uint16_t* gelu) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRows + wave / W;
+  const int64_t row = row0 + wave / W;
   const bool valid = row < rows;
   const int part = wave % W;
   const int nch = K >> 3;
@@ -169,7 +172,7 @@ __global__ __launch_bounds__(256) void k_int8_rows(const uint16_t* __restrict__ 
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int c = part * 512 + lane + 64 * i;
-        if (c < nch) v[i] = produce8<BF16, PROD>(v[i], c, rstd, pa);
+        if (c < nch) v[i] = produce8<BF16, PROD>(v[i], c, rstd, pa, gelu);
       }
     }
   }
@@ -178,7 +181,7 @@ __global__ __launch_bounds__(256) void k_int8_rows(const uint16_t* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int c = part * 512 + lane + 64 * i;
-      if (c < nch) mx = pk_max_u16(mx, chunk_scan<ACT>(v[i], t2, flags, c));
+      if (c < nch) mx = pk_max_u16(mx, chunk_scan<ACT>(v[i], t2, flags, c, stamp));
     }
   }
   mx = wave_max_u32(max(mx & 0xFFFFu, mx >> 16));
@@ -188,6 +191,7 @@ __global__ __launch_bounds__(256) void k_int8_rows(const uint16_t* __restrict__ 
     const int w0 = (wave / W) * W;
 #pragma unroll
     for (int w = 0; w < W; ++w) mx = max(mx, red[w0 + w]);
+    __syncthreads();                             // red and red64 are reused by the next iteration
   }
   if (!valid) return;
   const float s = decode_mag<BF16>(mx);
@@ -201,11 +205,44 @@ __global__ __launch_bounds__(256) void k_int8_rows(const uint16_t* __restrict__ 
   if (part == 0 && lane == 0) sx[row] = s;
 }
 
+template <bool BF16, int W, bool ACT, int PROD>
+__global__ __launch_bounds__(256) void k_int8_rows(const uint16_t* __restrict__ X, int64_t rows, int K,
+                                                   uint32_t tbits, int8_t* __restrict__ q, float* __restrict__ sx,
+                                                   uint32_t* __restrict__ flags, uint32_t stamp, ProdArgs pa) {
+  __shared__ uint32_t red[4];
+  __shared__ double red64[4];
+  rows_iter<BF16, W, 4, ACT, PROD>(X, rows, K, tbits, q, sx, flags, stamp, pa,
+                                   static_cast<int64_t>(blockIdx.x) * (4 / W), red, red64, nullptr);
+}
+
+// The GELU-fused row pass: X = gelu(H) from the format's table, copied once
+// into LDS by each block (128 KB, so one block of 8 waves per CU); the blocks
+// then walk the row groups grid-stride.
+constexpr int kGeluWaves = 8;
+
+template <bool BF16, int W>
+__global__ __launch_bounds__(64 * kGeluWaves) void k_int8_rows_gelu(const uint16_t* __restrict__ X, int64_t rows,
+                                                                    int K, uint32_t tbits, int8_t* __restrict__ q,
+                                                                    float* __restrict__ sx,
+                                                                    uint32_t* __restrict__ flags, uint32_t stamp) {
+  __shared__ __attribute__((aligned(16))) uint16_t gtab[65536];
+  __shared__ uint32_t red[kGeluWaves];
+  __shared__ double red64[kGeluWaves];
+  gelu_table_to_lds<BF16>(gtab);
+  __syncthreads();
+  constexpr int kRows = kGeluWaves / W;
+  const ProdArgs none{nullptr, nullptr, nullptr, 0.0f, nullptr};
+  for (int64_t row0 = static_cast<int64_t>(blockIdx.x) * kRows; row0 < rows;
+       row0 += static_cast<int64_t>(gridDim.x) * kRows)
+    rows_iter<BF16, W, kGeluWaves, true, kProdGelu>(X, rows, K, tbits, q, sx, flags, stamp, none, row0, red, red64,
+                                                    gtab);
+}
+
 // Row pass, streaming form for K > 16384: one block per row, two passes.
 template <bool BF16, bool ACT>
 __global__ __launch_bounds__(256) void k_int8_rows_long(const uint16_t* __restrict__ X, int K, uint32_t tbits,
                                                         int8_t* __restrict__ q, float* __restrict__ sx,
-                                                        uint8_t* __restrict__ flags) {
+                                                        uint32_t* __restrict__ flags, uint32_t stamp) {
   __shared__ uint32_t red[4];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t row = blockIdx.x;
@@ -214,7 +251,7 @@ __global__ __launch_bounds__(256) void k_int8_rows_long(const uint16_t* __restri
   const uint4* xr = reinterpret_cast<const uint4*>(X + row * K);
   uint32_t mx = 0;
 #pragma unroll 4
-  for (int c = threadIdx.x; c < nch; c += 256) mx = pk_max_u16(mx, chunk_scan<ACT>(xr[c], t2, flags, c));
+  for (int c = threadIdx.x; c < nch; c += 256) mx = pk_max_u16(mx, chunk_scan<ACT>(xr[c], t2, flags, c, stamp));
   mx = wave_max_u32(max(mx & 0xFFFFu, mx >> 16));
   if (lane == 0) red[wave] = mx;
   __syncthreads();
@@ -236,7 +273,10 @@ __global__ __launch_bounds__(256) void k_int8_rows_long(const uint16_t* __restri
 // LDS), then spreads (row, outlier slot) pairs over all threads, so the
 // scattered loads of a block are all in flight together. Dynamic LDS: mask
 // words, their exclusive popcount prefix, and the outlier list (up to kOcap
-// entries; a larger set takes the per-row loops).
+// entries; a larger set takes the per-row loops). A column is an outlier
+// column when its flag word holds this call's stamp. XO and WO are written
+// only when the padded outlier count fits their kOutCap columns; beyond that
+// the GEMM gathers the outlier columns itself.
 constexpr int kFixRows = 16;
 constexpr int kFixWRows = 64;
 constexpr int kOcap = 4096;
@@ -252,8 +292,8 @@ size_t outlier_fixup_lds_bytes(int K) {
 // from H again.
 template <bool BF16, int PROD>
 __global__ __launch_bounds__(256) void k_outlier_fixup(
-    const uint16_t* __restrict__ X, int M, int K, uint32_t tbits, const uint8_t* __restrict__ colflag,
-    int8_t* __restrict__ q, float* __restrict__ sx, int* __restrict__ O, int* __restrict__ nO_out,
+    const uint16_t* __restrict__ X, int M, int K, uint32_t tbits, const uint32_t* __restrict__ colflag,
+    uint32_t stamp, int8_t* __restrict__ q, float* __restrict__ sx, int* __restrict__ O, int* __restrict__ nO_out,
     uint16_t* __restrict__ XO, const int8_t* __restrict__ Wq, int N, uint16_t* __restrict__ WO, int xblocks,
     ProdArgs pa) {
   extern __shared__ uint32_t smem[];
@@ -279,14 +319,16 @@ __global__ __launch_bounds__(256) void k_outlier_fixup(
     if (w < nwords) {
       if (32 * w + 32 <= K) {
         const uint4* fp = reinterpret_cast<const uint4*>(colflag + 32 * w);
-        const uint4 a = fp[0], b = fp[1];
-        const uint32_t wd[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) bits |= ((wd[i] >> (8 * j)) & 1u) << (4 * i + j);
+        for (int i = 0; i < 8; ++i) {
+          const uint4 a = fp[i];
+          bits |= (a.x == stamp ? 1u : 0u) << (4 * i);
+          bits |= (a.y == stamp ? 1u : 0u) << (4 * i + 1);
+          bits |= (a.z == stamp ? 1u : 0u) << (4 * i + 2);
+          bits |= (a.w == stamp ? 1u : 0u) << (4 * i + 3);
+        }
       } else {
-        for (int j = 0; 32 * w + j < K; ++j) bits |= static_cast<uint32_t>(colflag[32 * w + j] & 1u) << j;
+        for (int j = 0; 32 * w + j < K; ++j) bits |= (colflag[32 * w + j] == stamp ? 1u : 0u) << j;
       }
       smask[w] = bits;
     }
@@ -308,6 +350,8 @@ __global__ __launch_bounds__(256) void k_outlier_fixup(
   const int nO = carry;
   const int P = (nO + 31) & ~31;
   const bool listed = nO <= kOcap;
+  if (P > kOutCap) XO = nullptr, WO = nullptr;    // the GEMM gathers the outlier columns itself
+  const uint16_t* gelu = gelu_table_global<BF16>();
 
   // ascending outlier list: in LDS for this block, in global memory from block 0
   for (int w = tid; w < nwords; w += 256) {
@@ -338,7 +382,7 @@ __global__ __launch_bounds__(256) void k_outlier_fixup(
     // note per row the largest gathered magnitude <= t
     auto take = [&](int r, int64_t m, int k) -> uint16_t {
       const uint16_t v = static_cast<uint16_t>(produce1<BF16, PROD>(X[m * K + k], k,
-                                                                   PROD == kProdRms ? srstd[r] : 0.0f, pa));
+                                                                   PROD == kProdRms ? srstd[r] : 0.0f, pa, gelu));
       q[m * K + k] = 0;
       const uint32_t mag = v & 0x7FFFu;
       if (mag <= tbits) atomicMax(&somax[r], mag);
@@ -366,7 +410,8 @@ __global__ __launch_bounds__(256) void k_outlier_fixup(
           const int64_t m = r0 + r;
           uint16_t val = 0;
           if (j < nO) {
-            val = static_cast<uint16_t>(produce1<BF16, PROD>(v[u], sO[j], PROD == kProdRms ? srstd[r] : 0.0f, pa));
+            val = static_cast<uint16_t>(
+                produce1<BF16, PROD>(v[u], sO[j], PROD == kProdRms ? srstd[r] : 0.0f, pa, gelu));
             q[m * K + sO[j]] = 0;
             const uint32_t mag = val & 0x7FFFu;
             if (mag <= tbits) atomicMax(&somax[r], mag);
@@ -444,7 +489,7 @@ __global__ __launch_bounds__(256) void k_outlier_fixup(
         for (int i = 0; i < 8; ++i) {
           const int c = tid + 256 * i;
           if (c < nch) {
-            xv[i] = produce8<BF16, PROD>(xr[c], c, rr_std, pa);
+            xv[i] = produce8<BF16, PROD>(xr[c], c, rr_std, pa, gelu);
             float f[8];
             unpack8<BF16>(xv[i], f);
             chunk_best(f, c);
@@ -606,48 +651,52 @@ __global__ __launch_bounds__(256) void k_fp8_rows(const uint16_t* __restrict__ X
 // --------------------------------------------------------------------------
 // Host-side launchers (called by the ABI layer after validation).
 
-__global__ void k_clear_words(uint32_t* __restrict__ p, int n) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
-}
-
-void launch_clear_words(uint32_t* p, int n, hipStream_t s) {
-  k_clear_words<<<dim3((n + 255) / 256 < 64 ? (n + 255) / 256 : 64), dim3(256), 0, s>>>(p, n);
-}
-
 template <bool BF16, bool ACT, int PROD>
 static void launch_int8_rows_t(const uint16_t* X, int64_t rows, int K, uint32_t tbits, int8_t* q, float* sx,
-                               uint8_t* flags, const ProdArgs& pa, hipStream_t s) {
+                               uint32_t* flags, uint32_t stamp, const ProdArgs& pa, hipStream_t s) {
   const dim3 block(256);
   auto blocks = [&](int rpb) { return dim3(static_cast<unsigned>((rows + rpb - 1) / rpb)); };
-  if (K <= 4096)
-    k_int8_rows<BF16, 1, ACT, PROD><<<blocks(4), block, 0, s>>>(X, rows, K, tbits, q, sx, flags, pa);
-  else if (K <= 8192)
-    k_int8_rows<BF16, 2, ACT, PROD><<<blocks(2), block, 0, s>>>(X, rows, K, tbits, q, sx, flags, pa);
-  else if (K <= 16384)
-    k_int8_rows<BF16, 4, ACT, PROD><<<blocks(1), block, 0, s>>>(X, rows, K, tbits, q, sx, flags, pa);
-  else if constexpr (PROD == kProdNone)
-    k_int8_rows_long<BF16, ACT><<<dim3(static_cast<unsigned>(rows)), block, 0, s>>>(X, K, tbits, q, sx, flags);
+  if constexpr (PROD == kProdGelu) {
+    // one block per CU at most (the 128 KB table fills the LDS)
+    const int W = K <= 4096 ? 1 : (K <= 8192 ? 2 : 4);
+    const int64_t groups = (rows + kGeluWaves / W - 1) / (kGeluWaves / W);
+    const dim3 grid(static_cast<unsigned>(std::min<int64_t>(groups, std::max(device_cus(), 1))));
+    const dim3 gblock(64 * kGeluWaves);
+    if (W == 1) k_int8_rows_gelu<BF16, 1><<<grid, gblock, 0, s>>>(X, rows, K, tbits, q, sx, flags, stamp);
+    else if (W == 2) k_int8_rows_gelu<BF16, 2><<<grid, gblock, 0, s>>>(X, rows, K, tbits, q, sx, flags, stamp);
+    else k_int8_rows_gelu<BF16, 4><<<grid, gblock, 0, s>>>(X, rows, K, tbits, q, sx, flags, stamp);
+  } else if (K <= 4096) {
+    k_int8_rows<BF16, 1, ACT, PROD><<<blocks(4), block, 0, s>>>(X, rows, K, tbits, q, sx, flags, stamp, pa);
+  } else if (K <= 8192) {
+    k_int8_rows<BF16, 2, ACT, PROD><<<blocks(2), block, 0, s>>>(X, rows, K, tbits, q, sx, flags, stamp, pa);
+  } else if (K <= 16384) {
+    k_int8_rows<BF16, 4, ACT, PROD><<<blocks(1), block, 0, s>>>(X, rows, K, tbits, q, sx, flags, stamp, pa);
+  } else if constexpr (PROD == kProdNone) {
+    k_int8_rows_long<BF16, ACT><<<dim3(static_cast<unsigned>(rows)), block, 0, s>>>(X, K, tbits, q, sx, flags,
+                                                                                    stamp);
+  }
 }
 
 template <bool BF16>
 static void launch_int8_rows_b(const uint16_t* X, int64_t rows, int K, uint32_t tbits, int8_t* q, float* sx,
-                               uint8_t* flags, int prod, const ProdArgs& pa, hipStream_t s) {
-  if (!flags) launch_int8_rows_t<BF16, false, kProdNone>(X, rows, K, tbits, q, sx, flags, pa, s);
-  else if (prod == kProdRms) launch_int8_rows_t<BF16, true, kProdRms>(X, rows, K, tbits, q, sx, flags, pa, s);
-  else if (prod == kProdGelu) launch_int8_rows_t<BF16, true, kProdGelu>(X, rows, K, tbits, q, sx, flags, pa, s);
-  else launch_int8_rows_t<BF16, true, kProdNone>(X, rows, K, tbits, q, sx, flags, pa, s);
+                               uint32_t* flags, uint32_t stamp, int prod, const ProdArgs& pa, hipStream_t s) {
+  if (!flags) launch_int8_rows_t<BF16, false, kProdNone>(X, rows, K, tbits, q, sx, flags, stamp, pa, s);
+  else if (prod == kProdRms) launch_int8_rows_t<BF16, true, kProdRms>(X, rows, K, tbits, q, sx, flags, stamp, pa, s);
+  else if (prod == kProdGelu) launch_int8_rows_t<BF16, true, kProdGelu>(X, rows, K, tbits, q, sx, flags, stamp, pa, s);
+  else launch_int8_rows_t<BF16, true, kProdNone>(X, rows, K, tbits, q, sx, flags, stamp, pa, s);
 }
 
 // flags == nullptr: weight pass (no threshold, no producer). A producer needs
 // K <= 16384 (checked by the caller).
 void launch_int8_rows(const void* X, bool bf16, int64_t rows, int K, uint32_t tbits, int8_t* q, float* sx,
-                      uint8_t* flags, int prod, const ProdArgs& pa, hipStream_t s) {
+                      uint32_t* flags, uint32_t stamp, int prod, const ProdArgs& pa, hipStream_t s) {
   const uint16_t* x = static_cast<const uint16_t*>(X);
-  if (bf16) launch_int8_rows_b<true>(x, rows, K, tbits, q, sx, flags, prod, pa, s);
-  else launch_int8_rows_b<false>(x, rows, K, tbits, q, sx, flags, prod, pa, s);
+  if (bf16) launch_int8_rows_b<true>(x, rows, K, tbits, q, sx, flags, stamp, prod, pa, s);
+  else launch_int8_rows_b<false>(x, rows, K, tbits, q, sx, flags, stamp, prod, pa, s);
 }
 
-// X = producer(H) written out (parity export): one block per row.
+// X = producer(H) written out (the parity export, and the GELU before the
+// 16-bit down-projection of the block driver). RMSNorm: one block per row.
 template <bool BF16, int PROD>
 __global__ __launch_bounds__(256) void k_produce(const uint16_t* __restrict__ H, int K, ProdArgs pa,
                                                  uint16_t* __restrict__ X) {
@@ -666,42 +715,72 @@ __global__ __launch_bounds__(256) void k_produce(const uint16_t* __restrict__ H,
     ss = ((red64[0] + red64[1]) + red64[2]) + red64[3];
     rstd = rms_rstd(ss, K, pa.eps);
   }
-  for (int c = threadIdx.x; c < nch; c += 256) xr[c] = produce8<BF16, PROD>(hr[c], c, rstd, pa);
+  for (int c = threadIdx.x; c < nch; c += 256) xr[c] = produce8<BF16, PROD>(hr[c], c, rstd, pa, nullptr);
+}
+
+// GELU is elementwise: each block copies the table into LDS and then maps
+// 16-byte chunks of the whole array, grid-stride, four chunks in flight per
+// thread.
+template <bool BF16>
+__global__ __launch_bounds__(512) void k_produce_gelu(const uint16_t* __restrict__ H, int64_t nchunks,
+                                                      uint16_t* __restrict__ X) {
+  __shared__ __attribute__((aligned(16))) uint16_t gtab[65536];
+  gelu_table_to_lds<BF16>(gtab);
+  __syncthreads();
+  const uint4* h = reinterpret_cast<const uint4*>(H);
+  uint4* x = reinterpret_cast<uint4*>(X);
+  const ProdArgs none{nullptr, nullptr, nullptr, 0.0f, nullptr};
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  for (; c + 3 * stride < nchunks; c += 4 * stride) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = h[c + u * stride];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[c + u * stride] = produce8<BF16, kProdGelu>(v[u], 0, 0.0f, none, gtab);
+  }
+  for (; c < nchunks; c += stride) x[c] = produce8<BF16, kProdGelu>(h[c], 0, 0.0f, none, gtab);
 }
 
 void launch_produce(const void* H, bool bf16, int64_t M, int K, int prod, const ProdArgs& pa, void* X,
                     hipStream_t s) {
   const uint16_t* h = static_cast<const uint16_t*>(H);
   uint16_t* x = static_cast<uint16_t*>(X);
+  if (prod == kProdGelu) {
+    const int64_t nchunks = M * K / 8;
+    const dim3 grid(static_cast<unsigned>(std::min<int64_t>((nchunks + 511) / 512, std::max(device_cus(), 1))));
+    if (bf16) k_produce_gelu<true><<<grid, dim3(512), 0, s>>>(h, nchunks, x);
+    else k_produce_gelu<false><<<grid, dim3(512), 0, s>>>(h, nchunks, x);
+    return;
+  }
   const dim3 grid(static_cast<unsigned>(M)), block(256);
   if (bf16) {
     if (prod == kProdRms) k_produce<true, kProdRms><<<grid, block, 0, s>>>(h, K, pa, x);
-    else if (prod == kProdGelu) k_produce<true, kProdGelu><<<grid, block, 0, s>>>(h, K, pa, x);
     else k_produce<true, kProdNone><<<grid, block, 0, s>>>(h, K, pa, x);
   } else {
     if (prod == kProdRms) k_produce<false, kProdRms><<<grid, block, 0, s>>>(h, K, pa, x);
-    else if (prod == kProdGelu) k_produce<false, kProdGelu><<<grid, block, 0, s>>>(h, K, pa, x);
     else k_produce<false, kProdNone><<<grid, block, 0, s>>>(h, K, pa, x);
   }
 }
 
 template <bool BF16, int PROD>
-static void launch_fixup_t(const uint16_t* X, int64_t M, int K, uint32_t tbits, const uint8_t* colflag, int8_t* q,
+static void launch_fixup_t(const uint16_t* X, int64_t M, int K, uint32_t tbits, const uint32_t* colflag,
+                           uint32_t stamp, int8_t* q,
                            float* sx, int* O, int* nO, uint16_t* XO, const int8_t* Wq, int64_t N, uint16_t* WO,
                            const ProdArgs& pa, hipStream_t s) {
   const int xblocks = static_cast<int>((M + kFixRows - 1) / kFixRows);
   const int wblocks = WO ? static_cast<int>((N + kFixWRows - 1) / kFixWRows) : 0;
   const size_t lds = outlier_fixup_lds_bytes(K);
   const dim3 grid(xblocks + wblocks), block(256);
-  k_outlier_fixup<BF16, PROD><<<grid, block, lds, s>>>(X, (int)M, K, tbits, colflag, q, sx, O, nO, XO, Wq, (int)N, WO,
-                                                       xblocks, pa);
+  k_outlier_fixup<BF16, PROD><<<grid, block, lds, s>>>(X, (int)M, K, tbits, colflag, stamp, q, sx, O, nO, XO, Wq,
+                                                       (int)N, WO, xblocks, pa);
 }
 
-void launch_outlier_fixup(const void* X, bool bf16, int64_t M, int K, uint32_t tbits, const uint8_t* colflag,
-                          int8_t* q, float* sx, int* O, int* nO, uint16_t* XO, const int8_t* Wq, int64_t N,
+void launch_outlier_fixup(const void* X, bool bf16, int64_t M, int K, uint32_t tbits, const uint32_t* colflag,
+                          uint32_t stamp, int8_t* q, float* sx, int* O, int* nO, uint16_t* XO, const int8_t* Wq, int64_t N,
                           uint16_t* WO, int prod, const ProdArgs& pa, hipStream_t s) {
   const uint16_t* x = static_cast<const uint16_t*>(X);
-#define W8_FIX_ARGS x, M, K, tbits, colflag, q, sx, O, nO, XO, Wq, N, WO, pa, s
+#define W8_FIX_ARGS x, M, K, tbits, colflag, stamp, q, sx, O, nO, XO, Wq, N, WO, pa, s
   if (bf16) {
     if (prod == kProdRms) launch_fixup_t<true, kProdRms>(W8_FIX_ARGS);
     else if (prod == kProdGelu) launch_fixup_t<true, kProdGelu>(W8_FIX_ARGS);
