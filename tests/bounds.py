@@ -9,6 +9,16 @@ accumulated terms), with a factor 2 of slack. The terms use magnitudes from
 the oracle's exact intermediates, so a wrong scale, bias or outlier term in
 one column moves that column far outside its bound even when a norm over the
 row would not notice it.
+
+The matrix cores' own summation, measured on gfx950 with products of known
+size: an MFMA adds its products in aligned groups of 8 consecutive k; inside a
+group every product is cut to the grid of the group's largest one, 2^-13 of
+its leading bit for E4M3 operands (v_mfma_scale_f32_32x32x64_f8f6f4) and 2^-22
+for bf16/f16 operands (v_mfma_f32_32x32x16_*); the group sums then add in
+float32. The truncation error of a group is below 7 grid units, at most
+7 * 2^-w of its largest |product|, and that largest product is at most the
+product of the group's largest |a| and largest |b|: group_err sums this over
+the groups with one small matrix product. The int8 MFMA is exact.
 """
 from __future__ import annotations
 
@@ -17,6 +27,19 @@ import numpy as np
 from oracle import w8ref as o
 
 U = 2.0 ** -24
+W_FP8 = 13          # grid of an E4M3 MFMA product group, bits below its largest term
+W_16 = 22           # the same for bf16 / f16 operands
+
+
+def group_err(a_abs: np.ndarray, b_abs: np.ndarray, window: int) -> np.ndarray:
+    """Upper bound [M, N] on the in-group truncation of an MFMA sum of a[m, k]
+    b[n, k] over k: sum over groups g of 8 consecutive k of 7 * 2^-window *
+    max_g |a| * max_g |b| (K padded with zeros to a multiple of 8)."""
+    K = a_abs.shape[1]
+    pad = (-K) % 8
+    a = np.pad(a_abs, ((0, 0), (0, pad))).reshape(a_abs.shape[0], -1, 8).max(axis=2)
+    b = np.pad(b_abs, ((0, 0), (0, pad))).reshape(b_abs.shape[0], -1, 8).max(axis=2)
+    return 7.0 * 2.0 ** -window * (a @ b.T)
 
 
 def half_ulp(v: np.ndarray, dtype: str) -> np.ndarray:
@@ -55,28 +78,35 @@ def int8_err32(ref: dict, x_bits, x_dtype: str, wq: np.ndarray, sw: np.ndarray, 
     O = ref["O"]
     nO = len(O)
     A = np.abs(ref["acc"].astype(np.float64)) * (ref["sx"].astype(np.float64)[:, None] / 127.0)
-    S = np.abs(xf[:, O]) @ np.abs(wq[:, O].astype(np.float64)).T if nO else np.zeros_like(A)
+    if nO:
+        xo, wo = np.abs(xf[:, O]), np.abs(wq[:, O].astype(np.float64))
+        S = xo @ wo.T
+        G = group_err(xo, wo, W_16)
+    else:
+        S = G = np.zeros_like(A)
     c = np.asarray(sw, np.float64)[None, :] / 127.0
     b = np.zeros((1, A.shape[1])) if bias is None else np.abs(np.asarray(bias, np.float64))[None, :]
     y = np.abs(ref["y"])
-    return U * (c * (5.0 * A + (nO + 3) * S) + y + b)
+    return U * (c * (5.0 * A + (nO + 3) * S) + y + b) + c * G
 
 
 def fp8_err32(ref: dict, wq8: np.ndarray, sw: np.ndarray, K: int) -> np.ndarray:
-    """float32 error of the FP8 GEMM: K products (exact) accumulated in
-    float32 (gamma_K of the sum of |products|), then scaled by sx and sw (two
-    roundings of |y|)."""
+    """Error of the FP8 GEMM before its output rounding: the E4M3 MFMA's
+    in-group truncation (group_err, 13-bit grid), the float32 additions of the
+    group sums and partial sums (gamma_K of the sum of |products|), then the
+    scaling by sx and sw (two roundings of |y|)."""
     a = np.abs(o.e4m3_decode(ref["xq"]))
     w = np.abs(o.e4m3_decode(wq8))
     P = a @ w.T
     s = ref["sx"].astype(np.float64)[:, None] * np.asarray(sw, np.float64)[None, :]
-    return U * (K * s * P + 3.0 * np.abs(ref["y"]))
+    return U * (K * s * P + 3.0 * np.abs(ref["y"])) + s * group_err(a, w, W_FP8)
 
 
 def dense_err32(x_abs: np.ndarray, w_abs: np.ndarray, y: np.ndarray, K: int) -> np.ndarray:
-    """float32 error of a 16-bit product with float32 accumulation: gamma_K of
-    the sum of |products| plus one rounding of |y|."""
-    return U * (K * (x_abs @ w_abs.T) + np.abs(y))
+    """Error of a 16-bit product on bf16/f16 MFMA: the in-group truncation
+    (group_err, 22-bit grid), float32 accumulation (gamma_K of the sum of
+    |products|) and one rounding of |y|."""
+    return U * (K * (x_abs @ w_abs.T) + np.abs(y)) + group_err(x_abs, w_abs, W_16)
 
 
 def w4a8_err32(ref: dict, sw4: np.ndarray) -> np.ndarray:

@@ -203,10 +203,11 @@ def _check_linear_step(got_bits, h_bits, kind, blk, name, norm, label, rows, rst
 
 
 def _check_residual(got_bits, a_bits, d_values, label):
-    """y = rne16(fl32(a) + fl32(d)): within half an fp16 ulp plus one float32
-    rounding of the exact sum."""
+    """y = rne16(fl32(a + fl32(d))), d itself the float32 sum of the linear's
+    output and the bias when the bias is added here: within half an fp16 ulp
+    plus a float32 rounding of d and one of the sum."""
     s = o.decode16(a_bits, "f16").astype(np.float64) + d_values
-    bounds.assert_elementwise(got_bits, "f16", s, bounds.U * np.abs(s), label)
+    bounds.assert_elementwise(got_bits, "f16", s, bounds.U * (np.abs(s) + np.abs(d_values)), label)
 
 
 def _check_block_steps(x_bits, blk, gpu, ws, M, rows):
@@ -217,9 +218,13 @@ def _check_block_steps(x_bits, blk, gpu, ws, M, rows):
     assert np.array_equal(a, qkv[:, 2 * D:3 * D])                       # the attention stub
     _check_linear_step(o_, a, "none", blk, "o", None, "o", rows)
     _check_residual(h, x_bits, o.decode16(o_, "f16").astype(np.float64), "h")
-    # the up projection's rstd is the last one the shared int8 workspace holds
-    lay = w8.int8_workspace_layout(M, F, D)
-    rstd2 = ws[lay["rstd"]:lay["rstd"] + 4 * M].view(torch.float32).cpu().numpy()
+    # with the 16-bit down-projection, the up projection is the last int8
+    # call in the shared workspace, which still holds its rstd (an int8 down
+    # projection overwrites it with its codes)
+    rstd2 = None
+    if blk.get("w16_down") is not None:
+        lay = w8.int8_workspace_layout(M, F, D)
+        rstd2 = ws[lay["rstd"]:lay["rstd"] + 4 * M].view(torch.float32).cpu().numpy()
     _check_linear_step(u, h, "rmsnorm", blk, "up", blk["norm2"], "u", rows, rstd=rstd2)
     if blk.get("w16_down") is not None:
         g = _f16(it["g"])

@@ -286,7 +286,7 @@ def test_outlier_counts_past_the_lds_staging(n_out, t, x_dtype):
     """More than 32 outlier columns: the epilogue reads the staged XO/WO from
     global memory (up to 256 columns), or, past that, gathers the outlier
     columns from X and Wq itself; t = 0 makes every column an outlier."""
-    K = 640 if n_out < 600 else 600
+    K = 640 if n_out < 600 else 608
     c = synth.random_linear(300, K, 520, seed=50 + n_out, x_dtype=x_dtype, outlier_cols=min(n_out, K))
     wq, sw, wq_ref, sw_ref = _quant_weights_both(c)
     ref = o.int8_mixed_linear(c.x_bits, x_dtype, wq_ref, sw_ref, t, "f32")
