@@ -154,6 +154,29 @@ w8_status int8_mixed_linear(const void* X, int x_dt, int64_t M, int64_t K,
                             void* stream);
 
 /*
+ * int8_mixed_linear_noalloc -- int8_mixed_linear without a workspace argument,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation. Arguments,
+ * results and errors are those of int8_mixed_linear.
+ *
+ * The workspace is a static 96 MiB region of the library's own device memory:
+ * each device the library runs on holds one copy from the load of the
+ * library's code until the process ends. The call allocates nothing (no
+ * hipMalloc, no allocating library routine); its first call on a device looks
+ * up that device's copy (hipGetSymbolAddress). A shape whose codes, scales and
+ * outlier operands do not fit (the int8 workspace without split-K partials;
+ * e.g. M x K above about 90 million) is rejected with W8_ERR_UNSUPPORTED
+ * before anything runs; split-K partials are used when they fit too, else
+ * the same tiles run without K-slicing (same results). Every call on a device
+ * shares that device's region, and it keeps the last call's contents: calls
+ * that may overlap on one device (different streams, threads) race and give
+ * undefined results; serialise them.
+ */
+w8_status int8_mixed_linear_noalloc(const void* X, int x_dt, int64_t M, int64_t K,
+                                    const int8_t* Wq, const float* sw, int64_t N, float threshold,
+                                    void* Y, int y_dt, void* stream);
+
+/*
  * The op that produces X, for int8_mixed_linear_fused. X is made from H in the
  * quantisation pass itself and never stored; it is the 16-bit value (H's type)
  * that a separate producer op would store:

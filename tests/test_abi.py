@@ -352,3 +352,22 @@ def test_events_exports_validate_like_the_linears():
     assert qkv >= lib.int8_mixed_linear_workspace_size(M, D, F)
     assert a >= qkv + 2 * M * 3 * D and o >= a + 2 * M * D and h >= o + 2 * M * D and u >= h + 2 * M * D
     assert g >= u + 2 * M * F and d >= g + 2 * M * F
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch():
+    """int8_mixed_linear_noalloc validates on the host like int8_mixed_linear
+    and rejects a shape whose workspace exceeds its 96 MiB scratch before
+    touching the device (the DiT 2048^2 MLP down projection: 16640 x 16384
+    codes alone are 272 MB)."""
+    lib = _abi.lib()
+    f = lib.int8_mixed_linear_noalloc
+    bf, f16 = _abi.W8_DT_BF16, _abi.W8_DT_F16
+    assert f(A, bf, 16640, 16384, A, A, 4096, 6.0, A, f16, None) == _abi.W8_ERR_UNSUPPORTED
+    assert "scratch" in lib.w8_last_error().decode()
+    assert f(None, bf, 64, 256, A, A, 32, 6.0, A, f16, None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert f(A, bf, 64, 24, A, A, 32, 6.0, A, f16, None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert f(A, bf, 64, 256, A, A, 32, float("nan"), A, f16, None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert f(A, bf, 64, 256, A, A, 0, 6.0, A, f16, None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert f(A, bf, 64, 256, None, A, 32, 6.0, A, f16, None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert f(A, bf, 64, 256, A, A, 32, 6.0, None, f16, None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert f(A, bf, 64, 256, A, A, 32, 6.0, A, _abi.W8_DT_BF16, None) == _abi.W8_ERR_UNSUPPORTED

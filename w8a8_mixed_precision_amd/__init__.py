@@ -20,6 +20,7 @@ __all__ = [
     "debug_int8_quantize_activations", "debug_int8_gemm_i32", "debug_fp8_quantize_activations", "debug_fp8_gemm",
     "int8_mixed_linear_workspace_size", "fp8_w8a8_linear_workspace_size", "new_workspace", "W8Error",
     "int8_workspace_layout", "debug_int8_mixed_linear_events", "debug_fp8_w8a8_linear_events",
+    "int8_mixed_linear_noalloc",
 ]
 
 
@@ -165,6 +166,22 @@ def int8_mixed_linear(x: torch.Tensor, wq: torch.Tensor, sw: torch.Tensor, thres
                                                  bias.data_ptr() if bias is not None else None, N,
                                                  float(threshold), y.data_ptr(), _dt(y), ws.data_ptr(), ws.numel(),
                                                  _stream(x)))
+    return y
+
+
+def int8_mixed_linear_noalloc(x: torch.Tensor, wq: torch.Tensor, sw: torch.Tensor, threshold: float = 6.0,
+                              out_dtype: torch.dtype = torch.float16, out: torch.Tensor | None = None) -> torch.Tensor:
+    """int8_mixed_linear on the library's static device scratch: no workspace
+    argument and no allocation inside the call (pass `out` to allocate nothing
+    here either). Calls that may overlap on one device race (include/w8mp.h)."""
+    _dev(x, "x"), _dev(wq, "wq"), _dev(sw, "sw")
+    M, K = x.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K or wq.dtype != torch.int8 or sw.shape != (N,) or sw.dtype != torch.float32:
+        raise ValueError("wq must be int8 [N,K] and sw fp32 [N]")
+    y = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=x.device)
+    _abi.check(lib().int8_mixed_linear_noalloc(x.data_ptr(), _dt(x), M, K, wq.data_ptr(), sw.data_ptr(), N,
+                                               float(threshold), y.data_ptr(), _dt(y), _stream(x)))
     return y
 
 

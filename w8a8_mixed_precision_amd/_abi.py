@@ -40,6 +40,7 @@ SIGNATURES = {
     "quantize_weight_rowwise": (_int, [_p, _int, _i64, _i64, _int, _p, _p, _p]),
     "int8_mixed_linear_workspace_size": (_size, [_i64, _i64, _i64]),
     "int8_mixed_linear": (_int, [_p, _int, _i64, _i64, _p, _p, _i64, _f, _p, _int, _p, _size, _p]),
+    "int8_mixed_linear_noalloc": (_int, [_p, _int, _i64, _i64, _p, _p, _i64, _f, _p, _int, _p]),
     "int8_mixed_linear_fused": (_int, [_p, _int, _i64, _i64, _p, _p, _p, _p, _i64, _f, _p, _int, _p, _size, _p]),
     "fp8_w8a8_linear_workspace_size": (_size, [_i64, _i64, _i64]),
     "fp8_w8a8_linear": (_int, [_p, _int, _i64, _i64, _p, _p, _i64, _p, _p, _int, _p, _size, _p]),

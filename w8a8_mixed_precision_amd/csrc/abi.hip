@@ -325,7 +325,7 @@ static w8_status producer_args(const w8_producer* p, int64_t K, int* kind, w8::P
 static w8_status int8_linear_impl(const void* X, int x_dt, int64_t M, int64_t K, const w8_producer* producer,
                                   const int8_t* Wq, const float* sw, const float* bias, int64_t N, float threshold,
                                   void* Y, int y_dt, void* workspace, size_t workspace_bytes, void* stream,
-                                  void* const* events, const char* what) {
+                                  void* const* events, const char* what, size_t need = 0) {
   if (w8_status st = int8_common_checks(X, x_dt, M, K, threshold); st != W8_OK) return st;
   W8_REQUIRE(Wq && sw && Y, W8_ERR_INVALID_ARGUMENT, "null pointer argument");
   W8_REQUIRE(N >= 1 && N <= kMaxDim, W8_ERR_INVALID_ARGUMENT, "N must be in [1, 2^31)");
@@ -336,7 +336,8 @@ static w8_status int8_linear_impl(const void* X, int x_dt, int64_t M, int64_t K,
   w8::ProdArgs pa{};
   if (w8_status st = producer_args(producer, K, &kind, &pa); st != W8_OK) return st;
   const Int8Ws L = int8_layout(M, N, K);
-  if (w8_status st = check_ws(workspace, workspace_bytes, int8_ws_size(M, N, K)); st != W8_OK) return st;
+  if (w8_status st = check_ws(workspace, workspace_bytes, need ? need : int8_ws_size(M, N, K)); st != W8_OK)
+    return st;
   const w8::GemmPlan plan = int8_plan(M, N, K, workspace_bytes - L.base);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -378,6 +379,54 @@ w8_status int8_mixed_linear_fused(const void* H, int h_dt, int64_t M, int64_t K,
                                   void* Y, int y_dt, void* workspace, size_t workspace_bytes, void* stream) {
   return int8_linear_impl(H, h_dt, M, K, producer, Wq, sw, bias, N, threshold, Y, y_dt, workspace, workspace_bytes,
                           stream, nullptr, "int8_mixed_linear_fused");
+}
+
+}  // extern "C"
+
+// Scratch of int8_mixed_linear_noalloc: its workspace, in the library's own
+// device memory. Each device holds its own copy from the time the library's
+// code is loaded on it until the process ends, zero at load. In host code the
+// name is only a stand-in: the address a kernel can use comes from
+// hipGetSymbolAddress, once per device, kept in g_scratch_ptr.
+static constexpr size_t kNoAllocBytes = size_t{96} << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocBytes];
+
+namespace {
+
+std::atomic<void*> g_scratch_ptr[64];
+
+// The device address of this device's scratch (null if it cannot be found).
+void* scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+  g_scratch_ptr[dev].store(p, std::memory_order_release);   // racing threads store the same address
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+w8_status int8_mixed_linear_noalloc(const void* X, int x_dt, int64_t M, int64_t K, const int8_t* Wq, const float* sw,
+                                    int64_t N, float threshold, void* Y, int y_dt, void* stream) {
+  // every argument check of int8_mixed_linear, before the device is touched
+  if (w8_status st = int8_common_checks(X, x_dt, M, K, threshold); st != W8_OK) return st;
+  W8_REQUIRE(Wq && sw && Y, W8_ERR_INVALID_ARGUMENT, "null pointer argument");
+  W8_REQUIRE(N >= 1 && N <= kMaxDim, W8_ERR_INVALID_ARGUMENT, "N must be in [1, 2^31)");
+  W8_REQUIRE(y_dt == W8_DT_F16 || y_dt == W8_DT_F32, W8_ERR_UNSUPPORTED, "Y must be f16 or f32");
+  W8_REQUIRE(aligned16(Wq) && aligned16(sw) && aligned16(Y), W8_ERR_INVALID_ARGUMENT,
+             "pointers must be 16-byte aligned");
+  const size_t need = int8_layout(M, N, K).base;
+  W8_REQUIRE(need <= kNoAllocBytes, W8_ERR_UNSUPPORTED,
+             "M=%lld N=%lld K=%lld needs %zu bytes of scratch; int8_mixed_linear_noalloc has %zu (use "
+             "int8_mixed_linear with a workspace)", (long long)M, (long long)N, (long long)K, need, kNoAllocBytes);
+  void* ws = scratch_ptr();
+  W8_REQUIRE(ws != nullptr, W8_ERR_HIP, "hipGetSymbolAddress of the no-allocation scratch failed");
+  return int8_linear_impl(X, x_dt, M, K, nullptr, Wq, sw, nullptr, N, threshold, Y, y_dt, ws, kNoAllocBytes, stream,
+                          nullptr, "int8_mixed_linear_noalloc", need);
 }
 
 size_t fp8_w8a8_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
