@@ -235,3 +235,22 @@ def test_dit_mlp_fused_full_size(idx):
     ref = P.fused_int8_linear(c.h_bits, c.h_dtype, c.kind, wq_ref, sw_ref, c.threshold, c.bias, "f16",
                               rows=rows, x_bits=x_bits, **kw)
     _check(y[torch.from_numpy(rows).cuda()], ref, "f16", c.name, c.h_dtype, wq_ref, sw_ref, c.bias, rows)
+
+
+@pytest.mark.parametrize("kind,t", [("gelu", 0.25), ("rmsnorm", 0.5)])
+@pytest.mark.parametrize("K", [640, 528])
+def test_fused_linear_with_gathered_outlier_columns(kind, t, K):
+    """A low threshold makes more than 256 outlier columns: the GEMM epilogue
+    gathers them from H through the producer (RMSNorm with the row pass's
+    rstd, GELU from the global table). K = 528 takes the GEMM for K % 64 != 0."""
+    c = synth.fused_case(kind, 300, K, 520, 91 + K, name=f"{kind}_gathered_{K}")
+    wq, sw, wq_ref, sw_ref = _weights(c)
+    prod, kw = _producer(c)
+    announce("fused gathered", c.name, t)
+    x_bits = _x_ref(c, kw, prod)
+    ref = P.fused_int8_linear(c.h_bits, c.h_dtype, kind, wq_ref, sw_ref, t, c.bias, "f32", x_bits=x_bits, **kw)
+    assert len(ref["O"]) > 256
+    y = w8.int8_mixed_linear(dev16(c.h_bits, c.h_dtype), wq, sw, t, torch.float32,
+                             bias=torch.from_numpy(c.bias).cuda(), producer=prod)
+    torch.cuda.synchronize()
+    _check(y, ref, "f32", c.name, c.h_dtype, wq_ref, sw_ref, c.bias)

@@ -279,14 +279,14 @@ def test_one_workspace_serves_shapes_of_both_kinds():
     assert torch.equal(y, w8.int8_mixed_linear(xd, wd, sd, 6.0, torch.float16))
 
 
-@pytest.mark.parametrize("n_out,t", [(40, 6.0), (300, 6.0), (600, 0.0)], ids=["staged_global", "gathered",
-                                                                                "all_gathered"])
+@pytest.mark.parametrize("n_out,t", [(40, 6.0), (300, 6.0), (600, 0.0), (528, 0.0)],
+                         ids=["staged_global", "gathered", "all_gathered", "all_gathered_k528"])
 @pytest.mark.parametrize("x_dtype", ["bf16", "f16"])
 def test_outlier_counts_past_the_lds_staging(n_out, t, x_dtype):
     """More than 32 outlier columns: the epilogue reads the staged XO/WO from
     global memory (up to 256 columns), or, past that, gathers the outlier
     columns from X and Wq itself; t = 0 makes every column an outlier."""
-    K = 640 if n_out < 600 else 608
+    K = {40: 640, 300: 640, 600: 608, 528: 528}[n_out]     # 528: the GEMM for K % 64 != 0
     c = synth.random_linear(300, K, 520, seed=50 + n_out, x_dtype=x_dtype, outlier_cols=min(n_out, K))
     wq, sw, wq_ref, sw_ref = _quant_weights_both(c)
     ref = o.int8_mixed_linear(c.x_bits, x_dtype, wq_ref, sw_ref, t, "f32")

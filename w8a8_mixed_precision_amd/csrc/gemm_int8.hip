@@ -163,37 +163,51 @@ __device__ __forceinline__ void flush_cols(const char* stg, char* __restrict__ y
   }
 }
 
-// More outlier columns than the XO/WO staging holds (kOutCap): the side
-// product gathers them one by one, from X (made from H by the producer) and
-// from Wq, through the ascending outlier list. o[i] += the outlier product of
-// weight row n and rows m_base + 32 i (clamped into [M, N); rows past M are
-// computed and not stored).
+// More outlier columns than the XO/WO staging holds (kOutCap): the whole
+// block gathers 32 of them at a time into an LDS area laid out like the
+// tile-start staging (side_off), from X (made from H by the producer) and from
+// Wq, through the ascending outlier list: rows m0 .. m0+R-1 of X, then rows
+// n0 .. n0+R-1 of Wq (R = 64 WT, clamped into [M, N); slots past nO are 0).
 template <bool XBF16, int WT>
-__device__ __noinline__ void side_gather(v16f* o, const SideSrc& src, int M, int N, int n, int m_base, int nO, int P,
-                                         int fh) {
-  using V8 = typename std::conditional<XBF16, v8bf, v8h>::type;
+__device__ __forceinline__ void gather_side_chunk(char* buf, const SideSrc& src, int M, int N, int m0, int n0,
+                                                  int c0, int nO) {
+  constexpr int R = 64 * WT;
   using E = typename std::conditional<XBF16, __bf16, _Float16>::type;
-  const int8_t* wrow = src.Wq + static_cast<int64_t>(min(n, N - 1)) * src.K;
-  for (int c = 0; c < P; c += 16) {
-    int idx[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = c + 8 * fh + e;
-      idx[e] = j < nO ? src.O[j] : -1;
-    }
-    V8 wa;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) wa[e] = static_cast<E>(idx[e] >= 0 ? static_cast<float>(wrow[idx[e]]) : 0.0f);
-    for (int i = 0; i < WT; ++i) {
-      const int m = min(m_base + 32 * i, M - 1);
-      const uint16_t* hrow = src.H + static_cast<int64_t>(m) * src.K;
-      const float rstd = src.prod == kProdRms ? src.pa.rstd[m] : 0.0f;
-      V8 xb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t b = idx[e] >= 0 ? produce1_any<XBF16>(src.prod, hrow[idx[e]], idx[e], rstd, src.pa) : 0u;
-        xb[e] = __builtin_bit_cast(E, static_cast<uint16_t>(b));
+#pragma unroll 1
+  for (int idx = threadIdx.x; idx < 2 * R * 32; idx += 256) {
+    const int row = idx >> 5, jj = idx & 31, j = c0 + jj;
+    const bool xrow = row < R;
+    const int r = xrow ? row : row - R;
+    uint32_t v = 0;
+    if (j < nO) {
+      const int k = src.O[j];
+      if (xrow) {
+        const int m = min(m0 + r, M - 1);
+        const float rstd = src.prod == kProdRms ? src.pa.rstd[m] : 0.0f;
+        v = produce1_any<XBF16>(src.prod, src.H[static_cast<int64_t>(m) * src.K + k], k, rstd, src.pa);
+      } else {
+        const int n = min(n0 + r, N - 1);
+        v = __builtin_bit_cast(uint16_t, static_cast<E>(static_cast<float>(src.Wq[static_cast<int64_t>(n) * src.K + k])));
       }
+    }
+    char* base = buf + (xrow ? 0 : kSideRows * 64);
+    *reinterpret_cast<uint16_t*>(base + side_off(r, jj >> 3) + (jj & 7) * 2) = static_cast<uint16_t>(v);
+  }
+}
+
+// o[i] += the outlier product of one 32-column block over 32 outlier columns
+// staged in LDS (side_off layout: X rows, then W rows from kSideRows).
+template <bool XBF16, int WT>
+__device__ __forceinline__ void side_from_lds(v16f* o, const char* side, int ncol, int wm, int fr, int fh) {
+  using V8 = typename std::conditional<XBF16, v8bf, v8h>::type;
+  const char* sx_rows = side;
+  const char* sw_rows = side + kSideRows * 64;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const V8 wa = *reinterpret_cast<const V8*>(sw_rows + side_off(ncol + fr, 2 * c + fh));
+#pragma unroll
+    for (int i = 0; i < WT; ++i) {
+      const V8 xb = *reinterpret_cast<const V8*>(sx_rows + side_off(wm * 32 * WT + 32 * i + fr, 2 * c + fh));
       o[i] = mfma_side<XBF16>(wa, xb, o[i]);
     }
   }
@@ -216,7 +230,8 @@ template <int MODE, bool XBF16, int WT = 4>
 __device__ __forceinline__ void epilogue(v16i (&acc)[WT][WT], int M, int N, int m0, int n0, int wm, int wn, int lane,
                                          const float (&rsx)[4], const float* scol, const float* sbias, int nO,
                                          const uint16_t* __restrict__ XO, const uint16_t* __restrict__ WO,
-                                         const SideSrc& src, const char* side, void* __restrict__ Y, char* stg) {
+                                         const SideSrc& src, const char* side, char* side_buf, void* __restrict__ Y,
+                                         char* stg) {
   const int fr = lane & 31, fh = lane >> 5;
   constexpr int EB = MODE == 1 ? 2 : 4;         // bytes per output element
   constexpr int WR = 32 * WT;                   // rows (= columns) of the wave tile
@@ -241,17 +256,7 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[WT][WT], int M, int N, int 
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[i][r] = 0.0f;
       if (side && P == 32) {
-        const char* sx_rows = side;
-        const char* sw_rows = side + kSideRows * 64;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const V8 wa = *reinterpret_cast<const V8*>(sw_rows + side_off(ncol + fr, 2 * c + fh));
-#pragma unroll
-          for (int i = 0; i < WT; ++i) {
-            const V8 xb = *reinterpret_cast<const V8*>(sx_rows + side_off(wm * WR + 32 * i + fr, 2 * c + fh));
-            o[i] = mfma_side<XBF16>(wa, xb, o[i]);
-          }
-        }
+        side_from_lds<XBF16, WT>(o, side, ncol, wm, fr, fh);
       } else if (P <= kOutCap) {
         const int64_t wrow = static_cast<int64_t>(min(n0 + ncol + fr, N - 1)) * P;
         for (int c = 0; c < P; c += 16) {
@@ -264,7 +269,13 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[WT][WT], int M, int N, int 
           }
         }
       } else {
-        side_gather<XBF16, WT>(o, src, M, N, n0 + ncol + fr, row0 + fr, nO, P, fh);
+        // every wave runs this branch (P is the block's), so the barriers match
+        for (int c0 = 0; c0 < P; c0 += 32) {
+          __syncthreads();                      // the previous chunk is fully read
+          gather_side_chunk<XBF16, WT>(side_buf, src, M, N, m0, n0, c0, nO);
+          __syncthreads();
+          side_from_lds<XBF16, WT>(o, side_buf, ncol, wm, fr, fh);
+        }
       }
       stage_cols<MODE, true, WT>(acc, o, j, rsx, scol, sbias, ncol, lane, stg + soff);
     }
@@ -311,7 +322,7 @@ template <int MODE, bool XBF16, int WT = 4>
 __device__ __forceinline__ void finish_tile(v16i (&acc)[WT][WT], EpiIn& e, char* lds, int M, int N, int m0, int n0,
                                             int wm, int wn, int lane, const uint16_t* __restrict__ XO,
                                             const uint16_t* __restrict__ WO, const SideSrc& src, const char* side,
-                                            void* __restrict__ Y) {
+                                            char* side_buf, void* __restrict__ Y) {
   float* scol = reinterpret_cast<float*>(lds);
   float* sbias = scol + 256;
   if constexpr (MODE != 0) {
@@ -321,8 +332,8 @@ __device__ __forceinline__ void finish_tile(v16i (&acc)[WT][WT], EpiIn& e, char*
     sbias[threadIdx.x] = e.my_bias;             // 0 without a bias
     __syncthreads();
   }
-  epilogue<MODE, XBF16, WT>(acc, M, N, m0, n0, wm, wn, lane, e.rsx, scol, sbias, e.nO, XO, WO, src, side, Y,
-                            lds + kEpiCols + (threadIdx.x >> 6) * kStgWaveJ);
+  epilogue<MODE, XBF16, WT>(acc, M, N, m0, n0, wm, wn, lane, e.rsx, scol, sbias, e.nO, XO, WO, src, side, side_buf,
+                            Y, lds + kEpiCols + (threadIdx.x >> 6) * kStgWaveJ);
 }
 
 __device__ __forceinline__ void zero_acc(v16i (&acc)[4][4]) {
@@ -348,7 +359,10 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm(const int8_t* __restrict__
                                                       int tiles_m, int tiles_n, SideSrc src) {
   // two stages of A and B, and the epilogue's LDS after the K loop
   constexpr int kLdsBytes = 4 * kBM * kBK > kEpiLds8 ? 4 * kBM * kBK : kEpiLds8;
-  __shared__ __attribute__((aligned(16))) int8_t lds_raw[kLdsBytes];
+  // the K loop's two stages (later the epilogue's staging), then the area of
+  // the outlier columns gathered in the epilogue when there are more than
+  // kOutCap of them
+  __shared__ __attribute__((aligned(16))) int8_t lds_raw[kLdsBytes + kSideLds];
   int8_t (*lds)[2][kBM * kBK] = reinterpret_cast<int8_t (*)[2][kBM * kBK]>(lds_raw);
 
   int tm, tn;
@@ -404,7 +418,7 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm(const int8_t* __restrict__
     __syncthreads();
   }
   finish_tile<MODE, XBF16>(acc, ein, reinterpret_cast<char*>(&lds[0][0][0]), M, N, m0, n0, wm, wn, lane, XO, WO,
-                           src, nullptr, Y);
+                           src, nullptr, reinterpret_cast<char*>(lds_raw) + kLdsBytes, Y);
 }
 
 // ---------------------------------------------------------------------------
@@ -667,7 +681,7 @@ __device__ __forceinline__ void small_block(int8_t* lds, const int8_t* __restric
     }
   }
   finish_tile<MODE, XBF16, 2>(acc, ein, reinterpret_cast<char*>(lds), M, N, m0, n0, wm, wn, lane, XO, WO, src, nullptr,
-                              Y);
+                              reinterpret_cast<char*>(lds) + S * 2 * kBM * kBK, Y);
 }
 
 // Work split for the last, partial wave of tiles (split-K). The first
@@ -849,7 +863,8 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
     }
   }
   finish_tile<MODE, XBF16>(acc, ein, reinterpret_cast<char*>(lds), M, N, m0, n0, wm, wn, lane, XO, WO, src,
-                           side ? reinterpret_cast<const char*>(lds) + S * kStage : nullptr, Y);
+                           side ? reinterpret_cast<const char*>(lds) + S * kStage : nullptr,
+                           reinterpret_cast<char*>(lds) + S * kStage, Y);
 }
 
 // ---------------------------------------------------------------------------
