@@ -440,11 +440,12 @@ def recorded_traffic(w8) -> float | None:
 
 
 def gemm_sources_sha256() -> str:
-    """Digest of the sources the int8 GEMM kernel is built from."""
+    """Digest of the sources the int8 GEMM kernel is built from (its file, the
+    headers it includes and the generator of the GELU table they embed)."""
     import hashlib
 
     h = hashlib.sha256()
-    for f in ("gemm_int8.hip", "tile.h", "common.h"):
+    for f in ("gemm_int8.hip", "tile.h", "common.h", "launch.h", "produce.h", "producer.h", "gelu_table_gen.cpp"):
         with open(os.path.join(ROOT, "w8a8_mixed_precision_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()

@@ -152,12 +152,9 @@ struct Fp8Tile {
   static constexpr int kPartBytes = BM * BM * 4;      // one fp32 partial
 };
 
-// The two builtins of the K loop behind plain (non-template) wrappers: called
+// The MFMA builtin of the K loop behind a plain (non-template) wrapper: called
 // with template-dependent arguments directly, the host compilation pass drops
-// the kernel templates that use them.
-__device__ __forceinline__ void lds_dma16(const uint8_t* src, uint8_t* dst) {
-  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
-}
+// the kernel templates that use it.
 __device__ __forceinline__ v16f mfma_fp8(v8i a, v8i b, v16f c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
@@ -186,8 +183,7 @@ __device__ __forceinline__ int frag_row(int f, int wm, int wn, int fr) {
 // over the MFMAs; sched_barrier keeps that interleaving.
 template <int WT>
 __device__ __forceinline__ void fp8_step(const v8i* fc, v8i* fn, v16f (*acc)[WT], const uint8_t* sn, int wm, int wn,
-                                         int lane, const uint8_t* const* a_src, const uint8_t* const* b_src, int k0,
-                                         uint8_t* st, int wave) {
+                                         int lane, const DmaSrc& src, int k0, uint8_t* st, int wave) {
   using T = Fp8Tile<WT>;
   const int fr = lane & 31, fh = lane >> 5;
   constexpr int kReads = 2 * T::kFrags;
@@ -211,10 +207,11 @@ __device__ __forceinline__ void fp8_step(const v8i* fc, v8i* fn, v16f (*acc)[WT]
     }
 #pragma unroll
     for (int d = t * T::kLoads / T::kMfma; d < (t + 1) * T::kLoads / T::kMfma; ++d) {
+      int8_t* const s8 = reinterpret_cast<int8_t*>(st);
       if (d < WT)
-        lds_dma16(a_src[d] + k0, st + (wave * WT + d) * 1024);
+        dma_a(src, s8 + (wave * WT + d) * 1024, d, k0);
       else
-        lds_dma16(b_src[d - WT] + k0, st + T::BM * kBK + (wave * WT + d - WT) * 1024);
+        dma_b(src, s8 + T::BM * kBK + (wave * WT + d - WT) * 1024, d - WT, k0);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -224,15 +221,14 @@ __device__ __forceinline__ void fp8_step(const v8i* fc, v8i* fn, v16f (*acc)[WT]
 // last step into the slot just retired (read by no later step), so every step
 // issues the same number of loads and one constant wait fits all.
 template <int WT, int S>
-__device__ __forceinline__ void fp8_issue(uint8_t* lds, int kt, int nk, const uint8_t* const* a_src,
-                                          const uint8_t* const* b_src, int wave) {
+__device__ __forceinline__ void fp8_issue(uint8_t* lds, int kt, int nk, const DmaSrc& src, int wave) {
   using T = Fp8Tile<WT>;
-  uint8_t* st = lds + (kt % S) * T::kStage;
+  int8_t* st = reinterpret_cast<int8_t*>(lds) + (kt % S) * T::kStage;
   const int k0 = min(kt, nk - 1) * kBK;
 #pragma unroll
   for (int i = 0; i < WT; ++i) {
-    lds_dma16(a_src[i] + k0, st + (wave * WT + i) * 1024);
-    lds_dma16(b_src[i] + k0, st + T::BM * kBK + (wave * WT + i) * 1024);
+    dma_a(src, st + (wave * WT + i) * 1024, i, k0);
+    dma_b(src, st + T::BM * kBK + (wave * WT + i) * 1024, i, k0);
   }
 }
 
@@ -244,13 +240,12 @@ __device__ __forceinline__ void fp8_issue(uint8_t* lds, int kt, int nk, const ui
 // harmless, and one loop body keeps register use at the loop's.
 template <int WT, int S>
 __device__ __forceinline__ void fp8_body(const v8i* fc, v8i* fn, v16f (*acc)[WT], uint8_t* lds, int kt, int nk,
-                                         int wm, int wn, int lane, const uint8_t* const* a_src,
-                                         const uint8_t* const* b_src, int wave) {
+                                         int wm, int wn, int lane, const DmaSrc& src, int wave) {
   using T = Fp8Tile<WT>;
   wait_lgkmcnt<0>();
   wait_vmcnt<(S - 2) * T::kLoads>();
   block_barrier();
-  fp8_step<WT>(fc, fn, acc, lds + ((kt + 1) % S) * T::kStage, wm, wn, lane, a_src, b_src, min(kt + S, nk - 1) * kBK,
+  fp8_step<WT>(fc, fn, acc, lds + ((kt + 1) % S) * T::kStage, wm, wn, lane, src, min(kt + S, nk - 1) * kBK,
                lds + (kt % S) * T::kStage, wave);
 }
 
@@ -294,7 +289,7 @@ __global__ __launch_bounds__(256, 4 / WT) void k_fp8_gemm_dma(const uint8_t* __r
     ke = (piece + 1) * nk_all / split;
   }
   const int m0 = tm * BM, n0 = tn * BM;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int fr = lane & 31, fh = lane >> 5;
   // epilogue inputs, fetched now so their latency hides under the K loop
@@ -303,18 +298,11 @@ __global__ __launch_bounds__(256, 4 / WT) void k_fp8_gemm_dma(const uint8_t* __r
   for (int i = 0; i < WT; ++i) rsx[i] = sx[min(m0 + wm * 32 * WT + 32 * i + fr, M - 1)];
   const float my_sw = sw[min(n0 + (tid & (BM - 1)), N - 1)];
 
-  // DMA source of this lane for load instruction i of each operand: tile row
-  // r = wave*16*WT + 16*i + lane/4 lands in LDS slot (lane & 3) of that row,
-  // which holds logical 16-byte chunk (lane & 3) ^ swz_term(r).
-  const uint8_t* a_src[WT];
-  const uint8_t* b_src[WT];
-#pragma unroll
-  for (int i = 0; i < WT; ++i) {
-    const int r = wave * 16 * WT + 16 * i + (lane >> 2);
-    const int ch = (lane & 3) ^ swz_term(r);
-    a_src[i] = A + static_cast<int64_t>(min(m0 + r, M - 1)) * K + kb * kBK + ch * 16;
-    b_src[i] = B + static_cast<int64_t>(min(n0 + r, N - 1)) * K + kb * kBK + ch * 16;
-  }
+  // load instruction i of each operand: tile row r = wave*16*WT + 16*i +
+  // lane/4 lands in LDS slot (lane & 3) of that row, which holds logical
+  // 16-byte chunk (lane & 3) ^ swz_term(r)
+  const DmaSrc src_k = dma_src(reinterpret_cast<const int8_t*>(A), reinterpret_cast<const int8_t*>(B), m0, n0, M, N,
+                               K, kb * kBK, BM, wave, lane);
   const int nk = ke - kb;
 
   v16f acc[WT][WT];
@@ -325,7 +313,7 @@ __global__ __launch_bounds__(256, 4 / WT) void k_fp8_gemm_dma(const uint8_t* __r
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  for (int s = 0; s < S; ++s) fp8_issue<WT, S>(lds, s, nk, a_src, b_src, wave);
+  for (int s = 0; s < S; ++s) fp8_issue<WT, S>(lds, s, nk, src_k, wave);
   wait_vmcnt<(S - 1) * T::kLoads>();            // step 0 landed (this wave)
   block_barrier();                              // ... for every wave
   v8i fa[2 * WT], fb[2 * WT];
@@ -334,10 +322,10 @@ __global__ __launch_bounds__(256, 4 / WT) void k_fp8_gemm_dma(const uint8_t* __r
 
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
-    fp8_body<WT, S>(fa, fb, acc, lds, kt, nk, wm, wn, lane, a_src, b_src, wave);
-    fp8_body<WT, S>(fb, fa, acc, lds, kt + 1, nk, wm, wn, lane, a_src, b_src, wave);
+    fp8_body<WT, S>(fa, fb, acc, lds, kt, nk, wm, wn, lane, src_k, wave);
+    fp8_body<WT, S>(fb, fa, acc, lds, kt + 1, nk, wm, wn, lane, src_k, wave);
   }
-  if (kt < nk) fp8_body<WT, S>(fa, fb, acc, lds, kt, nk, wm, wn, lane, a_src, b_src, wave);
+  if (kt < nk) fp8_body<WT, S>(fa, fb, acc, lds, kt, nk, wm, wn, lane, src_k, wave);
   wait_lgkmcnt<0>();
   wait_vmcnt<0>();                              // retire the trailing repeat loads
   block_barrier();                              // every wave is done with the ring

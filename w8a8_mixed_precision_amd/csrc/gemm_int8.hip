@@ -241,7 +241,10 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[WT][WT], int M, int N, int 
   const bool vec = (static_cast<int64_t>(N) * EB) % 16 == 0;
   using V8 = typename std::conditional<XBF16, v8bf, v8h>::type;
   char* const y = static_cast<char*>(Y);
-  const int row0 = m0 + wm * WR;
+  // an opaque copy: the row indices below are then recomputed here rather than
+  // kept live across the K loop from the prologue's identical expressions
+  int row0 = m0 + wm * WR;
+  __asm__ volatile("" : "+s"(row0));
 #pragma unroll
   for (int j = 0; j < WT; ++j) {
     const int ncol = wn * WR + 32 * j;
@@ -368,7 +371,7 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm(const int8_t* __restrict__
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * kBM, n0 = tn * kBN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   EpiIn ein;
   epi_prefetch<MODE>(ein, M, N, m0, n0, wm, lane, sx, sw, bias, nO_ptr);
@@ -462,9 +465,8 @@ __device__ __forceinline__ void mfma_sub(const v4i (&f)[8], v16i (&acc)[4][4]) {
 // the time the wave waits for them at the barrier.
 template <bool DMA>
 __device__ __forceinline__ void mma_phase(const v4i (&fm)[8], v16i (&acc)[4][4], const int8_t* sfr, int sub,
-                                          int wm, int wn, int lane, v4i (&fl)[8],
-                                          const int8_t* const (&a_src)[4], const int8_t* const (&b_src)[4],
-                                          int k0, int8_t* st, int wave) {
+                                          int wm, int wn, int lane, v4i (&fl)[8], const DmaSrc& src, int k0,
+                                          int8_t* st, int wave) {
   const int fr = lane & 31, fh = lane >> 5;
   constexpr int kOrder[8] = {0, 4, 5, 6, 7, 1, 2, 3};   // fragment index: 0..3 rows of A, 4..7 rows of B
   auto read = [&](int f) {
@@ -483,9 +485,9 @@ __device__ __forceinline__ void mma_phase(const v4i (&fm)[8], v16i (&acc)[4][4],
     if (DMA) {
       read(kOrder[t]);
       if (t < 4)
-        __builtin_amdgcn_global_load_lds(a_src[t] + k0, st + (wave * 4 + t) * 1024, 16, 0, 0);
+        dma_a(src, st + (wave * 4 + t) * 1024, t, k0);
       else
-        __builtin_amdgcn_global_load_lds(b_src[t - 4] + k0, st + kBM * kBK + (wave * 4 + t - 4) * 1024, 16, 0, 0);
+        dma_b(src, st + kBM * kBK + (wave * 4 + t - 4) * 1024, t - 4, k0);
     } else if (t < 4) {
       read(kOrder[2 * t]);
       read(kOrder[2 * t + 1]);
@@ -507,14 +509,11 @@ constexpr int kSmallStage = 2 * kSmall * kBK;   // one K step of A then B, 16 KB
 constexpr int kSmallLoads = 4;                  // DMA instructions per wave per step
 constexpr int kSmallPartBytes = kSmall * kSmall * 4;
 
-// The builtins of the small-block loop behind plain functions (with
+// The MFMA builtin of the small-block loop behind a plain function (with
 // template-dependent arguments the host compilation pass can drop the kernel
-// templates that use them).
+// templates that use it).
 __device__ __forceinline__ v16i mfma_i8(v4i a, v4i b, v16i c) {
   return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ void lds_dma16(const int8_t* src, int8_t* dst) {
-  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 }
 __device__ __forceinline__ v4i lo4(v8i v) { return __builtin_shufflevector(v, v, 0, 1, 2, 3); }
 __device__ __forceinline__ v4i hi4(v8i v) { return __builtin_shufflevector(v, v, 4, 5, 6, 7); }
@@ -525,14 +524,13 @@ __device__ __forceinline__ const int8_t* small_frag(const int8_t* slot, int f, i
 }
 
 template <int SS>
-__device__ __forceinline__ void small_issue(int8_t* lds, int kt, int nk, const int8_t* const* a_src,
-                                            const int8_t* const* b_src, int wave) {
+__device__ __forceinline__ void small_issue(int8_t* lds, int kt, int nk, const DmaSrc& src, int wave) {
   int8_t* st = lds + (kt % SS) * kSmallStage;
   const int k0 = min(kt, nk - 1) * kBK;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    lds_dma16(a_src[i] + k0, st + (wave * 2 + i) * 1024);
-    lds_dma16(b_src[i] + k0, st + kSmall * kBK + (wave * 2 + i) * 1024);
+    dma_a(src, st + (wave * 2 + i) * 1024, i, k0);
+    dma_b(src, st + kSmall * kBK + (wave * 2 + i) * 1024, i, k0);
   }
 }
 
@@ -545,8 +543,7 @@ __device__ __forceinline__ void small_issue(int8_t* lds, int kt, int nk, const i
 // step into its own, retired slot.
 template <int SS>
 __device__ __forceinline__ void small_body(const v8i* fc, v8i* fn, v16i (*acc)[2], int8_t* lds, int kt, int nk,
-                                           int wm, int wn, int lane, const int8_t* const* a_src,
-                                           const int8_t* const* b_src, int wave) {
+                                           int wm, int wn, int lane, const DmaSrc& src, int wave) {
   wait_lgkmcnt<0>();
   wait_vmcnt<(SS - 2) * kSmallLoads>();
   block_barrier();
@@ -566,8 +563,8 @@ __device__ __forceinline__ void small_body(const v8i* fc, v8i* fn, v16i (*acc)[2
     if ((t & 1) == 0) {
       lo = *reinterpret_cast<const v4i*>(small_frag(sn, f, wm, wn, fr, fh));
       const int d = t >> 1;
-      if (d < 2) lds_dma16(a_src[d] + k0, st + (wave * 2 + d) * 1024);
-      else lds_dma16(b_src[d - 2] + k0, st + kSmall * kBK + (wave * 2 + d - 2) * 1024);
+      if (d < 2) dma_a(src, st + (wave * 2 + d) * 1024, d, k0);
+      else dma_b(src, st + kSmall * kBK + (wave * 2 + d - 2) * 1024, d - 2, k0);
     } else {
       const v4i hi = *reinterpret_cast<const v4i*>(small_frag(sn, f, wm, wn, fr, 2 + fh));
       fn[f] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -601,23 +598,15 @@ __device__ __forceinline__ void small_block(int8_t* lds, const int8_t* __restric
   if (m0 >= M || n0 >= N) return;
   const int nk_all = K / kBK;
   const int kb = piece * nk_all / split, ke = (piece + 1) * nk_all / split, nk = ke - kb;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int fr = lane & 31, fh = lane >> 5;
   EpiIn ein;
   epi_prefetch<MODE, 2>(ein, M, N, m0, n0, wm, lane, sx, sw, bias, nO_ptr);
 
-  // DMA source of this lane for load i (0, 1) of each operand: block row
-  // r = wave*32 + 16*i + lane/4 lands in LDS slot (lane & 3) of that row.
-  const int8_t* a_src[2];
-  const int8_t* b_src[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = wave * 32 + 16 * i + (lane >> 2);
-    const int ch = (lane & 3) ^ swz_term(r);
-    a_src[i] = A + static_cast<int64_t>(min(m0 + r, M - 1)) * K + kb * kBK + ch * 16;
-    b_src[i] = B + static_cast<int64_t>(min(n0 + r, N - 1)) * K + kb * kBK + ch * 16;
-  }
+  // load i (0, 1) of each operand: block row r = wave*32 + 16*i + lane/4
+  // lands in LDS slot (lane & 3) of that row
+  const DmaSrc src_k = dma_src(A, B, m0, n0, M, N, K, kb * kBK, kSmall, wave, lane);
   v16i acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -626,7 +615,7 @@ __device__ __forceinline__ void small_block(int8_t* lds, const int8_t* __restric
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-  for (int st = 0; st < SS; ++st) small_issue<SS>(lds, st, nk, a_src, b_src, wave);
+  for (int st = 0; st < SS; ++st) small_issue<SS>(lds, st, nk, src_k, wave);
   wait_vmcnt<(SS - 1) * kSmallLoads>();
   block_barrier();
   v8i fa[4], fb[4];
@@ -638,10 +627,10 @@ __device__ __forceinline__ void small_block(int8_t* lds, const int8_t* __restric
   }
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
-    small_body<SS>(fa, fb, acc, lds, kt, nk, wm, wn, lane, a_src, b_src, wave);
-    small_body<SS>(fb, fa, acc, lds, kt + 1, nk, wm, wn, lane, a_src, b_src, wave);
+    small_body<SS>(fa, fb, acc, lds, kt, nk, wm, wn, lane, src_k, wave);
+    small_body<SS>(fb, fa, acc, lds, kt + 1, nk, wm, wn, lane, src_k, wave);
   }
-  if (kt < nk) small_body<SS>(fa, fb, acc, lds, kt, nk, wm, wn, lane, a_src, b_src, wave);
+  if (kt < nk) small_body<SS>(fa, fb, acc, lds, kt, nk, wm, wn, lane, src_k, wave);
   wait_lgkmcnt<0>();
   wait_vmcnt<0>();
   block_barrier();
@@ -740,23 +729,15 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
     ke = (piece + 1) * nk_all / split;
   }
   const int m0 = tm * kBM, n0 = tn * kBN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   EpiIn ein;
   epi_prefetch<MODE>(ein, M, N, m0, n0, wm, lane, sx, sw, bias, nO_ptr);
 
-  // DMA source of this lane for load instruction i (0..3) of each operand:
-  // tile row r = wave*64 + 16*i + lane/4 lands in LDS slot (lane & 3) of that
-  // row, which holds logical 16-byte chunk (lane & 3) ^ swz_term(r).
-  const int8_t* a_src[4];
-  const int8_t* b_src[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = wave * 64 + 16 * i + (lane >> 2);
-    const int ch = (lane & 3) ^ swz_term(r);
-    a_src[i] = A + static_cast<int64_t>(min(m0 + r, M - 1)) * K + kb * kBK + ch * 16;
-    b_src[i] = B + static_cast<int64_t>(min(n0 + r, N - 1)) * K + kb * kBK + ch * 16;
-  }
+  // load instruction i (0..3) of each operand: tile row r = wave*64 + 16*i +
+  // lane/4 lands in LDS slot (lane & 3) of that row, which holds logical
+  // 16-byte chunk (lane & 3) ^ swz_term(r)
+  const DmaSrc src_k = dma_src(A, B, m0, n0, M, N, K, kb * kBK, kBM, wave, lane);
   const int nk = ke - kb;
   // DMA of K-step kt into its ring slot. Past the last step the load repeats
   // the last step's data into the slot just retired, which no later step
@@ -767,8 +748,8 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
     const int k0 = min(kt, nk - 1) * kBK;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_global_load_lds(a_src[i] + k0, st + (wave * 4 + i) * 1024, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(b_src[i] + k0, st + kBM * kBK + (wave * 4 + i) * 1024, 16, 0, 0);
+      dma_a(src_k, st + (wave * 4 + i) * 1024, i, k0);
+      dma_b(src_k, st + kBM * kBK + (wave * 4 + i) * 1024, i, k0);
     }
   };
 
@@ -803,13 +784,13 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
   for (int kt = 0; kt < nk - 1; ++kt) {
     int8_t* sa = lds + (kt % S) * kStage;
     // sub-step 0 multiplies while sub-step 1's fragments are read
-    mma_phase<false>(f0, acc, sa, 1, wm, wn, lane, f1, a_src, b_src, 0, nullptr, wave);
+    mma_phase<false>(f0, acc, sa, 1, wm, wn, lane, f1, src_k, 0, nullptr, wave);
     wait_lgkmcnt<0>();                            // this slot is fully read
     wait_vmcnt<(S - 2) * kLoads>();               // step kt+1 landed (this wave)
     block_barrier();                              // ... for every wave; slot kt retired
     // sub-step 1 multiplies while step kt+1's first fragments are read and
     // step kt+S is fetched into the retired slot
-    mma_phase<true>(f1, acc, lds + ((kt + 1) % S) * kStage, 0, wm, wn, lane, f0, a_src, b_src,
+    mma_phase<true>(f1, acc, lds + ((kt + 1) % S) * kStage, 0, wm, wn, lane, f0, src_k,
                     min(kt + S, nk - 1) * kBK, sa, wave);
   }
   load_frags(lds + ((nk - 1) % S) * kStage, 1, wm, wn, lane, f1);

@@ -147,4 +147,49 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(void* part, int s
                                            kRawBuffer);
 }
 
+// Operand rows for the LDS-DMA K loops. Each wave loads 16 rows per
+// instruction, 4 lanes (16 bytes each) per 64-byte row segment; the rows a
+// lane loads are 16 apart, so with the swizzle (row >> 2) & 3 its chunk is the
+// same for all of them and one byte offset per lane serves every load of both
+// operands. The descriptor covers rows r0.. of a K-contiguous int8 matrix with
+// R rows (at most `rows` of them) from byte k_off of each row on; a load past
+// the last valid row reads zeros (the buffer range check), and every offset
+// stays below rows * K, within 32 bits for any K the library accepts.
+struct DmaSrc {
+  __amdgpu_buffer_rsrc_t a, b;   // the tile's rows of A and of B
+  uint32_t voff;                 // this lane's offset: row and swizzled chunk
+  int rows16;                    // bytes between the 16-row groups of a wave: 16 K
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t operand_rsrc(const int8_t* P, int r0, int R, int K, int k_off,
+                                                               int rows) {
+  const int valid = min(R - r0, rows);
+  const uint32_t n = valid > 0 ? static_cast<uint32_t>(valid) * static_cast<uint32_t>(K) - k_off : 0u;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(P) + static_cast<int64_t>(r0) * K + k_off, 0, n,
+                                           kRawBuffer);
+}
+
+// rows_per_wave: 64 (256-row tiles) or 32 (128-row blocks).
+__device__ __forceinline__ DmaSrc dma_src(const int8_t* A, const int8_t* B, int m0, int n0, int M, int N, int K,
+                                          int k_off, int rows, int wave, int lane) {
+  DmaSrc d;
+  d.a = operand_rsrc(A, m0, M, K, k_off, rows);
+  d.b = operand_rsrc(B, n0, N, K, k_off, rows);
+  const int r = wave * (rows / 4) + (lane >> 2);
+  d.voff = static_cast<uint32_t>(r) * static_cast<uint32_t>(K) + (((lane & 3) ^ swz_term(r)) << 4);
+  d.rows16 = 16 * K;
+  return d;
+}
+
+// Load i (16 rows) of this wave's share of operand A or B at byte k0 of the
+// K range into LDS at dst (1 KB: the 16 rows' 64-byte segments). The row goes
+// into the per-lane offset, which the range check covers (the scalar offset
+// is added to the address but not checked); k0 stays inside the row.
+__device__ __forceinline__ void dma_a(const DmaSrc& d, int8_t* dst, int i, int k0) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(d.a, dst, 16, d.voff + i * d.rows16, k0, 0, 0);
+}
+__device__ __forceinline__ void dma_b(const DmaSrc& d, int8_t* dst, int i, int k0) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(d.b, dst, 16, d.voff + i * d.rows16, k0, 0, 0);
+}
+
 }  // namespace w8
