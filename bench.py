@@ -523,6 +523,49 @@ def extra_shapes(torch, w8, steps: int) -> dict:
     return res
 
 
+def tile_timeline(w8, c, call) -> dict:
+    """One GEMM launch of the shape with its per-block timeline (the
+    library's timeline export; a second call, after one warm-up): medians over
+    the blocks that own whole 256x256 tiles of the stretch before the K loop
+    (operand ring fill), the K loop and the epilogue; the K loop in shader-clock
+    cycles per 64-byte K step (1024 is the MFMA issue floor: 32 MFMAs of 32
+    cycles per wave) and that clock's rate; the start of each round of whole
+    tiles; the 128x128 tail's start and length. Times in us from the first
+    block's start (constant 100 MHz clock)."""
+    import numpy as np
+
+    x, wq, sw, y, ws = call
+    w8.debug_int8_gemm_timeline(x, wq, sw, THRESHOLD, y, ws)
+    r = w8.debug_int8_gemm_timeline(x, wq, sw, THRESHOLD, y, ws)
+    st = r["stamps"].astype(np.float64)
+    dp = r["dp_tiles"]
+    t0 = st[:, 0].min()
+    big = st[:dp]
+    nk = c.K // 64
+    done = big[:, 3] >= 0
+    loop_us = (big[:, 2] - big[:, 1]) * 0.01
+    cyc = big[:, 5] - big[:, 4]
+    starts = np.sort(big[:, 0] - t0) * 0.01
+    cus = 256
+    out = {
+        "blocks": r["grid"],
+        "whole_tiles": dp,
+        "span_us": round(float((st[:, 3].max() - t0) * 0.01), 2),
+        "ring_fill_us": round(float(np.median(big[:, 1] - big[:, 0]) * 0.01), 2),
+        "k_loop_us": round(float(np.median(loop_us)), 2),
+        "epilogue_us": round(float(np.median(big[done, 3] - big[done, 2]) * 0.01), 2),
+        "k_step_cycles": round(float(np.median(cyc) / nk), 1),
+        "clock64_mhz": round(float(np.median(cyc / loop_us)), 1),
+        "round_starts_us": [round(float(starts[i]), 2) for i in range(0, dp, cus)],
+    }
+    if r["grid"] > dp:
+        tail = st[dp:]
+        out["tail_start_us"] = round(float((tail[:, 0].min() - t0) * 0.01), 2)
+        out["tail_us"] = round(float((tail[:, 3].max() - tail[:, 0].min()) * 0.01), 2)
+        out["tail_block_us"] = round(float(np.median(tail[:, 3] - tail[:, 0]) * 0.01), 2)
+    return out
+
+
 def measured_peaks(torch, w8) -> dict:
     """The chip's attainable rates, measured here: dense MFMA issue (int8,
     fp8, bf16) with every SIMD busy (the library's peak kernel, median of 5
@@ -627,6 +670,7 @@ def main() -> int:
     per_shape = {}
     for i, c in enumerate(cases):
         per_shape[c.name] = shape_timing(torch, w8, c, calls[i], st[i], args.steps)
+        per_shape[c.name]["tile_timeline"] = tile_timeline(w8, c, calls[i])
         print(f"[bench] {c.name}: {per_shape[c.name]}", file=sys.stderr, flush=True)
     del st
 

@@ -444,6 +444,22 @@ w8_status w8dbg_fp8_w8a16_linear(const void* X, int x_dt, int64_t M, int64_t K, 
                                  const float* sw, int64_t N, int split, int tile, void* Y, int y_dt,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* int8_mixed_linear that also records a per-block timeline of its GEMM
+ * launch: block b writes stamps[8b .. 8b+7] (device memory, int64): [0] its
+ * start, [1] the start of its K loop, [2] the end of the K loop, [3] its end,
+ * in ticks of the GPU's constant 100 MHz clock (wall_clock64); [4] and [5] the
+ * shader-clock counter (clock64) at [1] and [2]. Blocks of the 128x128 tail
+ * write [0] and [3] only, a split-K slice that leaves the epilogue to another
+ * slice writes no [3]; words a block does not write keep their contents.
+ * grid (host, 3 ints) receives the launch's block count, the number of blocks
+ * that own whole 256x256 tiles (the first ones), and 1 if K % 64 == 0 (the
+ * kernel that records the timeline) else 0. With stamps NULL only grid is
+ * filled and nothing runs. stamps_len < 8 * blocks is an invalid argument. */
+w8_status w8dbg_int8_gemm_timeline(const void* X, int x_dt, int64_t M, int64_t K, const int8_t* Wq,
+                                   const float* sw, int64_t N, float threshold, void* Y, int y_dt,
+                                   void* workspace, size_t workspace_bytes, long long* stamps,
+                                   size_t stamps_len, int* grid, void* stream);
+
 /* int8_mixed_linear_fused that also records the caller's HIP events
  * events[0..3] (hipEvent_t, created by the caller; NULL entries are skipped)
  * on `stream`: before the row pass, after it, after the outlier fix-up and

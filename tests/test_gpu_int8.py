@@ -329,6 +329,31 @@ def test_deterministic_non_default_stream_and_no_out_of_bounds_writes():
     _check_outputs(y2, ref, "f32", "stream", c.x_bits, "bf16", wq_ref, sw_ref)
 
 
+def test_gemm_timeline_export_is_ordered_and_output_unchanged():
+    """The timeline export runs the same launch as int8_mixed_linear (the same
+    output bits) and every block's stamps are ordered: whole tiles start, fill
+    the ring, run the K loop and finish in order; tail blocks start and end."""
+    c = synth.random_linear(4100, 256, 4352, seed=44, x_dtype="bf16", outlier_cols=3)   # 289 tiles: 256 whole + a tail
+    wq, sw, _, _ = _quant_weights_both(c)
+    x = dev16(c.x_bits, "bf16")
+    ws = w8.new_workspace(w8.int8_mixed_linear_workspace_size(c.M, c.N, c.K))
+    announce("int8 gemm timeline")
+    y_ref = w8.int8_mixed_linear(x, wq, sw, 6.0, torch.float16, workspace=ws)
+    y = torch.empty_like(y_ref)
+    r = w8.debug_int8_gemm_timeline(x, wq, sw, 6.0, y, ws)
+    assert torch.equal(y, y_ref)
+    st, dp = r["stamps"], r["dp_tiles"]
+    assert st.shape == (r["grid"], 8) and 0 < dp <= r["grid"]
+    big = st[:dp]
+    assert np.all(big[:, 0] > 0)
+    assert np.all(big[:, 0] <= big[:, 1]) and np.all(big[:, 1] <= big[:, 2])
+    assert np.all(big[:, 4] < big[:, 5])
+    done = big[:, 3] >= 0
+    assert np.all(big[done, 2] <= big[done, 3])
+    tail = st[dp:]
+    assert np.all(tail[:, 0] > 0) and np.all(tail[:, 3] >= tail[:, 0]) and np.all(tail[:, 1] == -1)
+
+
 # ----------------------------------------------------------------------------
 # the DiT workloads at full size: 1024^2 in the configuration bench.py times,
 # and 2048^2 (16640 tokens)

@@ -194,6 +194,27 @@ def _events_arg(events):
     return arr
 
 
+def debug_int8_gemm_timeline(x: torch.Tensor, wq: torch.Tensor, sw: torch.Tensor, threshold: float,
+                             out: torch.Tensor, workspace: torch.Tensor) -> dict:
+    """int8_mixed_linear with its GEMM launch's per-block timeline (see
+    w8dbg_int8_gemm_timeline in include/w8mp.h). Returns {"stamps": int64
+    [blocks, 8] on the host (unwritten words -1), "grid": blocks, "dp_tiles":
+    blocks that own whole 256x256 tiles}."""
+    import ctypes
+
+    M, K = x.shape
+    N = wq.shape[0]
+    g = (ctypes.c_int * 3)()
+    args = (x.data_ptr(), _dt(x), M, K, wq.data_ptr(), sw.data_ptr(), N, float(threshold), out.data_ptr(), _dt(out),
+            workspace.data_ptr(), workspace.numel())
+    _abi.check(lib().w8dbg_int8_gemm_timeline(*args, None, 0, g, _stream(x)))
+    if g[2] != 1:
+        raise W8Error(_abi.W8_ERR_UNSUPPORTED, "the timeline needs K % 64 == 0")
+    stamps = torch.full((g[0], 8), -1, dtype=torch.int64, device=x.device)
+    _abi.check(lib().w8dbg_int8_gemm_timeline(*args, stamps.data_ptr(), stamps.numel(), g, _stream(x)))
+    return {"stamps": stamps.cpu().numpy(), "grid": int(g[0]), "dp_tiles": int(g[1])}
+
+
 def debug_int8_mixed_linear_events(x: torch.Tensor, wq: torch.Tensor, sw: torch.Tensor, threshold: float, events,
                                    out: torch.Tensor, workspace: torch.Tensor, bias: torch.Tensor | None = None,
                                    producer: Producer | None = None) -> torch.Tensor:

@@ -69,6 +69,8 @@ SIGNATURES = {
     "w8dbg_int8_mixed_linear_events": (_int, [_p, _int, _i64, _i64, _p, _p, _p, _p, _i64, _f, _p, _int, _p, _size,
                                                _p, _p]),
     "w8dbg_fp8_w8a8_linear_events": (_int, [_p, _int, _i64, _i64, _p, _p, _i64, _p, _p, _int, _p, _size, _p, _p]),
+    "w8dbg_int8_gemm_timeline": (_int, [_p, _int, _i64, _i64, _p, _p, _i64, _f, _p, _int, _p, _size, _p, _size,
+                                         ctypes.POINTER(ctypes.c_int), _p]),
     "w8dbg_int8_workspace_layout": (_int, [_i64, _i64, _i64, ctypes.POINTER(_size)]),
     "w8dbg_dit_block_layout": (_int, [_i64, _i64, _i64, ctypes.POINTER(_size)]),
     "w8dbg_mfma_peak": (_int, [_int, _int, _int, _p, ctypes.POINTER(ctypes.c_double), _p]),

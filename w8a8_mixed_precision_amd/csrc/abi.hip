@@ -325,7 +325,8 @@ static w8_status producer_args(const w8_producer* p, int64_t K, int* kind, w8::P
 static w8_status int8_linear_impl(const void* X, int x_dt, int64_t M, int64_t K, const w8_producer* producer,
                                   const int8_t* Wq, const float* sw, const float* bias, int64_t N, float threshold,
                                   void* Y, int y_dt, void* workspace, size_t workspace_bytes, void* stream,
-                                  void* const* events, const char* what, size_t need = 0) {
+                                  void* const* events, const char* what, size_t need = 0,
+                                  long long* timeline = nullptr) {
   if (w8_status st = int8_common_checks(X, x_dt, M, K, threshold); st != W8_OK) return st;
   W8_REQUIRE(Wq && sw && Y, W8_ERR_INVALID_ARGUMENT, "null pointer argument");
   W8_REQUIRE(N >= 1 && N <= kMaxDim, W8_ERR_INVALID_ARGUMENT, "N must be in [1, 2^31)");
@@ -362,7 +363,7 @@ static w8_status int8_linear_impl(const void* X, int x_dt, int64_t M, int64_t K,
   w8::launch_outlier_fixup(X, bf, M, (int)K, tb, flags, stamp, q, sx, O, nO, XO, Wq, N, WO, kind, pa, s);
   mark(events, 2, s);
   w8::launch_int8_gemm(q, Wq, M, N, K, sx, sw, nO, XO, WO, bf, bias, Y, y_dt == W8_DT_F16 ? 1 : 2, plan, part, cnt,
-                       src, s);
+                       src, s, timeline);
   mark(events, 3, s);
   return check_launch(what);
 }
@@ -609,6 +610,26 @@ w8_status w8dbg_int8_mixed_linear_events(const void* H, int h_dt, int64_t M, int
                                          void* const* events, void* stream) {
   return int8_linear_impl(H, h_dt, M, K, producer, Wq, sw, bias, N, threshold, Y, y_dt, workspace, workspace_bytes,
                           stream, events, "w8dbg_int8_mixed_linear_events");
+}
+
+w8_status w8dbg_int8_gemm_timeline(const void* X, int x_dt, int64_t M, int64_t K, const int8_t* Wq, const float* sw,
+                                    int64_t N, float threshold, void* Y, int y_dt, void* workspace,
+                                    size_t workspace_bytes, long long* stamps, size_t stamps_len, int* grid,
+                                    void* stream) {
+  W8_REQUIRE(grid, W8_ERR_INVALID_ARGUMENT, "null pointer argument");
+  W8_REQUIRE(M >= 1 && N >= 1 && K >= 1, W8_ERR_INVALID_ARGUMENT, "M, N, K must be >= 1");
+  const Int8Ws L = int8_layout(M, N, K);
+  W8_REQUIRE(workspace_bytes >= L.base, W8_ERR_WORKSPACE, "workspace smaller than its fixed regions");
+  const w8::GemmPlan plan = int8_plan(M, N, K, workspace_bytes - L.base);
+  grid[0] = plan.grid();
+  grid[1] = plan.dp_tiles;
+  grid[2] = K % 64 == 0 ? 1 : 0;                // the timeline is recorded by the 64-byte-step kernel only
+  if (!stamps) return ok();
+  W8_REQUIRE(grid[2] == 1, W8_ERR_UNSUPPORTED, "the timeline needs K %% 64 == 0");
+  W8_REQUIRE(stamps_len >= 8 * static_cast<size_t>(grid[0]), W8_ERR_INVALID_ARGUMENT,
+             "stamps holds %zu words; the launch needs 8 per block (%d blocks)", stamps_len, grid[0]);
+  return int8_linear_impl(X, x_dt, M, K, nullptr, Wq, sw, nullptr, N, threshold, Y, y_dt, workspace, workspace_bytes,
+                          stream, nullptr, "w8dbg_int8_gemm_timeline", 0, stamps);
 }
 
 w8_status w8dbg_fp8_w8a8_linear_events(const void* X, int x_dt, int64_t M, int64_t K, const uint8_t* Wq8,

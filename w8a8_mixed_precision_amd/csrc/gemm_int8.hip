@@ -244,7 +244,7 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[WT][WT], int M, int N, int 
   // an opaque copy: the row indices below are then recomputed here rather than
   // kept live across the K loop from the prologue's identical expressions
   int row0 = m0 + wm * WR;
-  __asm__ volatile("" : "+s"(row0));
+  __asm__ volatile("" : "+v"(row0));
 #pragma unroll
   for (int j = 0; j < WT; ++j) {
     const int ncol = wn * WR + 32 * j;
@@ -691,7 +691,7 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
                                                           const float* __restrict__ bias, void* __restrict__ Y,
                                                           int tiles_m, int tiles_n, int dp_tiles, int split,
                                                           int small, int* __restrict__ part, int* __restrict__ cnt,
-                                                          SideSrc src) {
+                                                          SideSrc src, long long* __restrict__ tl) {
   constexpr int kStage = 2 * kBM * kBK;       // A then B, 32 KB
   constexpr int kLoads = 8;                   // DMA instructions per wave per step
   // the ring, then the tile's outlier operands (kSideLds)
@@ -705,9 +705,21 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
   int* const s_last = reinterpret_cast<int*>(lds + kEpiLds8);
   static_assert(S * kStage >= kEpiLds8 + 4, "epilogue LDS and arrival flag");
 
+  // Optional per-block timeline (debug export only; tl is null otherwise):
+  // wave 0's first lane writes 8 words per block: [0] start, [1] K loop
+  // start, [2] K loop end, [3] end (100 MHz constant clock, wall_clock64),
+  // [4], [5] the shader-clock counter (clock64) at [1] and [2]. A K-slice
+  // that hands its partial to another block writes no end.
+  auto stamp = [&](int p, long long v) {
+    if (tl != nullptr && threadIdx.x == 0) {
+      tl[static_cast<int64_t>(blockIdx.x) * 8 + p] = v;
+    }
+  };
   if (small && static_cast<int>(blockIdx.x) >= dp_tiles) {
+    stamp(0, wall_clock64());
     small_block<MODE, XBF16, S>(lds, A, B, M, N, K, sx, sw, nO_ptr, XO, WO, bias, Y, tiles_m, tiles_n, dp_tiles,
                                 split, part, cnt, src);
+    stamp(3, wall_clock64());
     return;
   }
   const int nk_all = K / kBK;
@@ -739,6 +751,7 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
   // 16-byte chunk (lane & 3) ^ swz_term(r)
   const DmaSrc src_k = dma_src(A, B, m0, n0, M, N, K, kb * kBK, kBM, wave, lane);
   const int nk = ke - kb;
+  stamp(0, wall_clock64());                       // (after the set-up: a store before it costs uniformity)
   // DMA of K-step kt into its ring slot. Past the last step the load repeats
   // the last step's data into the slot just retired, which no later step
   // reads: every iteration then issues the same number of loads, so the wait
@@ -779,6 +792,8 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
   if (side) wait_vmcnt<(S - 1) * kLoads + 8>();
   else wait_vmcnt<(S - 1) * kLoads>();
   block_barrier();                                // ... for every wave
+  stamp(1, wall_clock64());
+  stamp(4, clock64());
   v4i f0[8], f1[8];
   load_frags(lds, 0, wm, wn, lane, f0);
   for (int kt = 0; kt < nk - 1; ++kt) {
@@ -798,6 +813,8 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
   mfma_sub(f1, acc);
   wait_vmcnt<0>();                                // retire the trailing repeat loads
   block_barrier();                                // every wave is done with the ring
+  stamp(2, wall_clock64());
+  stamp(5, clock64());
 
   if (slot >= 0) {
     // Partials go through sc1 buffer accesses (partial_rsrc). Once a wave's
@@ -846,6 +863,7 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
   finish_tile<MODE, XBF16>(acc, ein, reinterpret_cast<char*>(lds), M, N, m0, n0, wm, wn, lane, XO, WO, src,
                            side ? reinterpret_cast<const char*>(lds) + S * kStage : nullptr,
                            reinterpret_cast<char*>(lds) + S * kStage, Y);
+  stamp(3, wall_clock64());
 }
 
 // ---------------------------------------------------------------------------
@@ -934,7 +952,7 @@ GemmPlan plan_int8_gemm_forced(int64_t M, int64_t N, int cus, bool small, int sp
 void launch_int8_gemm(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t K, const float* sx,
                       const float* sw, const int* nO, const uint16_t* XO, const uint16_t* WO, bool xbf16,
                       const float* bias, void* Y, int mode, const GemmPlan& plan, int* part, int* cnt,
-                      const SideSrc& src, hipStream_t s) {
+                      const SideSrc& src, hipStream_t s, long long* timeline) {
   const int tiles_m = plan.tiles_m, tiles_n = plan.tiles_n;
   const int m = (int)M, n = (int)N, k = (int)K;
   const dim3 block(256);
@@ -942,7 +960,7 @@ void launch_int8_gemm(const int8_t* A, const int8_t* B, int64_t M, int64_t N, in
     constexpr int S = 4;
     const dim3 grid(plan.grid());
 #define W8_GEMM_ARGS A, B, m, n, k, sx, sw, nO, XO, WO, bias, Y, tiles_m, tiles_n, plan.dp_tiles, plan.split, \
-    plan.small ? 1 : 0, part, cnt, src
+    plan.small ? 1 : 0, part, cnt, src, timeline
     if (mode == 0) k_int8_gemm_dma<0, true, S><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
     else if (mode == 1 && xbf16) k_int8_gemm_dma<1, true, S><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
     else if (mode == 1) k_int8_gemm_dma<1, false, S><<<grid, block, 0, s>>>(W8_GEMM_ARGS);

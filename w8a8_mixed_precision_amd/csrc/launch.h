@@ -77,7 +77,7 @@ void launch_fp8_rows(const void* X, bool bf16, int64_t rows, int K, const float*
 void launch_int8_gemm(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t K, const float* sx,
                       const float* sw, const int* nO, const uint16_t* XO, const uint16_t* WO, bool xbf16,
                       const float* bias, void* Y, int mode, const GemmPlan& plan, int* part, int* cnt,
-                      const SideSrc& src, hipStream_t s);
+                      const SideSrc& src, hipStream_t s, long long* timeline = nullptr);
 GemmPlan plan_fp8_gemm(int64_t M, int64_t N, int64_t K, int cus);
 GemmPlan plan_fp8_gemm_split(int64_t M, int64_t N, int split, int bm);
 void launch_fp8_gemm(const uint8_t* A, const uint8_t* B, int64_t M, int64_t N, int64_t K, const float* sx,
