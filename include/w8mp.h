@@ -382,7 +382,10 @@ w8_status w8dbg_produce(const void* H, int h_dt, int64_t M, int64_t K, const w8_
  * tile when there are fewer tiles than compute units) run as `split` K-slices
  * of whole tiles (tail = 1; split = 1 runs every tile whole) or of 128x128
  * quarters (tail = 2); tail 1 with split > 1 and tail 2 need K % 64 == 0 and
- * split <= K / 64 (else W8_ERR_UNSUPPORTED). Workspace:
+ * split <= K / 64 (else W8_ERR_UNSUPPORTED). tail = 3 (split must be 1,
+ * K % 64 == 0): stream-K, the tiles of the last full wave and the leftover
+ * ones (every tile when there are fewer than two waves) shared evenly by one
+ * block per compute unit, K step by K step. Workspace:
  * w8dbg_int8_gemm_i32_workspace_size(M, N, K, tail, split) bytes on the
  * current device (may be 0, then workspace may be NULL), zero-filled before
  * first use (left zero by every call). */
@@ -451,10 +454,14 @@ w8_status w8dbg_fp8_w8a16_linear(const void* X, int x_dt, int64_t M, int64_t K, 
  * shader-clock counter (clock64) at [1] and [2]. Blocks of the 128x128 tail
  * write [0] and [3] only, a split-K slice that leaves the epilogue to another
  * slice writes no [3]; words a block does not write keep their contents.
- * grid (host, 3 ints) receives the launch's block count, the number of blocks
- * that own whole 256x256 tiles (the first ones), and 1 if K % 64 == 0 (the
- * kernel that records the timeline) else 0. With stamps NULL only grid is
- * filled and nothing runs. stamps_len < 8 * blocks is an invalid argument. */
+ * A stream-K block with several tile pieces keeps [1], [2], [4], [5] of the
+ * last piece that wrote them and [3] of the last piece that ran an epilogue.
+ * grid (host, 4 ints) receives the launch's block count, the number of blocks
+ * that own whole 256x256 tiles (the first ones), 1 if K % 64 == 0 (the
+ * kernel that records the timeline) else 0, and what the other blocks are:
+ * 0 K-slices of whole tiles, 1 128x128 quarters, 2 stream-K blocks. With
+ * stamps NULL only grid is filled and nothing runs. stamps_len < 8 * blocks
+ * is an invalid argument. */
 w8_status w8dbg_int8_gemm_timeline(const void* X, int x_dt, int64_t M, int64_t K, const int8_t* Wq,
                                    const float* sw, int64_t N, float threshold, void* Y, int y_dt,
                                    void* workspace, size_t workspace_bytes, long long* stamps,

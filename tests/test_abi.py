@@ -263,7 +263,9 @@ def test_debug_exports_reject():
     lib = _abi.lib()
     assert lib.w8dbg_int8_gemm_i32(A, A, 4, 4, 20, 0, 1, A, None, 0, None) == _abi.W8_ERR_INVALID_ARGUMENT
     assert lib.w8dbg_int8_gemm_i32(None, A, 4, 4, 32, 0, 1, A, None, 0, None) == _abi.W8_ERR_INVALID_ARGUMENT
-    assert lib.w8dbg_int8_gemm_i32(A, A, 4, 4, 64, 3, 1, A, None, 0, None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert lib.w8dbg_int8_gemm_i32(A, A, 4, 4, 64, 4, 1, A, None, 0, None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert lib.w8dbg_int8_gemm_i32(A, A, 4, 4, 64, 3, 2, A, None, 0, None) == _abi.W8_ERR_INVALID_ARGUMENT  # stream-K
+    assert lib.w8dbg_int8_gemm_i32(A, A, 4, 4, 80, 3, 1, A, None, 0, None) == _abi.W8_ERR_UNSUPPORTED
     assert lib.w8dbg_int8_gemm_i32(A, A, 4, 4, 64, 2, 0, A, None, 0, None) == _abi.W8_ERR_INVALID_ARGUMENT
     assert lib.w8dbg_int8_gemm_i32(A, A, 4, 4, 80, 2, 1, A, None, 0, None) == _abi.W8_ERR_UNSUPPORTED
     assert lib.w8dbg_int8_gemm_i32(A, A, 4, 4, 128, 1, 3, A, None, 0, None) == _abi.W8_ERR_UNSUPPORTED
@@ -376,15 +378,16 @@ def test_noalloc_rejects_shapes_beyond_its_scratch():
 def test_gemm_timeline_query_and_rejects():
     """With stamps NULL the timeline export reports the launch's grid without
     running anything. For the DiT 1024^2 QKV linear that is 816 whole tiles
-    with no device to plan for (here), or 768 plus the 48 leftover tiles as 4
-    quarters each on a 256-CU device; a short stamps buffer is rejected."""
+    with no device to plan for (here), or on a 256-CU device 768 whole tiles
+    and the 48 leftover ones as 128x128 quarters; a short stamps buffer is
+    rejected."""
     lib = _abi.lib()
     bf, f16 = _abi.W8_DT_BF16, _abi.W8_DT_F16
     M, N, K = 4352, 12288, 4096
     ws = lib.int8_mixed_linear_workspace_size(M, N, K)
-    g = (ctypes.c_int * 3)()
+    g = (ctypes.c_int * 4)()
     assert lib.w8dbg_int8_gemm_timeline(A, bf, M, K, A, A, N, 6.0, A, f16, A, ws, None, 0, g, None) == _abi.W8_OK
-    assert list(g) in ([816, 816, 1], [768 + 4 * 48, 768, 1])
+    assert list(g) in ([816, 816, 1, 0], [768 + 4 * 48, 768, 1, 1])
     assert lib.w8dbg_int8_gemm_timeline(A, bf, M, K, A, A, N, 6.0, A, f16, A, ws, A, 8 * g[0] - 1, g,
                                         None) == _abi.W8_ERR_INVALID_ARGUMENT
     assert lib.w8dbg_int8_gemm_timeline(A, bf, 64, 48, A, A, 32, 6.0, A, f16, A, WS_BIG, A, 1 << 20, g,

@@ -185,14 +185,18 @@ def test_int8_gemm_accumulators_bit_exact(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 520, 4096), (77, 300, 2048), (513, 1040, 1024), (256, 512, 192),
-                                   (1, 16, 640)])
-@pytest.mark.parametrize("tail,split", [(1, 1), (1, 2), (1, 3), (2, 1), (2, 2), (2, 5)])
+                                   (1, 16, 640), (4352, 4352, 128), (4352, 12288, 128)])
+@pytest.mark.parametrize("tail,split", [(1, 1), (1, 2), (1, 3), (2, 1), (2, 2), (2, 5), (3, 1)])
 def test_int8_gemm_tail_treatments_bit_exact(M, N, K, tail, split):
-    """Every treatment of the leftover tiles of a partial wave (here all tiles:
-    fewer tiles than compute units): whole 256x256 tiles, K-sliced 256x256
-    tiles, and 128x128 quarters whole or K-sliced (quarters outside [M, N)
-    included). Repeated calls through one workspace stay exact and leave the
-    split-K counters zero."""
+    """Every treatment of the leftover tiles of a partial wave (all tiles
+    when there are fewer tiles than compute units): whole 256x256 tiles,
+    K-sliced 256x256 tiles, 128x128 quarters whole or K-sliced (quarters
+    outside [M, N) included), and stream-K (tail 3): one block per compute
+    unit over the last full wave and the leftover tiles: from 32
+    blocks sharing one tile (6 tiles of 64 K steps) to pieces of 3 steps that
+    cross tile boundaries (289 tiles of 2 steps; 816 tiles of 2 steps: two
+    rounds of whole tiles, then stream-K over 304). Repeated calls through
+    one workspace stay exact and leave the counters zero."""
     if split > K // 64:
         pytest.skip("more slices than K steps")
     rng = np.random.default_rng(M * 5 + N + K + 10 * tail + split)
@@ -331,27 +335,31 @@ def test_deterministic_non_default_stream_and_no_out_of_bounds_writes():
 
 def test_gemm_timeline_export_is_ordered_and_output_unchanged():
     """The timeline export runs the same launch as int8_mixed_linear (the same
-    output bits) and every block's stamps are ordered: whole tiles start, fill
-    the ring, run the K loop and finish in order; tail blocks start and end."""
-    c = synth.random_linear(4100, 256, 4352, seed=44, x_dtype="bf16", outlier_cols=3)   # 289 tiles: 256 whole + a tail
-    wq, sw, _, _ = _quant_weights_both(c)
-    x = dev16(c.x_bits, "bf16")
-    ws = w8.new_workspace(w8.int8_mixed_linear_workspace_size(c.M, c.N, c.K))
+    output bits) and every block's stamps are ordered: it starts, fills the
+    ring, runs the K loop and finishes in order (stream-K blocks: for their
+    last piece); 128x128 tail blocks write their start and end only."""
     announce("int8 gemm timeline")
-    y_ref = w8.int8_mixed_linear(x, wq, sw, 6.0, torch.float16, workspace=ws)
-    y = torch.empty_like(y_ref)
-    r = w8.debug_int8_gemm_timeline(x, wq, sw, 6.0, y, ws)
-    assert torch.equal(y, y_ref)
-    st, dp = r["stamps"], r["dp_tiles"]
-    assert st.shape == (r["grid"], 8) and 0 < dp <= r["grid"]
-    big = st[:dp]
-    assert np.all(big[:, 0] > 0)
-    assert np.all(big[:, 0] <= big[:, 1]) and np.all(big[:, 1] <= big[:, 2])
-    assert np.all(big[:, 4] < big[:, 5])
-    done = big[:, 3] >= 0
-    assert np.all(big[done, 2] <= big[done, 3])
-    tail = st[dp:]
-    assert np.all(tail[:, 0] > 0) and np.all(tail[:, 3] >= tail[:, 0]) and np.all(tail[:, 1] == -1)
+    for M, K, N in [(4100, 256, 4352), (600, 512, 1100)]:
+        c = synth.random_linear(M, K, N, seed=44, x_dtype="bf16", outlier_cols=3)
+        wq, sw, _, _ = _quant_weights_both(c)
+        x = dev16(c.x_bits, "bf16")
+        ws = w8.new_workspace(w8.int8_mixed_linear_workspace_size(c.M, c.N, c.K))
+        y_ref = w8.int8_mixed_linear(x, wq, sw, 6.0, torch.float16, workspace=ws)
+        y = torch.empty_like(y_ref)
+        r = w8.debug_int8_gemm_timeline(x, wq, sw, 6.0, y, ws)
+        assert torch.equal(y, y_ref)
+        st, dp = r["stamps"], r["dp_tiles"]
+        assert st.shape == (r["grid"], 8) and 0 <= dp <= r["grid"]
+        loop = st[:dp] if r["rest"] == "small" else st
+        ran = loop[:, 1] >= 0                     # stream-K blocks past the last K step do nothing
+        assert np.all(loop[ran, 0] > 0)
+        assert np.all(loop[ran, 0] <= loop[ran, 1]) and np.all(loop[ran, 1] <= loop[ran, 2])
+        assert np.all(loop[ran, 4] < loop[ran, 5])
+        done = ran & (loop[:, 3] >= 0)
+        assert np.all(loop[done, 2] <= loop[done, 3])
+        if r["rest"] == "small":
+            tail = st[dp:]
+            assert np.all(tail[:, 0] > 0) and np.all(tail[:, 3] >= tail[:, 0]) and np.all(tail[:, 1] == -1)
 
 
 # ----------------------------------------------------------------------------

@@ -199,12 +199,13 @@ def debug_int8_gemm_timeline(x: torch.Tensor, wq: torch.Tensor, sw: torch.Tensor
     """int8_mixed_linear with its GEMM launch's per-block timeline (see
     w8dbg_int8_gemm_timeline in include/w8mp.h). Returns {"stamps": int64
     [blocks, 8] on the host (unwritten words -1), "grid": blocks, "dp_tiles":
-    blocks that own whole 256x256 tiles}."""
+    blocks that own whole 256x256 tiles, "rest": what the other blocks are
+    ("split", "small" or "streamk")}."""
     import ctypes
 
     M, K = x.shape
     N = wq.shape[0]
-    g = (ctypes.c_int * 3)()
+    g = (ctypes.c_int * 4)()
     args = (x.data_ptr(), _dt(x), M, K, wq.data_ptr(), sw.data_ptr(), N, float(threshold), out.data_ptr(), _dt(out),
             workspace.data_ptr(), workspace.numel())
     _abi.check(lib().w8dbg_int8_gemm_timeline(*args, None, 0, g, _stream(x)))
@@ -212,7 +213,8 @@ def debug_int8_gemm_timeline(x: torch.Tensor, wq: torch.Tensor, sw: torch.Tensor
         raise W8Error(_abi.W8_ERR_UNSUPPORTED, "the timeline needs K % 64 == 0")
     stamps = torch.full((g[0], 8), -1, dtype=torch.int64, device=x.device)
     _abi.check(lib().w8dbg_int8_gemm_timeline(*args, stamps.data_ptr(), stamps.numel(), g, _stream(x)))
-    return {"stamps": stamps.cpu().numpy(), "grid": int(g[0]), "dp_tiles": int(g[1])}
+    return {"stamps": stamps.cpu().numpy(), "grid": int(g[0]), "dp_tiles": int(g[1]),
+            "rest": ("split", "small", "streamk")[g[3]]}
 
 
 def debug_int8_mixed_linear_events(x: torch.Tensor, wq: torch.Tensor, sw: torch.Tensor, threshold: float, events,
@@ -440,7 +442,8 @@ def debug_int8_gemm_i32(q: torch.Tensor, wq: torch.Tensor, tail: int = 0, split:
                         workspace: torch.Tensor | None = None) -> torch.Tensor:
     """acc [M,N] int32 = q . wq^T on the int8 MFMA kernel. tail 0: the linear's
     own grid; 1: leftover tiles as `split` 256x256 K-slices (1: all whole);
-    2: as `split` K-slices of 128x128 quarters (see include/w8mp.h)."""
+    2: as `split` K-slices of 128x128 quarters; 3: stream-K over the last full
+    wave and the leftover tiles (see include/w8mp.h)."""
     _dev(q, "q"), _dev(wq, "wq")
     M, K = q.shape
     N = wq.shape[0]

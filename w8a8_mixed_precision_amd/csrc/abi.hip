@@ -193,6 +193,7 @@ uint32_t threshold_bits(float t, bool bf16) {
 // leftover tiles as `split` 256x256 slices (split 1: every tile whole); 2 as
 // `split` slices of 128x128 quarters. Workspace: the front, then partials.
 w8::GemmPlan int8_debug_plan(int64_t M, int64_t N, int64_t K, int tail, int split, int cus) {
+  if (tail == 3) return w8::plan_int8_gemm_streamk(M, N, cus);
   return tail == 0 ? w8::plan_int8_gemm(M, N, K, cus) : w8::plan_int8_gemm_forced(M, N, cus, tail == 2, split);
 }
 
@@ -624,6 +625,7 @@ w8_status w8dbg_int8_gemm_timeline(const void* X, int x_dt, int64_t M, int64_t K
   grid[0] = plan.grid();
   grid[1] = plan.dp_tiles;
   grid[2] = K % 64 == 0 ? 1 : 0;                // the timeline is recorded by the 64-byte-step kernel only
+  grid[3] = plan.streamk ? 2 : (plan.small ? 1 : 0);
   if (!stamps) return ok();
   W8_REQUIRE(grid[2] == 1, W8_ERR_UNSUPPORTED, "the timeline needs K %% 64 == 0");
   W8_REQUIRE(stamps_len >= 8 * static_cast<size_t>(grid[0]), W8_ERR_INVALID_ARGUMENT,
@@ -715,7 +717,7 @@ w8_status w8dbg_int8_quantize_activations(const void* X, int x_dt, int64_t M, in
 }
 
 size_t w8dbg_int8_gemm_i32_workspace_size(int64_t M, int64_t N, int64_t K, int tail, int split) {
-  if (M < 1 || N < 1 || K < 1 || tail < 0 || tail > 2 || split < 1) return 0;
+  if (M < 1 || N < 1 || K < 1 || tail < 0 || tail > 3 || split < 1) return 0;
   return kFront + up(int8_debug_plan(M, N, K, tail, split, cu_count()).partial_bytes());
 }
 
@@ -724,7 +726,8 @@ w8_status w8dbg_int8_gemm_i32(const int8_t* q, const int8_t* Wq, int64_t M, int6
   W8_REQUIRE(q && Wq && acc, W8_ERR_INVALID_ARGUMENT, "null pointer argument");
   if (w8_status st = check_mk(M, K, W8_INT8_MAX_K); st != W8_OK) return st;
   W8_REQUIRE(N >= 1 && N <= kMaxDim, W8_ERR_INVALID_ARGUMENT, "N must be in [1, 2^31)");
-  W8_REQUIRE(tail >= 0 && tail <= 2 && split >= 1, W8_ERR_INVALID_ARGUMENT, "tail must be 0..2 and split >= 1");
+  W8_REQUIRE(tail >= 0 && tail <= 3 && split >= 1, W8_ERR_INVALID_ARGUMENT, "tail must be 0..3 and split >= 1");
+  W8_REQUIRE(tail != 3 || split == 1, W8_ERR_INVALID_ARGUMENT, "stream-K (tail 3) takes split = 1");
   W8_REQUIRE(tail == 0 || (tail == 1 && split == 1) || (K % 64 == 0 && split <= K / 64), W8_ERR_UNSUPPORTED,
              "this tail treatment needs K %% 64 == 0 and split <= K / 64");
   W8_REQUIRE(aligned16(q) && aligned16(Wq) && aligned16(acc), W8_ERR_INVALID_ARGUMENT,

@@ -19,20 +19,30 @@ int device_cus();
 // GEMM uses bm = 256, and with `small` runs each of the sk_tiles leftover
 // tiles as four 128x128 blocks (each cut into `split` slices); the FP8 GEMM
 // and the FP8 weight-only GEMMs use bm = 256 or 128, the W4A8 GEMM 128.
+// Tiles past dp_tiles (sk_tiles of them) run as `split` K-slices of whole
+// tiles, as `split` K-slices of 128x128 quarters (small), or (streamk, int8
+// only) as sk_blocks blocks that share their K steps evenly.
 struct GemmPlan {
   int tiles_m, tiles_n, dp_tiles, split, sk_tiles;
   int bm = 256;
   bool small = false;
+  bool streamk = false;
+  int sk_blocks = 0;
   int units() const { return small ? 4 * sk_tiles : sk_tiles; }       // blocks per K-slice past dp_tiles
-  int grid() const { return dp_tiles + units() * split; }
+  int grid() const { return dp_tiles + (streamk ? sk_blocks : units() * split); }
   size_t partial_bytes() const {
+    if (streamk) return size_t(2) * sk_blocks * bm * bm * 4;           // two slots per stream-K block
     const size_t b = small ? 128 * 128 * 4 : size_t(bm) * bm * 4;
     return split > 1 ? size_t(units()) * split * b : 0;
   }
-  int counters() const { return split > 1 ? units() : 0; }
+  int counters() const { return streamk ? sk_tiles : (split > 1 ? units() : 0); }
 };
 GemmPlan plan_int8_gemm(int64_t M, int64_t N, int64_t K, int cus);
 GemmPlan plan_int8_gemm_forced(int64_t M, int64_t N, int cus, bool small, int split);
+// Stream-K over the last round of whole tiles and the leftover ones (all
+// tiles when there are fewer than two rounds): `cus` blocks share their K
+// steps evenly. K % 64 == 0.
+GemmPlan plan_int8_gemm_streamk(int64_t M, int64_t N, int cus);
 
 // The front of every workspace (abi.hip): kCntCap split-K arrival counters
 // (zero between calls), then the int8 outlier-column flag words, one per
