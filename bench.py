@@ -406,6 +406,49 @@ def counter_workload(torch, w8, cases, steps: int, copy_mib: int) -> None:
     print(f"[bench] counter workload done: {steps} steps, 3 copies of {copy_mib} MiB", file=sys.stderr, flush=True)
 
 
+def vendor_reference(torch, steps: int) -> dict:
+    """The ROCm libraries behind torch on the same shapes, for context: plain
+    int8 x int8 -> int32 products (torch._int_mm) on the DiT 1024^2 linears and
+    FP8-E4M3 products with per-tensor scales and bf16 output (torch._scaled_mm)
+    on the text-encoder linears at 512 tokens and the DiT 1024^2 linears. They
+    compute less than the library's linears (no outlier decomposition, no row
+    scales, no activation quantisation). Medians of `steps` calls, each timed
+    with events on torch's stream; random operands (timing only)."""
+    out = {"int8_mm": {}, "fp8_scaled_mm": {}}
+    g = torch.Generator(device="cuda").manual_seed(7)
+
+    def med(fn):
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return _median(ts)
+
+    for M, K, N in [(4352, 4096, 12288), (4352, 4096, 16384), (4352, 16384, 4096)]:
+        a = torch.randint(-127, 128, (M, K), dtype=torch.int8, device="cuda", generator=g)
+        b = torch.randint(-127, 128, (N, K), dtype=torch.int8, device="cuda", generator=g)
+        us = med(lambda: torch._int_mm(a, b.t()))
+        out["int8_mm"][f"{M}x{K}x{N}"] = {"us": round(us, 2), "tops": round(2 * M * N * K / us / 1e6, 1)}
+        print(f"[bench] vendor int8 {M}x{K}x{N}: {out['int8_mm'][f'{M}x{K}x{N}']}", file=sys.stderr, flush=True)
+        del a, b
+    one = torch.ones((), device="cuda")
+    for M, K, N in [(512, 4096, 4096), (512, 4096, 1024), (512, 4096, 12288), (512, 12288, 4096),
+                    (4352, 4096, 12288), (4352, 4096, 16384)]:
+        x = torch.randn(M, K, device="cuda", generator=g).to(torch.float8_e4m3fn)
+        w = torch.randn(N, K, device="cuda", generator=g).to(torch.float8_e4m3fn)
+        us = med(lambda: torch._scaled_mm(x, w.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16))
+        out["fp8_scaled_mm"][f"{M}x{K}x{N}"] = {"us": round(us, 2), "tflops": round(2 * M * N * K / us / 1e6, 1)}
+        print(f"[bench] vendor fp8 {M}x{K}x{N}: {out['fp8_scaled_mm'][f'{M}x{K}x{N}']}", file=sys.stderr, flush=True)
+        del x, w
+    return out
+
+
 def _prepare(torch, w8, cases):
     """Inputs resident in HBM, weights quantized once (untimed)."""
     xs, wqs, sws, ys, wss = [], [], [], [], []
@@ -613,6 +656,9 @@ def main() -> int:
     ap.add_argument("--no-block", action="store_true", help="skip the DiT block driver timings")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the measured peaks and the DiT 2048^2 and tiny int8 shapes")
+    ap.add_argument("--vendor", action="store_true",
+                    help="only time the ROCm libraries behind torch (torch._int_mm, torch._scaled_mm) on the same "
+                         "shapes, for context; prints one JSON line")
     ap.add_argument("--counters", type=int, default=0, metavar="MIB",
                     help="counter-collection mode: a few int8 steps, then plain copies of MIB MiB; no JSON line")
     args = ap.parse_args()
@@ -631,6 +677,9 @@ def main() -> int:
     cases = synth.dit_1024_block()
     print(f"[bench] workload: {[c.name for c in cases]}", file=sys.stderr, flush=True)
 
+    if args.vendor:
+        print(json.dumps({"vendor_reference": vendor_reference(torch, max(5, args.steps // 2))}), flush=True)
+        return 0
     if args.counters:
         counter_workload(torch, w8, cases, args.steps, args.counters)
         return 0
