@@ -612,7 +612,9 @@ def tile_timeline(w8, c, call) -> dict:
 def measured_peaks(torch, w8) -> dict:
     """The chip's attainable rates, measured here: dense MFMA issue (int8,
     fp8, bf16) with every SIMD busy (the library's peak kernel, median of 5
-    launches) and a device-to-device copy of 2 GiB (median of 5)."""
+    launches), a device-to-device copy of 2 GiB (median of 5), and the rate at
+    which one block per CU streams operand rows into LDS (the library's
+    streaming kernel), per CU."""
     res = {}
     blocks = 4 * max(torch.cuda.get_device_properties(0).multi_processor_count, 1)
     for kind, iters in (("int8", 20000), ("fp8", 10000), ("bf16", 20000)):
@@ -640,6 +642,25 @@ def measured_peaks(torch, w8) -> dict:
         ts.append(e0.elapsed_time(e1) * 1e-3)
     res["copy_GBs"] = round(2 * n / _median(ts) / 1e9, 1)
     del src, dst
+    # the GEMMs' operand path: 256-row panels streamed into LDS by one block
+    # per CU, 64-byte (the GEMMs' K step) or 128-byte row segments, from
+    # panels that stay in L2 (4 MiB in all) or that do not (96 MiB)
+    cus = max(torch.cuda.get_device_properties(0).multi_processor_count, 1)
+    K = 4096
+    panel_buf = torch.ones(96 * 256 * K, dtype=torch.uint8, device="cuda")
+    for panels, where in ((4, "l2"), (96, "mall")):
+        for seg in (64, 128):
+            w8.debug_lds_stream(panel_buf, K, seg, cus, panels, 64)
+            ts = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                _, nbytes = w8.debug_lds_stream(panel_buf, K, seg, cus, panels, 2048)
+                e1.record()
+                e1.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e-3)
+            res[f"lds_stream_{where}_seg{seg}_GBs_per_cu"] = round(nbytes / _median(ts) / 1e9 / cus, 1)
+    del panel_buf
     print(f"[bench] measured peaks: {res}", file=sys.stderr, flush=True)
     return res
 

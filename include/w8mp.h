@@ -503,6 +503,17 @@ w8_status w8dbg_dit_block_layout(int64_t M, int64_t D, int64_t F, size_t* offset
  * (2 M N K per instruction); the caller times the launch. */
 w8_status w8dbg_mfma_peak(int kind, int blocks, int iters, unsigned* out, double* ops, void* stream);
 
+/* The GEMMs' operand load path measured alone: `blocks` blocks (one per
+ * compute unit at a time) each stream 256 rows of a panel (row pitch K bytes,
+ * block b reading panel b % panels of buf, which holds at least
+ * panels * 256 * K bytes) into LDS with buffer loads, one K step of `seg` (64
+ * or 128) bytes of all 256 rows per iteration, `iters` iterations, walking the
+ * panel's K steps round robin. *bytes receives the bytes moved; out[blocks]
+ * receives a checksum. Invalid sizes (seg not 64/128, K not a multiple of
+ * seg, 256 K >= 2^31, buf too small) are W8_ERR_INVALID_ARGUMENT. */
+w8_status w8dbg_lds_stream(const void* buf, size_t buf_bytes, int K, int seg, int blocks, int panels, int iters,
+                           unsigned* out, double* bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

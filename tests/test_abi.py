@@ -395,3 +395,16 @@ def test_gemm_timeline_query_and_rejects():
     assert g[2] == 0
     assert lib.w8dbg_int8_gemm_timeline(A, bf, M, K, A, A, N, 6.0, A, f16, A, ws, None, 0, None,
                                         None) == _abi.W8_ERR_INVALID_ARGUMENT
+
+
+def test_lds_stream_rejects():
+    lib = _abi.lib()
+    f = lib.w8dbg_lds_stream
+    d = ctypes.c_double()
+    big = 256 * 4096 * 4
+    assert f(A, big, 4096, 96, 256, 4, 10, A, ctypes.byref(d), None) == _abi.W8_ERR_INVALID_ARGUMENT    # seg
+    assert f(A, big, 4100, 64, 256, 4, 10, A, ctypes.byref(d), None) == _abi.W8_ERR_INVALID_ARGUMENT    # K % seg
+    assert f(A, big - 1, 4096, 64, 256, 4, 10, A, ctypes.byref(d), None) == _abi.W8_ERR_INVALID_ARGUMENT  # buf
+    assert f(None, big, 4096, 64, 256, 4, 10, A, ctypes.byref(d), None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert f(A, 1 << 40, 1 << 23, 64, 256, 1, 10, A, ctypes.byref(d), None) == _abi.W8_ERR_INVALID_ARGUMENT  # 256 K
+    assert f(A, big, 4096, 64, 0, 4, 10, A, ctypes.byref(d), None) == _abi.W8_ERR_INVALID_ARGUMENT

@@ -474,6 +474,20 @@ def debug_mfma_peak(kind: str, blocks: int, iters: int, device="cuda"):
     return out, ops.value
 
 
+def debug_lds_stream(buf: torch.Tensor, K: int, seg: int, blocks: int, panels: int, iters: int):
+    """Launch the operand-streaming kernel (w8dbg_lds_stream in include/w8mp.h)
+    over the device buffer `buf` on the current stream; returns (checksum
+    tensor, bytes moved). The caller times it."""
+    import ctypes
+
+    out = torch.empty(blocks, dtype=torch.int32, device=buf.device)
+    nbytes = ctypes.c_double()
+    _abi.check(lib().w8dbg_lds_stream(buf.data_ptr(), buf.numel() * buf.element_size(), int(K), int(seg),
+                                      int(blocks), int(panels), int(iters), out.data_ptr(), ctypes.byref(nbytes),
+                                      torch.cuda.current_stream(buf.device).cuda_stream))
+    return out, nbytes.value
+
+
 def debug_fp8_quantize_activations(x: torch.Tensor, act_scale: torch.Tensor | None = None):
     """(E4M3 codes uint8 [M,K], sx fp32 [M])."""
     _dev(x, "x")

@@ -74,6 +74,7 @@ SIGNATURES = {
     "w8dbg_int8_workspace_layout": (_int, [_i64, _i64, _i64, ctypes.POINTER(_size)]),
     "w8dbg_dit_block_layout": (_int, [_i64, _i64, _i64, ctypes.POINTER(_size)]),
     "w8dbg_mfma_peak": (_int, [_int, _int, _int, _p, ctypes.POINTER(ctypes.c_double), _p]),
+    "w8dbg_lds_stream": (_int, [_p, _size, _int, _int, _int, _int, _int, _p, ctypes.POINTER(ctypes.c_double), _p]),
 }
 
 

@@ -79,6 +79,42 @@ __global__ __launch_bounds__(256) void k_mfma_peak(int iters, int seed, unsigned
   out[blockIdx.x * blockDim.x + threadIdx.x] = sum;
 }
 
+// Operand streaming into LDS, the GEMMs' load path: every block owns a panel
+// of 256 rows with row pitch K bytes (block b takes panel b % panels) and
+// moves one K step of SEG bytes of all 256 rows per iteration into a 4-slot
+// LDS ring with buffer loads (1 KB per wave instruction: 1024 / SEG rows of
+// SEG bytes), keeping 12 KB per wave in flight, walking the panel's K
+// steps round robin. With panels small enough to stay in L2 this is the L2 ->
+// LDS rate; SEG 64 is the GEMMs' 64-byte K step (half a 128-byte line per
+// row), SEG 128 whole lines.
+template <int SEG>
+__global__ __launch_bounds__(256, 1) void k_lds_stream(const int8_t* __restrict__ buf, int K, int panels, int iters,
+                                                      unsigned* __restrict__ out) {
+  __shared__ __attribute__((aligned(1024))) int8_t lds[4 * 32768];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  constexpr int kLpr = SEG / 16;               // lanes per row
+  constexpr int kRpi = 64 / kLpr;              // rows per instruction
+  constexpr int kNi = 256 / kRpi / 4;          // instructions per wave per step
+  const int panel = blockIdx.x % panels;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(buf) + static_cast<int64_t>(panel) * 256 * K, 0, 256u * static_cast<uint32_t>(K), 0x00020000);
+  const int nk = K / SEG;
+  for (int it = 0; it < iters; ++it) {
+    int8_t* st = lds + (it & 3) * 32768;
+    const int k0 = (it % nk) * SEG;
+#pragma unroll
+    for (int i = 0; i < kNi; ++i) {
+      const int row = (wave * kNi + i) * kRpi + lane / kLpr;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, st + ((wave * kNi + i) * 1024) % 32768, 16,
+                                               static_cast<uint32_t>(row * K + (lane % kLpr) * 16), k0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70 | 12);   // vmcnt(12)
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0)
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = static_cast<unsigned>(lds[4 * lane]);
+}
+
 }  // namespace
 
 }  // namespace w8
@@ -96,6 +132,21 @@ w8_status w8dbg_mfma_peak(int kind, int blocks, int iters, unsigned* out, double
   else w8::k_mfma_peak<2><<<grid, block, 0, s>>>(iters, 1, out);
   const double per_inst = kind == 0 ? 2.0 * 32 * 32 * 32 : (kind == 1 ? 2.0 * 32 * 32 * 64 : 2.0 * 32 * 32 * 16);
   *ops = per_inst * 4.0 * iters * (static_cast<double>(blocks) * 4.0);   // 4 waves per block, 4 per round
+  return hipGetLastError() == hipSuccess ? W8_OK : W8_ERR_HIP;
+}
+
+// See include/w8mp.h.
+w8_status w8dbg_lds_stream(const void* buf, size_t buf_bytes, int K, int seg, int blocks, int panels, int iters,
+                           unsigned* out, double* bytes, void* stream) {
+  if (!buf || !out || !bytes || (seg != 64 && seg != 128) || K < seg || K % seg != 0 || blocks < 1 || panels < 1 ||
+      iters < 1 || static_cast<int64_t>(K) * 256 >= (int64_t{1} << 31) ||
+      buf_bytes < static_cast<size_t>(panels) * 256 * static_cast<size_t>(K))
+    return W8_ERR_INVALID_ARGUMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(blocks), block(256);
+  if (seg == 64) w8::k_lds_stream<64><<<grid, block, 0, s>>>(static_cast<const int8_t*>(buf), K, panels, iters, out);
+  else w8::k_lds_stream<128><<<grid, block, 0, s>>>(static_cast<const int8_t*>(buf), K, panels, iters, out);
+  *bytes = 256.0 * seg * iters * static_cast<double>(blocks);
   return hipGetLastError() == hipSuccess ? W8_OK : W8_ERR_HIP;
 }
 
