@@ -460,9 +460,9 @@ __device__ __forceinline__ void mfma_sub(const v4i (&f)[8], v16i (&acc)[4][4]) {
 // sched_barrier keeps the order: the loads are spread over the MFMA shadow
 // instead of stalling the wave's in-order issue in a burst. The next
 // fragments are read in the order the next sub-step consumes them (A0, then
-// B0..B3, then A1..A3). Without DMA (the sub-step before the barrier) the
-// reads go two per group into the first four groups, so they have landed by
-// the time the wave waits for them at the barrier.
+// B0..B3, then A1..A3), two per group in the first four groups, so they have
+// landed when the next sub-step starts: the compiler puts a wait for every
+// outstanding LDS read there, as it counts the LDS DMAs in flight among them.
 template <bool DMA>
 __device__ __forceinline__ void mma_phase(const v4i (&fm)[8], v16i (&acc)[4][4], const int8_t* sfr, int sub,
                                           int wm, int wn, int lane, v4i (&fl)[8], const DmaSrc& src, int k0,
@@ -483,7 +483,10 @@ __device__ __forceinline__ void mma_phase(const v4i (&fm)[8], v16i (&acc)[4][4],
     acc[p1 >> 2][p1 & 3] =
         __builtin_amdgcn_mfma_i32_32x32x32_i8(fm[4 + (p1 & 3)], fm[p1 >> 2], acc[p1 >> 2][p1 & 3], 0, 0, 0);
     if (DMA) {
-      read(kOrder[t]);
+      if (t < 4) {
+        read(kOrder[2 * t]);
+        read(kOrder[2 * t + 1]);
+      }
       if (t < 4)
         dma_a(src, st + (wave * 4 + t) * 1024, t, k0);
       else
@@ -673,6 +676,184 @@ __device__ __forceinline__ void small_block(int8_t* lds, const int8_t* __restric
                               reinterpret_cast<char*>(lds) + S * 2 * kBM * kBK, Y);
 }
 
+// ---------------------------------------------------------------------------
+// Whole 256x256 tiles on 128-byte K steps (K % 128 == 0). Each row segment a
+// step moves is a whole 128-byte line, which the L2 -> LDS path streams about
+// 25% faster than the 64-byte half lines of the 64-byte step (measured with
+// w8dbg_lds_stream), and a step is 64 MFMAs per wave between barriers. The
+// ring holds two 64 KB steps; the loads of step kt + 2 go out right after the
+// barrier that retires step kt's slot, in the phase that multiplies its last
+// 32-byte sub-step, so they have the three sub-steps of step kt + 1 to land.
+// LDS rows are 128 bytes; chunk c of row r sits at chunk c ^ ((r >> 1) & 7),
+// so 16 consecutive rows read at one chunk hit 16 distinct 16-byte bank groups.
+constexpr int kBK2 = 128;
+constexpr int kStage2 = 2 * kBM * kBK2;         // 64 KB: A rows, then B rows
+
+__device__ __forceinline__ int swz128(int row, int ch) { return row * kBK2 + ((ch ^ ((row >> 1) & 7)) << 4); }
+
+// Fragments of 32-byte sub-step `sub` (0..3) of the step in slot `sa`.
+__device__ __forceinline__ void load_frags128(const int8_t* sa, int sub, int wm, int wn, int lane, v4i (&f)[8]) {
+  const int fr = lane & 31, fh = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f[i] = *reinterpret_cast<const v4i*>(sa + swz128(wm * 128 + i * 32 + fr, 2 * sub + fh));
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    f[4 + j] = *reinterpret_cast<const v4i*>(sa + kBM * kBK2 + swz128(wn * 128 + j * 32 + fr, 2 * sub + fh));
+}
+
+// The 128-byte step's loads: load i (0..7) of a wave covers tile rows
+// wave*64 + 8i + lane/8, 8 lanes (16 bytes each) per row; lane l's 16 bytes
+// land in physical chunk l & 7 of its row, which holds logical chunk
+// (l & 7) ^ ((row >> 1) & 7). For odd i that XOR term is 4 more than for
+// even i, so two per-lane offsets serve all 8 loads.
+struct Dma128 {
+  __amdgpu_buffer_rsrc_t a, b;   // the tile's rows of A and of B (zeros past M / N)
+  uint32_t voff[2];              // this lane's row and chunk offset for even / odd i
+  int rows8;                     // bytes between a wave's consecutive loads: 8 K
+};
+
+__device__ __forceinline__ Dma128 dma128_src(const int8_t* A, const int8_t* B, int m0, int n0, int M, int N, int K,
+                                             int wave, int lane) {
+  Dma128 d;
+  d.a = operand_rsrc(A, m0, M, K, 0, kBM);
+  d.b = operand_rsrc(B, n0, N, K, 0, kBN);
+  const int r = wave * 64 + (lane >> 3);
+  const int ch = (lane & 7) ^ ((r >> 1) & 7);
+  d.voff[0] = static_cast<uint32_t>(r) * static_cast<uint32_t>(K) + (ch << 4);
+  d.voff[1] = static_cast<uint32_t>(r) * static_cast<uint32_t>(K) + ((ch ^ 4) << 4);
+  d.rows8 = 8 * K;
+  return d;
+}
+
+// Load q (0..15) of a step: q < 8 are A's loads 0..7, q >= 8 B's.
+__device__ __forceinline__ void dma128(const Dma128& d, int8_t* st, int q, int k0, int wave) {
+  const int i = q & 7;
+  if (q < 8)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.a, st + (wave * 8 + i) * 1024, 16, d.voff[i & 1] + i * d.rows8, k0, 0,
+                                             0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.b, st + kBM * kBK2 + (wave * 8 + i) * 1024, 16,
+                                             d.voff[i & 1] + i * d.rows8, k0, 0, 0);
+}
+
+// One 32-byte sub-step: 16 MFMAs on fm, interleaved with the 8 fragment reads
+// of the next sub-step (READ, two per MFMA pair in the first half, so they
+// have landed when the next sub-step starts: the compiler waits for every LDS
+// read there, because it counts the LDS DMAs in flight as LDS operations too)
+// and the 16 loads of a future step (LOAD), order pinned with sched_barrier.
+template <bool READ, bool LOAD>
+__device__ __forceinline__ void phase128(const v4i (&fm)[8], v16i (&acc)[4][4], const int8_t* sn, int sub, int wm,
+                                         int wn, int lane, v4i (&fl)[8], const Dma128& d, int k0, int8_t* st,
+                                         int wave) {
+  const int fr = lane & 31, fh = lane >> 5;
+  constexpr int kOrder[8] = {0, 4, 5, 6, 7, 1, 2, 3};   // next fragments in the order they are consumed
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int p0 = 2 * t, p1 = 2 * t + 1;
+    acc[p0 >> 2][p0 & 3] =
+        __builtin_amdgcn_mfma_i32_32x32x32_i8(fm[4 + (p0 & 3)], fm[p0 >> 2], acc[p0 >> 2][p0 & 3], 0, 0, 0);
+    if (LOAD) dma128(d, st, 2 * t, k0, wave);
+    acc[p1 >> 2][p1 & 3] =
+        __builtin_amdgcn_mfma_i32_32x32x32_i8(fm[4 + (p1 & 3)], fm[p1 >> 2], acc[p1 >> 2][p1 & 3], 0, 0, 0);
+    if (LOAD) dma128(d, st, 2 * t + 1, k0, wave);
+    if (READ && t < 4) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int f = kOrder[2 * t + u];
+        if (f < 4)
+          fl[f] = *reinterpret_cast<const v4i*>(sn + swz128(wm * 128 + f * 32 + fr, 2 * sub + fh));
+        else
+          fl[f] = *reinterpret_cast<const v4i*>(sn + kBM * kBK2 + swz128(wn * 128 + (f - 4) * 32 + fr, 2 * sub + fh));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// A whole-tile block of the 128-byte-step kernel: ring fill, K loop, epilogue.
+template <int MODE, bool XBF16>
+__device__ __forceinline__ void tile128(int8_t* lds, const int8_t* __restrict__ A, const int8_t* __restrict__ B, int M,
+                                        int N, int K, const float* __restrict__ sx, const float* __restrict__ sw,
+                                        const int* __restrict__ nO_ptr, const uint16_t* __restrict__ XO,
+                                        const uint16_t* __restrict__ WO, const float* __restrict__ bias,
+                                        void* __restrict__ Y, int tiles_m, int tiles_n, int dp_tiles,
+                                        const SideSrc& src, long long* __restrict__ tl) {
+  auto stamp = [&](int p, long long v) {
+    if (tl != nullptr && threadIdx.x == 0) tl[static_cast<int64_t>(blockIdx.x) * 8 + p] = v;
+  };
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  tile_coords(blockIdx.x, dp_tiles, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * kBM, n0 = tn * kBN;
+  EpiIn ein;
+  epi_prefetch<MODE>(ein, M, N, m0, n0, wm, lane, sx, sw, bias, nO_ptr);
+  const Dma128 d = dma128_src(A, B, m0, n0, M, N, K, wave, lane);
+  const int nk = K / kBK2;
+  stamp(0, wall_clock64());
+
+  v16i acc[4][4];
+  zero_acc(acc);
+  // steps 0 and 1 (step 0 again when there is only one)
+#pragma unroll
+  for (int q = 0; q < 16; ++q) dma128(d, lds, q, 0, wave);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) dma128(d, lds + kStage2, q, min(1, nk - 1) * kBK2, wave);
+  const bool side = MODE != 0 && XO != nullptr && WO != nullptr;
+  if (side) {
+    int8_t* sl = lds + 2 * kStage2;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int r = (wave * 4 + t) * 16 + (lane >> 2);
+      const int ch = (lane & 3) ^ ((r >> 2) & 3);
+      __builtin_amdgcn_global_load_lds(XO + static_cast<int64_t>(min(m0 + r, M - 1)) * 32 + ch * 8,
+                                       sl + (wave * 4 + t) * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(WO + static_cast<int64_t>(min(n0 + r, N - 1)) * 32 + ch * 8,
+                                       sl + kSideRows * 64 + (wave * 4 + t) * 1024, 16, 0, 0);
+    }
+  }
+  // step 0 landed (this wave); step 1's loads and the side loads are behind it
+  if (side) wait_vmcnt<16 + 8>();
+  else wait_vmcnt<16>();
+  block_barrier();                                // ... for every wave
+  stamp(1, wall_clock64());
+  stamp(4, clock64());
+  v4i f0[8], f1[8];
+  load_frags128(lds, 0, wm, wn, lane, f0);
+  for (int kt = 0; kt < nk - 1; ++kt) {
+    int8_t* sa = lds + (kt & 1) * kStage2;
+    phase128<true, false>(f0, acc, sa, 1, wm, wn, lane, f1, d, 0, nullptr, wave);
+    phase128<true, false>(f1, acc, sa, 2, wm, wn, lane, f0, d, 0, nullptr, wave);
+    phase128<true, false>(f0, acc, sa, 3, wm, wn, lane, f1, d, 0, nullptr, wave);
+    wait_lgkmcnt<0>();                            // this slot is fully read
+    wait_vmcnt<0>();                              // step kt+1 landed (this wave)
+    block_barrier();                              // ... for every wave; slot kt retired
+    // the last sub-step multiplies while step kt+1's first fragments are read
+    // and step kt+2 (or a repeat of the last step) is fetched into the
+    // retired slot
+    phase128<true, true>(f1, acc, lds + ((kt + 1) & 1) * kStage2, 0, wm, wn, lane, f0, d,
+                         min(kt + 2, nk - 1) * kBK2, sa, wave);
+  }
+  {
+    const int8_t* sa = lds + ((nk - 1) & 1) * kStage2;
+    load_frags128(sa, 1, wm, wn, lane, f1);
+    mfma_sub(f0, acc);
+    load_frags128(sa, 2, wm, wn, lane, f0);
+    mfma_sub(f1, acc);
+    load_frags128(sa, 3, wm, wn, lane, f1);
+    mfma_sub(f0, acc);
+    mfma_sub(f1, acc);
+  }
+  wait_vmcnt<0>();                                // retire the trailing repeat loads
+  block_barrier();                                // every wave is done with the ring
+  stamp(2, wall_clock64());
+  stamp(5, clock64());
+  finish_tile<MODE, XBF16>(acc, ein, reinterpret_cast<char*>(lds), M, N, m0, n0, wm, wn, lane, XO, WO, src,
+                           side ? reinterpret_cast<const char*>(lds) + 2 * kStage2 : nullptr,
+                           reinterpret_cast<char*>(lds) + 2 * kStage2, Y);
+  stamp(3, wall_clock64());
+}
+
 // Work split for the last, partial wave of tiles (split-K). The first
 // dp_tiles blocks each own a whole 256x256 tile. The remaining blocks are
 // `split` K-slices of each of the R = (gridDim.x - dp_tiles) / split leftover
@@ -682,7 +863,7 @@ __device__ __forceinline__ void small_block(int8_t* lds, const int8_t* __restric
 // own and runs the epilogue. Integer sums are exact in any order, so the result does not
 // depend on which slice arrives last. No block ever waits for another.
 
-template <int MODE, bool XBF16, int S>
+template <int MODE, bool XBF16, int S, bool K128>
 __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restrict__ A, const int8_t* __restrict__ B,
                                                           int M, int N, int K, const float* __restrict__ sx,
                                                           const float* __restrict__ sw, const int* __restrict__ nO_ptr,
@@ -721,6 +902,12 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
     small_block<MODE, XBF16, S>(lds, A, B, M, N, K, sx, sw, nO_ptr, XO, WO, bias, Y, tiles_m, tiles_n, dp_tiles,
                                 split, part, cnt, src);
     stamp(3, wall_clock64());
+    return;
+  }
+  if constexpr (K128) {
+    // every other block owns a whole tile (the launcher's condition)
+    static_assert(S * kStage == 2 * kStage2, "the 128-byte steps use the same ring");
+    tile128<MODE, XBF16>(lds, A, B, M, N, K, sx, sw, nO_ptr, XO, WO, bias, Y, tiles_m, tiles_n, dp_tiles, src, tl);
     return;
   }
   const int nk_all = K / kBK;
@@ -1045,13 +1232,23 @@ void launch_int8_gemm(const int8_t* A, const int8_t* B, int64_t M, int64_t N, in
   if (K % kBK == 0) {
     constexpr int S = 4;
     const dim3 grid(plan.grid());
+    // 128-byte K steps when K allows and every block past the small tail owns a whole tile
+    const bool k128 = K % kBK2 == 0 && !plan.streamk && (plan.small || plan.split == 1);
 #define W8_GEMM_ARGS A, B, m, n, k, sx, sw, nO, XO, WO, bias, Y, tiles_m, tiles_n, plan.dp_tiles, plan.split, \
     plan.streamk ? 2 : (plan.small ? 1 : 0), part, cnt, src, timeline
-    if (mode == 0) k_int8_gemm_dma<0, true, S><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
-    else if (mode == 1 && xbf16) k_int8_gemm_dma<1, true, S><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
-    else if (mode == 1) k_int8_gemm_dma<1, false, S><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
-    else if (xbf16) k_int8_gemm_dma<2, true, S><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
-    else k_int8_gemm_dma<2, false, S><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
+    if (k128) {
+      if (mode == 0) k_int8_gemm_dma<0, true, S, true><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
+      else if (mode == 1 && xbf16) k_int8_gemm_dma<1, true, S, true><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
+      else if (mode == 1) k_int8_gemm_dma<1, false, S, true><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
+      else if (xbf16) k_int8_gemm_dma<2, true, S, true><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
+      else k_int8_gemm_dma<2, false, S, true><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
+    } else {
+      if (mode == 0) k_int8_gemm_dma<0, true, S, false><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
+      else if (mode == 1 && xbf16) k_int8_gemm_dma<1, true, S, false><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
+      else if (mode == 1) k_int8_gemm_dma<1, false, S, false><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
+      else if (xbf16) k_int8_gemm_dma<2, true, S, false><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
+      else k_int8_gemm_dma<2, false, S, false><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
+    }
 #undef W8_GEMM_ARGS
   } else {
     const dim3 grid(tiles_m * tiles_n);
