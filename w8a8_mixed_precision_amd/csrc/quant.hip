@@ -125,19 +125,16 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // from them in registers (produce.h) before anything else; RMSNorm first
 // reduces the row's sum of squares and stores the row's rstd for the fix-up.
 // flags: one word per column; a column with some |x| > t gets `stamp`.
-template <bool BF16, int W, int NW, bool ACT, int PROD>
-__device__ __forceinline__ void rows_iter(const uint16_t* __restrict__ X, int64_t rows, int K, uint32_t tbits,
-                                          int8_t* __restrict__ q, float* __restrict__ sx,
-                                          uint32_t* __restrict__ flags, uint32_t stamp, const ProdArgs& pa,
-                                          int64_t row0, uint32_t* red, double* red64, const uint16_t* gelu) {
+// This wave's share of row group row0 (row row0 + wave / W, part wave % W):
+// up to 8 chunks of 8 values per lane.
+template <int W>
+__device__ __forceinline__ void rows_load(const uint16_t* __restrict__ X, int64_t rows, int K, int64_t row0,
+                                          uint4 (&v)[8]) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t row = row0 + wave / W;
-  const bool valid = row < rows;
   const int part = wave % W;
   const int nch = K >> 3;
-  const uint32_t t2 = tbits | (tbits << 16);
-  uint4 v[8];
-  if (valid) {
+  if (row < rows) {
     const uint4* xr = reinterpret_cast<const uint4*>(X + row * K);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -145,6 +142,20 @@ __device__ __forceinline__ void rows_iter(const uint16_t* __restrict__ X, int64_
       if (c < nch) v[i] = xr[c];
     }
   }
+}
+
+// The row pass over one row group whose chunks rows_load put in v.
+template <bool BF16, int W, int NW, bool ACT, int PROD>
+__device__ __forceinline__ void rows_process(uint4 (&v)[8], int64_t rows, int K, uint32_t tbits,
+                                             int8_t* __restrict__ q, float* __restrict__ sx,
+                                             uint32_t* __restrict__ flags, uint32_t stamp, const ProdArgs& pa,
+                                             int64_t row0, uint32_t* red, double* red64, const uint16_t* gelu) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t row = row0 + wave / W;
+  const bool valid = row < rows;
+  const int part = wave % W;
+  const int nch = K >> 3;
+  const uint32_t t2 = tbits | (tbits << 16);
   if constexpr (PROD != kProdNone) {
     float rstd = 0.0f;
     if constexpr (PROD == kProdRms) {
@@ -211,13 +222,17 @@ __global__ __launch_bounds__(256) void k_int8_rows(const uint16_t* __restrict__ 
                                                    uint32_t* __restrict__ flags, uint32_t stamp, ProdArgs pa) {
   __shared__ uint32_t red[4];
   __shared__ double red64[4];
-  rows_iter<BF16, W, 4, ACT, PROD>(X, rows, K, tbits, q, sx, flags, stamp, pa,
-                                   static_cast<int64_t>(blockIdx.x) * (4 / W), red, red64, nullptr);
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * (4 / W);
+  uint4 v[8];
+  rows_load<W>(X, rows, K, row0, v);
+  rows_process<BF16, W, 4, ACT, PROD>(v, rows, K, tbits, q, sx, flags, stamp, pa, row0, red, red64, nullptr);
 }
 
 // The GELU-fused row pass: X = gelu(H) from the format's table, copied once
 // into LDS by each block (128 KB, so one block of 8 waves per CU); the blocks
-// then walk the row groups grid-stride.
+// then walk the row groups grid-stride, each wave loading its share of the
+// next group before it works on the current one, so two groups' loads are in
+// flight per CU (one group alone leaves the pass latency-bound).
 constexpr int kGeluWaves = 8;
 
 template <bool BF16, int W>
@@ -228,14 +243,21 @@ __global__ __launch_bounds__(64 * kGeluWaves) void k_int8_rows_gelu(const uint16
   __shared__ __attribute__((aligned(16))) uint16_t gtab[65536];
   __shared__ uint32_t red[kGeluWaves];
   __shared__ double red64[kGeluWaves];
+  constexpr int kRows = kGeluWaves / W;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kRows;
+  const ProdArgs none{nullptr, nullptr, nullptr, 0.0f, nullptr};
+  uint4 v[8], vn[8];
+  int64_t row0 = static_cast<int64_t>(blockIdx.x) * kRows;
+  rows_load<W>(X, rows, K, row0, v);              // in flight while the table is copied
   gelu_table_to_lds<BF16>(gtab);
   __syncthreads();
-  constexpr int kRows = kGeluWaves / W;
-  const ProdArgs none{nullptr, nullptr, nullptr, 0.0f, nullptr};
-  for (int64_t row0 = static_cast<int64_t>(blockIdx.x) * kRows; row0 < rows;
-       row0 += static_cast<int64_t>(gridDim.x) * kRows)
-    rows_iter<BF16, W, kGeluWaves, true, kProdGelu>(X, rows, K, tbits, q, sx, flags, stamp, none, row0, red, red64,
-                                                    gtab);
+  for (; row0 < rows; row0 += stride) {
+    rows_load<W>(X, rows, K, row0 + stride, vn);  // the next group (nothing past the last row)
+    rows_process<BF16, W, kGeluWaves, true, kProdGelu>(v, rows, K, tbits, q, sx, flags, stamp, none, row0, red, red64,
+                                                       gtab);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = vn[i];
+  }
 }
 
 // Row pass, streaming form for K > 16384: one block per row, two passes.
