@@ -424,16 +424,28 @@ __global__ __launch_bounds__(256) void k_outlier_fixup(
           const bool live = idx < total && j < nO;
           v[u] = X[live ? static_cast<int64_t>(r0 + r) * K + sO[j] : 0];
         }
+        // the producer's values first, then the stores: with GELU every value
+        // is a table load, and stores in between would hold each load back
+        // until the stores before it (the compiler cannot tell the table from
+        // the outputs)
+        uint16_t pv[kGatherUnroll];
+#pragma unroll
+        for (int u = 0; u < kGatherUnroll; ++u) {
+          const int idx = base + tid + 256 * u;
+          const int r = idx / P, j = idx - r * P;
+          pv[u] = idx < total && j < nO
+                      ? static_cast<uint16_t>(
+                            produce1<BF16, PROD>(v[u], sO[j], PROD == kProdRms ? srstd[r] : 0.0f, pa, gelu))
+                      : uint16_t{0};
+        }
 #pragma unroll
         for (int u = 0; u < kGatherUnroll; ++u) {
           const int idx = base + tid + 256 * u;
           if (idx >= total) break;
           const int r = idx / P, j = idx - r * P;
           const int64_t m = r0 + r;
-          uint16_t val = 0;
+          const uint16_t val = pv[u];
           if (j < nO) {
-            val = static_cast<uint16_t>(
-                produce1<BF16, PROD>(v[u], sO[j], PROD == kProdRms ? srstd[r] : 0.0f, pa, gelu));
             q[m * K + sO[j]] = 0;
             const uint32_t mag = val & 0x7FFFu;
             if (mag <= tbits) atomicMax(&somax[r], mag);
@@ -505,13 +517,25 @@ __global__ __launch_bounds__(256) void k_outlier_fixup(
       };
       if constexpr (PROD != kProdNone) {
         // K <= 16384 with a producer: the row's X is made once and held in
-        // registers (8 chunks per thread) for both passes
+        // registers (8 chunks per thread) for both passes. All 8 chunks of H
+        // are loaded first, then all their producer values made (with GELU,
+        // 64 independent table loads): one memory latency for each step
+        // rather than two per chunk.
         uint4 xv[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int c = tid + 256 * i;
+          xv[i] = c < nch ? xr[c] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int c = tid + 256 * i;
+          if (c < nch) xv[i] = produce8<BF16, PROD>(xv[i], c, rr_std, pa, gelu);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int c = tid + 256 * i;
           if (c < nch) {
-            xv[i] = produce8<BF16, PROD>(xr[c], c, rr_std, pa, gelu);
             float f[8];
             unpack8<BF16>(xv[i], f);
             chunk_best(f, c);
