@@ -612,12 +612,14 @@ def tile_timeline(w8, c, call) -> dict:
 def measured_peaks(torch, w8) -> dict:
     """The chip's attainable rates, measured here: dense MFMA issue (int8,
     fp8, bf16) with every SIMD busy (the library's peak kernel, median of 5
-    launches), a device-to-device copy of 2 GiB (median of 5), and the rate at
-    which one block per CU streams operand rows into LDS (the library's
-    streaming kernel), per CU."""
+    launches), the same with operands that change every round (random bits, as
+    a GEMM's: the chip holds a lower clock), a device-to-device copy of 2 GiB
+    (median of 5), and the rate at which one block per CU streams operand rows
+    into LDS (the library's streaming kernel), per CU."""
     res = {}
     blocks = 4 * max(torch.cuda.get_device_properties(0).multi_processor_count, 1)
-    for kind, iters in (("int8", 20000), ("fp8", 10000), ("bf16", 20000)):
+    for kind, iters in (("int8", 20000), ("fp8", 10000), ("bf16", 20000), ("int8_random", 20000),
+                        ("fp8_random", 10000)):
         w8.debug_mfma_peak(kind, blocks, 100)
         ts = []
         for _ in range(5):
@@ -780,6 +782,8 @@ def main() -> int:
     if not args.no_extra:
         out["measured_peak"] = measured_peaks(torch, w8)
         out["roofline"]["frac_of_measured_peak"] = round(gemm_tops / out["measured_peak"]["int8_mfma_tops"], 4)
+        out["roofline"]["frac_of_measured_random_operand_peak"] = round(
+            gemm_tops / out["measured_peak"]["int8_random_mfma_tops"], 4)
         out["pct_of_measured_mfma_peak"] = round(100.0 * tops / out["measured_peak"]["int8_mfma_tops"], 2)
         out["other_int8_shapes"] = extra_shapes(torch, w8, max(5, args.steps // 2))
     if not args.no_fp8:

@@ -498,9 +498,12 @@ w8_status w8dbg_dit_block_layout(int64_t M, int64_t D, int64_t F, size_t* offset
 /* Measured MFMA peak (measurement export): `blocks` blocks of 4 waves each
  * issue `iters` rounds of 4 independent back-to-back MFMAs on register
  * operands -- kind 0: v_mfma_i32_32x32x32_i8, 1: v_mfma_scale_f32_32x32x64_f8f6f4
- * (E4M3), 2: v_mfma_f32_32x32x16_bf16 -- and store a checksum per thread in
- * out[blocks * 256] (device). *ops (host) receives the operations launched
- * (2 M N K per instruction); the caller times the launch. */
+ * (E4M3), 2: v_mfma_f32_32x32x16_bf16; 3 and 4: kinds 0 and 1 with operands
+ * that change every round (random bits, as a GEMM's; the matrix cores then
+ * draw more power and the chip holds a lower clock) -- and store a checksum
+ * per thread in out[blocks * 256] (device). *ops (host) receives the
+ * operations launched (2 M N K per instruction); the caller times the
+ * launch. */
 w8_status w8dbg_mfma_peak(int kind, int blocks, int iters, unsigned* out, double* ops, void* stream);
 
 /* The GEMMs' operand load path measured alone: `blocks` blocks (one per

@@ -408,3 +408,12 @@ def test_lds_stream_rejects():
     assert f(None, big, 4096, 64, 256, 4, 10, A, ctypes.byref(d), None) == _abi.W8_ERR_INVALID_ARGUMENT
     assert f(A, 1 << 40, 1 << 23, 64, 256, 1, 10, A, ctypes.byref(d), None) == _abi.W8_ERR_INVALID_ARGUMENT  # 256 K
     assert f(A, big, 4096, 64, 0, 4, 10, A, ctypes.byref(d), None) == _abi.W8_ERR_INVALID_ARGUMENT
+
+
+def test_mfma_peak_rejects():
+    lib = _abi.lib()
+    d = ctypes.c_double()
+    assert lib.w8dbg_mfma_peak(5, 4, 10, A, ctypes.byref(d), None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert lib.w8dbg_mfma_peak(-1, 4, 10, A, ctypes.byref(d), None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert lib.w8dbg_mfma_peak(3, 0, 10, A, ctypes.byref(d), None) == _abi.W8_ERR_INVALID_ARGUMENT
+    assert lib.w8dbg_mfma_peak(4, 4, 10, None, ctypes.byref(d), None) == _abi.W8_ERR_INVALID_ARGUMENT

@@ -461,12 +461,13 @@ def debug_int8_gemm_i32_workspace_size(M: int, N: int, K: int, tail: int = 0, sp
 
 
 def debug_mfma_peak(kind: str, blocks: int, iters: int, device="cuda"):
-    """Launch the measured-peak MFMA kernel ("int8", "fp8" or "bf16") on the
-    current stream; returns (checksum tensor, operations launched). The caller
-    times it."""
+    """Launch the measured-peak MFMA kernel ("int8", "fp8" or "bf16" on
+    constant operands; "int8_random", "fp8_random" on operands that change
+    every round) on the current stream; returns (checksum tensor, operations
+    launched). The caller times it."""
     import ctypes
 
-    k = {"int8": 0, "fp8": 1, "bf16": 2}[kind]
+    k = {"int8": 0, "fp8": 1, "bf16": 2, "int8_random": 3, "fp8_random": 4}[kind]
     out = torch.empty(blocks * 256, dtype=torch.int32, device=device)
     ops = ctypes.c_double()
     _abi.check(lib().w8dbg_mfma_peak(k, int(blocks), int(iters), out.data_ptr(), ctypes.byref(ops),

@@ -5,6 +5,10 @@
 // is optimised away. The rate this reaches with every SIMD busy is the
 // chip's attainable dense MFMA peak at the clock it holds under that load;
 // GEMM fractions can be read against it beside the published figure.
+// The matrix cores' power, and so the clock the chip holds, depends on the
+// operand bits: with RND the operands change every round (a linear
+// congruential step per register, hidden under the MFMAs), as a GEMM's
+// operands do, which gives the rate a GEMM on random data can approach.
 #include <hip/hip_runtime.h>
 
 #include "common.h"
@@ -19,7 +23,7 @@ typedef float v16f_ __attribute__((ext_vector_type(16)));
 
 // kind 0: v_mfma_i32_32x32x32_i8 (2*32*32*32 ops); 1: v_mfma_scale_f32_32x32x64_f8f6f4
 // with E4M3 operands (2*32*32*64 flops); 2: v_mfma_f32_32x32x16_bf16 (2*32*32*16).
-template <int KIND>
+template <int KIND, bool RND>
 __global__ __launch_bounds__(256) void k_mfma_peak(int iters, int seed, unsigned* __restrict__ out) {
   const int lane = threadIdx.x & 63;
   unsigned sum = 0;
@@ -30,9 +34,17 @@ __global__ __launch_bounds__(256) void k_mfma_peak(int iters, int seed, unsigned
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) c[j][r] = 0;
+    if (RND) {
+      a = v4i{a[0] * 2654435 + lane, a[1] * 40503 + 1, a[2] ^ (lane << 8), a[3] + lane * 977};
+      b = v4i{b[0] * 69069 + 7, b[1] ^ (lane << 16), b[2] * 3 + lane, b[3] * 1103515245};
+    }
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) c[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c[j], 0, 0, 0);
+      if (RND) {
+        a = a * 1664525 + 1013904223;
+        b = b * 22695477 + 1;
+      }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -46,10 +58,24 @@ __global__ __launch_bounds__(256) void k_mfma_peak(int iters, int seed, unsigned
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) c[j][r] = 0.0f;
+    // changing E4M3 operands keep every byte's exponent field at most 0111
+    // (no NaN, no overflow of the sums)
+    constexpr int kF8Mask = 0x3F3F3F3F;
+    if (RND) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        a[e] = (a[e] * (2654435 + 2 * e) + lane * 977) & kF8Mask;
+        b[e] = (b[e] * (40503 + 2 * e) + lane) & kF8Mask;
+      }
+    }
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         c[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c[j], 0, 0, 0, 127, 0, 127);
+      if (RND) {
+        a = (a * 1664525 + 1013904223) & kF8Mask;
+        b = (b * 22695477 + 1) & kF8Mask;
+      }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -123,13 +149,16 @@ extern "C" {
 
 // See include/w8mp.h.
 w8_status w8dbg_mfma_peak(int kind, int blocks, int iters, unsigned* out, double* ops, void* stream) {
-  if (!out || !ops || kind < 0 || kind > 2 || blocks < 1 || iters < 1)
+  if (!out || !ops || kind < 0 || kind > 4 || blocks < 1 || iters < 1)
     return W8_ERR_INVALID_ARGUMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(blocks), block(256);
-  if (kind == 0) w8::k_mfma_peak<0><<<grid, block, 0, s>>>(iters, 1, out);
-  else if (kind == 1) w8::k_mfma_peak<1><<<grid, block, 0, s>>>(iters, 1, out);
-  else w8::k_mfma_peak<2><<<grid, block, 0, s>>>(iters, 1, out);
+  if (kind == 0) w8::k_mfma_peak<0, false><<<grid, block, 0, s>>>(iters, 1, out);
+  else if (kind == 1) w8::k_mfma_peak<1, false><<<grid, block, 0, s>>>(iters, 1, out);
+  else if (kind == 2) w8::k_mfma_peak<2, false><<<grid, block, 0, s>>>(iters, 1, out);
+  else if (kind == 3) w8::k_mfma_peak<0, true><<<grid, block, 0, s>>>(iters, 1, out);
+  else w8::k_mfma_peak<1, true><<<grid, block, 0, s>>>(iters, 1, out);
+  kind = kind == 3 ? 0 : (kind == 4 ? 1 : kind);
   const double per_inst = kind == 0 ? 2.0 * 32 * 32 * 32 : (kind == 1 ? 2.0 * 32 * 32 * 64 : 2.0 * 32 * 32 * 16);
   *ops = per_inst * 4.0 * iters * (static_cast<double>(blocks) * 4.0);   // 4 waves per block, 4 per round
   return hipGetLastError() == hipSuccess ? W8_OK : W8_ERR_HIP;
