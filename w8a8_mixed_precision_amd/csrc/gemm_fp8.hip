@@ -261,7 +261,8 @@ __global__ __launch_bounds__(256, 4 / WT) void k_fp8_gemm_dma(const uint8_t* __r
                                                               const float* __restrict__ sx,
                                                               const float* __restrict__ sw, void* __restrict__ Y,
                                                               int tiles_m, int tiles_n, int dp_tiles, int split,
-                                                              float* __restrict__ part, int* __restrict__ cnt) {
+                                                              float* __restrict__ part, int* __restrict__ cnt,
+                                                              int quarters) {
   using T = Fp8Tile<WT>;
   constexpr int BM = T::BM;
   // One LDS object only (a second one would make the compiler put a full vmcnt
@@ -274,8 +275,19 @@ __global__ __launch_bounds__(256, 4 / WT) void k_fp8_gemm_dma(const uint8_t* __r
   const int nk_all = K / kBK;
   int tm, tn, kb = 0, ke = nk_all;
   int slot = -1, sk_tile = 0, piece = 0, R = 0;
-  if (static_cast<int>(blockIdx.x) < dp_tiles) {
+  int m0, n0;
+  if (quarters) {
+    // (128x128 blocks only) the quarters of the leftover 256x256 tiles of a
+    // 256x256 launch: tiles_m, tiles_n count 256x256 tiles, and the leftover
+    // tiles are those from dp_tiles on in the grouped order
+    const int v = xcd_remap(blockIdx.x, gridDim.x);
+    group_tile(dp_tiles + v / 4, tiles_m, tiles_n, tm, tn);
+    m0 = tm * 256 + ((v >> 1) & 1) * 128;
+    n0 = tn * 256 + (v & 1) * 128;
+    if (m0 >= M || n0 >= N) return;
+  } else if (static_cast<int>(blockIdx.x) < dp_tiles) {
     tile_coords(blockIdx.x, dp_tiles, tiles_m, tiles_n, tm, tn);
+    m0 = tm * BM, n0 = tn * BM;
   } else {
     // slice-major per XCD: the blocks of one XCD share a K range
     const int nu = gridDim.x - dp_tiles;
@@ -287,8 +299,8 @@ __global__ __launch_bounds__(256, 4 / WT) void k_fp8_gemm_dma(const uint8_t* __r
     group_tile(dp_tiles + sk_tile, tiles_m, tiles_n, tm, tn);
     kb = piece * nk_all / split;
     ke = (piece + 1) * nk_all / split;
+    m0 = tm * BM, n0 = tn * BM;
   }
-  const int m0 = tm * BM, n0 = tn * BM;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int fr = lane & 31, fh = lane >> 5;
@@ -484,7 +496,17 @@ GemmPlan plan_fp8_gemm(int64_t M, int64_t N, int64_t K, int cus) {
       if (!have || t < best_t) have = true, best_t = t, best_bm = bm, best_s = s;
     }
   }
-  return plan_fp8_gemm_split(M, N, best_s, best_bm);
+  GemmPlan p = plan_fp8_gemm_split(M, N, best_s, best_bm);
+  // Whole 256x256 tiles in full waves and a partial last wave of R tiles:
+  // that wave costs a full tile time on its CUs; as 4R 128x128 quarters (two
+  // per CU) it takes about the time of one quarter, a little over half.
+  const int T = p.tiles_m * p.tiles_n, R = T % cus;
+  if (best_bm == 256 && best_s == 1 && T >= cus && R > 0 && 4 * R <= 2 * cus) {
+    p.dp_tiles = T - R;
+    p.sk_tiles = R;
+    p.small = true;
+  }
+  return p;
 }
 
 // ydt: 0 bf16, 1 fp16, 2 fp32. `part` / `cnt`: plan.partial_bytes() of fp32
@@ -494,9 +516,28 @@ void launch_fp8_gemm(const uint8_t* A, const uint8_t* B, int64_t M, int64_t N, i
   const dim3 block(256);
   if (K % kBK == 0) {
     constexpr int S = 4;
+    if (plan.bm == 256 && plan.small) {
+      // whole 256x256 tiles, then the leftover tiles as 128x128 quarters (a
+      // second launch on the same stream, so it starts as the first ends)
+      const dim3 grid(plan.dp_tiles), qgrid(4 * plan.sk_tiles);
+#define W8_FP8_ARGS(Q) A, B, (int)M, (int)N, (int)K, sx, sw, Y, plan.tiles_m, plan.tiles_n, plan.dp_tiles, 1, part, \
+    cnt, Q
+      if (ydt == 0) {
+        k_fp8_gemm_dma<0, S, 4><<<grid, block, 0, s>>>(W8_FP8_ARGS(0));
+        k_fp8_gemm_dma<0, S, 2><<<qgrid, block, 0, s>>>(W8_FP8_ARGS(1));
+      } else if (ydt == 1) {
+        k_fp8_gemm_dma<1, S, 4><<<grid, block, 0, s>>>(W8_FP8_ARGS(0));
+        k_fp8_gemm_dma<1, S, 2><<<qgrid, block, 0, s>>>(W8_FP8_ARGS(1));
+      } else {
+        k_fp8_gemm_dma<2, S, 4><<<grid, block, 0, s>>>(W8_FP8_ARGS(0));
+        k_fp8_gemm_dma<2, S, 2><<<qgrid, block, 0, s>>>(W8_FP8_ARGS(1));
+      }
+#undef W8_FP8_ARGS
+      return;
+    }
     const dim3 grid(plan.dp_tiles + plan.sk_tiles * plan.split);
 #define W8_FP8_ARGS A, B, (int)M, (int)N, (int)K, sx, sw, Y, plan.tiles_m, plan.tiles_n, plan.dp_tiles, plan.split, \
-    part, cnt
+    part, cnt, 0
     if (plan.bm == 256) {
       if (ydt == 0) k_fp8_gemm_dma<0, S, 4><<<grid, block, 0, s>>>(W8_FP8_ARGS);
       else if (ydt == 1) k_fp8_gemm_dma<1, S, 4><<<grid, block, 0, s>>>(W8_FP8_ARGS);
