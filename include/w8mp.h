@@ -476,6 +476,21 @@ w8_status w8dbg_int8_mixed_linear_events(const void* H, int h_dt, int64_t M, int
                                          float threshold, void* Y, int y_dt, void* workspace, size_t workspace_bytes,
                                          void* const* events, void* stream);
 
+/* int8_mixed_linear_fused with the GEMM grid planned for `cus` compute units
+ * instead of the device's own (the parity tests' way to run other devices'
+ * grids): whole 256x256 tiles in rounds of `cus`, the leftover tiles of a
+ * partial round whole, as K-slices or as 128x128 quarters, as that plan
+ * chooses. Every output element is the same sequence of operations whichever
+ * block computes it, so results equal int8_mixed_linear_fused's bit for bit.
+ * Workspace: at least w8dbg_int8_mixed_linear_plan_workspace_size(M, N, K,
+ * cus) bytes (0 for an invalid shape or cus), zero-filled before its first
+ * use, as for int8_mixed_linear. cus must be in [1, 4096]. */
+size_t w8dbg_int8_mixed_linear_plan_workspace_size(int64_t M, int64_t N, int64_t K, int cus);
+w8_status w8dbg_int8_mixed_linear_plan(const void* H, int h_dt, int64_t M, int64_t K, const w8_producer* producer,
+                                       const int8_t* Wq, const float* sw, const float* bias, int64_t N,
+                                       float threshold, void* Y, int y_dt, void* workspace, size_t workspace_bytes,
+                                       int cus, void* stream);
+
 /* fp8_w8a8_linear recording events[0..3]: before the activation pass, after
  * it (events 1 and 2), after the GEMM. */
 w8_status w8dbg_fp8_w8a8_linear_events(const void* X, int x_dt, int64_t M, int64_t K, const uint8_t* Wq8,

@@ -232,6 +232,22 @@ def debug_int8_mixed_linear_events(x: torch.Tensor, wq: torch.Tensor, sw: torch.
     return out
 
 
+def debug_int8_mixed_linear_plan(x: torch.Tensor, wq: torch.Tensor, sw: torch.Tensor, threshold: float, cus: int,
+                                 out: torch.Tensor, bias: torch.Tensor | None = None,
+                                 producer: Producer | None = None) -> torch.Tensor:
+    """int8_mixed_linear_fused with the GEMM grid planned for `cus` compute
+    units (w8dbg_int8_mixed_linear_plan in include/w8mp.h); a fresh zeroed
+    workspace."""
+    M, K = x.shape
+    N = wq.shape[0]
+    ws = new_workspace(lib().w8dbg_int8_mixed_linear_plan_workspace_size(M, N, K, int(cus)), x.device)
+    _abi.check(lib().w8dbg_int8_mixed_linear_plan(
+        x.data_ptr(), _dt(x), M, K, _producer_arg(producer, K), wq.data_ptr(), sw.data_ptr(),
+        bias.data_ptr() if bias is not None else None, N, float(threshold), out.data_ptr(), _dt(out),
+        ws.data_ptr(), ws.numel(), int(cus), _stream(x)))
+    return out
+
+
 def debug_fp8_w8a8_linear_events(x: torch.Tensor, wq8: torch.Tensor, sw: torch.Tensor, act_scale, events,
                                  out: torch.Tensor, workspace: torch.Tensor) -> torch.Tensor:
     """fp8_w8a8_linear that records `events` (before the activation pass, after

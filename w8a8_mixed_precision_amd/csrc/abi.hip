@@ -327,7 +327,7 @@ static w8_status int8_linear_impl(const void* X, int x_dt, int64_t M, int64_t K,
                                   const int8_t* Wq, const float* sw, const float* bias, int64_t N, float threshold,
                                   void* Y, int y_dt, void* workspace, size_t workspace_bytes, void* stream,
                                   void* const* events, const char* what, size_t need = 0,
-                                  long long* timeline = nullptr) {
+                                  long long* timeline = nullptr, const w8::GemmPlan* forced = nullptr) {
   if (w8_status st = int8_common_checks(X, x_dt, M, K, threshold); st != W8_OK) return st;
   W8_REQUIRE(Wq && sw && Y, W8_ERR_INVALID_ARGUMENT, "null pointer argument");
   W8_REQUIRE(N >= 1 && N <= kMaxDim, W8_ERR_INVALID_ARGUMENT, "N must be in [1, 2^31)");
@@ -340,7 +340,7 @@ static w8_status int8_linear_impl(const void* X, int x_dt, int64_t M, int64_t K,
   const Int8Ws L = int8_layout(M, N, K);
   if (w8_status st = check_ws(workspace, workspace_bytes, need ? need : int8_ws_size(M, N, K)); st != W8_OK)
     return st;
-  const w8::GemmPlan plan = int8_plan(M, N, K, workspace_bytes - L.base);
+  const w8::GemmPlan plan = forced ? *forced : int8_plan(M, N, K, workspace_bytes - L.base);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = x_dt == W8_DT_BF16;
@@ -632,6 +632,25 @@ w8_status w8dbg_int8_gemm_timeline(const void* X, int x_dt, int64_t M, int64_t K
              "stamps holds %zu words; the launch needs 8 per block (%d blocks)", stamps_len, grid[0]);
   return int8_linear_impl(X, x_dt, M, K, nullptr, Wq, sw, nullptr, N, threshold, Y, y_dt, workspace, workspace_bytes,
                           stream, nullptr, "w8dbg_int8_gemm_timeline", 0, stamps);
+}
+
+size_t w8dbg_int8_mixed_linear_plan_workspace_size(int64_t M, int64_t N, int64_t K, int cus) {
+  if (M < 1 || N < 1 || K < 1 || cus < 1 || cus > 4096) return 0;
+  return int8_layout(M, N, K).base + plan_part(w8::plan_int8_gemm(M, N, K, cus));
+}
+
+w8_status w8dbg_int8_mixed_linear_plan(const void* H, int h_dt, int64_t M, int64_t K, const w8_producer* producer,
+                                       const int8_t* Wq, const float* sw, const float* bias, int64_t N,
+                                       float threshold, void* Y, int y_dt, void* workspace, size_t workspace_bytes,
+                                       int cus, void* stream) {
+  W8_REQUIRE(M >= 1 && N >= 1 && K >= 1, W8_ERR_INVALID_ARGUMENT, "M, N, K must be >= 1");
+  W8_REQUIRE(cus >= 1 && cus <= 4096, W8_ERR_INVALID_ARGUMENT, "cus must be in [1, 4096]");
+  const w8::GemmPlan plan = w8::plan_int8_gemm(M, N, K, cus);
+  W8_REQUIRE(plan.counters() <= kCntCap, W8_ERR_UNSUPPORTED, "too many split tiles (%d > %d)", plan.counters(),
+             kCntCap);
+  return int8_linear_impl(H, h_dt, M, K, producer, Wq, sw, bias, N, threshold, Y, y_dt, workspace, workspace_bytes,
+                          stream, nullptr, "w8dbg_int8_mixed_linear_plan",
+                          w8dbg_int8_mixed_linear_plan_workspace_size(M, N, K, cus), nullptr, &plan);
 }
 
 w8_status w8dbg_fp8_w8a8_linear_events(const void* X, int x_dt, int64_t M, int64_t K, const uint8_t* Wq8,

@@ -45,8 +45,15 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// x, a float32 value, rounded to fp16 (v_cvt_f16_f32, RNE). The empty asm
+// hides where x came from: otherwise instruction selection may fuse an FMA
+// producing x with this conversion into one mixed-precision FMA
+// (v_fma_mixlo_f16), which rounds the exact result once, to fp16, and so
+// differs from rounding x in about one result in 10^5, for some elements of
+// a kernel and not others.
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
-  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));  // v_cvt_f16_f32, RNE
+  __asm__("" : "+v"(x));
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
 }
 
 // ---- integer code of the symmetric absmax int8 scheme ----------------------
