@@ -403,8 +403,11 @@ w8_status w8dbg_fp8_quantize_activations(const void* X, int x_dt, int64_t M, int
  * sx[m] * sw[n] * sum_k xq[m,k] * Wq8[n,k] (E4M3 codes, fp32 accumulation).
  * split = 0: the output tiling and K-slicing fp8_w8a8_linear would choose
  * (tile ignored). split >= 1: output tiles of tile x tile (128 or 256; 0 means
- * 256), each with its K range cut into `split` slices; needs K % 64 == 0 and
- * split <= K / 64 (else W8_ERR_UNSUPPORTED) unless split is 1. Workspace:
+ * 256) on 64-byte K steps, or, with tile 129 / 192, 128 x 128 / 128 x 192
+ * tiles on 128-byte K steps, each with its K range cut into `split` slices;
+ * needs K % 64 == 0 and split <= K / 64 (tiles 129 and 192: K % 128 == 0 and
+ * split <= K / 128) else W8_ERR_UNSUPPORTED, unless split is 1 (tiles 128
+ * and 256). Workspace:
  * w8dbg_fp8_gemm_workspace_size(M, N, K, split, tile) bytes (0 means none,
  * then workspace may be NULL), zero-filled before first use (left zero). */
 size_t w8dbg_fp8_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int split, int tile);

@@ -174,14 +174,20 @@ GEMM_SHAPES = [(300, 4096, 520), (77, 2048, 300), (512, 1024, 256), (1, 640, 16)
 
 @pytest.mark.parametrize("shape", GEMM_SHAPES, ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("tile,split", [(0, 0), (256, 1), (256, 2), (256, 3), (256, 5), (256, 8),
-                                        (128, 1), (128, 2), (128, 3), (128, 8)])
+                                        (128, 1), (128, 2), (128, 3), (128, 8),
+                                        (129, 1), (129, 2), (129, 5), (192, 1), (192, 2), (192, 3), (192, 8)])
 @pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
 def test_fp8_gemm_tiling_and_k_slicing_match_oracle(shape, tile, split, out_dtype):
-    """The FP8 GEMM for both block sizes and several K-slicings against the
-    exact contraction; the sliced result is bitwise the same on a repeated call
-    (fixed summation order) and the bookkeeping counters are left zero."""
+    """The FP8 GEMM for every block shape (256x256, 128x128 on 64-byte K steps;
+    128x128 = tile 129 and 128x192 on 128-byte K steps) and several K-slicings
+    against the exact contraction; the sliced result is bitwise the same on a
+    repeated call (fixed summation order) and the bookkeeping counters are left
+    zero."""
     M, K, N = shape
-    if split > K // 64:
+    step = 128 if tile in (129, 192) else 64
+    if tile in (129, 192) and K % 128:
+        pytest.skip("128-byte K steps need K % 128 == 0")
+    if split > K // step:
         pytest.skip("more slices than K steps")
     rng = np.random.default_rng(7000 + M + K + N + split + tile)
     xq, wq = _random_codes(rng, (M, K)), _random_codes(rng, (N, K))

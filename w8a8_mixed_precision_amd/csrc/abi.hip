@@ -223,8 +223,9 @@ w8::GemmPlan fp8_plan(int64_t M, int64_t N, int64_t K, size_t avail) {
 // Grid of the FP8 GEMM parity export: the linear's own plan (split 0) or the
 // given block size and K-slicing.
 w8::GemmPlan fp8_debug_plan(int64_t M, int64_t N, int64_t K, int split, int tile, int cus) {
-  return split == 0 ? w8::plan_fp8_gemm(M, N, K, cus)
-                    : w8::plan_fp8_gemm_split(M, N, split, tile == 128 ? 128 : 256);
+  if (split == 0) return w8::plan_fp8_gemm(M, N, K, cus);
+  if (tile == 129 || tile == 192) return w8::plan_fp8_gemm_rect(M, N, split, tile == 192 ? 192 : 128);
+  return w8::plan_fp8_gemm_split(M, N, split, tile == 128 ? 128 : 256);
 }
 
 template <typename T>
@@ -775,8 +776,11 @@ w8_status w8dbg_fp8_gemm(const uint8_t* xq, const float* sx, const uint8_t* Wq8,
   if (w8_status st = check_mk(M, K, 65536); st != W8_OK) return st;
   W8_REQUIRE(N >= 1 && N <= kMaxDim, W8_ERR_INVALID_ARGUMENT, "N must be in [1, 2^31)");
   W8_REQUIRE(split >= 0, W8_ERR_INVALID_ARGUMENT, "split must be >= 0");
-  W8_REQUIRE(tile == 0 || tile == 128 || tile == 256, W8_ERR_INVALID_ARGUMENT, "tile must be 0, 128 or 256");
+  W8_REQUIRE(tile == 0 || tile == 128 || tile == 256 || tile == 129 || tile == 192, W8_ERR_INVALID_ARGUMENT,
+             "tile must be 0, 128, 129, 192 or 256");
   W8_REQUIRE(split == 0 || tile == 0 || K % 64 == 0, W8_ERR_UNSUPPORTED, "a tile size needs K %% 64 == 0");
+  W8_REQUIRE(split == 0 || (tile != 129 && tile != 192) || (K % 128 == 0 && split <= K / 128), W8_ERR_UNSUPPORTED,
+             "128-byte K steps need K %% 128 == 0 and at most K / 128 slices");
   W8_REQUIRE(split <= 1 || (K % 64 == 0 && split <= K / 64), W8_ERR_UNSUPPORTED,
              "split %d needs K %% 64 == 0 and at most K / 64 slices", split);
   W8_REQUIRE(aligned16(xq) && aligned16(sx) && aligned16(Wq8) && aligned16(sw) && aligned16(Y),

@@ -435,6 +435,319 @@ __global__ __launch_bounds__(256, 4 / WT) void k_fp8_gemm_dma(const uint8_t* __r
 }
 
 // ---------------------------------------------------------------------------
+// Rectangular blocks on 128-byte K steps (K % 128 == 0), for grids with few
+// tokens. A block is 128 rows x 64*TN columns (TN = 2: 128x128, TN = 3:
+// 128x192) of 2x2 waves, each wave 2 x TN MFMA tiles of 32x32. At 512 tokens a
+// 128x192 grid of the text encoder's gate and up projections is one block per
+// CU (4 x 64 blocks), where 128x128 blocks left half the CUs with two blocks
+// and streamed 20% more operand bytes; a GEMM step at this size is bound by
+// the rate at which a CU streams operand rows into LDS, and whole 128-byte
+// row segments stream faster than 64-byte halves. Ring: 4 stages of one K
+// step (A rows, then B rows, 128 bytes each, chunk c of row r at chunk
+// c ^ ((r >> 1) & 7)). Each step is two 64-byte sub-steps of one
+// v_mfma_scale_f32_32x32x64_f8f6f4 per MFMA tile, with the operand bytes of
+// the square kernel's 64-byte step (lane l: row l & 31, chunks l >> 5 and
+// 2 + (l >> 5) of the sub-step), so the products and their order are the
+// same. Split-K and the epilogue arithmetic are those of the square kernel.
+template <int TN>
+struct Fp8Rect {
+  static constexpr int BM = 128, BN = 64 * TN;
+  static constexpr int kStep = 128;                    // K bytes per step
+  static constexpr int kStage = (BM + BN) * kStep;     // 32 or 40 KB
+  static constexpr int kLoadsA = 4, kLoadsB = 2 * TN;  // DMA instructions per wave per step (rect_dma)
+  static constexpr int kLoads = kLoadsA + kLoadsB;
+  static constexpr int kMfma = 2 * TN;                 // MFMAs per wave per sub-step
+  static constexpr int kReads = 2 * (2 + TN);          // 16-byte fragment reads per wave per sub-step
+  static constexpr int kChunks = 8 * TN;               // 16-byte accumulator chunks per lane
+  static constexpr int kPartBytes = BM * BN * 4;       // one fp32 partial
+  static constexpr int kS = 4;                         // ring stages
+};
+
+__device__ __forceinline__ int rswz(int row, int ch) { return row * 128 + ((ch ^ ((row >> 1) & 7)) << 4); }
+
+// The block's operand rows for the DMA: A rows m0 .. m0+127 and B rows
+// n0 .. n0+64*TN-1 from byte k_off of each row (rows past M / N read as zeros,
+// the buffer range check). Load i of a wave covers 8 rows, 8 lanes (16 bytes
+// each) per row; lane l lands in physical chunk l & 7 of its row, which holds
+// logical chunk (l & 7) ^ ((row >> 1) & 7); the wave's rows start at a
+// multiple of 16, so that term depends on l and the parity of i only.
+struct RectSrc {
+  __amdgpu_buffer_rsrc_t a, b;
+  uint32_t va[2], vb[2];                         // per-lane offsets for even / odd i
+  int rows8;                                     // bytes between a wave's consecutive loads: 8 K
+};
+
+template <int TN>
+__device__ __forceinline__ RectSrc rect_src(const uint8_t* A, const uint8_t* B, int m0, int n0, int M, int N, int K,
+                                            int k_off, int wave, int lane) {
+  RectSrc d;
+  d.a = operand_rsrc(reinterpret_cast<const int8_t*>(A), m0, M, K, k_off, Fp8Rect<TN>::BM);
+  d.b = operand_rsrc(reinterpret_cast<const int8_t*>(B), n0, N, K, k_off, Fp8Rect<TN>::BN);
+  const uint32_t ra = static_cast<uint32_t>(wave * 32 + (lane >> 3));
+  const uint32_t rb = static_cast<uint32_t>(wave * 16 * TN + (lane >> 3));
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const uint32_t ch = static_cast<uint32_t>((lane & 7) ^ ((par * 4 + (lane >> 4)) & 7)) << 4;
+    d.va[par] = ra * static_cast<uint32_t>(K) + ch;
+    d.vb[par] = rb * static_cast<uint32_t>(K) + ch;
+  }
+  d.rows8 = 8 * K;
+  return d;
+}
+
+// Load q of K step k0 into stage st: q < 4 are A's loads, the others B's (lb
+// per wave). Not a template: a target builtin with template-dependent
+// arguments can make the host compilation pass drop the kernel templates.
+__device__ __forceinline__ void rect_dma(const RectSrc& d, uint8_t* st, int q, int k0, int wave, int lb) {
+  if (q < 4)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.a, st + (wave * 4 + q) * 1024, 16, d.va[q & 1] + q * d.rows8, k0, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.b, st + 128 * 128 + (wave * lb + q - 4) * 1024, 16,
+                                             d.vb[(q - 4) & 1] + (q - 4) * d.rows8, k0, 0, 0);
+}
+
+template <int TN>
+__device__ __forceinline__ void rect_issue(uint8_t* lds, int kt, int nk, const RectSrc& d, int wave) {
+  using T = Fp8Rect<TN>;
+  uint8_t* st = lds + (kt % T::kS) * T::kStage;
+  const int k0 = min(kt, nk - 1) * T::kStep;
+#pragma unroll
+  for (int q = 0; q < T::kLoads; ++q) rect_dma(d, st, q, k0, wave, T::kLoadsB);
+}
+
+// Row in the stage of fragment f (0, 1: A row blocks; 2..: B row blocks).
+template <int TN>
+__device__ __forceinline__ int rect_row(int f, int wm, int wn, int fr) {
+  return f < 2 ? wm * 64 + f * 32 + fr : Fp8Rect<TN>::BM + wn * 32 * TN + (f - 2) * 32 + fr;
+}
+
+// One 64-byte sub-step: the wave's 2 x TN MFMAs on fragments fc while the
+// fragments of sub-step `sub` of the stage sn are read into fn (in the order
+// the MFMAs consume them: A0, B0 .., A1) and, with DMA, the loads of a future
+// K step go to stage st; both spread evenly over the MFMAs, the interleaving
+// pinned by sched_barrier.
+template <int TN, bool DMA>
+__device__ __forceinline__ void rect_phase(const v8i* fc, v8i* fn, v16f (*acc)[TN], const uint8_t* sn, int sub,
+                                           int wm, int wn, int lane, const RectSrc& d, int k0, uint8_t* st,
+                                           int wave) {
+  using T = Fp8Rect<TN>;
+  const int fr = lane & 31, fh = lane >> 5;
+  constexpr int kDma = DMA ? T::kLoads : 0;
+  v4i lo;
+#pragma unroll
+  for (int t = 0; t < T::kMfma; ++t) {
+    const int i = t / TN, j = t % TN;
+    acc[i][j] = mfma_fp8(fc[2 + j], fc[i], acc[i][j]);
+#pragma unroll
+    for (int q = t * T::kReads / T::kMfma; q < (t + 1) * T::kReads / T::kMfma; ++q) {
+      const int o = q >> 1;                              // o-th fragment in consumption order
+      const int f = o == 0 ? 0 : (o <= TN ? 2 + o - 1 : 1);
+      const int row = rect_row<TN>(f, wm, wn, fr);
+      if ((q & 1) == 0) {
+        lo = *reinterpret_cast<const v4i*>(sn + rswz(row, 4 * sub + fh));
+      } else {
+        const v4i hi = *reinterpret_cast<const v4i*>(sn + rswz(row, 4 * sub + 2 + fh));
+        fn[f] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    }
+#pragma unroll
+    for (int q = t * kDma / T::kMfma; q < (t + 1) * kDma / T::kMfma; ++q) rect_dma(d, st, q, k0, wave, T::kLoadsB);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// YDT: 0 bf16, 1 fp16, 2 fp32. Grid as in the square kernel: blocks below
+// dp_tiles own whole tiles, the rest are `split` K-slices of the
+// (gridDim.x - dp_tiles) / split remaining tiles, numbered slice-major per XCD.
+template <int YDT, int TN>
+__global__ __launch_bounds__(256, 1) void k_fp8_gemm_rect(const uint8_t* __restrict__ A,
+                                                          const uint8_t* __restrict__ B, int M, int N, int K,
+                                                          const float* __restrict__ sx, const float* __restrict__ sw,
+                                                          void* __restrict__ Y, int tiles_m, int tiles_n,
+                                                          int dp_tiles, int split, float* __restrict__ part,
+                                                          int* __restrict__ cnt) {
+  using T = Fp8Rect<TN>;
+  constexpr int BM = T::BM, BN = T::BN, S = T::kS;
+  constexpr int EB = YDT == 2 ? 4 : 2;                 // bytes per output element
+  constexpr int RB = 32 * TN * EB;                     // bytes of one output row of the wave's tile
+  constexpr int kPitch = RB + 16;                      // staged row
+  constexpr int kEpi = 1024 + 4 * 32 * kPitch;         // column scales, then 4 staging areas
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[S * T::kStage];
+  static_assert(S * T::kStage >= kEpi + 4, "epilogue LDS and arrival flag");
+  int* const s_last = reinterpret_cast<int*>(lds + kEpi);
+
+  const int nk_all = K / T::kStep;
+  int tm, tn, kb = 0, ke = nk_all, slot = -1, sk_tile = 0, R = 0;
+  if (static_cast<int>(blockIdx.x) < dp_tiles) {
+    tile_coords(blockIdx.x, dp_tiles, tiles_m, tiles_n, tm, tn);
+  } else {
+    const int nu = gridDim.x - dp_tiles;
+    const int v = xcd_remap(blockIdx.x - dp_tiles, nu);
+    R = nu / split;
+    const int piece = v / R;
+    sk_tile = v % R;
+    slot = v;
+    group_tile(dp_tiles + sk_tile, tiles_m, tiles_n, tm, tn);
+    kb = piece * nk_all / split;
+    ke = (piece + 1) * nk_all / split;
+  }
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int fr = lane & 31, fh = lane >> 5;
+  // epilogue inputs, fetched now so their latency hides under the K loop
+  float rsx[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) rsx[i] = sx[min(m0 + wm * 64 + 32 * i + fr, M - 1)];
+  const float my_sw = sw[min(n0 + min(tid, BN - 1), N - 1)];
+
+  const RectSrc d = rect_src<TN>(A, B, m0, n0, M, N, K, kb * T::kStep, wave, lane);
+  const int nk = ke - kb;
+
+  v16f acc[2][TN];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  for (int s = 0; s < S; ++s) rect_issue<TN>(lds, s, nk, d, wave);
+  wait_vmcnt<(S - 1) * T::kLoads>();              // step 0 landed (this wave)
+  block_barrier();                                // ... for every wave
+  v8i fa[2 + TN], fb[2 + TN];
+#pragma unroll
+  for (int f = 0; f < 2 + TN; ++f) {
+    const int row = rect_row<TN>(f, wm, wn, fr);
+    const v4i lo = *reinterpret_cast<const v4i*>(lds + rswz(row, fh));
+    const v4i hi = *reinterpret_cast<const v4i*>(lds + rswz(row, 2 + fh));
+    fa[f] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  // K step kt: its first sub-step multiplies while its second's fragments are
+  // read; then (step kt+1 landed everywhere, slot kt read by every wave) the
+  // second multiplies while step kt+1's first fragments are read and step
+  // kt+S is fetched into slot kt. The last step runs the same code: its stray
+  // reads stay in the ring, its load repeats the last step into its own,
+  // retired slot.
+  for (int kt = 0; kt < nk; ++kt) {
+    uint8_t* sc = lds + (kt % S) * T::kStage;
+    rect_phase<TN, false>(fa, fb, acc, sc, 1, wm, wn, lane, d, 0, nullptr, wave);
+    wait_lgkmcnt<0>();
+    wait_vmcnt<(S - 2) * T::kLoads>();
+    block_barrier();
+    rect_phase<TN, true>(fb, fa, acc, lds + ((kt + 1) % S) * T::kStage, 0, wm, wn, lane, d,
+                         min(kt + S, nk - 1) * T::kStep, sc, wave);
+  }
+  wait_lgkmcnt<0>();
+  wait_vmcnt<0>();                                // retire the trailing repeat loads
+  block_barrier();                                // every wave is done with the ring
+
+  if (slot >= 0) {
+    // the square kernel's partial protocol: 16-byte chunk c of wave w's
+    // accumulators at byte ((w * kChunks + c) * 64 + lane) * 16
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int lane_off = (wv * T::kChunks * 64 + lane) * 16;
+    const __amdgpu_buffer_rsrc_t mine = partial_rsrc(part, slot, T::kPartBytes);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = (i * TN + j) * 4 + q;
+          const v4f v{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), mine, lane_off + c * 1024, 0, kSc1);
+        }
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's partial is visible
+    __syncthreads();                                        // ... and every wave's
+    if (tid == 0)
+      *s_last = __hip_atomic_fetch_add(cnt + sk_tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == split - 1;
+    __syncthreads();
+    if (!__builtin_amdgcn_readfirstlane(*s_last)) return;
+    if (tid == 0) cnt[sk_tile] = 0;               // every slice has arrived: leave the counter zero
+    // all slices' partials in slice order, this one's own included
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      for (int p = 0; p < split; ++p) {
+        const __amdgpu_buffer_rsrc_t src = partial_rsrc(part, p * R + sk_tile, T::kPartBytes);
+        v4f w[4 * TN];
+#pragma unroll
+        for (int t = 0; t < 4 * TN; ++t)
+          w[t] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                                             src, lane_off + (i * 4 * TN + t) * 1024, 0, kSc1));
+#pragma unroll
+        for (int t = 0; t < 4 * TN; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[i][t >> 2][4 * (t & 3) + e] = p == 0 ? w[t][e] : acc[i][t >> 2][4 * (t & 3) + e] + w[t][e];
+      }
+    }
+  }
+
+  // Epilogue: Y = acc * sx[m] * sw[n] rounded to the output type, staged one
+  // 32-row block at a time (element r of tile (i, j) of a lane is row
+  // m0 + wm*64 + 32i + (lane&31), column n0 + wn*32*TN + 32j + 8(r>>2) +
+  // 4(lane>>5) + (r&3)) and stored as 16-byte pieces of whole rows.
+  float* scol = reinterpret_cast<float*>(lds);
+  if (tid < BN) scol[tid] = my_sw;
+  __syncthreads();
+  constexpr int CPR = RB / 16;                    // 16-byte chunks per staged row
+  constexpr int EPC = 16 / EB;                    // elements per chunk
+  const bool vec = (static_cast<int64_t>(N) * EB) % 16 == 0;
+  char* const stg = reinterpret_cast<char*>(lds) + 1024 + wave * 32 * kPitch;
+  char* const y = static_cast<char*>(Y);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        char* dst = stg + fr * kPitch + (32 * j + 8 * g + 4 * fh) * EB;
+        const v4f cs = *reinterpret_cast<const v4f*>(scol + wn * 32 * TN + 32 * j + 8 * g + 4 * fh);
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] * rsx[i] * cs[e];
+        if constexpr (YDT == 0) {
+          *reinterpret_cast<uint2*>(dst) = make_uint2(bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16),
+                                                      bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16));
+        } else if constexpr (YDT == 1) {
+          const uint32_t lo = f32_to_f16_bits(v[0]) | (static_cast<uint32_t>(f32_to_f16_bits(v[1])) << 16);
+          const uint32_t hi = f32_to_f16_bits(v[2]) | (static_cast<uint32_t>(f32_to_f16_bits(v[3])) << 16);
+          *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+        } else {
+          *reinterpret_cast<v4f*>(dst) = v4f{v[0], v[1], v[2], v[3]};
+        }
+      }
+    wave_lds_fence();
+    const int mb = m0 + wm * 64 + 32 * i;
+    const int nb = n0 + wn * 32 * TN;
+#pragma unroll
+    for (int t = 0; t < 32 * CPR / 64; ++t) {
+      const int q = t * 64 + lane, row = q / CPR, c = q % CPR;
+      const uint4 val = *reinterpret_cast<const uint4*>(stg + row * kPitch + c * 16);
+      const int m = mb + row, n = nb + c * EPC;
+      if (m < M) {
+        char* dp = y + (static_cast<int64_t>(m) * N + n) * EB;
+        if (vec && n + EPC <= N) {
+          *reinterpret_cast<uint4*>(dp) = val;
+        } else {
+          const uint32_t w[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) {
+            if (n + e >= N) break;
+            if constexpr (EB == 2)
+              *reinterpret_cast<uint16_t*>(dp + 2 * e) = static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)));
+            else
+              *reinterpret_cast<uint32_t*>(dp + 4 * e) = w[e];
+          }
+        }
+      }
+    }
+    wave_lds_fence();                             // staging reads done before the next block writes
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launch plan: block size (256 or 128) and K-slicing, all tiles alike, chosen
 // by a bandwidth model of MI355X fitted to measured timings (microseconds):
 //  * a 256x256 block step (32 KB of operands, 1024 MFMA cycles) takes
@@ -444,8 +757,12 @@ __global__ __launch_bounds__(256, 4 / WT) void k_fp8_gemm_dma(const uint8_t* __r
 //  * all CUs together stream at most kL2Rate bytes/us from L2;
 //  * K-slicing writes every slice's fp32 partial and re-reads them all for the
 //    last slice (through memory, kPartRate bytes/us) after a latency kSplitLat;
-//  * kFixed per launch (start-up, epilogue).
+//  * kFixed per launch (start-up, epilogue);
+//  * with K % 128 == 0, 128 x 128 and 128 x 192 blocks on 128-byte K steps
+//    (one per CU, not sliced): whole 128-byte row segments stream at
+//    kCuRateRect per CU, under the same aggregate L2 rate.
 constexpr double kStep256 = 0.65;
+constexpr double kCuRateRect = 75e3;
 constexpr double kCuRate = 62e3;
 constexpr double kMfma128 = 0.13;
 constexpr double kL2Rate = 12e6;
@@ -484,6 +801,20 @@ GemmPlan plan_fp8_gemm_split(int64_t M, int64_t N, int split, int bm) {
   return p;
 }
 
+GemmPlan plan_fp8_gemm_rect(int64_t M, int64_t N, int split, int bn) {
+  GemmPlan p{};
+  p.bm = 128;
+  p.bn = bn;
+  p.rect = true;
+  p.tiles_m = static_cast<int>((M + 127) / 128);
+  p.tiles_n = static_cast<int>((N + bn - 1) / bn);
+  const int T = p.tiles_m * p.tiles_n;
+  p.split = split;
+  p.dp_tiles = split > 1 ? 0 : T;
+  p.sk_tiles = split > 1 ? T : 0;
+  return p;
+}
+
 GemmPlan plan_fp8_gemm(int64_t M, int64_t N, int64_t K, int cus) {
   if (K % kBK != 0 || cus <= 0) return plan_fp8_gemm_split(M, N, 1, 256);
   const int64_t nk = K / kBK;
@@ -495,6 +826,18 @@ GemmPlan plan_fp8_gemm(int64_t M, int64_t N, int64_t K, int cus) {
       const double t = fp8_plan_time(M, N, nk, bm, s, cus);
       if (!have || t < best_t) have = true, best_t = t, best_bm = bm, best_s = s;
     }
+  }
+  if (K % 128 == 0) {
+    for (int bn : {128, 192}) {
+      const int64_t T = ((M + 127) / 128) * ((N + bn - 1) / bn);
+      const double step_bytes = (128.0 + bn) * 128.0;
+      const double steps = static_cast<double>(K / 128);
+      const double per_cu = static_cast<double>((T + cus - 1) / cus);
+      const double t = std::max(static_cast<double>(T) * steps * step_bytes / kL2Rate,
+                                per_cu * steps * step_bytes / kCuRateRect) + kFixed;
+      if (t < best_t) best_t = t, best_bm = -bn;
+    }
+    if (best_bm < 0) return plan_fp8_gemm_rect(M, N, 1, -best_bm);
   }
   GemmPlan p = plan_fp8_gemm_split(M, N, best_s, best_bm);
   // Whole 256x256 tiles in full waves and a partial last wave of R tiles:
@@ -514,6 +857,22 @@ GemmPlan plan_fp8_gemm(int64_t M, int64_t N, int64_t K, int cus) {
 void launch_fp8_gemm(const uint8_t* A, const uint8_t* B, int64_t M, int64_t N, int64_t K, const float* sx,
                      const float* sw, void* Y, int ydt, const GemmPlan& plan, float* part, int* cnt, hipStream_t s) {
   const dim3 block(256);
+  if (plan.rect && K % 128 == 0) {
+    const dim3 grid(plan.dp_tiles + plan.sk_tiles * plan.split);
+#define W8_FP8_ARGS A, B, (int)M, (int)N, (int)K, sx, sw, Y, plan.tiles_m, plan.tiles_n, plan.dp_tiles, plan.split, \
+    part, cnt
+    if (plan.bn == 192) {
+      if (ydt == 0) k_fp8_gemm_rect<0, 3><<<grid, block, 0, s>>>(W8_FP8_ARGS);
+      else if (ydt == 1) k_fp8_gemm_rect<1, 3><<<grid, block, 0, s>>>(W8_FP8_ARGS);
+      else k_fp8_gemm_rect<2, 3><<<grid, block, 0, s>>>(W8_FP8_ARGS);
+    } else {
+      if (ydt == 0) k_fp8_gemm_rect<0, 2><<<grid, block, 0, s>>>(W8_FP8_ARGS);
+      else if (ydt == 1) k_fp8_gemm_rect<1, 2><<<grid, block, 0, s>>>(W8_FP8_ARGS);
+      else k_fp8_gemm_rect<2, 2><<<grid, block, 0, s>>>(W8_FP8_ARGS);
+    }
+#undef W8_FP8_ARGS
+    return;
+  }
   if (K % kBK == 0) {
     constexpr int S = 4;
     if (plan.bm == 256 && plan.small) {

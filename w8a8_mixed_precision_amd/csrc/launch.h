@@ -22,17 +22,22 @@ int device_cus();
 // Tiles past dp_tiles (sk_tiles of them) run as `split` K-slices of whole
 // tiles, as `split` K-slices of 128x128 quarters (small), or (streamk, int8
 // only) as sk_blocks blocks that share their K steps evenly.
+//
+// rect (FP8 GEMM, K % 128 == 0): blocks of bm = 128 rows x bn = 128 or 192
+// columns on 128-byte K steps.
 struct GemmPlan {
   int tiles_m, tiles_n, dp_tiles, split, sk_tiles;
   int bm = 256;
   bool small = false;
   bool streamk = false;
   int sk_blocks = 0;
+  bool rect = false;
+  int bn = 0;                                    // block columns when rect (else bm)
   int units() const { return small ? 4 * sk_tiles : sk_tiles; }       // blocks per K-slice past dp_tiles
   int grid() const { return dp_tiles + (streamk ? sk_blocks : units() * split); }
   size_t partial_bytes() const {
     if (streamk) return size_t(2) * sk_blocks * bm * bm * 4;           // two slots per stream-K block
-    const size_t b = small ? 128 * 128 * 4 : size_t(bm) * bm * 4;
+    const size_t b = small ? 128 * 128 * 4 : size_t(bm) * (rect ? bn : bm) * 4;
     return split > 1 ? size_t(units()) * split * b : 0;
   }
   int counters() const { return streamk ? sk_tiles : (split > 1 ? units() : 0); }
@@ -90,6 +95,9 @@ void launch_int8_gemm(const int8_t* A, const int8_t* B, int64_t M, int64_t N, in
                       const SideSrc& src, hipStream_t s, long long* timeline = nullptr);
 GemmPlan plan_fp8_gemm(int64_t M, int64_t N, int64_t K, int cus);
 GemmPlan plan_fp8_gemm_split(int64_t M, int64_t N, int split, int bm);
+// 128 x bn blocks (bn = 128 or 192) on 128-byte K steps, `split` K-slices
+// each (K % 128 == 0).
+GemmPlan plan_fp8_gemm_rect(int64_t M, int64_t N, int split, int bn);
 void launch_fp8_gemm(const uint8_t* A, const uint8_t* B, int64_t M, int64_t N, int64_t K, const float* sx,
                      const float* sw, void* Y, int ydt, const GemmPlan& plan, float* part, int* cnt, hipStream_t s);
 // W4A8: int4 weight codes packed two per byte with one fp32 scale per group of
