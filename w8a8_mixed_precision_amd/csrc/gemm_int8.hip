@@ -576,23 +576,23 @@ __device__ __forceinline__ void small_body(const v8i* fc, v8i* fn, v16i (*acc)[2
   }
 }
 
-// One 128x128 block of the leftover tiles: blocks dp_tiles.. of the grid are
-// `split` K-slices of 4*R quarter tiles (R leftover 256x256 tiles, numbered
-// slice-major per XCD like the big split). A quarter outside [M, N) returns at
-// once (its other slices do too). With split > 1 the slices exchange int32
-// partials and counters as the big split-K does (exact sums, any order).
+// One 128x128 block of the leftover tiles: block tb of the nu tail blocks,
+// which are `split` K-slices of 4*R quarter tiles (R leftover 256x256 tiles,
+// numbered slice-major per XCD like the big split). A quarter outside [M, N)
+// returns at once (its other slices do too). With split > 1 the slices
+// exchange int32 partials and counters as the big split-K does (exact sums,
+// any order).
 template <int MODE, bool XBF16, int S>
 __device__ __forceinline__ void small_block(int8_t* lds, const int8_t* __restrict__ A, const int8_t* __restrict__ B,
                                             int M, int N, int K, const float* __restrict__ sx,
                                             const float* __restrict__ sw, const int* __restrict__ nO_ptr,
                                             const uint16_t* __restrict__ XO, const uint16_t* __restrict__ WO,
                                             const float* __restrict__ bias, void* __restrict__ Y, int tiles_m,
-                                            int tiles_n, int dp_tiles, int split, int* __restrict__ part,
-                                            int* __restrict__ cnt, const SideSrc& src) {
+                                            int tiles_n, int dp_tiles, int tb, int nu, int split,
+                                            int* __restrict__ part, int* __restrict__ cnt, const SideSrc& src) {
   constexpr int SS = 2 * S;                     // the same LDS as S big stages
   int* const s_last = reinterpret_cast<int*>(lds + kEpiLds8);
-  const int nu = gridDim.x - dp_tiles;
-  const int v = xcd_remap(blockIdx.x - dp_tiles, nu);
+  const int v = xcd_remap(tb, nu);
   const int Q = nu / split;                     // quarter tiles
   const int piece = v / Q, sub = v % Q;
   int tm, tn;
@@ -776,15 +776,15 @@ __device__ __forceinline__ void tile128(int8_t* lds, const int8_t* __restrict__ 
                                         int N, int K, const float* __restrict__ sx, const float* __restrict__ sw,
                                         const int* __restrict__ nO_ptr, const uint16_t* __restrict__ XO,
                                         const uint16_t* __restrict__ WO, const float* __restrict__ bias,
-                                        void* __restrict__ Y, int tiles_m, int tiles_n, int dp_tiles,
+                                        void* __restrict__ Y, int tiles_m, int tiles_n, int dp_tiles, int lb,
                                         const SideSrc& src, long long* __restrict__ tl) {
   auto stamp = [&](int p, long long v) {
-    if (tl != nullptr && threadIdx.x == 0) tl[static_cast<int64_t>(blockIdx.x) * 8 + p] = v;
+    if (tl != nullptr && threadIdx.x == 0) tl[static_cast<int64_t>(lb) * 8 + p] = v;
   };
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   int tm, tn;
-  tile_coords(blockIdx.x, dp_tiles, tiles_m, tiles_n, tm, tn);
+  tile_coords(lb, dp_tiles, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * kBM, n0 = tn * kBN;
   EpiIn ein;
   epi_prefetch<MODE>(ein, M, N, m0, n0, wm, lane, sx, sw, bias, nO_ptr);
@@ -871,8 +871,9 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
                                                           const uint16_t* __restrict__ WO,
                                                           const float* __restrict__ bias, void* __restrict__ Y,
                                                           int tiles_m, int tiles_n, int dp_tiles, int split,
-                                                          int small, int* __restrict__ part, int* __restrict__ cnt,
-                                                          SideSrc src, long long* __restrict__ tl) {
+                                                          int small, int tfirst, int* __restrict__ part,
+                                                          int* __restrict__ cnt, SideSrc src,
+                                                          long long* __restrict__ tl) {
   constexpr int kStage = 2 * kBM * kBK;       // A then B, 32 KB
   constexpr int kLoads = 8;                   // DMA instructions per wave per step
   // the ring, then the tile's outlier operands (kSideLds)
@@ -886,28 +887,35 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
   int* const s_last = reinterpret_cast<int*>(lds + kEpiLds8);
   static_assert(S * kStage >= kEpiLds8 + 4, "epilogue LDS and arrival flag");
 
+  // Logical block index: whole tiles 0 .. dp_tiles-1, then the blocks past
+  // them. With tfirst > 0 (128x128 quarters only) the grid launches those
+  // tfirst blocks first, so the partial last wave starts with the first one
+  // instead of after the last (tfirst % 8 == 0 keeps every block's XCD).
+  const int bid = static_cast<int>(blockIdx.x);
+  const int lb = tfirst > 0 ? (bid < tfirst ? dp_tiles + bid : bid - tfirst) : bid;
   // Optional per-block timeline (debug export only; tl is null otherwise):
-  // wave 0's first lane writes 8 words per block: [0] start, [1] K loop
-  // start, [2] K loop end, [3] end (100 MHz constant clock, wall_clock64),
-  // [4], [5] the shader-clock counter (clock64) at [1] and [2]. A block with
-  // several tile pieces leaves [1]..[5] of its last piece that writes them; a
-  // piece that hands its partial to another block writes no end.
+  // wave 0's first lane writes 8 words per logical block: [0] start, [1] K
+  // loop start, [2] K loop end, [3] end (100 MHz constant clock,
+  // wall_clock64), [4], [5] the shader-clock counter (clock64) at [1] and [2].
+  // A block with several tile pieces leaves [1]..[5] of its last piece that
+  // writes them; a piece that hands its partial to another block writes no end.
   auto stamp = [&](int p, long long v) {
     if (tl != nullptr && threadIdx.x == 0) {
-      tl[static_cast<int64_t>(blockIdx.x) * 8 + p] = v;
+      tl[static_cast<int64_t>(lb) * 8 + p] = v;
     }
   };
-  if (small == 1 && static_cast<int>(blockIdx.x) >= dp_tiles) {
+  if (small == 1 && lb >= dp_tiles) {
     stamp(0, wall_clock64());
     small_block<MODE, XBF16, S>(lds, A, B, M, N, K, sx, sw, nO_ptr, XO, WO, bias, Y, tiles_m, tiles_n, dp_tiles,
-                                split, part, cnt, src);
+                                lb - dp_tiles, static_cast<int>(gridDim.x) - dp_tiles, split, part, cnt, src);
     stamp(3, wall_clock64());
     return;
   }
   if constexpr (K128) {
     // every other block owns a whole tile (the launcher's condition)
     static_assert(S * kStage == 2 * kStage2, "the 128-byte steps use the same ring");
-    tile128<MODE, XBF16>(lds, A, B, M, N, K, sx, sw, nO_ptr, XO, WO, bias, Y, tiles_m, tiles_n, dp_tiles, src, tl);
+    tile128<MODE, XBF16>(lds, A, B, M, N, K, sx, sw, nO_ptr, XO, WO, bias, Y, tiles_m, tiles_n, dp_tiles, lb, src,
+                         tl);
     return;
   }
   const int nk_all = K / kBK;
@@ -925,16 +933,16 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
   // writes its int32 partial to its slot, bumps the tile's arrival counter,
   // and the last piece to arrive adds the others' partials to its own and
   // runs the epilogue. Integer sums are exact in any order.
-  const int mode = static_cast<int>(blockIdx.x) < dp_tiles ? 0 : (small == 2 ? 2 : 1);
+  const int mode = lb < dp_tiles ? 0 : (small == 2 ? 2 : 1);
   const int nb = gridDim.x - dp_tiles;          // blocks past the whole tiles
   int v = 0, R = 0, piece = 0, dp_id = 0, per = 1, t = 0;
   int g0 = 0, g1 = nk_all;                        // (W < 2^31: at most 2 cus leftover tiles)
   if (mode == 0) {
-    dp_id = blockIdx.x;
+    dp_id = lb;
   } else {
     // slices and stream-K blocks are numbered per XCD (xcd_remap), so the
     // blocks of one XCD share the A rows of neighbouring tiles
-    v = xcd_remap(blockIdx.x - dp_tiles, nb);
+    v = xcd_remap(lb - dp_tiles, nb);
     if (mode == 1) {
       R = nb / split;
       piece = v / R;
@@ -1175,6 +1183,7 @@ GemmPlan plan_int8_gemm(int64_t M, int64_t N, int64_t K, int cus) {
   p.split = best_split;
   p.sk_tiles = R;
   p.small = best_small;
+  p.tail_first = best_small && (p.grid() - p.dp_tiles) % kXcds == 0;
   return p;
 }
 
@@ -1235,7 +1244,8 @@ void launch_int8_gemm(const int8_t* A, const int8_t* B, int64_t M, int64_t N, in
     // 128-byte K steps when K allows and every block past the small tail owns a whole tile
     const bool k128 = K % kBK2 == 0 && !plan.streamk && (plan.small || plan.split == 1);
 #define W8_GEMM_ARGS A, B, m, n, k, sx, sw, nO, XO, WO, bias, Y, tiles_m, tiles_n, plan.dp_tiles, plan.split, \
-    plan.streamk ? 2 : (plan.small ? 1 : 0), part, cnt, src, timeline
+    plan.streamk ? 2 : (plan.small ? 1 : 0), plan.tail_first ? plan.grid() - plan.dp_tiles : 0, part, cnt, src, \
+    timeline
     if (k128) {
       if (mode == 0) k_int8_gemm_dma<0, true, S, true><<<grid, block, 0, s>>>(W8_GEMM_ARGS);
       else if (mode == 1 && xbf16) k_int8_gemm_dma<1, true, S, true><<<grid, block, 0, s>>>(W8_GEMM_ARGS);

@@ -33,6 +33,7 @@ struct GemmPlan {
   int sk_blocks = 0;
   bool rect = false;
   int bn = 0;                                    // block columns when rect (else bm)
+  bool tail_first = false;                       // int8 quarters: launched before the whole tiles
   int units() const { return small ? 4 * sk_tiles : sk_tiles; }       // blocks per K-slice past dp_tiles
   int grid() const { return dp_tiles + (streamk ? sk_blocks : units() * split); }
   size_t partial_bytes() const {
