@@ -535,6 +535,15 @@ w8_status w8dbg_mfma_peak(int kind, int blocks, int iters, unsigned* out, double
 w8_status w8dbg_lds_stream(const void* buf, size_t buf_bytes, int K, int seg, int blocks, int panels, int iters,
                            unsigned* out, double* bytes, void* stream);
 
+/* Checks the packed float32 -> fp16 conversion of the library's epilogues
+ * (v_cvt_pk_f16_f32, two values per instruction) against the scalar one
+ * (v_cvt_f16_f32, round to nearest even) on every float32 bit pattern x,
+ * paired with x ^ 0x5A5A5A5A. out (device, 3 words, out[0..1] zero and out[2]
+ * 0xFFFFFFFF on entry) receives the number of mismatching pairs of non-NaN
+ * inputs, the number of pairs with a NaN input whose results differ, and the
+ * smallest x of a non-NaN mismatch. Asynchronous on `stream`. */
+w8_status w8dbg_cvt_f16_pair_check(unsigned* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -224,3 +224,13 @@ def test_fp8_linear_workspace_reuse_is_bitwise_stable():
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
     assert not ws[:4 * 4096].any()                             # the front's split-K counters
+
+
+def test_packed_f16_conversion_equals_the_scalar_one_on_every_float():
+    """The epilogues' fp16 outputs come from v_cvt_pk_f16_f32 (two values per
+    instruction); on every float32 bit pattern it gives the bits of the scalar
+    round-to-nearest-even conversion, NaN inputs included."""
+    announce("packed fp16 conversion, all 2^32 float32 patterns")
+    r = w8.debug_cvt_f16_pair_check()
+    assert r["mismatch"] == 0, r
+    assert r["mismatch_nan"] == 0, r

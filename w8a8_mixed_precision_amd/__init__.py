@@ -491,6 +491,15 @@ def debug_mfma_peak(kind: str, blocks: int, iters: int, device="cuda"):
     return out, ops.value
 
 
+def debug_cvt_f16_pair_check(device="cuda") -> dict:
+    """The packed float32 -> fp16 conversion against the scalar one over every
+    float32 bit pattern (w8dbg_cvt_f16_pair_check in include/w8mp.h)."""
+    out = torch.tensor([0, 0, -1], dtype=torch.int32, device=device)
+    _abi.check(lib().w8dbg_cvt_f16_pair_check(out.data_ptr(), _stream(out)))
+    o = [v & 0xFFFFFFFF for v in out.cpu().tolist()]
+    return {"mismatch": o[0], "mismatch_nan": o[1], "first": o[2]}
+
+
 def debug_lds_stream(buf: torch.Tensor, K: int, seg: int, blocks: int, panels: int, iters: int):
     """Launch the operand-streaming kernel (w8dbg_lds_stream in include/w8mp.h)
     over the device buffer `buf` on the current stream; returns (checksum

@@ -66,6 +66,7 @@ SIGNATURES = {
     "w8dbg_fp8_gemm": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _int, _int, _p, _int, _p, _size, _p]),
     "w8dbg_fp8_w8a16_linear_workspace_size": (_size, [_i64, _i64, _i64, _int, _int]),
     "w8dbg_fp8_w8a16_linear": (_int, [_p, _int, _i64, _i64, _p, _p, _i64, _int, _int, _p, _int, _p, _size, _p]),
+    "w8dbg_cvt_f16_pair_check": (_int, [_p, _p]),
     "w8dbg_int8_mixed_linear_plan_workspace_size": (_size, [_i64, _i64, _i64, _int]),
     "w8dbg_int8_mixed_linear_plan": (_int, [_p, _int, _i64, _i64, _p, _p, _p, _p, _i64, _f, _p, _int, _p, _size,
                                             _int, _p]),

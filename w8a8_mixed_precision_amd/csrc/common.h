@@ -56,6 +56,18 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
 }
 
+// The pair (a, b), float32 values, each rounded to fp16 as f32_to_f16_bits
+// does, packed a | b << 16: one v_cvt_pk_f16_f32 (gfx950) instead of two
+// conversions and an OR. Equal to the two scalar conversions for every pair
+// of float32 bit patterns (w8dbg_cvt_f16_pair_check).
+typedef float w8_f2 __attribute__((ext_vector_type(2)));
+typedef _Float16 w8_h2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_f16x2_bits(float a, float b) {
+  w8_f2 v{a, b};
+  __asm__("" : "+v"(v));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, w8_h2));
+}
+
 // ---- integer code of the symmetric absmax int8 scheme ----------------------
 // q = clamp(rne(fl32(x * r)), -127, 127), 0 for x == 0 (r may be +inf).
 __device__ __forceinline__ int absmax_code(float x, float r) {

@@ -419,8 +419,8 @@ __global__ __launch_bounds__(256, 4 / WT) void k_fp8_gemm_dma(const uint8_t* __r
             *reinterpret_cast<uint2*>(dst) = make_uint2(bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16),
                                                         bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16));
           } else if constexpr (YDT == 1) {
-            const uint32_t lo = f32_to_f16_bits(v[0]) | (static_cast<uint32_t>(f32_to_f16_bits(v[1])) << 16);
-            const uint32_t hi = f32_to_f16_bits(v[2]) | (static_cast<uint32_t>(f32_to_f16_bits(v[3])) << 16);
+            const uint32_t lo = f32x2_to_f16x2_bits(v[0], v[1]);
+            const uint32_t hi = f32x2_to_f16x2_bits(v[2], v[3]);
             *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
           } else {
             *reinterpret_cast<v4f*>(dst) = v4f{v[0], v[1], v[2], v[3]};
@@ -711,8 +711,8 @@ __global__ __launch_bounds__(256, 1) void k_fp8_gemm_rect(const uint8_t* __restr
           *reinterpret_cast<uint2*>(dst) = make_uint2(bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16),
                                                       bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16));
         } else if constexpr (YDT == 1) {
-          const uint32_t lo = f32_to_f16_bits(v[0]) | (static_cast<uint32_t>(f32_to_f16_bits(v[1])) << 16);
-          const uint32_t hi = f32_to_f16_bits(v[2]) | (static_cast<uint32_t>(f32_to_f16_bits(v[3])) << 16);
+          const uint32_t lo = f32x2_to_f16x2_bits(v[0], v[1]);
+          const uint32_t hi = f32x2_to_f16x2_bits(v[2], v[3]);
           *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
         } else {
           *reinterpret_cast<v4f*>(dst) = v4f{v[0], v[1], v[2], v[3]};

@@ -110,8 +110,8 @@ __device__ __forceinline__ void stage_cols(const v16i (&acc)[WT][WT], const v16f
           v[e] = __builtin_fmaf(t, cs[g][e], bs[g][e]);
         }
         if constexpr (MODE == 1) {
-          const uint32_t lo = f32_to_f16_bits(v[0]) | (static_cast<uint32_t>(f32_to_f16_bits(v[1])) << 16);
-          const uint32_t hi = f32_to_f16_bits(v[2]) | (static_cast<uint32_t>(f32_to_f16_bits(v[3])) << 16);
+          const uint32_t lo = f32x2_to_f16x2_bits(v[0], v[1]);
+          const uint32_t hi = f32x2_to_f16x2_bits(v[2], v[3]);
           *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
         } else {
           *reinterpret_cast<v4f*>(dst) = v4f{v[0], v[1], v[2], v[3]};

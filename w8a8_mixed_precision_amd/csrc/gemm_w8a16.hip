@@ -431,8 +431,8 @@ __global__ __launch_bounds__(256, BK == kBE4M3 ? 4 / WT : 1) void k_w8a16_gemm(c
             *reinterpret_cast<uint2*>(dst) = make_uint2(bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16),
                                                         bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16));
           } else if constexpr (YDT == 1) {
-            const uint32_t lo = f32_to_f16_bits(v[0]) | (static_cast<uint32_t>(f32_to_f16_bits(v[1])) << 16);
-            const uint32_t hi = f32_to_f16_bits(v[2]) | (static_cast<uint32_t>(f32_to_f16_bits(v[3])) << 16);
+            const uint32_t lo = f32x2_to_f16x2_bits(v[0], v[1]);
+            const uint32_t hi = f32x2_to_f16x2_bits(v[2], v[3]);
             *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
           } else {
             *reinterpret_cast<v4f*>(dst) = v4f{v[0], v[1], v[2], v[3]};

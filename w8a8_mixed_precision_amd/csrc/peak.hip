@@ -141,11 +141,46 @@ __global__ __launch_bounds__(256, 1) void k_lds_stream(const int8_t* __restrict_
   if (threadIdx.x == 0) out[blockIdx.x] = static_cast<unsigned>(lds[4 * lane]);
 }
 
+// Every float32 bit pattern x, paired with y = x ^ 0x5A5A5A5A (so every
+// pattern takes both places of a pair): the packed conversion against the two
+// scalar ones. out[0]: mismatching pairs of non-NaN inputs; out[1]: pairs with
+// a NaN input whose fp16 results differ; out[2]: the smallest x of a non-NaN
+// mismatch (0xFFFFFFFF if none).
+__global__ __launch_bounds__(256) void k_cvt_f16_pair_check(unsigned* __restrict__ out) {
+  const uint32_t stride = gridDim.x * blockDim.x;
+  unsigned bad = 0, bad_nan = 0, first = 0xFFFFFFFFu;
+  for (uint64_t p = blockIdx.x * blockDim.x + threadIdx.x; p < (uint64_t{1} << 32); p += stride) {
+    const uint32_t xb = static_cast<uint32_t>(p), yb = xb ^ 0x5A5A5A5Au;
+    const float x = __uint_as_float(xb), y = __uint_as_float(yb);
+    const uint32_t pk = f32x2_to_f16x2_bits(x, y);
+    const uint32_t sc = f32_to_f16_bits(x) | (static_cast<uint32_t>(f32_to_f16_bits(y)) << 16);
+    if (pk != sc) {
+      if (__builtin_isnan(x) || __builtin_isnan(y)) {
+        ++bad_nan;
+      } else {
+        ++bad;
+        first = min(first, xb);
+      }
+    }
+  }
+  if (bad) atomicAdd(out, bad);
+  if (bad_nan) atomicAdd(out + 1, bad_nan);
+  if (first != 0xFFFFFFFFu) atomicMin(out + 2, first);
+}
+
 }  // namespace
 
 }  // namespace w8
 
 extern "C" {
+
+// See include/w8mp.h.
+w8_status w8dbg_cvt_f16_pair_check(unsigned* out, void* stream) {
+  if (!out) return W8_ERR_INVALID_ARGUMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  w8::k_cvt_f16_pair_check<<<dim3(2048), dim3(256), 0, s>>>(out);
+  return hipGetLastError() == hipSuccess ? W8_OK : W8_ERR_HIP;
+}
 
 // See include/w8mp.h.
 w8_status w8dbg_mfma_peak(int kind, int blocks, int iters, unsigned* out, double* ops, void* stream) {
