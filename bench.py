@@ -406,6 +406,30 @@ def counter_workload(torch, w8, cases, steps: int, copy_mib: int) -> None:
     print(f"[bench] counter workload done: {steps} steps, 3 copies of {copy_mib} MiB", file=sys.stderr, flush=True)
 
 
+def counter_workload_fp8(torch, w8, steps: int) -> None:
+    """Minimal run for hardware-counter collection on the FP8 W8A8 linears: one
+    warm-up call and `steps` calls per layer; the text-encoder linears at 512
+    tokens (q, k, v, gate, up, down) with the dynamic per-token scale, then the
+    DiT 1024^2 QKV and MLP-up shapes with a static per-tensor scale."""
+    import synth
+
+    cases = [(synth.fp8_text_encoder(layer), False) for layer in synth.FP8_TEXT_LAYERS]
+    cases += [(synth.dit_qkv_1024(), True), (synth.dit_mlp_1024("up"), True)]
+    for c, static in cases:
+        x = _dev16(c.x_bits, torch)
+        wq, sw = w8.quantize_weight_rowwise(_dev16(c.w_bits, torch), "fp8")
+        y = torch.empty((c.M, c.N), dtype=torch.bfloat16, device="cuda")
+        ws = w8.new_workspace(w8.fp8_w8a8_linear_workspace_size(c.M, c.N, c.K))
+        act = None
+        if static:
+            act = (x.float().abs().max() / 448.0).reshape(1).contiguous()
+        for _ in range(1 + steps):
+            w8.fp8_w8a8_linear(x, wq, sw, act, out=y, workspace=ws)
+        torch.cuda.synchronize()
+        del x, wq, y, ws
+    print(f"[bench] fp8 counter workload done: {steps} calls per layer", file=sys.stderr, flush=True)
+
+
 def vendor_reference(torch, steps: int) -> dict:
     """The ROCm libraries behind torch on the same shapes, for context: plain
     int8 x int8 -> int32 products (torch._int_mm) on the DiT 1024^2 linears and
@@ -684,6 +708,9 @@ def main() -> int:
                          "shapes, for context; prints one JSON line")
     ap.add_argument("--counters", type=int, default=0, metavar="MIB",
                     help="counter-collection mode: a few int8 steps, then plain copies of MIB MiB; no JSON line")
+    ap.add_argument("--counters-fp8", action="store_true",
+                    help="counter-collection mode: --steps calls of each FP8 W8A8 linear (text encoder, DiT 1024^2); "
+                         "no JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported: the library has no "
@@ -705,6 +732,9 @@ def main() -> int:
         return 0
     if args.counters:
         counter_workload(torch, w8, cases, args.steps, args.counters)
+        return 0
+    if args.counters_fp8:
+        counter_workload_fp8(torch, w8, args.steps)
         return 0
 
     # inputs resident in HBM, weights quantized once (untimed)
