@@ -456,14 +456,16 @@ __device__ __forceinline__ void mfma_sub(const v4i (&f)[8], v16i (&acc)[4][4]) {
 }
 
 // One 32-byte sub-step as 8 fixed groups of {2 MFMAs on the current
-// fragments, LDS reads of the next fragments, [1 DMA of a future K-step]}.
+// fragments, LDS reads of the next fragments, [a DMA of a future K-step]}.
 // sched_barrier keeps the order: the loads are spread over the MFMA shadow
 // instead of stalling the wave's in-order issue in a burst. The next
 // fragments are read in the order the next sub-step consumes them (A0, then
 // B0..B3, then A1..A3), two per group in the first four groups, so they have
 // landed when the next sub-step starts: the compiler puts a wait for every
 // outstanding LDS read there, as it counts the LDS DMAs in flight among them.
-template <bool DMA>
+// LOAD 1 issues a future step's 4 A loads, LOAD 2 its 4 B loads, one every
+// other group: a step's loads are spread over two sub-steps.
+template <int LOAD>
 __device__ __forceinline__ void mma_phase(const v4i (&fm)[8], v16i (&acc)[4][4], const int8_t* sfr, int sub,
                                           int wm, int wn, int lane, v4i (&fl)[8], const DmaSrc& src, int k0,
                                           int8_t* st, int wave) {
@@ -482,19 +484,12 @@ __device__ __forceinline__ void mma_phase(const v4i (&fm)[8], v16i (&acc)[4][4],
         __builtin_amdgcn_mfma_i32_32x32x32_i8(fm[4 + (p0 & 3)], fm[p0 >> 2], acc[p0 >> 2][p0 & 3], 0, 0, 0);
     acc[p1 >> 2][p1 & 3] =
         __builtin_amdgcn_mfma_i32_32x32x32_i8(fm[4 + (p1 & 3)], fm[p1 >> 2], acc[p1 >> 2][p1 & 3], 0, 0, 0);
-    if (DMA) {
-      if (t < 4) {
-        read(kOrder[2 * t]);
-        read(kOrder[2 * t + 1]);
-      }
-      if (t < 4)
-        dma_a(src, st + (wave * 4 + t) * 1024, t, k0);
-      else
-        dma_b(src, st + kBM * kBK + (wave * 4 + t - 4) * 1024, t - 4, k0);
-    } else if (t < 4) {
+    if (t < 4) {
       read(kOrder[2 * t]);
       read(kOrder[2 * t + 1]);
     }
+    if (LOAD == 1 && (t & 1) == 0) dma_a(src, st + (wave * 4 + t / 2) * 1024, t / 2, k0);
+    if (LOAD == 2 && (t & 1) == 0) dma_b(src, st + kBM * kBK + (wave * 4 + t / 2) * 1024, t / 2, k0);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -681,9 +676,14 @@ __device__ __forceinline__ void small_block(int8_t* lds, const int8_t* __restric
 // step moves is a whole 128-byte line, which the L2 -> LDS path streams about
 // 25% faster than the 64-byte half lines of the 64-byte step (measured with
 // w8dbg_lds_stream), and a step is 64 MFMAs per wave between barriers. The
-// ring holds two 64 KB steps; the loads of step kt + 2 go out right after the
-// barrier that retires step kt's slot, in the phase that multiplies its last
-// 32-byte sub-step, so they have the three sub-steps of step kt + 1 to land.
+// ring holds two 64 KB steps; the loads of step kt + 2 go out after the
+// barrier that retires step kt's slot: its A rows in the phase that
+// multiplies step kt's last 32-byte sub-step, its B rows in the first phase of
+// step kt + 1, one load per MFMA pair. The B rows then have two sub-steps to
+// land. All 16 loads of a wave in one phase (64 per CU, 1 KB each, about
+// twice what the CU's load path moves in that phase) held up the MFMA issue
+// behind the queued loads: 2790 against 2405 shader cycles per step on the
+// DiT QKV shape.
 // LDS rows are 128 bytes; chunk c of row r sits at chunk c ^ ((r >> 1) & 7),
 // so 16 consecutive rows read at one chunk hit 16 distinct 16-byte bank groups.
 constexpr int kBK2 = 128;
@@ -740,8 +740,9 @@ __device__ __forceinline__ void dma128(const Dma128& d, int8_t* st, int q, int k
 // of the next sub-step (READ, two per MFMA pair in the first half, so they
 // have landed when the next sub-step starts: the compiler waits for every LDS
 // read there, because it counts the LDS DMAs in flight as LDS operations too)
-// and the 16 loads of a future step (LOAD), order pinned with sched_barrier.
-template <bool READ, bool LOAD>
+// and, one per MFMA pair, the 8 loads of a future step's A rows (LOAD 1) or
+// B rows (LOAD 2); order pinned with sched_barrier.
+template <bool READ, int LOAD>
 __device__ __forceinline__ void phase128(const v4i (&fm)[8], v16i (&acc)[4][4], const int8_t* sn, int sub, int wm,
                                          int wn, int lane, v4i (&fl)[8], const Dma128& d, int k0, int8_t* st,
                                          int wave) {
@@ -752,10 +753,9 @@ __device__ __forceinline__ void phase128(const v4i (&fm)[8], v16i (&acc)[4][4], 
     const int p0 = 2 * t, p1 = 2 * t + 1;
     acc[p0 >> 2][p0 & 3] =
         __builtin_amdgcn_mfma_i32_32x32x32_i8(fm[4 + (p0 & 3)], fm[p0 >> 2], acc[p0 >> 2][p0 & 3], 0, 0, 0);
-    if (LOAD) dma128(d, st, 2 * t, k0, wave);
+    if (LOAD != 0) dma128(d, st, 8 * (LOAD - 1) + t, k0, wave);
     acc[p1 >> 2][p1 & 3] =
         __builtin_amdgcn_mfma_i32_32x32x32_i8(fm[4 + (p1 & 3)], fm[p1 >> 2], acc[p1 >> 2][p1 & 3], 0, 0, 0);
-    if (LOAD) dma128(d, st, 2 * t + 1, k0, wave);
     if (READ && t < 4) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -822,17 +822,22 @@ __device__ __forceinline__ void tile128(int8_t* lds, const int8_t* __restrict__ 
   load_frags128(lds, 0, wm, wn, lane, f0);
   for (int kt = 0; kt < nk - 1; ++kt) {
     int8_t* sa = lds + (kt & 1) * kStage2;
-    phase128<true, false>(f0, acc, sa, 1, wm, wn, lane, f1, d, 0, nullptr, wave);
-    phase128<true, false>(f1, acc, sa, 2, wm, wn, lane, f0, d, 0, nullptr, wave);
-    phase128<true, false>(f0, acc, sa, 3, wm, wn, lane, f1, d, 0, nullptr, wave);
+    // step kt+1's B rows go out with the first sub-step (its A rows went out
+    // in the previous step's last phase; step 1 came whole with the fill)
+    if (kt > 0)
+      phase128<true, 2>(f0, acc, sa, 1, wm, wn, lane, f1, d, (kt + 1) * kBK2, lds + ((kt + 1) & 1) * kStage2, wave);
+    else
+      phase128<true, 0>(f0, acc, sa, 1, wm, wn, lane, f1, d, 0, nullptr, wave);
+    phase128<true, 0>(f1, acc, sa, 2, wm, wn, lane, f0, d, 0, nullptr, wave);
+    phase128<true, 0>(f0, acc, sa, 3, wm, wn, lane, f1, d, 0, nullptr, wave);
     wait_lgkmcnt<0>();                            // this slot is fully read
     wait_vmcnt<0>();                              // step kt+1 landed (this wave)
     block_barrier();                              // ... for every wave; slot kt retired
     // the last sub-step multiplies while step kt+1's first fragments are read
-    // and step kt+2 (or a repeat of the last step) is fetched into the
-    // retired slot
-    phase128<true, true>(f1, acc, lds + ((kt + 1) & 1) * kStage2, 0, wm, wn, lane, f0, d,
-                         min(kt + 2, nk - 1) * kBK2, sa, wave);
+    // and the A rows of step kt+2 (or of a repeat of the last step) are
+    // fetched into the retired slot
+    phase128<true, 1>(f1, acc, lds + ((kt + 1) & 1) * kStage2, 0, wm, wn, lane, f0, d,
+                      min(kt + 2, nk - 1) * kBK2, sa, wave);
   }
   {
     const int8_t* sa = lds + ((nk - 1) & 1) * kStage2;
@@ -1012,10 +1017,11 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
     const int nk = ke - kb;
     block_barrier();                              // the previous piece's epilogue is done with the LDS
     if (first_piece) stamp(0, wall_clock64());    // (after the set-up: a store before it costs uniformity)
-    // DMA of K-step kt into its ring slot. Past the last step the load repeats
-    // the last step's data into the slot just retired, which no later step
-    // reads: every iteration then issues the same number of loads, so the wait
-    // below is one constant.
+    // DMA of K-step kt into its ring slot (the fill; in the loop a step's A
+    // rows go out after the barrier that retires its slot and its B rows in
+    // the next sub-step). Past the last step the load repeats the last step's
+    // data into the slot just retired, which no later step reads: every step
+    // then issues the same number of loads, so the wait below is one constant.
     auto issue = [&](int kt) {
       int8_t* st = lds + (kt % S) * kStage;
       const int k0 = min(kt, nk - 1) * kBK;
@@ -1057,15 +1063,21 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
     load_frags(lds, 0, wm, wn, lane, f0);
     for (int kt = 0; kt < nk - 1; ++kt) {
       int8_t* sa = lds + (kt % S) * kStage;
-      // sub-step 0 multiplies while sub-step 1's fragments are read
-      mma_phase<false>(f0, acc, sa, 1, wm, wn, lane, f1, src_k, 0, nullptr, wave);
+      // sub-step 0 multiplies while sub-step 1's fragments are read and the
+      // B rows of step kt-1+S go into the slot retired in the previous step
+      // (its A rows went out there; the first S steps came whole with the fill)
+      if (kt > 0)
+        mma_phase<2>(f0, acc, sa, 1, wm, wn, lane, f1, src_k, min(kt - 1 + S, nk - 1) * kBK,
+                     lds + ((kt - 1) % S) * kStage, wave);
+      else
+        mma_phase<0>(f0, acc, sa, 1, wm, wn, lane, f1, src_k, 0, nullptr, wave);
       wait_lgkmcnt<0>();                          // this slot is fully read
       wait_vmcnt<(S - 2) * kLoads>();             // step kt+1 landed (this wave)
       block_barrier();                            // ... for every wave; slot kt retired
       // sub-step 1 multiplies while step kt+1's first fragments are read and
-      // step kt+S is fetched into the retired slot
-      mma_phase<true>(f1, acc, lds + ((kt + 1) % S) * kStage, 0, wm, wn, lane, f0, src_k,
-                      min(kt + S, nk - 1) * kBK, sa, wave);
+      // the A rows of step kt+S are fetched into the retired slot
+      mma_phase<1>(f1, acc, lds + ((kt + 1) % S) * kStage, 0, wm, wn, lane, f0, src_k,
+                   min(kt + S, nk - 1) * kBK, sa, wave);
     }
     load_frags(lds + ((nk - 1) % S) * kStage, 1, wm, wn, lane, f1);
     mfma_sub(f0, acc);
