@@ -523,16 +523,20 @@ __device__ __forceinline__ int rect_row(int f, int wm, int wn, int fr) {
 
 // One 64-byte sub-step: the wave's 2 x TN MFMAs on fragments fc while the
 // fragments of sub-step `sub` of the stage sn are read into fn (in the order
-// the MFMAs consume them: A0, B0 .., A1) and, with DMA, the loads of a future
-// K step go to stage st; both spread evenly over the MFMAs, the interleaving
-// pinned by sched_barrier.
-template <int TN, bool DMA>
+// the MFMAs consume them: A0, B0 .., A1) and the loads of a future K step's
+// A rows (LOAD 1) or B rows (LOAD 2) go to stage st; both spread evenly over
+// the MFMAs, the interleaving pinned by sched_barrier. A step's loads are
+// split over two sub-steps: all of them in one (40 KB per CU for TN = 3 in
+// 384 MFMA cycles) is more than the CU's load path moves meanwhile, and the
+// queued loads hold up the wave's in-order issue.
+template <int TN, int LOAD>
 __device__ __forceinline__ void rect_phase(const v8i* fc, v8i* fn, v16f (*acc)[TN], const uint8_t* sn, int sub,
                                            int wm, int wn, int lane, const RectSrc& d, int k0, uint8_t* st,
                                            int wave) {
   using T = Fp8Rect<TN>;
   const int fr = lane & 31, fh = lane >> 5;
-  constexpr int kDma = DMA ? T::kLoads : 0;
+  constexpr int kQ0 = LOAD == 2 ? T::kLoadsA : 0;                          // first load of the phase
+  constexpr int kDma = LOAD == 1 ? T::kLoadsA : (LOAD == 2 ? T::kLoadsB : 0);
   v4i lo;
 #pragma unroll
   for (int t = 0; t < T::kMfma; ++t) {
@@ -551,7 +555,8 @@ __device__ __forceinline__ void rect_phase(const v8i* fc, v8i* fn, v16f (*acc)[T
       }
     }
 #pragma unroll
-    for (int q = t * kDma / T::kMfma; q < (t + 1) * kDma / T::kMfma; ++q) rect_dma(d, st, q, k0, wave, T::kLoadsB);
+    for (int q = t * kDma / T::kMfma; q < (t + 1) * kDma / T::kMfma; ++q)
+      rect_dma(d, st, kQ0 + q, k0, wave, T::kLoadsB);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -624,19 +629,24 @@ __global__ __launch_bounds__(256, 1) void k_fp8_gemm_rect(const uint8_t* __restr
     fa[f] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
   // K step kt: its first sub-step multiplies while its second's fragments are
-  // read; then (step kt+1 landed everywhere, slot kt read by every wave) the
-  // second multiplies while step kt+1's first fragments are read and step
-  // kt+S is fetched into slot kt. The last step runs the same code: its stray
-  // reads stay in the ring, its load repeats the last step into its own,
-  // retired slot.
+  // read and the B rows of step kt-1+S go into the slot retired in the
+  // previous step; then (step kt+1 landed everywhere, slot kt read by every
+  // wave) the second multiplies while step kt+1's first fragments are read
+  // and the A rows of step kt+S are fetched into slot kt. The first S steps
+  // came whole with the fill. The last step runs the same code: its stray
+  // reads stay in the ring, its loads repeat the last step into retired slots.
   for (int kt = 0; kt < nk; ++kt) {
     uint8_t* sc = lds + (kt % S) * T::kStage;
-    rect_phase<TN, false>(fa, fb, acc, sc, 1, wm, wn, lane, d, 0, nullptr, wave);
+    if (kt > 0)
+      rect_phase<TN, 2>(fa, fb, acc, sc, 1, wm, wn, lane, d, min(kt - 1 + S, nk - 1) * T::kStep,
+                        lds + ((kt - 1) % S) * T::kStage, wave);
+    else
+      rect_phase<TN, 0>(fa, fb, acc, sc, 1, wm, wn, lane, d, 0, nullptr, wave);
     wait_lgkmcnt<0>();
     wait_vmcnt<(S - 2) * T::kLoads>();
     block_barrier();
-    rect_phase<TN, true>(fb, fa, acc, lds + ((kt + 1) % S) * T::kStage, 0, wm, wn, lane, d,
-                         min(kt + S, nk - 1) * T::kStep, sc, wave);
+    rect_phase<TN, 1>(fb, fa, acc, lds + ((kt + 1) % S) * T::kStage, 0, wm, wn, lane, d,
+                      min(kt + S, nk - 1) * T::kStep, sc, wave);
   }
   wait_lgkmcnt<0>();
   wait_vmcnt<0>();                                // retire the trailing repeat loads
