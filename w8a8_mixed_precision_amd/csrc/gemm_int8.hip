@@ -133,6 +133,30 @@ __device__ __forceinline__ void flush_cols(const char* stg, char* __restrict__ y
   constexpr int T = R / RPI;                    // store instructions
   constexpr int TB = T > 8 ? 8 : T;             // chunks read ahead
   const int ch = lane % CPR;
+  // wave-uniform block origin (the callers' row index is a per-lane copy)
+  const int mb = __builtin_amdgcn_readfirstlane(m_base), nb = __builtin_amdgcn_readfirstlane(n_base);
+  if (vec && mb + R <= M && nb + CPR * EPC <= N && static_cast<int64_t>(R) * N * EB < (int64_t{1} << 31)) {
+    // Interior block: every staged row and column lies in [M, N). One buffer
+    // store per chunk from the block origin: the lane's row and column in the
+    // per-lane offset, the 8-row step of each store in the scalar offset, so
+    // no address arithmetic or bounds test per store.
+    const uint32_t rowb = static_cast<uint32_t>(N) * EB;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        y + (static_cast<int64_t>(mb) * N + nb) * EB, 0, static_cast<int>(R * rowb), kRawBuffer);
+    const uint32_t voff = static_cast<uint32_t>(lane / CPR) * rowb + ch * 16;
+#pragma unroll
+    for (int t0 = 0; t0 < T; t0 += TB) {
+      uint4 v[TB];
+#pragma unroll
+      for (int t = 0; t < TB; ++t)
+        v[t] = *reinterpret_cast<const uint4*>(stg + (RPI * (t0 + t) + lane / CPR) * kStgPitchJ + ch * 16);
+#pragma unroll
+      for (int t = 0; t < TB; ++t)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v[t]), rs, voff,
+                                               static_cast<int>(static_cast<uint32_t>(RPI * (t0 + t)) * rowb), 0);
+    }
+    return;
+  }
   const int n = n_base + ch * EPC;
 #pragma unroll
   for (int t0 = 0; t0 < T; t0 += TB) {
