@@ -595,13 +595,104 @@ __device__ __forceinline__ void small_body(const v8i* fc, v8i* fn, v16i (*acc)[2
   }
 }
 
+// 128-byte K steps (K % 128 == 0; the 256x256 tiles and the quarter blocks
+// below). LDS rows are 128 bytes; chunk c of row r sits at chunk
+// c ^ ((r >> 1) & 7), so 16 consecutive rows read at one chunk hit 16
+// distinct 16-byte bank groups.
+constexpr int kBK2 = 128;
+constexpr int kStage2 = 2 * kBM * kBK2;         // 64 KB: A rows, then B rows
+
+__device__ __forceinline__ int swz128(int row, int ch) { return row * kBK2 + ((ch ^ ((row >> 1) & 7)) << 4); }
+
+// Sources of a block's 128-byte-step loads: its rows of A and of B, and the
+// lane's row and chunk offset for even / odd loads i (the XOR term of the
+// chunk differs by 4 between them).
+struct Dma128 {
+  __amdgpu_buffer_rsrc_t a, b;   // the block's rows of A and of B (zeros past M / N)
+  uint32_t voff[2];              // this lane's row and chunk offset for even / odd i
+  int rows8;                     // bytes between a wave's consecutive loads: 8 K
+};
+
+// The quarter blocks of the 128-byte-step kernel (K % 128 == 0, at most
+// K / 128 slices): whole 128-byte row segments, as in the 256x256 tiles, which
+// the load path moves faster than the 64-byte half lines of the 64-byte steps
+// (a quarter block streams twice a whole tile's bytes per MFMA). Ring of 4
+// stages of 32 KB (A rows, then B rows; chunk c of row r at chunk
+// c ^ ((r >> 1) & 7)) in the same LDS; a step is two 64-byte phases of 8 MFMAs
+// per wave, one barrier per step, and its 8 loads per wave are split between
+// the phase after the barrier (A rows) and the next step's first phase (B
+// rows), like the whole tiles'.
+constexpr int kSmallStage2 = 2 * kSmall * kBK2;  // 32 KB
+constexpr int kSmallS2 = 4;
+
+// Load i (0..3) of a wave covers block rows wave*32 + 8i + lane/8, 8 lanes of
+// 16 bytes per row; the XOR term of its chunk alternates with the parity of i.
+__device__ __forceinline__ Dma128 small128_src(const int8_t* A, const int8_t* B, int m0, int n0, int M, int N, int K,
+                                               int k_off, int wave, int lane) {
+  Dma128 d;
+  d.a = operand_rsrc(A, m0, M, K, k_off, kSmall);
+  d.b = operand_rsrc(B, n0, N, K, k_off, kSmall);
+  const int r = wave * 32 + (lane >> 3);
+  const int ch = (lane & 7) ^ ((r >> 1) & 7);
+  d.voff[0] = static_cast<uint32_t>(r) * static_cast<uint32_t>(K) + (ch << 4);
+  d.voff[1] = static_cast<uint32_t>(r) * static_cast<uint32_t>(K) + ((ch ^ 4) << 4);
+  d.rows8 = 8 * K;
+  return d;
+}
+
+// Load q (0..7) of a step into stage st: q < 4 are A's loads 0..3, the others B's.
+__device__ __forceinline__ void small128_dma(const Dma128& d, int8_t* st, int q, int k0, int wave) {
+  const int i = q & 3;
+  if (q < 4)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.a, st + (wave * 4 + i) * 1024, 16, d.voff[i & 1] + i * d.rows8, k0, 0,
+                                             0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.b, st + kSmall * kBK2 + (wave * 4 + i) * 1024, 16,
+                                             d.voff[i & 1] + i * d.rows8, k0, 0, 0);
+}
+
+// 16-byte chunk ch of the lane's row of fragment f (0, 1: A row blocks; 2, 3: B).
+__device__ __forceinline__ const int8_t* small128_frag(const int8_t* slot, int f, int wm, int wn, int fr, int ch) {
+  return f < 2 ? slot + swz128(wm * 64 + f * 32 + fr, ch)
+               : slot + kSmall * kBK2 + swz128(wn * 64 + (f - 2) * 32 + fr, ch);
+}
+
+// One 64-byte phase: 8 MFMAs on fc (both 32-byte sub-steps of the 2x2 tiles,
+// sub-step-major so back-to-back MFMAs are independent) while the fragments
+// of half `half` of stage sn are read into fn (two 16-byte reads per MFMA in
+// the first four, in the order the next phase consumes them: A0, B0, B1, A1)
+// and, one per MFMA pair, the 4 loads of a future step's A rows (LOAD 1) or
+// B rows (LOAD 2) go to stage st.
+template <int LOAD>
+__device__ __forceinline__ void small128_phase(const v8i* fc, v8i* fn, v16i (*acc)[2], const int8_t* sn, int half,
+                                               int wm, int wn, int lane, const Dma128& d, int k0, int8_t* st,
+                                               int wave) {
+  const int fr = lane & 31, fh = lane >> 5;
+  constexpr int kOrd[4] = {0, 2, 3, 1};
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int h = t >> 2, i = (t >> 1) & 1, j = t & 1;
+    const v4i a = h ? hi4(fc[i]) : lo4(fc[i]);
+    const v4i b = h ? hi4(fc[2 + j]) : lo4(fc[2 + j]);
+    acc[i][j] = mfma_i8(b, a, acc[i][j]);
+    if (t < 4) {
+      const int f = kOrd[t];
+      const v4i lo = *reinterpret_cast<const v4i*>(small128_frag(sn, f, wm, wn, fr, 4 * half + fh));
+      const v4i hi = *reinterpret_cast<const v4i*>(small128_frag(sn, f, wm, wn, fr, 4 * half + 2 + fh));
+      fn[f] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    if (LOAD != 0 && (t & 1) == 0) small128_dma(d, st, 4 * (LOAD - 1) + t / 2, k0, wave);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // One 128x128 block of the leftover tiles: block tb of the nu tail blocks,
 // which are `split` K-slices of 4*R quarter tiles (R leftover 256x256 tiles,
 // numbered slice-major per XCD like the big split). A quarter outside [M, N)
 // returns at once (its other slices do too). With split > 1 the slices
 // exchange int32 partials and counters as the big split-K does (exact sums,
 // any order).
-template <int MODE, bool XBF16, int S>
+template <int MODE, bool XBF16, int S, bool K128>
 __device__ __forceinline__ void small_block(int8_t* lds, const int8_t* __restrict__ A, const int8_t* __restrict__ B,
                                             int M, int N, int K, const float* __restrict__ sx,
                                             const float* __restrict__ sw, const int* __restrict__ nO_ptr,
@@ -618,7 +709,8 @@ __device__ __forceinline__ void small_block(int8_t* lds, const int8_t* __restric
   group_tile(dp_tiles + sub / 4, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * kBM + (sub & 2) * 64, n0 = tn * kBN + (sub & 1) * 128;
   if (m0 >= M || n0 >= N) return;
-  const int nk_all = K / kBK;
+  const int kstep = K128 ? kBK2 : kBK;          // K bytes per step
+  const int nk_all = K / kstep;
   const int kb = piece * nk_all / split, ke = (piece + 1) * nk_all / split, nk = ke - kb;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -626,9 +718,6 @@ __device__ __forceinline__ void small_block(int8_t* lds, const int8_t* __restric
   EpiIn ein;
   epi_prefetch<MODE, 2>(ein, M, N, m0, n0, wm, lane, sx, sw, bias, nO_ptr);
 
-  // load i (0, 1) of each operand: block row r = wave*32 + 16*i + lane/4
-  // lands in LDS slot (lane & 3) of that row
-  const DmaSrc src_k = dma_src(A, B, m0, n0, M, N, K, kb * kBK, kSmall, wave, lane);
   v16i acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -637,6 +726,47 @@ __device__ __forceinline__ void small_block(int8_t* lds, const int8_t* __restric
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
+  if constexpr (K128) {
+    constexpr int SS2 = kSmallS2;
+    static_assert(SS2 * kSmallStage2 <= S * 2 * kBM * kBK, "the 128-byte ring fits the big one");
+    const Dma128 d = small128_src(A, B, m0, n0, M, N, K, kb * kBK2, wave, lane);
+    for (int st = 0; st < SS2; ++st)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) small128_dma(d, lds + st * kSmallStage2, q, min(st, nk - 1) * kBK2, wave);
+    wait_vmcnt<(SS2 - 1) * 8>();                // step 0 landed (this wave)
+    block_barrier();                            // ... for every wave
+    v8i fa[4], fb[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const v4i lo = *reinterpret_cast<const v4i*>(small128_frag(lds, f, wm, wn, fr, fh));
+      const v4i hi = *reinterpret_cast<const v4i*>(small128_frag(lds, f, wm, wn, fr, 2 + fh));
+      fa[f] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    // Step kt: its first half multiplies while its second half's fragments
+    // are read and the B rows of step kt-1+S2 go into the slot retired in the
+    // previous step (the first S2 steps came whole with the fill); then (step
+    // kt+1 landed everywhere, slot kt read by every wave) the second half
+    // multiplies while step kt+1's first fragments are read and the A rows of
+    // step kt+S2 are fetched into slot kt. The last step runs the same code:
+    // its stray reads stay in the ring, its loads repeat the last step into
+    // retired slots.
+    for (int kt = 0; kt < nk; ++kt) {
+      int8_t* sc = lds + (kt % SS2) * kSmallStage2;
+      if (kt > 0)
+        small128_phase<2>(fa, fb, acc, sc, 1, wm, wn, lane, d, min(kt - 1 + SS2, nk - 1) * kBK2,
+                          lds + ((kt - 1) % SS2) * kSmallStage2, wave);
+      else
+        small128_phase<0>(fa, fb, acc, sc, 1, wm, wn, lane, d, 0, nullptr, wave);
+      wait_lgkmcnt<0>();
+      wait_vmcnt<(SS2 - 2) * 8>();
+      block_barrier();
+      small128_phase<1>(fb, fa, acc, lds + ((kt + 1) % SS2) * kSmallStage2, 0, wm, wn, lane, d,
+                        min(kt + SS2, nk - 1) * kBK2, sc, wave);
+    }
+  } else {
+  // load i (0, 1) of each operand: block row r = wave*32 + 16*i + lane/4
+  // lands in LDS slot (lane & 3) of that row
+  const DmaSrc src_k = dma_src(A, B, m0, n0, M, N, K, kb * kBK, kSmall, wave, lane);
   for (int st = 0; st < SS; ++st) small_issue<SS>(lds, st, nk, src_k, wave);
   wait_vmcnt<(SS - 1) * kSmallLoads>();
   block_barrier();
@@ -653,9 +783,10 @@ __device__ __forceinline__ void small_block(int8_t* lds, const int8_t* __restric
     small_body<SS>(fb, fa, acc, lds, kt + 1, nk, wm, wn, lane, src_k, wave);
   }
   if (kt < nk) small_body<SS>(fa, fb, acc, lds, kt, nk, wm, wn, lane, src_k, wave);
+  }
   wait_lgkmcnt<0>();
-  wait_vmcnt<0>();
-  block_barrier();
+  wait_vmcnt<0>();                              // retire the trailing repeat loads
+  block_barrier();                              // every wave is done with the ring
 
   if (split > 1) {
     const int wv = __builtin_amdgcn_readfirstlane(wave);
@@ -708,12 +839,6 @@ __device__ __forceinline__ void small_block(int8_t* lds, const int8_t* __restric
 // twice what the CU's load path moves in that phase) held up the MFMA issue
 // behind the queued loads: 2790 against 2405 shader cycles per step on the
 // DiT QKV shape.
-// LDS rows are 128 bytes; chunk c of row r sits at chunk c ^ ((r >> 1) & 7),
-// so 16 consecutive rows read at one chunk hit 16 distinct 16-byte bank groups.
-constexpr int kBK2 = 128;
-constexpr int kStage2 = 2 * kBM * kBK2;         // 64 KB: A rows, then B rows
-
-__device__ __forceinline__ int swz128(int row, int ch) { return row * kBK2 + ((ch ^ ((row >> 1) & 7)) << 4); }
 
 // Fragments of 32-byte sub-step `sub` (0..3) of the step in slot `sa`.
 __device__ __forceinline__ void load_frags128(const int8_t* sa, int sub, int wm, int wn, int lane, v4i (&f)[8]) {
@@ -730,12 +855,6 @@ __device__ __forceinline__ void load_frags128(const int8_t* sa, int sub, int wm,
 // land in physical chunk l & 7 of its row, which holds logical chunk
 // (l & 7) ^ ((row >> 1) & 7). For odd i that XOR term is 4 more than for
 // even i, so two per-lane offsets serve all 8 loads.
-struct Dma128 {
-  __amdgpu_buffer_rsrc_t a, b;   // the tile's rows of A and of B (zeros past M / N)
-  uint32_t voff[2];              // this lane's row and chunk offset for even / odd i
-  int rows8;                     // bytes between a wave's consecutive loads: 8 K
-};
-
 __device__ __forceinline__ Dma128 dma128_src(const int8_t* A, const int8_t* B, int m0, int n0, int M, int N, int K,
                                              int wave, int lane) {
   Dma128 d;
@@ -935,7 +1054,7 @@ __global__ __launch_bounds__(256, 1) void k_int8_gemm_dma(const int8_t* __restri
   };
   if (small == 1 && lb >= dp_tiles) {
     stamp(0, wall_clock64());
-    small_block<MODE, XBF16, S>(lds, A, B, M, N, K, sx, sw, nO_ptr, XO, WO, bias, Y, tiles_m, tiles_n, dp_tiles,
+    small_block<MODE, XBF16, S, K128>(lds, A, B, M, N, K, sx, sw, nO_ptr, XO, WO, bias, Y, tiles_m, tiles_n, dp_tiles,
                                 lb - dp_tiles, static_cast<int>(gridDim.x) - dp_tiles, split, part, cnt, src);
     stamp(3, wall_clock64());
     return;
@@ -1277,8 +1396,10 @@ void launch_int8_gemm(const int8_t* A, const int8_t* B, int64_t M, int64_t N, in
   if (K % kBK == 0) {
     constexpr int S = 4;
     const dim3 grid(plan.grid());
-    // 128-byte K steps when K allows and every block past the small tail owns a whole tile
-    const bool k128 = K % kBK2 == 0 && !plan.streamk && (plan.small || plan.split == 1);
+    // 128-byte K steps when K allows and every block past the small tail owns a
+    // whole tile (the tail's quarter blocks then step 128 bytes too, so at
+    // most K / 128 slices of them)
+    const bool k128 = K % kBK2 == 0 && !plan.streamk && (plan.small ? plan.split <= K / kBK2 : plan.split == 1);
 #define W8_GEMM_ARGS A, B, m, n, k, sx, sw, nO, XO, WO, bias, Y, tiles_m, tiles_n, plan.dp_tiles, plan.split, \
     plan.streamk ? 2 : (plan.small ? 1 : 0), plan.tail_first ? plan.grid() - plan.dp_tiles : 0, part, cnt, src, \
     timeline
