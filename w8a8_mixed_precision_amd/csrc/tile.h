@@ -183,8 +183,10 @@ __device__ __forceinline__ DmaSrc dma_src(const int8_t* A, const int8_t* B, int 
 
 // Load i (16 rows) of this wave's share of operand A or B at byte k0 of the
 // K range into LDS at dst (1 KB: the 16 rows' 64-byte segments). The row goes
-// into the per-lane offset, which the range check covers (the scalar offset
-// is added to the address but not checked); k0 stays inside the row.
+// into the per-lane offset and k0 into the scalar one. The range check covers
+// their sum (measured: with a descriptor spanning one row and the row's start
+// in the scalar offset, every row past the first read as zeros); for a row
+// inside the descriptor, row * K + k0 plus the chunk stays below its range.
 __device__ __forceinline__ void dma_a(const DmaSrc& d, int8_t* dst, int i, int k0) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(d.a, dst, 16, d.voff + i * d.rows16, k0, 0, 0);
 }
