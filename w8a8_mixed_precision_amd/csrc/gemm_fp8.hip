@@ -769,8 +769,12 @@ __global__ __launch_bounds__(256, 1) void k_fp8_gemm_rect(const uint8_t* __restr
 //    last slice (through memory, kPartRate bytes/us) after a latency kSplitLat;
 //  * kFixed per launch (start-up, epilogue);
 //  * with K % 128 == 0, 128 x 128 and 128 x 192 blocks on 128-byte K steps
-//    (one per CU, not sliced): whole 128-byte row segments stream at
-//    kCuRateRect per CU, under the same aggregate L2 rate.
+//    (one per CU): whole 128-byte row segments stream at kCuRateRect per CU,
+//    under the same aggregate L2 rate; cut into at most kFp8RectMaxSplit
+//    K-slices, the last slice of a tile writes its partial and reads all of
+//    them at that per-CU rate after kSplitLat (measured at 512 tokens: two
+//    slices pay off for K = 12288, N = 4096, where the whole tiles fill only
+//    half the CUs; more slices, or slicing a grid that fills the chip, lose).
 constexpr double kStep256 = 0.65;
 constexpr double kCuRateRect = 75e3;
 constexpr double kCuRate = 62e3;
@@ -781,6 +785,7 @@ constexpr double kSplitLat = 2.0;
 constexpr double kFixed = 3.0;
 constexpr int kFp8MinSliceSteps = 4;
 constexpr int kFp8MaxSplit = 16;
+constexpr int kFp8RectMaxSplit = 2;
 
 double fp8_plan_time(int64_t M, int64_t N, int64_t nk, int bm, int s, int cus) {
   const int64_t T = ((M + bm - 1) / bm) * ((N + bm - 1) / bm);
@@ -838,16 +843,21 @@ GemmPlan plan_fp8_gemm(int64_t M, int64_t N, int64_t K, int cus) {
     }
   }
   if (K % 128 == 0) {
+    int rect_s = 1;
     for (int bn : {128, 192}) {
       const int64_t T = ((M + 127) / 128) * ((N + bn - 1) / bn);
       const double step_bytes = (128.0 + bn) * 128.0;
-      const double steps = static_cast<double>(K / 128);
-      const double per_cu = static_cast<double>((T + cus - 1) / cus);
-      const double t = std::max(static_cast<double>(T) * steps * step_bytes / kL2Rate,
-                                per_cu * steps * step_bytes / kCuRateRect) + kFixed;
-      if (t < best_t) best_t = t, best_bm = -bn;
+      for (int s = 1; s <= kFp8RectMaxSplit && s * kFp8MinSliceSteps <= K / 128; ++s) {
+        const int64_t units = T * s;
+        const double steps = static_cast<double>((K / 128 + s - 1) / s);
+        const double per_cu = static_cast<double>((units + cus - 1) / cus);
+        double t = std::max(static_cast<double>(units) * steps * step_bytes / kL2Rate,
+                            per_cu * steps * step_bytes / kCuRateRect) + kFixed;
+        if (s > 1) t += (s + 1) * 4.0 * 128.0 * bn / kCuRateRect + kSplitLat;
+        if (t < best_t) best_t = t, best_bm = -bn, rect_s = s;
+      }
     }
-    if (best_bm < 0) return plan_fp8_gemm_rect(M, N, 1, -best_bm);
+    if (best_bm < 0) return plan_fp8_gemm_rect(M, N, rect_s, -best_bm);
   }
   GemmPlan p = plan_fp8_gemm_split(M, N, best_s, best_bm);
   // Whole 256x256 tiles in full waves and a partial last wave of R tiles:
