@@ -770,11 +770,13 @@ __global__ __launch_bounds__(256, 1) void k_fp8_gemm_rect(const uint8_t* __restr
 //  * kFixed per launch (start-up, epilogue);
 //  * with K % 128 == 0, 128 x 128 and 128 x 192 blocks on 128-byte K steps
 //    (one per CU): whole 128-byte row segments stream at kCuRateRect per CU,
-//    under the same aggregate L2 rate; cut into at most kFp8RectMaxSplit
-//    K-slices, the last slice of a tile writes its partial and reads all of
-//    them at that per-CU rate after kSplitLat (measured at 512 tokens: two
-//    slices pay off for K = 12288, N = 4096, where the whole tiles fill only
-//    half the CUs; more slices, or slicing a grid that fills the chip, lose).
+//    under the same aggregate L2 rate; 128 x 128 blocks may be cut into at
+//    most kFp8RectMaxSplit K-slices, the last slice of a tile writing its
+//    partial and reading all of them at that per-CU rate after kSplitLat
+//    (measured at 512 tokens: two slices of 128 x 128 blocks pay off for
+//    K = 12288, N = 4096, where the whole tiles fill only half the CUs; more
+//    slices, sliced 128 x 192 blocks, or slicing a grid that fills the chip
+//    lose).
 constexpr double kStep256 = 0.65;
 constexpr double kCuRateRect = 75e3;
 constexpr double kCuRate = 62e3;
@@ -847,7 +849,8 @@ GemmPlan plan_fp8_gemm(int64_t M, int64_t N, int64_t K, int cus) {
     for (int bn : {128, 192}) {
       const int64_t T = ((M + 127) / 128) * ((N + bn - 1) / bn);
       const double step_bytes = (128.0 + bn) * 128.0;
-      for (int s = 1; s <= kFp8RectMaxSplit && s * kFp8MinSliceSteps <= K / 128; ++s) {
+      const int smax = bn == 128 ? kFp8RectMaxSplit : 1;
+      for (int s = 1; s <= smax && s * kFp8MinSliceSteps <= K / 128; ++s) {
         const int64_t units = T * s;
         const double steps = static_cast<double>((K / 128 + s - 1) / s);
         const double per_cu = static_cast<double>((units + cus - 1) / cus);
