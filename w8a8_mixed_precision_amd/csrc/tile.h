@@ -138,6 +138,7 @@ __device__ __forceinline__ void flush_staged(const char* stg, char* __restrict__
 // w's 256 accumulators at byte ((w*64 + c)*64 + lane)*16, so every access is
 // 1 KB contiguous.
 constexpr int kSc1 = 16;                        // cache-policy bit sc1
+constexpr int kNt = 2;                          // cache-policy bit nt: streaming (non-temporal) access
 constexpr int kRawBuffer = 0x00020000;          // word 3 of a raw buffer descriptor (32-bit data format)
 constexpr int kPartWords = kBM * kBN;           // one 256x256 partial, 4-byte words
 
